@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for the selective state-space scan.
+
+TEST INFRASTRUCTURE ONLY.  This package is the plain, slow, sequential
+reference that the GPU path is checked against.  Only the test-suite, the
+smoke check and the CPU-baseline leg of the benchmark may import it; the
+product path never does, and the two share no code.
+
+The arithmetic lives in ``ssm_ref.c`` (plain C, fp64); ``ref.py`` marshals
+numpy arrays into it.  Parity pins are in ``tests/test_oracle_pins.py``.
+"""

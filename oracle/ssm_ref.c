@@ -1,0 +1,157 @@
+/*
+ * ssm_ref.c -- fp64 CPU oracle for the selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE ONLY: the reference the GPU path is checked against.
+ * Plain sequential C99, double precision, no SIMD intrinsics, no fast-math.
+ * It shares no code with the GPU path.
+ *
+ * What it computes (notation of the pages):
+ *   - the discrete recurrence and readout h_t = Abar h_{t-1} + Bbar u_t,
+ *     y_t = C h_t  ("The State That Must Remember Everything", Part 2,
+ *     "The Equation"), with no nonlinearity between steps;
+ *   - Abar = exp(delta * A) for the diagonal A of each channel and
+ *     Bbar = delta * B, the exponential-Euler reading of the discretisation
+ *     that the same page (Part 7) attributes to Mamba-1/2;
+ *   - delta, B and C given per token ("State Space Models and the
+ *     Post-Transformer Era", "The Selection Mechanism");
+ *   - the skip term D*u of the continuous model y = Cx + Du (same page,
+ *     "From Convolutions to State Spaces: S4");
+ *   - y_t reads the state AFTER token t has been written into it;
+ *   - optional softplus on delta (with a per-channel bias) and an optional
+ *     SiLU(z) gate on the output.
+ */
+#include "ssm_ref.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stddef.h>
+
+double ssm_ref_softplus(double x) {
+  /* log(1 + e^x), written so that e^x never overflows:
+   * for x > 0, log(1 + e^x) = x + log(1 + e^-x). */
+  if (x > 0.0) return x + log1p(exp(-x));
+  return log1p(exp(x));
+}
+
+double ssm_ref_silu(double z) {
+  /* z * sigmoid(z) = z / (1 + e^-z) */
+  return z / (1.0 + exp(-z));
+}
+
+void ssm_ref_pair_then(long n, const double* a1, const double* b1,
+                       const double* a2, const double* b2,
+                       double* a_out, double* b_out) {
+  for (long i = 0; i < n; ++i) {
+    double a = a1[i] * a2[i];
+    double b = a2[i] * b1[i] + b2[i];
+    a_out[i] = a;
+    b_out[i] = b;
+  }
+}
+
+/* delta for one (token, channel): raw value plus bias, then softplus. */
+static double step_delta(double raw, const double* bias, long d, int softplus_flag) {
+  double x = raw + (bias ? bias[d] : 0.0);
+  return softplus_flag ? ssm_ref_softplus(x) : x;
+}
+
+/* One recurrence step for one channel d: updates h[0:N] in place and
+ * returns the gated output.  Bt, Ct point at this token's B and C rows. */
+static double one_step(double* h, double ut, double dt_raw, const double* zt,
+                       const double* Arow, const double* Bt, const double* Ct,
+                       const double* D, const double* bias, long d, long N,
+                       int softplus_flag) {
+  double delta = step_delta(dt_raw, bias, d, softplus_flag);
+  double acc = 0.0;
+  for (long n = 0; n < N; ++n) {
+    double abar = exp(delta * Arow[n]);        /* fade */
+    double bbar_u = delta * Bt[n] * ut;        /* add */
+    h[n] = abar * h[n] + bbar_u;               /* h_t = Abar h_{t-1} + Bbar u_t */
+    acc += Ct[n] * h[n];                       /* y_t = C_t . h_t */
+  }
+  double v = acc + (D ? D[d] : 0.0) * ut;      /* + D u_t */
+  if (zt) v = v * ssm_ref_silu(*zt);           /* gate */
+  return v;
+}
+
+typedef struct {
+  const double *u, *delta, *A, *B, *C, *D, *z, *bias;
+  int softplus_flag;
+  double *y, *final_state;
+  long batch, L, dim, N;
+  long first, last; /* range of flattened (b, d) channels for this worker */
+} scan_job;
+
+static void scan_channels(const scan_job* j) {
+  double hbuf[4096];
+  for (long bd = j->first; bd < j->last; ++bd) {
+    long b = bd / j->dim, d = bd % j->dim;
+    double* h = hbuf;
+    for (long n = 0; n < j->N; ++n) h[n] = 0.0;   /* the scan starts from a zero state */
+    for (long t = 0; t < j->L; ++t) {
+      long io = (b * j->L + t) * j->dim + d;      /* [batch, L, dim] */
+      long bc = (b * j->L + t) * j->N;            /* [batch, L, dstate] */
+      j->y[io] = one_step(h, j->u[io], j->delta[io], j->z ? &j->z[io] : NULL,
+                          &j->A[d * j->N], &j->B[bc], &j->C[bc], j->D, j->bias, d,
+                          j->N, j->softplus_flag);
+    }
+    if (j->final_state)
+      for (long n = 0; n < j->N; ++n) j->final_state[(b * j->dim + d) * j->N + n] = h[n];
+  }
+}
+
+static void* scan_worker(void* arg) {
+  scan_channels((const scan_job*)arg);
+  return NULL;
+}
+
+int ssm_ref_scan_fwd(const double* u, const double* delta, const double* A,
+                     const double* B, const double* C, const double* D,
+                     const double* z, const double* delta_bias, int softplus_flag,
+                     double* y, double* final_state,
+                     long batch, long L, long dim, long dstate, int nthreads) {
+  if (!u || !delta || !A || !B || !C || !y) return -1;
+  if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 4096) return -1;
+  long channels = batch * dim;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (nthreads > channels) nthreads = (int)channels;
+
+  scan_job jobs[256];
+  pthread_t tids[256];
+  int running[256];
+  for (int i = 0; i < nthreads; ++i) {
+    scan_job j = {u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, final_state,
+                  batch, L, dim, dstate, channels * i / nthreads, channels * (i + 1) / nthreads};
+    jobs[i] = j;
+  }
+  if (nthreads == 1) {
+    scan_channels(&jobs[0]);
+    return 0;
+  }
+  for (int i = 0; i < nthreads; ++i) {
+    running[i] = pthread_create(&tids[i], NULL, scan_worker, &jobs[i]) == 0;
+    if (!running[i]) scan_channels(&jobs[i]); /* no thread: do this share here */
+  }
+  for (int i = 0; i < nthreads; ++i)
+    if (running[i]) pthread_join(tids[i], NULL);
+  return 0;
+}
+
+int ssm_ref_state_update(double* state, const double* u, const double* delta,
+                         const double* A, const double* B, const double* C,
+                         const double* D, const double* z, const double* delta_bias,
+                         int softplus_flag, double* y,
+                         long batch, long dim, long dstate) {
+  if (!state || !u || !delta || !A || !B || !C || !y) return -1;
+  if (batch <= 0 || dim <= 0 || dstate <= 0) return -1;
+  for (long b = 0; b < batch; ++b) {
+    for (long d = 0; d < dim; ++d) {
+      long io = b * dim + d;                       /* [batch, dim] */
+      y[io] = one_step(&state[io * dstate], u[io], delta[io], z ? &z[io] : NULL,
+                       &A[d * dstate], &B[b * dstate], &C[b * dstate], D, delta_bias, d,
+                       dstate, softplus_flag);
+    }
+  }
+  return 0;
+}

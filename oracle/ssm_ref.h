@@ -1,0 +1,71 @@
+/*
+ * ssm_ref.h -- fp64 CPU oracle for the selective state-space scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the slow, obviously-correct
+ * reference that the GPU path is checked against.  Only the test-suite, the
+ * smoke check and the CPU-baseline leg of the benchmark load it; the product
+ * path never calls it and shares no code, header or constant with it.
+ *
+ * Every buffer is a HOST pointer to contiguous row-major fp64 data owned by
+ * the caller.  Layouts (dimension names follow the pages):
+ *   u, delta, z, y        [batch, L, dim]
+ *   B, C                  [batch, L, dstate]   (shared by every channel)
+ *   A                     [dim, dstate]        (diagonal state matrix per channel)
+ *   D, delta_bias         [dim]
+ *   state / final_state   [batch, dim, dstate]
+ * Nullable arguments: D (treated as 0), z (no gate), delta_bias (treated as 0),
+ * final_state (not written).
+ *
+ * Return value: 0 on success, -1 on a bad argument (null required pointer or
+ * a size <= 0).  Nothing is allocated that outlives a call.
+ */
+#ifndef SSM_REF_H
+#define SSM_REF_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Selective scan over a whole sequence from a zero state.
+ *   "The State That Must Remember Everything", Part 2, "The Equation":
+ *       h_t = Abar h_{t-1} + Bbar u_t,   y_t = C h_t
+ *   with Abar = exp(delta_t * A) (exponential-Euler, Part 7) and
+ *   Bbar u_t = delta_t * B_t * u_t; delta, B and C are per token
+ *   ("State Space Models and the Post-Transformer Era", "The Selection
+ *   Mechanism").  The D*u skip comes from the continuous model
+ *   y = Cx + Du (same page, "From Convolutions to State Spaces: S4").
+ *   delta_t = softplus(delta_raw + bias) when softplus_flag != 0, and the
+ *   output is multiplied by SiLU(z) when z is given.
+ * nthreads >= 1 splits the independent (batch, channel) recurrences over
+ * POSIX threads; the arithmetic of each recurrence is unchanged, so the
+ * result does not depend on nthreads. */
+int ssm_ref_scan_fwd(const double* u, const double* delta, const double* A,
+                     const double* B, const double* C, const double* D,
+                     const double* z, const double* delta_bias, int softplus_flag,
+                     double* y, double* final_state,
+                     long batch, long L, long dim, long dstate, int nthreads);
+
+/* One recurrent (decode) step from the given state, updated in place.
+ *   u, delta, z, y: [batch, dim];  B, C: [batch, dstate];
+ *   state: [batch, dim, dstate].  Same arithmetic as one step of the scan. */
+int ssm_ref_state_update(double* state, const double* u, const double* delta,
+                         const double* A, const double* B, const double* C,
+                         const double* D, const double* z, const double* delta_bias,
+                         int softplus_flag, double* y,
+                         long batch, long dim, long dstate);
+
+/* The fade-and-add composition "(a1,b1) then (a2,b2) = (a1 a2, a2 b1 + b2)"
+ * ("Mamba is attention all you really need, part 2", "The relay"),
+ * applied elementwise to n pairs. */
+void ssm_ref_pair_then(long n, const double* a1, const double* b1,
+                       const double* a2, const double* b2,
+                       double* a_out, double* b_out);
+
+/* Scalar helpers used by the scan, exported so tests can pin them. */
+double ssm_ref_softplus(double x);  /* log(1 + e^x) */
+double ssm_ref_silu(double z);      /* z * sigmoid(z) */
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,48 @@
+"""Seeded input generators: determinism, bf16 rounding, and the stated distributions."""
+import numpy as np
+import torch
+
+from selective_state_space_33_amd import inputs as I
+
+
+def test_bf16_rounding_matches_torch_round_to_nearest_even():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100_000).astype(np.float32) * 10.0 ** rng.integers(-6, 6, 100_000),
+                        # exact ties: low 16 bits = 0x8000, even and odd upper parts
+                        (np.arange(1000, dtype=np.uint32) << 16 | 0x8000).view(np.float32) + 0,
+                        np.array([0.0, -0.0, 1.0, -1.0, 3.4e38, -3.4e38], dtype=np.float32)])
+    ours = I.round_to_bf16(x)
+    theirs = torch.from_numpy(x.copy()).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(ours.view(np.uint32), theirs.view(np.uint32))
+    assert np.array_equal(I.bf16_bits(ours).astype(np.uint32) << 16, ours.view(np.uint32))
+
+
+def test_generators_are_deterministic_and_shaped():
+    w = I.WORKLOADS["tiny_fp32"]
+    a, b = I.make_inputs(w, 0), I.make_inputs(w, 0)
+    for k in a:
+        if a[k] is not None:
+            assert np.array_equal(a[k], b[k]), k
+    assert a["u"].shape == (1, 256, 16) and a["B"].shape == (1, 256, 4) and a["A"].shape == (16, 4)
+    c = I.make_inputs(w, 1)
+    assert not np.array_equal(a["u"], c["u"])
+    d = I.make_inputs(I.WORKLOADS["decode_bf16"].scaled(batch=4, dim=64), 0)
+    assert d["u"].shape == (4, 64) and d["B"].shape == (4, 16) and d["h0"].shape == (4, 64, 16)
+    assert np.array_equal(I.round_to_bf16(d["u"]), d["u"])
+
+
+def test_distributions():
+    w = I.WORKLOADS["mamba130m_bf16"].scaled(batch=2, L=512, dim=256)
+    x = I.make_inputs(w, 0)
+    for k in ("u", "z", "delta", "B", "C"):
+        assert abs(float(x[k].mean())) < 0.02 and abs(float(x[k].std()) - 1.0) < 0.02, k
+    sp = np.logaddexp(0.0, x["delta_bias"].astype(np.float64))
+    assert sp.min() >= 1e-3 * (1 - 1e-5) and sp.max() <= 0.1 * (1 + 1e-5)
+    assert np.all(x["A"] == -(np.arange(16) + 1.0)) and np.all(x["D"] == 1.0)
+    # long audio-style input: unit variance overall, slow-fade bias range
+    wa = I.WORKLOADS["long_audio_fp32"].scaled(L=1 << 15)
+    xa = I.make_inputs(wa, 0)
+    assert xa["z"] is None
+    assert abs(float(xa["u"].var()) - 1.0) < 0.15
+    spa = np.logaddexp(0.0, xa["delta_bias"].astype(np.float64))
+    assert spa.min() >= 1e-4 * (1 - 1e-5) and spa.max() <= 1e-2 * (1 + 1e-5)
