@@ -1,0 +1,246 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 selective scan on one MI355X.
+
+One step = one ssm_scan_fwd call (prologue, discretisation, in-chunk scan,
+chunk carry, readout and gated epilogue) over the Mamba-2.8B-shaped bf16
+layer: batch 4, L 4096, dim 5120, dstate 16, z gate on, final state
+returned.  Inputs are seeded synthetic tensors already resident in HBM.
+The one-token decode step (ssm_state_update, batch 256, dim 5120,
+dstate 16) is timed separately in the same run and reported under "decode".
+
+Prints ONE JSON line.  Fields beyond the common ones:
+  roofline      the dominant kernel against its binding roofline (VALU issue:
+                the scan needs 4 fp32 VALU ops + 1 transcendental per state
+                update, which takes longer at peak than moving its bytes);
+  hbm           the same launch against the 8 TB/s HBM roofline (the metric's
+                second half);
+  cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
+VALU_PEAK_TFLOPS = 157.3        # MI355X fp32 vector peak: 256 CU x 4 SIMD x 32 lanes/clk x 2 flops x 2.4 GHz
+TRANS_SLOTS = 4                 # a transcendental (exp2/log2/rcp) issues at a quarter of the fp32 FMA rate
+# FMA-equivalent VALU slots the method needs: per state update 4 fp32 ops (delta*A, delta*u*B,
+# the fade-and-add fma, the readout fma) + 1 exp; per (token, channel) softplus (exp, log + 2 ops),
+# delta*u, the D skip fma, SiLU (exp, rcp + 2 ops) and the gate multiply.
+SLOTS_PER_UPDATE = 4 + 1 * TRANS_SLOTS
+SLOTS_PER_TOKEN_CHANNEL = 4 * TRANS_SLOTS + 7
+
+
+def scan_bytes(w, with_final=True):
+    s = 2 if w.dtype == "bf16" else 4
+    n_io = 4 if w.gate else 3  # u, delta, (z), y
+    b = w.batch * w.L * w.dim * n_io * s + w.batch * w.L * w.dstate * 2 * s
+    b += w.dim * w.dstate * 4 + 2 * w.dim * 4
+    if with_final:
+        b += w.batch * w.dim * w.dstate * 4
+    return b
+
+
+def decode_bytes(w):
+    s = 2 if w.dtype == "bf16" else 4
+    return (2 * w.batch * w.dim * w.dstate * 4 + w.batch * w.dim * 4 * s + w.batch * w.dstate * 2 * s
+            + w.dim * w.dstate * 4 + 2 * w.dim * 4)
+
+
+def scan_slots(w):
+    return w.updates * SLOTS_PER_UPDATE + w.batch * w.L * w.dim * SLOTS_PER_TOKEN_CHANNEL
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    cdir = os.path.join(ROOT, "selective_state_space_33_amd", "csrc")
+    for name in sorted(os.listdir(cdir)):
+        with open(os.path.join(cdir, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload_name):
+    """HBM bytes per launch from committed rocprofv3 --pmc counters, if taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(workload_name)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def gpu_inputs(x, dtype, dev):
+    import numpy as np
+    import torch
+
+    def t(a, f32=False):
+        if a is None:
+            return None
+        g = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+        return g if (f32 or dtype == "f32") else g.to(torch.bfloat16)
+
+    return dict(u=t(x["u"]), delta=t(x["delta"]), z=t(x["z"]), B=t(x["B"]), C=t(x["C"]), A=t(x["A"], True),
+                D=t(x["D"], True), delta_bias=t(x["delta_bias"], True), h0=t(x.get("h0"), True))
+
+
+def time_calls(fn, steps, warmup, stream):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall / steps * 1e3
+
+
+def cpu_baseline(w, x, budget_s):
+    """The fp64 oracle on the first channels of every batch row (full sequence), sized to ~budget_s of wall time.
+
+    When the whole workload fits in the budget it is run whole, once.
+    """
+    import numpy as np
+
+    from oracle import ref as R
+
+    threads = max(1, min(16, os.cpu_count() or 1))
+
+    def run(nch):
+        sub = dict(u=x["u"][:, :, :nch], delta=x["delta"][:, :, :nch],
+                   z=None if x["z"] is None else x["z"][:, :, :nch], B=x["B"], C=x["C"],
+                   A=x["A"][:nch], D=x["D"][:nch], delta_bias=x["delta_bias"][:nch])
+        sub = {k: (None if v is None else np.ascontiguousarray(v, dtype=np.float64)) for k, v in sub.items()}
+        t0 = time.perf_counter()
+        R.scan_fwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], D=sub["D"], z=sub["z"],
+                   delta_bias=sub["delta_bias"], nthreads=threads)
+        return time.perf_counter() - t0
+
+    per_channel = w.batch * w.L * w.dstate
+    probe = min(w.dim, max(1, threads // max(1, w.batch)) * 4)
+    dt = run(probe)
+    rate = probe * per_channel / dt
+    nch = int(min(w.dim, max(probe, budget_s * rate / per_channel)))
+    dt = run(nch)
+    ups = nch * per_channel / dt
+    what = "the whole workload" if nch == w.dim else f"channels 0..{nch - 1} of every batch row"
+    return {"value": ups, "unit": "updates/s", "cores": threads, "kind": "oracle",
+            "sample": f"{w.name}: {what}, all {w.L} tokens, dstate {w.dstate} "
+                      f"({nch * per_channel:.3e} updates in {dt:.2f} s; fp64 sequential recurrence, "
+                      f"{threads} threads over channels)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2p8b_bf16", help="scan workload to time (default: the 2.8B layer)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: there is no multi-GPU path here (the scan would shard over "
+              "batch and channels with no communication, or over the sequence with one exchange of chunk "
+              "pairs).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from selective_state_space_33_amd import inputs as I
+    from selective_state_space_33_amd import ops
+
+    ops.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    w = I.WORKLOADS[args.workload]
+    assert w.op == "scan"
+    x = I.make_inputs(w, 0)
+    g = gpu_inputs(x, w.dtype, dev)
+    y = torch.empty_like(g["u"])
+    fs = torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev)
+    need = ops.ssm_scan_workspace_size(w.batch, w.L, w.dim, w.dstate, g["u"].dtype)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
+
+    def step():
+        ops.ssm_scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"], delta_bias=g["delta_bias"],
+                         y=y, final_state=fs, workspace=ws, stream=stream)
+
+    ms, wall_ms = time_calls(step, args.steps, args.warmup, stream)
+    ups = w.updates / (ms * 1e-3)
+    nbytes = scan_bytes(w)
+    slots = scan_slots(w)
+    achieved_tf = 2.0 * slots / (ms * 1e-3) / 1e12
+    achieved_gbs = nbytes / (ms * 1e-3) / 1e9
+    traffic = measured_traffic(w.name)
+
+    out = {
+        "metric": "selective-scan state updates/s (B*L*D*N) and % of MI355X HBM roofline",
+        "value": ups,
+        "unit": "updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "op": "ssm_scan_fwd", "batch": w.batch, "seq_len": w.L, "dim": w.dim,
+                   "dstate": w.dstate, "storage_dtype": w.dtype, "z_gate": w.gate, "final_state": True,
+                   "workspace_bytes": need, "seed": 0, "wall_ms_per_step": wall_ms},
+        "roofline": {"bound": "alu", "achieved": achieved_tf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved_tf / VALU_PEAK_TFLOPS, "traffic": traffic,
+                     "counted": f"FMA-equivalent fp32 VALU slots x 2 flops: {SLOTS_PER_UPDATE} per state update, "
+                                f"{SLOTS_PER_TOKEN_CHANNEL} per (token, channel); transcendental = "
+                                f"{TRANS_SLOTS} slots"},
+        "hbm": {"algorithmic_bytes": nbytes, "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved_gbs / HBM_PEAK_GBS},
+    }
+
+    if not args.no_decode:
+        wd = I.WORKLOADS["decode_bf16"]
+        xd = I.make_inputs(wd, 0)
+        gd = gpu_inputs(xd, wd.dtype, dev)
+        yd = torch.empty_like(gd["u"])
+        state = gd["h0"]
+
+        def dstep():
+            ops.ssm_state_update(state, gd["u"], gd["delta"], gd["A"], gd["B"], gd["C"], D=gd["D"], z=gd["z"],
+                                 delta_bias=gd["delta_bias"], y=yd, stream=stream)
+
+        dms, _ = time_calls(dstep, max(args.steps, 20), args.warmup, stream)
+        db = decode_bytes(wd)
+        out["decode"] = {"workload": wd.name, "op": "ssm_state_update", "ms_per_step": dms,
+                         "value": wd.updates / (dms * 1e-3), "unit": "updates/s",
+                         "roofline": {"bound": "hbm", "achieved": db / (dms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": db / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                      "algorithmic_bytes": db, "traffic": measured_traffic(wd.name)}}
+        del gd, yd, state
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,111 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) selective state-space scan.
+ *
+ * The operation.  For every batch b and channel d the library runs the
+ * discretised, input-dependent state-space recurrence
+ *     h_t = exp(delta_t * A[d,:]) (.) h_{t-1} + delta_t * B_t * u_t
+ *     y_t = (C_t . h_t + D[d] * u_t) * SiLU(z_t)
+ * with delta_t = softplus(delta_raw_t + delta_bias[d]) (or delta_raw_t +
+ * delta_bias[d] when softplus_flag is 0).  Sources, by page title:
+ *   - "The State That Must Remember Everything", Part 2 "The Equation":
+ *     the discrete recurrence h_t = Abar h_{t-1} + Bbar u_t, y_t = C h_t, and
+ *     the continuous model with the D u term; Part 7: Mamba-1/2 use an
+ *     exponential-Euler discretisation (Abar = exp(delta A), Bbar = delta B);
+ *     Part 3 "The Hardware-Aware Way Out": scan, fusion, state kept on chip.
+ *   - "State Space Models and the Post-Transformer Era", "The Selection
+ *     Mechanism": delta, B and C are computed per token; A is diagonal per
+ *     channel ("Mamba-2 and Structured State Space Duality" contrasts it with
+ *     Mamba-2's scalar A).
+ *   - "Mamba is attention all you really need, part 2", "The relay": each
+ *     step is a fade-and-add pair (a, b) and pairs compose as
+ *     (a1,b1) then (a2,b2) = (a1 a2, a2 b1 + b2), which is what lets the
+ *     sequence be cut into chunks that are scanned in parallel.
+ * The SiLU(z) output gate, the softplus on delta and its per-channel bias
+ * are the conventional Mamba block epilogue/prologue; the pages leave them
+ * unspecified and this library takes that standard form.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the
+ *     library allocates and frees nothing and keeps no state between calls,
+ *     so concurrent calls on different streams are safe.
+ *   - Layouts are contiguous row-major:
+ *       u, delta, z, y        [batch, L, dim]     (decode: [batch, dim])
+ *       B, C                  [batch, L, dstate]  (decode: [batch, dstate]),
+ *                             shared by all dim channels of a token
+ *       A                     [dim, dstate]  fp32
+ *       D, delta_bias         [dim]          fp32
+ *       state, final_state    [batch, dim, dstate]  fp32
+ *   - u, delta, z, B, C and y have dtype `dt` (fp32 or bf16); A, D,
+ *     delta_bias and the state are fp32.  All arithmetic is fp32; bf16
+ *     outputs are rounded to nearest even.
+ *   - Work is enqueued on `stream` and the call returns at once; outputs are
+ *     valid after the stream is synchronised.
+ *   - Arguments are validated before any HIP call: a null required pointer,
+ *     a size <= 0, an unknown dtype or a too-small workspace gives
+ *     SSM_ERR_INVALID_ARG; a dstate outside 1..64, an odd dstate with bf16,
+ *     or batch / chunk counts above 65535 give SSM_ERR_UNSUPPORTED.  Nothing
+ *     is launched in either case.  A failed launch gives SSM_ERR_HIP.
+ *     Input values are not inspected (NaN in gives NaN out).
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_ERR_INVALID_ARG = 1,
+  SSM_ERR_UNSUPPORTED = 2,
+  SSM_ERR_HIP = 3
+} ssm_status_t;
+
+typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
+
+/* Bytes of device workspace that ssm_scan_fwd needs for this shape (0 when
+ * the sequence is scanned in a single chunk).  The workspace holds, per
+ * chunk of the sequence, the composed fade-and-add pair of that chunk and
+ * the state carried into it ("The relay": squash each chunk to one pair,
+ * combine the chunk pairs, pass the real states back).  Returns 0 for
+ * arguments ssm_scan_fwd would reject. */
+size_t ssm_scan_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt);
+
+/* Selective scan over a whole sequence, starting from a zero state.
+ *   Required: u, delta, A, B, C, y.  Optional (NULL allowed): D (no skip
+ *   term), z (no gate), delta_bias (zero bias), final_state (not written).
+ *   final_state receives h_L, the state after the last token (before the
+ *   gate, which only touches y).  workspace may be NULL only when
+ *   ssm_scan_workspace_size() returns 0; otherwise it must point at
+ *   workspace_bytes >= that size of device memory, 256-byte aligned, which
+ *   the call overwrites and which must not be shared with a concurrent call.
+ *   y must not alias any input. */
+ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                          void* y, float* final_state,
+                          int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One recurrent (decode) step: the same arithmetic as one token of the scan,
+ * reading `state` as h_{t-1} and overwriting it in place with h_t
+ * ("Mamba: The State Space Models Challenging the Transformer", "What a
+ * state space model actually is": each new token is one cheap state update).
+ *   Required: state, u, delta, A, B, C, y.  Optional: D, z, delta_bias.
+ *   state must not alias any other argument. */
+ssm_status_t ssm_state_update(float* state, const void* u, const void* delta, const float* A, const void* B,
+                              const void* C, const float* D, const void* z, const float* delta_bias,
+                              int softplus_flag, void* y, int64_t batch, int64_t dim, int64_t dstate,
+                              ssm_dtype_t dt, hipStream_t stream);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* ssm_status_string(ssm_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSM_SCAN_H */

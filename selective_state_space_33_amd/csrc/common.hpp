@@ -1,0 +1,142 @@
+// common.hpp -- device helpers shared by the gfx950 selective-scan kernels.
+//
+// Element I/O for fp32 and bf16 storage, the softplus and SiLU used around the
+// recurrence, and the fp32 -> bf16 store (round to nearest even, done by the
+// hardware v_cvt_pk_bf16_f32 on gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;  // 1 / ln 2
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Storage tags.
+struct F32 {};
+struct BF16 {};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 values -> two bf16 (round to nearest even) packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t to_bf16(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+// Raw storage of VW consecutive elements, loaded with one vector access.
+template <class IO, int VW> struct Raw;
+template <> struct Raw<F32, 4> { float4 v; };
+template <> struct Raw<F32, 1> { float v; };
+template <> struct Raw<BF16, 4> { uint2 v; };
+template <> struct Raw<BF16, 1> { uint16_t v; };
+
+template <class IO, int VW> __device__ __forceinline__ Raw<IO, VW> raw_zero() {
+  Raw<IO, VW> r;
+  __builtin_memset(&r, 0, sizeof(r));
+  return r;
+}
+
+// Load elements [idx, idx + VW) of a row-major tensor.  idx must be a
+// multiple of VW and the base suitably aligned (checked on the host).
+template <class IO, int VW> __device__ __forceinline__ Raw<IO, VW> raw_load(const void* base, int64_t idx);
+template <> __device__ __forceinline__ Raw<F32, 4> raw_load<F32, 4>(const void* base, int64_t idx) {
+  return {*reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx)};
+}
+template <> __device__ __forceinline__ Raw<F32, 1> raw_load<F32, 1>(const void* base, int64_t idx) {
+  return {static_cast<const float*>(base)[idx]};
+}
+template <> __device__ __forceinline__ Raw<BF16, 4> raw_load<BF16, 4>(const void* base, int64_t idx) {
+  return {*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx)};
+}
+template <> __device__ __forceinline__ Raw<BF16, 1> raw_load<BF16, 1>(const void* base, int64_t idx) {
+  return {static_cast<const uint16_t*>(base)[idx]};
+}
+
+template <class IO, int VW> __device__ __forceinline__ void unpack(const Raw<IO, VW>& r, float* out);
+template <> __device__ __forceinline__ void unpack<F32, 4>(const Raw<F32, 4>& r, float* o) {
+  o[0] = r.v.x; o[1] = r.v.y; o[2] = r.v.z; o[3] = r.v.w;
+}
+template <> __device__ __forceinline__ void unpack<F32, 1>(const Raw<F32, 1>& r, float* o) { o[0] = r.v; }
+template <> __device__ __forceinline__ void unpack<BF16, 4>(const Raw<BF16, 4>& r, float* o) {
+  o[0] = bf16_lo(r.v.x); o[1] = bf16_hi(r.v.x); o[2] = bf16_lo(r.v.y); o[3] = bf16_hi(r.v.y);
+}
+template <> __device__ __forceinline__ void unpack<BF16, 1>(const Raw<BF16, 1>& r, float* o) {
+  o[0] = __uint_as_float(static_cast<uint32_t>(r.v) << 16);
+}
+
+template <class IO, int VW> __device__ __forceinline__ void store_vals(void* base, int64_t idx, const float* v);
+template <> __device__ __forceinline__ void store_vals<F32, 4>(void* base, int64_t idx, const float* v) {
+  *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void store_vals<F32, 1>(void* base, int64_t idx, const float* v) {
+  static_cast<float*>(base)[idx] = v[0];
+}
+template <> __device__ __forceinline__ void store_vals<BF16, 4>(void* base, int64_t idx, const float* v) {
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) =
+      make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+template <> __device__ __forceinline__ void store_vals<BF16, 1>(void* base, int64_t idx, const float* v) {
+  static_cast<uint16_t*>(base)[idx] = to_bf16(v[0]);
+}
+
+// B_t and C_t rows are shared by every channel of a token, so within a
+// wavefront their addresses are uniform.  Reading them through the constant
+// address space lets the compiler use scalar (s_load) loads into SGPRs, which
+// the VALU then takes as operands directly.
+typedef const __attribute__((address_space(4))) float* cfloat_p;
+typedef const __attribute__((address_space(4))) uint32_t* cu32_p;
+
+// NPL consecutive elements of a B/C row starting at flat index off (uniform).
+// bf16: off is even whenever NPL is even (dstate is even), so whole dwords are
+// read and split; NPL == 1 reads the enclosing dword and picks its half.
+template <int NPL> struct RowF32 {
+  static __device__ __forceinline__ void load(const void* base, int64_t off, float* v) {
+    cfloat_p p = (cfloat_p)(base);
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) v[j] = p[off + j];
+  }
+};
+template <int NPL> struct RowBF16 {
+  static __device__ __forceinline__ void load(const void* base, int64_t off, float* v) {
+    cu32_p p = (cu32_p)(base);
+    if constexpr (NPL == 1) {
+      const uint32_t w = p[off >> 1];
+      v[0] = (off & 1) ? bf16_hi(w) : bf16_lo(w);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NPL / 2; ++k) {
+        const uint32_t w = p[(off >> 1) + k];
+        v[2 * k] = bf16_lo(w);
+        v[2 * k + 1] = bf16_hi(w);
+      }
+    }
+  }
+};
+template <class IO, int NPL> struct Row;
+template <int NPL> struct Row<F32, NPL> : RowF32<NPL> {};
+template <int NPL> struct Row<BF16, NPL> : RowBF16<NPL> {};
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).
+// log1p(e) uses a short series when e < 1/16 (relative error < 2e-7) and
+// log2(1 + e) * ln 2 otherwise (relative error < 1e-6), so no branch diverges.
+__device__ __forceinline__ float softplus_f(float x) {
+  const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
+  const float viaLog = __builtin_amdgcn_logf(1.0f + e) * kLn2;
+  const float series = e * (1.0f + e * (-0.5f + e * (1.0f / 3.0f + e * (-0.25f + e * 0.2f))));
+  return __builtin_fmaxf(x, 0.0f) + (e < 0.0625f ? series : viaLog);
+}
+
+// SiLU(z) = z * sigmoid(z) = z / (1 + e^-z); e^-z = inf for very negative z gives -0.
+__device__ __forceinline__ float silu_f(float z) {
+  const float e = __builtin_amdgcn_exp2f(-z * kLog2e);
+  return z * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+}  // namespace ssm

@@ -1,0 +1,159 @@
+"""ctypes binding of libssmscan.so (the gfx950 selective-scan C ABI).
+
+The functions carry the names of the C entry points and only marshal
+arguments: tensor checks, default outputs/workspace allocated with torch on
+the inputs' device, and the raw device pointers plus the current HIP stream
+handed to the library.  Every step of the computation runs in the HIP
+kernels; there is no fallback.  If the library is missing, ``lib()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssmscan.so")
+
+SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP = 0, 1, 2, 3
+SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
+
+# Every symbol include/ssm_scan.h declares.
+EXPORTED = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update", "ssm_status_string")
+
+_lib = None
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+
+
+class SSMError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where} failed: {ssm_status_string(code)} ({code})")
+        self.code = code
+
+
+def lib() -> ctypes.CDLL:
+    """Open libssmscan.so (built in-tree by __graft_entry__.build()); raises if it is absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        L.ssm_scan_workspace_size.restype = ctypes.c_size_t
+        L.ssm_scan_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+        L.ssm_scan_fwd.restype = ctypes.c_int
+        L.ssm_scan_fwd.argtypes = ([_vp] * 8 + [ctypes.c_int, _vp, _vp] + [_i64] * 4 +
+                                   [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
+        L.ssm_state_update.restype = ctypes.c_int
+        L.ssm_state_update.argtypes = [_vp] * 9 + [ctypes.c_int, _vp] + [_i64] * 3 + [ctypes.c_int, _vp]
+        L.ssm_status_string.restype = ctypes.c_char_p
+        L.ssm_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def ssm_status_string(code: int) -> str:
+    return lib().ssm_status_string(int(code)).decode()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return SSM_DTYPE_F32
+    if t == torch.bfloat16:
+        return SSM_DTYPE_BF16
+    raise TypeError(f"unsupported storage dtype {t}; use float32 or bfloat16")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t: Optional[torch.Tensor], name: str, dtype, shape, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device, stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def ssm_scan_workspace_size(batch: int, L: int, dim: int, dstate: int, dtype: torch.dtype) -> int:
+    return int(lib().ssm_scan_workspace_size(batch, L, dim, dstate, _dtype_code(dtype)))
+
+
+def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+                 y=None, final_state=None, workspace=None, return_final_state: bool = True, stream=None):
+    """Selective scan from a zero state on the GPU.
+
+    u, delta, z: [batch, L, dim]; B, C: [batch, L, dstate] (float32 or bfloat16,
+    all the same); A: [dim, dstate], D, delta_bias: [dim] (float32).
+    Returns (y, final_state); final_state is None if not requested.
+    """
+    batch, L, dim = u.shape
+    dstate = A.shape[1]
+    dev, dt = u.device, u.dtype
+    code = _dtype_code(dt)
+    for name, t, shp in (("u", u, (batch, L, dim)), ("delta", delta, (batch, L, dim)), ("z", z, (batch, L, dim)),
+                         ("B", B, (batch, L, dstate)), ("C", C, (batch, L, dstate))):
+        _check(t, name, dt, shp, dev)
+    _check(A, "A", torch.float32, (dim, dstate), dev)
+    _check(D, "D", torch.float32, (dim,), dev)
+    _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    if y is None:
+        y = torch.empty((batch, L, dim), dtype=dt, device=dev)
+    _check(y, "y", dt, (batch, L, dim), dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", torch.float32, (batch, dim, dstate), dev)
+    need = ssm_scan_workspace_size(batch, L, dim, dstate, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                            1 if softplus else 0, _ptr(y), _ptr(final_state), batch, L, dim, dstate, code,
+                            _ptr(workspace), ws_bytes, _stream(dev, stream))
+    if rc != SSM_OK:
+        raise SSMError(rc, "ssm_scan_fwd")
+    return y, final_state
+
+
+def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+                     y=None, stream=None):
+    """One decode step on the GPU; `state` [batch, dim, dstate] (float32) is updated in place.
+
+    u, delta, z: [batch, dim]; B, C: [batch, dstate]. Returns y [batch, dim].
+    """
+    batch, dim = u.shape
+    dstate = A.shape[1]
+    dev, dt = u.device, u.dtype
+    code = _dtype_code(dt)
+    _check(state, "state", torch.float32, (batch, dim, dstate), dev)
+    for name, t, shp in (("u", u, (batch, dim)), ("delta", delta, (batch, dim)), ("z", z, (batch, dim)),
+                         ("B", B, (batch, dstate)), ("C", C, (batch, dstate))):
+        _check(t, name, dt, shp, dev)
+    _check(A, "A", torch.float32, (dim, dstate), dev)
+    _check(D, "D", torch.float32, (dim,), dev)
+    _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    if y is None:
+        y = torch.empty((batch, dim), dtype=dt, device=dev)
+    _check(y, "y", dt, (batch, dim), dev)
+    rc = lib().ssm_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                _ptr(delta_bias), 1 if softplus else 0, _ptr(y), batch, dim, dstate, code,
+                                _stream(dev, stream))
+    if rc != SSM_OK:
+        raise SSMError(rc, "ssm_state_update")
+    return y
