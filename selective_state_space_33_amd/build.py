@@ -25,7 +25,7 @@ def hipcc_path() -> str:
 
 
 def compile_flags():
-    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
+    return ["--offload-arch=" + ARCH, "-O3", "-std=c++20", "-fPIC", "-Wall",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-I", INCLUDE, "-I", os.path.join(HERE, "csrc")]
 

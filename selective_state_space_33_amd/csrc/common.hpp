@@ -33,8 +33,10 @@ __device__ __forceinline__ uint16_t to_bf16(float x) { return __builtin_bit_cast
 // Raw storage of VW consecutive elements, loaded with one vector access.
 template <class IO, int VW> struct Raw;
 template <> struct Raw<F32, 4> { float4 v; };
+template <> struct Raw<F32, 2> { float2 v; };
 template <> struct Raw<F32, 1> { float v; };
 template <> struct Raw<BF16, 4> { uint2 v; };
+template <> struct Raw<BF16, 2> { uint32_t v; };
 template <> struct Raw<BF16, 1> { uint16_t v; };
 
 template <class IO, int VW> __device__ __forceinline__ Raw<IO, VW> raw_zero() {
@@ -49,11 +51,17 @@ template <class IO, int VW> __device__ __forceinline__ Raw<IO, VW> raw_load(cons
 template <> __device__ __forceinline__ Raw<F32, 4> raw_load<F32, 4>(const void* base, int64_t idx) {
   return {*reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx)};
 }
+template <> __device__ __forceinline__ Raw<F32, 2> raw_load<F32, 2>(const void* base, int64_t idx) {
+  return {*reinterpret_cast<const float2*>(static_cast<const float*>(base) + idx)};
+}
 template <> __device__ __forceinline__ Raw<F32, 1> raw_load<F32, 1>(const void* base, int64_t idx) {
   return {static_cast<const float*>(base)[idx]};
 }
 template <> __device__ __forceinline__ Raw<BF16, 4> raw_load<BF16, 4>(const void* base, int64_t idx) {
   return {*reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx)};
+}
+template <> __device__ __forceinline__ Raw<BF16, 2> raw_load<BF16, 2>(const void* base, int64_t idx) {
+  return {*reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(base) + idx)};
 }
 template <> __device__ __forceinline__ Raw<BF16, 1> raw_load<BF16, 1>(const void* base, int64_t idx) {
   return {static_cast<const uint16_t*>(base)[idx]};
@@ -63,9 +71,15 @@ template <class IO, int VW> __device__ __forceinline__ void unpack(const Raw<IO,
 template <> __device__ __forceinline__ void unpack<F32, 4>(const Raw<F32, 4>& r, float* o) {
   o[0] = r.v.x; o[1] = r.v.y; o[2] = r.v.z; o[3] = r.v.w;
 }
+template <> __device__ __forceinline__ void unpack<F32, 2>(const Raw<F32, 2>& r, float* o) {
+  o[0] = r.v.x; o[1] = r.v.y;
+}
 template <> __device__ __forceinline__ void unpack<F32, 1>(const Raw<F32, 1>& r, float* o) { o[0] = r.v; }
 template <> __device__ __forceinline__ void unpack<BF16, 4>(const Raw<BF16, 4>& r, float* o) {
   o[0] = bf16_lo(r.v.x); o[1] = bf16_hi(r.v.x); o[2] = bf16_lo(r.v.y); o[3] = bf16_hi(r.v.y);
+}
+template <> __device__ __forceinline__ void unpack<BF16, 2>(const Raw<BF16, 2>& r, float* o) {
+  o[0] = bf16_lo(r.v); o[1] = bf16_hi(r.v);
 }
 template <> __device__ __forceinline__ void unpack<BF16, 1>(const Raw<BF16, 1>& r, float* o) {
   o[0] = __uint_as_float(static_cast<uint32_t>(r.v) << 16);
@@ -75,6 +89,9 @@ template <class IO, int VW> __device__ __forceinline__ void store_vals(void* bas
 template <> __device__ __forceinline__ void store_vals<F32, 4>(void* base, int64_t idx, const float* v) {
   *reinterpret_cast<float4*>(static_cast<float*>(base) + idx) = make_float4(v[0], v[1], v[2], v[3]);
 }
+template <> __device__ __forceinline__ void store_vals<F32, 2>(void* base, int64_t idx, const float* v) {
+  *reinterpret_cast<float2*>(static_cast<float*>(base) + idx) = make_float2(v[0], v[1]);
+}
 template <> __device__ __forceinline__ void store_vals<F32, 1>(void* base, int64_t idx, const float* v) {
   static_cast<float*>(base)[idx] = v[0];
 }
@@ -82,46 +99,28 @@ template <> __device__ __forceinline__ void store_vals<BF16, 4>(void* base, int6
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) =
       make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
+template <> __device__ __forceinline__ void store_vals<BF16, 2>(void* base, int64_t idx, const float* v) {
+  *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(base) + idx) = pack_bf16x2(v[0], v[1]);
+}
 template <> __device__ __forceinline__ void store_vals<BF16, 1>(void* base, int64_t idx, const float* v) {
   static_cast<uint16_t*>(base)[idx] = to_bf16(v[0]);
 }
 
-// B_t and C_t rows are shared by every channel of a token, so within a
-// wavefront their addresses are uniform.  Reading them through the constant
-// address space lets the compiler use scalar (s_load) loads into SGPRs, which
-// the VALU then takes as operands directly.
+// Loads of wave-uniform fp32 data through the constant address space, so the
+// compiler issues scalar (s_load) loads into SGPRs, which the VALU then takes
+// as operands directly.
 typedef const __attribute__((address_space(4))) float* cfloat_p;
-typedef const __attribute__((address_space(4))) uint32_t* cu32_p;
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef const __attribute__((address_space(4))) f32x16_t* cf32x16_p;
 
-// NPL consecutive elements of a B/C row starting at flat index off (uniform).
-// bf16: off is even whenever NPL is even (dstate is even), so whole dwords are
-// read and split; NPL == 1 reads the enclosing dword and picks its half.
-template <int NPL> struct RowF32 {
-  static __device__ __forceinline__ void load(const void* base, int64_t off, float* v) {
-    cfloat_p p = (cfloat_p)(base);
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) v[j] = p[off + j];
-  }
-};
-template <int NPL> struct RowBF16 {
-  static __device__ __forceinline__ void load(const void* base, int64_t off, float* v) {
-    cu32_p p = (cu32_p)(base);
-    if constexpr (NPL == 1) {
-      const uint32_t w = p[off >> 1];
-      v[0] = (off & 1) ? bf16_hi(w) : bf16_lo(w);
-    } else {
-#pragma unroll
-      for (int k = 0; k < NPL / 2; ++k) {
-        const uint32_t w = p[(off >> 1) + k];
-        v[2 * k] = bf16_lo(w);
-        v[2 * k + 1] = bf16_hi(w);
-      }
-    }
-  }
-};
-template <class IO, int NPL> struct Row;
-template <int NPL> struct Row<F32, NPL> : RowF32<NPL> {};
-template <int NPL> struct Row<BF16, NPL> : RowBF16<NPL> {};
+// Element idx of a bf16 or fp32 tensor, widened to fp32.
+template <class IO> __device__ __forceinline__ float load_elem(const void* base, int64_t idx);
+template <> __device__ __forceinline__ float load_elem<F32>(const void* base, int64_t idx) {
+  return static_cast<const float*>(base)[idx];
+}
+template <> __device__ __forceinline__ float load_elem<BF16>(const void* base, int64_t idx) {
+  return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16);
+}
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).
 // log1p(e) uses a short series when e < 1/16 (relative error < 2e-7) and

@@ -28,14 +28,6 @@ struct DecodeParams {
   int softplus;
 };
 
-template <class IO> __device__ __forceinline__ float load_elem(const void* base, int64_t idx);
-template <> __device__ __forceinline__ float load_elem<F32>(const void* base, int64_t idx) {
-  return static_cast<const float*>(base)[idx];
-}
-template <> __device__ __forceinline__ float load_elem<BF16>(const void* base, int64_t idx) {
-  return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16);
-}
-
 // NQ lanes per channel (power of two, 4 * NQ >= N); VEC4: dstate % 4 == 0.
 template <class IO, int NQ, bool VEC4>
 __global__ void __launch_bounds__(256) state_update_kernel(DecodeParams p) {

@@ -1,35 +1,49 @@
 // scan_kernels.hpp -- gfx950 kernels of the selective scan forward pass.
 //
 // Work decomposition.  A workgroup owns 64 consecutive channels d of one batch
-// row and one chunk of the sequence.  It has G wavefronts; wavefront w owns
-// the states n in [w*NPL, (w+1)*NPL) of those 64 channels, one channel per
-// lane, so each lane runs NPL independent fp32 recurrences in registers and
-// B_t, C_t for its states are wave-uniform (scalar loads).
+// row (a "tile") and a stretch of the sequence.  It has G wavefronts;
+// wavefront w owns the states n in [w*NPL, (w+1)*NPL) of those 64 channels,
+// one channel per lane, so each lane runs NPL independent fp32 recurrences in
+// registers, and the B_t, C_t it needs are the same for the whole wavefront.
 //
-// Per block of TB tokens the workgroup
-//   1. (prologue, all threads) loads u, delta_raw, z for TB x 64 tokens x
-//      channels with coalesced vector loads, computes delta = softplus(raw +
-//      bias) and delta*u once per (token, channel) and stages them in LDS;
-//   2. (scan, each wavefront) walks the TB tokens: for every state
-//      a = exp2(delta * A*log2 e), h = a*h + (delta*u)*B_t[n], and the partial
-//      readout y_w = sum over its states of C_t[n]*h -- the pair (a, b) of the
-//      fade-and-add step never leaves registers;
-//   3. (epilogue, all threads) sums the G partial readouts in a fixed order,
-//      adds D*u, multiplies by SiLU(z), rounds and stores y.
-// Loads of the next block are issued before the scan of the current one.
+// B and C are first packed (pack_bc_kernel) into fp32 records per state group,
+//   bc[b][g][t][0 .. NPL)       = B_t[g*NPL .. g*NPL+NPL)
+//   bc[b][g][t][NPL .. 2*NPL)   = C_t[g*NPL .. g*NPL+NPL)
+// (states beyond dstate are zero), so a wavefront fetches the B_t/C_t of
+// several tokens with one 64-byte scalar load and uses them as SGPR operands,
+// with no per-token conversion work.
 //
-// Long sequences are cut into K chunks ("Mamba is attention all you really
-// need, part 2", "The relay": squash each chunk into one fade-and-add pair,
-// combine the chunk pairs, pass the real states back):
-//   chunk_agg   (FULL = false) scans chunks 0..K-2 from a zero state and
-//               writes each chunk's pair (P, S) per (b, d, n): S is the state
-//               the chunk reaches from zero, P = exp(A * sum of its deltas)
-//               its total fade;
-//   carry       composes the pairs in order and writes the state entering
-//               every chunk;
-//   scan (FULL = true) rescans every chunk from its carried-in state and
-//               produces y and the final state.
+// The sequence is processed in blocks of TB tokens, software-pipelined over
+// three blocks with double-buffered LDS and one barrier per block: while the
+// wavefronts scan block k they also
+//   - (epilogue of block k-1) sum the G partial readouts of each (token,
+//     channel) in a fixed order, add D*u, multiply by SiLU(z), round, store y;
+//   - (prologue of block k+1) turn the u, delta_raw, z loaded two blocks
+//     earlier (coalesced vector loads) into delta = softplus(raw + bias) and
+//     delta*u, once per (token, channel), staged in LDS.
+// The scan of block k walks its TB tokens: for every state
+// a = exp2(delta * A*log2 e), h = a*h + (delta*u)*B_t[n], and the partial
+// readout y_w = sum over its states of C_t[n]*h -- the fade-and-add pair
+// (a, b) of each step never leaves registers.  The packed B/C records and the
+// staged (delta, delta*u) of the next group of tokens are fetched while the
+// current group is computed.
+//
+// Tiles are either scanned whole by one workgroup ("long" tiles) or, when
+// there are too few tiles to fill the GPU evenly, cut into Ks chunks of the
+// sequence ("Mamba is attention all you really need, part 2", "The relay":
+// squash each chunk into one fade-and-add pair, combine the chunk pairs, pass
+// the real states back):
+//   aggregate (FULL = false) scans chunks 0..Ks-2 of every split tile from a
+//             zero state and writes each chunk's pair (P, S) per (d, n): S is
+//             the state the chunk reaches from zero, P = exp(A * sum of its
+//             deltas) its total fade;
+//   carry     composes the pairs in order and writes the state entering every
+//             chunk;
+//   scan (FULL = true) runs the long tiles whole and every chunk of the split
+//             tiles from its carried-in state, producing y and the final state.
 #pragma once
+
+#include <utility>
 
 #include "common.hpp"
 
@@ -39,80 +53,121 @@ struct ScanParams {
   const void* u;
   const void* delta;
   const float* A;
-  const void* B;
-  const void* C;
   const float* D;      // nullable
   const void* z;       // nullable
   const float* bias;   // nullable
+  const float* bc;     // packed B/C records [batch][G][Lp][2*NPL]
   void* y;
   float* final_state;  // nullable
-  float* aggP;         // [batch][K][dim][N]  (K > 1 only)
-  float* aggS;         // [batch][K][dim][N]
-  float* carry;        // [batch][K][dim][N]  state entering chunk c (c >= 1)
-  int64_t batch, L, dim, N;
-  int64_t chunk_len;
-  int K;
+  // Chunk pairs and carried-in states of the split tiles: [n_split][Ks][64][Npad].
+  float* aggP;
+  float* aggS;
+  float* carry;
+  int64_t batch, L, Lp, dim, N;
+  int64_t chunk_len;   // tokens per chunk of a split tile
+  int ntd;             // 64-channel tiles per batch row
+  int n_long;          // tiles 0 .. n_long-1 are scanned whole
+  int Ks;              // chunks per split tile (tiles n_long .. T-1)
   int softplus;
 };
 
-// Tokens per staged block for a (G, VW) variant: 16 or G*VW, whichever is larger.
+// Tokens per staged block (every variant), and the prologue layout: a thread
+// handles VW consecutive channels of RPT token rows.
+constexpr int kTB = 16;
 template <int G, int VW> struct BlockShape {
-  static constexpr int TB = (G * VW > 16) ? G * VW : 16;
-  static constexpr int RPT = TB / (G * VW);  // rows handled by each prologue thread
+  static constexpr int TB = kTB;
+  static_assert(G * VW <= kTB, "a block row must fit the prologue threads");
+  static constexpr int RPT = TB / (G * VW);
+};
+constexpr int kMaxTB = kTB;  // packed B/C rows are padded to a multiple of this
+
+// Tokens per group: one group's packed B/C records are 16 floats (32 for NPL 16).
+template <int NPL> struct GroupShape {
+  static constexpr int SUB = (NPL >= 8) ? 1 : 8 / NPL;
+  static constexpr int FLOATS = SUB * 2 * NPL;
+  static constexpr int VEC16 = FLOATS / 16;
+  static_assert(FLOATS % 16 == 0, "group records are whole 16-float loads");
 };
 
-// B_t / C_t of this wavefront's states n0 .. n0+NPL-1 for one token row
-// (flat offset rowoff = row * N).  EXACT (NPL * G == N): the states split
-// evenly over the wavefronts and no masking is needed.  Otherwise states
-// n >= N read a clamped, in-bounds element and are set to zero (their A is
-// zero too, so they stay at zero and add nothing to the readout).
-template <class IO, int NPL, bool EXACT>
-__device__ __forceinline__ void load_bc(const void* base, int64_t rowoff, int n0, int64_t N, float* v) {
-  if constexpr (EXACT) {
-    Row<IO, NPL>::load(base, rowoff + n0, v);
-  } else {
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int64_t n = n0 + j;
-      float x[1];
-      Row<IO, 1>::load(base, rowoff + (n < N ? n : N - 1), x);
-      v[j] = n < N ? x[0] : 0.0f;
-    }
-  }
+template <int I> struct IC { static constexpr int value = I; };
+
+// Token blocks of u, delta_raw, z loaded ahead of the block being scanned
+// (ring of register buffers).  The scattered 128-byte rows of a tile need a
+// deep prefetch to cover HBM latency.
+#ifndef SSM_PREFETCH_BLOCKS
+#define SSM_PREFETCH_BLOCKS 4
+#endif
+constexpr int kPD = SSM_PREFETCH_BLOCKS;
+static_assert(kPD == 2 || kPD == 4 || kPD == 8, "prefetch ring is 2, 4 or 8 blocks");
+
+// lgkmcnt(0) with vmcnt and expcnt left at their maxima (gfx9 encoding).
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Pack B and C ([batch][L][N], fp32 or bf16) into fp32 per-group records
+// [batch][G][Lp][2*NPL]; states n >= N and tokens t >= L are zero.
+template <class IO>
+__global__ void __launch_bounds__(256) pack_bc_kernel(const void* __restrict__ B, const void* __restrict__ C,
+                                                     float* __restrict__ bc, int64_t batch, int64_t L, int64_t Lp,
+                                                     int64_t N, int npl, int G) {
+  const int64_t Npad = static_cast<int64_t>(npl) * G;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= batch * Lp * Npad) return;
+  const int64_t n = i % Npad;
+  const int64_t t = (i / Npad) % Lp;
+  const int64_t b = i / (Npad * Lp);
+  const bool ok = t < L && n < N;
+  const float vb = ok ? load_elem<IO>(B, (b * L + t) * N + n) : 0.0f;
+  const float vc = ok ? load_elem<IO>(C, (b * L + t) * N + n) : 0.0f;
+  const int64_t g = n / npl, j = n % npl;
+  const int64_t o = ((b * G + g) * Lp + t) * (2 * npl);
+  bc[o + j] = vb;
+  bc[o + npl + j] = vc;
 }
 
-// Tokens whose B/C words a wavefront preloads into SGPRs at once (about 32
-// SGPRs for B and C together).
-template <class IO, int NPL> struct Preload {
-  static constexpr int WORDS = __is_same(IO, BF16) ? (NPL >= 2 ? NPL / 2 : 1) : NPL;  // dwords per token
-  static constexpr int SUB = (16 / WORDS) > 0 ? 16 / WORDS : 1;
-};
-
-// NT: dstate as a compile-time constant when the states split evenly
-// (NT = NPL * G), or 0 when it is only known at run time.
-template <class IO, int NPL, int G, int VW, bool FULL, int NT>
+template <class IO, int NPL, int G, int VW, bool FULL>
 __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
-  constexpr bool EXACT = NT > 0;
-  static_assert(NT == 0 || NT == NPL * G, "compile-time dstate must equal NPL * G");
+  constexpr int NPAD = NPL * G;
   constexpr int TB = BlockShape<G, VW>::TB;
   constexpr int RPT = BlockShape<G, VW>::RPT;
   constexpr int RPR = 64 / VW;              // prologue threads per token row
   constexpr int ROWSTEP = (64 * G) / RPR;   // rows between one thread's runs
   static_assert(TB == RPT * ROWSTEP, "block shape");
+  using GS = GroupShape<NPL>;
+  constexpr int SUB = GS::SUB, NG = TB / SUB;
+  static_assert(TB % (2 * SUB) == 0, "groups come in pairs (double-buffered)");
 
-  __shared__ float2 sDU[TB][64];                 // (delta, delta*u) per token, channel
-  __shared__ float sY[FULL ? G : 1][TB][64];     // partial readouts per wavefront
+  // Double-buffered by block parity.
+  __shared__ float2 sDU[2][TB][64];                            // (delta, delta*u) per token, channel
+  __shared__ float sY[FULL ? 2 : 1][FULL ? G : 1][TB][64];     // partial readouts per wavefront
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t b = blockIdx.y;
-  const int c = blockIdx.z;
-  const int64_t dim = p.dim, L = p.L;
-  const int64_t N = EXACT ? static_cast<int64_t>(NT) : p.N;
-  const int64_t d0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int64_t t_begin = static_cast<int64_t>(c) * p.chunk_len;
-  const int64_t t_end = (t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L;
+  const int64_t dim = p.dim, L = p.L, N = p.N;
+
+  // ---- which tile and which part of the sequence this workgroup scans
+  const int bid = blockIdx.x;
+  int tile, c, st;
+  bool split;
+  if (FULL && bid < p.n_long) {
+    tile = bid;
+    c = 0;
+    st = 0;
+    split = false;
+  } else {
+    const int per = FULL ? p.Ks : p.Ks - 1;
+    const int j = FULL ? bid - p.n_long : bid;
+    st = j / per;
+    c = j % per;
+    tile = p.n_long + st;
+    split = true;
+  }
+  const int64_t b = tile / p.ntd;
+  const int64_t d0 = static_cast<int64_t>(tile % p.ntd) * 64;
+  const int64_t t_begin = split ? static_cast<int64_t>(c) * p.chunk_len : 0;
+  const int64_t t_end = split ? ((t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L) : L;
+  const int64_t pair_row = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;   // row of [n_split][Ks][64]
+  const int nblocks = static_cast<int>((t_end - t_begin + TB - 1) / TB);
 
   // ---- scan lane: channel d, states n0 .. n0+NPL-1
   const int64_t d = d0 + lane;
@@ -122,12 +177,14 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int n = n0 + j;
-    const bool ok = dvalid && n < N;
-    A2[j] = ok ? p.A[d * N + n] * kLog2e : 0.0f;
+    A2[j] = (dvalid && n < N) ? p.A[d * N + n] * kLog2e : 0.0f;
     h[j] = 0.0f;
-    if (FULL && c > 0 && ok) h[j] = p.carry[((b * p.K + c) * dim + d) * N + n];
+    if (FULL && split && c > 0 && dvalid) h[j] = p.carry[pair_row * NPAD + n];
   }
   float delta_total = 0.0f;  // chunk sum of delta (aggregate pass), summed per block then per chunk
+
+  // packed B/C records of this wavefront's state group
+  const float* bc_row = p.bc + (b * G + w) * p.Lp * (2 * NPL);
 
   // ---- prologue / epilogue thread: channels pd .. pd+VW-1, rows prow + i*ROWSTEP
   const int pcol = (tid % RPR) * VW;
@@ -142,27 +199,66 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   }
   const bool has_z = FULL && p.z != nullptr;
 
-  Raw<IO, VW> ru[RPT], rd[RPT], rz[RPT];  // loads for the block about to be staged
-  Raw<IO, VW> eu[RPT], ez[RPT];           // u, z of the block awaiting its epilogue
+  // Raw loads of u, delta_raw, z in a ring of kPD blocks (slot = block % kPD),
+  // and u, z kept for the epilogue by block parity.
+  Raw<IO, VW> ru[kPD][RPT], rd[kPD][RPT], rz[kPD][RPT];
+  Raw<IO, VW> eu[2][RPT], ez[2][RPT];
 
-  auto issue_loads = [&](int64_t t0) {
+  auto issue_loads = [&](auto slotc, int64_t t0) {
+    constexpr int S = decltype(slotc)::value;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int64_t t = t0 + prow + i * ROWSTEP;
       if (pvalid && t < t_end) {
         const int64_t idx = (b * L + t) * dim + pd;
-        ru[i] = raw_load<IO, VW>(p.u, idx);
-        rd[i] = raw_load<IO, VW>(p.delta, idx);
-        rz[i] = has_z ? raw_load<IO, VW>(p.z, idx) : raw_zero<IO, VW>();
+        ru[S][i] = raw_load<IO, VW>(p.u, idx);
+        rd[S][i] = raw_load<IO, VW>(p.delta, idx);
+        rz[S][i] = has_z ? raw_load<IO, VW>(p.z, idx) : raw_zero<IO, VW>();
       } else {
-        ru[i] = raw_zero<IO, VW>();
-        rd[i] = raw_zero<IO, VW>();
-        rz[i] = raw_zero<IO, VW>();
+        ru[S][i] = raw_zero<IO, VW>();
+        rd[S][i] = raw_zero<IO, VW>();
+        rz[S][i] = raw_zero<IO, VW>();
       }
     }
   };
 
-  auto epilogue = [&](int64_t t0) {
+  // Stage (delta, delta*u) of the block with parity P held in ring slot S.
+  auto prologue = [&](auto parc, auto slotc) {
+    constexpr int P = decltype(parc)::value;
+    constexpr int S = decltype(slotc)::value;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = prow + i * ROWSTEP;
+      float uf[VW], df[VW];
+      unpack<IO, VW>(ru[S][i], uf);
+      unpack<IO, VW>(rd[S][i], df);
+      float2 out[VW];
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+        const float x = df[e] + biasv[e];
+        const float dl = p.softplus ? softplus_f(x) : x;
+        out[e] = make_float2(dl, dl * uf[e]);
+      }
+      if constexpr (VW == 4) {
+        float4* dst = reinterpret_cast<float4*>(&sDU[P][row][pcol]);
+        dst[0] = make_float4(out[0].x, out[0].y, out[1].x, out[1].y);
+        dst[1] = make_float4(out[2].x, out[2].y, out[3].x, out[3].y);
+      } else if constexpr (VW == 2) {
+        *reinterpret_cast<float4*>(&sDU[P][row][pcol]) = make_float4(out[0].x, out[0].y, out[1].x, out[1].y);
+      } else {
+        sDU[P][row][pcol] = out[0];
+      }
+      if (FULL) {
+        eu[P][i] = ru[S][i];
+        ez[P][i] = rz[S][i];
+      }
+    }
+  };
+
+  // Finish the block with parity P that starts at token t0.
+  auto epilogue = [&](auto parc, int64_t t0) {
+    constexpr int P = FULL ? decltype(parc)::value : 0;
+    if constexpr (FULL) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = prow + i * ROWSTEP;
@@ -174,15 +270,18 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 #pragma unroll
       for (int ww = 0; ww < G; ++ww) {
         if constexpr (VW == 4) {
-          const float4 v = *reinterpret_cast<const float4*>(&sY[ww][row][pcol]);
+          const float4 v = *reinterpret_cast<const float4*>(&sY[P][ww][row][pcol]);
           ys[0] += v.x; ys[1] += v.y; ys[2] += v.z; ys[3] += v.w;
+        } else if constexpr (VW == 2) {
+          const float2 v = *reinterpret_cast<const float2*>(&sY[P][ww][row][pcol]);
+          ys[0] += v.x; ys[1] += v.y;
         } else {
-          ys[0] += sY[ww][row][pcol];
+          ys[0] += sY[P][ww][row][pcol];
         }
       }
       float uf[VW], zf[VW], out[VW];
-      unpack<IO, VW>(eu[i], uf);
-      if (has_z) unpack<IO, VW>(ez[i], zf);
+      unpack<IO, VW>(eu[P][i], uf);
+      if (has_z) unpack<IO, VW>(ez[P][i], zf);
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
         float v = __builtin_fmaf(Dv[e], uf[e], ys[e]);
@@ -191,149 +290,152 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       }
       store_vals<IO, VW>(p.y, (b * L + t) * dim + pd, out);
     }
+    }
   };
 
-  issue_loads(t_begin);
-  int64_t t_prev = -1;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += TB) {
-    const int nt = static_cast<int>((t_end - t0 < TB) ? (t_end - t0) : TB);
-    if (FULL && t_prev >= 0) epilogue(t_prev);
-
-    // prologue: stage (delta, delta*u) for this block
+  // One state update for a token: r points at the token's packed record (B then C).
+  auto update = [&](auto parc, const float2 dd, const float* r, int tt, float& block_delta) {
+    constexpr int P = decltype(parc)::value;
+    float yp = 0.0f;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int row = prow + i * ROWSTEP;
-      float uf[VW], df[VW];
-      unpack<IO, VW>(ru[i], uf);
-      unpack<IO, VW>(rd[i], df);
-      float2 out[VW];
-#pragma unroll
-      for (int e = 0; e < VW; ++e) {
-        const float x = df[e] + biasv[e];
-        const float dl = p.softplus ? softplus_f(x) : x;
-        out[e] = make_float2(dl, dl * uf[e]);
-      }
-      if constexpr (VW == 4) {
-        float4* dst = reinterpret_cast<float4*>(&sDU[row][pcol]);
-        dst[0] = make_float4(out[0].x, out[0].y, out[1].x, out[1].y);
-        dst[1] = make_float4(out[2].x, out[2].y, out[3].x, out[3].y);
-      } else {
-        sDU[row][pcol] = out[0];
-      }
-      if (FULL) {
-        eu[i] = ru[i];
-        ez[i] = rz[i];
-      }
+    for (int j = 0; j < NPL; ++j) {
+      const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
+      h[j] = __builtin_fmaf(a, h[j], dd.y * r[j]);
+      if (FULL) yp = __builtin_fmaf(r[NPL + j], h[j], yp);
     }
-    issue_loads(t0 + TB);
-    __syncthreads();
+    if (FULL) sY[FULL ? P : 0][w][tt][lane] = yp;
+    else block_delta += dd.x;
+  };
 
-    // scan: TB tokens for this wavefront's states
-    const int64_t row0 = b * L + t0;
+  // Double-buffered group state: packed records (SGPRs) and staged (delta, delta*u).
+  float rec[2][GS::FLOATS];
+  float2 dd[2][SUB];
+
+  auto fetch_records = [&](auto bufc, int64_t t) {  // t: first token of the group
+    constexpr int BUF = decltype(bufc)::value;
+    cf32x16_p src = (cf32x16_p)(bc_row + t * (2 * NPL));
+#pragma unroll
+    for (int v = 0; v < GS::VEC16; ++v) {
+      const f32x16_t x = src[v];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) rec[BUF][16 * v + k] = x[k];
+    }
+  };
+  auto fetch_dd = [&](auto parc, auto bufc, int g) {
+    constexpr int P = decltype(parc)::value;
+    constexpr int BUF = decltype(bufc)::value;
+#pragma unroll
+    for (int q = 0; q < SUB; ++q) dd[BUF][q] = sDU[P][g * SUB + q][lane];
+  };
+
+  // Group g of the block with parity P from buffer BUF; the next group's
+  // records and (delta, delta*u) are fetched into the other buffer while this
+  // one computes.
+  auto group = [&](auto parc, auto bufc, int g, int64_t t0, float& block_delta) {
+    constexpr int BUF = decltype(bufc)::value;
+    // This group's records and staged values (issued one group earlier) are
+    // complete here; the next group's loads are issued only after this wait,
+    // so they stay in flight while this group computes.
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g + 1 < NG) {
+      fetch_records(IC<1 - BUF>{}, t0 + (g + 1) * SUB);
+      fetch_dd(parc, IC<1 - BUF>{}, g + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < SUB; ++q) update(parc, dd[BUF][q], &rec[BUF][q * 2 * NPL], g * SUB + q, block_delta);
+  };
+
+  // Block k (parity P = k % 2, ring slot S = k % kPD, first token t0):
+  // epilogue of k-1, prologue of k+1, loads of k+kPD, scan of k.
+  auto iteration = [&](auto slotc, int k, int64_t t0) {
+    constexpr int S = decltype(slotc)::value;
+    constexpr int P = S & 1;
+    constexpr int S1 = (S + 1) % kPD;  // ring slot of block k+1
+    IC<P> parc;
+    const int nt = static_cast<int>((t_end - t0 < TB) ? (t_end - t0) : TB);
+    const bool full_block = nt == TB;
+    if (full_block) {
+      fetch_records(IC<0>{}, t0);
+      fetch_dd(parc, IC<0>{}, 0);
+    }
+    if constexpr (FULL) {
+      if (k >= 1) epilogue(IC<1 - P>{}, t0 - TB);
+    }
+    if (k + 1 < nblocks) {
+      prologue(IC<1 - P>{}, IC<S1>{});
+      issue_loads(IC<S1>{}, t0 + (kPD + 1) * TB);
+    }
     float block_delta = 0.0f;
-    auto step = [&](int tt) {
-      const float2 dd = sDU[tt][lane];
-      const int64_t rowoff = (row0 + tt) * N;
-      float Bv[NPL], Cv[NPL];
-      load_bc<IO, NPL, EXACT>(p.B, rowoff, n0, N, Bv);
-      if (FULL) load_bc<IO, NPL, EXACT>(p.C, rowoff, n0, N, Cv);
-      float yp = 0.0f;
+    if (full_block) {
 #pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
-        h[j] = __builtin_fmaf(a, h[j], dd.y * Bv[j]);
-        if (FULL) yp = __builtin_fmaf(Cv[j], h[j], yp);
-      }
-      if (FULL) sY[w][tt][lane] = yp;
-      else block_delta += dd.x;
-    };
-    if (EXACT && nt == TB) {
-      // Full block: issue the scalar loads of SUB tokens' B/C words back to back,
-      // then run those tokens, so the scalar-load latency is paid once per SUB.
-      constexpr int SUB = Preload<IO, NPL>::SUB;
-      constexpr int WORDS = Preload<IO, NPL>::WORDS;
-      static_assert(TB % SUB == 0, "sub-block");
-      cu32_p Bp = (cu32_p)(p.B);
-      cu32_p Cp = (cu32_p)(p.C);
-      constexpr int ES = __is_same(IO, BF16) ? 2 : 1;   // elements per dword
-#pragma unroll
-      for (int s0 = 0; s0 < TB; s0 += SUB) {
-        uint32_t bw[SUB][WORDS], cw[SUB][WORDS];
-        const int64_t wbase = ((row0 + s0) * N + n0) / ES;   // dword index of token s0, state n0
-#pragma unroll
-        for (int q = 0; q < SUB; ++q) {
-#pragma unroll
-          for (int k = 0; k < WORDS; ++k) {
-            bw[q][k] = Bp[wbase + (q * N) / ES + k];
-            if (FULL) cw[q][k] = Cp[wbase + (q * N) / ES + k];
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < SUB; ++q) {
-          const int tt = s0 + q;
-          const float2 dd = sDU[tt][lane];
-          float Bv[NPL], Cv[NPL];
-#pragma unroll
-          for (int j = 0; j < NPL; ++j) {
-            if constexpr (__is_same(IO, BF16)) {
-              if constexpr (NPL == 1) {
-                Bv[j] = (n0 & 1) ? bf16_hi(bw[q][0]) : bf16_lo(bw[q][0]);
-                Cv[j] = FULL ? ((n0 & 1) ? bf16_hi(cw[q][0]) : bf16_lo(cw[q][0])) : 0.0f;
-              } else {
-                Bv[j] = (j & 1) ? bf16_hi(bw[q][j / 2]) : bf16_lo(bw[q][j / 2]);
-                Cv[j] = FULL ? ((j & 1) ? bf16_hi(cw[q][j / 2]) : bf16_lo(cw[q][j / 2])) : 0.0f;
-              }
-            } else {
-              Bv[j] = __uint_as_float(bw[q][j]);
-              Cv[j] = FULL ? __uint_as_float(cw[q][j]) : 0.0f;
-            }
-          }
-          float yp = 0.0f;
-#pragma unroll
-          for (int j = 0; j < NPL; ++j) {
-            const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
-            h[j] = __builtin_fmaf(a, h[j], dd.y * Bv[j]);
-            if (FULL) yp = __builtin_fmaf(Cv[j], h[j], yp);
-          }
-          if (FULL) sY[w][tt][lane] = yp;
-          else block_delta += dd.x;
-        }
+      for (int g = 0; g < NG; g += 2) {
+        group(parc, IC<0>{}, g, t0, block_delta);
+        group(parc, IC<1>{}, g + 1, t0, block_delta);
       }
     } else {
-      for (int tt = 0; tt < nt; ++tt) step(tt);
+      for (int tt = 0; tt < nt; ++tt) {
+        float r[2 * NPL];
+        cfloat_p src = (cfloat_p)(bc_row + (t0 + tt) * (2 * NPL));
+#pragma unroll
+        for (int kk = 0; kk < 2 * NPL; ++kk) r[kk] = src[kk];
+        update(parc, sDU[P][tt][lane], r, tt, block_delta);
+      }
     }
     delta_total += block_delta;
     __syncthreads();
-    t_prev = t0;
-  }
-  if (FULL && t_prev >= 0) epilogue(t_prev);
+  };
 
+  // fill the ring, stage block 0, reuse its slot for block kPD
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (issue_loads(IC<I>{}, t_begin + static_cast<int64_t>(I) * TB), ...);
+  }(std::make_integer_sequence<int, kPD>{});
+  prologue(IC<0>{}, IC<0>{});
+  issue_loads(IC<0>{}, t_begin + static_cast<int64_t>(kPD) * TB);
+  __syncthreads();
+  for (int k = 0; k < nblocks; k += kPD) {
+    bool done = false;
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((done = done || (k + I >= nblocks), done ? void() : iteration(IC<I>{}, k + I, t_begin + static_cast<int64_t>(k + I) * TB)), ...);
+    }(std::make_integer_sequence<int, kPD>{});
+  }
+  if constexpr (FULL) {
+    const int64_t t_last = t_begin + static_cast<int64_t>(nblocks - 1) * TB;
+    if ((nblocks - 1) & 1)
+      epilogue(IC<1>{}, t_last);
+    else
+      epilogue(IC<0>{}, t_last);
+  }
+
+  if (!dvalid) return;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int n = n0 + j;
-    if (!(dvalid && n < N)) continue;
     if (FULL) {
-      if (c == p.K - 1 && p.final_state) p.final_state[(b * dim + d) * N + n] = h[j];
+      if ((!split || c == p.Ks - 1) && p.final_state && n < N) p.final_state[(b * dim + d) * N + n] = h[j];
     } else {
-      const int64_t idx = ((b * p.K + c) * dim + d) * N + n;
+      const int64_t idx = pair_row * NPAD + n;
       p.aggS[idx] = h[j];
       p.aggP[idx] = __builtin_amdgcn_exp2f(A2[j] * delta_total);
     }
   }
 }
 
-// State entering each chunk: carry_{c+1} = P_c * carry_c + S_c, carry_0 = 0.
-// One thread per (b, d, n); the chunk pairs are composed in order.
+// State entering each chunk of a split tile: carry_{c+1} = P_c * carry_c + S_c,
+// carry_0 = 0.  One thread per (split tile, lane channel, state); the chunk
+// pairs are composed in order.  Layout [n_split][Ks][64][Npad].
 __global__ void __launch_bounds__(256) carry_kernel(const float* __restrict__ P, const float* __restrict__ S,
-                                                   float* __restrict__ carry, int64_t batch, int K, int64_t DN) {
+                                                   float* __restrict__ carry, int64_t n_split, int Ks, int64_t Npad) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= batch * DN) return;
-  const int64_t b = i / DN, r = i % DN;
+  const int64_t per_tile = 64 * Npad;
+  if (i >= n_split * per_tile) return;
+  const int64_t st = i / per_tile, r = i % per_tile;
   float h = 0.0f;
-  for (int cc = 0; cc + 1 < K; ++cc) {
-    const int64_t idx = (b * K + cc) * DN + r;
+  for (int cc = 0; cc + 1 < Ks; ++cc) {
+    const int64_t idx = (st * Ks + cc) * per_tile + r;
     h = __builtin_fmaf(P[idx], h, S[idx]);
-    carry[idx + DN] = h;
+    carry[idx + per_tile] = h;
   }
 }
 

@@ -2,9 +2,10 @@
 //
 // Entry points are declared (with their contracts) in include/ssm_scan.h.
 // This file validates arguments before any HIP call, plans the launch
-// (states per lane, wavefronts per workgroup, number of sequence chunks) and
-// enqueues the kernels of scan_kernels.hpp / decode_kernel.hpp on the
-// caller's stream.  It allocates nothing and keeps no state.
+// (states per lane, wavefronts per workgroup, which tiles are cut into
+// sequence chunks) and enqueues the kernels of scan_kernels.hpp and
+// decode_kernel.hpp on the caller's stream.  It allocates nothing and keeps
+// no state.
 #include "ssm_scan.h"
 
 #include <hip/hip_runtime.h>
@@ -18,18 +19,11 @@
 namespace ssm {
 namespace {
 
-constexpr int64_t kMaxGrid = 65535;  // limit for grid.y (batch) and grid.z (chunks)
-constexpr int64_t kChunkQuantum = 32; // chunk lengths are multiples of the largest token block
-constexpr int64_t kMinChunk = 256;    // never cut the sequence finer than this
-constexpr int kTargetWaves = 2048;    // aim for ~2 wavefronts per SIMD (256 CUs x 4 SIMDs)
-
-struct Plan {
-  int npl;       // states per lane
-  int G;         // wavefronts per workgroup (state groups)
-  int K;         // sequence chunks
-  int64_t chunk_len;
-  size_t ws_bytes;
-};
+constexpr int64_t kMaxBatch = 65535;
+constexpr int64_t kChunkQuantum = kMaxTB; // chunk lengths are multiples of the largest token block
+constexpr int64_t kMinChunk = 256;        // never cut the sequence finer than this
+constexpr int64_t kNumCU = 256;           // MI355X compute units: the work is balanced over these
+constexpr int64_t kMaxChunks = 4096;      // chunks per split tile
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -41,7 +35,36 @@ int next_pow2(int64_t x) {
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Plan {
+  int vw;        // channels per prologue/epilogue thread (vector width of the token-row accesses)
+  int npl;       // states per lane
+  int G;         // wavefronts per workgroup (state groups); npl * G >= dstate
+  int ntd;       // 64-channel tiles per batch row
+  int n_long;    // tiles scanned whole
+  int n_split;   // tiles cut into Ks chunks
+  int Ks;        // chunks per split tile
+  int64_t chunk_len;
+  int64_t Lp;    // sequence length rounded up to whole token blocks (packed B/C rows)
+};
+
+// Workspace layout: [packed B/C][chunk fades P][chunk states S][carried-in states].
+struct Layout {
+  size_t bc, agg, total;
+};
+
+Layout layout_for(const Plan& pl, int64_t batch) {
+  const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
+  Layout l;
+  l.bc = align256(static_cast<size_t>(batch) * pl.Lp * 2 * npad * sizeof(float));
+  l.agg = pl.n_split > 0 ? align256(static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float)) : 0;
+  l.total = l.bc + 3 * l.agg;
+  return l;
+}
+
 // Optional override for tuning experiments: SSM_SCAN_VARIANT="npl,G[,K]".
+// K > 0 cuts every tile into K chunks; K = 0 (or absent) keeps the planner's split.
 bool env_variant(int* npl, int* G, int* K) {
   const char* s = getenv("SSM_SCAN_VARIANT");
   if (!s || !*s) return false;
@@ -54,20 +77,42 @@ bool env_variant(int* npl, int* G, int* K) {
   return true;
 }
 
+// Kernel variants (states per lane, wavefronts).  Each exists with its
+// preferred prologue width (channels per thread: 4 up to 4 wavefronts, 2 for
+// 8, 1 for 16) and with width 1.
 bool variant_exists(int npl, int G) {
   if (npl == 4 && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16)) return true;
-  if ((npl == 2 && G == 8) || (npl == 1 && G == 16) || (npl == 8 && G == 2) || (npl == 16 && G == 1)) return true;
-  return false;
+  return (npl == 2 && G == 8) || (npl == 1 && G == 16) || (npl == 8 && G == 2) || (npl == 16 && G == 1);
+}
+int preferred_vw(int G) { return G <= 4 ? 4 : (G == 8 ? 2 : 1); }
+
+// The generic variant for a state size: 4 states per lane, a power of two of wavefronts.
+void generic_variant(int64_t N, int* npl, int* G) {
+  *npl = 4;
+  *G = next_pow2(ceil_div(N, 4));
 }
 
-void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, Plan* pl) {
+// Work plan.  A tile (64 channels of one batch row) scanned whole costs one
+// pass over L tokens; cutting it into chunks adds an aggregate pass over all
+// but its last chunk (about three quarters of the cost per token), so tiles
+// are only cut where the GPU would otherwise run unevenly:
+//   - at least one tile per CU: the largest multiple of the CU count runs
+//     whole; the remaining r tiles (if any) are cut into ~CU/r chunks each;
+//   - fewer tiles than CUs: tiles run whole if they cover at least 3/4 of the
+//     CUs, otherwise every tile is cut so that each CU gets ~2 chunks.
+// vw_ok: the widest token-row access the pointers and dim allow (4, 2 or 1);
+// it decides the prologue width, not the split.
+void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int vw_ok, Plan* pl) {
   int npl, G, Kreq = 0;
+  const int64_t tiles = batch * ceil_div(dim, 64);
   if (N == 16) {
-    npl = 2;
-    G = 8;
+    // Many tiles: one state per lane over 16 wavefronts (4 per SIMD from one
+    // workgroup).  Few tiles (long sequences cut into many chunks): 8 states per
+    // lane over 2 wavefronts, which reads B_t/C_t for more work per scalar load.
+    npl = tiles * 4 >= kNumCU ? 1 : 8;
+    G = 16 / npl;
   } else {
-    npl = 4;
-    G = next_pow2(ceil_div(N, 4));
+    generic_variant(N, &npl, &G);
   }
   int enpl, eG, eK;
   if (env_variant(&enpl, &eG, &eK) && variant_exists(enpl, eG) && static_cast<int64_t>(enpl) * eG >= N) {
@@ -75,25 +120,41 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, Plan* pl) {
     G = eG;
     Kreq = eK;
   }
-  const int64_t tiles = batch * ceil_div(dim, 64);
-  int64_t K = Kreq > 0 ? Kreq : ceil_div(kTargetWaves, tiles * G);
-  const int64_t kmax = ceil_div(L, kMinChunk);
-  if (Kreq <= 0 && K > kmax) K = kmax;
+  const int vw = preferred_vw(G) <= vw_ok ? preferred_vw(G) : 1;
+  const int64_t ntd = ceil_div(dim, 64);
+  const int64_t T = batch * ntd;
+  const int64_t kmax = ceil_div(L, kMinChunk) < kMaxChunks ? ceil_div(L, kMinChunk) : kMaxChunks;
+  int64_t n_long, K;
+  if (Kreq > 0) {
+    K = Kreq;
+    n_long = 0;
+  } else if (T >= kNumCU) {
+    n_long = (T / kNumCU) * kNumCU;
+    const int64_t r = T - n_long;
+    K = r ? (kNumCU + r / 2) / r : 1;
+    if (K > kmax) K = kmax;
+  } else if (4 * T >= 3 * kNumCU) {
+    n_long = T;
+    K = 1;
+  } else {
+    n_long = 0;
+    K = ceil_div(2 * kNumCU, T);
+    if (K > kmax) K = kmax;
+  }
   if (K < 1) K = 1;
   int64_t chunk = ceil_div(ceil_div(L, K), kChunkQuantum) * kChunkQuantum;
   K = ceil_div(L, chunk);
+  if (K == 1) n_long = T;
+  pl->vw = vw;
   pl->npl = npl;
   pl->G = G;
-  pl->K = static_cast<int>(K > kMaxGrid + 1 ? kMaxGrid + 1 : K);
+  pl->ntd = static_cast<int>(ntd);
+  pl->n_long = static_cast<int>(n_long);
+  pl->n_split = static_cast<int>(T - n_long);
+  pl->Ks = static_cast<int>(K);
   pl->chunk_len = chunk;
-  pl->ws_bytes = 0;
-  if (K > 1) {
-    const size_t one = align256(static_cast<size_t>(batch) * K * dim * N * sizeof(float));
-    pl->ws_bytes = 3 * one;
-  }
+  pl->Lp = ceil_div(L, kMaxTB) * kMaxTB;
 }
-
-bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, const void* B, const void* C,
                              const float* D, const void* z, const float* bias, void* y, float* fs,
@@ -102,74 +163,62 @@ ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, c
   if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0) return SSM_ERR_INVALID_ARG;
   if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return SSM_ERR_INVALID_ARG;
   const size_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
-  if (!aligned(u, es) || !aligned(delta, es) || !aligned(y, es) || (z && !aligned(z, es))) return SSM_ERR_INVALID_ARG;
-  if (!aligned(B, 4) || !aligned(C, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) || (bias && !aligned(bias, 4)) ||
-      (fs && !aligned(fs, 4)))
+  if (!aligned(u, es) || !aligned(delta, es) || !aligned(y, es) || (z && !aligned(z, es)) || !aligned(B, es) ||
+      !aligned(C, es))
+    return SSM_ERR_INVALID_ARG;
+  if (!aligned(A, 4) || (D && !aligned(D, 4)) || (bias && !aligned(bias, 4)) || (fs && !aligned(fs, 4)))
     return SSM_ERR_INVALID_ARG;
   if (dstate > 64) return SSM_ERR_UNSUPPORTED;
   if (dt == SSM_DTYPE_BF16 && (dstate & 1)) return SSM_ERR_UNSUPPORTED;
-  if (batch > kMaxGrid) return SSM_ERR_UNSUPPORTED;
+  if (batch > kMaxBatch) return SSM_ERR_UNSUPPORTED;
   return SSM_OK;
 }
 
-template <class IO, int VW, bool FULL>
-hipError_t launch_scan(int npl, int G, bool exact, const ScanParams& p, dim3 grid, hipStream_t s) {
-#define SSM_SCAN_CASE(NPL_, G_, EX_)                                                                \
-  if (npl == NPL_ && G == G_ && exact == EX_) {                                                   \
-    hipLaunchKernelGGL((scan_kernel<IO, NPL_, G_, VW, FULL, (EX_ ? NPL_ * G_ : 0)>), grid,         \
-                       dim3(64 * G_), 0, s, p);                                                   \
-    return hipGetLastError();                                                                     \
+template <class IO, bool FULL>
+hipError_t launch_scan(int npl, int G, int vw, const ScanParams& p, dim3 grid, hipStream_t s) {
+#define SSM_SCAN_CASE(NPL_, G_)                                                                            \
+  if (npl == NPL_ && G == G_) {                                                                          \
+    constexpr int VWP = (G_ <= 4) ? 4 : ((G_ == 8) ? 2 : 1);                                             \
+    if (vw == VWP)                                                                                       \
+      hipLaunchKernelGGL((scan_kernel<IO, NPL_, G_, VWP, FULL>), grid, dim3(64 * G_), 0, s, p);           \
+    else                                                                                                 \
+      hipLaunchKernelGGL((scan_kernel<IO, NPL_, G_, 1, FULL>), grid, dim3(64 * G_), 0, s, p);             \
+    return hipGetLastError();                                                                            \
   }
-  if constexpr (VW == 4) {
-    SSM_SCAN_CASE(4, 1, true)
-    SSM_SCAN_CASE(4, 2, true)
-    SSM_SCAN_CASE(4, 4, true)
-    SSM_SCAN_CASE(4, 8, true)
-    SSM_SCAN_CASE(4, 1, false)
-    SSM_SCAN_CASE(4, 2, false)
-    SSM_SCAN_CASE(4, 4, false)
-    SSM_SCAN_CASE(4, 8, false)
-    SSM_SCAN_CASE(2, 8, true)
-    SSM_SCAN_CASE(8, 2, true)
-    SSM_SCAN_CASE(16, 1, true)
-  } else {
-    SSM_SCAN_CASE(4, 1, true)
-    SSM_SCAN_CASE(4, 2, true)
-    SSM_SCAN_CASE(4, 4, true)
-    SSM_SCAN_CASE(4, 8, true)
-    SSM_SCAN_CASE(4, 16, true)
-    SSM_SCAN_CASE(4, 1, false)
-    SSM_SCAN_CASE(4, 2, false)
-    SSM_SCAN_CASE(4, 4, false)
-    SSM_SCAN_CASE(4, 8, false)
-    SSM_SCAN_CASE(4, 16, false)
-    SSM_SCAN_CASE(1, 16, true)
-  }
+  SSM_SCAN_CASE(4, 1)
+  SSM_SCAN_CASE(4, 2)
+  SSM_SCAN_CASE(4, 4)
+  SSM_SCAN_CASE(4, 8)
+  SSM_SCAN_CASE(4, 16)
+  SSM_SCAN_CASE(2, 8)
+  SSM_SCAN_CASE(1, 16)
+  SSM_SCAN_CASE(8, 2)
+  SSM_SCAN_CASE(16, 1)
 #undef SSM_SCAN_CASE
   return hipErrorInvalidValue;
 }
 
 template <class IO>
-hipError_t run_scan(const Plan& pl, bool vec4, const ScanParams& p, hipStream_t s) {
-  const bool exact = static_cast<int64_t>(pl.npl) * pl.G == p.N;
-  const dim3 grid_full(static_cast<unsigned>(ceil_div(p.dim, 64)), static_cast<unsigned>(p.batch),
-                       static_cast<unsigned>(pl.K));
-  hipError_t e = hipSuccess;
-  if (pl.K > 1) {
-    const dim3 grid_agg(grid_full.x, grid_full.y, static_cast<unsigned>(pl.K - 1));
-    e = vec4 ? launch_scan<IO, 4, false>(pl.npl, pl.G, exact, p, grid_agg, s)
-             : launch_scan<IO, 1, false>(pl.npl, pl.G, exact, p, grid_agg, s);
+hipError_t run_scan(const Plan& pl, const void* B, const void* C, float* bc, ScanParams p, hipStream_t s) {
+  const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
+  const int64_t packed = p.batch * pl.Lp * npad;
+  hipLaunchKernelGGL(pack_bc_kernel<IO>, dim3(static_cast<unsigned>(ceil_div(packed, 256))), dim3(256), 0, s, B,
+                     C, bc, p.batch, p.L, pl.Lp, p.N, pl.npl, pl.G);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (pl.n_split > 0 && pl.Ks > 1) {
+    const dim3 grid_agg(static_cast<unsigned>(static_cast<int64_t>(pl.n_split) * (pl.Ks - 1)));
+    e = launch_scan<IO, false>(pl.npl, pl.G, pl.vw, p, grid_agg, s);
     if (e != hipSuccess) return e;
-    const int64_t DN = p.dim * p.N;
-    const int64_t threads = p.batch * DN;
+    const int64_t threads = static_cast<int64_t>(pl.n_split) * 64 * npad;
     hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>(ceil_div(threads, 256))), dim3(256), 0, s,
-                       static_cast<const float*>(p.aggP), static_cast<const float*>(p.aggS), p.carry, p.batch,
-                       pl.K, DN);
+                       static_cast<const float*>(p.aggP), static_cast<const float*>(p.aggS), p.carry,
+                       static_cast<int64_t>(pl.n_split), pl.Ks, npad);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return vec4 ? launch_scan<IO, 4, true>(pl.npl, pl.G, exact, p, grid_full, s)
-              : launch_scan<IO, 1, true>(pl.npl, pl.G, exact, p, grid_full, s);
+  const dim3 grid_full(static_cast<unsigned>(pl.n_long + static_cast<int64_t>(pl.n_split) * pl.Ks));
+  return launch_scan<IO, true>(pl.npl, pl.G, pl.vw, p, grid_full, s);
 }
 
 template <class IO>
@@ -201,12 +250,16 @@ hipError_t run_decode(const DecodeParams& p, hipStream_t s) {
 using namespace ssm;
 
 extern "C" size_t ssm_scan_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt) {
-  if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 64 || batch > kMaxGrid) return 0;
+  if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 64 || batch > kMaxBatch) return 0;
   if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return 0;
   if (dt == SSM_DTYPE_BF16 && (dstate & 1)) return 0;
-  Plan pl;
-  plan_scan(batch, L, dim, dstate, &pl);
-  return pl.ws_bytes;
+  // The packed layout depends only on the variant, which the pointers do not
+  // change; size it for the widest and the narrowest prologue anyway.
+  Plan p4, p1;
+  plan_scan(batch, L, dim, dstate, 4, &p4);
+  plan_scan(batch, L, dim, dstate, 1, &p1);
+  const size_t a = layout_for(p4, batch).total, b = layout_for(p1, batch).total;
+  return a > b ? a : b;
 }
 
 extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -217,50 +270,53 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
   const ssm_status_t st =
       check_scan_args(u, delta, A, B, C, D, z, delta_bias, y, final_state, batch, L, dim, dstate, dt);
   if (st != SSM_OK) return st;
+  // A prologue width vw needs dim % vw == 0 and token rows aligned to vw elements.
+  const size_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
+  int vw_ok = 1;
+  for (int v = 4; v >= 2; v /= 2) {
+    const size_t vb = es * v;
+    if ((dim % v) == 0 && aligned(u, vb) && aligned(delta, vb) && aligned(y, vb) && (!z || aligned(z, vb))) {
+      vw_ok = v;
+      break;
+    }
+  }
   Plan pl;
-  plan_scan(batch, L, dim, dstate, &pl);
-  if (pl.K > kMaxGrid) return SSM_ERR_UNSUPPORTED;
-  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned(workspace, 256)))
-    return SSM_ERR_INVALID_ARG;
+  plan_scan(batch, L, dim, dstate, vw_ok, &pl);
+  if (static_cast<int64_t>(pl.n_long) + static_cast<int64_t>(pl.n_split) * pl.Ks > 0x7fffffffLL)
+    return SSM_ERR_UNSUPPORTED;
+  const Layout lay = layout_for(pl, batch);
+  if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256)) return SSM_ERR_INVALID_ARG;
 
+  char* ws = static_cast<char*>(workspace);
   ScanParams p;
   p.u = u;
   p.delta = delta;
   p.A = A;
-  p.B = B;
-  p.C = C;
   p.D = D;
   p.z = z;
   p.bias = delta_bias;
+  p.bc = reinterpret_cast<const float*>(ws);
   p.y = y;
   p.final_state = final_state;
+  p.aggP = p.aggS = p.carry = nullptr;
+  if (pl.n_split > 0) {
+    p.aggP = reinterpret_cast<float*>(ws + lay.bc);
+    p.aggS = reinterpret_cast<float*>(ws + lay.bc + lay.agg);
+    p.carry = reinterpret_cast<float*>(ws + lay.bc + 2 * lay.agg);
+  }
   p.batch = batch;
   p.L = L;
+  p.Lp = pl.Lp;
   p.dim = dim;
   p.N = dstate;
   p.chunk_len = pl.chunk_len;
-  p.K = pl.K;
+  p.ntd = pl.ntd;
+  p.n_long = pl.n_long;
+  p.Ks = pl.Ks;
   p.softplus = softplus_flag ? 1 : 0;
-  p.aggP = p.aggS = p.carry = nullptr;
-  if (pl.K > 1) {
-    const size_t one = pl.ws_bytes / 3;
-    char* ws = static_cast<char*>(workspace);
-    p.aggP = reinterpret_cast<float*>(ws);
-    p.aggS = reinterpret_cast<float*>(ws + one);
-    p.carry = reinterpret_cast<float*>(ws + 2 * one);
-  }
-  // Vector (4-wide) prologue/epilogue needs dim % 4 == 0 and aligned token rows.
-  const size_t vbytes = dt == SSM_DTYPE_F32 ? 16 : 8;
-  bool vec4 = (dim % 4) == 0 && aligned(u, vbytes) && aligned(delta, vbytes) && aligned(y, vbytes) &&
-              (!z || aligned(z, vbytes));
-  // Variants with 16 wavefronts only exist with the 1-wide prologue.
-  if (pl.G == 16) vec4 = false;
-  // The 1-wide family is the (npl = 4) one plus (1, 16); fall back to it when needed.
-  if (!vec4 && !(pl.npl == 4 || (pl.npl == 1 && pl.G == 16))) {
-    pl.npl = 4;
-    pl.G = next_pow2(ceil_div(dstate, 4));
-  }
-  const hipError_t e = dt == SSM_DTYPE_F32 ? run_scan<F32>(pl, vec4, p, stream) : run_scan<BF16>(pl, vec4, p, stream);
+  float* bc = reinterpret_cast<float*>(ws);
+  const hipError_t e = dt == SSM_DTYPE_F32 ? run_scan<F32>(pl, B, C, bc, p, stream)
+                                           : run_scan<BF16>(pl, B, C, bc, p, stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

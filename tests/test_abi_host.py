@@ -51,13 +51,14 @@ def test_status_strings():
 
 def test_workspace_size():
     L = ops.lib()
-    # one chunk (far more channels than the machine needs): no workspace
-    assert L.ssm_scan_workspace_size(64, 256, 8192, 16, BF16) == 0
-    # few channels, long sequence: chunked, workspace = 3 arrays of batch*K*dim*N fp32
-    ws = L.ssm_scan_workspace_size(1, 1 << 20, 64, 16, F32)
-    assert ws > 0 and ws % 256 == 0
-    per = 1 * 64 * 16 * 4
-    assert ws >= 3 * 2 * per
+    # B and C are always repacked into fp32 per-state-group records: at least
+    # batch * L(rounded up to 32) * 2 * dstate floats, 256-byte granular
+    ws = L.ssm_scan_workspace_size(64, 256, 8192, 16, BF16)
+    assert ws >= 64 * 256 * 2 * 16 * 4 and ws % 256 == 0
+    # few channels, long sequence: the tile is cut into chunks, which adds
+    # chunk pairs and carried-in states on top of the packed B/C
+    ws_long = L.ssm_scan_workspace_size(1, 1 << 20, 64, 16, F32)
+    assert ws_long > (1 << 20) * 2 * 16 * 4 and ws_long % 256 == 0
     # rejected shapes report 0
     assert L.ssm_scan_workspace_size(0, 10, 10, 16, F32) == 0
     assert L.ssm_scan_workspace_size(1, 10, 10, 65, F32) == 0
@@ -83,7 +84,8 @@ def _scan(lib_, **kw):
     (dict(u=0x1001), INVALID), (dict(B=0x4002), INVALID), (dict(fs=0x7002), INVALID),
     (dict(dt=BF16, u=0x1001), INVALID),
     (dict(N=65), UNSUPPORTED), (dict(N=15, dt=BF16), UNSUPPORTED), (dict(batch=70000), UNSUPPORTED),
-    # chunked shape with a missing / too small / misaligned workspace
+    # missing / too small workspace
+    (dict(batch=1, L=8, dim=8, N=16), INVALID),
     (dict(batch=1, L=1 << 20, dim=64, N=16), INVALID),
     (dict(batch=1, L=1 << 20, dim=64, N=16, ws=0x100000, wsb=1024), INVALID),
 ])
