@@ -155,6 +155,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="instead of the scan, time a plain device copy of this many MiB (calibrates HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -164,6 +166,18 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_mib > 0:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters scale the scan's to bytes.
+        dev = torch.device("cuda:0")
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        ms, _ = time_calls(lambda: dst.copy_(src), args.steps, args.warmup, torch.cuda.current_stream(dev))
+        nbytes = 4 * n
+        print(json.dumps({"metric": "device copy GB/s", "value": 2 * nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
+                          "copy_bytes_each_way": nbytes, "ms_per_copy": ms, "steps": args.steps}), flush=True)
+        return
 
     from selective_state_space_33_amd import inputs as I
     from selective_state_space_33_amd import ops

@@ -106,6 +106,64 @@ template <> __device__ __forceinline__ void store_vals<BF16, 1>(void* base, int6
   static_cast<uint16_t*>(base)[idx] = to_bf16(v[0]);
 }
 
+// Buffer (V#) access.  A raw buffer resource covers [base, base + bytes);
+// loads at offsets outside it return zero and stores there are dropped by the
+// hardware, so a ragged tail needs no branch.  Offsets are 32-bit bytes.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kBufWord3 = 0x00020000;  // gfx9 descriptor word 3: 32-bit data format, raw (unswizzled) addressing
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t n = bytes < 0 ? 0 : (bytes > 0xffffffffLL ? 0xffffffffLL : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(static_cast<uint32_t>(n)),
+                                           kBufWord3);
+}
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+template <class IO, int VW> __device__ __forceinline__ Raw<IO, VW> buf_load(rsrc_t r, int voff, int soff);
+template <> __device__ __forceinline__ Raw<F32, 4> buf_load<F32, 4>(rsrc_t r, int voff, int soff) {
+  return {__builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0))};
+}
+template <> __device__ __forceinline__ Raw<F32, 2> buf_load<F32, 2>(rsrc_t r, int voff, int soff) {
+  return {__builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0))};
+}
+template <> __device__ __forceinline__ Raw<F32, 1> buf_load<F32, 1>(rsrc_t r, int voff, int soff) {
+  return {__uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0))};
+}
+template <> __device__ __forceinline__ Raw<BF16, 4> buf_load<BF16, 4>(rsrc_t r, int voff, int soff) {
+  return {__builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0))};
+}
+template <> __device__ __forceinline__ Raw<BF16, 2> buf_load<BF16, 2>(rsrc_t r, int voff, int soff) {
+  return {__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0)};
+}
+template <> __device__ __forceinline__ Raw<BF16, 1> buf_load<BF16, 1>(rsrc_t r, int voff, int soff) {
+  return {__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0)};
+}
+
+template <class IO, int VW> __device__ __forceinline__ void buf_store(rsrc_t r, int voff, int soff, const float* v);
+template <> __device__ __forceinline__ void buf_store<F32, 4>(rsrc_t r, int voff, int soff, const float* v) {
+  const u32x4_t x = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+  __builtin_amdgcn_raw_buffer_store_b128(x, r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ void buf_store<F32, 2>(rsrc_t r, int voff, int soff, const float* v) {
+  const u32x2_t x = {__float_as_uint(v[0]), __float_as_uint(v[1])};
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ void buf_store<F32, 1>(rsrc_t r, int voff, int soff, const float* v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[0]), r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ void buf_store<BF16, 4>(rsrc_t r, int voff, int soff, const float* v) {
+  const u32x2_t x = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  __builtin_amdgcn_raw_buffer_store_b64(x, r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ void buf_store<BF16, 2>(rsrc_t r, int voff, int soff, const float* v) {
+  __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(v[0], v[1]), r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ void buf_store<BF16, 1>(rsrc_t r, int voff, int soff, const float* v) {
+  __builtin_amdgcn_raw_buffer_store_b16(to_bf16(v[0]), r, voff, soff, 0);
+}
+
 // Loads of wave-uniform fp32 data through the constant address space, so the
 // compiler issues scalar (s_load) loads into SGPRs, which the VALU then takes
 // as operands directly.

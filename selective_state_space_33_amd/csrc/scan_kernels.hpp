@@ -19,8 +19,13 @@
 //   - (epilogue of block k-1) sum the G partial readouts of each (token,
 //     channel) in a fixed order, add D*u, multiply by SiLU(z), round, store y;
 //   - (prologue of block k+1) turn the u, delta_raw, z loaded two blocks
-//     earlier (coalesced vector loads) into delta = softplus(raw + bias) and
-//     delta*u, once per (token, channel), staged in LDS.
+//     earlier (coalesced buffer loads) into delta = softplus(raw + bias) and
+//     delta*u, once per (token, channel), staged in LDS;
+//   - issue the loads of block k+3.
+// The main loop has no data-dependent branch: the sequence is padded to whole
+// trips of blocks, token rows past the end read as zero through the buffer
+// resources' range check (and their stores are dropped), and a padding
+// token's delta is forced to 0, which makes its step the identity pair (1, 0).
 // The scan of block k walks its TB tokens: for every state
 // a = exp2(delta * A*log2 e), h = a*h + (delta*u)*B_t[n], and the partial
 // readout y_w = sum over its states of C_t[n]*h -- the fade-and-add pair
@@ -79,7 +84,6 @@ template <int G, int VW> struct BlockShape {
   static_assert(G * VW <= kTB, "a block row must fit the prologue threads");
   static constexpr int RPT = TB / (G * VW);
 };
-constexpr int kMaxTB = kTB;  // packed B/C rows are padded to a multiple of this
 
 // Tokens per group: one group's packed B/C records are 16 floats (32 for NPL 16).
 template <int NPL> struct GroupShape {
@@ -91,14 +95,20 @@ template <int NPL> struct GroupShape {
 
 template <int I> struct IC { static constexpr int value = I; };
 
-// Token blocks of u, delta_raw, z loaded ahead of the block being scanned
-// (ring of register buffers).  The scattered 128-byte rows of a tile need a
-// deep prefetch to cover HBM latency.
-#ifndef SSM_PREFETCH_BLOCKS
-#define SSM_PREFETCH_BLOCKS 4
-#endif
-constexpr int kPD = SSM_PREFETCH_BLOCKS;
-static_assert(kPD == 2 || kPD == 4 || kPD == 8, "prefetch ring is 2, 4 or 8 blocks");
+// Ring of raw token blocks (u, delta_raw, z) in registers.  Block k+kPD+1 is
+// loaded while block k is scanned, staged by the prologue while block k+kPD is
+// scanned, and its u, z are read again by its epilogue while block k+kPD+2 is
+// scanned, so the ring has kRing = kPD + 2 slots and the main loop is unrolled
+// by kRing:
+// every slot is then written and read at fixed points of the loop body and
+// stays in the same registers across iterations (no copies, so no waits on
+// loads in flight).
+constexpr int kPD = 2;
+constexpr int kRing = kPD + 2;
+// Tokens per unrolled trip of the main loop.  Chunk lengths and the packed B/C
+// rows are multiples of it; one group of records past the end is read (and
+// not used), so the packed buffer carries kTB rows of padding.
+constexpr int kTrip = kRing * kTB;
 
 // lgkmcnt(0) with vmcnt and expcnt left at their maxima (gfx9 encoding).
 constexpr int kWaitLgkm0 = 0xC07F;
@@ -134,7 +144,9 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   static_assert(TB == RPT * ROWSTEP, "block shape");
   using GS = GroupShape<NPL>;
   constexpr int SUB = GS::SUB, NG = TB / SUB;
-  static_assert(TB % (2 * SUB) == 0, "groups come in pairs (double-buffered)");
+  static_assert(NG % 2 == 0, "groups come in pairs (double-buffered)");
+  static_assert(kRing % 2 == 0, "ring slots keep their block parity");
+  constexpr int ES = __is_same(IO, F32) ? 4 : 2;  // bytes per stored element
 
   // Double-buffered by block parity.
   __shared__ float2 sDU[2][TB][64];                            // (delta, delta*u) per token, channel
@@ -166,8 +178,14 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   const int64_t d0 = static_cast<int64_t>(tile % p.ntd) * 64;
   const int64_t t_begin = split ? static_cast<int64_t>(c) * p.chunk_len : 0;
   const int64_t t_end = split ? ((t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L) : L;
+  const int64_t rows = t_end - t_begin;
+  const int rows32 = static_cast<int>(rows);
   const int64_t pair_row = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;   // row of [n_split][Ks][64]
-  const int nblocks = static_cast<int>((t_end - t_begin + TB - 1) / TB);
+  // Whole trips of kRing blocks; blocks past the chunk are padding whose
+  // tokens are identity steps (delta = 0) and whose outputs fall outside the
+  // buffers.
+  const int ntrips = static_cast<int>((rows + kTrip - 1) / kTrip);
+  const int nblocks = ntrips * kRing;
 
   // ---- scan lane: channel d, states n0 .. n0+NPL-1
   const int64_t d = d0 + lane;
@@ -181,12 +199,12 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     h[j] = 0.0f;
     if (FULL && split && c > 0 && dvalid) h[j] = p.carry[pair_row * NPAD + n];
   }
-  float delta_total = 0.0f;  // chunk sum of delta (aggregate pass), summed per block then per chunk
+  float delta_total = 0.0f;  // chunk sum of delta (aggregate pass)
 
-  // packed B/C records of this wavefront's state group
-  const float* bc_row = p.bc + (b * G + w) * p.Lp * (2 * NPL);
+  // packed B/C records of this wavefront's state group, from the chunk's first token
+  const float* bc_row = p.bc + ((b * G + w) * p.Lp + t_begin) * (2 * NPL);
 
-  // ---- prologue / epilogue thread: channels pd .. pd+VW-1, rows prow + i*ROWSTEP
+  // ---- prologue / epilogue thread: channels pd .. pd+VW-1, rows prow + i*ROWSTEP of a block
   const int pcol = (tid % RPR) * VW;
   const int prow = tid / RPR;
   const int64_t pd = d0 + pcol;
@@ -199,36 +217,47 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   }
   const bool has_z = FULL && p.z != nullptr;
 
-  // Raw loads of u, delta_raw, z in a ring of kPD blocks (slot = block % kPD),
-  // and u, z kept for the epilogue by block parity.
-  Raw<IO, VW> ru[kPD][RPT], rd[kPD][RPT], rz[kPD][RPT];
-  Raw<IO, VW> eu[2][RPT], ez[2][RPT];
+  // Token rows of u, delta_raw, z, y are reached through buffer resources
+  // covering (b, t_begin, d0) up to the end of the chunk's last row, so rows
+  // past the chunk read as zero and are not written.  The host keeps a
+  // chunk's rows within 2^31 bytes, so offsets are 32-bit.
+  const int row_bytes = static_cast<int>(dim * ES);
+  const int blk_bytes = TB * row_bytes;
+  const int64_t base_off = ((b * L + t_begin) * dim + d0) * ES;
+  const int64_t chunk_bytes = rows * row_bytes - d0 * ES;
+  const rsrc_t rs_u = make_rsrc(static_cast<const char*>(p.u) + base_off, chunk_bytes);
+  const rsrc_t rs_d = make_rsrc(static_cast<const char*>(p.delta) + base_off, chunk_bytes);
+  const rsrc_t rs_z = make_rsrc(has_z ? static_cast<const char*>(p.z) + base_off : nullptr, has_z ? chunk_bytes : 0);
+  const rsrc_t rs_y = make_rsrc(FULL ? static_cast<const char*>(p.y) + base_off : nullptr, FULL ? chunk_bytes : 0);
+  int voff[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) voff[i] = (prow + i * ROWSTEP) * row_bytes + pcol * ES;
 
-  auto issue_loads = [&](auto slotc, int64_t t0) {
+  // Raw u, delta_raw, z of kRing blocks (slot = block % kRing).
+  Raw<IO, VW> ru[kRing][RPT], rd[kRing][RPT], rz[kRing][RPT];
+
+  auto issue_loads = [&](auto slotc, int blk) {
     constexpr int S = decltype(slotc)::value;
+    const int bo = blk * blk_bytes;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int64_t t = t0 + prow + i * ROWSTEP;
-      if (pvalid && t < t_end) {
-        const int64_t idx = (b * L + t) * dim + pd;
-        ru[S][i] = raw_load<IO, VW>(p.u, idx);
-        rd[S][i] = raw_load<IO, VW>(p.delta, idx);
-        rz[S][i] = has_z ? raw_load<IO, VW>(p.z, idx) : raw_zero<IO, VW>();
-      } else {
-        ru[S][i] = raw_zero<IO, VW>();
-        rd[S][i] = raw_zero<IO, VW>();
-        rz[S][i] = raw_zero<IO, VW>();
-      }
+      ru[S][i] = buf_load<IO, VW>(rs_u, voff[i] + bo, 0);
+      rd[S][i] = buf_load<IO, VW>(rs_d, voff[i] + bo, 0);
+    }
+    if (has_z) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) rz[S][i] = buf_load<IO, VW>(rs_z, voff[i] + bo, 0);
     }
   };
 
-  // Stage (delta, delta*u) of the block with parity P held in ring slot S.
-  auto prologue = [&](auto parc, auto slotc) {
+  // Stage (delta, delta*u) of block blk (parity P) held in ring slot S.
+  auto prologue = [&](auto parc, auto slotc, int blk) {
     constexpr int P = decltype(parc)::value;
     constexpr int S = decltype(slotc)::value;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = prow + i * ROWSTEP;
+      const bool live = blk * TB + row < rows32;
       float uf[VW], df[VW];
       unpack<IO, VW>(ru[S][i], uf);
       unpack<IO, VW>(rd[S][i], df);
@@ -236,7 +265,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
         const float x = df[e] + biasv[e];
-        const float dl = p.softplus ? softplus_f(x) : x;
+        float dl = p.softplus ? softplus_f(x) : x;
+        dl = live ? dl : 0.0f;  // padding token: the identity step (1, 0)
         out[e] = make_float2(dl, dl * uf[e]);
       }
       if constexpr (VW == 4) {
@@ -248,48 +278,51 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       } else {
         sDU[P][row][pcol] = out[0];
       }
-      if (FULL) {
-        eu[P][i] = ru[S][i];
-        ez[P][i] = rz[S][i];
-      }
     }
   };
 
-  // Finish the block with parity P that starts at token t0.
-  auto epilogue = [&](auto parc, int64_t t0) {
-    constexpr int P = FULL ? decltype(parc)::value : 0;
+  // Finish block blk (parity P, ring slot S):
+  // y = (sum of partial readouts + D*u) * SiLU(z).
+  auto epilogue = [&](auto parc, auto slotc, int blk) {
     if constexpr (FULL) {
+      constexpr int P = decltype(parc)::value;
+      constexpr int S = decltype(slotc)::value;
+      const int bo = blk * blk_bytes;
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int row = prow + i * ROWSTEP;
-      const int64_t t = t0 + row;
-      if (!pvalid || t >= t_end) continue;
-      float ys[VW];
+      for (int i = 0; i < RPT; ++i) {
+        const int row = prow + i * ROWSTEP;
+        // all G partials are read before the (fixed-order) sum
+        float part[G][VW];
 #pragma unroll
-      for (int e = 0; e < VW; ++e) ys[e] = 0.0f;
-#pragma unroll
-      for (int ww = 0; ww < G; ++ww) {
-        if constexpr (VW == 4) {
-          const float4 v = *reinterpret_cast<const float4*>(&sY[P][ww][row][pcol]);
-          ys[0] += v.x; ys[1] += v.y; ys[2] += v.z; ys[3] += v.w;
-        } else if constexpr (VW == 2) {
-          const float2 v = *reinterpret_cast<const float2*>(&sY[P][ww][row][pcol]);
-          ys[0] += v.x; ys[1] += v.y;
-        } else {
-          ys[0] += sY[P][ww][row][pcol];
+        for (int ww = 0; ww < G; ++ww) {
+          if constexpr (VW == 4) {
+            const float4 v = *reinterpret_cast<const float4*>(&sY[P][ww][row][pcol]);
+            part[ww][0] = v.x; part[ww][1] = v.y; part[ww][2] = v.z; part[ww][3] = v.w;
+          } else if constexpr (VW == 2) {
+            const float2 v = *reinterpret_cast<const float2*>(&sY[P][ww][row][pcol]);
+            part[ww][0] = v.x; part[ww][1] = v.y;
+          } else {
+            part[ww][0] = sY[P][ww][row][pcol];
+          }
         }
-      }
-      float uf[VW], zf[VW], out[VW];
-      unpack<IO, VW>(eu[P][i], uf);
-      if (has_z) unpack<IO, VW>(ez[P][i], zf);
+        float ys[VW];
 #pragma unroll
-      for (int e = 0; e < VW; ++e) {
-        float v = __builtin_fmaf(Dv[e], uf[e], ys[e]);
-        if (has_z) v *= silu_f(zf[e]);
-        out[e] = v;
+        for (int e = 0; e < VW; ++e) {
+          ys[e] = part[0][e];
+#pragma unroll
+          for (int ww = 1; ww < G; ++ww) ys[e] += part[ww][e];
+        }
+        float uf[VW], zf[VW], out[VW];
+        unpack<IO, VW>(ru[S][i], uf);
+        if (has_z) unpack<IO, VW>(rz[S][i], zf);
+#pragma unroll
+        for (int e = 0; e < VW; ++e) {
+          float v = __builtin_fmaf(Dv[e], uf[e], ys[e]);
+          if (has_z) v *= silu_f(zf[e]);
+          out[e] = v;
+        }
+        if (pvalid) buf_store<IO, VW>(rs_y, voff[i] + bo, 0, out);
       }
-      store_vals<IO, VW>(p.y, (b * L + t) * dim + pd, out);
-    }
     }
   };
 
@@ -311,7 +344,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   float rec[2][GS::FLOATS];
   float2 dd[2][SUB];
 
-  auto fetch_records = [&](auto bufc, int64_t t) {  // t: first token of the group
+  auto fetch_records = [&](auto bufc, int64_t t) {  // t: first token of the group, from t_begin
     constexpr int BUF = decltype(bufc)::value;
     cf32x16_p src = (cf32x16_p)(bc_row + t * (2 * NPL));
 #pragma unroll
@@ -328,85 +361,56 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     for (int q = 0; q < SUB; ++q) dd[BUF][q] = sDU[P][g * SUB + q][lane];
   };
 
-  // Group g of the block with parity P from buffer BUF; the next group's
-  // records and (delta, delta*u) are fetched into the other buffer while this
-  // one computes.
-  auto group = [&](auto parc, auto bufc, int g, int64_t t0, float& block_delta) {
+  // Group g of the block with parity P from buffer BUF.  The next group's
+  // records (the next block's first group after the last one) and staged
+  // values are fetched into the other buffer while this one computes.
+  auto group = [&](auto parc, auto bufc, auto gc, int64_t t0, float& block_delta) {
     constexpr int BUF = decltype(bufc)::value;
-    // This group's records and staged values (issued one group earlier) are
-    // complete here; the next group's loads are issued only after this wait,
-    // so they stay in flight while this group computes.
+    constexpr int g = decltype(gc)::value;
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_sched_barrier(0);
-    if (g + 1 < NG) {
-      fetch_records(IC<1 - BUF>{}, t0 + (g + 1) * SUB);
-      fetch_dd(parc, IC<1 - BUF>{}, g + 1);
-    }
+    fetch_records(IC<1 - BUF>{}, t0 + (g + 1) * SUB);
+    if constexpr (g + 1 < NG) fetch_dd(parc, IC<1 - BUF>{}, g + 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < SUB; ++q) update(parc, dd[BUF][q], &rec[BUF][q * 2 * NPL], g * SUB + q, block_delta);
   };
 
-  // Block k (parity P = k % 2, ring slot S = k % kPD, first token t0):
-  // epilogue of k-1, prologue of k+1, loads of k+kPD, scan of k.
-  auto iteration = [&](auto slotc, int k, int64_t t0) {
+  // Block k (parity P = k % 2, ring slot S = k % kRing): epilogue of k-1,
+  // prologue of k+1, loads of k+kPD+1 into the slot block k-1 frees, scan of k.
+  auto iteration = [&](auto slotc, int k) {
     constexpr int S = decltype(slotc)::value;
     constexpr int P = S & 1;
-    constexpr int S1 = (S + 1) % kPD;  // ring slot of block k+1
+    constexpr int Sm1 = (S + kRing - 1) % kRing;  // block k-1, refilled with block k+kPD+1
+    constexpr int Sp1 = (S + 1) % kRing;          // block k+1
+    static_assert((S + kPD + 1) % kRing == Sm1, "ring");
     IC<P> parc;
-    const int nt = static_cast<int>((t_end - t0 < TB) ? (t_end - t0) : TB);
-    const bool full_block = nt == TB;
-    if (full_block) {
-      fetch_records(IC<0>{}, t0);
-      fetch_dd(parc, IC<0>{}, 0);
-    }
-    if constexpr (FULL) {
-      if (k >= 1) epilogue(IC<1 - P>{}, t0 - TB);
-    }
-    if (k + 1 < nblocks) {
-      prologue(IC<1 - P>{}, IC<S1>{});
-      issue_loads(IC<S1>{}, t0 + (kPD + 1) * TB);
-    }
+    const int64_t t0 = static_cast<int64_t>(k) * TB;
+    fetch_dd(parc, IC<0>{}, 0);
+    if (k >= 1) epilogue(IC<1 - P>{}, IC<Sm1>{}, k - 1);
+    prologue(IC<1 - P>{}, IC<Sp1>{}, k + 1);
+    issue_loads(IC<Sm1>{}, k + kPD + 1);
     float block_delta = 0.0f;
-    if (full_block) {
-#pragma unroll
-      for (int g = 0; g < NG; g += 2) {
-        group(parc, IC<0>{}, g, t0, block_delta);
-        group(parc, IC<1>{}, g + 1, t0, block_delta);
-      }
-    } else {
-      for (int tt = 0; tt < nt; ++tt) {
-        float r[2 * NPL];
-        cfloat_p src = (cfloat_p)(bc_row + (t0 + tt) * (2 * NPL));
-#pragma unroll
-        for (int kk = 0; kk < 2 * NPL; ++kk) r[kk] = src[kk];
-        update(parc, sDU[P][tt][lane], r, tt, block_delta);
-      }
-    }
+    [&]<int... I>(std::integer_sequence<int, I...>) {
+      ((group(parc, IC<I % 2>{}, IC<I>{}, t0, block_delta)), ...);
+    }(std::make_integer_sequence<int, NG>{});
     delta_total += block_delta;
     __syncthreads();
   };
 
-  // fill the ring, stage block 0, reuse its slot for block kPD
+  // fill the ring with blocks 0 .. kPD, stage block 0
   [&]<int... I>(std::integer_sequence<int, I...>) {
-    (issue_loads(IC<I>{}, t_begin + static_cast<int64_t>(I) * TB), ...);
-  }(std::make_integer_sequence<int, kPD>{});
-  prologue(IC<0>{}, IC<0>{});
-  issue_loads(IC<0>{}, t_begin + static_cast<int64_t>(kPD) * TB);
+    (issue_loads(IC<I>{}, I), ...);
+  }(std::make_integer_sequence<int, kPD + 1>{});
+  fetch_records(IC<0>{}, 0);
+  prologue(IC<0>{}, IC<0>{}, 0);
   __syncthreads();
-  for (int k = 0; k < nblocks; k += kPD) {
-    bool done = false;
+  for (int k = 0; k < nblocks; k += kRing) {
     [&]<int... I>(std::integer_sequence<int, I...>) {
-      ((done = done || (k + I >= nblocks), done ? void() : iteration(IC<I>{}, k + I, t_begin + static_cast<int64_t>(k + I) * TB)), ...);
-    }(std::make_integer_sequence<int, kPD>{});
+      (iteration(IC<I>{}, k + I), ...);
+    }(std::make_integer_sequence<int, kRing>{});
   }
-  if constexpr (FULL) {
-    const int64_t t_last = t_begin + static_cast<int64_t>(nblocks - 1) * TB;
-    if ((nblocks - 1) & 1)
-      epilogue(IC<1>{}, t_last);
-    else
-      epilogue(IC<0>{}, t_last);
-  }
+  epilogue(IC<1>{}, IC<kRing - 1>{}, nblocks - 1);  // nblocks is a multiple of kRing (even)
 
   if (!dvalid) return;
 #pragma unroll

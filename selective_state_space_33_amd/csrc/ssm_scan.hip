@@ -20,7 +20,7 @@ namespace ssm {
 namespace {
 
 constexpr int64_t kMaxBatch = 65535;
-constexpr int64_t kChunkQuantum = kMaxTB; // chunk lengths are multiples of the largest token block
+constexpr int64_t kChunkQuantum = kTrip;  // chunk lengths are multiples of the main loop trip
 constexpr int64_t kMinChunk = 256;        // never cut the sequence finer than this
 constexpr int64_t kNumCU = 256;           // MI355X compute units: the work is balanced over these
 constexpr int64_t kMaxChunks = 4096;      // chunks per split tile
@@ -57,7 +57,7 @@ struct Layout {
 Layout layout_for(const Plan& pl, int64_t batch) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
   Layout l;
-  l.bc = align256(static_cast<size_t>(batch) * pl.Lp * 2 * npad * sizeof(float));
+  l.bc = align256((static_cast<size_t>(batch) * pl.Lp + kTB) * 2 * npad * sizeof(float));
   l.agg = pl.n_split > 0 ? align256(static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float)) : 0;
   l.total = l.bc + 3 * l.agg;
   return l;
@@ -92,25 +92,28 @@ void generic_variant(int64_t N, int* npl, int* G) {
   *G = next_pow2(ceil_div(N, 4));
 }
 
+// The kernels address a chunk's token rows with 32-bit byte offsets: a chunk
+// (plus one trip of padding) must stay below 2^31 bytes per tensor, so very
+// long rows force every tile to be cut.
+int64_t max_chunk_len(int64_t dim, int64_t es) {
+  return (0x7fffffffLL / (dim * es) - kTrip) / kTrip * kTrip;
+}
+
 // Work plan.  A tile (64 channels of one batch row) scanned whole costs one
 // pass over L tokens; cutting it into chunks adds an aggregate pass over all
-// but its last chunk (about three quarters of the cost per token), so tiles
-// are only cut where the GPU would otherwise run unevenly:
-//   - at least one tile per CU: the largest multiple of the CU count runs
-//     whole; the remaining r tiles (if any) are cut into ~CU/r chunks each;
-//   - fewer tiles than CUs: tiles run whole if they cover at least 3/4 of the
-//     CUs, otherwise every tile is cut so that each CU gets ~2 chunks.
+// but its last chunk (about four fifths of the cost per token), so tiles are
+// only cut when there are too few of them to keep the GPU busy: with at least
+// 3/4 as many tiles as CUs every tile runs whole; otherwise every tile is cut
+// so that each CU gets about two chunks (two workgroups of the 16-state
+// variant fit on a CU).
 // vw_ok: the widest token-row access the pointers and dim allow (4, 2 or 1);
 // it decides the prologue width, not the split.
-void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int vw_ok, Plan* pl) {
+void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int vw_ok, Plan* pl) {
   int npl, G, Kreq = 0;
-  const int64_t tiles = batch * ceil_div(dim, 64);
   if (N == 16) {
-    // Many tiles: one state per lane over 16 wavefronts (4 per SIMD from one
-    // workgroup).  Few tiles (long sequences cut into many chunks): 8 states per
-    // lane over 2 wavefronts, which reads B_t/C_t for more work per scalar load.
-    npl = tiles * 4 >= kNumCU ? 1 : 8;
-    G = 16 / npl;
+    // 2 states per lane over 8 wavefronts: 80 KB of LDS, two workgroups per CU.
+    npl = 2;
+    G = 8;
   } else {
     generic_variant(N, &npl, &G);
   }
@@ -128,11 +131,6 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int vw_ok, Plan
   if (Kreq > 0) {
     K = Kreq;
     n_long = 0;
-  } else if (T >= kNumCU) {
-    n_long = (T / kNumCU) * kNumCU;
-    const int64_t r = T - n_long;
-    K = r ? (kNumCU + r / 2) / r : 1;
-    if (K > kmax) K = kmax;
   } else if (4 * T >= 3 * kNumCU) {
     n_long = T;
     K = 1;
@@ -142,6 +140,11 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int vw_ok, Plan
     if (K > kmax) K = kmax;
   }
   if (K < 1) K = 1;
+  const int64_t kmin = ceil_div(L, max_chunk_len(dim, es));
+  if (kmin > 1) {
+    n_long = 0;
+    if (K < kmin) K = kmin;
+  }
   int64_t chunk = ceil_div(ceil_div(L, K), kChunkQuantum) * kChunkQuantum;
   K = ceil_div(L, chunk);
   if (K == 1) n_long = T;
@@ -153,7 +156,7 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int vw_ok, Plan
   pl->n_split = static_cast<int>(T - n_long);
   pl->Ks = static_cast<int>(K);
   pl->chunk_len = chunk;
-  pl->Lp = ceil_div(L, kMaxTB) * kMaxTB;
+  pl->Lp = ceil_div(L, kTrip) * kTrip;
 }
 
 ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -256,8 +259,10 @@ extern "C" size_t ssm_scan_workspace_size(int64_t batch, int64_t L, int64_t dim,
   // The packed layout depends only on the variant, which the pointers do not
   // change; size it for the widest and the narrowest prologue anyway.
   Plan p4, p1;
-  plan_scan(batch, L, dim, dstate, 4, &p4);
-  plan_scan(batch, L, dim, dstate, 1, &p1);
+  const int64_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
+  if (max_chunk_len(dim, es) < kChunkQuantum) return 0;
+  plan_scan(batch, L, dim, dstate, es, 4, &p4);
+  plan_scan(batch, L, dim, dstate, es, 1, &p1);
   const size_t a = layout_for(p4, batch).total, b = layout_for(p1, batch).total;
   return a > b ? a : b;
 }
@@ -280,8 +285,9 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
       break;
     }
   }
+  if (max_chunk_len(dim, static_cast<int64_t>(es)) < kChunkQuantum) return SSM_ERR_UNSUPPORTED;
   Plan pl;
-  plan_scan(batch, L, dim, dstate, vw_ok, &pl);
+  plan_scan(batch, L, dim, dstate, static_cast<int64_t>(es), vw_ok, &pl);
   if (static_cast<int64_t>(pl.n_long) + static_cast<int64_t>(pl.n_split) * pl.Ks > 0x7fffffffLL)
     return SSM_ERR_UNSUPPORTED;
   const Layout lay = layout_for(pl, batch);
