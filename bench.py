@@ -10,8 +10,8 @@ dstate 16) is timed separately in the same run and reported under "decode".
 
 Prints ONE JSON line.  Fields beyond the common ones:
   roofline      the dominant kernel against its binding roofline (VALU issue:
-                the scan needs 4 fp32 VALU ops + 1 transcendental per state
-                update, which takes longer at peak than moving its bytes);
+                the scan needs 4 fp32 VALU ops + 1 exp per state update, which
+                takes longer at the chip's issue rate than moving its bytes);
   hbm           the same launch against the 8 TB/s HBM roofline (the metric's
                 second half);
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
@@ -28,13 +28,17 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
-VALU_PEAK_TFLOPS = 157.3        # MI355X fp32 vector peak: 256 CU x 4 SIMD x 32 lanes/clk x 2 flops x 2.4 GHz
-TRANS_SLOTS = 4                 # a transcendental (exp2/log2/rcp) issues at a quarter of the fp32 FMA rate
-# FMA-equivalent VALU slots the method needs: per state update 4 fp32 ops (delta*A, delta*u*B,
-# the fade-and-add fma, the readout fma) + 1 exp; per (token, channel) softplus (exp, log + 2 ops),
-# delta*u, the D skip fma, SiLU (exp, rcp + 2 ops) and the gate multiply.
+# fp32 VALU issue peak without packed-fp32 instructions (this build disables them): 256 CUs x 4 SIMDs x 16 lanes
+# per clock x 2.4 GHz = 39.3e12 lane-ops/s, i.e. 78.6 TFLOP/s counting an FMA as 2 flops.  (The 157.3 TFLOP/s
+# datasheet figure needs v_pk_fma_f32, two fp32 FMAs per lane per instruction.)
+VALU_LANE_OPS_PEAK = 256 * 4 * 16 * 2.4e9
+VALU_PEAK_TFLOPS = 2 * VALU_LANE_OPS_PEAK / 1e12
+TRANS_SLOTS = 2                 # exp2/log2/rcp: a wave64 issues every ~8-9.6 clocks on a SIMD vs 4 for an fp32 FMA
+# VALU issue slots the method itself needs (FMA-equivalents).  Per state update: delta*A, the exp, delta*u*B
+# (delta*u is per channel), the fade-and-add fma, the readout fma.  Per (token, channel): bias add, softplus
+# (exp, log + 3 ops), delta*u, the D skip fma, SiLU (exp, rcp + 2 ops), the gate multiply.
 SLOTS_PER_UPDATE = 4 + 1 * TRANS_SLOTS
-SLOTS_PER_TOKEN_CHANNEL = 4 * TRANS_SLOTS + 7
+SLOTS_PER_TOKEN_CHANNEL = 4 * TRANS_SLOTS + 9
 
 
 def scan_bytes(w, with_final=True):
@@ -150,7 +154,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mamba2p8b_bf16", help="scan workload to time (default: the 2.8B layer)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -224,9 +228,9 @@ def main():
                    "workspace_bytes": need, "seed": 0, "wall_ms_per_step": wall_ms},
         "roofline": {"bound": "alu", "achieved": achieved_tf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved_tf / VALU_PEAK_TFLOPS, "traffic": traffic,
-                     "counted": f"FMA-equivalent fp32 VALU slots x 2 flops: {SLOTS_PER_UPDATE} per state update, "
-                                f"{SLOTS_PER_TOKEN_CHANNEL} per (token, channel); transcendental = "
-                                f"{TRANS_SLOTS} slots"},
+                     "counted": f"algorithmic fp32 VALU issue slots x 2 flops: {SLOTS_PER_UPDATE} per state update, "
+                                f"{SLOTS_PER_TOKEN_CHANNEL} per (token, channel), a transcendental = {TRANS_SLOTS} "
+                                f"slots; peak = non-packed fp32 issue rate"},
         "hbm": {"algorithmic_bytes": nbytes, "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved_gbs / HBM_PEAK_GBS},
     }

@@ -41,10 +41,12 @@
  *   - Work is enqueued on `stream` and the call returns at once; outputs are
  *     valid after the stream is synchronised.
  *   - Arguments are validated before any HIP call: a null required pointer,
- *     a size <= 0, an unknown dtype or a too-small workspace gives
- *     SSM_ERR_INVALID_ARG; a dstate outside 1..64, an odd dstate with bf16,
- *     or batch / chunk counts above 65535 give SSM_ERR_UNSUPPORTED.  Nothing
- *     is launched in either case.  A failed launch gives SSM_ERR_HIP.
+ *     a size <= 0, an unknown dtype, a pointer not aligned to its element
+ *     size, or a missing, too small or misaligned workspace gives
+ *     SSM_ERR_INVALID_ARG; a dstate above 64, a batch above 65535 or a token
+ *     row (dim * element size) above 16 MiB gives SSM_ERR_UNSUPPORTED.
+ *     Nothing is launched in either case.  A failed launch gives
+ *     SSM_ERR_HIP.
  *     Input values are not inspected (NaN in gives NaN out).
  */
 #ifndef SSM_SCAN_H
@@ -68,22 +70,24 @@ typedef enum {
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
 
-/* Bytes of device workspace that ssm_scan_fwd needs for this shape (0 when
- * the sequence is scanned in a single chunk).  The workspace holds, per
- * chunk of the sequence, the composed fade-and-add pair of that chunk and
- * the state carried into it ("The relay": squash each chunk to one pair,
- * combine the chunk pairs, pass the real states back).  Returns 0 for
- * arguments ssm_scan_fwd would reject. */
+/* Bytes of device workspace that ssm_scan_fwd needs for this shape (always
+ * > 0 for a valid shape).  The workspace holds B and C repacked as fp32
+ * records per group of states (about batch * L * 2 * dstate * 4 bytes) and,
+ * when the sequence is cut into chunks, the composed fade-and-add pair of
+ * every chunk and the state carried into it ("Mamba is attention all you
+ * really need, part 2", "The relay": squash each chunk to one pair, combine
+ * the chunk pairs, pass the real states back).  Returns 0 for arguments
+ * ssm_scan_fwd would reject. */
 size_t ssm_scan_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt);
 
 /* Selective scan over a whole sequence, starting from a zero state.
  *   Required: u, delta, A, B, C, y.  Optional (NULL allowed): D (no skip
  *   term), z (no gate), delta_bias (zero bias), final_state (not written).
  *   final_state receives h_L, the state after the last token (before the
- *   gate, which only touches y).  workspace may be NULL only when
- *   ssm_scan_workspace_size() returns 0; otherwise it must point at
- *   workspace_bytes >= that size of device memory, 256-byte aligned, which
- *   the call overwrites and which must not be shared with a concurrent call.
+ *   gate, which only touches y).  workspace must point at workspace_bytes >=
+ *   ssm_scan_workspace_size() bytes of device memory, 256-byte aligned,
+ *   which the call overwrites and which must not be shared with a
+ *   concurrent call.
  *   y must not alias any input. */
 ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                           const float* D, const void* z, const float* delta_bias, int softplus_flag,

@@ -172,7 +172,6 @@ ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, c
   if (!aligned(A, 4) || (D && !aligned(D, 4)) || (bias && !aligned(bias, 4)) || (fs && !aligned(fs, 4)))
     return SSM_ERR_INVALID_ARG;
   if (dstate > 64) return SSM_ERR_UNSUPPORTED;
-  if (dt == SSM_DTYPE_BF16 && (dstate & 1)) return SSM_ERR_UNSUPPORTED;
   if (batch > kMaxBatch) return SSM_ERR_UNSUPPORTED;
   return SSM_OK;
 }
@@ -255,7 +254,6 @@ using namespace ssm;
 extern "C" size_t ssm_scan_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt) {
   if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 64 || batch > kMaxBatch) return 0;
   if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return 0;
-  if (dt == SSM_DTYPE_BF16 && (dstate & 1)) return 0;
   // The packed layout depends only on the variant, which the pointers do not
   // change; size it for the widest and the narrowest prologue anyway.
   Plan p4, p1;

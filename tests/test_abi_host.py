@@ -62,7 +62,8 @@ def test_workspace_size():
     # rejected shapes report 0
     assert L.ssm_scan_workspace_size(0, 10, 10, 16, F32) == 0
     assert L.ssm_scan_workspace_size(1, 10, 10, 65, F32) == 0
-    assert L.ssm_scan_workspace_size(1, 10, 10, 15, BF16) == 0
+    assert L.ssm_scan_workspace_size(1, 10, 10, 15, BF16) > 0       # odd dstate is fine with bf16
+    assert L.ssm_scan_workspace_size(1, 10, 9_000_000, 16, BF16) == 0  # a token row over 16 MiB
     assert L.ssm_scan_workspace_size(1, 10, 10, 16, 7) == 0
 
 
@@ -83,7 +84,8 @@ def _scan(lib_, **kw):
     (dict(dt=5), INVALID),
     (dict(u=0x1001), INVALID), (dict(B=0x4002), INVALID), (dict(fs=0x7002), INVALID),
     (dict(dt=BF16, u=0x1001), INVALID),
-    (dict(N=65), UNSUPPORTED), (dict(N=15, dt=BF16), UNSUPPORTED), (dict(batch=70000), UNSUPPORTED),
+    (dict(N=65), UNSUPPORTED), (dict(batch=70000), UNSUPPORTED),
+    (dict(dim=9_000_000, dt=BF16), UNSUPPORTED),  # a token row over 16 MiB
     # missing / too small workspace
     (dict(batch=1, L=8, dim=8, N=16), INVALID),
     (dict(batch=1, L=1 << 20, dim=64, N=16), INVALID),

@@ -106,7 +106,8 @@ def test_every_variant_and_chunking(npl, G, K, dtype):
 
 
 @pytest.mark.parametrize("dtype,N", [("f32", 1), ("f32", 3), ("f32", 4), ("bf16", 2), ("bf16", 6), ("f32", 8),
-                                     ("bf16", 10), ("bf16", 32), ("f32", 64), ("bf16", 64)])
+                                     ("bf16", 10), ("bf16", 32), ("f32", 64), ("bf16", 64), ("bf16", 15),
+                                     ("bf16", 1)])
 @pytest.mark.parametrize("K", [1, 4])
 def test_other_state_sizes(dtype, N, K):
     rng = np.random.default_rng(N * 7 + K)
@@ -207,7 +208,7 @@ def test_decode_continues_scan(dtype):
     assert rel_err(yd.float().cpu().numpy(), y_full[:, L]) <= TOL[dtype]
 
 
-@pytest.mark.parametrize("dtype,N", [("bf16", 16), ("f32", 16), ("f32", 3), ("bf16", 64), ("f32", 1)])
+@pytest.mark.parametrize("dtype,N", [("bf16", 16), ("f32", 16), ("f32", 3), ("bf16", 64), ("f32", 1), ("bf16", 15)])
 def test_decode_small_against_oracle(dtype, N):
     rng = np.random.default_rng(35 + N)
     batch, dim = 5, 77
