@@ -114,27 +114,55 @@ constexpr int kTrip = kRing * kTB;
 constexpr int kWaitLgkm0 = 0xC07F;
 
 // Pack B and C ([batch][L][N], fp32 or bf16) into fp32 per-group records
-// [batch][G][Lp][2*NPL]; states n >= N and tokens t >= L are zero.
-template <class IO>
+// [batch][G][Lp][2*NPL]; states n >= N and tokens t >= L are zero.  A
+// workgroup transposes kPackT tokens through LDS: the token rows are read
+// contiguously (one element per thread), the records written contiguously
+// (one record per thread, vector stores).
+constexpr int kPackT = 16;
+
+template <class IO, int NPL>
 __global__ void __launch_bounds__(256) pack_bc_kernel(const void* __restrict__ B, const void* __restrict__ C,
                                                      float* __restrict__ bc, int64_t batch, int64_t L, int64_t Lp,
-                                                     int64_t N, int npl, int G) {
-  const int64_t Npad = static_cast<int64_t>(npl) * G;
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= batch * Lp * Npad) return;
-  const int64_t n = i % Npad;
-  const int64_t t = (i / Npad) % Lp;
-  const int64_t b = i / (Npad * Lp);
-  const bool ok = t < L && n < N;
-  const float vb = ok ? load_elem<IO>(B, (b * L + t) * N + n) : 0.0f;
-  const float vc = ok ? load_elem<IO>(C, (b * L + t) * N + n) : 0.0f;
-  const int64_t g = n / npl, j = n % npl;
-  const int64_t o = ((b * G + g) * Lp + t) * (2 * npl);
-  bc[o + j] = vb;
-  bc[o + npl + j] = vc;
+                                                     int64_t N, int G) {
+  __shared__ float sB[kPackT * 64], sC[kPackT * 64];
+  const int Npad = NPL * G;  // <= 64
+  const int64_t nblk = Lp / kPackT;
+  const int64_t b = blockIdx.x / nblk;
+  const int64_t t0 = (blockIdx.x % nblk) * kPackT;
+  for (int e = threadIdx.x; e < kPackT * Npad; e += 256) {
+    const int tt = e / Npad, n = e % Npad;
+    const int64_t t = t0 + tt;
+    const bool ok = t < L && n < N;
+    sB[e] = ok ? load_elem<IO>(B, (b * L + t) * N + n) : 0.0f;
+    sC[e] = ok ? load_elem<IO>(C, (b * L + t) * N + n) : 0.0f;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < G * kPackT; q += 256) {
+    const int g = q / kPackT, tt = q % kPackT;
+    float rec[2 * NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      rec[j] = sB[tt * Npad + g * NPL + j];
+      rec[NPL + j] = sC[tt * Npad + g * NPL + j];
+    }
+    float* out = bc + ((b * G + g) * Lp + t0 + tt) * (2 * NPL);
+    if constexpr (NPL == 1) {
+      *reinterpret_cast<float2*>(out) = make_float2(rec[0], rec[1]);
+    } else {
+#pragma unroll
+      for (int v = 0; v < NPL / 2; ++v)
+        reinterpret_cast<float4*>(out)[v] = make_float4(rec[4 * v], rec[4 * v + 1], rec[4 * v + 2], rec[4 * v + 3]);
+    }
+  }
 }
 
-template <class IO, int NPL, int G, int VW, bool FULL>
+// TOUCH: also read one word per 128-byte line of each upcoming block's packed
+// B/C records with the vector loads of the ring, so that the wavefronts'
+// scalar loads of those records hit in L2.  That pays off when a CU holds a
+// single workgroup (latency exposed) or the records stream from HBM (long
+// sequences cut into chunks); with two workgroups per CU and L2-resident
+// records it only adds issue work, so the planner turns it off there.
+template <class IO, int NPL, int G, int VW, bool FULL, bool TOUCH>
 __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   constexpr int NPAD = NPL * G;
   constexpr int TB = BlockShape<G, VW>::TB;
@@ -216,6 +244,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     Dv[e] = (pvalid && p.D) ? p.D[pd + e] : 0.0f;
   }
   const bool has_z = FULL && p.z != nullptr;
+  const bool softplus_on = p.softplus != 0;
 
   // Token rows of u, delta_raw, z, y are reached through buffer resources
   // covering (b, t_begin, d0) up to the end of the chunk's last row, so rows
@@ -235,10 +264,20 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 
   // Raw u, delta_raw, z of kRing blocks (slot = block % kRing).
   Raw<IO, VW> ru[kRing][RPT], rd[kRing][RPT], rz[kRing][RPT];
+  // L2 touch of the wavefront's group records (one float per 128-byte line);
+  // the records run on for kTB rows of padding past Lp.
+  constexpr int kRecBlk = TB * 2 * NPL;  // record floats per block and group
+  float touch[kRing];
+  const float* touch_row = bc_row + (lane * 32) % kRecBlk;
+  const int64_t touch_lim = (p.Lp - t_begin) * 2 * NPL;
 
   auto issue_loads = [&](auto slotc, int blk) {
     constexpr int S = decltype(slotc)::value;
     const int bo = blk * blk_bytes;
+    if constexpr (TOUCH) {
+      const int64_t off = static_cast<int64_t>(blk) * kRecBlk;
+      touch[S] = (off + kRecBlk <= touch_lim) ? touch_row[off] : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       ru[S][i] = buf_load<IO, VW>(rs_u, voff[i] + bo, 0);
@@ -254,6 +293,9 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   auto prologue = [&](auto parc, auto slotc, int blk) {
     constexpr int P = decltype(parc)::value;
     constexpr int S = decltype(slotc)::value;
+    // the touched word is not needed; consuming it here (where the slot's
+    // loads are complete anyway) keeps the load alive at no cost
+    if constexpr (TOUCH) asm volatile("" ::"v"(touch[S]));
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = prow + i * ROWSTEP;
@@ -265,7 +307,10 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
         const float x = df[e] + biasv[e];
-        float dl = p.softplus ? softplus_f(x) : x;
+        // softplus is evaluated either way and selected, so no branch splits
+        // the loop body (the flag is uniform, the select is one v_cndmask)
+        float dl = softplus_f(x);
+        dl = softplus_on ? dl : x;
         dl = live ? dl : 0.0f;  // padding token: the identity step (1, 0)
         out[e] = make_float2(dl, dl * uf[e]);
       }
@@ -335,6 +380,11 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
       h[j] = __builtin_fmaf(a, h[j], dd.y * r[j]);
       if (FULL) yp = __builtin_fmaf(r[NPL + j], h[j], yp);
+      // Without the readout store nothing ties the update to its token's
+      // group: the optimiser would sink a whole block of updates below all
+      // of its record fetches and spill the records.  An empty asm with h as
+      // an in/out operand keeps each update where it is written.
+      if (!FULL) asm volatile("" : "+v"(h[j]));
     }
     if (FULL) sY[FULL ? P : 0][w][tt][lane] = yp;
     else block_delta += dd.x;
@@ -427,19 +477,50 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 }
 
 // State entering each chunk of a split tile: carry_{c+1} = P_c * carry_c + S_c,
-// carry_0 = 0.  One thread per (split tile, lane channel, state); the chunk
-// pairs are composed in order.  Layout [n_split][Ks][64][Npad].
+// carry_0 = 0, for every column (lane channel, state) of the tile; layout
+// [n_split][Ks][64][Npad].  The Ks-1 pairs of a column are cut into kCarryRuns
+// runs: each thread composes one run of one column into a single pair, the
+// runs' pairs are combined in order through LDS, and each thread walks its
+// run again from the state entering it, writing the carries.  A workgroup
+// holds kCarryRuns runs of 256 / kCarryRuns columns.
+constexpr int kCarryRuns = 32;
+constexpr int kCarryCols = 256 / kCarryRuns;
+
 __global__ void __launch_bounds__(256) carry_kernel(const float* __restrict__ P, const float* __restrict__ S,
                                                    float* __restrict__ carry, int64_t n_split, int Ks, int64_t Npad) {
-  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  __shared__ float sP[kCarryRuns][kCarryCols], sS[kCarryRuns][kCarryCols];
+  const int run = threadIdx.x / kCarryCols;
+  const int cl = threadIdx.x % kCarryCols;
   const int64_t per_tile = 64 * Npad;
-  if (i >= n_split * per_tile) return;
-  const int64_t st = i / per_tile, r = i % per_tile;
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * kCarryCols + cl;  // over n_split * per_tile
+  const bool ok = col < n_split * per_tile;
+  const int64_t st = ok ? col / per_tile : 0, r = col % per_tile;
+  const int npairs = Ks - 1;
+  const int len = (npairs + kCarryRuns - 1) / kCarryRuns;
+  const int c0 = run * len;
+  const int c1 = (c0 + len < npairs) ? c0 + len : npairs;
+  auto at = [&](int cc) { return (st * Ks + cc) * per_tile + r; };
+  // this run's pair: (a, b) composed over chunks c0 .. c1-1, in order
+  float a = 1.0f, bb = 0.0f;
+  if (ok) {
+#pragma unroll 8
+    for (int cc = c0; cc < c1; ++cc) {
+      const float pc = P[at(cc)];
+      a *= pc;
+      bb = __builtin_fmaf(pc, bb, S[at(cc)]);
+    }
+  }
+  sP[run][cl] = a;
+  sS[run][cl] = bb;
+  __syncthreads();
+  // state entering this run: the runs before it, composed in order
   float h = 0.0f;
-  for (int cc = 0; cc + 1 < Ks; ++cc) {
-    const int64_t idx = (st * Ks + cc) * per_tile + r;
-    h = __builtin_fmaf(P[idx], h, S[idx]);
-    carry[idx + per_tile] = h;
+  for (int q = 0; q < run; ++q) h = __builtin_fmaf(sP[q][cl], h, sS[q][cl]);
+  if (!ok) return;
+#pragma unroll 8
+  for (int cc = c0; cc < c1; ++cc) {
+    h = __builtin_fmaf(P[at(cc)], h, S[at(cc)]);
+    carry[at(cc + 1)] = h;
   }
 }
 

@@ -47,6 +47,7 @@ struct Plan {
   int Ks;        // chunks per split tile
   int64_t chunk_len;
   int64_t Lp;    // sequence length rounded up to whole token blocks (packed B/C rows)
+  bool touch;    // L2 touch of upcoming B/C records (scan_kernel's TOUCH)
 };
 
 // Workspace layout: [packed B/C][chunk fades P][chunk states S][carried-in states].
@@ -157,6 +158,11 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
   pl->Ks = static_cast<int>(K);
   pl->chunk_len = chunk;
   pl->Lp = ceil_div(L, kTrip) * kTrip;
+  // With fewer tiles than CUs a CU holds one workgroup and the scalar loads'
+  // latency is exposed (or the records stream from HBM): touch them into L2.
+  pl->touch = T < kNumCU;
+  const char* te = getenv("SSM_SCAN_TOUCH");  // tuning override: "0" or "1"
+  if (te && (te[0] == '0' || te[0] == '1')) pl->touch = te[0] == '1';
 }
 
 ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -177,14 +183,20 @@ ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, c
 }
 
 template <class IO, bool FULL>
-hipError_t launch_scan(int npl, int G, int vw, const ScanParams& p, dim3 grid, hipStream_t s) {
+hipError_t launch_scan(int npl, int G, int vw, bool touch, const ScanParams& p, dim3 grid, hipStream_t s) {
+#define SSM_SCAN_LAUNCH(NPL_, G_, VW_)                                                                     \
+  if (touch)                                                                                             \
+    hipLaunchKernelGGL((scan_kernel<IO, NPL_, G_, VW_, FULL, true>), grid, dim3(64 * G_), 0, s, p);       \
+  else                                                                                                   \
+    hipLaunchKernelGGL((scan_kernel<IO, NPL_, G_, VW_, FULL, false>), grid, dim3(64 * G_), 0, s, p);
 #define SSM_SCAN_CASE(NPL_, G_)                                                                            \
   if (npl == NPL_ && G == G_) {                                                                          \
     constexpr int VWP = (G_ <= 4) ? 4 : ((G_ == 8) ? 2 : 1);                                             \
-    if (vw == VWP)                                                                                       \
-      hipLaunchKernelGGL((scan_kernel<IO, NPL_, G_, VWP, FULL>), grid, dim3(64 * G_), 0, s, p);           \
-    else                                                                                                 \
-      hipLaunchKernelGGL((scan_kernel<IO, NPL_, G_, 1, FULL>), grid, dim3(64 * G_), 0, s, p);             \
+    if (vw == VWP) {                                                                                     \
+      SSM_SCAN_LAUNCH(NPL_, G_, VWP)                                                                     \
+    } else {                                                                                             \
+      SSM_SCAN_LAUNCH(NPL_, G_, 1)                                                                       \
+    }                                                                                                    \
     return hipGetLastError();                                                                            \
   }
   SSM_SCAN_CASE(4, 1)
@@ -197,30 +209,39 @@ hipError_t launch_scan(int npl, int G, int vw, const ScanParams& p, dim3 grid, h
   SSM_SCAN_CASE(8, 2)
   SSM_SCAN_CASE(16, 1)
 #undef SSM_SCAN_CASE
+#undef SSM_SCAN_LAUNCH
   return hipErrorInvalidValue;
 }
 
 template <class IO>
 hipError_t run_scan(const Plan& pl, const void* B, const void* C, float* bc, ScanParams p, hipStream_t s) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
-  const int64_t packed = p.batch * pl.Lp * npad;
-  hipLaunchKernelGGL(pack_bc_kernel<IO>, dim3(static_cast<unsigned>(ceil_div(packed, 256))), dim3(256), 0, s, B,
-                     C, bc, p.batch, p.L, pl.Lp, p.N, pl.npl, pl.G);
+  const dim3 pgrid(static_cast<unsigned>(p.batch * (pl.Lp / kPackT)));
+#define SSM_PACK_CASE(NPL_)                                                                                  \
+  if (pl.npl == NPL_)                                                                                       \
+    hipLaunchKernelGGL((pack_bc_kernel<IO, NPL_>), pgrid, dim3(256), 0, s, B, C, bc, p.batch, p.L, pl.Lp, p.N, \
+                       pl.G);
+  SSM_PACK_CASE(1)
+  SSM_PACK_CASE(2)
+  SSM_PACK_CASE(4)
+  SSM_PACK_CASE(8)
+  SSM_PACK_CASE(16)
+#undef SSM_PACK_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (pl.n_split > 0 && pl.Ks > 1) {
     const dim3 grid_agg(static_cast<unsigned>(static_cast<int64_t>(pl.n_split) * (pl.Ks - 1)));
-    e = launch_scan<IO, false>(pl.npl, pl.G, pl.vw, p, grid_agg, s);
+    e = launch_scan<IO, false>(pl.npl, pl.G, pl.vw, pl.touch, p, grid_agg, s);
     if (e != hipSuccess) return e;
-    const int64_t threads = static_cast<int64_t>(pl.n_split) * 64 * npad;
-    hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>(ceil_div(threads, 256))), dim3(256), 0, s,
+    const int64_t cols = static_cast<int64_t>(pl.n_split) * 64 * npad;
+    hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>(ceil_div(cols, kCarryCols))), dim3(256), 0, s,
                        static_cast<const float*>(p.aggP), static_cast<const float*>(p.aggS), p.carry,
                        static_cast<int64_t>(pl.n_split), pl.Ks, npad);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const dim3 grid_full(static_cast<unsigned>(pl.n_long + static_cast<int64_t>(pl.n_split) * pl.Ks));
-  return launch_scan<IO, true>(pl.npl, pl.G, pl.vw, p, grid_full, s);
+  return launch_scan<IO, true>(pl.npl, pl.G, pl.vw, pl.touch, p, grid_full, s);
 }
 
 template <class IO>
@@ -286,7 +307,8 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
   if (max_chunk_len(dim, static_cast<int64_t>(es)) < kChunkQuantum) return SSM_ERR_UNSUPPORTED;
   Plan pl;
   plan_scan(batch, L, dim, dstate, static_cast<int64_t>(es), vw_ok, &pl);
-  if (static_cast<int64_t>(pl.n_long) + static_cast<int64_t>(pl.n_split) * pl.Ks > 0x7fffffffLL)
+  if (static_cast<int64_t>(pl.n_long) + static_cast<int64_t>(pl.n_split) * pl.Ks > 0x7fffffffLL ||
+      batch * (pl.Lp / kPackT) > 0x7fffffffLL)
     return SSM_ERR_UNSUPPORTED;
   const Layout lay = layout_for(pl, batch);
   if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256)) return SSM_ERR_INVALID_ARG;

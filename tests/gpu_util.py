@@ -105,18 +105,30 @@ def sample_channels(rng, batch, dim, count):
     return [(int(f // dim), int(f % dim)) for f in flat]
 
 
-class Variant:
-    """Temporarily force a launch variant (states per lane, wavefronts, chunks) through the library's override."""
-
-    def __init__(self, npl, G, K=0):
-        self.value = f"{npl},{G},{K}"
+class _Env:
+    def __init__(self, name, value):
+        self.name, self.value = name, value
 
     def __enter__(self):
-        self.old = os.environ.get("SSM_SCAN_VARIANT")
-        os.environ["SSM_SCAN_VARIANT"] = self.value
+        self.old = os.environ.get(self.name)
+        os.environ[self.name] = self.value
 
     def __exit__(self, *a):
         if self.old is None:
-            os.environ.pop("SSM_SCAN_VARIANT", None)
+            os.environ.pop(self.name, None)
         else:
-            os.environ["SSM_SCAN_VARIANT"] = self.old
+            os.environ[self.name] = self.old
+
+
+class Variant(_Env):
+    """Temporarily force a launch variant (states per lane, wavefronts, chunks) through the library's override."""
+
+    def __init__(self, npl, G, K=0):
+        super().__init__("SSM_SCAN_VARIANT", f"{npl},{G},{K}")
+
+
+class Touch(_Env):
+    """Temporarily force the L2 touch of upcoming B/C records on (True) or off (False)."""
+
+    def __init__(self, on):
+        super().__init__("SSM_SCAN_TOUCH", "1" if on else "0")
