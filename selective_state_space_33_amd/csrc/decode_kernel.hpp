@@ -94,4 +94,95 @@ __global__ void __launch_bounds__(256) state_update_kernel(DecodeParams p) {
   }
 }
 
+// Vector path (dstate % 4 == 0, 16-byte aligned state and A, B/C rows aligned
+// to 4 elements).  A thread owns one (channel d, group of 4 states) for R
+// batch rows: A, bias and D are read once and reused, the R state quads are
+// all in flight before any is used, and B_b/C_b come in as one 4-element
+// vector load each.  Consecutive threads take consecutive state quads, so a
+// wavefront reads and writes 1 KB of contiguous state per batch row.
+template <class IO> struct Vec4In;
+template <> struct Vec4In<F32> {
+  static __device__ __forceinline__ void load(const void* base, int64_t idx, float* o) {
+    const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(base) + idx);
+    o[0] = v.x; o[1] = v.y; o[2] = v.z; o[3] = v.w;
+  }
+};
+template <> struct Vec4In<BF16> {
+  static __device__ __forceinline__ void load(const void* base, int64_t idx, float* o) {
+    const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(base) + idx);
+    o[0] = bf16_lo(v.x); o[1] = bf16_hi(v.x); o[2] = bf16_lo(v.y); o[3] = bf16_hi(v.y);
+  }
+};
+
+template <class IO, int NQ, int R>
+__global__ void __launch_bounds__(256) state_update_vec_kernel(DecodeParams p) {
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int q = static_cast<int>(gid & (NQ - 1));
+  const int64_t dq = gid / NQ;
+  const int64_t dim = p.dim, N = p.N;
+  const int64_t nbg = (p.batch + R - 1) / R;
+  const bool valid = dq < dim * nbg;
+  const int64_t d = valid ? dq % dim : 0;
+  const int64_t b0 = valid ? (dq / dim) * R : 0;
+  const int n0 = 4 * q;
+  const bool qok = valid && n0 < N;
+
+  float A2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (qok) {
+    const float4 av = *reinterpret_cast<const float4*>(p.A + d * N + n0);
+    A2[0] = av.x * kLog2e; A2[1] = av.y * kLog2e; A2[2] = av.z * kLog2e; A2[3] = av.w * kLog2e;
+  }
+  const float bias = (valid && p.bias) ? p.bias[d] : 0.0f;
+  const float Dd = (valid && p.D) ? p.D[d] : 0.0f;
+
+  float h[R][4], Bv[R][4], Cv[R][4], uu[R], xr[R], zz[R];
+  bool ok[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t b = b0 + r;
+    ok[r] = qok && b < p.batch;
+    const bool cok = valid && b < p.batch;  // channel-level values (all NQ lanes need them)
+    if (ok[r]) {
+      const float4 hv = *reinterpret_cast<const float4*>(p.state + (b * dim + d) * N + n0);
+      h[r][0] = hv.x; h[r][1] = hv.y; h[r][2] = hv.z; h[r][3] = hv.w;
+      Vec4In<IO>::load(p.B, b * N + n0, Bv[r]);
+      Vec4In<IO>::load(p.C, b * N + n0, Cv[r]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) h[r][j] = Bv[r][j] = Cv[r][j] = 0.0f;
+    }
+    uu[r] = cok ? load_elem<IO>(p.u, b * dim + d) : 0.0f;
+    xr[r] = cok ? load_elem<IO>(p.delta, b * dim + d) : 0.0f;
+    zz[r] = (cok && p.z) ? load_elem<IO>(p.z, b * dim + d) : 0.0f;
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t b = b0 + r;
+    const float x = xr[r] + bias;
+    float dl = softplus_f(x);
+    dl = p.softplus ? dl : x;
+    const float du = dl * uu[r];
+    float yp = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float a = __builtin_amdgcn_exp2f(dl * A2[j]);
+      h[r][j] = __builtin_fmaf(a, h[r][j], du * Bv[r][j]);
+      yp = __builtin_fmaf(Cv[r][j], h[r][j], yp);
+    }
+    if (ok[r])
+      *reinterpret_cast<float4*>(p.state + (b * dim + d) * N + n0) = make_float4(h[r][0], h[r][1], h[r][2], h[r][3]);
+#pragma unroll
+    for (int off = 1; off < NQ; off <<= 1) yp += __shfl_xor(yp, off, NQ);
+    if (valid && b < p.batch && q == 0) {
+      float v = __builtin_fmaf(Dd, uu[r], yp);
+      if (p.z) v *= silu_f(zz[r]);
+      if constexpr (__is_same(IO, F32)) {
+        static_cast<float*>(p.y)[b * dim + d] = v;
+      } else {
+        static_cast<uint16_t*>(p.y)[b * dim + d] = to_bf16(v);
+      }
+    }
+  }
+}
+
 }  // namespace ssm

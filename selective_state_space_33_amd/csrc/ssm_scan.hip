@@ -247,7 +247,31 @@ hipError_t run_scan(const Plan& pl, const void* B, const void* C, float* bc, Sca
 template <class IO>
 hipError_t run_decode(const DecodeParams& p, hipStream_t s) {
   const int nq = next_pow2(ceil_div(p.N, 4));
+  const size_t es = __is_same(IO, F32) ? 4 : 2;
   const bool vec4 = (p.N % 4) == 0 && aligned(p.state, 16) && aligned(p.A, 16);
+  if (vec4 && aligned(p.B, 4 * es) && aligned(p.C, 4 * es)) {
+    // R batch rows per thread: A, bias and D are then read once per R rows.
+    const int R = p.batch >= 4 ? 4 : (p.batch >= 2 ? 2 : 1);
+    const int64_t threads = ceil_div(p.batch, R) * p.dim * nq;
+    const dim3 grid(static_cast<unsigned>(ceil_div(threads, 256)));
+#define SSM_DECV_CASE(NQ_)                                                                         \
+  if (nq == NQ_) {                                                                                 \
+    if (R == 4)                                                                                    \
+      hipLaunchKernelGGL((state_update_vec_kernel<IO, NQ_, 4>), grid, dim3(256), 0, s, p);         \
+    else if (R == 2)                                                                               \
+      hipLaunchKernelGGL((state_update_vec_kernel<IO, NQ_, 2>), grid, dim3(256), 0, s, p);         \
+    else                                                                                           \
+      hipLaunchKernelGGL((state_update_vec_kernel<IO, NQ_, 1>), grid, dim3(256), 0, s, p);         \
+    return hipGetLastError();                                                                      \
+  }
+    SSM_DECV_CASE(1)
+    SSM_DECV_CASE(2)
+    SSM_DECV_CASE(4)
+    SSM_DECV_CASE(8)
+    SSM_DECV_CASE(16)
+#undef SSM_DECV_CASE
+    return hipErrorInvalidValue;
+  }
   const int64_t threads = p.batch * p.dim * nq;
   const dim3 grid(static_cast<unsigned>(ceil_div(threads, 256)));
 #define SSM_DEC_CASE(NQ_)                                                                         \
