@@ -5,14 +5,16 @@ All HIP code is compiled with packed-fp32 instructions disabled
 operations, transcendentals through the hardware exp2/log2/rcp instructions,
 and bf16 conversions through v_cvt_pk_bf16_f32.
 """
+import glob
 import os
 import shutil
 import subprocess
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libssmscan.so")
-SRC = os.path.join(HERE, "csrc", "ssm_scan.hip")
+CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
 
@@ -30,9 +32,7 @@ def compile_flags():
             "-I", INCLUDE, "-I", os.path.join(HERE, "csrc")]
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [hipcc_path(), *compile_flags(), *extra, "-shared", "-o", tmp, SRC]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -40,9 +40,25 @@ def build(verbose: bool = False, extra=()) -> str:
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
     if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
+        raise RuntimeError("hipcc failed:\n" + " ".join(cmd) + "\n" + err)
     if verbose and err.strip():
         print(err)
+
+
+def build(verbose: bool = False, extra=(), jobs: int = 0) -> str:
+    """Compile every csrc/*.hip to an object (in parallel) and link libssmscan.so."""
+    sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    hipcc = hipcc_path()
+    jobs = jobs or max(1, min(len(sources), os.cpu_count() or 1))
+    objs = [os.path.join(objdir, os.path.basename(src)[:-4] + ".o") for src in sources]
+    cmds = [[hipcc, *compile_flags(), *extra, "-c", "-o", obj, src] for src, obj in zip(sources, objs)]
+    with ThreadPoolExecutor(max_workers=jobs) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -1,0 +1,60 @@
+// carry_kernel.hpp -- composition of chunk pairs into carried-in states, for
+// tiles cut into many chunks ("Mamba is attention all you really need, part
+// 2", "The relay": combine the chunk pairs in order, pass the real states
+// back).  Included by ssm_scan.hip only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+// State entering each chunk of a split tile: carry_{c+1} = P_c * carry_c + S_c,
+// carry_0 = 0, for every column (lane channel, state) of the tile; layout
+// [n_split][Ks][64][Npad].  The Ks-1 pairs of a column are cut into kCarryRuns
+// runs: each thread composes one run of one column into a single pair, the
+// runs' pairs are combined in order through LDS, and each thread walks its
+// run again from the state entering it, writing the carries.  A workgroup
+// holds kCarryRuns runs of 256 / kCarryRuns columns.
+constexpr int kCarryRuns = 32;
+constexpr int kCarryCols = 256 / kCarryRuns;
+
+__global__ void __launch_bounds__(256) carry_kernel(const float* __restrict__ P, const float* __restrict__ S,
+                                                   float* __restrict__ carry, int64_t n_split, int Ks, int64_t Npad) {
+  __shared__ float sP[kCarryRuns][kCarryCols], sS[kCarryRuns][kCarryCols];
+  const int run = threadIdx.x / kCarryCols;
+  const int cl = threadIdx.x % kCarryCols;
+  const int64_t per_tile = 64 * Npad;
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * kCarryCols + cl;  // over n_split * per_tile
+  const bool ok = col < n_split * per_tile;
+  const int64_t st = ok ? col / per_tile : 0, r = col % per_tile;
+  const int npairs = Ks - 1;
+  const int len = (npairs + kCarryRuns - 1) / kCarryRuns;
+  const int c0 = run * len;
+  const int c1 = (c0 + len < npairs) ? c0 + len : npairs;
+  auto at = [&](int cc) { return (st * Ks + cc) * per_tile + r; };
+  // this run's pair: (a, b) composed over chunks c0 .. c1-1, in order
+  float a = 1.0f, bb = 0.0f;
+  if (ok) {
+#pragma unroll 8
+    for (int cc = c0; cc < c1; ++cc) {
+      const float pc = P[at(cc)];
+      a *= pc;
+      bb = __builtin_fmaf(pc, bb, S[at(cc)]);
+    }
+  }
+  sP[run][cl] = a;
+  sS[run][cl] = bb;
+  __syncthreads();
+  // state entering this run: the runs before it, composed in order
+  float h = 0.0f;
+  for (int q = 0; q < run; ++q) h = __builtin_fmaf(sP[q][cl], h, sS[q][cl]);
+  if (!ok) return;
+#pragma unroll 8
+  for (int cc = c0; cc < c1; ++cc) {
+    h = __builtin_fmaf(P[at(cc)], h, S[at(cc)]);
+    carry[at(cc + 1)] = h;
+  }
+}
+
+}  // namespace ssm

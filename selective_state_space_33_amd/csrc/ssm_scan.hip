@@ -13,8 +13,9 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include "carry_kernel.hpp"
 #include "decode_kernel.hpp"
-#include "scan_kernels.hpp"
+#include "scan_launch.hpp"
 
 namespace ssm {
 namespace {
@@ -24,6 +25,7 @@ constexpr int64_t kChunkQuantum = kTrip;  // chunk lengths are multiples of the 
 constexpr int64_t kMinChunk = 256;        // never cut the sequence finer than this
 constexpr int64_t kNumCU = 256;           // MI355X compute units: the work is balanced over these
 constexpr int64_t kMaxChunks = 4096;      // chunks per split tile
+constexpr int64_t kMaxChained = 8;        // chunks per tile in a chained launch (the carry hops in series)
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -48,24 +50,37 @@ struct Plan {
   int64_t chunk_len;
   int64_t Lp;    // sequence length rounded up to whole token blocks (packed B/C rows)
   bool touch;    // L2 touch of upcoming B/C records (scan_kernel's TOUCH)
+  bool chained;  // split tiles chain their carries inside the one scan launch
 };
 
-// Workspace layout: [packed B/C][chunk fades P][chunk states S][carried-in states].
+// Workspace layout: [packed B/C][chunk fades P][chunk states S][carried-in
+// states][flags, ticket, status].  The chained plan needs no P, S; the others
+// no flags.
 struct Layout {
-  size_t bc, agg, total;
+  size_t bc, pairs, carry, words, total;
+  int n_words;
 };
 
 Layout layout_for(const Plan& pl, int64_t batch) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
+  const size_t per = static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float);
   Layout l;
   l.bc = align256((static_cast<size_t>(batch) * pl.Lp + kTB) * 2 * npad * sizeof(float));
-  l.agg = pl.n_split > 0 ? align256(static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float)) : 0;
-  l.total = l.bc + 3 * l.agg;
+  l.pairs = (pl.n_split > 0 && !pl.chained) ? align256(per) : 0;
+  l.carry = pl.n_split > 0 ? align256(per) : 0;
+  l.n_words = pl.chained ? pl.n_split * pl.Ks + 3 + kCuSlots : 0;
+  l.words = align256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
+  l.total = l.bc + 2 * l.pairs + l.carry + l.words;
   return l;
 }
 
-// Optional override for tuning experiments: SSM_SCAN_VARIANT="npl,G[,K]".
-// K > 0 cuts every tile into K chunks; K = 0 (or absent) keeps the planner's split.
+// Optional overrides for tuning experiments and tests:
+//   SSM_SCAN_VARIANT="npl,G[,K]"  K > 0 cuts every tile into K chunks; K = 0
+//                                 (or absent) keeps the planner's split;
+//   SSM_SCAN_CHAINED=0|1          chunks chain their carries in the scan launch
+//                                 (1) or go through the pair and carry passes (0);
+//   SSM_SCAN_TOUCH=0|1            L2 touch of upcoming B/C records;
+//   SSM_SCAN_CHAIN_K=k            chunks per left-over tile in a chained plan.
 bool env_variant(int* npl, int* G, int* K) {
   const char* s = getenv("SSM_SCAN_VARIANT");
   if (!s || !*s) return false;
@@ -77,15 +92,6 @@ bool env_variant(int* npl, int* G, int* K) {
   *K = (n >= 3) ? k : 0;
   return true;
 }
-
-// Kernel variants (states per lane, wavefronts).  Each exists with its
-// preferred prologue width (channels per thread: 4 up to 4 wavefronts, 2 for
-// 8, 1 for 16) and with width 1.
-bool variant_exists(int npl, int G) {
-  if (npl == 4 && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16)) return true;
-  return (npl == 2 && G == 8) || (npl == 1 && G == 16) || (npl == 8 && G == 2) || (npl == 16 && G == 1);
-}
-int preferred_vw(int G) { return G <= 4 ? 4 : (G == 8 ? 2 : 1); }
 
 // The generic variant for a state size: 4 states per lane, a power of two of wavefronts.
 void generic_variant(int64_t N, int* npl, int* G) {
@@ -100,13 +106,25 @@ int64_t max_chunk_len(int64_t dim, int64_t es) {
   return (0x7fffffffLL / (dim * es) - kTrip) / kTrip * kTrip;
 }
 
+int env_flag(const char* name) {  // -1 when unset
+  const char* v = getenv(name);
+  return (v && (v[0] == '0' || v[0] == '1')) ? v[0] - '0' : -1;
+}
+
 // Work plan.  A tile (64 channels of one batch row) scanned whole costs one
-// pass over L tokens; cutting it into chunks adds an aggregate pass over all
-// but its last chunk (about four fifths of the cost per token), so tiles are
-// only cut when there are too few of them to keep the GPU busy: with at least
-// 3/4 as many tiles as CUs every tile runs whole; otherwise every tile is cut
-// so that each CU gets about two chunks (two workgroups of the 16-state
-// variant fit on a CU).
+// pass over L tokens; cutting it into chunks adds a pass computing each
+// chunk's pair over all but the last chunk (about as costly per token as the
+// scan itself), so tiles are cut only where the GPU would otherwise run
+// unevenly:
+//   - up to a quarter as many tiles again as CUs: one tile per CU runs whole
+//     and the r left over are cut into ~CUs/r chunks (at most kMaxChained)
+//     that chain their carries inside the same launch, each CU pairing a whole
+//     tile with chunk work (measured on the 2.8B-shaped layer, 320 tiles:
+//     560 -> 475 us; with more left over the chunks' extra pass costs more
+//     than the balance gains);
+//   - otherwise, with at least 3/4 as many tiles as CUs, every tile runs whole;
+//   - with fewer tiles, every tile is cut so that each CU gets about two
+//     chunks, through the separate pair and carry passes.
 // vw_ok: the widest token-row access the pointers and dim allow (4, 2 or 1);
 // it decides the prologue width, not the split.
 void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int vw_ok, Plan* pl) {
@@ -124,14 +142,27 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
     G = eG;
     Kreq = eK;
   }
+  const int env_chained = env_flag("SSM_SCAN_CHAINED");
   const int vw = preferred_vw(G) <= vw_ok ? preferred_vw(G) : 1;
   const int64_t ntd = ceil_div(dim, 64);
   const int64_t T = batch * ntd;
   const int64_t kmax = ceil_div(L, kMinChunk) < kMaxChunks ? ceil_div(L, kMinChunk) : kMaxChunks;
   int64_t n_long, K;
+  bool chained = false;
   if (Kreq > 0) {
     K = Kreq;
     n_long = 0;
+    chained = env_chained == 1;
+  } else if (T > kNumCU && 4 * (T - kNumCU) <= kNumCU && env_chained != 0) {
+    const int64_t r = T - kNumCU;
+    n_long = kNumCU;
+    K = (kNumCU + r / 2) / r;
+    if (K < 2) K = 2;
+    if (K > kMaxChained) K = kMaxChained;
+    const char* ke = getenv("SSM_SCAN_CHAIN_K");  // tuning override of the chunk count
+    if (ke && atoi(ke) >= 2) K = atoi(ke);
+    if (K > kmax) K = kmax;
+    chained = true;
   } else if (4 * T >= 3 * kNumCU) {
     n_long = T;
     K = 1;
@@ -144,11 +175,15 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
   const int64_t kmin = ceil_div(L, max_chunk_len(dim, es));
   if (kmin > 1) {
     n_long = 0;
+    chained = false;
     if (K < kmin) K = kmin;
   }
   int64_t chunk = ceil_div(ceil_div(L, K), kChunkQuantum) * kChunkQuantum;
   K = ceil_div(L, chunk);
-  if (K == 1) n_long = T;
+  if (K == 1) {
+    n_long = T;
+    chained = false;
+  }
   pl->vw = vw;
   pl->npl = npl;
   pl->G = G;
@@ -158,11 +193,13 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
   pl->Ks = static_cast<int>(K);
   pl->chunk_len = chunk;
   pl->Lp = ceil_div(L, kTrip) * kTrip;
+  pl->chained = chained;
   // With fewer tiles than CUs a CU holds one workgroup and the scalar loads'
   // latency is exposed (or the records stream from HBM): touch them into L2.
-  pl->touch = T < kNumCU;
-  const char* te = getenv("SSM_SCAN_TOUCH");  // tuning override: "0" or "1"
-  if (te && (te[0] == '0' || te[0] == '1')) pl->touch = te[0] == '1';
+  // Chained plans gain from it as well (measured).
+  pl->touch = T < kNumCU || chained;
+  const int env_touch = env_flag("SSM_SCAN_TOUCH");
+  if (env_touch >= 0) pl->touch = env_touch == 1;
 }
 
 ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -182,45 +219,15 @@ ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, c
   return SSM_OK;
 }
 
-template <class IO, bool FULL>
-hipError_t launch_scan(int npl, int G, int vw, bool touch, const ScanParams& p, dim3 grid, hipStream_t s) {
-#define SSM_SCAN_LAUNCH(NPL_, G_, VW_)                                                                     \
-  if (touch)                                                                                             \
-    hipLaunchKernelGGL((scan_kernel<IO, NPL_, G_, VW_, FULL, true>), grid, dim3(64 * G_), 0, s, p);       \
-  else                                                                                                   \
-    hipLaunchKernelGGL((scan_kernel<IO, NPL_, G_, VW_, FULL, false>), grid, dim3(64 * G_), 0, s, p);
-#define SSM_SCAN_CASE(NPL_, G_)                                                                            \
-  if (npl == NPL_ && G == G_) {                                                                          \
-    constexpr int VWP = (G_ <= 4) ? 4 : ((G_ == 8) ? 2 : 1);                                             \
-    if (vw == VWP) {                                                                                     \
-      SSM_SCAN_LAUNCH(NPL_, G_, VWP)                                                                     \
-    } else {                                                                                             \
-      SSM_SCAN_LAUNCH(NPL_, G_, 1)                                                                       \
-    }                                                                                                    \
-    return hipGetLastError();                                                                            \
-  }
-  SSM_SCAN_CASE(4, 1)
-  SSM_SCAN_CASE(4, 2)
-  SSM_SCAN_CASE(4, 4)
-  SSM_SCAN_CASE(4, 8)
-  SSM_SCAN_CASE(4, 16)
-  SSM_SCAN_CASE(2, 8)
-  SSM_SCAN_CASE(1, 16)
-  SSM_SCAN_CASE(8, 2)
-  SSM_SCAN_CASE(16, 1)
-#undef SSM_SCAN_CASE
-#undef SSM_SCAN_LAUNCH
-  return hipErrorInvalidValue;
-}
-
 template <class IO>
-hipError_t run_scan(const Plan& pl, const void* B, const void* C, float* bc, ScanParams p, hipStream_t s) {
+hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void* C, float* bc, ScanParams p,
+                    hipStream_t s) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
   const dim3 pgrid(static_cast<unsigned>(p.batch * (pl.Lp / kPackT)));
 #define SSM_PACK_CASE(NPL_)                                                                                  \
   if (pl.npl == NPL_)                                                                                       \
     hipLaunchKernelGGL((pack_bc_kernel<IO, NPL_>), pgrid, dim3(256), 0, s, B, C, bc, p.batch, p.L, pl.Lp, p.N, \
-                       pl.G);
+                       pl.G, p.flags, lay.n_words);
   SSM_PACK_CASE(1)
   SSM_PACK_CASE(2)
   SSM_PACK_CASE(4)
@@ -229,9 +236,11 @@ hipError_t run_scan(const Plan& pl, const void* B, const void* C, float* bc, Sca
 #undef SSM_PACK_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  const dim3 grid_full(static_cast<unsigned>(pl.n_long + static_cast<int64_t>(pl.n_split) * pl.Ks));
+  if (pl.chained) return launch_scan<IO, kModeChained>(pl.npl, pl.G, pl.vw, pl.touch, p, grid_full, s);
   if (pl.n_split > 0 && pl.Ks > 1) {
     const dim3 grid_agg(static_cast<unsigned>(static_cast<int64_t>(pl.n_split) * (pl.Ks - 1)));
-    e = launch_scan<IO, false>(pl.npl, pl.G, pl.vw, pl.touch, p, grid_agg, s);
+    e = launch_scan<IO, kModeAgg>(pl.npl, pl.G, pl.vw, pl.touch, p, grid_agg, s);
     if (e != hipSuccess) return e;
     const int64_t cols = static_cast<int64_t>(pl.n_split) * 64 * npad;
     hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>(ceil_div(cols, kCarryCols))), dim3(256), 0, s,
@@ -240,8 +249,7 @@ hipError_t run_scan(const Plan& pl, const void* B, const void* C, float* bc, Sca
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const dim3 grid_full(static_cast<unsigned>(pl.n_long + static_cast<int64_t>(pl.n_split) * pl.Ks));
-  return launch_scan<IO, true>(pl.npl, pl.G, pl.vw, pl.touch, p, grid_full, s);
+  return launch_scan<IO, kModeFull>(pl.npl, pl.G, pl.vw, pl.touch, p, grid_full, s);
 }
 
 template <class IO>
@@ -349,10 +357,23 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
   p.y = y;
   p.final_state = final_state;
   p.aggP = p.aggS = p.carry = nullptr;
-  if (pl.n_split > 0) {
-    p.aggP = reinterpret_cast<float*>(ws + lay.bc);
-    p.aggS = reinterpret_cast<float*>(ws + lay.bc + lay.agg);
-    p.carry = reinterpret_cast<float*>(ws + lay.bc + 2 * lay.agg);
+  p.flags = p.ticket = p.status = p.cu_whole = nullptr;
+  size_t off = lay.bc;
+  if (lay.pairs) {
+    p.aggP = reinterpret_cast<float*>(ws + off);
+    p.aggS = reinterpret_cast<float*>(ws + off + lay.pairs);
+    off += 2 * lay.pairs;
+  }
+  if (lay.carry) {
+    p.carry = reinterpret_cast<float*>(ws + off);
+    off += lay.carry;
+  }
+  if (lay.n_words) {
+    unsigned* words = reinterpret_cast<unsigned*>(ws + off);
+    p.flags = words;                                           // [n_split][Ks]
+    p.ticket = words + static_cast<int64_t>(pl.n_split) * pl.Ks;  // [2]
+    p.status = p.ticket + 2;
+    p.cu_whole = p.status + 1;                                 // [kCuSlots]
   }
   p.batch = batch;
   p.L = L;
@@ -362,11 +383,12 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
   p.chunk_len = pl.chunk_len;
   p.ntd = pl.ntd;
   p.n_long = pl.n_long;
+  p.n_split = pl.n_split;
   p.Ks = pl.Ks;
   p.softplus = softplus_flag ? 1 : 0;
   float* bc = reinterpret_cast<float*>(ws);
-  const hipError_t e = dt == SSM_DTYPE_F32 ? run_scan<F32>(pl, B, C, bc, p, stream)
-                                           : run_scan<BF16>(pl, B, C, bc, p, stream);
+  const hipError_t e = dt == SSM_DTYPE_F32 ? run_scan<F32>(pl, lay, B, C, bc, p, stream)
+                                           : run_scan<BF16>(pl, lay, B, C, bc, p, stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 

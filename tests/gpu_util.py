@@ -127,6 +127,13 @@ class Variant(_Env):
         super().__init__("SSM_SCAN_VARIANT", f"{npl},{G},{K}")
 
 
+class Chained(_Env):
+    """Temporarily force chunks to chain their carries inside the scan launch (True) or not (False)."""
+
+    def __init__(self, on):
+        super().__init__("SSM_SCAN_CHAINED", "1" if on else "0")
+
+
 class Touch(_Env):
     """Temporarily force the L2 touch of upcoming B/C records on (True) or off (False)."""
 

@@ -13,7 +13,7 @@ from oracle import ref as R
 from selective_state_space_33_amd import inputs as I
 from selective_state_space_33_amd import ops
 
-from .gpu_util import (TOL, Touch, Variant, gpu_scan, oracle_channels, oracle_scan, rel_err, sample_channels, say, to_dev,
+from .gpu_util import (TOL, Chained, Touch, Variant, gpu_scan, oracle_channels, oracle_scan, rel_err, sample_channels, say, to_dev,
                        to_dev_f32)
 
 pytestmark = pytest.mark.gpu
@@ -191,6 +191,51 @@ def test_record_touch_does_not_change_results(npl, G, K):
     assert np.array_equal(y0, y1) and np.array_equal(f0, f1)
     yo, fo = oracle_scan(x)
     assert rel_err(y0, yo) <= TOL["bf16"] and rel_err(f0, fo) <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ chained chunks (one launch)
+@pytest.mark.parametrize("npl,G,K", [(2, 8, 2), (2, 8, 3), (2, 8, 5), (4, 4, 3), (1, 16, 2)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chained_chunks_forced(npl, G, K, dtype):
+    """Every tile cut into K chunks that take their carried-in state from the chunk before, in one launch."""
+    rng = np.random.default_rng(40 + 10 * K + npl)
+    x = I.random_scan_inputs(rng, 2, 1000, 136, 16, dtype=dtype)
+    say(f"chained npl={npl} G={G} K={K} {dtype}")
+    with Variant(npl, G, K), Chained(True):
+        _compare_scan(x, dtype)
+
+
+def test_chained_plan_sampled_channels():
+    """272 tiles for 256 CUs: 256 run whole, the 16 left over are cut into chained chunks (planner's choice)."""
+    rng = np.random.default_rng(41)
+    batch, L, dim = 1, 1024, 64 * 272
+    x = I.random_scan_inputs(rng, batch, L, dim, 16, dtype="bf16")
+    say(f"chained plan batch={batch} L={L} dim={dim}")
+    y, fs = gpu_scan(x, "bf16")
+    whole = [(0, d) for d in (0, 63, 5000, 16383)]
+    cut = [(0, d) for d in (16384, 16447, 17000, 17407)] + [(0, int(d)) for d in rng.integers(16384, dim, 8)]
+    samples = whole + cut
+    yo, fo = oracle_channels(x, samples)
+    yg = np.stack([y[b, :, d] for b, d in samples], axis=1)
+    fg = np.stack([fs[b, d] for b, d in samples], axis=0)
+    ey, ef = rel_err(yg, yo), rel_err(fg, fo)
+    print(f"[parity] chained plan: y err {ey:.3e}  final-state err {ef:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= 1e-5, (ey, ef)
+
+
+def test_chained_deterministic_and_matches_pair_passes():
+    rng = np.random.default_rng(42)
+    x = I.random_scan_inputs(rng, 1, 3000, 200, 16, dtype="f32")
+    say("chained determinism")
+    with Variant(2, 8, 4):
+        with Chained(True):
+            y1, f1 = gpu_scan(x, "f32")
+            y2, f2 = gpu_scan(x, "f32")
+        with Chained(False):
+            y3, f3 = gpu_scan(x, "f32")
+    assert np.array_equal(y1, y2) and np.array_equal(f1, f2)
+    # same chunking, same pair arithmetic: the two ways of carrying agree to rounding
+    assert rel_err(y1, y3) <= 1e-6 and rel_err(f1, f3) <= 1e-6
 
 
 def test_chunk_count_independence():
