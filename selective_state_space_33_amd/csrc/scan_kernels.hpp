@@ -46,12 +46,11 @@
 //             chunk;
 //   scan (FULL = true) runs the long tiles whole and every chunk of the split
 //             tiles from its carried-in state, producing y and the final state.
-// When a few tiles more than there are CUs are left over, cutting only those
-// into a handful of chunks and running everything in one launch balances the
-// GPU better (kModeChained): every chunk workgroup scans its chunk from zero
-// (its pair), takes the state carried into it from the chunk before,
-// publishes the state it hands on, then runs the full pass, side by side with
-// a whole tile on its CU.
+// When a few tiles more than there are CUs are left over (the 2.8B-shaped
+// layer has 320 for 256 CUs), one workgroup per CU runs one tile whole and
+// one chunk of a left-over tile spliced into it (kModeChained): chunk c of a
+// left-over tile starts from the final state of chunk c-1, which another
+// workgroup has scanned by then, so no chunk-pair pass is needed.
 #pragma once
 
 #include <utility>
@@ -74,13 +73,11 @@ struct ScanParams {
   float* aggP;
   float* aggS;
   float* carry;
-  // Chained launches: one ready flag per (split tile, chunk), the tickets of
-  // whole tiles and of chunks, a status word and the whole tiles running per
-  // CU (all zeroed by pack_bc_kernel).
+  // Chained launches: one ready flag per (split tile, chunk), the workgroup
+  // ticket and a status word (all zeroed by pack_bc_kernel).
   unsigned* flags;
-  unsigned* ticket;      // [0] whole tiles, [1] chunks
+  unsigned* ticket;
   unsigned* status;
-  unsigned* cu_whole;    // [kCuSlots]
   int64_t batch, L, Lp, dim, N;
   int64_t chunk_len;   // tokens per chunk of a split tile
   int ntd;             // 64-channel tiles per batch row
@@ -93,14 +90,12 @@ struct ScanParams {
 // Launch modes of scan_kernel.
 constexpr int kModeFull = 0;     // whole tiles, and chunks of split tiles from their carried-in states
 constexpr int kModeAgg = 1;      // chunk pairs (P, S) of chunks 0..Ks-2 of every split tile
-constexpr int kModeChained = 2;  // whole tiles and chunk workgroups that chain their carries, in one launch
+constexpr int kModeChained = 2;  // one workgroup per CU: a whole tile with one chunk of a left-over tile spliced in
 
-// A chunk workgroup waits for the state carried into it for at most this many
-// polls (each after a short sleep); past that it records an error in the
-// status word and goes on from a zero state, so the kernel always ends.
+// A workgroup waits for the state carried into its chunk for at most this
+// many polls (each after a short sleep); past that it records an error in
+// the status word and goes on from a zero state, so the kernel always ends.
 constexpr unsigned kSpinLimit = 1u << 18;
-// Slots of the per-CU table: XCC id (4 bits) x the SE/SH/CU bits of HW_ID (8 bits).
-constexpr int kCuSlots = 16 * 256;
 constexpr unsigned kStatusCarryTimeout = 1u;
 
 // Tokens per staged block (every variant), and the prologue layout: a thread
@@ -195,10 +190,8 @@ __global__ void __launch_bounds__(256) pack_bc_kernel(const void* __restrict__ B
 // single workgroup (latency exposed) or the records stream from HBM (long
 // sequences cut into chunks); with two workgroups per CU and L2-resident
 // records it only adds issue work, so the planner turns it off there.
-// A chained launch must keep two workgroups per CU (a whole tile and a chunk
-// workgroup side by side), so its register budget is capped accordingly.
 template <class IO, int NPL, int G, int VW, int MODE, bool TOUCH>
-__global__ void __launch_bounds__(64 * G, MODE == kModeChained ? 2 : 1) scan_kernel(ScanParams p) {
+__global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   constexpr int NPAD = NPL * G;
   constexpr int TB = BlockShape<G, VW>::TB;
   constexpr int RPT = BlockShape<G, VW>::RPT;
@@ -220,137 +213,93 @@ __global__ void __launch_bounds__(64 * G, MODE == kModeChained ? 2 : 1) scan_ker
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t dim = p.dim, L = p.L, N = p.N;
-
-  // ---- which work unit this workgroup runs.  Chained launches number units
-  // in the order workgroups start (a ticket), so a chunk only ever waits for
-  // a unit that has already started.
-  int unit = blockIdx.x;
-  if constexpr (MODE == kModeChained) {
-    // A workgroup takes a whole tile if none runs on its CU yet, else a chunk
-    // (falling back to the other kind when its kind is used up), so each CU
-    // pairs one whole tile with chunk work.  Chunks are numbered by a ticket
-    // of their own in the order workgroups take them, chunk-major, so a chunk
-    // only waits for a chunk that has already started.  The choice goes
-    // through the staging buffer, not yet in use (an extra LDS word would
-    // push two workgroups past the CU's 160 KB).
-    unsigned* sUnit = reinterpret_cast<unsigned*>(&sDU[0][0][0]);
-    if (tid == 0) {
-      const unsigned hw = __builtin_amdgcn_s_getreg((31 << 11) | 4);    // HW_ID: CU, SH, SE in bits 8..15
-      const unsigned xcc = __builtin_amdgcn_s_getreg((31 << 11) | 20);  // XCC_ID
-      const unsigned slot = ((xcc & 15u) << 8) | ((hw >> 8) & 255u);
-      const unsigned on_cu =
-          __hip_atomic_fetch_add(p.cu_whole + slot, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const unsigned n_whole = static_cast<unsigned>(p.n_long);
-      const unsigned n_chunk = static_cast<unsigned>(p.n_split) * static_cast<unsigned>(p.Ks);
-      unsigned kind = on_cu == 0u ? 0u : 1u;
-      unsigned u = 0;
-      for (int attempt = 0; attempt < 2; ++attempt, kind ^= 1u) {
-        const unsigned cap = kind == 0u ? n_whole : n_chunk;
-        const unsigned t = __hip_atomic_fetch_add(p.ticket + kind, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (t < cap) {
-          u = kind == 0u ? t : n_whole + t;
-          break;
-        }
-      }
-      *sUnit = u;
-    }
-    __syncthreads();
-    unit = static_cast<int>(__builtin_amdgcn_readfirstlane(*sUnit));
-    __syncthreads();  // every wavefront has read it before the buffer is written
-  }
-  int tile, c, st;
-  bool split;
-  if (MODE != kModeAgg && unit < p.n_long) {
-    tile = unit;
-    c = 0;
-    st = 0;
-    split = false;
-  } else if (MODE == kModeChained) {
-    // chunk-major: chunk c of every split tile precedes chunk c+1 of any
-    const int j = unit - p.n_long;
-    c = j / p.n_split;
-    st = j % p.n_split;
-    tile = p.n_long + st;
-    split = true;
-  } else {
-    const int per = MODE == kModeFull ? p.Ks : p.Ks - 1;
-    const int j = MODE == kModeFull ? unit - p.n_long : unit;
-    st = j / per;
-    c = j % per;
-    tile = p.n_long + st;
-    split = true;
-  }
-  const int64_t b = tile / p.ntd;
-  const int64_t d0 = static_cast<int64_t>(tile % p.ntd) * 64;
-  const int64_t t_begin = split ? static_cast<int64_t>(c) * p.chunk_len : 0;
-  const int64_t t_end = split ? ((t_begin + p.chunk_len < L) ? t_begin + p.chunk_len : L) : L;
-  const int64_t rows = t_end - t_begin;
-  const int rows32 = static_cast<int>(rows);
-  const int64_t pair_row = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;   // row of [n_split][Ks][64]
-  // Whole trips of kRing blocks; blocks past the chunk are padding whose
-  // tokens are identity steps (delta = 0) and whose outputs fall outside the
-  // buffers.
-  const int ntrips = static_cast<int>((rows + kTrip - 1) / kTrip);
-  const int nblocks = ntrips * kRing;
-
-  // ---- scan lane: channel d, states n0 .. n0+NPL-1
-  const int64_t d = d0 + lane;
-  const bool dvalid = d < dim;
-  const int n0 = w * NPL;
-  float A2[NPL], h[NPL];
+  const int n0 = w * NPL;                 // this wavefront's states n0 .. n0+NPL-1
+  const int pcol = (tid % RPR) * VW;      // prologue / epilogue thread: channels pcol .. pcol+VW-1 of the tile,
+  const int prow = tid / RPR;             // rows prow + i*ROWSTEP of a block
+  int voff_rel[RPT];                      // (in units of token rows and elements; scaled by set_tile)
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const int n = n0 + j;
-    A2[j] = (dvalid && n < N) ? p.A[d * N + n] * kLog2e : 0.0f;
-    h[j] = 0.0f;
-  }
-
-  // packed B/C records of this wavefront's state group, from the chunk's first token
-  const float* bc_row = p.bc + ((b * G + w) * p.Lp + t_begin) * (2 * NPL);
-
-  // ---- prologue / epilogue thread: channels pd .. pd+VW-1, rows prow + i*ROWSTEP of a block
-  const int pcol = (tid % RPR) * VW;
-  const int prow = tid / RPR;
-  const int64_t pd = d0 + pcol;
-  const bool pvalid = pd < dim;  // dim is a multiple of VW
-  float biasv[VW], Dv[VW];
-#pragma unroll
-  for (int e = 0; e < VW; ++e) {
-    biasv[e] = (pvalid && p.bias) ? p.bias[pd + e] : 0.0f;
-    Dv[e] = (pvalid && p.D) ? p.D[pd + e] : 0.0f;
-  }
-  const bool has_z = HAS_FULL && p.z != nullptr;
+  for (int i = 0; i < RPT; ++i) voff_rel[i] = prow + i * ROWSTEP;
   const bool softplus_on = p.softplus != 0;
-
-  // Token rows of u, delta_raw, z, y are reached through buffer resources
-  // covering (b, t_begin, d0) up to the end of the chunk's last row, so rows
-  // past the chunk read as zero and are not written.  The host keeps a
-  // chunk's rows within 2^31 bytes, so offsets are 32-bit.
   const int row_bytes = static_cast<int>(dim * ES);
   const int blk_bytes = TB * row_bytes;
-  const int64_t base_off = ((b * L + t_begin) * dim + d0) * ES;
-  const int64_t chunk_bytes = rows * row_bytes - d0 * ES;
-  const rsrc_t rs_u = make_rsrc(static_cast<const char*>(p.u) + base_off, chunk_bytes);
-  const rsrc_t rs_d = make_rsrc(static_cast<const char*>(p.delta) + base_off, chunk_bytes);
-  const rsrc_t rs_z = make_rsrc(has_z ? static_cast<const char*>(p.z) + base_off : nullptr, has_z ? chunk_bytes : 0);
-  const rsrc_t rs_y =
-      make_rsrc(HAS_FULL ? static_cast<const char*>(p.y) + base_off : nullptr, HAS_FULL ? chunk_bytes : 0);
+
+  // ---- the tile (64 channels of one batch row) and stretch of the sequence
+  // a pass works on; set_tile points everything at them.
+  int64_t b = 0, d0 = 0, d = 0, pd = 0, t_begin = 0;
+  int rows32 = 0;
+  bool dvalid = false, pvalid = false, has_z = false;
+  float A2[NPL], biasv[VW], Dv[VW];
+  const float* bc_row = p.bc;
+  rsrc_t rs_u, rs_d, rs_z, rs_y;
   int voff[RPT];
+  constexpr int kRecBlk = TB * 2 * NPL;   // record floats per block and group
+  const float* touch_row = p.bc;
+  int64_t touch_lim = 0;
+
+  auto set_tile = [&](int tile, int64_t tb, int64_t te) {
+    b = tile / p.ntd;
+    d0 = static_cast<int64_t>(tile % p.ntd) * 64;
+    t_begin = tb;
+    const int64_t rows = te - tb;
+    rows32 = static_cast<int>(rows);
+    // scan lane: channel d, states n0 .. n0+NPL-1
+    d = d0 + lane;
+    dvalid = d < dim;
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) voff[i] = (prow + i * ROWSTEP) * row_bytes + pcol * ES;
+    for (int j = 0; j < NPL; ++j) {
+      const int n = n0 + j;
+      A2[j] = (dvalid && n < N) ? p.A[d * N + n] * kLog2e : 0.0f;
+    }
+    // packed B/C records of this wavefront's state group, from the stretch's first token
+    bc_row = p.bc + ((b * G + w) * p.Lp + t_begin) * (2 * NPL);
+    // L2 touch of the group records (one float per 128-byte line); the
+    // records run on for kTB rows of padding past Lp
+    touch_row = bc_row + (lane * 32) % kRecBlk;
+    touch_lim = (p.Lp - t_begin) * 2 * NPL;
+    pd = d0 + pcol;
+    pvalid = pd < dim;  // dim is a multiple of VW
+#pragma unroll
+    for (int e = 0; e < VW; ++e) {
+      biasv[e] = (pvalid && p.bias) ? p.bias[pd + e] : 0.0f;
+      Dv[e] = (pvalid && p.D) ? p.D[pd + e] : 0.0f;
+    }
+    has_z = HAS_FULL && p.z != nullptr;
+    // Token rows of u, delta_raw, z, y are reached through buffer resources
+    // covering (b, t_begin, d0) up to the end of the stretch's last row, so
+    // rows past it read as zero and are not written.  The host keeps a
+    // stretch within 2^31 bytes, so offsets are 32-bit.
+    const int64_t base_off = ((b * L + t_begin) * dim + d0) * ES;
+    const int64_t bytes = rows * row_bytes - d0 * ES;
+    rs_u = make_rsrc(static_cast<const char*>(p.u) + base_off, bytes);
+    rs_d = make_rsrc(static_cast<const char*>(p.delta) + base_off, bytes);
+    rs_z = make_rsrc(has_z ? static_cast<const char*>(p.z) + base_off : nullptr, has_z ? bytes : 0);
+    rs_y = make_rsrc(HAS_FULL ? static_cast<const char*>(p.y) + base_off : nullptr, HAS_FULL ? bytes : 0);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) voff[i] = voff_rel[i] * row_bytes + pcol * ES;
+  };
+  // blocks of the current stretch, in whole trips of kRing; blocks past the
+  // stretch are padding whose tokens are identity steps (delta = 0) and whose
+  // outputs fall outside the buffers
+  auto stretch_blocks = [&]() { return (rows32 + kTrip - 1) / kTrip * kRing; };
 
-  // L2 touch of the wavefront's group records (one float per 128-byte line);
-  // the records run on for kTB rows of padding past Lp.
-  constexpr int kRecBlk = TB * 2 * NPL;  // record floats per block and group
-  const float* touch_row = bc_row + (lane * 32) % kRecBlk;
-  const int64_t touch_lim = (p.Lp - t_begin) * 2 * NPL;
+  float h[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) h[j] = 0.0f;
 
-  // One pass over the chunk: FULL = true produces y (readout and epilogue),
-  // FULL = false only advances h.  Returns the chunk's sum of delta.
-  auto run_pass = [&](auto fullc) -> float {
+  // One pass over blocks [k_begin, k_end) of the current stretch (multiples
+  // of kRing): FULL = true produces y (readout and epilogue), FULL = false
+  // only advances h.  Returns the sum of delta over the blocks.  With a stop
+  // flag, the pass also ends after the first trip of kRing blocks that ends
+  // at or past block k_stop once the flag is set (k_end then returns the
+  // block it stopped at); the flag is polled once per trip, its load in
+  // flight while the trip computes.
+  unsigned* sStop = nullptr;  // LDS word for the polled flag (chained launches only)
+  auto run_pass = [&](auto fullc, int k_begin, int& k_end, const unsigned* stop_flag = nullptr,
+                      int k_stop = 0) -> float {
     constexpr bool FULL = decltype(fullc)::value;
     static_assert(!FULL || HAS_FULL, "a readout pass needs the partial-readout buffers");
     float delta_total = 0.0f;
+    if (k_begin >= k_end) return delta_total;
 
     // Raw u, delta_raw, z of kRing blocks (slot = block % kRing).
     Raw<IO, VW> ru[kRing][RPT], rd[kRing][RPT], rz[kRing][RPT];
@@ -522,7 +471,7 @@ __global__ void __launch_bounds__(64 * G, MODE == kModeChained ? 2 : 1) scan_ker
       IC<P> parc;
       const int64_t t0 = static_cast<int64_t>(k) * TB;
       fetch_dd(parc, IC<0>{}, 0);
-      if (k >= 1) epilogue(IC<1 - P>{}, IC<Sm1>{}, k - 1);
+      if (k > k_begin) epilogue(IC<1 - P>{}, IC<Sm1>{}, k - 1);
       prologue(IC<1 - P>{}, IC<Sp1>{}, k + 1);
       issue_loads(IC<Sm1>{}, k + kPD + 1);
       float block_delta = 0.0f;
@@ -533,101 +482,171 @@ __global__ void __launch_bounds__(64 * G, MODE == kModeChained ? 2 : 1) scan_ker
       __syncthreads();
     };
 
-    // fill the ring with blocks 0 .. kPD, stage block 0
+    // fill the ring with blocks k_begin .. k_begin+kPD, stage block k_begin
     [&]<int... I>(std::integer_sequence<int, I...>) {
-      (issue_loads(IC<I>{}, I), ...);
+      (issue_loads(IC<I>{}, k_begin + I), ...);
     }(std::make_integer_sequence<int, kPD + 1>{});
-    fetch_records(IC<0>{}, 0);
-    prologue(IC<0>{}, IC<0>{}, 0);
+    fetch_records(IC<0>{}, static_cast<int64_t>(k_begin) * TB);
+    prologue(IC<0>{}, IC<0>{}, k_begin);
     __syncthreads();
-    for (int k = 0; k < nblocks; k += kRing) {
+    for (int k = k_begin; k < k_end; k += kRing) {
+      const bool poll = stop_flag != nullptr && k + kRing >= k_stop;
+      unsigned seen = 0u;
+      if (poll && tid == 0) seen = __hip_atomic_load(stop_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       [&]<int... I>(std::integer_sequence<int, I...>) {
         (iteration(IC<I>{}, k + I), ...);
       }(std::make_integer_sequence<int, kRing>{});
+      if (poll) {
+        if (tid == 0) *sStop = seen;
+        __syncthreads();
+        if (*sStop != 0u) {
+          k_end = k + kRing;
+          break;
+        }
+      }
     }
-    epilogue(IC<1>{}, IC<kRing - 1>{}, nblocks - 1);  // nblocks is a multiple of kRing (even)
+    epilogue(IC<1>{}, IC<kRing - 1>{}, k_end - 1);  // k_end is a multiple of kRing (even)
+    __syncthreads();  // the staging buffers are free for whatever runs next
     return delta_total;
   };
 
-  if constexpr (MODE == kModeAgg) {
-    // chunk pair from a zero state: S = h, P = exp(A * sum of deltas)
-    const float dt = run_pass(IC<false>{});
-    if (!dvalid) return;
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      const int64_t idx = pair_row * NPAD + n0 + j;
-      p.aggS[idx] = h[j];
-      p.aggP[idx] = __builtin_amdgcn_exp2f(A2[j] * dt);
-    }
-    return;
-  } else {
-    if (MODE == kModeFull && split && c > 0 && dvalid) {
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) h[j] = p.carry[pair_row * NPAD + n0 + j];
-    }
-    if (MODE == kModeChained && split) {
-      // Chain the carry: pair of this chunk, state carried in from chunk c-1,
-      // state handed on to chunk c+1 (carry row c+1), then the full pass.
-      const bool last = c == p.Ks - 1;
-      float Pc[NPL], Sc[NPL];
-      if (!last) {
-        const float dt = run_pass(IC<false>{});
-#pragma unroll
-        for (int j = 0; j < NPL; ++j) {
-          Pc[j] = __builtin_amdgcn_exp2f(A2[j] * dt);
-          Sc[j] = h[j];
-        }
-      }
-      float cin[NPL];
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) cin[j] = 0.0f;
-      // The carries and flags are read and written only with device-coherent
-      // (agent-scope) loads and stores, which bypass the per-XCD L2s; waiting
-      // for the carry stores to complete before the flag store orders them.
-      // (Release/acquire fences would instead write back or invalidate the
-      // whole L2, slowing every workgroup on the XCD.)
-      if (c > 0) {
-        unsigned* flag = p.flags + static_cast<int64_t>(st) * p.Ks + c;
-        if (tid == 0) {
-          unsigned polls = 0;
-          while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-            if (++polls > kSpinLimit) {
-              __hip_atomic_fetch_or(p.status, kStatusCarryTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              break;
-            }
-            __builtin_amdgcn_s_sleep(4);
-          }
-        }
-        __syncthreads();
-        if (dvalid) {
-#pragma unroll
-          for (int j = 0; j < NPL; ++j)
-            cin[j] = __hip_atomic_load(p.carry + pair_row * NPAD + n0 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-      if (!last) {
-        const int64_t next_row = pair_row + 64;  // carry row of chunk c+1
-        if (dvalid) {
-#pragma unroll
-          for (int j = 0; j < NPL; ++j)
-            __hip_atomic_store(p.carry + next_row * NPAD + n0 + j, __builtin_fmaf(Pc[j], cin[j], Sc[j]),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this thread's carry stores have completed
-        __syncthreads();
-        if (tid == 0)
-          __hip_atomic_store(p.flags + static_cast<int64_t>(st) * p.Ks + c + 1, 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) h[j] = cin[j];
-    }
-    run_pass(IC<true>{});
-    if (!dvalid) return;
-    if ((!split || c == p.Ks - 1) && p.final_state) {
+  auto write_final_state = [&]() {
+    if (dvalid && p.final_state) {
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
         if (n0 + j < N) p.final_state[(b * dim + d) * N + n0 + j] = h[j];
+    }
+  };
+
+  if constexpr (MODE == kModeChained) {
+    // One workgroup per CU.  Ticket j (the order workgroups start) owns
+    // whole tile j and, for j < n_split * Ks, chunk c = j / n_split of
+    // left-over tile n_long + j % n_split.  Chunk 0 runs first; chunk c > 0
+    // is spliced in after about c chunk-lengths of the whole tile, by when the
+    // workgroup running chunk c-1 (an earlier ticket) has handed on its final
+    // state.  The whole tile's state waits in registers meanwhile.
+    unsigned* sTicket = reinterpret_cast<unsigned*>(&sDU[0][0][0]);  // the staging buffer is not yet in use
+    if (tid == 0) *sTicket = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int j = static_cast<int>(__builtin_amdgcn_readfirstlane(*sTicket));
+    __syncthreads();  // every wavefront has read it before the buffer is written
+    extern __shared__ unsigned sDyn[];  // the launch's dynamic LDS (at least one word)
+    sStop = sDyn;
+    set_tile(j, 0, L);
+    int nb_whole = stretch_blocks();
+    const bool has_chunk = j < p.n_split * p.Ks;
+    if (!has_chunk) {
+      run_pass(IC<true>{}, 0, nb_whole);
+      write_final_state();
+      return;
+    }
+    const int c = j / p.n_split, st = j % p.n_split;
+    const int64_t cb = static_cast<int64_t>(c) * p.chunk_len;
+    const int64_t ce = (cb + p.chunk_len < L) ? cb + p.chunk_len : L;
+    const int nb_chunk = static_cast<int>((ce - cb + kTrip - 1) / kTrip) * kRing;
+    // Splice point: not before c chunks' worth of blocks, and only once chunk
+    // c-1 has handed on its state (chunk 0 goes first).
+    int m = c * nb_chunk;
+    if (m > nb_whole) m = nb_whole;
+    unsigned* my_flag = p.flags + static_cast<int64_t>(st) * p.Ks + c;
+    if (c > 0) {
+      m = nb_whole;
+      run_pass(IC<true>{}, 0, m, my_flag, c * nb_chunk);
+    }
+    float hw[NPL];
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) {
+      hw[q] = h[q];
+      h[q] = 0.0f;
+    }
+    set_tile(p.n_long + st, cb, ce);
+    const int64_t crow = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;  // carry row [n_split][Ks][64]
+    // The carries and flags are read and written only with device-coherent
+    // (agent-scope) loads and stores, which bypass the per-XCD L2s; waiting
+    // for the carry stores to complete before the flag store orders them.
+    // (Release/acquire fences would instead write back or invalidate the
+    // whole L2, slowing every workgroup on the XCD.)
+    if (c > 0) {
+      if (tid == 0) {
+        unsigned polls = 0;
+        while (__hip_atomic_load(my_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+          if (++polls > kSpinLimit) {
+            __hip_atomic_fetch_or(p.status, kStatusCarryTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+      __syncthreads();
+      if (dvalid) {
+#pragma unroll
+        for (int q = 0; q < NPL; ++q)
+          h[q] = __hip_atomic_load(p.carry + crow * NPAD + n0 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    int nbc = nb_chunk;
+    run_pass(IC<true>{}, 0, nbc);
+    if (c + 1 < p.Ks) {
+      if (dvalid) {
+#pragma unroll
+        for (int q = 0; q < NPL; ++q)
+          __hip_atomic_store(p.carry + (crow + 64) * NPAD + n0 + q, h[q], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);  // this thread's carry stores have completed
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_store(p.flags + static_cast<int64_t>(st) * p.Ks + c + 1, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      write_final_state();
+    }
+    set_tile(j, 0, L);
+#pragma unroll
+    for (int q = 0; q < NPL; ++q) h[q] = hw[q];
+    run_pass(IC<true>{}, m, nb_whole);
+    write_final_state();
+  } else {
+    // ---- which tile and which part of the sequence this workgroup scans
+    const int unit = blockIdx.x;
+    int tile, c, st;
+    bool split;
+    if (MODE == kModeFull && unit < p.n_long) {
+      tile = unit;
+      c = 0;
+      st = 0;
+      split = false;
+    } else {
+      const int per = MODE == kModeFull ? p.Ks : p.Ks - 1;
+      const int jj = MODE == kModeFull ? unit - p.n_long : unit;
+      st = jj / per;
+      c = jj % per;
+      tile = p.n_long + st;
+      split = true;
+    }
+    const int64_t tb = split ? static_cast<int64_t>(c) * p.chunk_len : 0;
+    const int64_t te = split ? ((tb + p.chunk_len < L) ? tb + p.chunk_len : L) : L;
+    set_tile(tile, tb, te);
+    const int64_t pair_row = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;   // row of [n_split][Ks][64]
+    if constexpr (MODE == kModeAgg) {
+      // chunk pair from a zero state: S = h, P = exp(A * sum of deltas)
+      int nb = stretch_blocks();
+      const float dt = run_pass(IC<false>{}, 0, nb);
+      if (!dvalid) return;
+#pragma unroll
+      for (int q = 0; q < NPL; ++q) {
+        const int64_t idx = pair_row * NPAD + n0 + q;
+        p.aggS[idx] = h[q];
+        p.aggP[idx] = __builtin_amdgcn_exp2f(A2[q] * dt);
+      }
+    } else {
+      if (split && c > 0 && dvalid) {
+#pragma unroll
+        for (int q = 0; q < NPL; ++q) h[q] = p.carry[pair_row * NPAD + n0 + q];
+      }
+      int nb = stretch_blocks();
+      run_pass(IC<true>{}, 0, nb);
+      if (!split || c == p.Ks - 1) write_final_state();
     }
   }
 }

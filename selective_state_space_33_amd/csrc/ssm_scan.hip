@@ -68,7 +68,7 @@ Layout layout_for(const Plan& pl, int64_t batch) {
   l.bc = align256((static_cast<size_t>(batch) * pl.Lp + kTB) * 2 * npad * sizeof(float));
   l.pairs = (pl.n_split > 0 && !pl.chained) ? align256(per) : 0;
   l.carry = pl.n_split > 0 ? align256(per) : 0;
-  l.n_words = pl.chained ? pl.n_split * pl.Ks + 3 + kCuSlots : 0;
+  l.n_words = pl.chained ? pl.n_split * pl.Ks + 2 : 0;
   l.words = align256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
   l.total = l.bc + 2 * l.pairs + l.carry + l.words;
   return l;
@@ -112,16 +112,15 @@ int env_flag(const char* name) {  // -1 when unset
 }
 
 // Work plan.  A tile (64 channels of one batch row) scanned whole costs one
-// pass over L tokens; cutting it into chunks adds a pass computing each
-// chunk's pair over all but the last chunk (about as costly per token as the
-// scan itself), so tiles are cut only where the GPU would otherwise run
-// unevenly:
-//   - up to a quarter as many tiles again as CUs: one tile per CU runs whole
-//     and the r left over are cut into ~CUs/r chunks (at most kMaxChained)
-//     that chain their carries inside the same launch, each CU pairing a whole
-//     tile with chunk work (measured on the 2.8B-shaped layer, 320 tiles:
-//     560 -> 475 us; with more left over the chunks' extra pass costs more
-//     than the balance gains);
+// pass over L tokens; cutting it into chunks costs either a pass computing
+// each chunk's pair (about as costly per token as the scan itself) or waiting
+// for the chunk before it, so tiles are cut only where the GPU would
+// otherwise run unevenly:
+//   - up to a quarter as many tiles again as CUs (the 2.8B-shaped layer: 320
+//     tiles): one workgroup per CU runs one tile whole, and the r tiles left
+//     over are cut into CUs/r chunks (at most kMaxChained), one spliced into
+//     each workgroup's tile at the point where the chunk before it is done
+//     (scan_kernel's chained mode);
 //   - otherwise, with at least 3/4 as many tiles as CUs, every tile runs whole;
 //   - with fewer tiles, every tile is cut so that each CU gets about two
 //     chunks, through the separate pair and carry passes.
@@ -149,18 +148,27 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
   const int64_t kmax = ceil_div(L, kMinChunk) < kMaxChunks ? ceil_div(L, kMinChunk) : kMaxChunks;
   int64_t n_long, K;
   bool chained = false;
-  if (Kreq > 0) {
+  if (Kreq > 0 && env_chained == 1) {
+    // forced chained plan: cut as many tiles r into Kreq chunks as leave one
+    // chunk per whole-tile workgroup (r * K <= T - r)
+    K = Kreq;
+    int64_t r = T / (K + 1);
+    if (r < 1) r = 1;
+    n_long = T - r;
+    chained = r * K <= n_long;
+    if (!chained) n_long = 0;
+  } else if (Kreq > 0) {
     K = Kreq;
     n_long = 0;
-    chained = env_chained == 1;
   } else if (T > kNumCU && 4 * (T - kNumCU) <= kNumCU && env_chained != 0) {
     const int64_t r = T - kNumCU;
     n_long = kNumCU;
-    K = (kNumCU + r / 2) / r;
+    K = kNumCU / r;  // r * K <= kNumCU: one chunk per workgroup at most
     if (K < 2) K = 2;
     if (K > kMaxChained) K = kMaxChained;
     const char* ke = getenv("SSM_SCAN_CHAIN_K");  // tuning override of the chunk count
     if (ke && atoi(ke) >= 2) K = atoi(ke);
+    if (r * K > n_long) K = n_long / r;  // at most one chunk per workgroup
     if (K > kmax) K = kmax;
     chained = true;
   } else if (4 * T >= 3 * kNumCU) {
@@ -237,7 +245,8 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid_full(static_cast<unsigned>(pl.n_long + static_cast<int64_t>(pl.n_split) * pl.Ks));
-  if (pl.chained) return launch_scan<IO, kModeChained>(pl.npl, pl.G, pl.vw, pl.touch, p, grid_full, s);
+  if (pl.chained)  // one workgroup per whole tile, each also running at most one chunk
+    return launch_scan<IO, kModeChained>(pl.npl, pl.G, pl.vw, pl.touch, p, dim3(pl.n_long), s);
   if (pl.n_split > 0 && pl.Ks > 1) {
     const dim3 grid_agg(static_cast<unsigned>(static_cast<int64_t>(pl.n_split) * (pl.Ks - 1)));
     e = launch_scan<IO, kModeAgg>(pl.npl, pl.G, pl.vw, pl.touch, p, grid_agg, s);
@@ -357,7 +366,7 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
   p.y = y;
   p.final_state = final_state;
   p.aggP = p.aggS = p.carry = nullptr;
-  p.flags = p.ticket = p.status = p.cu_whole = nullptr;
+  p.flags = p.ticket = p.status = nullptr;
   size_t off = lay.bc;
   if (lay.pairs) {
     p.aggP = reinterpret_cast<float*>(ws + off);
@@ -371,9 +380,8 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
   if (lay.n_words) {
     unsigned* words = reinterpret_cast<unsigned*>(ws + off);
     p.flags = words;                                           // [n_split][Ks]
-    p.ticket = words + static_cast<int64_t>(pl.n_split) * pl.Ks;  // [2]
-    p.status = p.ticket + 2;
-    p.cu_whole = p.status + 1;                                 // [kCuSlots]
+    p.ticket = words + static_cast<int64_t>(pl.n_split) * pl.Ks;
+    p.status = p.ticket + 1;
   }
   p.batch = batch;
   p.L = L;

@@ -197,16 +197,18 @@ def test_record_touch_does_not_change_results(npl, G, K):
 @pytest.mark.parametrize("npl,G,K", [(2, 8, 2), (2, 8, 3), (2, 8, 5), (4, 4, 3), (1, 16, 2)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_chained_chunks_forced(npl, G, K, dtype):
-    """Every tile cut into K chunks that take their carried-in state from the chunk before, in one launch."""
+    """Some tiles cut into K chunks spliced into the other tiles' workgroups, each chunk starting from the
+    final state of the chunk before it (one launch)."""
     rng = np.random.default_rng(40 + 10 * K + npl)
-    x = I.random_scan_inputs(rng, 2, 1000, 136, 16, dtype=dtype)
+    x = I.random_scan_inputs(rng, 2, 1000, 64 * 7 - 8, 16, dtype=dtype)
     say(f"chained npl={npl} G={G} K={K} {dtype}")
     with Variant(npl, G, K), Chained(True):
         _compare_scan(x, dtype)
 
 
 def test_chained_plan_sampled_channels():
-    """272 tiles for 256 CUs: 256 run whole, the 16 left over are cut into chained chunks (planner's choice)."""
+    """272 tiles for 256 CUs: 256 run whole, the 16 left over are cut into chunks spliced into them
+    (the planner's own choice)."""
     rng = np.random.default_rng(41)
     batch, L, dim = 1, 1024, 64 * 272
     x = I.random_scan_inputs(rng, batch, L, dim, 16, dtype="bf16")
@@ -223,9 +225,9 @@ def test_chained_plan_sampled_channels():
     assert ey <= TOL["bf16"] and ef <= 1e-5, (ey, ef)
 
 
-def test_chained_deterministic_and_matches_pair_passes():
+def test_chained_deterministic_and_matches_other_plans():
     rng = np.random.default_rng(42)
-    x = I.random_scan_inputs(rng, 1, 3000, 200, 16, dtype="f32")
+    x = I.random_scan_inputs(rng, 1, 3000, 64 * 12, 16, dtype="f32")
     say("chained determinism")
     with Variant(2, 8, 4):
         with Chained(True):
@@ -234,8 +236,8 @@ def test_chained_deterministic_and_matches_pair_passes():
         with Chained(False):
             y3, f3 = gpu_scan(x, "f32")
     assert np.array_equal(y1, y2) and np.array_equal(f1, f2)
-    # same chunking, same pair arithmetic: the two ways of carrying agree to rounding
-    assert rel_err(y1, y3) <= 1e-6 and rel_err(f1, f3) <= 1e-6
+    # a different cut of the same recurrence: equal up to rounding
+    assert rel_err(y1, y3) <= 1e-5 and rel_err(f1, f3) <= 1e-5
 
 
 def test_chunk_count_independence():
