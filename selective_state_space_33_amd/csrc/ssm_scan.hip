@@ -116,7 +116,7 @@ int env_flag(const char* name) {  // -1 when unset
 // each chunk's pair (about as costly per token as the scan itself) or waiting
 // for the chunk before it, so tiles are cut only where the GPU would
 // otherwise run unevenly:
-//   - up to a quarter as many tiles again as CUs (the 2.8B-shaped layer: 320
+//   - up to half as many tiles again as CUs (the 2.8B-shaped layer: 320
 //     tiles): one workgroup per CU runs one tile whole, and the r tiles left
 //     over are cut into CUs/r chunks (at most kMaxChained), one spliced into
 //     each workgroup's tile at the point where the chunk before it is done
@@ -160,7 +160,7 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
   } else if (Kreq > 0) {
     K = Kreq;
     n_long = 0;
-  } else if (T > kNumCU && 4 * (T - kNumCU) <= kNumCU && env_chained != 0) {
+  } else if (T > kNumCU && 2 * (T - kNumCU) <= kNumCU && env_chained != 0) {
     const int64_t r = T - kNumCU;
     n_long = kNumCU;
     K = kNumCU / r;  // r * K <= kNumCU: one chunk per workgroup at most
