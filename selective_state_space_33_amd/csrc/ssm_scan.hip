@@ -202,10 +202,10 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
   pl->chunk_len = chunk;
   pl->Lp = ceil_div(L, kTrip) * kTrip;
   pl->chained = chained;
-  // With fewer tiles than CUs a CU holds one workgroup and the scalar loads'
-  // latency is exposed (or the records stream from HBM): touch them into L2.
-  // Chained plans gain from it as well (measured).
-  pl->touch = T < kNumCU || chained;
+  // With at most one tile per CU (and in chained plans) a CU holds one
+  // workgroup and the scalar loads' latency is exposed (or the records
+  // stream from HBM): touch them into L2.
+  pl->touch = T <= kNumCU || chained;
   const int env_touch = env_flag("SSM_SCAN_TOUCH");
   if (env_touch >= 0) pl->touch = env_touch == 1;
 }
