@@ -73,11 +73,11 @@ typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
 /* Bytes of device workspace that ssm_scan_fwd needs for this shape (always
  * > 0 for a valid shape).  The workspace holds B and C repacked as fp32
  * records per group of states (about batch * L * 2 * dstate * 4 bytes) and,
- * when the sequence is cut into chunks, the composed fade-and-add pair of
- * every chunk and the state carried into it ("Mamba is attention all you
- * really need, part 2", "The relay": squash each chunk to one pair, combine
- * the chunk pairs, pass the real states back).  Returns 0 for arguments
- * ssm_scan_fwd would reject. */
+ * when tiles of 64 channels are cut into chunks of the sequence, the state
+ * carried into every chunk ("Mamba is attention all you really need, part
+ * 2", "The relay": a chunk can start from the state the chunk before it hands
+ * on), plus either the chunks' composed fade-and-add pairs or a few words of
+ * ready flags.  Returns 0 for arguments ssm_scan_fwd would reject. */
 size_t ssm_scan_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt);
 
 /* Selective scan over a whole sequence, starting from a zero state.
