@@ -98,12 +98,15 @@ constexpr int kModeChained = 2;  // one workgroup per CU: a whole tile with one 
 constexpr unsigned kSpinLimit = 1u << 18;
 constexpr unsigned kStatusCarryTimeout = 1u;
 
-// Tokens per staged block (every variant), and the prologue layout: a thread
-// handles VW consecutive channels of RPT token rows.
-constexpr int kTB = 16;
-template <int G, int VW> struct BlockShape {
-  static constexpr int TB = kTB;
-  static_assert(G * VW <= kTB, "a block row must fit the prologue threads");
+// Tokens per staged block: 16, or 32 where one workgroup has the CU to
+// itself (the block's barrier is then paid half as often, and the staging
+// buffers take the whole 160 KB of LDS).  A prologue thread handles VW
+// consecutive channels of RPT token rows.
+constexpr int kTBMax = 32;
+template <int G, int VW, int TB_> struct BlockShape {
+  static constexpr int TB = TB_;
+  static_assert(TB == 16 || TB == 32, "block length");
+  static_assert(G * VW <= TB, "a block row must fit the prologue threads");
   static constexpr int RPT = TB / (G * VW);
 };
 
@@ -127,10 +130,11 @@ template <int I> struct IC { static constexpr int value = I; };
 // loads in flight).
 constexpr int kPD = 2;
 constexpr int kRing = kPD + 2;
-// Tokens per unrolled trip of the main loop.  Chunk lengths and the packed B/C
-// rows are multiples of it; one group of records past the end is read (and
-// not used), so the packed buffer carries kTB rows of padding.
-constexpr int kTrip = kRing * kTB;
+// Tokens per unrolled trip of the main loop at the longest block.  Chunk
+// lengths and the packed B/C rows are multiples of it (so of every variant's
+// trip); one group of records past the end is read (and not used), so the
+// packed buffer carries kTBMax rows of padding.
+constexpr int kTrip = kRing * kTBMax;
 
 // lgkmcnt(0) with vmcnt and expcnt left at their maxima, and vmcnt(0) with
 // expcnt and lgkmcnt left at theirs (gfx9 s_waitcnt encoding).
@@ -190,11 +194,12 @@ __global__ void __launch_bounds__(256) pack_bc_kernel(const void* __restrict__ B
 // single workgroup (latency exposed) or the records stream from HBM (long
 // sequences cut into chunks); with two workgroups per CU and L2-resident
 // records it only adds issue work, so the planner turns it off there.
-template <class IO, int NPL, int G, int VW, int MODE, bool TOUCH>
+template <class IO, int NPL, int G, int VW, int MODE, bool TOUCH, int TB_>
 __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   constexpr int NPAD = NPL * G;
-  constexpr int TB = BlockShape<G, VW>::TB;
-  constexpr int RPT = BlockShape<G, VW>::RPT;
+  constexpr int TB = BlockShape<G, VW, TB_>::TB;
+  constexpr int RPT = BlockShape<G, VW, TB_>::RPT;
+  constexpr int TRIP = kRing * TB;          // tokens per unrolled trip of the main loop
   constexpr int RPR = 64 / VW;              // prologue threads per token row
   constexpr int ROWSTEP = (64 * G) / RPR;   // rows between one thread's runs
   static_assert(TB == RPT * ROWSTEP, "block shape");
@@ -253,7 +258,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     // packed B/C records of this wavefront's state group, from the stretch's first token
     bc_row = p.bc + ((b * G + w) * p.Lp + t_begin) * (2 * NPL);
     // L2 touch of the group records (one float per 128-byte line); the
-    // records run on for kTB rows of padding past Lp
+    // records run on for kTBMax rows of padding past Lp
     touch_row = bc_row + (lane * 32) % kRecBlk;
     touch_lim = (p.Lp - t_begin) * 2 * NPL;
     pd = d0 + pcol;
@@ -280,7 +285,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   // blocks of the current stretch, in whole trips of kRing; blocks past the
   // stretch are padding whose tokens are identity steps (delta = 0) and whose
   // outputs fall outside the buffers
-  auto stretch_blocks = [&]() { return (rows32 + kTrip - 1) / kTrip * kRing; };
+  auto stretch_blocks = [&]() { return (rows32 + TRIP - 1) / TRIP * kRing; };
 
   float h[NPL];
 #pragma unroll
@@ -293,7 +298,6 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   // at or past block k_stop once the flag is set (k_end then returns the
   // block it stopped at); the flag is polled once per trip, its load in
   // flight while the trip computes.
-  unsigned* sStop = nullptr;  // LDS word for the polled flag (chained launches only)
   auto run_pass = [&](auto fullc, int k_begin, int& k_end, const unsigned* stop_flag = nullptr,
                       int k_stop = 0) -> float {
     constexpr bool FULL = decltype(fullc)::value;
@@ -496,12 +500,22 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       [&]<int... I>(std::integer_sequence<int, I...>) {
         (iteration(IC<I>{}, k + I), ...);
       }(std::make_integer_sequence<int, kRing>{});
-      if (poll) {
-        if (tid == 0) *sStop = seen;
-        __syncthreads();
-        if (*sStop != 0u) {
-          k_end = k + kRing;
-          break;
+      if constexpr (HAS_FULL) {
+        if (poll) {
+          // Thread 0 hands the flag to every wavefront through that
+          // wavefront's own word of the parity-0 partial readouts: the buffer
+          // is free at a trip boundary (its last reader, the epilogue in the
+          // trip's last block, is behind the barrier), and wavefront w next
+          // writes its word in the following block's scan, after reading it.
+          if (tid == 0) {
+#pragma unroll
+            for (int ww = 0; ww < G; ++ww) sY[0][ww][TB - 1][63] = __builtin_bit_cast(float, seen);
+          }
+          __syncthreads();
+          if (__builtin_bit_cast(unsigned, sY[0][w][TB - 1][63]) != 0u) {
+            k_end = k + kRing;
+            break;
+          }
         }
       }
     }
@@ -530,8 +544,6 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     __syncthreads();
     const int j = static_cast<int>(__builtin_amdgcn_readfirstlane(*sTicket));
     __syncthreads();  // every wavefront has read it before the buffer is written
-    extern __shared__ unsigned sDyn[];  // the launch's dynamic LDS (at least one word)
-    sStop = sDyn;
     set_tile(j, 0, L);
     int nb_whole = stretch_blocks();
     const bool has_chunk = j < p.n_split * p.Ks;
@@ -543,7 +555,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     const int c = j / p.n_split, st = j % p.n_split;
     const int64_t cb = static_cast<int64_t>(c) * p.chunk_len;
     const int64_t ce = (cb + p.chunk_len < L) ? cb + p.chunk_len : L;
-    const int nb_chunk = static_cast<int>((ce - cb + kTrip - 1) / kTrip) * kRing;
+    const int nb_chunk = static_cast<int>((ce - cb + TRIP - 1) / TRIP) * kRing;
     // Splice point: not before c chunks' worth of blocks, and only once chunk
     // c-1 has handed on its state (chunk 0 goes first).
     int m = c * nb_chunk;

@@ -12,19 +12,20 @@
 namespace ssm {
 
 // (npl, G): states per lane and wavefronts; vw: prologue width (the
-// variant's preferred width, else 1); touch: L2 touch of B/C records.
-// Returns hipErrorInvalidValue for a variant that does not exist.
+// variant's preferred width, else 1); touch: L2 touch of B/C records; tb:
+// tokens per block (16, or 32 where variant_has_tb32).  Returns
+// hipErrorInvalidValue for a variant that does not exist.
 template <class IO, int MODE>
-hipError_t launch_scan(int npl, int G, int vw, bool touch, const ScanParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_scan(int npl, int G, int vw, bool touch, int tb, const ScanParams& p, dim3 grid, hipStream_t s);
 
 // Instantiated (each in its own translation unit) for these six combinations.
-extern template hipError_t launch_scan<F32, kModeFull>(int, int, int, bool, const ScanParams&, dim3, hipStream_t);
-extern template hipError_t launch_scan<F32, kModeAgg>(int, int, int, bool, const ScanParams&, dim3, hipStream_t);
-extern template hipError_t launch_scan<F32, kModeChained>(int, int, int, bool, const ScanParams&, dim3, hipStream_t);
-extern template hipError_t launch_scan<BF16, kModeFull>(int, int, int, bool, const ScanParams&, dim3, hipStream_t);
-extern template hipError_t launch_scan<BF16, kModeAgg>(int, int, int, bool, const ScanParams&, dim3, hipStream_t);
-extern template hipError_t launch_scan<BF16, kModeChained>(int, int, int, bool, const ScanParams&, dim3,
-                                                           hipStream_t);
+extern template hipError_t launch_scan<F32, kModeFull>(int, int, int, bool, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<F32, kModeAgg>(int, int, int, bool, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<F32, kModeChained>(int, int, int, bool, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeFull>(int, int, int, bool, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeAgg>(int, int, int, bool, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeChained>(int, int, int, bool, int, const ScanParams&,
+                                                           dim3, hipStream_t);
 
 // Variants (states per lane, wavefronts).  Each exists with its preferred
 // prologue width (channels per thread: 4 up to 4 wavefronts, 2 for 8, 1 for
@@ -34,5 +35,9 @@ inline bool variant_exists(int npl, int G) {
   return (npl == 2 && G == 8) || (npl == 1 && G == 16) || (npl == 8 && G == 2) || (npl == 16 && G == 1);
 }
 inline int preferred_vw(int G) { return G <= 4 ? 4 : (G == 8 ? 2 : 1); }
+// 32-token blocks exist for (2, 8) at its preferred width, outside the chunk-pair pass.
+inline bool variant_has_tb32(int npl, int G, int vw, int mode) {
+  return npl == 2 && G == 8 && vw == 2 && mode != kModeAgg;
+}
 
 }  // namespace ssm

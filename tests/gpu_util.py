@@ -139,3 +139,10 @@ class Touch(_Env):
 
     def __init__(self, on):
         super().__init__("SSM_SCAN_TOUCH", "1" if on else "0")
+
+
+class BlockLen(_Env):
+    """Temporarily force the readout scan's tokens per block (16 or 32) where the variant has both."""
+
+    def __init__(self, tb):
+        super().__init__("SSM_SCAN_TB", str(tb))

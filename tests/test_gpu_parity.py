@@ -13,7 +13,7 @@ from oracle import ref as R
 from selective_state_space_33_amd import inputs as I
 from selective_state_space_33_amd import ops
 
-from .gpu_util import (TOL, Chained, Touch, Variant, gpu_scan, oracle_channels, oracle_scan, rel_err, sample_channels, say, to_dev,
+from .gpu_util import (TOL, BlockLen, Chained, Touch, Variant, gpu_scan, oracle_channels, oracle_scan, rel_err, sample_channels, say, to_dev,
                        to_dev_f32)
 
 pytestmark = pytest.mark.gpu
@@ -204,6 +204,24 @@ def test_chained_chunks_forced(npl, G, K, dtype):
     say(f"chained npl={npl} G={G} K={K} {dtype}")
     with Variant(npl, G, K), Chained(True):
         _compare_scan(x, dtype)
+
+
+@pytest.mark.parametrize("K,chained,dtype", [(1, False, "bf16"), (1, False, "f32"), (3, True, "bf16"),
+                                             (3, True, "f32"), (3, False, "f32")])
+def test_block_length_does_not_change_results(K, chained, dtype):
+    """16- and 32-token blocks change only where the barriers fall, not the arithmetic: outputs are bitwise
+    equal (whole tiles, chained chunks, and the readout pass of the chunk-pair plan), and match the oracle."""
+    rng = np.random.default_rng(50 + K + (10 if chained else 0))
+    x = I.random_scan_inputs(rng, 2, 1000, 64 * 7 - 8, 16, dtype=dtype)
+    say(f"block length 16/32 K={K} chained={chained} {dtype}")
+    outs = []
+    for tb in (16, 32):
+        with Variant(2, 8, K), Chained(chained), BlockLen(tb):
+            outs.append(gpu_scan(x, dtype))
+    (y16, f16), (y32, f32_) = outs
+    assert np.array_equal(y16, y32) and np.array_equal(f16, f32_)
+    yo, fo = oracle_scan(x)
+    assert rel_err(y32, yo) <= TOL[dtype] and rel_err(f32_, fo) <= TOL[dtype]
 
 
 def test_chained_plan_sampled_channels():
