@@ -190,6 +190,25 @@ __device__ __forceinline__ float softplus_f(float x) {
   return __builtin_fmaxf(x, 0.0f) + (e < 0.0625f ? series : viaLog);
 }
 
+// Lane K (0..15) of each 16-lane row of v, broadcast across the row (DPP
+// row_newbcast; the compiler folds it into a multiply's first operand).
+template <int K> __device__ __forceinline__ float row_bcast(float v) {
+  static_assert(K >= 0 && K < 16, "row lane");
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + K, 0xf, 0xf, true));
+}
+
+// acc + row_bcast<K>(v) * x as one v_fmac_f32_dpp: the compiler does not fold
+// a broadcast into an FMA that accumulates in place.  A DPP read of a VGPR
+// that a VALU instruction wrote in the two wait states before it is a hazard
+// the compiler cannot see inside asm.  Here v is only ever written by buffer
+// loads; the library build scans the generated assembly for the hazard and
+// fails if it finds one (build.py).
+template <int K> __device__ __forceinline__ float fmac_row_bcast(float acc, float v, float x) {
+  static_assert(K >= 0 && K < 16, "row lane");
+  asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf" : "+v"(acc) : "v"(v), "v"(x), "n"(K));
+  return acc;
+}
+
 // SiLU(z) = z * sigmoid(z) = z / (1 + e^-z); e^-z = inf for very negative z gives -0.
 __device__ __forceinline__ float silu_f(float z) {
   const float e = __builtin_amdgcn_exp2f(-z * kLog2e);

@@ -9,9 +9,10 @@
 // B and C are first packed (pack_bc_kernel) into fp32 records per state group,
 //   bc[b][g][t][0 .. NPL)       = B_t[g*NPL .. g*NPL+NPL)
 //   bc[b][g][t][NPL .. 2*NPL)   = C_t[g*NPL .. g*NPL+NPL)
-// (states beyond dstate are zero), so a wavefront fetches the B_t/C_t of
-// several tokens with one 64-byte scalar load and uses them as SGPR operands,
-// with no per-token conversion work.
+// (states beyond dstate are zero).  A wavefront loads a block's records with
+// vector loads, 16 consecutive floats per register, each replicated in the
+// four 16-lane rows, and an update takes B_t[n], C_t[n] straight from the
+// register with a DPP row broadcast: no conversion work and no scalar loads.
 //
 // The sequence is processed in blocks of TB tokens, software-pipelined over
 // three blocks with double-buffered LDS and one barrier per block: while the
@@ -29,9 +30,9 @@
 // The scan of block k walks its TB tokens: for every state
 // a = exp2(delta * A*log2 e), h = a*h + (delta*u)*B_t[n], and the partial
 // readout y_w = sum over its states of C_t[n]*h -- the fade-and-add pair
-// (a, b) of each step never leaves registers.  The packed B/C records and the
-// staged (delta, delta*u) of the next group of tokens are fetched while the
-// current group is computed.
+// (a, b) of each step never leaves registers.  The staged (delta, delta*u) of
+// the next group of tokens are read from LDS while the current group is
+// computed; the records of block k+1 are loaded while block k is scanned.
 //
 // Tiles are either scanned whole by one workgroup ("long" tiles) or, when
 // there are too few tiles to fill the GPU evenly, cut into Ks chunks of the
@@ -188,13 +189,7 @@ __global__ void __launch_bounds__(256) pack_bc_kernel(const void* __restrict__ B
   }
 }
 
-// TOUCH: also read one word per 128-byte line of each upcoming block's packed
-// B/C records with the vector loads of the ring, so that the wavefronts'
-// scalar loads of those records hit in L2.  That pays off when a CU holds a
-// single workgroup (latency exposed) or the records stream from HBM (long
-// sequences cut into chunks); with two workgroups per CU and L2-resident
-// records it only adds issue work, so the planner turns it off there.
-template <class IO, int NPL, int G, int VW, int MODE, bool TOUCH, int TB_>
+template <class IO, int NPL, int G, int VW, int MODE, int TB_>
 __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   constexpr int NPAD = NPL * G;
   constexpr int TB = BlockShape<G, VW, TB_>::TB;
@@ -237,9 +232,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   const float* bc_row = p.bc;
   rsrc_t rs_u, rs_d, rs_z, rs_y;
   int voff[RPT];
-  constexpr int kRecBlk = TB * 2 * NPL;   // record floats per block and group
-  const float* touch_row = p.bc;
-  int64_t touch_lim = 0;
+  rsrc_t rs_bc;                            // this wavefront's packed B/C records of the stretch
+  const int rec_voff = (lane & 15) * 4;    // lane l holds float l % 16 of a group's 16
 
   auto set_tile = [&](int tile, int64_t tb, int64_t te) {
     b = tile / p.ntd;
@@ -257,10 +251,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     }
     // packed B/C records of this wavefront's state group, from the stretch's first token
     bc_row = p.bc + ((b * G + w) * p.Lp + t_begin) * (2 * NPL);
-    // L2 touch of the group records (one float per 128-byte line); the
-    // records run on for kTBMax rows of padding past Lp
-    touch_row = bc_row + (lane * 32) % kRecBlk;
-    touch_lim = (p.Lp - t_begin) * 2 * NPL;
+    // the records run on for kTBMax rows of padding past Lp
+    rs_bc = make_rsrc(bc_row, (p.Lp + kTBMax - t_begin) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
     pd = d0 + pcol;
     pvalid = pd < dim;  // dim is a multiple of VW
 #pragma unroll
@@ -307,15 +299,23 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 
     // Raw u, delta_raw, z of kRing blocks (slot = block % kRing).
     Raw<IO, VW> ru[kRing][RPT], rd[kRing][RPT], rz[kRing][RPT];
-    float touch[kRing];
+    // Packed B/C records of two blocks (slot = block parity): register v of a
+    // block holds floats 16v .. 16v+15 of its records, float 16v + i in lane i
+    // of every 16-lane row, read with row broadcasts.
+    constexpr int NRV = TB * 2 * NPL / 16;
+    float rv[2][NRV];
+
+    auto load_records = [&](auto parc, int blk) {
+      constexpr int P = decltype(parc)::value;
+      const int bo = blk * (TB * 2 * NPL * 4);
+#pragma unroll
+      for (int v = 0; v < NRV; ++v)
+        rv[P][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bc, rec_voff + bo + v * 64, 0, 0));
+    };
 
     auto issue_loads = [&](auto slotc, int blk) {
       constexpr int S = decltype(slotc)::value;
       const int bo = blk * blk_bytes;
-      if constexpr (TOUCH) {
-        const int64_t off = static_cast<int64_t>(blk) * kRecBlk;
-        touch[S] = (off + kRecBlk <= touch_lim) ? touch_row[off] : 0.0f;
-      }
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         ru[S][i] = buf_load<IO, VW>(rs_u, voff[i] + bo, 0);
@@ -331,9 +331,6 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     auto prologue = [&](auto parc, auto slotc, int blk) {
       constexpr int P = decltype(parc)::value;
       constexpr int S = decltype(slotc)::value;
-      // the touched word is not needed; consuming it here (where the slot's
-      // loads are complete anyway) keeps the load alive at no cost
-      if constexpr (TOUCH) asm volatile("" ::"v"(touch[S]));
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const int row = prow + i * ROWSTEP;
@@ -409,39 +406,38 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       }
     };
 
-    // One state update for a token: r points at the token's packed record (B then C).
-    auto update = [&](auto parc, const float2 dd, const float* r, int tt, float& block_delta) {
+    // The state updates of token q of group g of a block whose records are in
+    // slot P: its record (B then C) is floats F .. F + 2*NPL of the block's.
+    auto update = [&](auto parc, auto gc, auto qc, const float2 dd, float& block_delta) {
       constexpr int P = decltype(parc)::value;
+      constexpr int F = (decltype(gc)::value * SUB + decltype(qc)::value) * 2 * NPL;
       float yp = 0.0f;
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
-        h[j] = __builtin_fmaf(a, h[j], dd.y * r[j]);
-        if (FULL) yp = __builtin_fmaf(r[NPL + j], h[j], yp);
-        // Without the readout store nothing ties the update to its token's
-        // group: the optimiser would sink a whole block of updates below all
-        // of its record fetches and spill the records.  An empty asm with h as
-        // an in/out operand keeps each update where it is written.
-        if (!FULL) asm volatile("" : "+v"(h[j]));
-      }
-      if constexpr (FULL) sY[P][w][tt][lane] = yp;
+      [&]<int... J>(std::integer_sequence<int, J...>) {
+        (([&] {
+           constexpr int j = J;
+           const float Bj = row_bcast<(F + j) % 16>(rv[P][(F + j) / 16]);
+           const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
+           h[j] = __builtin_fmaf(a, h[j], dd.y * Bj);
+           if constexpr (FULL) {
+             constexpr int fc = F + NPL + j;
+             if constexpr (j == 0) yp = row_bcast<fc % 16>(rv[P][fc / 16]) * h[0];
+             else yp = fmac_row_bcast<fc % 16>(yp, rv[P][fc / 16], h[j]);
+           } else {
+             // Without the readout store nothing ties the update to its
+             // token: the optimiser would sink a whole block of updates below
+             // the next loads.  An empty asm with h as an in/out operand
+             // keeps each update where it is written.
+             asm volatile("" : "+v"(h[j]));
+           }
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, NPL>{});
+      if constexpr (FULL) sY[P][w][decltype(gc)::value * SUB + decltype(qc)::value][lane] = yp;
       else block_delta += dd.x;
     };
 
-    // Double-buffered group state: packed records (SGPRs) and staged (delta, delta*u).
-    float rec[2][GS::FLOATS];
+    // Double-buffered staged (delta, delta*u) of a group's tokens.
     float2 dd[2][SUB];
-
-    auto fetch_records = [&](auto bufc, int64_t t) {  // t: first token of the group, from t_begin
-      constexpr int BUF = decltype(bufc)::value;
-      cf32x16_p src = (cf32x16_p)(bc_row + t * (2 * NPL));
-#pragma unroll
-      for (int v = 0; v < GS::VEC16; ++v) {
-        const f32x16_t x = src[v];
-#pragma unroll
-        for (int k = 0; k < 16; ++k) rec[BUF][16 * v + k] = x[k];
-      }
-    };
     auto fetch_dd = [&](auto parc, auto bufc, int g) {
       constexpr int P = decltype(parc)::value;
       constexpr int BUF = decltype(bufc)::value;
@@ -449,19 +445,18 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       for (int q = 0; q < SUB; ++q) dd[BUF][q] = sDU[P][g * SUB + q][lane];
     };
 
-    // Group g of the block with parity P from buffer BUF.  The next group's
-    // records (the next block's first group after the last one) and staged
-    // values are fetched into the other buffer while this one computes.
-    auto group = [&](auto parc, auto bufc, auto gc, int64_t t0, float& block_delta) {
+    // Group g of the block with parity P from buffer BUF: the next group's
+    // staged values are fetched into the other buffer while this one computes.
+    auto group = [&](auto parc, auto bufc, auto gc, float& block_delta) {
       constexpr int BUF = decltype(bufc)::value;
       constexpr int g = decltype(gc)::value;
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_sched_barrier(0);
-      fetch_records(IC<1 - BUF>{}, t0 + (g + 1) * SUB);
       if constexpr (g + 1 < NG) fetch_dd(parc, IC<1 - BUF>{}, g + 1);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int q = 0; q < SUB; ++q) update(parc, dd[BUF][q], &rec[BUF][q * 2 * NPL], g * SUB + q, block_delta);
+      [&]<int... Q>(std::integer_sequence<int, Q...>) {
+        (update(parc, gc, IC<Q>{}, dd[BUF][Q], block_delta), ...);
+      }(std::make_integer_sequence<int, SUB>{});
     };
 
     // Block k (parity P = k % 2, ring slot S = k % kRing): epilogue of k-1,
@@ -473,14 +468,14 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       constexpr int Sp1 = (S + 1) % kRing;          // block k+1
       static_assert((S + kPD + 1) % kRing == Sm1, "ring");
       IC<P> parc;
-      const int64_t t0 = static_cast<int64_t>(k) * TB;
       fetch_dd(parc, IC<0>{}, 0);
       if (k > k_begin) epilogue(IC<1 - P>{}, IC<Sm1>{}, k - 1);
       prologue(IC<1 - P>{}, IC<Sp1>{}, k + 1);
       issue_loads(IC<Sm1>{}, k + kPD + 1);
+      load_records(IC<1 - P>{}, k + 1);
       float block_delta = 0.0f;
       [&]<int... I>(std::integer_sequence<int, I...>) {
-        ((group(parc, IC<I % 2>{}, IC<I>{}, t0, block_delta)), ...);
+        ((group(parc, IC<I % 2>{}, IC<I>{}, block_delta)), ...);
       }(std::make_integer_sequence<int, NG>{});
       delta_total += block_delta;
       __syncthreads();
@@ -490,7 +485,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     [&]<int... I>(std::integer_sequence<int, I...>) {
       (issue_loads(IC<I>{}, k_begin + I), ...);
     }(std::make_integer_sequence<int, kPD + 1>{});
-    fetch_records(IC<0>{}, static_cast<int64_t>(k_begin) * TB);
+    load_records(IC<0>{}, k_begin);
     prologue(IC<0>{}, IC<0>{}, k_begin);
     __syncthreads();
     for (int k = k_begin; k < k_end; k += kRing) {

@@ -12,19 +12,19 @@
 namespace ssm {
 
 // (npl, G): states per lane and wavefronts; vw: prologue width (the
-// variant's preferred width, else 1); touch: L2 touch of B/C records; tb:
-// tokens per block (16, or 32 where variant_has_tb32).  Returns
-// hipErrorInvalidValue for a variant that does not exist.
+// variant's preferred width, else 1); tb: tokens per block (16, or 32 where
+// variant_has_tb32).  Returns hipErrorInvalidValue for a variant that does
+// not exist.
 template <class IO, int MODE>
-hipError_t launch_scan(int npl, int G, int vw, bool touch, int tb, const ScanParams& p, dim3 grid, hipStream_t s);
+hipError_t launch_scan(int npl, int G, int vw, int tb, const ScanParams& p, dim3 grid, hipStream_t s);
 
 // Instantiated (each in its own translation unit) for these six combinations.
-extern template hipError_t launch_scan<F32, kModeFull>(int, int, int, bool, int, const ScanParams&, dim3, hipStream_t);
-extern template hipError_t launch_scan<F32, kModeAgg>(int, int, int, bool, int, const ScanParams&, dim3, hipStream_t);
-extern template hipError_t launch_scan<F32, kModeChained>(int, int, int, bool, int, const ScanParams&, dim3, hipStream_t);
-extern template hipError_t launch_scan<BF16, kModeFull>(int, int, int, bool, int, const ScanParams&, dim3, hipStream_t);
-extern template hipError_t launch_scan<BF16, kModeAgg>(int, int, int, bool, int, const ScanParams&, dim3, hipStream_t);
-extern template hipError_t launch_scan<BF16, kModeChained>(int, int, int, bool, int, const ScanParams&,
+extern template hipError_t launch_scan<F32, kModeFull>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<F32, kModeAgg>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<F32, kModeChained>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeFull>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeAgg>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeChained>(int, int, int, int, const ScanParams&,
                                                            dim3, hipStream_t);
 
 // Variants (states per lane, wavefronts).  Each exists with its preferred

@@ -49,7 +49,6 @@ struct Plan {
   int Ks;        // chunks per split tile
   int64_t chunk_len;
   int64_t Lp;    // sequence length rounded up to whole token blocks (packed B/C rows)
-  bool touch;    // L2 touch of upcoming B/C records (scan_kernel's TOUCH)
   bool chained;  // split tiles chain their carries inside the one scan launch
   int tb;        // tokens per block of the readout scan (16, or 32 with a CU per workgroup)
 };
@@ -80,7 +79,6 @@ Layout layout_for(const Plan& pl, int64_t batch) {
 //                                 (or absent) keeps the planner's split;
 //   SSM_SCAN_CHAINED=0|1          chunks chain their carries in the scan launch
 //                                 (1) or go through the pair and carry passes (0);
-//   SSM_SCAN_TOUCH=0|1            L2 touch of upcoming B/C records;
 //   SSM_SCAN_CHAIN_K=k            chunks per left-over tile in a chained plan;
 //   SSM_SCAN_TB=16|32             tokens per block of the readout scan, where
 //                                 the variant has both.
@@ -205,12 +203,6 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
   pl->chunk_len = chunk;
   pl->Lp = ceil_div(L, kTrip) * kTrip;
   pl->chained = chained;
-  // With at most one tile per CU (and in chained plans) a CU holds one
-  // workgroup and the scalar loads' latency is exposed (or the records
-  // stream from HBM): touch them into L2.
-  pl->touch = T <= kNumCU || chained;
-  const int env_touch = env_flag("SSM_SCAN_TOUCH");
-  if (env_touch >= 0) pl->touch = env_touch == 1;
   // 32-token blocks (half the barriers, all of the LDS) where every
   // workgroup of the readout scan has a CU to itself.
   const bool tb32_ok = variant_has_tb32(npl, G, vw, kModeFull);
@@ -255,10 +247,10 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
   if (e != hipSuccess) return e;
   const dim3 grid_full(static_cast<unsigned>(pl.n_long + static_cast<int64_t>(pl.n_split) * pl.Ks));
   if (pl.chained)  // one workgroup per whole tile, each also running at most one chunk
-    return launch_scan<IO, kModeChained>(pl.npl, pl.G, pl.vw, pl.touch, pl.tb, p, dim3(pl.n_long), s);
+    return launch_scan<IO, kModeChained>(pl.npl, pl.G, pl.vw, pl.tb, p, dim3(pl.n_long), s);
   if (pl.n_split > 0 && pl.Ks > 1) {
     const dim3 grid_agg(static_cast<unsigned>(static_cast<int64_t>(pl.n_split) * (pl.Ks - 1)));
-    e = launch_scan<IO, kModeAgg>(pl.npl, pl.G, pl.vw, pl.touch, 16, p, grid_agg, s);
+    e = launch_scan<IO, kModeAgg>(pl.npl, pl.G, pl.vw, 16, p, grid_agg, s);
     if (e != hipSuccess) return e;
     const int64_t cols = static_cast<int64_t>(pl.n_split) * 64 * npad;
     hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>(ceil_div(cols, kCarryCols))), dim3(256), 0, s,
@@ -267,7 +259,7 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_scan<IO, kModeFull>(pl.npl, pl.G, pl.vw, pl.touch, pl.tb, p, grid_full, s);
+  return launch_scan<IO, kModeFull>(pl.npl, pl.G, pl.vw, pl.tb, p, grid_full, s);
 }
 
 template <class IO>

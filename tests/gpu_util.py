@@ -134,13 +134,6 @@ class Chained(_Env):
         super().__init__("SSM_SCAN_CHAINED", "1" if on else "0")
 
 
-class Touch(_Env):
-    """Temporarily force the L2 touch of upcoming B/C records on (True) or off (False)."""
-
-    def __init__(self, on):
-        super().__init__("SSM_SCAN_TOUCH", "1" if on else "0")
-
-
 class BlockLen(_Env):
     """Temporarily force the readout scan's tokens per block (16 or 32) where the variant has both."""
 

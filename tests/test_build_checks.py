@@ -1,0 +1,41 @@
+"""The build's DPP hazard scan (selective_state_space_33_amd/build.py, dpp_hazards) on small
+assembly fragments: every planted hazard is found, and correctly separated code passes."""
+from selective_state_space_33_amd.build import dpp_hazards
+
+ASM_DPP = ";;#ASMSTART\n\tv_fmac_f32_dpp v0, v5, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf\n;;#ASMEND\n"
+
+
+def test_source_written_by_a_load_only_is_clean():
+    asm = "\tbuffer_load_dword v5, v1, s[4:7], 0 offen\n\ts_waitcnt vmcnt(0)\n" + ASM_DPP
+    assert dpp_hazards(asm) == []
+
+
+def test_valu_write_of_the_source_right_before_is_found():
+    asm = "\tv_mov_b32_e32 v5, v1\n" + ASM_DPP
+    assert len(dpp_hazards(asm)) == 1
+
+
+def test_one_wait_state_is_not_enough_two_are():
+    assert len(dpp_hazards("\tv_add_f32_e32 v5, v1, v2\n\tv_mul_f32_e32 v7, v1, v2\n" + ASM_DPP)) == 1
+    assert dpp_hazards("\tv_add_f32_e32 v5, v1, v2\n\ts_nop 1\n" + ASM_DPP) == []
+    assert dpp_hazards("\tv_add_f32_e32 v5, v1, v2\n\tv_mul_f32_e32 v7, v1, v2\n\ts_nop 0\n" + ASM_DPP) == []
+
+
+def test_register_ranges_and_other_registers():
+    assert len(dpp_hazards("\tv_lshl_add_u64 v[4:5], v[2:3], 2, s[8:9]\n" + ASM_DPP)) == 1
+    assert dpp_hazards("\tv_lshl_add_u64 v[6:7], v[2:3], 2, s[8:9]\n" + ASM_DPP) == []
+    # the DPP operand is src0 only; writing the other source is not this hazard
+    assert dpp_hazards("\tv_mov_b32_e32 v2, v1\n" + ASM_DPP) == []
+
+
+def test_exec_written_by_valu_needs_five_wait_states():
+    cmpx = "\tv_cmpx_gt_u32_e32 vcc, 16, v0\n"
+    assert len(dpp_hazards(cmpx + "\ts_nop 3\n" + ASM_DPP)) == 1
+    assert dpp_hazards(cmpx + "\ts_nop 4\n" + ASM_DPP) == []
+
+
+def test_inline_asm_dpp_right_after_a_label_is_found():
+    assert len(dpp_hazards(".LBB0_3:\n" + ASM_DPP)) == 1
+    assert dpp_hazards(".LBB0_3:\n\ts_nop 4\n" + ASM_DPP) == []
+    # compiler-emitted DPP after a label is the compiler's to protect
+    assert dpp_hazards(".LBB0_3:\n\tv_mul_f32_dpp v1, v5, v2 row_newbcast:1 row_mask:0xf bank_mask:0xf\n") == []
