@@ -133,13 +133,12 @@ constexpr int kPD = 2;
 constexpr int kRing = kPD + 2;
 // Tokens per unrolled trip of the main loop at the longest block.  Chunk
 // lengths and the packed B/C rows are multiples of it (so of every variant's
-// trip); one group of records past the end is read (and not used), so the
-// packed buffer carries kTBMax rows of padding.
+// trip).  A pass loads the records of one block past its end (not used);
+// whatever of them lies past the packed buffer reads as zero through the
+// buffer resource's range check.
 constexpr int kTrip = kRing * kTBMax;
 
-// lgkmcnt(0) with vmcnt and expcnt left at their maxima, and vmcnt(0) with
-// expcnt and lgkmcnt left at theirs (gfx9 s_waitcnt encoding).
-constexpr int kWaitLgkm0 = 0xC07F;
+// vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 s_waitcnt encoding).
 constexpr int kWaitVm0 = 0x0F70;
 
 // Pack B and C ([batch][L][N], fp32 or bf16) into fp32 per-group records
@@ -447,13 +446,12 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 
     // Group g of the block with parity P from buffer BUF: the next group's
     // staged values are fetched into the other buffer while this one computes.
+    // (The only waits in the scan are on these LDS reads, which complete in
+    // order, so the compiler's own wait counts and schedule are left free.)
     auto group = [&](auto parc, auto bufc, auto gc, float& block_delta) {
       constexpr int BUF = decltype(bufc)::value;
       constexpr int g = decltype(gc)::value;
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-      __builtin_amdgcn_sched_barrier(0);
       if constexpr (g + 1 < NG) fetch_dd(parc, IC<1 - BUF>{}, g + 1);
-      __builtin_amdgcn_sched_barrier(0);
       [&]<int... Q>(std::integer_sequence<int, Q...>) {
         (update(parc, gc, IC<Q>{}, dd[BUF][Q], block_delta), ...);
       }(std::make_integer_sequence<int, SUB>{});
