@@ -180,15 +180,20 @@ template <> __device__ __forceinline__ float load_elem<BF16>(const void* base, i
   return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(base)[idx]) << 16);
 }
 
-// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).
-// log1p(e) uses a short series when e < 1/16 (relative error < 2e-7) and
-// log2(1 + e) * ln 2 otherwise (relative error < 1e-6), so no branch diverges.
-__device__ __forceinline__ float softplus_f(float x) {
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e^-|x|).  With e = e^-|x|
+// and u = 1 + e rounded to fp32, log1p(e) = ln 2 * log2(u) + (e - (u - 1)):
+// the second term is the rounding error of u (exact, since u - 1 is), which
+// keeps the sum accurate where e is tiny.  The hardware log2 is accurate to
+// ~1 ulp relative also next to 1, so no series or branch is needed; measured
+// on [-30, 30] the result is within 2e-6 relative of the exact value (the
+// rounding of the exp argument dominates).
+__device__ __forceinline__ float log1p_exp_neg_abs(float x) {
   const float e = __builtin_amdgcn_exp2f(-__builtin_fabsf(x) * kLog2e);
-  const float viaLog = __builtin_amdgcn_logf(1.0f + e) * kLn2;
-  const float series = e * (1.0f + e * (-0.5f + e * (1.0f / 3.0f + e * (-0.25f + e * 0.2f))));
-  return __builtin_fmaxf(x, 0.0f) + (e < 0.0625f ? series : viaLog);
+  const float u = 1.0f + e;
+  const float c = e - (u - 1.0f);
+  return __builtin_fmaf(__builtin_amdgcn_logf(u), kLn2, c);
 }
+__device__ __forceinline__ float softplus_f(float x) { return __builtin_fmaxf(x, 0.0f) + log1p_exp_neg_abs(x); }
 
 // Lane K (0..15) of each 16-lane row of v, broadcast across the row (DPP
 // row_newbcast; the compiler folds it into a multiply's first operand).

@@ -218,7 +218,10 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   int voff_rel[RPT];                      // (in units of token rows and elements; scaled by set_tile)
 #pragma unroll
   for (int i = 0; i < RPT; ++i) voff_rel[i] = prow + i * ROWSTEP;
-  const bool softplus_on = p.softplus != 0;
+  // delta = fma(sp_k, log1p(e^-|x|), max(x, sp_lo)): softplus(x) when on
+  // (sp_k = 1, sp_lo = 0), x itself when off (sp_k = 0, sp_lo = -inf)
+  const float sp_k = p.softplus != 0 ? 1.0f : 0.0f;
+  const float sp_lo = p.softplus != 0 ? 0.0f : -__builtin_inff();
   const int row_bytes = static_cast<int>(dim * ES);
   const int blk_bytes = TB * row_bytes;
 
@@ -341,10 +344,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 #pragma unroll
         for (int e = 0; e < VW; ++e) {
           const float x = df[e] + biasv[e];
-          // softplus is evaluated either way and selected, so no branch splits
-          // the loop body (the flag is uniform, the select is one v_cndmask)
-          float dl = softplus_f(x);
-          dl = softplus_on ? dl : x;
+          // evaluated either way, so no branch splits the loop body
+          float dl = __builtin_fmaf(sp_k, log1p_exp_neg_abs(x), __builtin_fmaxf(x, sp_lo));
           dl = live ? dl : 0.0f;  // padding token: the identity step (1, 0)
           out[e] = make_float2(dl, dl * uf[e]);
         }
