@@ -7,4 +7,7 @@ product path never does, and the two share no code.
 
 The arithmetic lives in ``ssm_ref.c`` (plain C, fp64); ``ref.py`` marshals
 numpy arrays into it.  Parity pins are in ``tests/test_oracle_pins.py``.
+``bwd.py`` is the backward pass: fp64 automatic differentiation (torch, CPU)
+of its own transcription of the forward, pinned in ``tests/test_oracle_bwd.py``
+against the C oracle's forward and central finite differences of it.
 """

@@ -1,0 +1,86 @@
+"""fp64 CPU oracle for the backward pass of the selective scan.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py): the test-suite and the
+smoke check may call it; the product path never does.
+
+The pages do not spell out a backward pass. They only say that the
+intermediate states are recomputed rather than stored when training ([P1]
+"Keeping the pad on the desk"; [P4] "The Selection Mechanism: Why Mamba
+Works"; [P5] "The Hardware-Aware Way Out", rematerialization).  The
+gradients themselves are fixed by the forward definition, so this oracle is
+reverse-mode automatic differentiation (torch.autograd, CPU, float64) of a
+plain transcription of the forward recurrence:
+
+    x_t  = delta_raw_t + bias                  Delta_t = softplus(x_t) or x_t
+    h_t  = exp(Delta_t * A) * h_{t-1} + Delta_t * u_t * B_t      (h_{-1} = 0)
+    v_t  = sum_n C_t[n] h_t[n] + D * u_t
+    y_t  = v_t * SiLU(z_t)   (or v_t without z)
+
+with softplus(x) = log(1 + e^x) exact (log-add-exp, no threshold) and
+SiLU(z) = z * sigmoid(z).  The scalar differentiated is
+    sum(y * dy) + sum(final_state * dfinal_state),
+so the result is the vector-Jacobian product for output gradients dy (and
+dfinal_state, the gradient reaching the final state, if any).
+
+The transcription is independent of the C oracle (ssm_ref.c); the tests pin
+it to that oracle's forward and to central finite differences of it.
+"""
+import numpy as np
+import torch
+
+
+def _t(x):
+    return None if x is None else torch.tensor(np.asarray(x, dtype=np.float64), dtype=torch.float64)
+
+
+def forward_torch(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True):
+    """The forward recurrence on float64 torch tensors; returns (y, final_state)."""
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    x = delta if delta_bias is None else delta + delta_bias
+    dl = torch.logaddexp(x, torch.zeros_like(x)) if softplus else x
+    h = torch.zeros((batch, dim, N), dtype=torch.float64)
+    ys = []
+    for t in range(L):
+        a = torch.exp(dl[:, t, :, None] * A[None, :, :])            # [batch, dim, N]
+        b = (dl[:, t, :] * u[:, t, :])[:, :, None] * B[:, t, None, :]
+        h = a * h + b
+        v = (h * C[:, t, None, :]).sum(-1)                           # [batch, dim]
+        if D is not None:
+            v = v + D[None, :] * u[:, t, :]
+        ys.append(v)
+    y = torch.stack(ys, dim=1)
+    if z is not None:
+        y = y * (z * torch.sigmoid(z))
+    return y, h
+
+
+def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, dfinal_state=None):
+    """Gradients of sum(y*dy) + sum(final_state*dfinal_state) with respect to every input.
+
+    Returns a dict of float64 numpy arrays: du, ddelta, dA, dB, dC, and dD, dz,
+    ddelta_bias for the optional inputs that were given (None otherwise)."""
+    names = ["u", "delta", "A", "B", "C", "D", "z", "delta_bias"]
+    vals = [u, delta, A, B, C, D, z, delta_bias]
+    ts = {}
+    for n, v in zip(names, vals):
+        tv = _t(v)
+        if tv is not None:
+            tv.requires_grad_(True)
+        ts[n] = tv
+    y, fs = forward_torch(ts["u"], ts["delta"], ts["A"], ts["B"], ts["C"], D=ts["D"], z=ts["z"],
+                          delta_bias=ts["delta_bias"], softplus=softplus)
+    obj = (y * _t(dy)).sum()
+    if dfinal_state is not None:
+        obj = obj + (fs * _t(dfinal_state)).sum()
+    leaves = [ts[n] for n in names if ts[n] is not None]
+    grads = torch.autograd.grad(obj, leaves, allow_unused=True)
+    out = {}
+    gi = iter(grads)
+    for n in names:
+        if ts[n] is None:
+            out["d" + n] = None
+        else:
+            g = next(gi)
+            out["d" + n] = np.zeros(np.shape(ts[n].detach().numpy())) if g is None else g.detach().numpy()
+    return out

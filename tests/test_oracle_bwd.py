@@ -1,0 +1,116 @@
+"""Pins of the fp64 backward oracle (oracle/bwd.py), all on the CPU.
+
+The backward oracle is automatic differentiation of its own transcription of
+the forward recurrence.  It is pinned against things outside itself:
+  - that transcription's forward equals the C oracle's forward (pinned in
+    test_oracle_pins.py against the pages and closed forms);
+  - central finite differences of the C oracle's forward, for every input,
+    with and without the optional inputs, and through the final state;
+  - gradients of the pages' two-token relay example ([P1] "The relay"),
+    derived by hand.
+"""
+import numpy as np
+import pytest
+
+from oracle import bwd as OB
+from oracle import ref as R
+
+
+def _inputs(rng, batch, L, dim, N, gated=True):
+    x = dict(
+        u=rng.standard_normal((batch, L, dim)),
+        delta=rng.standard_normal((batch, L, dim)) * 0.5 - 1.0,
+        A=-np.exp(rng.standard_normal((dim, N)) * 0.5),
+        B=rng.standard_normal((batch, L, N)),
+        C=rng.standard_normal((batch, L, N)),
+        D=rng.standard_normal(dim),
+        z=rng.standard_normal((batch, L, dim)) if gated else None,
+        delta_bias=rng.standard_normal(dim) * 0.3,
+    )
+    return x
+
+
+def _rel(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+@pytest.mark.parametrize("softplus,gated", [(True, True), (False, False), (True, False)])
+def test_transcription_forward_equals_c_oracle(softplus, gated):
+    rng = np.random.default_rng(7)
+    x = _inputs(rng, 2, 9, 5, 3, gated=gated)
+    import torch
+    t = {k: (None if v is None else torch.tensor(v)) for k, v in x.items()}
+    y, fs = OB.forward_torch(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                             delta_bias=t["delta_bias"], softplus=softplus)
+    yo, fo = R.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                        delta_bias=x["delta_bias"], softplus=softplus)
+    assert _rel(y.numpy(), yo) < 1e-13 and _rel(fs.numpy(), fo) < 1e-13
+
+
+def _objective(x, dy, dfs, softplus):
+    y, fs = R.scan_fwd(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                       delta_bias=x["delta_bias"], softplus=softplus)
+    val = float(np.sum(y * dy))
+    if dfs is not None:
+        val += float(np.sum(fs * dfs))
+    return val
+
+
+@pytest.mark.parametrize("softplus,gated,with_fs", [(True, True, False), (True, True, True), (False, False, True)])
+def test_gradients_match_central_differences_of_c_oracle(softplus, gated, with_fs):
+    rng = np.random.default_rng(11 + 2 * softplus + gated)
+    batch, L, dim, N = 2, 7, 3, 4
+    x = _inputs(rng, batch, L, dim, N, gated=gated)
+    if not gated:
+        x["D"] = None
+        x["delta_bias"] = None
+    if not softplus:
+        # without softplus delta is used as the step as given: keep it a positive step size
+        x["delta"] = np.abs(x["delta"]) + 0.05
+    dy = rng.standard_normal((batch, L, dim))
+    dfs = rng.standard_normal((batch, dim, N)) if with_fs else None
+    g = OB.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"],
+                    delta_bias=x["delta_bias"], softplus=softplus, dfinal_state=dfs)
+    checked = 0
+    for name in ["u", "delta", "A", "B", "C", "D", "z", "delta_bias"]:
+        if x[name] is None:
+            assert g["d" + name] is None
+            continue
+        flat = x[name].reshape(-1)
+        idx = rng.choice(flat.size, size=min(6, flat.size), replace=False)
+        for i in idx:
+            h = 1e-6 * max(1.0, abs(flat[i]))
+            orig = flat[i]
+            flat[i] = orig + h
+            fp = _objective(x, dy, dfs, softplus)
+            flat[i] = orig - h
+            fm = _objective(x, dy, dfs, softplus)
+            flat[i] = orig
+            fd = (fp - fm) / (2 * h)
+            an = g["d" + name].reshape(-1)[i]
+            assert abs(an - fd) <= 2e-7 * max(1.0, abs(fd)), (name, i, an, fd)
+            checked += 1
+    assert checked >= 20
+
+
+def test_relay_example_gradients_by_hand():
+    """[P1] "The relay": two steps (a1,b1) = (0.6, 0.4) and (a2,b2) = (0.5, 1.0) on N = 1 with A = -1,
+    C = 1, u = 1, no softplus, bias, D or gate.  Then y = (b1, a2*b1 + b2) = (0.4, 1.2) and, for dy = (1, 1),
+    the objective y1 + y2 = b1*(1 + a2) + b2, whose derivatives follow by hand."""
+    d1, d2 = -np.log(0.6), -np.log(0.5)
+    u = np.ones((1, 2, 1))
+    delta = np.array([d1, d2]).reshape(1, 2, 1)
+    A = np.array([[-1.0]])
+    B = np.array([0.4 / d1, 1.0 / d2]).reshape(1, 2, 1)
+    C = np.ones((1, 2, 1))
+    dy = np.ones((1, 2, 1))
+    g = OB.scan_bwd(u, delta, A, B, C, dy, softplus=False)
+    a2, b1 = 0.5, 0.4
+    np.testing.assert_allclose(g["dC"].ravel(), [0.4, 1.2], rtol=1e-14)              # dC_t = h_t
+    np.testing.assert_allclose(g["du"].ravel(), [b1 * (1 + a2), 1.0], rtol=1e-14)    # b_t is linear in u_t
+    np.testing.assert_allclose(g["dB"].ravel(), [d1 * (1 + a2), d2], rtol=1e-14)     # db_t/dB_t = Delta_t u_t
+    # d/dDelta_1: only b1 = Delta_1 B_1 depends on it (h_0 = 0 hides a1); d/dDelta_2: a2 = e^{-Delta_2}, b2
+    np.testing.assert_allclose(g["ddelta"].ravel(), [(0.4 / d1) * (1 + a2), -a2 * b1 + 1.0 / d2], rtol=1e-13)
+    # dA: a2 = exp(Delta_2 A), da2/dA = Delta_2 a2, times d(obj)/da2 = b1
+    np.testing.assert_allclose(g["dA"].ravel(), [d2 * a2 * b1], rtol=1e-13)
