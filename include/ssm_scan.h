@@ -106,6 +106,43 @@ ssm_status_t ssm_state_update(float* state, const void* u, const void* delta, co
                               int softplus_flag, void* y, int64_t batch, int64_t dim, int64_t dstate,
                               ssm_dtype_t dt, hipStream_t stream);
 
+/* Bytes of device workspace that ssm_scan_bwd needs for this shape (always
+ * > 0 for a valid shape): the packed B/C records, the state entering every
+ * 16-token block of every 64-channel tile (about batch * L * dim * dstate *
+ * 4 / 16 bytes), and per-tile partial sums of dB and dC (about 2 * batch *
+ * L * dim / 64 * dstate * 4 bytes) and of dA, dD and d(delta_bias) per batch
+ * row.  Returns 0 for arguments ssm_scan_bwd would reject. */
+size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt);
+
+/* Backward of ssm_scan_fwd: the gradients of
+ *     sum(y * dy) + sum(final_state * dfinal_state)
+ * with respect to u, delta, A, B, C, D, z and delta_bias, for the same
+ * inputs and flags as the forward call.  The states are recomputed from the
+ * inputs, not stored by the forward ("Mamba is attention all you really need,
+ * part 2", "Keeping the pad on the desk"; "The state that must remember
+ * everything", "The Hardware-Aware Way Out", rematerialization).
+ *   Inputs as for ssm_scan_fwd, plus dy [batch, L, dim] in dtype dt and
+ *   dfinal_state [batch, dim, dstate] fp32 (NULL: no gradient reaches the
+ *   final state).
+ *   Outputs, all overwritten: du, ddelta [batch, L, dim], dB, dC [batch, L,
+ *   dstate] in dtype dt (gradients of the sequence inputs, rounded like y);
+ *   dA [dim, dstate] fp32.  dD [dim], dz [batch, L, dim] (dtype dt) and
+ *   ddelta_bias [dim] fp32 are written when both the input (D, z,
+ *   delta_bias) and the output pointer are non-NULL.  The gradient of delta
+ *   is the one of the raw input (through softplus and the bias when on).
+ *   dA, dD and ddelta_bias sum over the batch and the sequence, dB and dC
+ *   over the channels, in a fixed order (results are deterministic).
+ *   No output may alias an input or another output.  workspace must hold
+ *   ssm_scan_bwd_workspace_size() bytes of device memory, 256-byte aligned.
+ *   UNSUPPORTED for dstate > 32 or batch > 65535. */
+ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                          const void* dy, const float* dfinal_state,
+                          void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                          float* ddelta_bias,
+                          int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static, human-readable name of a status code (never NULL). */
 const char* ssm_status_string(ssm_status_t s);
 

@@ -1,0 +1,379 @@
+// bwd_kernels.hpp -- gfx950 kernels of the selective scan backward pass.
+//
+// The forward per (batch b, channel d), as ssm_scan_fwd computes it:
+//   x_t = delta_raw_t + bias,  Delta_t = softplus(x_t) (or x_t),
+//   a_t = exp(Delta_t A),  h_t = a_t h_{t-1} + Delta_t u_t B_t,
+//   v_t = C_t . h_t + D u_t,  y_t = v_t SiLU(z_t) (or v_t).
+// Its gradients for output gradients dy (and dh_L, reaching the final state):
+//   dv_t = dy_t SiLU(z_t),  dz_t = dy_t v_t SiLU'(z_t),
+//   dh_t = C_t dv_t + a_{t+1} dh_{t+1}                       (adjoint, in reverse)
+//   per state: t_a = dh_t h_{t-1} a_t,  dA += t_a Delta_t,  dB_t += dh_t Delta_t u_t (over d),
+//              dC_t += dv_t h_t (over d);
+//   dDelta_t = sum_n (t_a A + dh_t B_t u_t),  du_t = Delta_t sum_n dh_t B_t + D dv_t,
+//   ddelta_raw_t = dDelta_t softplus'(x_t),  dbias += ddelta_raw_t,  dD += dv_t u_t.
+// The intermediate states are recomputed, not stored by the forward ("Mamba
+// is attention all you really need, part 2", "Keeping the pad on the desk";
+// "The state that must remember everything", "The Hardware-Aware Way Out"):
+// a forward launch (scan_kernel, checkpoint mode) leaves only the state
+// entering every 16-token block, and the backward kernel rebuilds each
+// block's states from it, in registers, just before running the adjoint back
+// through the block.
+//
+// scan_bwd_kernel: one workgroup per tile of 64 channels of one batch row,
+// the forward's layout (G wavefronts, wavefront w owning states w*NPL ..,
+// one channel per lane, B/C records by DPP row broadcast).  Blocks are taken
+// from the last to the first; per block:
+//   P  every thread: (Delta, Delta*u) and dv of its (token, channel) elements
+//      into LDS; u, Delta, softplus' and dy*SiLU'(z) stay in its registers;
+//   F  every wavefront: recompute its states through the block from the
+//      checkpoint, keeping h_t and a_t in registers, and its partial readout
+//      in LDS;
+//   E1 every thread: v_t = the partial readouts summed in a fixed order +
+//      D u_t, and dz_t;
+//   R  every wavefront: the adjoint back through the block; per token its
+//      partial sums over its states of t_a A and dh B (to LDS), and per state
+//      the dB, dC partials summed over the 16 lanes of each row (DPP) to LDS;
+//   E2 every thread: du, ddelta_raw of its elements; the tile's dB, dC
+//      partials (the 4 row sums) to the workspace.
+// dA, dD and dbias accumulate in registers over the whole sequence.  Partial
+// sums over tiles (dB, dC) and over batch rows (dA, dD, dbias) are added in
+// a fixed order by bwd_reduce_*; so every result is deterministic.
+#pragma once
+
+#include <utility>
+
+#include "common.hpp"
+
+namespace ssm {
+
+struct BwdParams {
+  const void* u;
+  const void* delta;
+  const float* A;
+  const float* D;      // nullable
+  const void* z;       // nullable
+  const float* bias;   // nullable
+  const float* bc;     // packed B/C records [batch][G][Lp][2*NPL] (as the forward's)
+  const float* ckpt;   // state entering every block: [tiles][ckpt_blocks][64][NPL*G]
+  const void* dy;
+  const float* dfs;    // nullable: gradient reaching the final state [batch][dim][N]
+  void* du;
+  void* ddelta;
+  void* dz;            // nullable
+  float* dA_part;      // [batch][dim][NPL*G]
+  float* dD_part;      // [batch][dim]
+  float* dbias_part;   // [batch][dim]
+  float* dB_part;      // [batch][ntd][Lp][NPL*G]
+  float* dC_part;
+  int64_t batch, L, Lp, dim, N, ckpt_blocks;
+  int ntd;
+  int softplus;
+};
+
+constexpr int kBwdTB = 16;  // tokens per block (the checkpoint spacing)
+
+// Sum over the 16 lanes of each row, left in the row's last lane (DPP row
+// shifts; lanes shifted in from outside the row read zero).
+__device__ __forceinline__ float row_sum_to_last(float x) {
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true));
+  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true));
+  return x;
+}
+
+template <class IO, int NPL, int G>
+__global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
+  constexpr int TB = kBwdTB;
+  constexpr int NPAD = NPL * G;
+  constexpr int RPT = TB / G;               // element rows per thread
+  static_assert(TB % G == 0, "element rows");
+  constexpr int NRV = TB * 2 * NPL / 16;    // record registers per block
+  static_assert((TB * 2 * NPL) % 16 == 0, "records fill whole registers");
+  constexpr int ES = __is_same(IO, F32) ? 4 : 2;
+
+  __shared__ float2 sDU[TB][64];             // (Delta, Delta*u)
+  __shared__ float sDV[TB][64];              // dv
+  __shared__ float2 sYS[G][TB][64];          // readout partials (.x), then (sum t_a A, sum dh B)
+  __shared__ float sRB[TB][NPAD][4];         // dB partials: one sum per 16-lane row
+  __shared__ float sRC[TB][NPAD][4];
+  __shared__ float sAcc[2][G][64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = w * NPL;
+  const int tile = blockIdx.x;
+  const int64_t b = tile / p.ntd;
+  const int64_t d0 = static_cast<int64_t>(tile % p.ntd) * 64;
+  const int64_t d = d0 + lane;
+  const int64_t dim = p.dim, L = p.L, N = p.N;
+  const bool dvalid = d < dim;
+
+  float A2[NPL], An[NPL], dhn[NPL], dAacc[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int n = n0 + j;
+    const bool ok = dvalid && n < N;
+    An[j] = ok ? p.A[d * N + n] : 0.0f;
+    A2[j] = An[j] * kLog2e;
+    dhn[j] = (ok && p.dfs) ? p.dfs[(b * dim + d) * N + n] : 0.0f;
+    dAacc[j] = 0.0f;
+  }
+  const float Dd = (dvalid && p.D) ? p.D[d] : 0.0f;
+  const float bias_d = (dvalid && p.bias) ? p.bias[d] : 0.0f;
+  const bool has_z = p.z != nullptr;
+  const bool sp_on = p.softplus != 0;
+
+  // Token rows of the tile (channels d0 .. d0+63 of batch row b), through
+  // buffer resources: rows past L read as zero and their stores are dropped;
+  // lanes past dim are masked at the stores.  The host keeps L rows of the
+  // tensor within 2^31 bytes.
+  const int row_bytes = static_cast<int>(dim * ES);
+  const int64_t base_off = (b * L * dim + d0) * ES;
+  const int64_t bytes = L * row_bytes - d0 * ES;
+  auto rs_of = [&](const void* ptr) {
+    return make_rsrc(ptr ? static_cast<const char*>(ptr) + base_off : nullptr, ptr ? bytes : 0);
+  };
+  const rsrc_t rs_u = rs_of(p.u), rs_d = rs_of(p.delta), rs_z = rs_of(p.z), rs_dy = rs_of(p.dy);
+  const rsrc_t rs_du = rs_of(p.du), rs_dd = rs_of(p.ddelta), rs_dz = rs_of(p.dz);
+  const float* bc_row = p.bc + ((b * G + w) * p.Lp) * (2 * NPL);
+  const rsrc_t rs_bc = make_rsrc(bc_row, (p.Lp + 32) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
+  const int rec_voff = (lane & 15) * 4;
+  const float* ckpt_row = p.ckpt + (static_cast<int64_t>(tile) * p.ckpt_blocks * 64 + lane) * NPAD + n0;
+
+  float accD = 0.0f, accBias = 0.0f;
+  const int nblk = static_cast<int>((L + TB - 1) / TB);
+
+  for (int k = nblk - 1; k >= 0; --k) {
+    const int t0 = k * TB;
+    // this block's records and the state entering it
+    float rv[NRV];
+#pragma unroll
+    for (int v = 0; v < NRV; ++v)
+      rv[v] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rs_bc, rec_voff + t0 * (2 * NPL * 4) + v * 64, 0, 0));
+    float hst[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) hst[j] = dvalid ? ckpt_row[static_cast<int64_t>(k) * 64 * NPAD + j] : 0.0f;
+
+    // ---- P: elements (row, lane) of the block
+    float eu[RPT], edl[RPT], esx[RPT], edv[RPT], egz[RPT];
+    bool elive[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = w + i * G;
+      const int off = (t0 + row) * row_bytes + lane * ES;
+      const bool live = t0 + row < L && dvalid;  // lanes past dim read the next row: keep them at zero
+      float uf, df, zf, gf;
+      unpack<IO, 1>(buf_load<IO, 1>(rs_u, off, 0), &uf);
+      unpack<IO, 1>(buf_load<IO, 1>(rs_d, off, 0), &df);
+      unpack<IO, 1>(buf_load<IO, 1>(rs_z, off, 0), &zf);
+      unpack<IO, 1>(buf_load<IO, 1>(rs_dy, off, 0), &gf);
+      const float x = df + bias_d;
+      float dl = sp_on ? __builtin_fmaxf(x, 0.0f) + log1p_exp_neg_abs(x) : x;
+      dl = live ? dl : 0.0f;  // padding tokens are identity steps
+      // softplus'(x) = sigmoid(x)
+      const float sx = sp_on ? __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e)) : 1.0f;
+      float g = 1.0f, gp = 0.0f;
+      if (has_z) {
+        const float sz = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-zf * kLog2e));
+        g = zf * sz;                                  // SiLU(z)
+        gp = sz * __builtin_fmaf(zf, 1.0f - sz, 1.0f);  // SiLU'(z) = s (1 + z (1 - s))
+      }
+      const float dv = live ? gf * g : 0.0f;
+      sDU[row][lane] = make_float2(dl, dl * uf);
+      sDV[row][lane] = dv;
+      eu[i] = uf;
+      edl[i] = dl;
+      esx[i] = sx;
+      edv[i] = dv;
+      egz[i] = gf * gp;
+      elive[i] = live;
+    }
+    __syncthreads();
+
+    // ---- F: recompute the block's states from the checkpoint
+    float hs[TB][NPL], as[TB][NPL];
+    {
+      float h[NPL];
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) h[j] = hst[j];
+      [&]<int... T>(std::integer_sequence<int, T...>) {
+        (([&] {
+           constexpr int t = T;
+           const float2 dd = sDU[t][lane];
+           float yp = 0.0f;
+           [&]<int... J>(std::integer_sequence<int, J...>) {
+             (([&] {
+                constexpr int j = J;
+                constexpr int fb = t * 2 * NPL + j, fc = fb + NPL;
+                const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
+                h[j] = __builtin_fmaf(a, h[j], dd.y * row_bcast<fb % 16>(rv[fb / 16]));
+                hs[t][j] = h[j];
+                as[t][j] = a;
+                if constexpr (j == 0) yp = row_bcast<fc % 16>(rv[fc / 16]) * h[0];
+                else yp = fmac_row_bcast<fc % 16>(yp, rv[fc / 16], h[j]);
+              }()),
+              ...);
+           }(std::make_integer_sequence<int, NPL>{});
+           sYS[w][t][lane].x = yp;
+         }()),
+         ...);
+      }(std::make_integer_sequence<int, TB>{});
+    }
+    __syncthreads();
+
+    // ---- E1: v and dz of the elements
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = w + i * G;
+      float v = sYS[0][row][lane].x;
+#pragma unroll
+      for (int ww = 1; ww < G; ++ww) v += sYS[ww][row][lane].x;
+      v = __builtin_fmaf(Dd, eu[i], v);
+      if (has_z) {
+        const float dzv = egz[i] * v;
+        const int off = elive[i] ? (t0 + row) * row_bytes + lane * ES : 0x7ffffff0;
+        buf_store<IO, 1>(rs_dz, off, 0, &dzv);
+      }
+    }
+    __syncthreads();
+
+    // ---- R: the adjoint back through the block
+    [&]<int... T>(std::integer_sequence<int, T...>) {
+      (([&] {
+         constexpr int t = TB - 1 - T;
+         const float dv = sDV[t][lane];
+         const float2 dd = sDU[t][lane];
+         float s1 = 0.0f, s2 = 0.0f;
+         float pb[NPL], pc[NPL];
+         [&]<int... J>(std::integer_sequence<int, J...>) {
+           (([&] {
+              constexpr int j = J;
+              constexpr int fb = t * 2 * NPL + j, fc = fb + NPL;
+              const float Bj = row_bcast<fb % 16>(rv[fb / 16]);
+              const float Cj = row_bcast<fc % 16>(rv[fc / 16]);
+              const float dh = __builtin_fmaf(Cj, dv, dhn[j]);
+              float hp;
+              if constexpr (t > 0) hp = hs[t - 1][j];
+              else hp = hst[j];
+              const float ta = dh * hp * as[t][j];
+              s1 = __builtin_fmaf(ta, An[j], s1);
+              s2 = __builtin_fmaf(dh, Bj, s2);
+              dAacc[j] = __builtin_fmaf(ta, dd.x, dAacc[j]);
+              pb[j] = row_sum_to_last(dh * dd.y);
+              pc[j] = row_sum_to_last(dv * hs[t][j]);
+              dhn[j] = as[t][j] * dh;
+            }()),
+            ...);
+         }(std::make_integer_sequence<int, NPL>{});
+         if ((lane & 15) == 15) {
+#pragma unroll
+           for (int j = 0; j < NPL; ++j) {
+             sRB[t][n0 + j][lane >> 4] = pb[j];
+             sRC[t][n0 + j][lane >> 4] = pc[j];
+           }
+         }
+         sYS[w][t][lane] = make_float2(s1, s2);
+       }()),
+       ...);
+    }(std::make_integer_sequence<int, TB>{});
+    __syncthreads();
+
+    // ---- E2: du, ddelta_raw of the elements; the tile's dB, dC partials
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int row = w + i * G;
+      float S1 = sYS[0][row][lane].x, S2 = sYS[0][row][lane].y;
+#pragma unroll
+      for (int ww = 1; ww < G; ++ww) {
+        S1 += sYS[ww][row][lane].x;
+        S2 += sYS[ww][row][lane].y;
+      }
+      const float dDelta = __builtin_fmaf(eu[i], S2, S1);
+      const float duv = __builtin_fmaf(edl[i], S2, Dd * edv[i]);
+      const float ddr = dDelta * esx[i];
+      const int off = elive[i] ? (t0 + row) * row_bytes + lane * ES : 0x7ffffff0;
+      buf_store<IO, 1>(rs_du, off, 0, &duv);
+      buf_store<IO, 1>(rs_dd, off, 0, &ddr);
+      if (elive[i]) {
+        accD = __builtin_fmaf(edv[i], eu[i], accD);
+        accBias += ddr;
+      }
+    }
+    for (int q = tid; q < TB * NPAD; q += 64 * G) {
+      const int t = q / NPAD, n = q % NPAD;
+      const float sb = (sRB[t][n][0] + sRB[t][n][1]) + (sRB[t][n][2] + sRB[t][n][3]);
+      const float sc = (sRC[t][n][0] + sRC[t][n][1]) + (sRC[t][n][2] + sRC[t][n][3]);
+      const int64_t o = ((b * p.ntd + tile % p.ntd) * p.Lp + t0 + t) * NPAD + n;
+      p.dB_part[o] = sb;
+      p.dC_part[o] = sc;
+    }
+    __syncthreads();
+  }
+
+  if (dvalid) {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) p.dA_part[(b * dim + d) * NPAD + n0 + j] = dAacc[j];
+  }
+  sAcc[0][w][lane] = accD;
+  sAcc[1][w][lane] = accBias;
+  __syncthreads();
+  if (w == 0 && dvalid) {
+    float sd = sAcc[0][0][lane], sb = sAcc[1][0][lane];
+#pragma unroll
+    for (int ww = 1; ww < G; ++ww) {
+      sd += sAcc[0][ww][lane];
+      sb += sAcc[1][ww][lane];
+    }
+    p.dD_part[b * dim + d] = sd;
+    p.dbias_part[b * dim + d] = sb;
+  }
+}
+
+// dB[b][t][n] (and dC) = sum over the tiles of batch row b of their partials,
+// in tile order; rounded to the storage type.
+template <class IO>
+__global__ void __launch_bounds__(256) bwd_reduce_bc_kernel(const float* __restrict__ dB_part,
+                                                           const float* __restrict__ dC_part, void* dB, void* dC,
+                                                           int64_t batch, int64_t L, int64_t Lp, int64_t N,
+                                                           int64_t npad, int ntd) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= batch * L * N) return;
+  const int64_t n = i % N, t = (i / N) % L, b = i / (N * L);
+  float sb = 0.0f, sc = 0.0f;
+  for (int col = 0; col < ntd; ++col) {
+    const int64_t o = ((b * ntd + col) * Lp + t) * npad + n;
+    sb += dB_part[o];
+    sc += dC_part[o];
+  }
+  store_vals<IO, 1>(dB, i, &sb);
+  store_vals<IO, 1>(dC, i, &sc);
+}
+
+// dA[d][n] = sum over batch rows of their partials (and dD[d], dbias[d]), in
+// batch order.
+__global__ void __launch_bounds__(256) bwd_reduce_param_kernel(const float* __restrict__ dA_part,
+                                                              const float* __restrict__ dD_part,
+                                                              const float* __restrict__ dbias_part, float* dA,
+                                                              float* dD, float* dbias, int64_t batch, int64_t dim,
+                                                              int64_t N, int64_t npad) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= dim * N) return;
+  const int64_t d = i / N, n = i % N;
+  float s = 0.0f;
+  for (int64_t b = 0; b < batch; ++b) s += dA_part[(b * dim + d) * npad + n];
+  dA[i] = s;
+  if (n == 0) {
+    float sd = 0.0f, sb = 0.0f;
+    for (int64_t b = 0; b < batch; ++b) {
+      sd += dD_part[b * dim + d];
+      sb += dbias_part[b * dim + d];
+    }
+    if (dD) dD[d] = sd;
+    if (dbias) dbias[d] = sb;
+  }
+}
+
+}  // namespace ssm

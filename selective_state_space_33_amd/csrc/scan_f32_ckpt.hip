@@ -1,0 +1,4 @@
+// scan_f32_ckpt.hip -- scan_kernel instantiations: f32 storage, kModeCkpt.
+#define SSM_IO F32
+#define SSM_MODE kModeCkpt
+#include "scan_launch.inc"

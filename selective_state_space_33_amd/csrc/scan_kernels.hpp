@@ -86,12 +86,17 @@ struct ScanParams {
   int n_split;         // tiles n_long .. n_long+n_split-1 are cut into Ks chunks
   int Ks;              // chunks per split tile
   int softplus;
+  // Checkpoint launches: the state entering every block of every tile,
+  // [tiles][ckpt_blocks][64][NPL*G].
+  float* ckpt;
+  int64_t ckpt_blocks;
 };
 
 // Launch modes of scan_kernel.
 constexpr int kModeFull = 0;     // whole tiles, and chunks of split tiles from their carried-in states
 constexpr int kModeAgg = 1;      // chunk pairs (P, S) of chunks 0..Ks-2 of every split tile
 constexpr int kModeChained = 2;  // one workgroup per CU: a whole tile with one chunk of a left-over tile spliced in
+constexpr int kModeCkpt = 3;     // whole tiles, no readout: the state entering every block (for the backward pass)
 
 // A workgroup waits for the state carried into its chunk for at most this
 // many polls (each after a short sleep); past that it records an error in
@@ -202,7 +207,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   static_assert(NG % 2 == 0, "groups come in pairs (double-buffered)");
   static_assert(kRing % 2 == 0, "ring slots keep their block parity");
   constexpr int ES = __is_same(IO, F32) ? 4 : 2;  // bytes per stored element
-  constexpr bool HAS_FULL = MODE != kModeAgg;      // a full (readout) pass runs in this launch
+  constexpr bool HAS_FULL = MODE == kModeFull || MODE == kModeChained;  // a readout pass runs in this launch
 
   // Double-buffered by block parity.
   __shared__ float2 sDU[2][TB][64];                                  // (delta, delta*u) per token, channel
@@ -235,6 +240,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   rsrc_t rs_u, rs_d, rs_z, rs_y;
   int voff[RPT];
   rsrc_t rs_bc;                            // this wavefront's packed B/C records of the stretch
+  float* ckpt_row = nullptr;               // checkpoint launches: this lane's states at the stretch's first block
   const int rec_voff = (lane & 15) * 4;    // lane l holds float l % 16 of a group's 16
 
   auto set_tile = [&](int tile, int64_t tb, int64_t te) {
@@ -253,6 +259,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     }
     // packed B/C records of this wavefront's state group, from the stretch's first token
     bc_row = p.bc + ((b * G + w) * p.Lp + t_begin) * (2 * NPL);
+    if constexpr (MODE == kModeCkpt)
+      ckpt_row = p.ckpt + (static_cast<int64_t>(tile) * p.ckpt_blocks * 64 + lane) * NPAD + n0;
     // the records run on for kTBMax rows of padding past Lp
     rs_bc = make_rsrc(bc_row, (p.Lp + kTBMax - t_begin) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
     pd = d0 + pcol;
@@ -467,6 +475,11 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       constexpr int Sp1 = (S + 1) % kRing;          // block k+1
       static_assert((S + kPD + 1) % kRing == Sm1, "ring");
       IC<P> parc;
+      if constexpr (MODE == kModeCkpt) {
+        // the state entering block k (the padding blocks at the end have room too)
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) ckpt_row[static_cast<int64_t>(k) * 64 * NPAD + j] = h[j];
+      }
       fetch_dd(parc, IC<0>{}, 0);
       if (k > k_begin) epilogue(IC<1 - P>{}, IC<Sm1>{}, k - 1);
       prologue(IC<1 - P>{}, IC<Sp1>{}, k + 1);
@@ -617,7 +630,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     const int unit = blockIdx.x;
     int tile, c, st;
     bool split;
-    if (MODE == kModeFull && unit < p.n_long) {
+    if (MODE == kModeCkpt || (MODE == kModeFull && unit < p.n_long)) {
       tile = unit;
       c = 0;
       st = 0;
@@ -634,7 +647,10 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     const int64_t te = split ? ((tb + p.chunk_len < L) ? tb + p.chunk_len : L) : L;
     set_tile(tile, tb, te);
     const int64_t pair_row = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;   // row of [n_split][Ks][64]
-    if constexpr (MODE == kModeAgg) {
+    if constexpr (MODE == kModeCkpt) {
+      int nb = stretch_blocks();
+      run_pass(IC<false>{}, 0, nb);
+    } else if constexpr (MODE == kModeAgg) {
       // chunk pair from a zero state: S = h, P = exp(A * sum of deltas)
       int nb = stretch_blocks();
       const float dt = run_pass(IC<false>{}, 0, nb);

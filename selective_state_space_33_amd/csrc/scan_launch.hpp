@@ -18,12 +18,14 @@ namespace ssm {
 template <class IO, int MODE>
 hipError_t launch_scan(int npl, int G, int vw, int tb, const ScanParams& p, dim3 grid, hipStream_t s);
 
-// Instantiated (each in its own translation unit) for these six combinations.
+// Instantiated (each in its own translation unit) for these eight combinations.
 extern template hipError_t launch_scan<F32, kModeFull>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<F32, kModeAgg>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<F32, kModeChained>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<BF16, kModeFull>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<BF16, kModeAgg>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<F32, kModeCkpt>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeCkpt>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<BF16, kModeChained>(int, int, int, int, const ScanParams&,
                                                            dim3, hipStream_t);
 
@@ -37,7 +39,7 @@ inline bool variant_exists(int npl, int G) {
 inline int preferred_vw(int G) { return G <= 4 ? 4 : (G == 8 ? 2 : 1); }
 // 32-token blocks exist for (2, 8) at its preferred width, outside the chunk-pair pass.
 inline bool variant_has_tb32(int npl, int G, int vw, int mode) {
-  return npl == 2 && G == 8 && vw == 2 && mode != kModeAgg;
+  return npl == 2 && G == 8 && vw == 2 && (mode == kModeFull || mode == kModeChained);
 }
 
 }  // namespace ssm

@@ -119,6 +119,43 @@ def test_state_update_rejects_bad_arguments_without_launching(kw, expect):
     assert _upd(ops.lib(), **kw) == expect
 
 
+def test_bwd_workspace_size():
+    L = ops.lib()
+    # at least the state entering every 16-token block of every 64-channel tile
+    ws = L.ssm_scan_bwd_workspace_size(2, 1000, 136, 16, BF16)
+    assert ws >= 2 * 3 * (1024 // 16) * 64 * 16 * 4 and ws % 256 == 0
+    assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 32, F32) > ws
+    assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 33, F32) == 0   # backward: dstate <= 32
+    assert L.ssm_scan_bwd_workspace_size(0, 10, 10, 16, F32) == 0
+    assert L.ssm_scan_bwd_workspace_size(1, 10, 10, 16, 7) == 0
+    assert L.ssm_scan_bwd_workspace_size(1, 1 << 24, 1024, 16, F32) == 0  # rows past 2^31 bytes
+
+
+def _bwd(lib_, **kw):
+    """Call ssm_scan_bwd with fake (never dereferenced) pointers; only rejection paths are used."""
+    a = dict(u=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, z=None, bias=None, sp=1, dy=0x6000,
+             dfs=None, du=0x7000, dd=0x8000, dA=0x9000, dB=0xa000, dC=0xb000, dD=None, dz=None, dbias=None,
+             batch=1, L=8, dim=8, N=16, dt=F32, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib_.ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["dy"],
+                             a["dfs"], a["du"], a["dd"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dbias"],
+                             a["batch"], a["L"], a["dim"], a["N"], a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(u=None), INVALID), (dict(dy=None), INVALID), (dict(du=None), INVALID), (dict(dd=None), INVALID),
+    (dict(dA=None), INVALID), (dict(dB=None), INVALID), (dict(dC=None), INVALID),
+    (dict(batch=0), INVALID), (dict(L=0), INVALID), (dict(N=0), INVALID), (dict(dt=3), INVALID),
+    (dict(dy=0x6001), INVALID), (dict(dt=BF16, dB=0xa001), INVALID), (dict(dfs=0xc002), INVALID),
+    (dict(N=33), UNSUPPORTED), (dict(batch=70000), UNSUPPORTED),
+    (dict(L=1 << 24, dim=1024), UNSUPPORTED),
+    (dict(), INVALID),                                  # no workspace
+    (dict(ws=0x100000, wsb=256), INVALID),              # too small
+])
+def test_bwd_rejects_bad_arguments_without_launching(kw, expect):
+    assert _bwd(ops.lib(), **kw) == expect
+
+
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(ops, "_lib", None)
