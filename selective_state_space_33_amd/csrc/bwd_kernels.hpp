@@ -46,6 +46,7 @@
 
 namespace ssm {
 
+
 struct BwdParams {
   const void* u;
   const void* delta;
@@ -72,14 +73,21 @@ struct BwdParams {
 
 constexpr int kBwdTB = 16;  // tokens per block (the checkpoint spacing)
 
-// Sum over the 16 lanes of each row, left in the row's last lane (DPP row
-// shifts; lanes shifted in from outside the row read zero).
-__device__ __forceinline__ float row_sum_to_last(float x) {
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x111, 0xf, 0xf, true));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x112, 0xf, 0xf, true));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x114, 0xf, 0xf, true));
-  x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x118, 0xf, 0xf, true));
-  return x;
+// Sums over the 16 lanes of each row of four values at once, each left in
+// the row's last lane: four steps of x += x shifted right by 1, 2, 4, 8 lanes
+// within the row (lanes shifted in from outside the row add zero).  One asm
+// block, so the order is fixed: each value's next step comes four
+// instructions after its last, past the two wait states a DPP read of a
+// VALU result needs; the leading s_nop covers the inputs' own writes.
+__device__ __forceinline__ void row_sums4_to_last(float& a, float& b, float& c, float& d) {
+#define SSM_ROW_STEP(K)                                                                 \
+  "v_add_f32_dpp %0, %0, %0 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_add_f32_dpp %1, %1, %1 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_add_f32_dpp %2, %2, %2 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+  "v_add_f32_dpp %3, %3, %3 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+  asm("s_nop 1\n\t" SSM_ROW_STEP(1) SSM_ROW_STEP(2) SSM_ROW_STEP(4) SSM_ROW_STEP(8)
+      : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+#undef SSM_ROW_STEP
 }
 
 template <class IO, int NPL, int G>
@@ -91,6 +99,9 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   constexpr int NRV = TB * 2 * NPL / 16;    // record registers per block
   static_assert((TB * 2 * NPL) % 16 == 0, "records fill whole registers");
   constexpr int ES = __is_same(IO, F32) ? 4 : 2;
+  // the decays a_t of a block are kept from the recompute for the adjoint
+  // where registers allow (2 states per lane), else recomputed
+  constexpr bool KEEP_A = NPL <= 2;
 
   __shared__ float2 sDU[TB][64];             // (Delta, Delta*u)
   __shared__ float sDV[TB][64];              // dv
@@ -145,17 +156,34 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   float accD = 0.0f, accBias = 0.0f;
   const int nblk = static_cast<int>((L + TB - 1) / TB);
 
-  for (int k = nblk - 1; k >= 0; --k) {
+  // Two-slot pipeline over the blocks (last to first): the loads of block
+  // k-1 are in flight while block k computes.  Unrolled by two so each slot
+  // keeps fixed registers (no copies, so no early waits on loads in flight).
+  Raw<IO, 1> qu[2][RPT], qd[2][RPT], qz[2][RPT], qg[2][RPT];
+  float qrv[2][NRV], qhs[2][NPL];
+  auto load_block = [&](auto slotc, int k) {
+    constexpr int S = decltype(slotc)::value;
     const int t0 = k * TB;
-    // this block's records and the state entering it
-    float rv[NRV];
 #pragma unroll
     for (int v = 0; v < NRV; ++v)
-      rv[v] = __uint_as_float(
+      qrv[S][v] = __uint_as_float(
           __builtin_amdgcn_raw_buffer_load_b32(rs_bc, rec_voff + t0 * (2 * NPL * 4) + v * 64, 0, 0));
-    float hst[NPL];
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) hst[j] = dvalid ? ckpt_row[static_cast<int64_t>(k) * 64 * NPAD + j] : 0.0f;
+    for (int j = 0; j < NPL; ++j) qhs[S][j] = dvalid ? ckpt_row[static_cast<int64_t>(k) * 64 * NPAD + j] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int off = (t0 + w + i * G) * row_bytes + lane * ES;
+      qu[S][i] = buf_load<IO, 1>(rs_u, off, 0);
+      qd[S][i] = buf_load<IO, 1>(rs_d, off, 0);
+      qz[S][i] = buf_load<IO, 1>(rs_z, off, 0);
+      qg[S][i] = buf_load<IO, 1>(rs_dy, off, 0);
+    }
+  };
+  auto process_block = [&](auto slotc, int k) {
+    constexpr int S = decltype(slotc)::value;
+    const int t0 = k * TB;
+    const float* rv = qrv[S];
+    const float* hst = qhs[S];
 
     // ---- P: elements (row, lane) of the block
     float eu[RPT], edl[RPT], esx[RPT], edv[RPT], egz[RPT];
@@ -163,13 +191,12 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = w + i * G;
-      const int off = (t0 + row) * row_bytes + lane * ES;
       const bool live = t0 + row < L && dvalid;  // lanes past dim read the next row: keep them at zero
       float uf, df, zf, gf;
-      unpack<IO, 1>(buf_load<IO, 1>(rs_u, off, 0), &uf);
-      unpack<IO, 1>(buf_load<IO, 1>(rs_d, off, 0), &df);
-      unpack<IO, 1>(buf_load<IO, 1>(rs_z, off, 0), &zf);
-      unpack<IO, 1>(buf_load<IO, 1>(rs_dy, off, 0), &gf);
+      unpack<IO, 1>(qu[S][i], &uf);
+      unpack<IO, 1>(qd[S][i], &df);
+      unpack<IO, 1>(qz[S][i], &zf);
+      unpack<IO, 1>(qg[S][i], &gf);
       const float x = df + bias_d;
       float dl = sp_on ? __builtin_fmaxf(x, 0.0f) + log1p_exp_neg_abs(x) : x;
       dl = live ? dl : 0.0f;  // padding tokens are identity steps
@@ -194,7 +221,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     __syncthreads();
 
     // ---- F: recompute the block's states from the checkpoint
-    float hs[TB][NPL], as[TB][NPL];
+    float hs[TB][NPL], as[KEEP_A ? TB : 1][NPL];
     {
       float h[NPL];
 #pragma unroll
@@ -211,7 +238,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
                 const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
                 h[j] = __builtin_fmaf(a, h[j], dd.y * row_bcast<fb % 16>(rv[fb / 16]));
                 hs[t][j] = h[j];
-                as[t][j] = a;
+                if constexpr (KEEP_A) as[t][j] = a;
                 if constexpr (j == 0) yp = row_bcast<fc % 16>(rv[fc / 16]) * h[0];
                 else yp = fmac_row_bcast<fc % 16>(yp, rv[fc / 16], h[j]);
               }()),
@@ -248,26 +275,31 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
          const float2 dd = sDU[t][lane];
          float s1 = 0.0f, s2 = 0.0f;
          float pb[NPL], pc[NPL];
+         static_assert(NPL % 2 == 0, "row sums go four values at a time");
          [&]<int... J>(std::integer_sequence<int, J...>) {
            (([&] {
               constexpr int j = J;
               constexpr int fb = t * 2 * NPL + j, fc = fb + NPL;
-              const float Bj = row_bcast<fb % 16>(rv[fb / 16]);
-              const float Cj = row_bcast<fc % 16>(rv[fc / 16]);
-              const float dh = __builtin_fmaf(Cj, dv, dhn[j]);
+              // dh = C dv + dhn and s2 += dh B with the records broadcast in the FMA itself
+              const float dh = fmac_row_bcast<fc % 16>(dhn[j], rv[fc / 16], dv);
               float hp;
               if constexpr (t > 0) hp = hs[t - 1][j];
               else hp = hst[j];
-              const float ta = dh * hp * as[t][j];
+              float a;
+              if constexpr (KEEP_A) a = as[t][j];
+              else a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
+              const float ta = dh * hp * a;
               s1 = __builtin_fmaf(ta, An[j], s1);
-              s2 = __builtin_fmaf(dh, Bj, s2);
+              s2 = fmac_row_bcast<fb % 16>(s2, rv[fb / 16], dh);
               dAacc[j] = __builtin_fmaf(ta, dd.x, dAacc[j]);
-              pb[j] = row_sum_to_last(dh * dd.y);
-              pc[j] = row_sum_to_last(dv * hs[t][j]);
-              dhn[j] = as[t][j] * dh;
+              pb[j] = dh * dd.y;
+              pc[j] = dv * hs[t][j];
+              dhn[j] = a * dh;
             }()),
             ...);
          }(std::make_integer_sequence<int, NPL>{});
+#pragma unroll
+         for (int j = 0; j < NPL; j += 2) row_sums4_to_last(pb[j], pb[j + 1], pc[j], pc[j + 1]);
          if ((lane & 15) == 15) {
 #pragma unroll
            for (int j = 0; j < NPL; ++j) {
@@ -311,6 +343,14 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       p.dC_part[o] = sc;
     }
     __syncthreads();
+  };
+  load_block(IC<0>{}, nblk - 1);
+  for (int k = nblk - 1; k >= 0; k -= 2) {
+    if (k >= 1) load_block(IC<1>{}, k - 1);
+    process_block(IC<0>{}, k);
+    if (k < 1) break;
+    if (k >= 2) load_block(IC<0>{}, k - 2);
+    process_block(IC<1>{}, k - 1);
   }
 
   if (dvalid) {

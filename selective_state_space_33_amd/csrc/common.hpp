@@ -195,6 +195,9 @@ __device__ __forceinline__ float log1p_exp_neg_abs(float x) {
 }
 __device__ __forceinline__ float softplus_f(float x) { return __builtin_fmaxf(x, 0.0f) + log1p_exp_neg_abs(x); }
 
+// A compile-time int as a type (for unrolled steps written as lambdas).
+template <int I> struct IC { static constexpr int value = I; };
+
 // Lane K (0..15) of each 16-lane row of v, broadcast across the row (DPP
 // row_newbcast; the compiler folds it into a multiply's first operand).
 template <int K> __device__ __forceinline__ float row_bcast(float v) {

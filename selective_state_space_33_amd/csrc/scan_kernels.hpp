@@ -124,7 +124,6 @@ template <int NPL> struct GroupShape {
   static_assert(FLOATS % 16 == 0, "group records are whole 16-float loads");
 };
 
-template <int I> struct IC { static constexpr int value = I; };
 
 // Ring of raw token blocks (u, delta_raw, z) in registers.  Block k+kPD+1 is
 // loaded while block k is scanned, staged by the prologue while block k+kPD is
