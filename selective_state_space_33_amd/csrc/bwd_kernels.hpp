@@ -32,9 +32,9 @@
 //      D u_t, and dz_t;
 //   R  every wavefront: the adjoint back through the block; per token its
 //      partial sums over its states of t_a A and dh B (to LDS), and per state
-//      the dB, dC partials summed over the 16 lanes of each row (DPP) to LDS;
+//      the dB, dC partials summed over groups of 4 lanes (DPP) to LDS;
 //   E2 every thread: du, ddelta_raw of its elements; the tile's dB, dC
-//      partials (the 4 row sums) to the workspace.
+//      partials (the 16 group sums, in order) to the workspace.
 // dA, dD and dbias accumulate in registers over the whole sequence.  Partial
 // sums over tiles (dB, dC) and over batch rows (dA, dD, dbias) are added in
 // a fixed order by bwd_reduce_*; so every result is deterministic.
@@ -73,19 +73,20 @@ struct BwdParams {
 
 constexpr int kBwdTB = 16;  // tokens per block (the checkpoint spacing)
 
-// Sums over the 16 lanes of each row of four values at once, each left in
-// the row's last lane: four steps of x += x shifted right by 1, 2, 4, 8 lanes
-// within the row (lanes shifted in from outside the row add zero).  One asm
-// block, so the order is fixed: each value's next step comes four
-// instructions after its last, past the two wait states a DPP read of a
-// VALU result needs; the leading s_nop covers the inputs' own writes.
-__device__ __forceinline__ void row_sums4_to_last(float& a, float& b, float& c, float& d) {
+// Sums over each group of 4 lanes of four values at once, each left in the
+// group's last lane: two steps of x += x shifted right by 1, 2 lanes within
+// the 16-lane row (lanes shifted in from outside the row add zero, and lane
+// 4g+3 only ever takes lanes 4g .. 4g+2).  One asm block, so the order is
+// fixed: each value's next step comes four instructions after its last, past
+// the two wait states a DPP read of a VALU result needs; the leading s_nop
+// covers the inputs' own writes.
+__device__ __forceinline__ void quad_sums4_to_last(float& a, float& b, float& c, float& d) {
 #define SSM_ROW_STEP(K)                                                                 \
   "v_add_f32_dpp %0, %0, %0 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
   "v_add_f32_dpp %1, %1, %1 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
   "v_add_f32_dpp %2, %2, %2 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
   "v_add_f32_dpp %3, %3, %3 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-  asm("s_nop 1\n\t" SSM_ROW_STEP(1) SSM_ROW_STEP(2) SSM_ROW_STEP(4) SSM_ROW_STEP(8)
+  asm("s_nop 1\n\t" SSM_ROW_STEP(1) SSM_ROW_STEP(2)
       : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
 #undef SSM_ROW_STEP
 }
@@ -106,8 +107,8 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   __shared__ float2 sDU[TB][64];             // (Delta, Delta*u)
   __shared__ float sDV[TB][64];              // dv
   __shared__ float2 sYS[G][TB][64];          // readout partials (.x), then (sum t_a A, sum dh B)
-  __shared__ float sRB[TB][NPAD][4];         // dB partials: one sum per 16-lane row
-  __shared__ float sRC[TB][NPAD][4];
+  __shared__ float sRB[TB][NPAD][16];        // dB partials: one sum per group of 4 lanes
+  __shared__ float sRC[TB][NPAD][16];
   __shared__ float sAcc[2][G][64];
 
   const int tid = threadIdx.x;
@@ -299,12 +300,12 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
             ...);
          }(std::make_integer_sequence<int, NPL>{});
 #pragma unroll
-         for (int j = 0; j < NPL; j += 2) row_sums4_to_last(pb[j], pb[j + 1], pc[j], pc[j + 1]);
-         if ((lane & 15) == 15) {
+         for (int j = 0; j < NPL; j += 2) quad_sums4_to_last(pb[j], pb[j + 1], pc[j], pc[j + 1]);
+         if ((lane & 3) == 3) {
 #pragma unroll
            for (int j = 0; j < NPL; ++j) {
-             sRB[t][n0 + j][lane >> 4] = pb[j];
-             sRC[t][n0 + j][lane >> 4] = pc[j];
+             sRB[t][n0 + j][lane >> 2] = pb[j];
+             sRC[t][n0 + j][lane >> 2] = pc[j];
            }
          }
          sYS[w][t][lane] = make_float2(s1, s2);
@@ -336,8 +337,12 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     }
     for (int q = tid; q < TB * NPAD; q += 64 * G) {
       const int t = q / NPAD, n = q % NPAD;
-      const float sb = (sRB[t][n][0] + sRB[t][n][1]) + (sRB[t][n][2] + sRB[t][n][3]);
-      const float sc = (sRC[t][n][0] + sRC[t][n][1]) + (sRC[t][n][2] + sRC[t][n][3]);
+      float sb = 0.0f, sc = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        sb += sRB[t][n][r];
+        sc += sRC[t][n][r];
+      }
       const int64_t o = ((b * p.ntd + tile % p.ntd) * p.Lp + t0 + t) * NPAD + n;
       p.dB_part[o] = sb;
       p.dC_part[o] = sc;
