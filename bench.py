@@ -6,7 +6,8 @@ chunk carry, readout and gated epilogue) over the Mamba-2.8B-shaped bf16
 layer: batch 4, L 4096, dim 5120, dstate 16, z gate on, final state
 returned.  Inputs are seeded synthetic tensors already resident in HBM.
 The one-token decode step (ssm_state_update, batch 256, dim 5120,
-dstate 16) is timed separately in the same run and reported under "decode".
+dstate 16) is timed separately in the same run and reported under "decode",
+and the backward pass (ssm_scan_bwd) of the same layer under "backward".
 
 Prints ONE JSON line.  Fields beyond the common ones:
   roofline      the dominant kernel against its binding roofline (VALU issue:
@@ -39,6 +40,13 @@ TRANS_SLOTS = 2                 # exp2/log2/rcp: a wave64 issues every ~8-9.6 cl
 # (exp, log + 3 ops), delta*u, the D skip fma, SiLU (exp, rcp + 2 ops), the gate multiply.
 SLOTS_PER_UPDATE = 4 + 1 * TRANS_SLOTS
 SLOTS_PER_TOKEN_CHANNEL = 4 * TRANS_SLOTS + 9
+# The backward with the states recomputed once: per state update the recompute (delta*A, exp, delta*u*B, the
+# fade-and-add and readout fmas), the adjoint (dh = C dv + dh', dh*h_prev, *a, t_a*A and dh*B accumulations, the dA
+# fma, dh*delta*u, dv*h, a*dh) and the sums over channels of the dB, dC terms (2 adds).  Per (token, channel):
+# softplus and its derivative (exp, log, exp, rcp + 4 ops), SiLU and its derivative (exp, rcp + 4 ops), and the dv,
+# dz, du, d delta, dD and d bias terms (8 ops).
+BWD_SLOTS_PER_UPDATE = 4 + TRANS_SLOTS + 9 + 2
+BWD_SLOTS_PER_TOKEN_CHANNEL = 6 * TRANS_SLOTS + 16
 
 
 def scan_bytes(w, with_final=True):
@@ -160,6 +168,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the scan, time a plain device copy of this many MiB (calibrates HBM counters)")
     args = ap.parse_args()
@@ -255,6 +264,27 @@ def main():
                                       "unit": "GB/s", "frac": db / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                       "algorithmic_bytes": db, "traffic": measured_traffic(wd.name)}}
         del gd, yd, state
+
+    if not args.no_backward:
+        dy = torch.empty_like(g["u"]).copy_(g["u"].flip(1))  # any seeded tensor of y's shape serves as dy
+        needb = ops.ssm_scan_bwd_workspace_size(w.batch, w.L, w.dim, w.dstate, g["u"].dtype)
+        wsb = torch.empty(needb, dtype=torch.uint8, device=dev)
+
+        def bstep():
+            ops.ssm_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"], z=g["z"],
+                             delta_bias=g["delta_bias"], workspace=wsb, stream=stream)
+
+        bms, _ = time_calls(bstep, max(args.steps // 5, 5), max(args.warmup // 10, 5), stream)
+        bslots = w.updates * BWD_SLOTS_PER_UPDATE + w.batch * w.L * w.dim * BWD_SLOTS_PER_TOKEN_CHANNEL
+        btf = 2.0 * bslots / (bms * 1e-3) / 1e12
+        out["backward"] = {"workload": w.name, "op": "ssm_scan_bwd", "ms_per_step": bms,
+                           "value": w.updates / (bms * 1e-3), "unit": "updates/s", "workspace_bytes": needb,
+                           "roofline": {"bound": "alu", "achieved": btf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": btf / VALU_PEAK_TFLOPS,
+                                        "counted": f"algorithmic fp32 VALU issue slots x 2 flops, states recomputed "
+                                                   f"once: {BWD_SLOTS_PER_UPDATE} per state update, "
+                                                   f"{BWD_SLOTS_PER_TOKEN_CHANNEL} per (token, channel)"}}
+        del dy, wsb
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)
