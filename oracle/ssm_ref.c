@@ -79,16 +79,23 @@ typedef struct {
   int softplus_flag;
   double *y, *final_state;
   long batch, L, dim, N;
-  long first, last; /* range of flattened (b, d) channels for this worker */
+  const double* h0;      /* initial states [rows][dim][N], or NULL for zero */
+  const long* cu;        /* packed sequences: row r is tokens cu[r] .. cu[r+1]-1 of batch row 0 */
+  long rows;             /* batch rows, or sequences when cu is given */
+  long first, last; /* range of flattened (row, d) channels for this worker */
 } scan_job;
 
 static void scan_channels(const scan_job* j) {
   double hbuf[4096];
-  for (long bd = j->first; bd < j->last; ++bd) {
-    long b = bd / j->dim, d = bd % j->dim;
+  for (long rd = j->first; rd < j->last; ++rd) {
+    long r = rd / j->dim, d = rd % j->dim;
+    /* the tokens of this recurrence: a whole batch row, or one packed sequence of row 0 */
+    long b = j->cu ? 0 : r;
+    long t0 = j->cu ? j->cu[r] : 0, t1 = j->cu ? j->cu[r + 1] : j->L;
     double* h = hbuf;
-    for (long n = 0; n < j->N; ++n) h[n] = 0.0;   /* the scan starts from a zero state */
-    for (long t = 0; t < j->L; ++t) {
+    for (long n = 0; n < j->N; ++n)                /* the given state, else zero */
+      h[n] = j->h0 ? j->h0[(r * j->dim + d) * j->N + n] : 0.0;
+    for (long t = t0; t < t1; ++t) {
       long io = (b * j->L + t) * j->dim + d;      /* [batch, L, dim] */
       long bc = (b * j->L + t) * j->N;            /* [batch, L, dstate] */
       j->y[io] = one_step(h, j->u[io], j->delta[io], j->z ? &j->z[io] : NULL,
@@ -96,7 +103,7 @@ static void scan_channels(const scan_job* j) {
                           j->N, j->softplus_flag);
     }
     if (j->final_state)
-      for (long n = 0; n < j->N; ++n) j->final_state[(b * j->dim + d) * j->N + n] = h[n];
+      for (long n = 0; n < j->N; ++n) j->final_state[(r * j->dim + d) * j->N + n] = h[n];
   }
 }
 
@@ -110,9 +117,26 @@ int ssm_ref_scan_fwd(const double* u, const double* delta, const double* A,
                      const double* z, const double* delta_bias, int softplus_flag,
                      double* y, double* final_state,
                      long batch, long L, long dim, long dstate, int nthreads) {
+  return ssm_ref_scan_fwd_ex(u, delta, A, B, C, D, z, delta_bias, softplus_flag, NULL, NULL, 0,
+                             y, final_state, batch, L, dim, dstate, nthreads);
+}
+
+int ssm_ref_scan_fwd_ex(const double* u, const double* delta, const double* A,
+                        const double* B, const double* C, const double* D,
+                        const double* z, const double* delta_bias, int softplus_flag,
+                        const double* initial_state, const long* cu_seqlens, long nseq,
+                        double* y, double* final_state,
+                        long batch, long L, long dim, long dstate, int nthreads) {
   if (!u || !delta || !A || !B || !C || !y) return -1;
   if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 4096) return -1;
-  long channels = batch * dim;
+  long rows = batch;
+  if (cu_seqlens) {
+    if (batch != 1 || nseq <= 0 || cu_seqlens[0] != 0 || cu_seqlens[nseq] != L) return -1;
+    for (long s = 0; s < nseq; ++s)
+      if (cu_seqlens[s + 1] < cu_seqlens[s]) return -1;
+    rows = nseq;
+  }
+  long channels = rows * dim;
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
   if (nthreads > channels) nthreads = (int)channels;
@@ -122,7 +146,8 @@ int ssm_ref_scan_fwd(const double* u, const double* delta, const double* A,
   int running[256];
   for (int i = 0; i < nthreads; ++i) {
     scan_job j = {u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, final_state,
-                  batch, L, dim, dstate, channels * i / nthreads, channels * (i + 1) / nthreads};
+                  batch, L, dim, dstate, initial_state, cu_seqlens, rows,
+                  channels * i / nthreads, channels * (i + 1) / nthreads};
     jobs[i] = j;
   }
   if (nthreads == 1) {

@@ -45,6 +45,22 @@ int ssm_ref_scan_fwd(const double* u, const double* delta, const double* A,
                      double* y, double* final_state,
                      long batch, long L, long dim, long dstate, int nthreads);
 
+/* The same scan from given initial states and/or over packed sequences.
+ *   initial_state (NULL: zero): h_{-1} for each recurrence, [rows][dim][dstate],
+ *   so the scan continues a state handed on by an earlier call ("Mamba is
+ *   attention all you really need, part 2", "The relay": a chunk starts from
+ *   whatever state it is handed).
+ *   cu_seqlens (NULL: none): batch must be 1; sequence s is tokens
+ *   cu_seqlens[s] .. cu_seqlens[s+1]-1, each its own recurrence from its own
+ *   initial state; rows = nseq, and final_state is [nseq][dim][dstate].
+ *   cu_seqlens[0] = 0, nondecreasing, cu_seqlens[nseq] = L (else -1). */
+int ssm_ref_scan_fwd_ex(const double* u, const double* delta, const double* A,
+                        const double* B, const double* C, const double* D,
+                        const double* z, const double* delta_bias, int softplus_flag,
+                        const double* initial_state, const long* cu_seqlens, long nseq,
+                        double* y, double* final_state,
+                        long batch, long L, long dim, long dstate, int nthreads);
+
 /* One recurrent (decode) step from the given state, updated in place.
  *   u, delta, z, y: [batch, dim];  B, C: [batch, dstate];
  *   state: [batch, dim, dstate].  Same arithmetic as one step of the scan. */

@@ -30,8 +30,8 @@ MUTANTS = {
     "gate_is_sigmoid_not_silu": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
     "composition_operands_swapped": ("double b = a2[i] * b1[i] + b2[i];", "double b = a1[i] * b2[i] + b1[i];"),
     "batch_and_time_axes_swapped": ("long io = (b * j->L + t) * j->dim + d;", "long io = (t * j->batch + b) * j->dim + d;"),
-    "final_state_not_per_channel": ("j->final_state[(b * j->dim + d) * j->N + n] = h[n];",
-                                    "j->final_state[b * j->N + n] = h[n];"),
+    "final_state_not_per_channel": ("j->final_state[(r * j->dim + d) * j->N + n] = h[n];",
+                                    "j->final_state[r * j->N + n] = h[n];"),
     "input_term_missing_u": ("double bbar_u = delta * Bt[n] * ut;", "double bbar_u = delta * Bt[n];"),
 }
 
