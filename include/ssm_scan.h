@@ -95,6 +95,38 @@ ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const float* A, cons
                           int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace for ssm_scan_fwd_ex: for nseq <= 0 (no packed sequences) the same
+ * as ssm_scan_workspace_size; for nseq > 0 packed sequences (batch must be 1)
+ * the packed B/C records only.  Returns 0 for arguments the call would
+ * reject. */
+size_t ssm_scan_fwd_ex_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int64_t nseq,
+                                      ssm_dtype_t dt);
+
+/* ssm_scan_fwd from given initial states and/or over packed sequences of
+ * variable length ("Mamba is attention all you really need, part 2", "The
+ * relay": a stretch of the sequence can start from whatever state it is
+ * handed, so a long prompt can be scanned in pieces and a state handed on;
+ * packed variable-length sequences as in "State Space Models and the
+ * Post-Transformer Era", "Mamba-2 and Structured State Space Duality").
+ *   initial_state (NULL: zero) is h_{-1} of every recurrence, fp32
+ *   [rows, dim, dstate], rows = batch, or nseq with packed sequences; it may
+ *   be the final_state of an earlier call (but not alias this call's).
+ *   cu_seqlens (NULL: none): device pointer to nseq + 1 int64 offsets,
+ *   8-byte aligned; batch must be 1, and sequence s is tokens cu_seqlens[s]
+ *   .. cu_seqlens[s+1]-1 of batch row 0, scanned on its own from its own
+ *   initial state; final_state is then [nseq, dim, dstate].  The offsets
+ *   should start at 0, not decrease and end at L; they are not checked
+ *   (values read on the device are clamped into [0, L]).  A sequence is
+ *   never cut, so L * dim elements must fit 2^31 bytes (else UNSUPPORTED).
+ *   Everything else as ssm_scan_fwd, whose call is this one with NULL,
+ *   NULL, 0. */
+ssm_status_t ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                             const float* initial_state, const int64_t* cu_seqlens, int64_t nseq,
+                             void* y, float* final_state,
+                             int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* One recurrent (decode) step: the same arithmetic as one token of the scan,
  * reading `state` as h_{t-1} and overwriting it in place with h_t
  * ("Mamba: The State Space Models Challenging the Transformer", "What a

@@ -10,7 +10,8 @@
 namespace ssm {
 
 // State entering each chunk of a split tile: carry_{c+1} = P_c * carry_c + S_c,
-// carry_0 = 0, for every column (lane channel, state) of the tile; layout
+// carry_0 = the tile's initial state (zero when h0 is null; h0 is
+// [batch][dim][N]), for every column (lane channel, state) of the tile; layout
 // [n_split][Ks][64][Npad].  The Ks-1 pairs of a column are cut into kCarryRuns
 // runs: each thread composes one run of one column into a single pair, the
 // runs' pairs are combined in order through LDS, and each thread walks its
@@ -20,7 +21,9 @@ constexpr int kCarryRuns = 32;
 constexpr int kCarryCols = 256 / kCarryRuns;
 
 __global__ void __launch_bounds__(256) carry_kernel(const float* __restrict__ P, const float* __restrict__ S,
-                                                   float* __restrict__ carry, int64_t n_split, int Ks, int64_t Npad) {
+                                                   float* __restrict__ carry, int64_t n_split, int Ks, int64_t Npad,
+                                                   const float* __restrict__ h0, int64_t n_long, int64_t ntd,
+                                                   int64_t dim, int64_t N) {
   __shared__ float sP[kCarryRuns][kCarryCols], sS[kCarryRuns][kCarryCols];
   const int run = threadIdx.x / kCarryCols;
   const int cl = threadIdx.x % kCarryCols;
@@ -46,8 +49,13 @@ __global__ void __launch_bounds__(256) carry_kernel(const float* __restrict__ P,
   sP[run][cl] = a;
   sS[run][cl] = bb;
   __syncthreads();
-  // state entering this run: the runs before it, composed in order
+  // state entering this run: the tile's initial state, then the runs before it, composed in order
   float h = 0.0f;
+  if (h0 && ok) {
+    const int64_t tile = n_long + st;
+    const int64_t d = (tile % ntd) * 64 + r / Npad, n = r % Npad;
+    if (d < dim && n < N) h = h0[((tile / ntd) * dim + d) * N + n];
+  }
   for (int q = 0; q < run; ++q) h = __builtin_fmaf(sP[q][cl], h, sS[q][cl]);
   if (!ok) return;
 #pragma unroll 8

@@ -90,6 +90,13 @@ struct ScanParams {
   // [tiles][ckpt_blocks][64][NPL*G].
   float* ckpt;
   int64_t ckpt_blocks;
+  // Initial states h_{-1} [rows][dim][N] (nullable: zero), rows being the
+  // batch rows, or the packed sequences when cu is given.  With cu (device
+  // offsets, nseq + 1 of them) batch row 0 holds nseq packed sequences: split
+  // "chunk" c of a tile column is sequence c, tokens cu[c] .. cu[c+1]-1, with
+  // its own initial and final state.
+  const float* h0;
+  const int64_t* cu;
 };
 
 // Launch modes of scan_kernel.
@@ -530,11 +537,19 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     return delta_total;
   };
 
-  auto write_final_state = [&]() {
+  // h_{-1} of the recurrence row `row` (batch row or packed sequence), when given
+  auto init_state = [&](int64_t row) {
+    if (p.h0 && dvalid) {
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (n0 + j < N) h[j] = p.h0[(row * dim + d) * N + n0 + j];
+    }
+  };
+  auto write_final_state = [&](int64_t row) {
     if (dvalid && p.final_state) {
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
-        if (n0 + j < N) p.final_state[(b * dim + d) * N + n0 + j] = h[j];
+        if (n0 + j < N) p.final_state[(row * dim + d) * N + n0 + j] = h[j];
     }
   };
 
@@ -551,11 +566,12 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     const int j = static_cast<int>(__builtin_amdgcn_readfirstlane(*sTicket));
     __syncthreads();  // every wavefront has read it before the buffer is written
     set_tile(j, 0, L);
+    init_state(b);
     int nb_whole = stretch_blocks();
     const bool has_chunk = j < p.n_split * p.Ks;
     if (!has_chunk) {
       run_pass(IC<true>{}, 0, nb_whole);
-      write_final_state();
+      write_final_state(b);
       return;
     }
     const int c = j / p.n_split, st = j % p.n_split;
@@ -578,6 +594,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       h[q] = 0.0f;
     }
     set_tile(p.n_long + st, cb, ce);
+    if (c == 0) init_state(b);
     const int64_t crow = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;  // carry row [n_split][Ks][64]
     // The carries and flags are read and written only with device-coherent
     // (agent-scope) loads and stores, which bypass the per-XCD L2s; waiting
@@ -617,13 +634,13 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
         __hip_atomic_store(p.flags + static_cast<int64_t>(st) * p.Ks + c + 1, 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     } else {
-      write_final_state();
+      write_final_state(b);
     }
     set_tile(j, 0, L);
 #pragma unroll
     for (int q = 0; q < NPL; ++q) h[q] = hw[q];
     run_pass(IC<true>{}, m, nb_whole);
-    write_final_state();
+    write_final_state(b);
   } else {
     // ---- which tile and which part of the sequence this workgroup scans
     const int unit = blockIdx.x;
@@ -642,11 +659,19 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       tile = p.n_long + st;
       split = true;
     }
-    const int64_t tb = split ? static_cast<int64_t>(c) * p.chunk_len : 0;
-    const int64_t te = split ? ((tb + p.chunk_len < L) ? tb + p.chunk_len : L) : L;
+    int64_t tb = split ? static_cast<int64_t>(c) * p.chunk_len : 0;
+    int64_t te = split ? ((tb + p.chunk_len < L) ? tb + p.chunk_len : L) : L;
+    const bool packed = MODE == kModeFull && split && p.cu != nullptr;
+    if (packed) {  // sequence c of batch row 0, offsets clamped into [0, L]
+      tb = p.cu[c];
+      tb = tb < 0 ? 0 : (tb > L ? L : tb);
+      te = p.cu[c + 1];
+      te = te < tb ? tb : (te > L ? L : te);
+    }
     set_tile(tile, tb, te);
     const int64_t pair_row = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;   // row of [n_split][Ks][64]
     if constexpr (MODE == kModeCkpt) {
+      init_state(b);
       int nb = stretch_blocks();
       run_pass(IC<false>{}, 0, nb);
     } else if constexpr (MODE == kModeAgg) {
@@ -661,13 +686,18 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
         p.aggP[idx] = __builtin_amdgcn_exp2f(A2[q] * dt);
       }
     } else {
-      if (split && c > 0 && dvalid) {
+      if (packed) {
+        init_state(c);
+      } else if (!split || c == 0) {
+        init_state(b);
+      } else if (dvalid) {
 #pragma unroll
         for (int q = 0; q < NPL; ++q) h[q] = p.carry[pair_row * NPAD + n0 + q];
       }
       int nb = stretch_blocks();
       run_pass(IC<true>{}, 0, nb);
-      if (!split || c == p.Ks - 1) write_final_state();
+      if (packed) write_final_state(c);
+      else if (!split || c == p.Ks - 1) write_final_state(b);
     }
   }
 }

@@ -51,6 +51,7 @@ struct Plan {
   int64_t Lp;    // sequence length rounded up to whole token blocks (packed B/C rows)
   bool chained;  // split tiles chain their carries inside the one scan launch
   int tb;        // tokens per block of the readout scan (16, or 32 with a CU per workgroup)
+  bool packed;   // packed sequences: "chunk" c of a tile column is sequence c (no pairs, no carries)
 };
 
 // Workspace layout: [packed B/C][chunk fades P][chunk states S][carried-in
@@ -66,8 +67,8 @@ Layout layout_for(const Plan& pl, int64_t batch) {
   const size_t per = static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float);
   Layout l;
   l.bc = align256((static_cast<size_t>(batch) * pl.Lp + kTBMax) * 2 * npad * sizeof(float));
-  l.pairs = (pl.n_split > 0 && !pl.chained) ? align256(per) : 0;
-  l.carry = pl.n_split > 0 ? align256(per) : 0;
+  l.pairs = (pl.n_split > 0 && !pl.chained && !pl.packed) ? align256(per) : 0;
+  l.carry = (pl.n_split > 0 && !pl.packed) ? align256(per) : 0;
   l.n_words = pl.chained ? pl.n_split * pl.Ks + 2 : 0;
   l.words = align256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
   l.total = l.bc + 2 * l.pairs + l.carry + l.words;
@@ -209,6 +210,33 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
   pl->tb = (tb32_ok && (chained || (n_long == T && T <= kNumCU))) ? 32 : 16;
   const char* te = getenv("SSM_SCAN_TB");
   if (te && tb32_ok && (atoi(te) == 16 || atoi(te) == 32)) pl->tb = atoi(te);
+  pl->packed = false;
+}
+
+// Packed sequences (batch row 0 holds nseq of them): every (tile column,
+// sequence) is one readout-pass unit from its own initial state, with no
+// chunking of a sequence.
+void plan_packed(int64_t L, int64_t dim, int64_t N, int vw_ok, int64_t nseq, Plan* pl) {
+  int npl, G;
+  if (N == 16) {
+    npl = 2;
+    G = 8;
+  } else {
+    generic_variant(N, &npl, &G);
+  }
+  pl->npl = npl;
+  pl->G = G;
+  pl->vw = preferred_vw(G) <= vw_ok ? preferred_vw(G) : 1;
+  pl->ntd = static_cast<int>(ceil_div(dim, 64));
+  pl->n_long = 0;
+  pl->n_split = pl->ntd;
+  pl->Ks = static_cast<int>(nseq);
+  pl->chunk_len = L;
+  pl->Lp = ceil_div(L, kTrip) * kTrip;
+  pl->chained = false;
+  pl->packed = true;
+  const bool tb32_ok = variant_has_tb32(npl, G, pl->vw, kModeFull);
+  pl->tb = (tb32_ok && static_cast<int64_t>(pl->ntd) * nseq <= kNumCU) ? 32 : 16;
 }
 
 ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -248,14 +276,15 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
   const dim3 grid_full(static_cast<unsigned>(pl.n_long + static_cast<int64_t>(pl.n_split) * pl.Ks));
   if (pl.chained)  // one workgroup per whole tile, each also running at most one chunk
     return launch_scan<IO, kModeChained>(pl.npl, pl.G, pl.vw, pl.tb, p, dim3(pl.n_long), s);
-  if (pl.n_split > 0 && pl.Ks > 1) {
+  if (pl.n_split > 0 && pl.Ks > 1 && !pl.packed) {
     const dim3 grid_agg(static_cast<unsigned>(static_cast<int64_t>(pl.n_split) * (pl.Ks - 1)));
     e = launch_scan<IO, kModeAgg>(pl.npl, pl.G, pl.vw, 16, p, grid_agg, s);
     if (e != hipSuccess) return e;
     const int64_t cols = static_cast<int64_t>(pl.n_split) * 64 * npad;
     hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>(ceil_div(cols, kCarryCols))), dim3(256), 0, s,
                        static_cast<const float*>(p.aggP), static_cast<const float*>(p.aggS), p.carry,
-                       static_cast<int64_t>(pl.n_split), pl.Ks, npad);
+                       static_cast<int64_t>(pl.n_split), pl.Ks, npad, p.h0, static_cast<int64_t>(pl.n_long),
+                       static_cast<int64_t>(pl.ntd), p.dim, p.N);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -328,14 +357,21 @@ extern "C" size_t ssm_scan_workspace_size(int64_t batch, int64_t L, int64_t dim,
   return a > b ? a : b;
 }
 
-extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                                     const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                                     void* y, float* final_state, int64_t batch, int64_t L, int64_t dim,
-                                     int64_t dstate, ssm_dtype_t dt, void* workspace, size_t workspace_bytes,
-                                     hipStream_t stream) {
+namespace ssm {
+namespace {
+
+// The forward, from given initial states and over packed sequences when
+// asked (cu_seqlens non-null: batch 1, nseq sequences).
+ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                           const float* h0, const int64_t* cu_seqlens, int64_t nseq, void* y, float* final_state,
+                           int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
   const ssm_status_t st =
       check_scan_args(u, delta, A, B, C, D, z, delta_bias, y, final_state, batch, L, dim, dstate, dt);
   if (st != SSM_OK) return st;
+  if (h0 && !aligned(h0, 4)) return SSM_ERR_INVALID_ARG;
+  if (cu_seqlens && (!aligned(cu_seqlens, 8) || batch != 1 || nseq <= 0)) return SSM_ERR_INVALID_ARG;
   // A prologue width vw needs dim % vw == 0 and token rows aligned to vw elements.
   const size_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
   int vw_ok = 1;
@@ -348,7 +384,14 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
   }
   if (max_chunk_len(dim, static_cast<int64_t>(es)) < kChunkQuantum) return SSM_ERR_UNSUPPORTED;
   Plan pl;
-  plan_scan(batch, L, dim, dstate, static_cast<int64_t>(es), vw_ok, &pl);
+  if (cu_seqlens) {
+    // a sequence is never cut, so the whole row of tokens must stay within the 32-bit offsets
+    if (ceil_div(L, kChunkQuantum) * kChunkQuantum > max_chunk_len(dim, static_cast<int64_t>(es)))
+      return SSM_ERR_UNSUPPORTED;
+    plan_packed(L, dim, dstate, vw_ok, nseq, &pl);
+  } else {
+    plan_scan(batch, L, dim, dstate, static_cast<int64_t>(es), vw_ok, &pl);
+  }
   if (static_cast<int64_t>(pl.n_long) + static_cast<int64_t>(pl.n_split) * pl.Ks > 0x7fffffffLL ||
       batch * (pl.Lp / kPackT) > 0x7fffffffLL)
     return SSM_ERR_UNSUPPORTED;
@@ -356,7 +399,7 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
   if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256)) return SSM_ERR_INVALID_ARG;
 
   char* ws = static_cast<char*>(workspace);
-  ScanParams p;
+  ScanParams p = {};
   p.u = u;
   p.delta = delta;
   p.A = A;
@@ -368,6 +411,8 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
   p.final_state = final_state;
   p.aggP = p.aggS = p.carry = nullptr;
   p.flags = p.ticket = p.status = nullptr;
+  p.h0 = h0;
+  p.cu = cu_seqlens;
   size_t off = lay.bc;
   if (lay.pairs) {
     p.aggP = reinterpret_cast<float*>(ws + off);
@@ -399,6 +444,43 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
   const hipError_t e = dt == SSM_DTYPE_F32 ? run_scan<F32>(pl, lay, B, C, bc, p, stream)
                                            : run_scan<BF16>(pl, lay, B, C, bc, p, stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace ssm
+
+extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                     const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                     void* y, float* final_state, int64_t batch, int64_t L, int64_t dim,
+                                     int64_t dstate, ssm_dtype_t dt, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus_flag, nullptr, nullptr, 0, y, final_state,
+                       batch, L, dim, dstate, dt, workspace, workspace_bytes, stream);
+}
+
+extern "C" size_t ssm_scan_fwd_ex_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate,
+                                                 int64_t nseq, ssm_dtype_t dt) {
+  if (nseq <= 0) return ssm_scan_workspace_size(batch, L, dim, dstate, dt);
+  if (batch != 1 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 64) return 0;
+  if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return 0;
+  const int64_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
+  if (max_chunk_len(dim, es) < ceil_div(L, kChunkQuantum) * kChunkQuantum) return 0;
+  Plan p4, p1;
+  plan_packed(L, dim, dstate, 4, nseq, &p4);
+  plan_packed(L, dim, dstate, 1, nseq, &p1);
+  const size_t a = layout_for(p4, 1).total, b = layout_for(p1, 1).total;
+  return a > b ? a : b;
+}
+
+extern "C" ssm_status_t ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
+                                        const void* C, const float* D, const void* z, const float* delta_bias,
+                                        int softplus_flag, const float* initial_state, const int64_t* cu_seqlens,
+                                        int64_t nseq, void* y, float* final_state, int64_t batch, int64_t L,
+                                        int64_t dim, int64_t dstate, ssm_dtype_t dt, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus_flag, initial_state, cu_seqlens,
+                       cu_seqlens ? nseq : 0, y, final_state, batch, L, dim, dstate, dt, workspace,
+                       workspace_bytes, stream);
 }
 
 extern "C" ssm_status_t ssm_state_update(float* state, const void* u, const void* delta, const float* A,

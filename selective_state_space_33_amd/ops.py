@@ -21,8 +21,8 @@ SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP = 0, 1, 2, 3
 SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 
 # Every symbol include/ssm_scan.h declares.
-EXPORTED = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_state_update", "ssm_scan_bwd_workspace_size",
-            "ssm_scan_bwd", "ssm_status_string")
+EXPORTED = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_ex_workspace_size", "ssm_scan_fwd_ex",
+            "ssm_state_update", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_status_string")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -49,6 +49,11 @@ def lib() -> ctypes.CDLL:
                                    [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
         L.ssm_state_update.restype = ctypes.c_int
         L.ssm_state_update.argtypes = [_vp] * 9 + [ctypes.c_int, _vp] + [_i64] * 3 + [ctypes.c_int, _vp]
+        L.ssm_scan_fwd_ex_workspace_size.restype = ctypes.c_size_t
+        L.ssm_scan_fwd_ex_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int]
+        L.ssm_scan_fwd_ex.restype = ctypes.c_int
+        L.ssm_scan_fwd_ex.argtypes = ([_vp] * 8 + [ctypes.c_int, _vp, _vp, _i64, _vp, _vp] + [_i64] * 4 +
+                                      [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_scan_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
         L.ssm_scan_bwd.restype = ctypes.c_int
@@ -134,6 +139,51 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: b
                             _ptr(workspace), ws_bytes, _stream(dev, stream))
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_scan_fwd")
+    return y, final_state
+
+
+def ssm_scan_fwd_ex(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+                    initial_state=None, cu_seqlens=None, y=None, final_state=None, workspace=None, stream=None):
+    """ssm_scan_fwd from given initial states and/or over packed sequences.
+
+    initial_state: [rows, dim, dstate] float32 (rows = batch, or the number of sequences).
+    cu_seqlens: int64 device tensor of nseq + 1 offsets into the L axis of batch row 0 (batch must be 1).
+    Returns (y, final_state [rows, dim, dstate])."""
+    batch, L, dim = u.shape
+    dstate = A.shape[1]
+    dev, dt = u.device, u.dtype
+    code = _dtype_code(dt)
+    nseq = 0
+    rows = batch
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int64 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-d int64 tensor on the device of u")
+        nseq = cu_seqlens.numel() - 1
+        rows = nseq
+        _check(cu_seqlens, "cu_seqlens", torch.int64, (nseq + 1,), dev)
+    for name, t, shp in (("u", u, (batch, L, dim)), ("delta", delta, (batch, L, dim)), ("z", z, (batch, L, dim)),
+                         ("B", B, (batch, L, dstate)), ("C", C, (batch, L, dstate))):
+        _check(t, name, dt, shp, dev)
+    _check(A, "A", torch.float32, (dim, dstate), dev)
+    _check(D, "D", torch.float32, (dim,), dev)
+    _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    _check(initial_state, "initial_state", torch.float32, (rows, dim, dstate), dev)
+    if y is None:
+        y = torch.empty((batch, L, dim), dtype=dt, device=dev)
+    _check(y, "y", dt, (batch, L, dim), dev)
+    if final_state is None:
+        final_state = torch.empty((rows, dim, dstate), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", torch.float32, (rows, dim, dstate), dev)
+    need = int(lib().ssm_scan_fwd_ex_workspace_size(batch, L, dim, dstate, nseq, code))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib().ssm_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                               1 if softplus else 0, _ptr(initial_state), _ptr(cu_seqlens), nseq, _ptr(y),
+                               _ptr(final_state), batch, L, dim, dstate, code, _ptr(workspace), ws_bytes,
+                               _stream(dev, stream))
+    if rc != SSM_OK:
+        raise SSMError(rc, "ssm_scan_fwd_ex")
     return y, final_state
 
 

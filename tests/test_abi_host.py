@@ -119,6 +119,37 @@ def test_state_update_rejects_bad_arguments_without_launching(kw, expect):
     assert _upd(ops.lib(), **kw) == expect
 
 
+def _ex(lib_, **kw):
+    """Call ssm_scan_fwd_ex with fake (never dereferenced) pointers; only rejection paths are used."""
+    a = dict(u=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, z=None, bias=None, sp=1, h0=None,
+             cu=None, nseq=0, y=0x6000, fs=None, batch=1, L=8, dim=8, N=16, dt=F32, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib_.ssm_scan_fwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
+                                a["h0"], a["cu"], a["nseq"], a["y"], a["fs"], a["batch"], a["L"], a["dim"], a["N"],
+                                a["dt"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(u=None), INVALID), (dict(h0=0x7002), INVALID),
+    (dict(cu=0x8004, nseq=2), INVALID),                 # offsets must be 8-byte aligned
+    (dict(cu=0x8000, nseq=0), INVALID), (dict(cu=0x8000, nseq=2, batch=2), INVALID),
+    (dict(cu=0x8000, nseq=2, L=1 << 22, dim=1024), UNSUPPORTED),  # a sequence is never cut
+    (dict(N=65), UNSUPPORTED),
+    (dict(cu=0x8000, nseq=2), INVALID),                 # no workspace
+])
+def test_scan_ex_rejects_bad_arguments_without_launching(kw, expect):
+    assert _ex(ops.lib(), **kw) == expect
+
+
+def test_scan_ex_workspace_size():
+    L = ops.lib()
+    assert L.ssm_scan_fwd_ex_workspace_size(2, 1000, 136, 16, 0, BF16) == L.ssm_scan_workspace_size(2, 1000, 136, 16, BF16)
+    ws = L.ssm_scan_fwd_ex_workspace_size(1, 1000, 136, 16, 7, BF16)
+    assert ws >= 1000 * 2 * 16 * 4 and ws % 256 == 0
+    assert L.ssm_scan_fwd_ex_workspace_size(2, 1000, 136, 16, 7, BF16) == 0       # packed needs batch 1
+    assert L.ssm_scan_fwd_ex_workspace_size(1, 1 << 22, 1024, 16, 3, F32) == 0    # rows past 2^31 bytes
+
+
 def test_bwd_workspace_size():
     L = ops.lib()
     # at least the state entering every 16-token block of every 64-channel tile
