@@ -146,21 +146,24 @@ ssm_status_t ssm_state_update(float* state, const void* u, const void* delta, co
  * row.  Returns 0 for arguments ssm_scan_bwd would reject. */
 size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt);
 
-/* Backward of ssm_scan_fwd: the gradients of
+/* Backward of ssm_scan_fwd (or of ssm_scan_fwd_ex from an initial state,
+ * without packed sequences): the gradients of
  *     sum(y * dy) + sum(final_state * dfinal_state)
- * with respect to u, delta, A, B, C, D, z and delta_bias, for the same
- * inputs and flags as the forward call.  The states are recomputed from the
+ * with respect to u, delta, A, B, C, D, z, delta_bias and the initial
+ * state, for the same inputs and flags as the forward call.  The states are recomputed from the
  * inputs, not stored by the forward ("Mamba is attention all you really need,
  * part 2", "Keeping the pad on the desk"; "The state that must remember
  * everything", "The Hardware-Aware Way Out", rematerialization).
- *   Inputs as for ssm_scan_fwd, plus dy [batch, L, dim] in dtype dt and
+ *   Inputs as for ssm_scan_fwd, plus dy [batch, L, dim] in dtype dt,
  *   dfinal_state [batch, dim, dstate] fp32 (NULL: no gradient reaches the
- *   final state).
+ *   final state) and initial_state [batch, dim, dstate] fp32 (NULL: zero).
  *   Outputs, all overwritten: du, ddelta [batch, L, dim], dB, dC [batch, L,
  *   dstate] in dtype dt (gradients of the sequence inputs, rounded like y);
  *   dA [dim, dstate] fp32.  dD [dim], dz [batch, L, dim] (dtype dt) and
  *   ddelta_bias [dim] fp32 are written when both the input (D, z,
- *   delta_bias) and the output pointer are non-NULL.  The gradient of delta
+ *   delta_bias) and the output pointer are non-NULL; dinitial_state [batch,
+ *   dim, dstate] fp32 is written when non-NULL (with or without an initial
+ *   state: it is the adjoint reaching h_{-1}).  The gradient of delta
  *   is the one of the raw input (through softplus and the bias when on).
  *   dA, dD and ddelta_bias sum over the batch and the sequence, dB and dC
  *   over the channels, in a fixed order (results are deterministic).
@@ -169,9 +172,9 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_
  *   UNSUPPORTED for dstate > 32 or batch > 65535. */
 ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                           const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                          const void* dy, const float* dfinal_state,
+                          const void* dy, const float* dfinal_state, const float* initial_state,
                           void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
-                          float* ddelta_bias,
+                          float* ddelta_bias, float* dinitial_state,
                           int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 

@@ -33,13 +33,13 @@ def _t(x):
     return None if x is None else torch.tensor(np.asarray(x, dtype=np.float64), dtype=torch.float64)
 
 
-def forward_torch(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True):
-    """The forward recurrence on float64 torch tensors; returns (y, final_state)."""
+def forward_torch(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, initial_state=None):
+    """The forward recurrence on float64 torch tensors from initial_state (None: zero); returns (y, final_state)."""
     batch, L, dim = u.shape
     N = A.shape[1]
     x = delta if delta_bias is None else delta + delta_bias
     dl = torch.logaddexp(x, torch.zeros_like(x)) if softplus else x
-    h = torch.zeros((batch, dim, N), dtype=torch.float64)
+    h = torch.zeros((batch, dim, N), dtype=torch.float64) if initial_state is None else initial_state
     ys = []
     for t in range(L):
         a = torch.exp(dl[:, t, :, None] * A[None, :, :])            # [batch, dim, N]
@@ -55,13 +55,14 @@ def forward_torch(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=T
     return y, h
 
 
-def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, dfinal_state=None):
+def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, dfinal_state=None,
+             initial_state=None):
     """Gradients of sum(y*dy) + sum(final_state*dfinal_state) with respect to every input.
 
     Returns a dict of float64 numpy arrays: du, ddelta, dA, dB, dC, and dD, dz,
-    ddelta_bias for the optional inputs that were given (None otherwise)."""
-    names = ["u", "delta", "A", "B", "C", "D", "z", "delta_bias"]
-    vals = [u, delta, A, B, C, D, z, delta_bias]
+    ddelta_bias, dinitial_state for the optional inputs that were given (None otherwise)."""
+    names = ["u", "delta", "A", "B", "C", "D", "z", "delta_bias", "initial_state"]
+    vals = [u, delta, A, B, C, D, z, delta_bias, initial_state]
     ts = {}
     for n, v in zip(names, vals):
         tv = _t(v)
@@ -69,7 +70,7 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
             tv.requires_grad_(True)
         ts[n] = tv
     y, fs = forward_torch(ts["u"], ts["delta"], ts["A"], ts["B"], ts["C"], D=ts["D"], z=ts["z"],
-                          delta_bias=ts["delta_bias"], softplus=softplus)
+                          delta_bias=ts["delta_bias"], softplus=softplus, initial_state=ts["initial_state"])
     obj = (y * _t(dy)).sum()
     if dfinal_state is not None:
         obj = obj + (fs * _t(dfinal_state)).sum()

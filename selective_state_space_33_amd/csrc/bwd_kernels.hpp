@@ -58,6 +58,7 @@ struct BwdParams {
   const float* ckpt;   // state entering every block: [tiles][ckpt_blocks][64][NPL*G]
   const void* dy;
   const float* dfs;    // nullable: gradient reaching the final state [batch][dim][N]
+  float* dh0;          // nullable: gradient of the initial state [batch][dim][N]
   void* du;
   void* ddelta;
   void* dz;            // nullable
@@ -360,7 +361,11 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
 
   if (dvalid) {
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) p.dA_part[(b * dim + d) * NPAD + n0 + j] = dAacc[j];
+    for (int j = 0; j < NPL; ++j) {
+      p.dA_part[(b * dim + d) * NPAD + n0 + j] = dAacc[j];
+      // the adjoint left after token 0 is the gradient of h_{-1}
+      if (p.dh0 && n0 + j < N) p.dh0[(b * dim + d) * N + n0 + j] = dhn[j];
+    }
   }
   sAcc[0][w][lane] = accD;
   sAcc[1][w][lane] = accBias;

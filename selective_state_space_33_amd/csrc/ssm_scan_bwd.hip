@@ -110,8 +110,9 @@ extern "C" size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t 
 
 extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                                      const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                                     const void* dy, const float* dfinal_state, void* du, void* ddelta, float* dA,
-                                     void* dB, void* dC, float* dD, void* dz, float* ddelta_bias, int64_t batch,
+                                     const void* dy, const float* dfinal_state, const float* initial_state, void* du,
+                                     void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                                     float* ddelta_bias, float* dinitial_state, int64_t batch,
                                      int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream) {
   if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return SSM_ERR_INVALID_ARG;
@@ -121,7 +122,7 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   const void* seq[] = {u, delta, B, C, dy, du, ddelta, dB, dC, z, dz};
   for (const void* q : seq)
     if (q && !is_aligned(q, es)) return SSM_ERR_INVALID_ARG;
-  const float* f32s[] = {A, D, delta_bias, dfinal_state, dA, dD, ddelta_bias};
+  const float* f32s[] = {A, D, delta_bias, dfinal_state, initial_state, dA, dD, ddelta_bias, dinitial_state};
   for (const float* q : f32s)
     if (q && !is_aligned(q, 4)) return SSM_ERR_INVALID_ARG;
   if (dstate > kBwdMaxState || batch > kBwdMaxBatch) return SSM_ERR_UNSUPPORTED;
@@ -170,6 +171,7 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   sp.softplus = softplus_flag ? 1 : 0;
   sp.ckpt = ckpt;
   sp.ckpt_blocks = pl.ckpt_blocks;
+  sp.h0 = initial_state;
 
   BwdParams bp;
   bp.u = u;
@@ -182,6 +184,7 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   bp.ckpt = ckpt;
   bp.dy = dy;
   bp.dfs = dfinal_state;
+  bp.dh0 = dinitial_state;
   bp.du = du;
   bp.ddelta = ddelta;
   bp.dz = z ? dz : nullptr;

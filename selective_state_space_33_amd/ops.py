@@ -57,7 +57,7 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_scan_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
         L.ssm_scan_bwd.restype = ctypes.c_int
-        L.ssm_scan_bwd.argtypes = ([_vp] * 8 + [ctypes.c_int] + [_vp] * 10 + [_i64] * 4 +
+        L.ssm_scan_bwd.argtypes = ([_vp] * 8 + [ctypes.c_int] + [_vp] * 12 + [_i64] * 4 +
                                    [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
         L.ssm_status_string.restype = ctypes.c_char_p
         L.ssm_status_string.argtypes = [ctypes.c_int]
@@ -220,12 +220,14 @@ def ssm_scan_bwd_workspace_size(batch: int, L: int, dim: int, dstate: int, dtype
 
 
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus: bool = True,
-                 dfinal_state=None, workspace=None, stream=None):
+                 dfinal_state=None, initial_state=None, want_dinitial_state: bool = False, workspace=None,
+                 stream=None):
     """Backward of ssm_scan_fwd on the GPU: gradients of sum(y*dy) + sum(final_state*dfinal_state).
 
     Same inputs as ssm_scan_fwd plus dy [batch, L, dim] (storage dtype) and dfinal_state
     [batch, dim, dstate] (float32, optional).  Returns a dict with du, ddelta, dB, dC (storage
-    dtype), dA (float32), and dD, dz, ddelta_bias for the optional inputs given (None otherwise).
+    dtype), dA (float32), and dD, dz, ddelta_bias for the optional inputs given (None otherwise);
+    dinitial_state [batch, dim, dstate] when an initial state is given or want_dinitial_state.
     """
     batch, L, dim = u.shape
     dstate = A.shape[1]
@@ -238,18 +240,22 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
     _check(D, "D", torch.float32, (dim,), dev)
     _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
     _check(dfinal_state, "dfinal_state", torch.float32, (batch, dim, dstate), dev)
+    _check(initial_state, "initial_state", torch.float32, (batch, dim, dstate), dev)
     g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(delta), dB=torch.empty_like(B),
              dC=torch.empty_like(C), dA=torch.empty_like(A),
              dD=None if D is None else torch.empty_like(D), dz=None if z is None else torch.empty_like(z),
-             ddelta_bias=None if delta_bias is None else torch.empty_like(delta_bias))
+             ddelta_bias=None if delta_bias is None else torch.empty_like(delta_bias),
+             dinitial_state=(torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+                             if (initial_state is not None or want_dinitial_state) else None))
     need = ssm_scan_bwd_workspace_size(batch, L, dim, dstate, dt)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                            1 if softplus else 0, _ptr(dy), _ptr(dfinal_state), _ptr(g["du"]), _ptr(g["ddelta"]),
-                            _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g["dz"]),
-                            _ptr(g["ddelta_bias"]), batch, L, dim, dstate, code, _ptr(workspace), ws_bytes,
+                            1 if softplus else 0, _ptr(dy), _ptr(dfinal_state), _ptr(initial_state), _ptr(g["du"]),
+                            _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
+                            _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dinitial_state"]), batch, L, dim, dstate,
+                            code, _ptr(workspace), ws_bytes,
                             _stream(dev, stream))
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_scan_bwd")

@@ -165,12 +165,13 @@ def test_bwd_workspace_size():
 def _bwd(lib_, **kw):
     """Call ssm_scan_bwd with fake (never dereferenced) pointers; only rejection paths are used."""
     a = dict(u=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, z=None, bias=None, sp=1, dy=0x6000,
-             dfs=None, du=0x7000, dd=0x8000, dA=0x9000, dB=0xa000, dC=0xb000, dD=None, dz=None, dbias=None,
-             batch=1, L=8, dim=8, N=16, dt=F32, ws=None, wsb=0, stream=None)
+             dfs=None, h0=None, du=0x7000, dd=0x8000, dA=0x9000, dB=0xa000, dC=0xb000, dD=None, dz=None, dbias=None,
+             dh0=None, batch=1, L=8, dim=8, N=16, dt=F32, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib_.ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["dy"],
-                             a["dfs"], a["du"], a["dd"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"], a["dbias"],
-                             a["batch"], a["L"], a["dim"], a["N"], a["dt"], a["ws"], a["wsb"], a["stream"])
+                             a["dfs"], a["h0"], a["du"], a["dd"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+                             a["dbias"], a["dh0"], a["batch"], a["L"], a["dim"], a["N"], a["dt"], a["ws"], a["wsb"],
+                             a["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -178,6 +179,7 @@ def _bwd(lib_, **kw):
     (dict(dA=None), INVALID), (dict(dB=None), INVALID), (dict(dC=None), INVALID),
     (dict(batch=0), INVALID), (dict(L=0), INVALID), (dict(N=0), INVALID), (dict(dt=3), INVALID),
     (dict(dy=0x6001), INVALID), (dict(dt=BF16, dB=0xa001), INVALID), (dict(dfs=0xc002), INVALID),
+    (dict(h0=0xc002), INVALID), (dict(dh0=0xd001), INVALID),
     (dict(N=33), UNSUPPORTED), (dict(batch=70000), UNSUPPORTED),
     (dict(L=1 << 24, dim=1024), UNSUPPORTED),
     (dict(), INVALID),                                  # no workspace

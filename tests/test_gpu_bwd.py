@@ -19,7 +19,7 @@ from .gpu_util import TOL, rel_err, say, to_dev, to_dev_f32
 pytestmark = pytest.mark.gpu
 
 SEQ_OUT = ("du", "ddelta", "dz", "dB", "dC")   # stored in the storage dtype
-F32_OUT = ("dA", "dD", "ddelta_bias")          # always fp32
+F32_OUT = ("dA", "dD", "ddelta_bias", "dinitial_state")  # always fp32
 
 
 def _round(x, dtype):
@@ -44,16 +44,16 @@ def _case(rng, batch, L, dim, N, dtype, gated=True, with_D=True, with_bias=True,
     return x, dy, dfs
 
 
-def _run_and_compare(x, dy, dfs, dtype, softplus=True, label=""):
+def _run_and_compare(x, dy, dfs, dtype, softplus=True, label="", h0=None):
     say(f"bwd {label} shape={x['u'].shape} N={x['A'].shape[1]} {dtype}")
     g = ops.ssm_scan_bwd(to_dev(x["u"], dtype), to_dev(x["delta"], dtype), to_dev_f32(x["A"]), to_dev(x["B"], dtype),
                          to_dev(x["C"], dtype), to_dev(dy, dtype), D=to_dev_f32(x["D"]),
                          z=to_dev(x["z"], dtype) if x["z"] is not None else None,
                          delta_bias=to_dev_f32(x["delta_bias"]), softplus=softplus,
-                         dfinal_state=to_dev_f32(dfs))
+                         dfinal_state=to_dev_f32(dfs), initial_state=to_dev_f32(h0))
     torch.cuda.synchronize()
     o = OB.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
-                    softplus=softplus, dfinal_state=dfs)
+                    softplus=softplus, dfinal_state=dfs, initial_state=h0)
     errs = {}
     for k in SEQ_OUT + F32_OUT:
         if o[k] is None:
@@ -91,6 +91,16 @@ def test_bwd_optional_inputs(opts):
     rng = np.random.default_rng(300 + len(opts))
     x, dy, dfs = _case(rng, 2, 90, 64 + 12, 16, "f32", **opts)
     _run_and_compare(x, dy, dfs, "f32", softplus=opts.get("softplus", True), label=str(opts))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 32])
+def test_bwd_with_initial_state(N, dtype):
+    """From an initial state h0: every gradient, and d h0 (the adjoint reaching h_{-1})."""
+    rng = np.random.default_rng(450 + N + (5 if dtype == "bf16" else 0))
+    x, dy, dfs = _case(rng, 2, 120, 64 + 40, N, dtype)
+    h0 = np.asarray(rng.standard_normal((2, 64 + 40, N)) * 0.5, np.float32).astype(np.float64)
+    _run_and_compare(x, dy, dfs, dtype, label=f"h0 N{N}", h0=h0)
 
 
 def test_bwd_is_deterministic():

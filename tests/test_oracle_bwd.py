@@ -94,6 +94,37 @@ def test_gradients_match_central_differences_of_c_oracle(softplus, gated, with_f
     assert checked >= 20
 
 
+def test_initial_state_gradients_match_central_differences():
+    """With an initial state h0 the transcription's forward is the C oracle's (pinned in test_oracle_ex.py)
+    and every gradient, d h0 included, matches central differences of that forward."""
+    rng = np.random.default_rng(21)
+    batch, L, dim, N = 2, 6, 3, 4
+    x = _inputs(rng, batch, L, dim, N)
+    h0 = rng.standard_normal((batch, dim, N))
+    dy = rng.standard_normal((batch, L, dim))
+    dfs = rng.standard_normal((batch, dim, N))
+
+    def obj():
+        y, fs = R.scan_fwd_ex(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                              delta_bias=x["delta_bias"], initial_state=h0)
+        return float(np.sum(y * dy) + np.sum(fs * dfs))
+
+    g = OB.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                    dfinal_state=dfs, initial_state=h0)
+    for arr, name in [(h0, "dinitial_state"), (x["delta"], "ddelta"), (x["A"], "dA")]:
+        flat = arr.reshape(-1)
+        for i in rng.choice(flat.size, size=6, replace=False):
+            e = 1e-6 * max(1.0, abs(flat[i]))
+            o = flat[i]
+            flat[i] = o + e
+            fp = obj()
+            flat[i] = o - e
+            fm = obj()
+            flat[i] = o
+            fd = (fp - fm) / (2 * e)
+            assert abs(g[name].reshape(-1)[i] - fd) <= 2e-7 * max(1.0, abs(fd)), (name, i)
+
+
 def test_relay_example_gradients_by_hand():
     """[P1] "The relay": two steps (a1,b1) = (0.6, 0.4) and (a2,b2) = (0.5, 1.0) on N = 1 with A = -1,
     C = 1, u = 1, no softplus, bias, D or gate.  Then y = (b1, a2*b1 + b2) = (0.4, 1.2) and, for dy = (1, 1),
