@@ -7,7 +7,9 @@ layer: batch 4, L 4096, dim 5120, dstate 16, z gate on, final state
 returned.  Inputs are seeded synthetic tensors already resident in HBM.
 The one-token decode step (ssm_state_update, batch 256, dim 5120,
 dstate 16) is timed separately in the same run and reported under "decode",
-and the backward pass (ssm_scan_bwd) of the same layer under "backward".
+the backward pass (ssm_scan_bwd) of the same layer under "backward", and the
+same layer's tokens as one packed row of variable-length sequences, each from
+its own initial state (ssm_scan_fwd_ex), under "packed".
 
 Prints ONE JSON line.  Fields beyond the common ones:
   roofline      the dominant kernel against its binding roofline (VALU issue:
@@ -169,6 +171,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-packed", action="store_true")
+    ap.add_argument("--packed-mean-len", type=float, default=1024.0,
+                    help="mean sequence length of the packed row (log-normal lengths, sigma 1)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the scan, time a plain device copy of this many MiB (calibrates HBM counters)")
     args = ap.parse_args()
@@ -285,6 +290,39 @@ def main():
                                                    f"once: {BWD_SLOTS_PER_UPDATE} per state update, "
                                                    f"{BWD_SLOTS_PER_TOKEN_CHANNEL} per (token, channel)"}}
         del dy, wsb
+
+    if not args.no_packed:
+        import numpy as np
+
+        # batch x L tokens as one row, cut into a seeded log-normal length mix; every sequence starts from a
+        # random state of its own and hands back its final state.
+        rng = np.random.default_rng(1)
+        cu = I.packed_offsets(rng, w.batch * w.L, args.packed_mean_len)
+        nseq = len(cu) - 1
+        row = lambda t: t.reshape(1, w.batch * w.L, t.shape[-1])
+        pu, pdl, pz, pB, pC = (row(g[k]) for k in ("u", "delta", "z", "B", "C"))
+        cu_t = torch.tensor(cu, dtype=torch.int64, device=dev)
+        h0 = (torch.randn((nseq, w.dim, w.dstate), generator=torch.Generator().manual_seed(2)) * 0.1).to(dev)
+        py = torch.empty_like(pu)
+        pfs = torch.empty((nseq, w.dim, w.dstate), dtype=torch.float32, device=dev)
+        needp = ops.ssm_scan_fwd_ex_workspace_size(1, w.batch * w.L, w.dim, w.dstate, nseq, pu.dtype)
+        wsp = torch.empty(max(needp, 1), dtype=torch.uint8, device=dev)
+
+        def pstep():
+            ops.ssm_scan_fwd_ex(pu, pdl, g["A"], pB, pC, D=g["D"], z=pz, delta_bias=g["delta_bias"],
+                                initial_state=h0, cu_seqlens=cu_t, y=py, final_state=pfs, workspace=wsp,
+                                stream=stream)
+
+        pms, _ = time_calls(pstep, args.steps, max(args.warmup // 4, 5), stream)
+        lens = np.diff(cu)
+        ptf = 2.0 * slots / (pms * 1e-3) / 1e12
+        out["packed"] = {"workload": f"{w.name} as 1 x {w.batch * w.L} packed tokens", "op": "ssm_scan_fwd_ex",
+                         "sequences": nseq, "len_min": int(lens.min()), "len_median": float(np.median(lens)),
+                         "len_max": int(lens.max()), "initial_state": True, "ms_per_step": pms,
+                         "value": w.updates / (pms * 1e-3), "unit": "updates/s",
+                         "roofline": {"bound": "alu", "achieved": ptf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                      "frac": ptf / VALU_PEAK_TFLOPS}}
+        del py, pfs, wsp, h0
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)

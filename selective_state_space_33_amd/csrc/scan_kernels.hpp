@@ -97,6 +97,9 @@ struct ScanParams {
   // its own initial and final state.
   const float* h0;
   const int64_t* cu;
+  // Packed launches: the sequences in launch order (nullable: index order);
+  // unit j scans tile column j % n_split of sequence order[j / n_split].
+  const int* order;
 };
 
 // Launch modes of scan_kernel.
@@ -654,8 +657,13 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     } else {
       const int per = MODE == kModeFull ? p.Ks : p.Ks - 1;
       const int jj = MODE == kModeFull ? unit - p.n_long : unit;
-      st = jj / per;
-      c = jj % per;
+      if (MODE == kModeFull && p.cu != nullptr) {  // packed: every tile column of a sequence together
+        st = jj % p.n_split;
+        c = p.order ? p.order[jj / p.n_split] : jj / p.n_split;
+      } else {
+        st = jj / per;
+        c = jj % per;
+      }
       tile = p.n_long + st;
       split = true;
     }

@@ -15,6 +15,7 @@
 
 #include "carry_kernel.hpp"
 #include "decode_kernel.hpp"
+#include "order_kernel.hpp"
 #include "scan_launch.hpp"
 
 namespace ssm {
@@ -55,10 +56,10 @@ struct Plan {
 };
 
 // Workspace layout: [packed B/C][chunk fades P][chunk states S][carried-in
-// states][flags, ticket, status].  The chained plan needs no P, S; the others
-// no flags.
+// states][flags, ticket, status][sequence order].  The chained plan needs no
+// P, S; the others no flags; only the packed plan has an order.
 struct Layout {
-  size_t bc, pairs, carry, words, total;
+  size_t bc, pairs, carry, words, order, total;
   int n_words;
 };
 
@@ -71,7 +72,8 @@ Layout layout_for(const Plan& pl, int64_t batch) {
   l.carry = (pl.n_split > 0 && !pl.packed) ? align256(per) : 0;
   l.n_words = pl.chained ? pl.n_split * pl.Ks + 2 : 0;
   l.words = align256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
-  l.total = l.bc + 2 * l.pairs + l.carry + l.words;
+  l.order = pl.packed ? align256(static_cast<size_t>(pl.Ks) * sizeof(int)) : 0;
+  l.total = l.bc + 2 * l.pairs + l.carry + l.words + l.order;
   return l;
 }
 
@@ -82,7 +84,9 @@ Layout layout_for(const Plan& pl, int64_t batch) {
 //                                 (1) or go through the pair and carry passes (0);
 //   SSM_SCAN_CHAIN_K=k            chunks per left-over tile in a chained plan;
 //   SSM_SCAN_TB=16|32             tokens per block of the readout scan, where
-//                                 the variant has both.
+//                                 the variant has both;
+//   SSM_SCAN_ORDER=0              packed sequences launch in index order rather
+//                                 than longest first.
 bool env_variant(int* npl, int* G, int* K) {
   const char* s = getenv("SSM_SCAN_VARIANT");
   if (!s || !*s) return false;
@@ -273,6 +277,12 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
 #undef SSM_PACK_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.order) {
+    hipLaunchKernelGGL(packed_order_kernel, dim3(1), dim3(kOrderBins), 0, s, p.cu, pl.Ks, p.L,
+                       const_cast<int*>(p.order));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid_full(static_cast<unsigned>(pl.n_long + static_cast<int64_t>(pl.n_split) * pl.Ks));
   if (pl.chained)  // one workgroup per whole tile, each also running at most one chunk
     return launch_scan<IO, kModeChained>(pl.npl, pl.G, pl.vw, pl.tb, p, dim3(pl.n_long), s);
@@ -428,7 +438,10 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
     p.flags = words;                                           // [n_split][Ks]
     p.ticket = words + static_cast<int64_t>(pl.n_split) * pl.Ks;
     p.status = p.ticket + 1;
+    off += lay.words;
   }
+  const char* oe = getenv("SSM_SCAN_ORDER");
+  p.order = (lay.order && !(oe && atoi(oe) == 0)) ? reinterpret_cast<const int*>(ws + off) : nullptr;
   p.batch = batch;
   p.L = L;
   p.Lp = pl.Lp;

@@ -159,3 +159,16 @@ def random_scan_inputs(rng: np.random.Generator, batch: int, L: int, dim: int, d
         "delta": _store(delta, dtype), "B": _store(B, dtype), "C": _store(C, dtype),
         "A": np.ascontiguousarray(A, dtype=np.float32), "D": D, "delta_bias": bias,
     }
+
+
+def packed_offsets(rng: np.random.Generator, total: int, mean_len: float, sigma: float = 1.0) -> list:
+    """Seeded cut of `total` tokens into packed sequences: cumulative offsets [0, ..., total].
+
+    Lengths are log-normal with median `mean_len` * exp(-sigma^2 / 2) (mean `mean_len`), at least 1 token,
+    so a row mixes a few long sequences with many short ones; the last length is clipped to fit."""
+    cu = [0]
+    mu = np.log(mean_len) - sigma * sigma / 2
+    while cu[-1] < total:
+        n = max(1, int(round(rng.lognormal(mu, sigma))))
+        cu.append(min(total, cu[-1] + n))
+    return cu

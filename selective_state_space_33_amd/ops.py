@@ -174,7 +174,7 @@ def ssm_scan_fwd_ex(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus
     if final_state is None:
         final_state = torch.empty((rows, dim, dstate), dtype=torch.float32, device=dev)
     _check(final_state, "final_state", torch.float32, (rows, dim, dstate), dev)
-    need = int(lib().ssm_scan_fwd_ex_workspace_size(batch, L, dim, dstate, nseq, code))
+    need = ssm_scan_fwd_ex_workspace_size(batch, L, dim, dstate, nseq, dt)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -213,6 +213,10 @@ def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, 
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_state_update")
     return y
+
+
+def ssm_scan_fwd_ex_workspace_size(batch: int, L: int, dim: int, dstate: int, nseq: int, dtype: torch.dtype) -> int:
+    return int(lib().ssm_scan_fwd_ex_workspace_size(batch, L, dim, dstate, nseq, _dtype_code(dtype)))
 
 
 def ssm_scan_bwd_workspace_size(batch: int, L: int, dim: int, dstate: int, dtype: torch.dtype) -> int:

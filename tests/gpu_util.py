@@ -139,3 +139,10 @@ class BlockLen(_Env):
 
     def __init__(self, tb):
         super().__init__("SSM_SCAN_TB", str(tb))
+
+
+class IndexOrder(_Env):
+    """Temporarily launch packed sequences in index order instead of longest first."""
+
+    def __init__(self):
+        super().__init__("SSM_SCAN_ORDER", "0")

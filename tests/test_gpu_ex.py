@@ -13,7 +13,7 @@ from oracle import ref as R
 from selective_state_space_33_amd import inputs as I
 from selective_state_space_33_amd import ops
 
-from .gpu_util import TOL, Chained, Variant, rel_err, say, to_dev, to_dev_f32
+from .gpu_util import TOL, Chained, IndexOrder, Variant, rel_err, say, to_dev, to_dev_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -99,3 +99,20 @@ def test_packed_other_state_sizes(N):
     rng = np.random.default_rng(540 + N)
     x = I.random_scan_inputs(rng, 1, 500, 72, N, dtype="f32")
     _check(x, "f32", h0=_h0(rng, 3, 72, N), cu=[0, 100, 101, 500], label=f"packed N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_launch_order_changes_no_result(dtype):
+    """Longest-first and index-order launches of the packed units give bit-identical outputs."""
+    rng = np.random.default_rng(550)
+    cu = [0, 5, 1500, 1500, 1510, 1800, 2000]
+    x = I.random_scan_inputs(rng, 1, 2000, 200, 16, dtype=dtype)
+    h0 = _h0(rng, len(cu) - 1, 200, 16)
+    say(f"ex launch order {dtype}")
+    y1, f1 = _gpu_ex(x, dtype, h0, cu)
+    with IndexOrder():
+        y0, f0 = _gpu_ex(x, dtype, h0, cu)
+    assert np.array_equal(y0, y1) and np.array_equal(f0, f1)
+    yo, fo = R.scan_fwd_ex(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                           delta_bias=x["delta_bias"], initial_state=h0, cu_seqlens=cu, nthreads=8)
+    assert rel_err(y1, yo) <= TOL[dtype] and rel_err(f1, fo) <= TOL[dtype]

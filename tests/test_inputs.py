@@ -1,5 +1,6 @@
 """Seeded input generators: determinism, bf16 rounding, and the stated distributions."""
 import numpy as np
+import pytest
 import torch
 
 from selective_state_space_33_amd import inputs as I
@@ -46,3 +47,11 @@ def test_distributions():
     assert abs(float(xa["u"].var()) - 1.0) < 0.15
     spa = np.logaddexp(0.0, xa["delta_bias"].astype(np.float64))
     assert spa.min() >= 1e-4 * (1 - 1e-5) and spa.max() <= 1e-2 * (1 + 1e-5)
+
+
+@pytest.mark.parametrize("total,mean", [(16384, 1024.0), (1000, 10.0), (7, 100.0)])
+def test_packed_offsets_cover_the_row(total, mean):
+    cu = I.packed_offsets(np.random.default_rng(1), total, mean)
+    lens = np.diff(cu)
+    assert cu[0] == 0 and cu[-1] == total and (lens >= 1).all()
+    assert cu == I.packed_offsets(np.random.default_rng(1), total, mean)  # seeded
