@@ -97,7 +97,8 @@ ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const float* A, cons
 
 /* Workspace for ssm_scan_fwd_ex: for nseq <= 0 (no packed sequences) the same
  * as ssm_scan_workspace_size; for nseq > 0 packed sequences (batch must be 1)
- * the packed B/C records only.  Returns 0 for arguments the call would
+ * the packed B/C records and the order in which the sequences are launched
+ * (longest first, nseq ints).  Returns 0 for arguments the call would
  * reject. */
 size_t ssm_scan_fwd_ex_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int64_t nseq,
                                       ssm_dtype_t dt);
