@@ -31,6 +31,8 @@ def _load():
         lib.ssm_ref_scan_fwd_ex.restype = ctypes.c_int
         lib.ssm_ref_scan_fwd_ex.argtypes = ([_dp] * 8 + [ctypes.c_int, _dp, ctypes.POINTER(ctypes.c_long), ctypes.c_long,
                                              _dp, _dp] + [ctypes.c_long] * 4 + [ctypes.c_int])
+        lib.ssm_ref_scan_trap_fwd_ex.restype = ctypes.c_int
+        lib.ssm_ref_scan_trap_fwd_ex.argtypes = lib.ssm_ref_scan_fwd_ex.argtypes
         lib.ssm_ref_state_update.restype = ctypes.c_int
         lib.ssm_ref_state_update.argtypes = [_dp] * 9 + [ctypes.c_int, _dp] + [ctypes.c_long] * 3
         lib.ssm_ref_pair_then.restype = None
@@ -83,7 +85,18 @@ def scan_fwd_ex(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
     initial_state: [rows, dim, dstate] (rows = batch, or the number of sequences), None for zero.
     cu_seqlens: None, or nseq+1 offsets into the L axis of batch row 0 (batch must be 1).
     Returns (y, final_state [rows, dim, dstate]) in float64."""
-    lib = _load()
+    return _scan_rows(_load().ssm_ref_scan_fwd_ex, u, delta, A, B, C, D, z, delta_bias, softplus, initial_state,
+                      cu_seqlens, nthreads)
+
+
+def scan_trap_fwd_ex(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, initial_state=None,
+                     cu_seqlens=None, nthreads=1):
+    """The Mamba-3 trapezoidal three-term scan (ssm_ref_scan_trap_fwd_ex), arguments as scan_fwd_ex."""
+    return _scan_rows(_load().ssm_ref_scan_trap_fwd_ex, u, delta, A, B, C, D, z, delta_bias, softplus,
+                      initial_state, cu_seqlens, nthreads)
+
+
+def _scan_rows(fn, u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, cu_seqlens, nthreads):
     u, delta, A, B, C, D, z, bias, h0 = map(_f64, (u, delta, A, B, C, D, z, delta_bias, initial_state))
     batch, L, dim = u.shape
     N = A.shape[1]
@@ -98,9 +111,8 @@ def scan_fwd_ex(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=Tru
     y = np.empty((batch, L, dim), dtype=np.float64)
     fs = np.empty((rows, dim, N), dtype=np.float64)
     cu_p = None if cu is None else cu.ctypes.data_as(ctypes.POINTER(ctypes.c_long))
-    rc = lib.ssm_ref_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(bias),
-                                 1 if softplus else 0, _ptr(h0), cu_p, nseq, _ptr(y), _ptr(fs),
-                                 batch, L, dim, N, int(nthreads))
+    rc = fn(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(bias),
+            1 if softplus else 0, _ptr(h0), cu_p, nseq, _ptr(y), _ptr(fs), batch, L, dim, N, int(nthreads))
     if rc != 0:
         raise ValueError("oracle scan rejected its arguments")
     return y, fs

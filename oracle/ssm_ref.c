@@ -18,7 +18,9 @@
  *     "From Convolutions to State Spaces: S4");
  *   - y_t reads the state AFTER token t has been written into it;
  *   - optional softplus on delta (with a per-channel bias) and an optional
- *     SiLU(z) gate on the output.
+ *     SiLU(z) gate on the output;
+ *   - and, for Mamba-3, the three-term trapezoidal recurrence (same page,
+ *     Part 7, "Mamba-3 (2026)"; alpha, beta, gamma as read in ssm_ref.h).
  */
 #include "ssm_ref.h"
 
@@ -74,6 +76,31 @@ static double one_step(double* h, double ut, double dt_raw, const double* zt,
   return v;
 }
 
+/* One step of the trapezoidal three-term recurrence for channel d:
+ *   h_t = alpha_t h_{t-1} + beta_t B_{t-1} u_{t-1} + gamma_t B_t u_t
+ * with alpha_t = exp(delta_t A), beta_t = delta_t/2 exp(delta_t A),
+ * gamma_t = delta_t/2.  Bprev is the previous token's B row (NULL at the
+ * first token of a recurrence, whose previous input is zero) and uprev its
+ * input. */
+static double trap_step(double* h, double ut, double dt_raw, const double* zt,
+                        const double* Arow, const double* Bprev, double uprev,
+                        const double* Bt, const double* Ct, const double* D,
+                        const double* bias, long d, long N, int softplus_flag) {
+  double delta = step_delta(dt_raw, bias, d, softplus_flag);
+  double acc = 0.0;
+  for (long n = 0; n < N; ++n) {
+    double alpha = exp(delta * Arow[n]);
+    double beta = 0.5 * delta * alpha;
+    double gamma = 0.5 * delta;
+    double prev_in = Bprev ? beta * Bprev[n] * uprev : 0.0;
+    h[n] = alpha * h[n] + prev_in + gamma * Bt[n] * ut;
+    acc += Ct[n] * h[n];                       /* y_t = C_t . h_t */
+  }
+  double v = acc + (D ? D[d] : 0.0) * ut;
+  if (zt) v = v * ssm_ref_silu(*zt);
+  return v;
+}
+
 typedef struct {
   const double *u, *delta, *A, *B, *C, *D, *z, *bias;
   int softplus_flag;
@@ -82,6 +109,7 @@ typedef struct {
   const double* h0;      /* initial states [rows][dim][N], or NULL for zero */
   const long* cu;        /* packed sequences: row r is tokens cu[r] .. cu[r+1]-1 of batch row 0 */
   long rows;             /* batch rows, or sequences when cu is given */
+  int trapezoid;         /* the three-term recurrence instead of exponential-Euler */
   long first, last; /* range of flattened (row, d) channels for this worker */
 } scan_job;
 
@@ -95,12 +123,22 @@ static void scan_channels(const scan_job* j) {
     double* h = hbuf;
     for (long n = 0; n < j->N; ++n)                /* the given state, else zero */
       h[n] = j->h0 ? j->h0[(r * j->dim + d) * j->N + n] : 0.0;
+    const double* Bprev = NULL;                   /* trapezoidal rule: the previous token's B and u */
+    double uprev = 0.0;
     for (long t = t0; t < t1; ++t) {
       long io = (b * j->L + t) * j->dim + d;      /* [batch, L, dim] */
       long bc = (b * j->L + t) * j->N;            /* [batch, L, dstate] */
-      j->y[io] = one_step(h, j->u[io], j->delta[io], j->z ? &j->z[io] : NULL,
-                          &j->A[d * j->N], &j->B[bc], &j->C[bc], j->D, j->bias, d,
-                          j->N, j->softplus_flag);
+      if (j->trapezoid) {
+        j->y[io] = trap_step(h, j->u[io], j->delta[io], j->z ? &j->z[io] : NULL,
+                             &j->A[d * j->N], Bprev, uprev, &j->B[bc], &j->C[bc], j->D,
+                             j->bias, d, j->N, j->softplus_flag);
+        Bprev = &j->B[bc];
+        uprev = j->u[io];
+      } else {
+        j->y[io] = one_step(h, j->u[io], j->delta[io], j->z ? &j->z[io] : NULL,
+                            &j->A[d * j->N], &j->B[bc], &j->C[bc], j->D, j->bias, d,
+                            j->N, j->softplus_flag);
+      }
     }
     if (j->final_state)
       for (long n = 0; n < j->N; ++n) j->final_state[(r * j->dim + d) * j->N + n] = h[n];
@@ -121,12 +159,12 @@ int ssm_ref_scan_fwd(const double* u, const double* delta, const double* A,
                              y, final_state, batch, L, dim, dstate, nthreads);
 }
 
-int ssm_ref_scan_fwd_ex(const double* u, const double* delta, const double* A,
-                        const double* B, const double* C, const double* D,
-                        const double* z, const double* delta_bias, int softplus_flag,
-                        const double* initial_state, const long* cu_seqlens, long nseq,
-                        double* y, double* final_state,
-                        long batch, long L, long dim, long dstate, int nthreads) {
+static int scan_rows(const double* u, const double* delta, const double* A,
+                     const double* B, const double* C, const double* D,
+                     const double* z, const double* delta_bias, int softplus_flag,
+                     const double* initial_state, const long* cu_seqlens, long nseq,
+                     double* y, double* final_state,
+                     long batch, long L, long dim, long dstate, int nthreads, int trapezoid) {
   if (!u || !delta || !A || !B || !C || !y) return -1;
   if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 4096) return -1;
   long rows = batch;
@@ -146,7 +184,7 @@ int ssm_ref_scan_fwd_ex(const double* u, const double* delta, const double* A,
   int running[256];
   for (int i = 0; i < nthreads; ++i) {
     scan_job j = {u, delta, A, B, C, D, z, delta_bias, softplus_flag, y, final_state,
-                  batch, L, dim, dstate, initial_state, cu_seqlens, rows,
+                  batch, L, dim, dstate, initial_state, cu_seqlens, rows, trapezoid,
                   channels * i / nthreads, channels * (i + 1) / nthreads};
     jobs[i] = j;
   }
@@ -161,6 +199,26 @@ int ssm_ref_scan_fwd_ex(const double* u, const double* delta, const double* A,
   for (int i = 0; i < nthreads; ++i)
     if (running[i]) pthread_join(tids[i], NULL);
   return 0;
+}
+
+int ssm_ref_scan_fwd_ex(const double* u, const double* delta, const double* A,
+                        const double* B, const double* C, const double* D,
+                        const double* z, const double* delta_bias, int softplus_flag,
+                        const double* initial_state, const long* cu_seqlens, long nseq,
+                        double* y, double* final_state,
+                        long batch, long L, long dim, long dstate, int nthreads) {
+  return scan_rows(u, delta, A, B, C, D, z, delta_bias, softplus_flag, initial_state, cu_seqlens, nseq,
+                   y, final_state, batch, L, dim, dstate, nthreads, 0);
+}
+
+int ssm_ref_scan_trap_fwd_ex(const double* u, const double* delta, const double* A,
+                             const double* B, const double* C, const double* D,
+                             const double* z, const double* delta_bias, int softplus_flag,
+                             const double* initial_state, const long* cu_seqlens, long nseq,
+                             double* y, double* final_state,
+                             long batch, long L, long dim, long dstate, int nthreads) {
+  return scan_rows(u, delta, A, B, C, D, z, delta_bias, softplus_flag, initial_state, cu_seqlens, nseq,
+                   y, final_state, batch, L, dim, dstate, nthreads, 1);
 }
 
 int ssm_ref_state_update(double* state, const double* u, const double* delta,

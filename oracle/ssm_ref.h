@@ -61,6 +61,26 @@ int ssm_ref_scan_fwd_ex(const double* u, const double* delta, const double* A,
                         double* y, double* final_state,
                         long batch, long L, long dim, long dstate, int nthreads);
 
+/* The same scan (and the same arguments) with the trapezoidal three-term
+ * recurrence of Mamba-3 ("The State That Must Remember Everything", Part 7,
+ * "Mamba-3 (2026)", item 1):
+ *       h_t = alpha_t h_{t-1} + beta_t B_{t-1} u_{t-1} + gamma_t B_t u_t
+ *   The page calls it a trapezoidal variant of the exponential-Euler rule and
+ *   leaves alpha, beta, gamma undefined.  Reading: the trapezoidal rule
+ *   applied to the step's input integral, whose integrand at the step's start
+ *   has faded by exp(delta_t A) and at its end not at all:
+ *       alpha_t = exp(delta_t A),  beta_t = delta_t/2 * exp(delta_t A),
+ *       gamma_t = delta_t/2.
+ *   At the first token of a recurrence (a batch row, or a packed sequence)
+ *   the previous input is zero, also when an initial state is given.  The
+ *   readout, skip and gate are those of ssm_ref_scan_fwd. */
+int ssm_ref_scan_trap_fwd_ex(const double* u, const double* delta, const double* A,
+                             const double* B, const double* C, const double* D,
+                             const double* z, const double* delta_bias, int softplus_flag,
+                             const double* initial_state, const long* cu_seqlens, long nseq,
+                             double* y, double* final_state,
+                             long batch, long L, long dim, long dstate, int nthreads);
+
 /* One recurrent (decode) step from the given state, updated in place.
  *   u, delta, z, y: [batch, dim];  B, C: [batch, dstate];
  *   state: [batch, dim, dstate].  Same arithmetic as one step of the scan. */

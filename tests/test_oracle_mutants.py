@@ -13,6 +13,7 @@ import pytest
 import oracle.ref as R
 from oracle import build as OB
 import tests.test_oracle_pins as P
+import tests.test_oracle_trap as PT
 
 SRC = os.path.join(os.path.dirname(OB.__file__), "ssm_ref.c")
 
@@ -35,6 +36,33 @@ MUTANTS = {
     "input_term_missing_u": ("double bbar_u = delta * Bt[n] * ut;", "double bbar_u = delta * Bt[n];"),
 }
 
+# Mistakes in the trapezoidal (Mamba-3) step, caught by the pins of test_oracle_trap.py.
+TRAP_MUTANTS = {
+    "trap_beta_without_fade": ("double beta = 0.5 * delta * alpha;", "double beta = 0.5 * delta;"),
+    "trap_beta_and_gamma_swapped": ("double prev_in = Bprev ? beta * Bprev[n] * uprev : 0.0;\n"
+                                    "    h[n] = alpha * h[n] + prev_in + gamma * Bt[n] * ut;",
+                                    "double prev_in = Bprev ? gamma * Bprev[n] * uprev : 0.0;\n"
+                                    "    h[n] = alpha * h[n] + prev_in + beta * Bt[n] * ut;"),
+    "trap_full_step_weights": ("double gamma = 0.5 * delta;", "double gamma = delta;"),
+    "trap_previous_input_never_kept": ("        Bprev = &j->B[bc];\n", ""),
+    "trap_previous_input_is_current": ("        uprev = j->u[io];\n", "        uprev = 0.0;\n"),
+    "trap_previous_B_is_current": ("double prev_in = Bprev ? beta * Bprev[n] * uprev : 0.0;",
+                                   "double prev_in = Bprev ? beta * Bt[n] * uprev : 0.0;"),
+    "trap_gate_dropped": ("  if (zt) v = v * ssm_ref_silu(*zt);\n  return v;\n}\n\ntypedef",
+                          "  return v;\n}\n\ntypedef"),
+    "trap_skip_dropped": ("  double v = acc + (D ? D[d] : 0.0) * ut;\n  if (zt) v = v * ssm_ref_silu(*zt);\n  return v;\n}\n\ntypedef",
+                          "  double v = acc;\n  if (zt) v = v * ssm_ref_silu(*zt);\n  return v;\n}\n\ntypedef"),
+}
+
+TRAP_PINS = [
+    PT.test_impulse_response_by_hand,
+    PT.test_constant_inputs_closed_form,
+    PT.test_second_order_convergence_to_the_continuous_model,
+    PT.test_no_decay_is_the_cumulative_trapezoid,
+    PT.test_initial_state_adds_its_own_decay,
+    PT.test_skip_and_gate_alone,
+]
+
 PINS = [
     P.test_p1_relay_worked_example_composition,
     P.test_p1_relay_for_any_pad_via_decode,
@@ -51,9 +79,10 @@ PINS = [
 ]
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(TRAP_MUTANTS))
 def test_mutant_is_caught(name, tmp_path, monkeypatch):
-    old, new = MUTANTS[name]
+    old, new = MUTANTS[name] if name in MUTANTS else TRAP_MUTANTS[name]
+    pins = PINS if name in MUTANTS else TRAP_PINS
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name} not found"
     mutated = src.replace(old, new, 1)
@@ -66,7 +95,7 @@ def test_mutant_is_caught(name, tmp_path, monkeypatch):
     monkeypatch.setattr(R._build, "LIB", str(lib))
     monkeypatch.setattr(R, "_lib", None)
     failed = []
-    for pin in PINS:
+    for pin in pins:
         try:
             pin()
         except AssertionError:
