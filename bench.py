@@ -9,7 +9,9 @@ The one-token decode step (ssm_state_update, batch 256, dim 5120,
 dstate 16) is timed separately in the same run and reported under "decode",
 the backward pass (ssm_scan_bwd) of the same layer under "backward", and the
 same layer's tokens as one packed row of variable-length sequences, each from
-its own initial state (ssm_scan_fwd_ex), under "packed".
+its own initial state (ssm_scan_fwd_ex), under "packed", and the same layer
+with the Mamba-3 trapezoidal three-term recurrence (ssm_scan_trap_fwd) under
+"trapezoid".
 
 Prints ONE JSON line.  Fields beyond the common ones:
   roofline      the dominant kernel against its binding roofline (VALU issue:
@@ -47,6 +49,9 @@ SLOTS_PER_TOKEN_CHANNEL = 4 * TRANS_SLOTS + 9
 # fma, dh*delta*u, dv*h, a*dh) and the sums over channels of the dB, dC terms (2 adds).  Per (token, channel):
 # softplus and its derivative (exp, log, exp, rcp + 4 ops), SiLU and its derivative (exp, rcp + 4 ops), and the dv,
 # dz, du, d delta, dD and d bias terms (8 ops).
+# The trapezoidal rule adds per (token, channel) u/2, the weight (delta' + delta) u'/2 of the previous token's
+# input, and the delta (u/2) (C.B) term of the readout (2 ops); the update itself costs what the two-term one does.
+TRAP_SLOTS_PER_TOKEN_CHANNEL = SLOTS_PER_TOKEN_CHANNEL + 4
 BWD_SLOTS_PER_UPDATE = 4 + TRANS_SLOTS + 9 + 2
 BWD_SLOTS_PER_TOKEN_CHANNEL = 6 * TRANS_SLOTS + 16
 
@@ -172,6 +177,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
+    ap.add_argument("--no-trapezoid", action="store_true")
     ap.add_argument("--packed-mean-len", type=float, default=1024.0,
                     help="mean sequence length of the packed row (log-normal lengths, sigma 1)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -323,6 +329,25 @@ def main():
                          "roofline": {"bound": "alu", "achieved": ptf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                                       "frac": ptf / VALU_PEAK_TFLOPS}}
         del py, pfs, wsp, h0
+
+    if not args.no_trapezoid:
+        needt = ops.ssm_scan_trap_fwd_workspace_size(w.batch, w.L, w.dim, w.dstate, 0, g["u"].dtype)
+        wst = torch.empty(needt, dtype=torch.uint8, device=dev)
+
+        def tstep():
+            ops.ssm_scan_trap_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
+                                  delta_bias=g["delta_bias"], y=y, final_state=fs, workspace=wst, stream=stream)
+
+        tms, _ = time_calls(tstep, args.steps, max(args.warmup // 4, 5), stream)
+        tslots = w.updates * SLOTS_PER_UPDATE + w.batch * w.L * w.dim * TRAP_SLOTS_PER_TOKEN_CHANNEL
+        ttf = 2.0 * tslots / (tms * 1e-3) / 1e12
+        out["trapezoid"] = {"workload": w.name, "op": "ssm_scan_trap_fwd", "ms_per_step": tms,
+                            "value": w.updates / (tms * 1e-3), "unit": "updates/s", "workspace_bytes": needt,
+                            "roofline": {"bound": "alu", "achieved": ttf, "peak": VALU_PEAK_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": ttf / VALU_PEAK_TFLOPS,
+                                         "counted": f"{SLOTS_PER_UPDATE} slots per state update, "
+                                                    f"{TRAP_SLOTS_PER_TOKEN_CHANNEL} per (token, channel)"}}
+        del wst
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)

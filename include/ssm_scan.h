@@ -128,6 +128,35 @@ ssm_status_t ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, c
                              int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace for ssm_scan_trap_fwd: that of ssm_scan_fwd_ex_workspace_size
+ * for the same arguments plus C_t . B_t of every token (about batch * L * 4
+ * bytes).  Returns 0 for arguments the call would reject. */
+size_t ssm_scan_trap_fwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int64_t nseq,
+                                        ssm_dtype_t dt);
+
+/* ssm_scan_fwd_ex with the trapezoidal three-term recurrence of Mamba-3
+ * ("The State That Must Remember Everything", Part 7, "Mamba-3 (2026)",
+ * item 1), which brings in the previous token's input as well:
+ *     h_t = alpha_t h_{t-1} + beta_t B_{t-1} u_{t-1} + gamma_t B_t u_t,
+ * read as the trapezoidal rule on the step's input integral (the page calls
+ * the recurrence a trapezoidal variant of exponential-Euler and leaves the
+ * coefficients open):
+ *     alpha_t = exp(delta_t A),  beta_t = delta_t/2 * exp(delta_t A),
+ *     gamma_t = delta_t/2,
+ * with delta_t = softplus(delta_raw + bias) (or raw + bias) as in
+ * ssm_scan_fwd.  The readout, D skip and SiLU(z) gate are those of
+ * ssm_scan_fwd; final_state is h after the last token.  At the first token of
+ * a recurrence (a batch row, or a packed sequence) the previous input is
+ * zero, also when an initial state is given: a call starts a sequence, it
+ * does not continue one.  Arguments, layouts, ownership and errors as
+ * ssm_scan_fwd_ex; the workspace comes from ssm_scan_trap_fwd_workspace_size. */
+ssm_status_t ssm_scan_trap_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                               const float* initial_state, const int64_t* cu_seqlens, int64_t nseq,
+                               void* y, float* final_state,
+                               int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* One recurrent (decode) step: the same arithmetic as one token of the scan,
  * reading `state` as h_{t-1} and overwriting it in place with h_t
  * ("Mamba: The State Space Models Challenging the Transformer", "What a

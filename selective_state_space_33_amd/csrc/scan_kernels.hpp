@@ -100,6 +100,8 @@ struct ScanParams {
   // Packed launches: the sequences in launch order (nullable: index order);
   // unit j scans tile column j % n_split of sequence order[j / n_split].
   const int* order;
+  // Trapezoidal rule: C_t . B_t per token, [batch][Lp + kTBMax] (pack_bc_kernel).
+  const float* cb;
 };
 
 // Launch modes of scan_kernel.
@@ -107,6 +109,10 @@ constexpr int kModeFull = 0;     // whole tiles, and chunks of split tiles from 
 constexpr int kModeAgg = 1;      // chunk pairs (P, S) of chunks 0..Ks-2 of every split tile
 constexpr int kModeChained = 2;  // one workgroup per CU: a whole tile with one chunk of a left-over tile spliced in
 constexpr int kModeCkpt = 3;     // whole tiles, no readout: the state entering every block (for the backward pass)
+
+// Discretisation rules of scan_kernel.
+constexpr int kRuleEuler = 0;    // h_t = exp(delta_t A) h_{t-1} + delta_t B_t u_t
+constexpr int kRuleTrap = 1;     // the trapezoidal three-term recurrence (Mamba-3), see scan_kernel
 
 // A workgroup waits for the state carried into its chunk for at most this
 // many polls (each after a short sleep); past that it records an error in
@@ -166,12 +172,16 @@ template <class IO, int NPL>
 __global__ void __launch_bounds__(256) pack_bc_kernel(const void* __restrict__ B, const void* __restrict__ C,
                                                      float* __restrict__ bc, int64_t batch, int64_t L, int64_t Lp,
                                                      int64_t N, int G, unsigned* __restrict__ zero_words,
-                                                     int n_zero) {
+                                                     int n_zero, float* __restrict__ cb) {
   __shared__ float sB[kPackT * 64], sC[kPackT * 64];
-  // the chained scan's flags, ticket and status start at zero on every call
-  if (blockIdx.x == 0)
-    for (int e = threadIdx.x; e < n_zero; e += 256) zero_words[e] = 0u;
   const int Npad = NPL * G;  // <= 64
+  if (blockIdx.x == 0) {
+    // the chained scan's flags, ticket and status start at zero on every call
+    for (int e = threadIdx.x; e < n_zero; e += 256) zero_words[e] = 0u;
+    // so do the kTBMax padding records past the last row, which a pass
+    // ending past Lp reads (their products with a zero step must stay zero)
+    for (int e = threadIdx.x; e < kTBMax * 2 * Npad; e += 256) bc[batch * Lp * 2 * Npad + e] = 0.0f;
+  }
   const int64_t nblk = Lp / kPackT;
   const int64_t b = blockIdx.x / nblk;
   const int64_t t0 = (blockIdx.x % nblk) * kPackT;
@@ -183,6 +193,12 @@ __global__ void __launch_bounds__(256) pack_bc_kernel(const void* __restrict__ B
     sC[e] = ok ? load_elem<IO>(C, (b * L + t) * N + n) : 0.0f;
   }
   __syncthreads();
+  // trapezoidal rule: C_t . B_t of every token (in state order)
+  if (cb && threadIdx.x < kPackT) {
+    float s = 0.0f;
+    for (int n = 0; n < Npad; ++n) s = __builtin_fmaf(sC[threadIdx.x * Npad + n], sB[threadIdx.x * Npad + n], s);
+    cb[b * (Lp + kTBMax) + t0 + threadIdx.x] = s;
+  }
   for (int q = threadIdx.x; q < G * kPackT; q += 256) {
     const int g = q / kPackT, tt = q % kPackT;
     float rec[2 * NPL];
@@ -202,7 +218,7 @@ __global__ void __launch_bounds__(256) pack_bc_kernel(const void* __restrict__ B
   }
 }
 
-template <class IO, int NPL, int G, int VW, int MODE, int TB_>
+template <class IO, int NPL, int G, int VW, int MODE, int TB_, int RULE>
 __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   constexpr int NPAD = NPL * G;
   constexpr int TB = BlockShape<G, VW, TB_>::TB;
@@ -217,9 +233,12 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   static_assert(kRing % 2 == 0, "ring slots keep their block parity");
   constexpr int ES = __is_same(IO, F32) ? 4 : 2;  // bytes per stored element
   constexpr bool HAS_FULL = MODE == kModeFull || MODE == kModeChained;  // a readout pass runs in this launch
+  constexpr bool TRAP = RULE == kRuleTrap;
+  static_assert(!TRAP || MODE != kModeCkpt, "the backward's checkpoints are of the two-term rule");
 
-  // Double-buffered by block parity.
-  __shared__ float2 sDU[2][TB][64];                                  // (delta, delta*u) per token, channel
+  // Double-buffered by block parity.  (delta, delta*u) per token, channel;
+  // (delta, u/2) with the trapezoidal rule.
+  __shared__ float2 sDU[2][TB][64];
   __shared__ float sY[HAS_FULL ? 2 : 1][HAS_FULL ? G : 1][TB][64];   // partial readouts per wavefront
 
   const int tid = threadIdx.x;
@@ -244,9 +263,10 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   int64_t b = 0, d0 = 0, d = 0, pd = 0, t_begin = 0;
   int rows32 = 0;
   bool dvalid = false, pvalid = false, has_z = false;
+  bool row_start = false;                  // the stretch starts a recurrence (no input before it)
   float A2[NPL], biasv[VW], Dv[VW];
   const float* bc_row = p.bc;
-  rsrc_t rs_u, rs_d, rs_z, rs_y;
+  rsrc_t rs_u, rs_d, rs_z, rs_y, rs_cb;
   int voff[RPT];
   rsrc_t rs_bc;                            // this wavefront's packed B/C records of the stretch
   float* ckpt_row = nullptr;               // checkpoint launches: this lane's states at the stretch's first block
@@ -256,6 +276,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     b = tile / p.ntd;
     d0 = static_cast<int64_t>(tile % p.ntd) * 64;
     t_begin = tb;
+    row_start = tb == 0;
     const int64_t rows = te - tb;
     rows32 = static_cast<int>(rows);
     // scan lane: channel d, states n0 .. n0+NPL-1
@@ -292,6 +313,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     rs_y = make_rsrc(HAS_FULL ? static_cast<const char*>(p.y) + base_off : nullptr, HAS_FULL ? bytes : 0);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) voff[i] = voff_rel[i] * row_bytes + pcol * ES;
+    if constexpr (TRAP && HAS_FULL)  // C_t . B_t of the stretch's tokens (zero past the row)
+      rs_cb = make_rsrc(p.cb + b * (p.Lp + kTBMax) + t_begin, (L - t_begin) * static_cast<int64_t>(sizeof(float)));
   };
   // blocks of the current stretch, in whole trips of kRing; blocks past the
   // stretch are padding whose tokens are identity steps (delta = 0) and whose
@@ -323,6 +346,22 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     // of every 16-lane row, read with row broadcasts.
     constexpr int NRV = TB * 2 * NPL / 16;
     float rv[2][NRV];
+    // Trapezoidal rule: C_t . B_t of a prologue thread's rows, per ring slot;
+    // the previous token's (delta, u/2) and B (this lane's states) as the
+    // scan walks the tokens.
+    float rcb[kRing][RPT];
+    float pv_d = 0.0f, pv_hx = 0.0f, Bprev[NPL];
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) Bprev[j] = 0.0f;
+    if constexpr (TRAP) {
+      // the pass continues a recurrence: token t-1 before its first one is real input
+      const int prev_row = k_begin * TB - 1;  // relative to the stretch
+      if (!(row_start && k_begin == 0) && t_begin + prev_row >= 0 && prev_row < rows32) {
+        if (dvalid) pv_hx = 0.5f * load_elem<IO>(p.u, (b * L + t_begin + prev_row) * dim + d);
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) Bprev[j] = bc_row[static_cast<int64_t>(prev_row) * (2 * NPL) + j];
+      }
+    }
 
     auto load_records = [&](auto parc, int blk) {
       constexpr int P = decltype(parc)::value;
@@ -344,6 +383,11 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) rz[S][i] = buf_load<IO, VW>(rs_z, voff[i] + bo, 0);
       }
+      if constexpr (TRAP && FULL) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+          rcb[S][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_cb, (blk * TB + voff_rel[i]) * 4, 0, 0));
+      }
     };
 
     // Stage (delta, delta*u) of block blk (parity P) held in ring slot S.
@@ -364,7 +408,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
           // evaluated either way, so no branch splits the loop body
           float dl = __builtin_fmaf(sp_k, log1p_exp_neg_abs(x), __builtin_fmaxf(x, sp_lo));
           dl = live ? dl : 0.0f;  // padding token: the identity step (1, 0)
-          out[e] = make_float2(dl, dl * uf[e]);
+          if constexpr (TRAP) out[e] = make_float2(dl, live ? 0.5f * uf[e] : 0.0f);
+          else out[e] = make_float2(dl, dl * uf[e]);
         }
         if constexpr (VW == 4) {
           float4* dst = reinterpret_cast<float4*>(&sDU[P][row][pcol]);
@@ -409,6 +454,24 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 #pragma unroll
             for (int ww = 1; ww < G; ++ww) ys[e] += part[ww][e];
           }
+          if constexpr (TRAP) {
+            // + delta_t (u_t/2) (C_t . B_t): the part of h_t the scan leaves out (see update)
+            float st[2 * VW];
+            if constexpr (VW == 4) {
+              const float4 v0 = *reinterpret_cast<const float4*>(&sDU[P][row][pcol]);
+              const float4 v1 = *reinterpret_cast<const float4*>(&sDU[P][row][pcol + 2]);
+              st[0] = v0.x; st[1] = v0.y; st[2] = v0.z; st[3] = v0.w;
+              st[4] = v1.x; st[5] = v1.y; st[6] = v1.z; st[7] = v1.w;
+            } else if constexpr (VW == 2) {
+              const float4 v0 = *reinterpret_cast<const float4*>(&sDU[P][row][pcol]);
+              st[0] = v0.x; st[1] = v0.y; st[2] = v0.z; st[3] = v0.w;
+            } else {
+              const float2 v0 = sDU[P][row][pcol];
+              st[0] = v0.x; st[1] = v0.y;
+            }
+#pragma unroll
+            for (int e = 0; e < VW; ++e) ys[e] = __builtin_fmaf(st[2 * e] * st[2 * e + 1], rcb[S][i], ys[e]);
+          }
           float uf[VW], zf[VW], out[VW];
           unpack<IO, VW>(ru[S][i], uf);
           if (has_z) unpack<IO, VW>(rz[S][i], zf);
@@ -425,10 +488,50 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 
     // The state updates of token q of group g of a block whose records are in
     // slot P: its record (B then C) is floats F .. F + 2*NPL of the block's.
+    //
+    // Trapezoidal rule.  The recurrence h_t = a_t h_{t-1} + (delta_t/2) a_t
+    // B_{t-1} u_{t-1} + (delta_t/2) B_t u_t (a_t = exp(delta_t A)) is scanned as
+    //   s_t = h_t - (delta_t/2) B_t u_t
+    //       = a_t (s_{t-1} + (delta_{t-1} + delta_t) (u_{t-1}/2) B_{t-1}),
+    // which costs an update what the two-term rule does: one fma on the
+    // previous token's B (a row broadcast of the record before this one), one
+    // multiply by the fade.  The epilogue adds the left-out part of y_t,
+    // delta_t (u_t/2) (C_t . B_t), and a pass hands on h (see run_pass's end).
     auto update = [&](auto parc, auto gc, auto qc, const float2 dd, float& block_delta) {
       constexpr int P = decltype(parc)::value;
-      constexpr int F = (decltype(gc)::value * SUB + decltype(qc)::value) * 2 * NPL;
+      constexpr int TQ = decltype(gc)::value * SUB + decltype(qc)::value;  // token within the block
+      constexpr int F = TQ * 2 * NPL;
       float yp = 0.0f;
+      if constexpr (TRAP) {
+        const float cw = (pv_d + dd.x) * pv_hx;
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+          (([&] {
+             constexpr int j = J;
+             const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
+             float g;
+             if constexpr (TQ == 0) {
+               g = __builtin_fmaf(cw, Bprev[j], h[j]);
+             } else {
+               constexpr int fp = F - 2 * NPL + j;  // B_{t-1}[n0 + j]
+               g = fmac_row_bcast<fp % 16>(h[j], rv[P][fp / 16], cw);
+             }
+             h[j] = a * g;
+             if constexpr (FULL) {
+               constexpr int fc = F + NPL + j;
+               if constexpr (j == 0) yp = row_bcast<fc % 16>(rv[P][fc / 16]) * h[0];
+               else yp = fmac_row_bcast<fc % 16>(yp, rv[P][fc / 16], h[j]);
+             } else {
+               asm volatile("" : "+v"(h[j]));
+             }
+           }()),
+           ...);
+        }(std::make_integer_sequence<int, NPL>{});
+        pv_d = dd.x;
+        pv_hx = dd.y;
+        if constexpr (FULL) sY[P][w][TQ][lane] = yp;
+        else block_delta += dd.x;
+        return;
+      }
       [&]<int... J>(std::integer_sequence<int, J...>) {
         (([&] {
            constexpr int j = J;
@@ -498,6 +601,13 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       [&]<int... I>(std::integer_sequence<int, I...>) {
         ((group(parc, IC<I % 2>{}, IC<I>{}, block_delta)), ...);
       }(std::make_integer_sequence<int, NG>{});
+      if constexpr (TRAP) {
+        // B of the block's last token, for the next block's first update
+        constexpr int LF = (TB - 1) * 2 * NPL;
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+          ((Bprev[J] = row_bcast<(LF + J) % 16>(rv[P][(LF + J) / 16])), ...);
+        }(std::make_integer_sequence<int, NPL>{});
+      }
       delta_total += block_delta;
       __syncthreads();
     };
@@ -537,6 +647,13 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     }
     epilogue(IC<1>{}, IC<kRing - 1>{}, k_end - 1);  // k_end is a multiple of kRing (even)
     __syncthreads();  // the staging buffers are free for whatever runs next
+    if constexpr (TRAP) {
+      // back from s to h: h = s + delta (u/2) B of the last token scanned (zero
+      // after a padding token, whose step already made the same correction)
+      const float e = pv_d * pv_hx;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) h[j] = __builtin_fmaf(e, Bprev[j], h[j]);
+    }
     return delta_total;
   };
 
@@ -677,6 +794,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       te = te < tb ? tb : (te > L ? L : te);
     }
     set_tile(tile, tb, te);
+    if (packed) row_start = true;  // a packed sequence has no input before its first token
     const int64_t pair_row = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;   // row of [n_split][Ks][64]
     if constexpr (MODE == kModeCkpt) {
       init_state(b);

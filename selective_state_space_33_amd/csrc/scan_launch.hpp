@@ -1,8 +1,8 @@
 // scan_launch.hpp -- launch of scan_kernel for a runtime-chosen variant.
 //
-// The kernel is instantiated per storage type and launch mode in separate
-// translation units (scan_<type>_<mode>.hip), which are compiled in parallel;
-// ssm_scan.hip only calls launch_scan.
+// The kernel is instantiated per storage type, launch mode and discretisation
+// rule in separate translation units (scan_<type>_<mode>[_trap].hip), which
+// are compiled in parallel; ssm_scan.hip only calls launch_scan.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,10 +15,10 @@ namespace ssm {
 // variant's preferred width, else 1); tb: tokens per block (16, or 32 where
 // variant_has_tb32).  Returns hipErrorInvalidValue for a variant that does
 // not exist.
-template <class IO, int MODE>
+template <class IO, int MODE, int RULE = kRuleEuler>
 hipError_t launch_scan(int npl, int G, int vw, int tb, const ScanParams& p, dim3 grid, hipStream_t s);
 
-// Instantiated (each in its own translation unit) for these eight combinations.
+// Instantiated (each in its own translation unit) for these fourteen combinations.
 extern template hipError_t launch_scan<F32, kModeFull>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<F32, kModeAgg>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<F32, kModeChained>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
@@ -28,6 +28,18 @@ extern template hipError_t launch_scan<F32, kModeCkpt>(int, int, int, int, const
 extern template hipError_t launch_scan<BF16, kModeCkpt>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<BF16, kModeChained>(int, int, int, int, const ScanParams&,
                                                            dim3, hipStream_t);
+extern template hipError_t launch_scan<F32, kModeFull, kRuleTrap>(int, int, int, int, const ScanParams&, dim3,
+                                                                 hipStream_t);
+extern template hipError_t launch_scan<F32, kModeAgg, kRuleTrap>(int, int, int, int, const ScanParams&, dim3,
+                                                                hipStream_t);
+extern template hipError_t launch_scan<F32, kModeChained, kRuleTrap>(int, int, int, int, const ScanParams&, dim3,
+                                                                    hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeFull, kRuleTrap>(int, int, int, int, const ScanParams&, dim3,
+                                                                  hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeAgg, kRuleTrap>(int, int, int, int, const ScanParams&, dim3,
+                                                                 hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeChained, kRuleTrap>(int, int, int, int, const ScanParams&, dim3,
+                                                                     hipStream_t);
 
 // Variants (states per lane, wavefronts).  Each exists with its preferred
 // prologue width (channels per thread: 4 up to 4 wavefronts, 2 for 8, 1 for

@@ -53,13 +53,15 @@ struct Plan {
   bool chained;  // split tiles chain their carries inside the one scan launch
   int tb;        // tokens per block of the readout scan (16, or 32 with a CU per workgroup)
   bool packed;   // packed sequences: "chunk" c of a tile column is sequence c (no pairs, no carries)
+  bool trap;     // trapezoidal rule: also C_t . B_t per token
 };
 
 // Workspace layout: [packed B/C][chunk fades P][chunk states S][carried-in
-// states][flags, ticket, status][sequence order].  The chained plan needs no
-// P, S; the others no flags; only the packed plan has an order.
+// states][flags, ticket, status][sequence order][C_t . B_t].  The chained
+// plan needs no P, S; the others no flags; only the packed plan has an
+// order, only the trapezoidal rule C . B.
 struct Layout {
-  size_t bc, pairs, carry, words, order, total;
+  size_t bc, pairs, carry, words, order, cb, total;
   int n_words;
 };
 
@@ -73,7 +75,8 @@ Layout layout_for(const Plan& pl, int64_t batch) {
   l.n_words = pl.chained ? pl.n_split * pl.Ks + 2 : 0;
   l.words = align256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
   l.order = pl.packed ? align256(static_cast<size_t>(pl.Ks) * sizeof(int)) : 0;
-  l.total = l.bc + 2 * l.pairs + l.carry + l.words + l.order;
+  l.cb = pl.trap ? align256(static_cast<size_t>(batch) * (pl.Lp + kTBMax) * sizeof(float)) : 0;
+  l.total = l.bc + 2 * l.pairs + l.carry + l.words + l.order + l.cb;
   return l;
 }
 
@@ -215,6 +218,7 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
   const char* te = getenv("SSM_SCAN_TB");
   if (te && tb32_ok && (atoi(te) == 16 || atoi(te) == 32)) pl->tb = atoi(te);
   pl->packed = false;
+  pl->trap = false;
 }
 
 // Packed sequences (batch row 0 holds nseq of them): every (tile column,
@@ -239,6 +243,7 @@ void plan_packed(int64_t L, int64_t dim, int64_t N, int vw_ok, int64_t nseq, Pla
   pl->Lp = ceil_div(L, kTrip) * kTrip;
   pl->chained = false;
   pl->packed = true;
+  pl->trap = false;
   const bool tb32_ok = variant_has_tb32(npl, G, pl->vw, kModeFull);
   pl->tb = (tb32_ok && static_cast<int64_t>(pl->ntd) * nseq <= kNumCU) ? 32 : 16;
 }
@@ -260,7 +265,7 @@ ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, c
   return SSM_OK;
 }
 
-template <class IO>
+template <class IO, int RULE>
 hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void* C, float* bc, ScanParams p,
                     hipStream_t s) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
@@ -268,7 +273,7 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
 #define SSM_PACK_CASE(NPL_)                                                                                  \
   if (pl.npl == NPL_)                                                                                       \
     hipLaunchKernelGGL((pack_bc_kernel<IO, NPL_>), pgrid, dim3(256), 0, s, B, C, bc, p.batch, p.L, pl.Lp, p.N, \
-                       pl.G, p.flags, lay.n_words);
+                       pl.G, p.flags, lay.n_words, const_cast<float*>(p.cb));
   SSM_PACK_CASE(1)
   SSM_PACK_CASE(2)
   SSM_PACK_CASE(4)
@@ -285,10 +290,10 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
   }
   const dim3 grid_full(static_cast<unsigned>(pl.n_long + static_cast<int64_t>(pl.n_split) * pl.Ks));
   if (pl.chained)  // one workgroup per whole tile, each also running at most one chunk
-    return launch_scan<IO, kModeChained>(pl.npl, pl.G, pl.vw, pl.tb, p, dim3(pl.n_long), s);
+    return launch_scan<IO, kModeChained, RULE>(pl.npl, pl.G, pl.vw, pl.tb, p, dim3(pl.n_long), s);
   if (pl.n_split > 0 && pl.Ks > 1 && !pl.packed) {
     const dim3 grid_agg(static_cast<unsigned>(static_cast<int64_t>(pl.n_split) * (pl.Ks - 1)));
-    e = launch_scan<IO, kModeAgg>(pl.npl, pl.G, pl.vw, 16, p, grid_agg, s);
+    e = launch_scan<IO, kModeAgg, RULE>(pl.npl, pl.G, pl.vw, 16, p, grid_agg, s);
     if (e != hipSuccess) return e;
     const int64_t cols = static_cast<int64_t>(pl.n_split) * 64 * npad;
     hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>(ceil_div(cols, kCarryCols))), dim3(256), 0, s,
@@ -298,7 +303,7 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return launch_scan<IO, kModeFull>(pl.npl, pl.G, pl.vw, pl.tb, p, grid_full, s);
+  return launch_scan<IO, kModeFull, RULE>(pl.npl, pl.G, pl.vw, pl.tb, p, grid_full, s);
 }
 
 template <class IO>
@@ -353,22 +358,32 @@ hipError_t run_decode(const DecodeParams& p, hipStream_t s) {
 
 using namespace ssm;
 
-extern "C" size_t ssm_scan_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt) {
+namespace ssm {
+namespace {
+
+// Workspace of a forward call (nseq > 0: packed sequences; trap: the
+// trapezoidal rule).  The layout depends only on the variant, which the
+// pointers do not change; size it for the widest and the narrowest prologue
+// anyway.  0 for arguments the call would reject.
+size_t fwd_workspace(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int64_t nseq, ssm_dtype_t dt,
+                     bool trap) {
   if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 64 || batch > kMaxBatch) return 0;
   if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return 0;
-  // The packed layout depends only on the variant, which the pointers do not
-  // change; size it for the widest and the narrowest prologue anyway.
-  Plan p4, p1;
   const int64_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
-  if (max_chunk_len(dim, es) < kChunkQuantum) return 0;
-  plan_scan(batch, L, dim, dstate, es, 4, &p4);
-  plan_scan(batch, L, dim, dstate, es, 1, &p1);
+  Plan p4, p1;
+  if (nseq > 0) {
+    if (batch != 1 || max_chunk_len(dim, es) < ceil_div(L, kChunkQuantum) * kChunkQuantum) return 0;
+    plan_packed(L, dim, dstate, 4, nseq, &p4);
+    plan_packed(L, dim, dstate, 1, nseq, &p1);
+  } else {
+    if (max_chunk_len(dim, es) < kChunkQuantum) return 0;
+    plan_scan(batch, L, dim, dstate, es, 4, &p4);
+    plan_scan(batch, L, dim, dstate, es, 1, &p1);
+  }
+  p4.trap = p1.trap = trap;
   const size_t a = layout_for(p4, batch).total, b = layout_for(p1, batch).total;
   return a > b ? a : b;
 }
-
-namespace ssm {
-namespace {
 
 // The forward, from given initial states and over packed sequences when
 // asked (cu_seqlens non-null: batch 1, nseq sequences).
@@ -376,7 +391,7 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
                            const float* D, const void* z, const float* delta_bias, int softplus_flag,
                            const float* h0, const int64_t* cu_seqlens, int64_t nseq, void* y, float* final_state,
                            int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
+                           size_t workspace_bytes, hipStream_t stream, int rule) {
   const ssm_status_t st =
       check_scan_args(u, delta, A, B, C, D, z, delta_bias, y, final_state, batch, L, dim, dstate, dt);
   if (st != SSM_OK) return st;
@@ -405,6 +420,7 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
   if (static_cast<int64_t>(pl.n_long) + static_cast<int64_t>(pl.n_split) * pl.Ks > 0x7fffffffLL ||
       batch * (pl.Lp / kPackT) > 0x7fffffffLL)
     return SSM_ERR_UNSUPPORTED;
+  pl.trap = rule == kRuleTrap;
   const Layout lay = layout_for(pl, batch);
   if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256)) return SSM_ERR_INVALID_ARG;
 
@@ -442,6 +458,8 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
   }
   const char* oe = getenv("SSM_SCAN_ORDER");
   p.order = (lay.order && !(oe && atoi(oe) == 0)) ? reinterpret_cast<const int*>(ws + off) : nullptr;
+  off += lay.order;
+  p.cb = lay.cb ? reinterpret_cast<const float*>(ws + off) : nullptr;
   p.batch = batch;
   p.L = L;
   p.Lp = pl.Lp;
@@ -454,13 +472,22 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
   p.Ks = pl.Ks;
   p.softplus = softplus_flag ? 1 : 0;
   float* bc = reinterpret_cast<float*>(ws);
-  const hipError_t e = dt == SSM_DTYPE_F32 ? run_scan<F32>(pl, lay, B, C, bc, p, stream)
-                                           : run_scan<BF16>(pl, lay, B, C, bc, p, stream);
+  hipError_t e;
+  if (pl.trap)
+    e = dt == SSM_DTYPE_F32 ? run_scan<F32, kRuleTrap>(pl, lay, B, C, bc, p, stream)
+                            : run_scan<BF16, kRuleTrap>(pl, lay, B, C, bc, p, stream);
+  else
+    e = dt == SSM_DTYPE_F32 ? run_scan<F32, kRuleEuler>(pl, lay, B, C, bc, p, stream)
+                            : run_scan<BF16, kRuleEuler>(pl, lay, B, C, bc, p, stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 }  // namespace
 }  // namespace ssm
+
+extern "C" size_t ssm_scan_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt) {
+  return fwd_workspace(batch, L, dim, dstate, 0, dt, false);
+}
 
 extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                                      const float* D, const void* z, const float* delta_bias, int softplus_flag,
@@ -468,21 +495,12 @@ extern "C" ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const flo
                                      int64_t dstate, ssm_dtype_t dt, void* workspace, size_t workspace_bytes,
                                      hipStream_t stream) {
   return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus_flag, nullptr, nullptr, 0, y, final_state,
-                       batch, L, dim, dstate, dt, workspace, workspace_bytes, stream);
+                       batch, L, dim, dstate, dt, workspace, workspace_bytes, stream, kRuleEuler);
 }
 
 extern "C" size_t ssm_scan_fwd_ex_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate,
                                                  int64_t nseq, ssm_dtype_t dt) {
-  if (nseq <= 0) return ssm_scan_workspace_size(batch, L, dim, dstate, dt);
-  if (batch != 1 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 64) return 0;
-  if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return 0;
-  const int64_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
-  if (max_chunk_len(dim, es) < ceil_div(L, kChunkQuantum) * kChunkQuantum) return 0;
-  Plan p4, p1;
-  plan_packed(L, dim, dstate, 4, nseq, &p4);
-  plan_packed(L, dim, dstate, 1, nseq, &p1);
-  const size_t a = layout_for(p4, 1).total, b = layout_for(p1, 1).total;
-  return a > b ? a : b;
+  return fwd_workspace(batch, L, dim, dstate, nseq, dt, false);
 }
 
 extern "C" ssm_status_t ssm_scan_fwd_ex(const void* u, const void* delta, const float* A, const void* B,
@@ -493,7 +511,23 @@ extern "C" ssm_status_t ssm_scan_fwd_ex(const void* u, const void* delta, const 
                                         size_t workspace_bytes, hipStream_t stream) {
   return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus_flag, initial_state, cu_seqlens,
                        cu_seqlens ? nseq : 0, y, final_state, batch, L, dim, dstate, dt, workspace,
-                       workspace_bytes, stream);
+                       workspace_bytes, stream, kRuleEuler);
+}
+
+extern "C" size_t ssm_scan_trap_fwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate,
+                                                   int64_t nseq, ssm_dtype_t dt) {
+  return fwd_workspace(batch, L, dim, dstate, nseq, dt, true);
+}
+
+extern "C" ssm_status_t ssm_scan_trap_fwd(const void* u, const void* delta, const float* A, const void* B,
+                                          const void* C, const float* D, const void* z, const float* delta_bias,
+                                          int softplus_flag, const float* initial_state, const int64_t* cu_seqlens,
+                                          int64_t nseq, void* y, float* final_state, int64_t batch, int64_t L,
+                                          int64_t dim, int64_t dstate, ssm_dtype_t dt, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus_flag, initial_state, cu_seqlens,
+                       cu_seqlens ? nseq : 0, y, final_state, batch, L, dim, dstate, dt, workspace,
+                       workspace_bytes, stream, kRuleTrap);
 }
 
 extern "C" ssm_status_t ssm_state_update(float* state, const void* u, const void* delta, const float* A,

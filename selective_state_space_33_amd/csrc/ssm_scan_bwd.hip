@@ -68,10 +68,10 @@ hipError_t run_bwd(const BwdPlan& pl, const void* B, const void* C, float* bc, S
   const dim3 pgrid(static_cast<unsigned>(sp.batch * (pl.Lp / kPackT)));
   if (pl.npl == 2)
     hipLaunchKernelGGL((pack_bc_kernel<IO, 2>), pgrid, dim3(256), 0, s, B, C, bc, sp.batch, sp.L, pl.Lp, sp.N,
-                       pl.G, static_cast<unsigned*>(nullptr), 0);
+                       pl.G, static_cast<unsigned*>(nullptr), 0, static_cast<float*>(nullptr));
   else
     hipLaunchKernelGGL((pack_bc_kernel<IO, 4>), pgrid, dim3(256), 0, s, B, C, bc, sp.batch, sp.L, pl.Lp, sp.N,
-                       pl.G, static_cast<unsigned*>(nullptr), 0);
+                       pl.G, static_cast<unsigned*>(nullptr), 0, static_cast<float*>(nullptr));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_scan<IO, kModeCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.T)), s);

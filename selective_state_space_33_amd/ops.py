@@ -22,7 +22,8 @@ SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 
 # Every symbol include/ssm_scan.h declares.
 EXPORTED = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_ex_workspace_size", "ssm_scan_fwd_ex",
-            "ssm_state_update", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_status_string")
+            "ssm_scan_trap_fwd_workspace_size", "ssm_scan_trap_fwd", "ssm_state_update",
+            "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_status_string")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -54,6 +55,10 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_fwd_ex.restype = ctypes.c_int
         L.ssm_scan_fwd_ex.argtypes = ([_vp] * 8 + [ctypes.c_int, _vp, _vp, _i64, _vp, _vp] + [_i64] * 4 +
                                       [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
+        L.ssm_scan_trap_fwd_workspace_size.restype = ctypes.c_size_t
+        L.ssm_scan_trap_fwd_workspace_size.argtypes = L.ssm_scan_fwd_ex_workspace_size.argtypes
+        L.ssm_scan_trap_fwd.restype = ctypes.c_int
+        L.ssm_scan_trap_fwd.argtypes = L.ssm_scan_fwd_ex.argtypes
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_scan_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
         L.ssm_scan_bwd.restype = ctypes.c_int
@@ -149,6 +154,24 @@ def ssm_scan_fwd_ex(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus
     initial_state: [rows, dim, dstate] float32 (rows = batch, or the number of sequences).
     cu_seqlens: int64 device tensor of nseq + 1 offsets into the L axis of batch row 0 (batch must be 1).
     Returns (y, final_state [rows, dim, dstate])."""
+    return _fwd_rows("ssm_scan_fwd_ex", u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, cu_seqlens,
+                     y, final_state, workspace, stream)
+
+
+def ssm_scan_trap_fwd_workspace_size(batch: int, L: int, dim: int, dstate: int, nseq: int,
+                                     dtype: torch.dtype) -> int:
+    return int(lib().ssm_scan_trap_fwd_workspace_size(batch, L, dim, dstate, nseq, _dtype_code(dtype)))
+
+
+def ssm_scan_trap_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
+                      initial_state=None, cu_seqlens=None, y=None, final_state=None, workspace=None, stream=None):
+    """The Mamba-3 trapezoidal three-term scan; arguments and results as ssm_scan_fwd_ex."""
+    return _fwd_rows("ssm_scan_trap_fwd", u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, cu_seqlens,
+                     y, final_state, workspace, stream)
+
+
+def _fwd_rows(entry, u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, cu_seqlens, y, final_state,
+              workspace, stream):
     batch, L, dim = u.shape
     dstate = A.shape[1]
     dev, dt = u.device, u.dtype
@@ -174,16 +197,16 @@ def ssm_scan_fwd_ex(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus
     if final_state is None:
         final_state = torch.empty((rows, dim, dstate), dtype=torch.float32, device=dev)
     _check(final_state, "final_state", torch.float32, (rows, dim, dstate), dev)
-    need = ssm_scan_fwd_ex_workspace_size(batch, L, dim, dstate, nseq, dt)
+    need = int(getattr(lib(), entry + "_workspace_size")(batch, L, dim, dstate, nseq, code))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = lib().ssm_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+    rc = getattr(lib(), entry)(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                                1 if softplus else 0, _ptr(initial_state), _ptr(cu_seqlens), nseq, _ptr(y),
                                _ptr(final_state), batch, L, dim, dstate, code, _ptr(workspace), ws_bytes,
                                _stream(dev, stream))
     if rc != SSM_OK:
-        raise SSMError(rc, "ssm_scan_fwd_ex")
+        raise SSMError(rc, entry)
     return y, final_state
 
 

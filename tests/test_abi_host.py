@@ -119,12 +119,13 @@ def test_state_update_rejects_bad_arguments_without_launching(kw, expect):
     assert _upd(ops.lib(), **kw) == expect
 
 
-def _ex(lib_, **kw):
-    """Call ssm_scan_fwd_ex with fake (never dereferenced) pointers; only rejection paths are used."""
+def _ex(lib_, entry="ssm_scan_fwd_ex", **kw):
+    """Call ssm_scan_fwd_ex (or ssm_scan_trap_fwd) with fake (never dereferenced) pointers; only rejection paths
+    are used."""
     a = dict(u=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, z=None, bias=None, sp=1, h0=None,
              cu=None, nseq=0, y=0x6000, fs=None, batch=1, L=8, dim=8, N=16, dt=F32, ws=None, wsb=0, stream=None)
     a.update(kw)
-    return lib_.ssm_scan_fwd_ex(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
+    return getattr(lib_, entry)(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"],
                                 a["h0"], a["cu"], a["nseq"], a["y"], a["fs"], a["batch"], a["L"], a["dim"], a["N"],
                                 a["dt"], a["ws"], a["wsb"], a["stream"])
 
@@ -137,8 +138,21 @@ def _ex(lib_, **kw):
     (dict(N=65), UNSUPPORTED),
     (dict(cu=0x8000, nseq=2), INVALID),                 # no workspace
 ])
-def test_scan_ex_rejects_bad_arguments_without_launching(kw, expect):
-    assert _ex(ops.lib(), **kw) == expect
+@pytest.mark.parametrize("entry", ["ssm_scan_fwd_ex", "ssm_scan_trap_fwd"])
+def test_scan_ex_rejects_bad_arguments_without_launching(kw, expect, entry):
+    assert _ex(ops.lib(), entry, **kw) == expect
+
+
+def test_trap_workspace_size():
+    """The trapezoidal rule needs the plain workspace plus C_t . B_t of every token (fp32)."""
+    L = ops.lib()
+    for args in ((2, 1000, 136, 16, 0, BF16), (1, 1000, 136, 16, 7, F32), (4, 4096, 5120, 16, 0, BF16)):
+        plain = L.ssm_scan_fwd_ex_workspace_size(*args)
+        trap = L.ssm_scan_trap_fwd_workspace_size(*args)
+        batch, Lq = args[0], args[1]
+        assert plain > 0 and trap >= plain + batch * Lq * 4 and trap % 256 == 0
+    assert L.ssm_scan_trap_fwd_workspace_size(2, 1000, 136, 16, 7, BF16) == 0     # packed needs batch 1
+    assert L.ssm_scan_trap_fwd_workspace_size(1, 100, 64, 65, 0, F32) == 0        # dstate > 64
 
 
 def test_scan_ex_workspace_size():
