@@ -10,4 +10,6 @@ numpy arrays into it.  Parity pins are in ``tests/test_oracle_pins.py``.
 ``bwd.py`` is the backward pass: fp64 automatic differentiation (torch, CPU)
 of its own transcription of the forward, pinned in ``tests/test_oracle_bwd.py``
 against the C oracle's forward and central finite differences of it.
+``ssd.py`` is the Mamba-2 SSD layer in its quadratic masked-matrix form (numpy),
+pinned in ``tests/test_oracle_ssd.py`` against the C oracle's recurrence.
 """

@@ -1,0 +1,69 @@
+"""fp64 CPU oracle for the Mamba-2 state-space-duality (SSD) layer.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py): the test-suite, the smoke
+check and the benchmark's CPU baseline may call it; the product path never
+does.
+
+What it computes.  Mamba-2 restricts the state matrix of every head to one
+number times the identity ("State Space Models and the Post-Transformer Era",
+"Mamba-2 and Structured State Space Duality"; "Mamba is attention all you
+really need, part 2", the Mamba-2 entry of the lineage), and the page shows
+the resulting sequence map to be multiplication by a causal 1-semiseparable
+matrix, the same object masked linear attention multiplies by ("The State That
+Must Remember Everything", Part 4).  Reading (the pages give no shapes): a head
+is a group of `headdim` channels sharing the step delta_t and the scalar A of
+the head; B_t and C_t (dstate each) are shared by all heads, as in the
+two-term scan.  Per batch row and head, with x_t the head's headdim inputs:
+
+    H_t = exp(delta_t A) H_{t-1} + delta_t x_t B_t^T      (H: headdim x dstate, H_{-1} = 0)
+    y_t = H_t C_t + D x_t,  then times SiLU(z_t) when z is given
+
+This oracle evaluates the other ordering of the same computation, the
+quadratic "attention" form, literally:
+
+    M[t, s] = (C_t . B_s) * exp(A * (cs_t - cs_s)) * delta_s   for s <= t, else 0,
+    cs_t = delta_0 + ... + delta_t,
+    y = M x + D x,   final state H_{L-1} = sum_s exp(A (cs_{L-1} - cs_s)) delta_s x_s B_s^T,
+
+with numpy matrix products.  delta_t = softplus(delta_raw + bias) with the
+exact log-add-exp, or delta_raw + bias when softplus is off.  The tests pin it
+to the recurrent oracle (ssm_ref.c) on head-broadcast inputs and to plain
+causal linear attention at A = 0, delta = 1.
+"""
+import numpy as np
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=np.float64)
+
+
+def ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True):
+    """SSD layer in the masked-matrix form.
+
+    x, z: [batch, L, heads, headdim]; delta: [batch, L, heads]; A, D, delta_bias: [heads];
+    B, C: [batch, L, dstate].  Returns (y [batch, L, heads, headdim],
+    final_state [batch, heads, headdim, dstate]) in float64."""
+    x, delta, A, B, C, D, z, bias = map(_f64, (x, delta, A, B, C, D, z, delta_bias))
+    batch, L, H, P = x.shape
+    N = B.shape[2]
+    assert delta.shape == (batch, L, H) and A.shape == (H,)
+    assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+    raw = delta if bias is None else delta + bias
+    dl = np.logaddexp(raw, 0.0) if softplus else raw                       # [batch, L, H]
+    y = np.empty((batch, L, H, P))
+    fs = np.empty((batch, H, P, N))
+    causal = np.tril(np.ones((L, L), dtype=bool))
+    for b in range(batch):
+        G = C[b] @ B[b].T                                                   # [t, s] = C_t . B_s
+        for h in range(H):
+            cs = np.cumsum(dl[b, :, h])
+            decay = np.exp(np.where(causal, A[h] * (cs[:, None] - cs[None, :]), -np.inf))
+            M = G * decay * dl[b, None, :, h]                               # [t, s]
+            y[b, :, h] = M @ x[b, :, h]
+            if D is not None:
+                y[b, :, h] += D[h] * x[b, :, h]
+            w = np.exp(A[h] * (cs[-1] - cs)) * dl[b, :, h]                  # weight of token s in H_{L-1}
+            fs[b, h] = (x[b, :, h] * w[:, None]).T @ B[b]
+    if z is not None:
+        y = y * (z / (1.0 + np.exp(-z)))
+    return y, fs

@@ -172,3 +172,32 @@ def packed_offsets(rng: np.random.Generator, total: int, mean_len: float, sigma:
         n = max(1, int(round(rng.lognormal(mu, sigma))))
         cu.append(min(total, cu[-1] + n))
     return cu
+
+
+# The Mamba-2 (SSD) layer shaped like the 2.7B model: d_inner 5120 as 80 heads of 64 channels, state 128
+# (8x the two-term layer's 16), batch 4, L 4096, bf16.
+SSD_WORKLOADS = {
+    "mamba2_2p7b_bf16": dict(batch=4, L=4096, heads=80, headdim=64, dstate=128, dtype="bf16"),
+    "ssd_small_bf16": dict(batch=2, L=300, heads=3, headdim=64, dstate=64, dtype="bf16"),
+}
+
+
+def random_ssd_inputs(rng: np.random.Generator, batch: int, L: int, heads: int, headdim: int, dstate: int,
+                      dtype: str = "bf16", gate: bool = True) -> dict:
+    """Seeded inputs of the SSD layer (float32 arrays, bf16-representable where stored as bf16).
+
+    x, z: [batch, L, heads, headdim] ~ N(0, 1); delta (raw): [batch, L, heads] ~ N(0, 1); B, C: [batch, L, dstate]
+    ~ N(0, 1); A: [heads] = -U[1, 16] (a scalar per head); D = 1; delta_bias = log(expm1(U[1e-3, 0.1])), so
+    softplus(bias) is uniform in [1e-3, 0.1]."""
+    x = rng.standard_normal((batch, L, heads, headdim), dtype=np.float32)
+    z = rng.standard_normal((batch, L, heads, headdim), dtype=np.float32) if gate else None
+    delta = rng.standard_normal((batch, L, heads), dtype=np.float32)
+    B = rng.standard_normal((batch, L, dstate), dtype=np.float32)
+    C = rng.standard_normal((batch, L, dstate), dtype=np.float32)
+    A = -rng.uniform(1.0, 16.0, size=heads).astype(np.float32)
+    bias = np.log(np.expm1(rng.uniform(1e-3, 0.1, size=heads))).astype(np.float32)
+    return {
+        "x": _store(x, dtype), "z": _store(z, dtype) if z is not None else None, "delta": _store(delta, dtype),
+        "B": _store(B, dtype), "C": _store(C, dtype), "A": A, "D": np.ones(heads, dtype=np.float32),
+        "delta_bias": bias,
+    }

@@ -1,0 +1,129 @@
+"""Pins of the SSD oracle (oracle/ssd.py, the quadratic masked-matrix form), on the CPU.
+
+  - Duality: the masked-matrix form equals the recurrent selective scan
+    (the C oracle, pinned in test_oracle_pins.py) run with the head's scalar
+    A on every state and the head's step on every channel of the head, for y
+    and the final state ("The State That Must Remember Everything", Part 4:
+    two orderings of one semiseparable matrix).
+  - At A = 0 and delta = 1 the layer is plain causal linear attention,
+    y_t = sum_{s<=t} (C_t . B_s) x_s, computed here by explicit loops.
+  - The decay mask is 1-semiseparable: every block of it below the diagonal
+    has rank one.
+"""
+import numpy as np
+import pytest
+
+from oracle import ref as R
+from oracle import ssd as S
+from selective_state_space_33_amd import inputs as I
+
+
+def _case(seed, batch, L, H, P, N, gate=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, L, H, P))
+    z = rng.standard_normal((batch, L, H, P)) if gate else None
+    dl = rng.standard_normal((batch, L, H))
+    A = -rng.uniform(0.2, 3.0, H)
+    B = rng.standard_normal((batch, L, N))
+    C = rng.standard_normal((batch, L, N))
+    D = rng.uniform(0.5, 1.5, H)
+    bias = np.log(np.expm1(rng.uniform(1e-3, 0.2, H)))
+    return x, dl, A, B, C, D, z, bias
+
+
+def _broadcast_scan(x, dl, A, B, C, D, z, bias, softplus=True):
+    """The same layer as a selective scan over H*P channels."""
+    batch, L, H, P = x.shape
+    N = B.shape[2]
+    rep = lambda a: np.repeat(a, P, axis=-1)
+    return R.scan_fwd(x.reshape(batch, L, H * P), rep(dl), np.repeat(A, P)[:, None] * np.ones((1, N)), B, C,
+                      D=None if D is None else rep(D), z=None if z is None else z.reshape(batch, L, H * P),
+                      delta_bias=None if bias is None else rep(bias), softplus=softplus)
+
+
+@pytest.mark.parametrize("gate,softplus", [(True, True), (False, True), (True, False)])
+def test_masked_form_equals_the_recurrent_scan(gate, softplus):
+    x, dl, A, B, C, D, z, bias = _case(1, 2, 37, 3, 5, 6, gate)
+    if not softplus:
+        dl, bias = np.abs(dl) * 0.3 + 0.01, np.abs(bias) * 0.01
+    y, fs = S.ssd_fwd(x, dl, A, B, C, D=D, z=z, delta_bias=bias, softplus=softplus)
+    yr, fr = _broadcast_scan(x, dl, A, B, C, D, z, bias, softplus)
+    batch, L, H, P = x.shape
+    np.testing.assert_allclose(y.reshape(batch, L, H * P), yr, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(fs.reshape(batch, H * P, -1), fr, rtol=1e-10, atol=1e-12)
+
+
+def test_no_decay_unit_step_is_causal_linear_attention():
+    rng = np.random.default_rng(2)
+    batch, L, H, P, N = 1, 9, 2, 3, 4
+    x = rng.standard_normal((batch, L, H, P))
+    B = rng.standard_normal((batch, L, N))
+    C = rng.standard_normal((batch, L, N))
+    y, fs = S.ssd_fwd(x, np.ones((batch, L, H)), np.zeros(H), B, C, softplus=False)
+    for h in range(H):
+        for t in range(L):
+            ref = sum((C[0, t] @ B[0, s]) * x[0, s, h] for s in range(t + 1))
+            np.testing.assert_allclose(y[0, t, h], ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(fs[0, h], sum(np.outer(x[0, s, h], B[0, s]) for s in range(L)), rtol=1e-12)
+
+
+def test_decay_mask_is_one_semiseparable():
+    """Below the diagonal exp(A (cs_t - cs_s)) factors as exp(A cs_t) exp(-A cs_s): rank one."""
+    x, dl, A, B, C, D, z, bias = _case(3, 1, 30, 1, 1, 1, False)
+    # with x = e_s, B = C = 1 and no skip, column s of the output is the mask column times delta_s
+    L = 30
+    M = np.empty((L, L))
+    for s in range(L):
+        xs = np.zeros((1, L, 1, 1))
+        xs[0, s] = 1.0
+        y, _ = S.ssd_fwd(xs, dl, A, np.ones((1, L, 1)), np.ones((1, L, 1)), delta_bias=bias)
+        M[:, s] = y[0, :, 0, 0]
+    assert np.all(M[np.triu_indices(L, 1)] == 0.0)
+    block = M[15:, :15]                                  # strictly below the diagonal
+    sv = np.linalg.svd(block, compute_uv=False)
+    assert sv[1] < 1e-12 * sv[0]
+
+
+def test_workload_inputs_match_the_scan():
+    """On the seeded SSD inputs of the parity tests as well."""
+    x = I.random_ssd_inputs(np.random.default_rng(4), 2, 70, 3, 8, 16, dtype="f32")
+    y, fs = S.ssd_fwd(x["x"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"], delta_bias=x["delta_bias"])
+    yr, fr = _broadcast_scan(x["x"].astype(np.float64), x["delta"].astype(np.float64), x["A"].astype(np.float64),
+                             x["B"].astype(np.float64), x["C"].astype(np.float64), x["D"].astype(np.float64),
+                             x["z"].astype(np.float64), x["delta_bias"].astype(np.float64))
+    np.testing.assert_allclose(y.reshape(yr.shape), yr, rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(fs.reshape(fr.shape), fr, rtol=1e-9, atol=1e-11)
+
+
+SSD_MUTANTS = {
+    "decay_includes_own_step": ("A[h] * (cs[:, None] - cs[None, :])",
+                                "A[h] * (cs[:, None] - cs[None, :] + dl[b, None, :, h])"),
+    "step_weight_dropped": ("M = G * decay * dl[b, None, :, h]", "M = G * decay"),
+    "B_and_C_swapped": ("G = C[b] @ B[b].T", "G = B[b] @ C[b].T"),
+    "mask_not_causal": ("np.where(causal, A[h] * (cs[:, None] - cs[None, :]), -np.inf)",
+                        "A[h] * np.abs(cs[:, None] - cs[None, :])"),
+    "skip_dropped": ("y[b, :, h] += D[h] * x[b, :, h]", "y[b, :, h] += 0.0"),
+    "final_state_without_decay": ("w = np.exp(A[h] * (cs[-1] - cs)) * dl[b, :, h]", "w = dl[b, :, h]"),
+    "gate_is_sigmoid": ("y = y * (z / (1.0 + np.exp(-z)))", "y = y * (1.0 / (1.0 + np.exp(-z)))"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SSD_MUTANTS))
+def test_ssd_mutant_is_caught(name, monkeypatch):
+    import types
+
+    old, new = SSD_MUTANTS[name]
+    src = open(S.__file__).read()
+    assert src.count(old) == 1, name
+    mod = types.ModuleType("ssd_mutant")
+    exec(compile(src.replace(old, new), "ssd_mutant", "exec"), mod.__dict__)
+    monkeypatch.setattr(S, "ssd_fwd", mod.ssd_fwd)
+    pins = [lambda: test_masked_form_equals_the_recurrent_scan(True, True),
+            test_no_decay_unit_step_is_causal_linear_attention, test_decay_mask_is_one_semiseparable]
+    caught = 0
+    for pin in pins:
+        try:
+            pin()
+        except AssertionError:
+            caught += 1
+    assert caught, f"no pin caught {name}"
