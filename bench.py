@@ -11,7 +11,8 @@ the backward pass (ssm_scan_bwd) of the same layer under "backward", and the
 same layer's tokens as one packed row of variable-length sequences, each from
 its own initial state (ssm_scan_fwd_ex), under "packed", and the same layer
 with the Mamba-3 trapezoidal three-term recurrence (ssm_scan_trap_fwd) under
-"trapezoid".
+"trapezoid".  The Mamba-2 SSD layer (ssm_ssd_fwd, MFMA) on a 2.7B-shaped layer
+(batch 4, L 4096, 80 heads of 64 channels, state 128, bf16) is under "ssd".
 
 Prints ONE JSON line.  Fields beyond the common ones:
   roofline      the dominant kernel against its binding roofline (VALU issue:
@@ -33,6 +34,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 # fp32 VALU issue peak without packed-fp32 instructions (this build disables them): 256 CUs x 4 SIMDs x 16 lanes
 # per clock x 2.4 GHz = 39.3e12 lane-ops/s, i.e. 78.6 TFLOP/s counting an FMA as 2 flops.  (The 157.3 TFLOP/s
 # datasheet figure needs v_pk_fma_f32, two fp32 FMAs per lane per instruction.)
@@ -178,6 +180,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-packed", action="store_true")
     ap.add_argument("--no-trapezoid", action="store_true")
+    ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--packed-mean-len", type=float, default=1024.0,
                     help="mean sequence length of the packed row (log-normal lengths, sigma 1)")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -348,6 +351,45 @@ def main():
                                          "counted": f"{SLOTS_PER_UPDATE} slots per state update, "
                                                     f"{TRAP_SLOTS_PER_TOKEN_CHANNEL} per (token, channel)"}}
         del wst
+
+    if not args.no_ssd:
+        import numpy as np
+
+        cfg = I.SSD_WORKLOADS["mamba2_2p7b_bf16"]
+        sb, sL, sH, sP, sN = cfg["batch"], cfg["L"], cfg["heads"], cfg["headdim"], cfg["dstate"]
+        xs = I.random_ssd_inputs(np.random.default_rng(0), sb, sL, sH, sP, sN)
+        to = lambda a, f32=False: None if a is None else (
+            torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev) if f32 else
+            torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev).to(torch.bfloat16))
+        gs = dict(x=to(xs["x"]), delta=to(xs["delta"]), B=to(xs["B"]), C=to(xs["C"]), z=to(xs["z"]),
+                  A=to(xs["A"], True), D=to(xs["D"], True), bias=to(xs["delta_bias"], True))
+        del xs
+        ys = torch.empty_like(gs["x"])
+        fss = torch.empty((sb, sH, sP, sN), dtype=torch.float32, device=dev)
+
+        def sstep():
+            ops.ssm_ssd_fwd(gs["x"], gs["delta"], gs["A"], gs["B"], gs["C"], D=gs["D"], z=gs["z"],
+                            delta_bias=gs["bias"], y=ys, final_state=fss, stream=stream)
+
+        sms, _ = time_calls(sstep, max(args.steps // 2, 5), max(args.warmup // 10, 5), stream)
+        supd = sb * sL * sH * sP * sN
+        # algorithmic bytes: x, z, y, B, C, delta once each (bf16), A, D, bias, the final state (fp32)
+        sbytes = sb * sL * sH * sP * 2 * 3 + sb * sL * sN * 2 * 2 + sb * sL * sH * 2 + sb * sH * sP * sN * 4 + sH * 12
+        # algorithmic matrix flops of the chunked form (64-token chunks): per (row, chunk) C B^T (2 Q^2 N, shared
+        # by the heads); per (row, chunk, head) the intra-chunk product (2 Q^2 P), the inter-chunk readout and the
+        # state update (2 Q N P each)
+        Q = 64
+        nch = (sL + Q - 1) // Q
+        sflops = sb * nch * (2 * Q * Q * sN + sH * (2 * Q * Q * sP + 4 * Q * sN * sP))
+        sgbs = sbytes / (sms * 1e-3) / 1e9
+        stf = sflops / (sms * 1e-3) / 1e12
+        out["ssd"] = {"workload": "mamba2_2p7b_bf16 (batch 4, L 4096, 80 heads x 64, state 128)", "op": "ssm_ssd_fwd",
+                      "ms_per_step": sms, "value": supd / (sms * 1e-3), "unit": "updates/s",
+                      "roofline": {"bound": "hbm", "achieved": sgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                   "frac": sgbs / HBM_PEAK_GBS, "algorithmic_bytes": sbytes},
+                      "mfma": {"achieved": stf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": stf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": sflops}}
+        del gs, ys, fss
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)

@@ -157,6 +157,32 @@ ssm_status_t ssm_scan_trap_fwd(const void* u, const void* delta, const float* A,
                                int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The Mamba-2 state-space-duality (SSD) layer ("State Space Models and the
+ * Post-Transformer Era", "Mamba-2 and Structured State Space Duality"; "The
+ * State That Must Remember Everything", Part 4): every head has one scalar
+ * state matrix A (times the identity), which makes the sequence map a causal
+ * 1-semiseparable matrix computed blockwise with matrix products.  Per batch
+ * row and head (headdim channels sharing the step and A; B_t, C_t shared by
+ * all heads) the state H (headdim x dstate) runs
+ *     H_t = exp(delta_t A) H_{t-1} + delta_t x_t B_t^T,   H_{-1} = 0,
+ *     y_t = (H_t C_t + D x_t) * SiLU(z_t)   (skip and gate optional),
+ * with delta_t = softplus(delta_raw + bias) (or raw + bias when
+ * softplus_flag = 0).  This equals ssm_scan_fwd with dim = heads * headdim,
+ * A[d][n] = A[head of d] and the head's step on each of its channels.
+ *   x, z, y: [batch, L, heads, headdim]; delta: [batch, L, heads]; B, C:
+ *   [batch, L, dstate] (all bf16); A, D, delta_bias: [heads] fp32;
+ *   final_state (nullable): [batch, heads, headdim, dstate] fp32.
+ *   Required: x, delta, A, B, C, y; optional: D, z, delta_bias, final_state.
+ *   x, B, C must be 16-byte aligned, delta, z, y 2-byte, the fp32 arrays
+ *   4-byte (else INVALID_ARG).  Supported: dt = BF16, headdim = 64 and
+ *   dstate = 32, 64 or 128, with (L + 64) * heads * headdim * 2 bytes below
+ *   2^31 (else UNSUPPORTED).  Arithmetic: bf16 matrix products with fp32
+ *   accumulation, fp32 state.  No workspace; y must not alias an input. */
+ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
+                         const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                         void* y, float* final_state, int64_t batch, int64_t L, int64_t heads, int64_t headdim,
+                         int64_t dstate, ssm_dtype_t dt, hipStream_t stream);
+
 /* One recurrent (decode) step: the same arithmetic as one token of the scan,
  * reading `state` as h_{t-1} and overwriting it in place with h_t
  * ("Mamba: The State Space Models Challenging the Transformer", "What a

@@ -22,7 +22,7 @@ SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 
 # Every symbol include/ssm_scan.h declares.
 EXPORTED = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_ex_workspace_size", "ssm_scan_fwd_ex",
-            "ssm_scan_trap_fwd_workspace_size", "ssm_scan_trap_fwd", "ssm_state_update",
+            "ssm_scan_trap_fwd_workspace_size", "ssm_scan_trap_fwd", "ssm_ssd_fwd", "ssm_state_update",
             "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_status_string")
 
 _lib = None
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_trap_fwd_workspace_size.argtypes = L.ssm_scan_fwd_ex_workspace_size.argtypes
         L.ssm_scan_trap_fwd.restype = ctypes.c_int
         L.ssm_scan_trap_fwd.argtypes = L.ssm_scan_fwd_ex.argtypes
+        L.ssm_ssd_fwd.restype = ctypes.c_int
+        L.ssm_ssd_fwd.argtypes = [_vp] * 8 + [ctypes.c_int, _vp, _vp] + [_i64] * 5 + [ctypes.c_int, _vp]
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_scan_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
         L.ssm_scan_bwd.restype = ctypes.c_int
@@ -207,6 +209,36 @@ def _fwd_rows(entry, u, delta, A, B, C, D, z, delta_bias, softplus, initial_stat
                                _stream(dev, stream))
     if rc != SSM_OK:
         raise SSMError(rc, entry)
+    return y, final_state
+
+
+def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, y=None,
+                final_state=None, return_final_state: bool = True, stream=None):
+    """The Mamba-2 SSD layer on the GPU.
+
+    x, z: [batch, L, heads, headdim]; delta: [batch, L, heads]; B, C: [batch, L, dstate] (bfloat16);
+    A, D, delta_bias: [heads] (float32).  Returns (y, final_state [batch, heads, headdim, dstate] or None)."""
+    batch, L, heads, headdim = x.shape
+    dstate = B.shape[2]
+    dev, dt = x.device, x.dtype
+    code = _dtype_code(dt)
+    for name, t, shp in (("x", x, (batch, L, heads, headdim)), ("z", z, (batch, L, heads, headdim)),
+                         ("delta", delta, (batch, L, heads)), ("B", B, (batch, L, dstate)),
+                         ("C", C, (batch, L, dstate))):
+        _check(t, name, dt, shp, dev)
+    for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias)):
+        _check(t, name, torch.float32, (heads,), dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _check(y, "y", dt, (batch, L, heads, headdim), dev)
+    if final_state is None and return_final_state:
+        final_state = torch.empty((batch, heads, headdim, dstate), dtype=torch.float32, device=dev)
+    _check(final_state, "final_state", torch.float32, (batch, heads, headdim, dstate), dev)
+    rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                           1 if softplus else 0, _ptr(y), _ptr(final_state), batch, L, heads, headdim, dstate, code,
+                           _stream(dev, stream))
+    if rc != SSM_OK:
+        raise SSMError(rc, "ssm_ssd_fwd")
     return y, final_state
 
 

@@ -1,0 +1,118 @@
+"""GPU parity of ssm_ssd_fwd (the Mamba-2 SSD layer on MFMA) against the oracle.
+
+Compared element by element with oracle/ssd.py (the masked-matrix form,
+pinned in test_oracle_ssd.py to the recurrent oracle) on the same seeded bf16
+inputs.  Tolerance 2e-2 (bf16 storage), with the forward's error measure,
+for y and the final state: the kernel multiplies bf16 operands (C B^T masked
+and decayed, x, the state and the weighted B each rounded to bf16) with fp32
+accumulation, which keeps the error near the bf16 rounding of y (~4e-3).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import ssd as S
+from selective_state_space_33_amd import inputs as I
+from selective_state_space_33_amd import ops
+
+from .gpu_util import TOL, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _dev(a, f32=False):
+    if a is None:
+        return None
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+    return t if f32 else t.to(torch.bfloat16)
+
+
+def _run(x, softplus=True):
+    y, fs = ops.ssm_ssd_fwd(_dev(x["x"]), _dev(x["delta"]), _dev(x["A"], True), _dev(x["B"]), _dev(x["C"]),
+                            D=_dev(x["D"], True), z=_dev(x["z"]), delta_bias=_dev(x["delta_bias"], True),
+                            softplus=softplus)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy().astype(np.float64), fs.cpu().numpy().astype(np.float64)
+
+
+def _check(x, label, softplus=True, tol=TOL["bf16"]):
+    say(f"ssd {label} x={x['x'].shape} N={x['B'].shape[2]}")
+    yg, fg = _run(x, softplus)
+    yo, fo = S.ssd_fwd(x["x"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                       softplus=softplus)
+    ey, ef = rel_err(yg, yo), rel_err(fg, fo)
+    print(f"[parity] ssd {label}: y {ey:.2e}  final {ef:.2e}", flush=True)
+    assert ey <= tol and ef <= tol, (ey, ef)
+
+
+@pytest.mark.parametrize("N", [32, 64, 128])
+@pytest.mark.parametrize("L", [64, 300, 1000])
+def test_ssd_matches_oracle(N, L):
+    x = I.random_ssd_inputs(np.random.default_rng(700 + N + L), 2, L, 3, 64, N)
+    _check(x, f"L={L} N={N}")
+
+
+@pytest.mark.parametrize("L", [1, 17, 63, 65, 129])
+def test_ssd_short_and_ragged(L):
+    x = I.random_ssd_inputs(np.random.default_rng(720 + L), 3, L, 2, 64, 64)
+    _check(x, f"L={L}")
+
+
+@pytest.mark.parametrize("opts", ["no_gate", "no_skip", "no_bias", "no_softplus"])
+def test_ssd_optional_inputs(opts):
+    rng = np.random.default_rng(730 + len(opts))
+    x = I.random_ssd_inputs(rng, 2, 200, 2, 64, 64, gate=opts != "no_gate")
+    softplus = True
+    if opts == "no_skip":
+        x["D"] = None
+    elif opts == "no_bias":
+        x["delta_bias"] = None
+    elif opts == "no_softplus":
+        softplus = False
+        x["delta"] = I.round_to_bf16(np.abs(x["delta"]) * 0.1 + 0.01)  # the step itself: keep it positive
+        x["delta_bias"] = np.abs(x["delta_bias"]) * 0.01
+    _check(x, opts, softplus=softplus)
+
+
+def test_ssd_slow_decay_long_memory():
+    """A near zero: states carry across many chunks (the inter-chunk path dominates)."""
+    rng = np.random.default_rng(740)
+    x = I.random_ssd_inputs(rng, 1, 700, 2, 64, 64)
+    x["A"] = -rng.uniform(0.001, 0.01, 2).astype(np.float32)
+    _check(x, "slow decay")
+
+
+def test_ssd_many_heads_and_batch_rows():
+    x = I.random_ssd_inputs(np.random.default_rng(750), 3, 130, 11, 64, 32)
+    _check(x, "batch 3, 11 heads")
+
+
+def test_ssd_full_size_sampled_heads():
+    """The 2.7B-shaped layer (batch 4, L 4096, 80 heads of 64, state 128) as bench.py times it; oracle on 6
+    sampled (batch row, head) pairs."""
+    cfg = I.SSD_WORKLOADS["mamba2_2p7b_bf16"]
+    x = I.random_ssd_inputs(np.random.default_rng(0), cfg["batch"], cfg["L"], cfg["heads"], cfg["headdim"],
+                            cfg["dstate"])
+    say("ssd full-size 2.7B layer")
+    yg, fg = _run(x)
+    assert np.all(np.isfinite(yg))
+    ey = ef = 0.0
+    for b, h in [(0, 0), (0, 79), (1, 17), (2, 40), (3, 63), (3, 79)]:
+        sub = {k: None if v is None else v for k, v in x.items()}
+        sub = dict(x=x["x"][b:b + 1, :, h:h + 1], z=x["z"][b:b + 1, :, h:h + 1], delta=x["delta"][b:b + 1, :, h:h + 1],
+                   B=x["B"][b:b + 1], C=x["C"][b:b + 1], A=x["A"][h:h + 1], D=x["D"][h:h + 1],
+                   delta_bias=x["delta_bias"][h:h + 1])
+        yo, fo = S.ssd_fwd(sub["x"], sub["delta"], sub["A"], sub["B"], sub["C"], D=sub["D"], z=sub["z"],
+                           delta_bias=sub["delta_bias"])
+        ey = max(ey, rel_err(yg[b:b + 1, :, h:h + 1], yo))
+        ef = max(ef, rel_err(fg[b:b + 1, h:h + 1], fo))
+    print(f"[parity] ssd 2.7B sampled heads: y {ey:.2e}  final {ef:.2e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (ey, ef)
+
+
+def test_ssd_deterministic():
+    x = I.random_ssd_inputs(np.random.default_rng(760), 2, 300, 4, 64, 128)
+    say("ssd determinism")
+    y1, f1 = _run(x)
+    y2, f2 = _run(x)
+    assert np.array_equal(y1, y2) and np.array_equal(f1, f2)
