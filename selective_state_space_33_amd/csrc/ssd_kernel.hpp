@@ -6,34 +6,35 @@
 // Models and the Post-Transformer Era", "Mamba-2 and Structured State Space
 // Duality"; "The State That Must Remember Everything", Part 4).  Per batch row
 // and head (headdim P = 64 channels sharing delta_t and A, with B_t, C_t of
-// dstate N shared by all heads) the state H (P x N) runs
-//     H_t = exp(delta_t A) H_{t-1} + delta_t x_t B_t^T,   y_t = H_t C_t + D x_t,
+// dstate N shared by all heads) the state H (N x P) runs
+//     H_t = exp(delta_t A) H_{t-1} + delta_t B_t x_t^T,   y_t = H_t^T C_t + D x_t,
 // then y is gated by SiLU(z).  Over a chunk of Q tokens with
 // cs_t = A (delta_0 + ... + delta_t) (chunk-local, inclusive) this is
-//     y_t   = exp(cs_t) C_t . H_prev                                  (inter)
+//     y_t   = exp(cs_t) H_prev^T C_t                                  (inter)
 //           + sum_{s<=t} (C_t . B_s) exp(cs_t - cs_s) delta_s x_s        (intra)
-//     H_end = exp(cs_end) H_prev + sum_s exp(cs_end - cs_s) delta_s x_s B_s^T.
+//     H_end = exp(cs_end) H_prev + sum_s exp(cs_end - cs_s) delta_s B_s x_s^T.
 //
-// One workgroup (4 wavefronts) per (batch row, head) walks the chunks in
-// order; the head's state stays in MFMA accumulators (fp32) the whole time,
-// so no chunk states go to HBM and x, z, y, B, C are each read or written
-// once.  Per chunk, with bf16 operands and fp32 accumulation
-// (v_mfma_f32_16x16x32_bf16; wavefront w owns rows 16w..16w+15 of each product):
-//   G   = C B^T                  (Q x Q, K = N)  -> M = G * exp(cs_t - cs_s) * delta_s on s <= t, to LDS
-//   Y   = exp(cs_t) (C H^T^T)    (Q x P, K = N)  +  M x   (K = Q)   -> epilogue D x, SiLU(z), y
-//   H^T = exp(cs_end) H^T + x^T W  (P x N, K = Q), W[s][n] = exp(cs_end - cs_s) delta_s B[s][n]
-// Operands sit in LDS in the orientation whose K index is contiguous, so
-// every fragment is one 16-byte read: C and B row-major, x, W and H
-// transposed.  W takes the LDS of B once G is done.
+// One workgroup (8 wavefronts) per (batch row, head) walks the chunks in
+// order; the head's state stays in MFMA accumulators (fp32), so no chunk
+// state goes to HBM and x, z, y, B, C are each read or written once.  Per
+// chunk (v_mfma_f32_16x16x32_bf16, bf16 operands, fp32 accumulation):
+//   G^T = B C^T              (Q x Q, K = N) -> M[t][s] = G[t][s] exp(cs_t - cs_s) delta_s on s <= t
+//   Y   = exp(cs_t) C H + M x  (Q x P; K = N, then K = Q)  -> + D x, times SiLU(z), y
+//   H   = exp(cs_end) H + W^T x   (N x P, K = Q),  W[s][n] = exp(cs_end - cs_s) delta_s B[s][n]
+// Every operand sits in LDS with its K index contiguous, so a fragment is one
+// 16-byte read: C and B by token row, M by output row, x, W and H transposed
+// (x^T [p][s], W^T [n][s], H^T [p][n]).  The orientations are chosen so that
+// every write is an 8-byte run: the accumulators of G^T and H hold four
+// consecutive K-side indices per lane, and B and x are loaded four token rows
+// at a time so that their transposes are written four tokens per store.
 //
 // Precision.  C, B and x arrive as bf16 and are exact operands.  M, W and the
-// state are fp32 values; rounded to bf16 once, the sums they enter lose
-// about 2^-9 of their largest terms, which measured against the fp64 oracle
-// puts y near 2e-2 of its scale.  Each of the three is therefore carried as a
-// pair hi + lo of bf16 (hi = bf16(v), lo = bf16(v - hi), 16 significant bits)
-// and enters its product as two MFMAs, which brings y to the rounding of its
-// own bf16 store (~4e-3) and the state to ~2e-5.  The pairs take the
-// workgroup to 115 KB of LDS, one per CU.
+// state are fp32 values; rounded to bf16 once, the sums they enter lose about
+// 2^-9 of their largest terms, which against the fp64 oracle puts y near 2e-2
+// of its scale.  Each of the three is therefore carried as a pair hi + lo of
+// bf16 (hi = bf16(v), lo = bf16(v - hi)) and enters its product as two
+// MFMAs, which keeps y at the rounding of its own bf16 store (~4e-3) and the
+// state near 2e-5.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -58,8 +59,9 @@ struct SsdParams {
   int softplus;
 };
 
-constexpr int kSsdQ = 64;  // tokens per chunk
-constexpr int kSsdP = 64;  // channels per head
+constexpr int kSsdQ = 64;         // tokens per chunk
+constexpr int kSsdP = 64;         // channels per head
+constexpr int kSsdThreads = 512;  // 8 wavefronts
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -68,28 +70,47 @@ __device__ __forceinline__ unsigned short bf16_bits_of(float f) {
   return __builtin_bit_cast(unsigned short, static_cast<__bf16>(f));
 }
 __device__ __forceinline__ float bf16_value(unsigned short b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+__device__ __forceinline__ float bf16_lo_of(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi_of(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+
+// hi and lo bf16 of four fp32 values, packed as two 8-byte runs.
+__device__ __forceinline__ void split4(const float* v, u32x2_t& hi, u32x2_t& lo) {
+  unsigned short hb[4], lb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    hb[j] = bf16_bits_of(v[j]);
+    lb[j] = bf16_bits_of(v[j] - bf16_value(hb[j]));
+  }
+  hi = u32x2_t{hb[0] | (static_cast<uint32_t>(hb[1]) << 16), hb[2] | (static_cast<uint32_t>(hb[3]) << 16)};
+  lo = u32x2_t{lb[0] | (static_cast<uint32_t>(lb[1]) << 16), lb[2] | (static_cast<uint32_t>(lb[3]) << 16)};
+}
 
 template <int N>
-__global__ void __launch_bounds__(256) ssd_kernel(SsdParams p) {
-  constexpr int Q = kSsdQ, P = kSsdP;
-  static_assert(N % 32 == 0 && N <= 128, "dstate: a multiple of 32 up to 128");
+__global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
+  constexpr int Q = kSsdQ, P = kSsdP, NTH = kSsdThreads;
+  static_assert(N == 32 || N == 64 || N == 128, "dstate: 32, 64 or 128");
   constexpr int SN = N + 8;  // padded rows (elements) of the [.][N] arrays: 16-byte aligned, banks staggered
   constexpr int SQ = Q + 8;  // padded rows of the [.][Q] arrays
-  constexpr int BW = (Q * SN > N * SQ) ? Q * SN : N * SQ;
-  constexpr int NT = N / 16;               // 16-wide state tiles
-  constexpr int BC_PASSES = N / 32;        // 16-byte pieces of a chunk's B (or C) rows per thread
+  constexpr int NT = N / 16;  // 16-wide state tiles
+  constexpr int HT = NT / 2;  // state tiles per wavefront (NT x 4 tiles over 8 wavefronts)
+  constexpr int C_PIECES = Q * N / 8;         // 16-byte pieces of a chunk's C
+  constexpr int C_PER = (C_PIECES + NTH - 1) / NTH;
+  constexpr int B_ITEMS = (Q / 4) * (N / 2);  // (4 tokens) x (2 states) items of a chunk's B
+  constexpr int B_PER = (B_ITEMS + NTH - 1) / NTH;
+  static_assert((Q / 4) * (P / 2) == NTH, "one x item per thread");
   constexpr float kLog2eF = 1.4426950408889634f;
 
-  __shared__ __attribute__((aligned(16))) unsigned short sC[Q * SN];   // C rows [t][n]
-  __shared__ __attribute__((aligned(16))) unsigned short sB[BW];       // B rows [s][n], then W (hi) [n][s]
-  __shared__ __attribute__((aligned(16))) unsigned short sWl[N * SQ];  // W (lo) [n][s]
-  __shared__ __attribute__((aligned(16))) unsigned short sXT[P * SQ];  // x transposed [p][s]
-  __shared__ __attribute__((aligned(16))) unsigned short sM[Q * SQ];   // masked, decayed C B^T (hi) [t][s]
-  __shared__ __attribute__((aligned(16))) unsigned short sMl[Q * SQ];  // (lo)
-  __shared__ __attribute__((aligned(16))) unsigned short sHT[P * SN];  // H^T (hi) [p][n]
-  __shared__ __attribute__((aligned(16))) unsigned short sHl[P * SN];  // (lo)
-  __shared__ __attribute__((aligned(16))) float sCS[Q];             // A * (cumulative step) within the chunk
-  __shared__ float sDL[Q];                                             // the step delta_t
+  __shared__ __attribute__((aligned(16))) unsigned short sC[Q * SN];   // C [t][n]
+  __shared__ __attribute__((aligned(16))) unsigned short sB[Q * SN];   // B [s][n]
+  __shared__ __attribute__((aligned(16))) unsigned short sWh[N * SQ];  // W^T [n][s], hi
+  __shared__ __attribute__((aligned(16))) unsigned short sWl[N * SQ];  // lo
+  __shared__ __attribute__((aligned(16))) unsigned short sXT[P * SQ];  // x^T [p][s]
+  __shared__ __attribute__((aligned(16))) unsigned short sMh[Q * SQ];  // M [t][s], hi
+  __shared__ __attribute__((aligned(16))) unsigned short sMl[Q * SQ];  // lo
+  __shared__ __attribute__((aligned(16))) unsigned short sHh[P * SN];  // H^T [p][n], hi
+  __shared__ __attribute__((aligned(16))) unsigned short sHl[P * SN];  // lo
+  __shared__ __attribute__((aligned(16))) float sCS[Q];                // A * (cumulative step) within the chunk
+  __shared__ __attribute__((aligned(16))) float sDL[Q];                // the step delta_t
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -112,56 +133,92 @@ __global__ void __launch_bounds__(256) ssd_kernel(SsdParams p) {
   const rsrc_t rs_c = make_rsrc(static_cast<const unsigned short*>(p.C) + b * L * N, L * N * 2);
   const rsrc_t rs_d = make_rsrc(static_cast<const unsigned short*>(p.delta) + b * L * H + h, (L * H - h) * 2);
 
-  // Loads of one chunk: x (2 pieces of 8 channels of a token row per
-  // thread), B and C (BC_PASSES pieces of 8 states), the raw step (one token per thread of wavefront 0).
-  u32x4_t gx[2], gb[BC_PASSES], gc[BC_PASSES];
+  // Work of this wavefront.  Y tiles: token block ty, channel blocks py0, py0+1.
+  const int ty = w & 3, py0 = 2 * (w >> 2);
+  // State tiles: channel block ph, state blocks nb0 + 2i.
+  const int ph = w & 3, nb0 = w >> 2;
+
+  // Chunk loads (registers): C in 16-byte pieces; B and x four token rows at a
+  // time (4-byte pieces: two states / two channels); the raw step; z for this
+  // wavefront's Y tiles.
+  u32x4_t gc[C_PER];
+  uint32_t gb[B_PER][4], gx[4];
   float graw = 0.0f;
-  const int xr = tid >> 3, xc = (tid & 7) * 8;                  // x piece: row xr (+32), channels xc..xc+7
-  constexpr int BC_TPR = N / 8;                                  // threads per B/C row
-  const int bcr = tid / BC_TPR, bcc = (tid % BC_TPR) * 8;        // B/C piece: row bcr (+256/BC_TPR), states bcc..
-  constexpr int BC_RSTEP = 256 / BC_TPR;
-  auto load_xc = [&](int64_t t0) {
+  unsigned short gz[2][4];
+  auto load_c = [&](int64_t t0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      gx[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rs_x, static_cast<int>(((t0 + xr + 32 * i) * rowe + xc) * 2), 0, 0));
+    for (int i = 0; i < C_PER; ++i) {
+      const int e = tid + NTH * i;
+      const int row = e / (N / 8), col = (e % (N / 8)) * 8;
+      if (e < C_PIECES)
+        gc[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rs_c, static_cast<int>(((t0 + row) * N + col) * 2), 0, 0));
+    }
+  };
+  auto load_b = [&](int64_t t0) {
 #pragma unroll
-    for (int i = 0; i < BC_PASSES; ++i)
-      gc[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rs_c, static_cast<int>(((t0 + bcr + BC_RSTEP * i) * N + bcc) * 2), 0, 0));
+    for (int i = 0; i < B_PER; ++i) {
+      const int e = tid + NTH * i;
+      const int np = e % (N / 2), s0 = 4 * (e / (N / 2));
+      if (e < B_ITEMS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          gb[i][r] = __builtin_amdgcn_raw_buffer_load_b32(rs_b, static_cast<int>(((t0 + s0 + r) * N + 2 * np) * 2), 0, 0);
+      }
+    }
+  };
+  const int xpp = tid % (P / 2), xs0 = 4 * (tid / (P / 2));  // x item: channels 2xpp, 2xpp+1 of tokens xs0..xs0+3
+  auto load_x = [&](int64_t t0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      gx[r] = __builtin_amdgcn_raw_buffer_load_b32(rs_x, static_cast<int>(((t0 + xs0 + r) * rowe + 2 * xpp) * 2), 0, 0);
     if (w == 0)
       graw = bf16_value(static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(
           rs_d, static_cast<int>((t0 + lane) * H * 2), 0, 0)));
   };
-  auto load_b = [&](int64_t t0) {
+  auto load_z = [&](int64_t t0) {
+    if (!p.z) return;
 #pragma unroll
-    for (int i = 0; i < BC_PASSES; ++i)
-      gb[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                              rs_b, static_cast<int>(((t0 + bcr + BC_RSTEP * i) * N + bcc) * 2), 0, 0));
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        gz[c][j] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(
+            rs_z, static_cast<int>(((t0 + 16 * ty + 4 * lq + j) * rowe + 16 * (py0 + c) + lr) * 2), 0, 0));
   };
 
-  // The state H^T [P x N]: wavefront w owns rows 16w..16w+15, NT tiles of 16 states.
-  f32x4_t hacc[NT];
+  f32x4_t hacc[HT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) hacc[nt] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int e = tid; e < P * SN; e += 256) sHT[e] = sHl[e] = 0;
+  for (int i = 0; i < HT; ++i) hacc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int e = tid; e < P * SN; e += NTH) sHh[e] = sHl[e] = 0;
 
   const int64_t nchunks = (L + Q - 1) / Q;
-  load_xc(0);
+  load_c(0);
   load_b(0);
+  load_x(0);
   for (int64_t k = 0; k < nchunks; ++k) {
     const int64_t t0 = k * Q;
-    // ---- stage the chunk: C, B rows; x transposed; steps and their cumulative sums
+    load_z(t0);
+    // ---- stage: C and B by token row, x transposed, the steps and their cumulative sums
 #pragma unroll
-    for (int i = 0; i < BC_PASSES; ++i) {
-      *reinterpret_cast<u32x4_t*>(&sC[(bcr + BC_RSTEP * i) * SN + bcc]) = gc[i];
-      *reinterpret_cast<u32x4_t*>(&sB[(bcr + BC_RSTEP * i) * SN + bcc]) = gb[i];
+    for (int i = 0; i < C_PER; ++i) {
+      const int e = tid + NTH * i;
+      if (e < C_PIECES) *reinterpret_cast<u32x4_t*>(&sC[(e / (N / 8)) * SN + (e % (N / 8)) * 8]) = gc[i];
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < B_PER; ++i) {
+      const int e = tid + NTH * i;
+      if (e < B_ITEMS) {
+        const int np = e % (N / 2), s0 = 4 * (e / (N / 2));
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sXT[(xc + e) * SQ + xr + 32 * i] = static_cast<unsigned short>(gx[i][e / 2] >> (16 * (e % 2)));
+        for (int r = 0; r < 4; ++r) *reinterpret_cast<uint32_t*>(&sB[(s0 + r) * SN + 2 * np]) = gb[i][r];
+      }
+    }
+    {
+      // x^T: channel 2xpp takes the low halves of the four rows, 2xpp+1 the high halves
+      const u32x2_t even = {(gx[0] & 0xffffu) | (gx[1] << 16), (gx[2] & 0xffffu) | (gx[3] << 16)};
+      const u32x2_t odd = {(gx[0] >> 16) | (gx[1] & 0xffff0000u), (gx[2] >> 16) | (gx[3] & 0xffff0000u)};
+      *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp) * SQ + xs0]) = even;
+      *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp + 1) * SQ + xs0]) = odd;
     }
     if (w == 0) {
       const float xv = graw + biash;
@@ -177,144 +234,175 @@ __global__ void __launch_bounds__(256) ssd_kernel(SsdParams p) {
       sCS[lane] = cs;
     }
     __syncthreads();
-    if (k + 1 < nchunks) load_xc(t0 + Q);  // in flight through the chunk's products
+    if (k + 1 < nchunks) {  // in flight through the chunk's products
+      load_c(t0 + Q);
+      load_x(t0 + Q);
+    }
 
-    // ---- M = (C B^T) * exp(cs_t - cs_s) * delta_s on s <= t (wavefront w: rows 16w..16w+15)
-    {
-      f32x4_t g[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) g[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kk = 0; kk < N / 32; ++kk) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sC[(16 * w + lr) * SN + 32 * kk + 8 * lq]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (c > w) continue;  // wholly above the diagonal
-          const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sB[(16 * c + lr) * SN + 32 * kk + 8 * lq]);
-          g[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, g[c], 0, 0, 0);
-        }
+    // ---- M[t][s] = G[t][s] exp(cs_t - cs_s) delta_s on s <= t, from tiles of G^T = B C^T on or
+    // below the diagonal (wavefronts 0 and 1 take two of the ten, the others one), and zero for the
+    // two tiles above it that the Y products read
+    for (int gi = w; gi < 12; gi += 8) {
+      int gs, gt;
+      if (gi < 4) {
+        gs = 0;
+        gt = gi;
+      } else if (gi < 7) {
+        gs = 1;
+        gt = gi - 3;
+      } else if (gi < 9) {
+        gs = 2;
+        gt = gi - 5;
+      } else if (gi < 10) {
+        gs = 3;
+        gt = 3;
+      } else {
+        gs = gi == 10 ? 1 : 3;
+        gt = gs - 1;
       }
-      const f32x4_t cst = *reinterpret_cast<const f32x4_t*>(&sCS[16 * w + 4 * lq]);
+      const int t = 16 * gt + lr, s0 = 16 * gs + 4 * lq;
+      float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (gi < 10) {
+        f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int s = 16 * c + lr;
-        const float css = sCS[s], dls = sDL[s];
+        for (int kk = 0; kk < N / 32; ++kk) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sB[(16 * gs + lr) * SN + 32 * kk + 8 * lq]);
+          const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sC[(16 * gt + lr) * SN + 32 * kk + 8 * lq]);
+          g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, g, 0, 0, 0);
+        }
+        const float cst = sCS[t];
+        const f32x4_t css = *reinterpret_cast<const f32x4_t*>(&sCS[s0]);
+        const f32x4_t dls = *reinterpret_cast<const f32x4_t*>(&sDL[s0]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = 16 * w + 4 * lq + j;
-          const float m = (s <= t) ? g[c][j] * __builtin_amdgcn_exp2f((cst[j] - css) * kLog2eF) * dls : 0.0f;
-          const unsigned short hi = bf16_bits_of(m);
-          sM[t * SQ + s] = hi;
-          sMl[t * SQ + s] = bf16_bits_of(m - bf16_value(hi));
+        for (int j = 0; j < 4; ++j)
+          m[j] = (s0 + j <= t) ? g[j] * __builtin_amdgcn_exp2f((cst - css[j]) * kLog2eF) * dls[j] : 0.0f;
+      }
+      u32x2_t hi, lo;
+      split4(m, hi, lo);
+      *reinterpret_cast<u32x2_t*>(&sMh[t * SQ + s0]) = hi;
+      *reinterpret_cast<u32x2_t*>(&sMl[t * SQ + s0]) = lo;
+    }
+    // ---- W^T[n][s] = exp(cs_end - cs_s) delta_s B[s][n], from the B rows in registers
+    {
+      const float cse = sCS[Q - 1];
+#pragma unroll
+      for (int i = 0; i < B_PER; ++i) {
+        const int e = tid + NTH * i;
+        if (e < B_ITEMS) {
+          const int np = e % (N / 2), s0 = 4 * (e / (N / 2));
+          const f32x4_t css = *reinterpret_cast<const f32x4_t*>(&sCS[s0]);
+          const f32x4_t dls = *reinterpret_cast<const f32x4_t*>(&sDL[s0]);
+          float v0[4], v1[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float ws = __builtin_amdgcn_exp2f((cse - css[r]) * kLog2eF) * dls[r];
+            v0[r] = ws * bf16_lo_of(gb[i][r]);
+            v1[r] = ws * bf16_hi_of(gb[i][r]);
+          }
+          u32x2_t hi, lo;
+          split4(v0, hi, lo);
+          *reinterpret_cast<u32x2_t*>(&sWh[(2 * np) * SQ + s0]) = hi;
+          *reinterpret_cast<u32x2_t*>(&sWl[(2 * np) * SQ + s0]) = lo;
+          split4(v1, hi, lo);
+          *reinterpret_cast<u32x2_t*>(&sWh[(2 * np + 1) * SQ + s0]) = hi;
+          *reinterpret_cast<u32x2_t*>(&sWl[(2 * np + 1) * SQ + s0]) = lo;
         }
       }
     }
     __syncthreads();
-
-    // ---- W = exp(cs_end - cs_s) delta_s B[s][n], transposed into B's LDS (B's reads are done)
-    {
-      const float cse = sCS[Q - 1];
-#pragma unroll
-      for (int i = 0; i < BC_PASSES; ++i) {
-        const int s = bcr + BC_RSTEP * i;
-        const float ws = __builtin_amdgcn_exp2f((cse - sCS[s]) * kLog2eF) * sDL[s];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = ws * bf16_value(static_cast<unsigned short>(gb[i][e / 2] >> (16 * (e % 2))));
-          const unsigned short hi = bf16_bits_of(v);
-          sB[(bcc + e) * SQ + s] = hi;
-          sWl[(bcc + e) * SQ + s] = bf16_bits_of(v - bf16_value(hi));
-        }
-      }
-    }
     if (k + 1 < nchunks) load_b(t0 + Q);
 
-    // ---- Y = exp(cs_t) C H_prev^T + M x  (wavefront w: token rows 16w..16w+15, 4 tiles of 16 channels)
+    // ---- Y = exp(cs_t) C H + M x  (token block ty, channel blocks py0, py0+1), then the epilogue
     {
-      f32x4_t yacc[4];
+      f32x4_t yacc[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) yacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int c = 0; c < 2; ++c) yacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < N / 32; ++kk) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sC[(16 * w + lr) * SN + 32 * kk + 8 * lq]);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sC[(16 * ty + lr) * SN + 32 * kk + 8 * lq]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&sHT[(16 * c + lr) * SN + 32 * kk + 8 * lq]);
-          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&sHl[(16 * c + lr) * SN + 32 * kk + 8 * lq]);
+        for (int c = 0; c < 2; ++c) {
+          const int pr = (16 * (py0 + c) + lr) * SN + 32 * kk + 8 * lq;
+          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&sHh[pr]);
+          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&sHl[pr]);
           yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, yacc[c], 0, 0, 0);
           yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, yacc[c], 0, 0, 0);
         }
       }
-      const f32x4_t cst = *reinterpret_cast<const f32x4_t*>(&sCS[16 * w + 4 * lq]);
+      const f32x4_t cst = *reinterpret_cast<const f32x4_t*>(&sCS[16 * ty + 4 * lq]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) yacc[c][j] *= __builtin_amdgcn_exp2f(cst[j] * kLog2eF);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        if (32 * kk > 16 * w + 15) continue;  // M is zero past the diagonal
-        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sM[(16 * w + lr) * SQ + 32 * kk + 8 * lq]);
-        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sMl[(16 * w + lr) * SQ + 32 * kk + 8 * lq]);
+        if (32 * kk > 16 * ty + 15) continue;  // M is zero past the diagonal
+        const int mr = (16 * ty + lr) * SQ + 32 * kk + 8 * lq;
+        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sMh[mr]);
+        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sMl[mr]);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sXT[(16 * c + lr) * SQ + 32 * kk + 8 * lq]);
+        for (int c = 0; c < 2; ++c) {
+          const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sXT[(16 * (py0 + c) + lr) * SQ + 32 * kk + 8 * lq]);
           yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, yacc[c], 0, 0, 0);
           yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb, yacc[c], 0, 0, 0);
         }
       }
-      // epilogue: + D x, times SiLU(z), rounded to bf16
+      // + D x, times SiLU(z), rounded to bf16; x of four consecutive tokens is one 8-byte read of x^T
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int pch = 16 * c + lr;
+      for (int c = 0; c < 2; ++c) {
+        const int pch = 16 * (py0 + c) + lr;
+        const u32x2_t xq = *reinterpret_cast<const u32x2_t*>(&sXT[pch * SQ + 16 * ty + 4 * lq]);
+        const float xv[4] = {bf16_lo_of(xq[0]), bf16_hi_of(xq[0]), bf16_lo_of(xq[1]), bf16_hi_of(xq[1])};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int t = 16 * w + 4 * lq + j;
-          const int off = static_cast<int>(((t0 + t) * rowe + pch) * 2);
-          float v = __builtin_fmaf(Dh, bf16_value(sXT[pch * SQ + t]), yacc[c][j]);
-          if (p.z) v *= silu_f(bf16_value(static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(rs_z, off, 0, 0))));
-          __builtin_amdgcn_raw_buffer_store_b16(bf16_bits_of(v), rs_y, off, 0, 0);
+          const int t = 16 * ty + 4 * lq + j;
+          float v = __builtin_fmaf(Dh, xv[j], yacc[c][j]);
+          if (p.z) v *= silu_f(bf16_value(gz[c][j]));
+          __builtin_amdgcn_raw_buffer_store_b16(bf16_bits_of(v), rs_y, static_cast<int>(((t0 + t) * rowe + pch) * 2),
+                                                0, 0);
         }
       }
     }
-    __syncthreads();  // W is staged; every read of H_prev is done
 
-    // ---- H^T = exp(cs_end) H^T + x^T W  (wavefront w: channels 16w..16w+15, NT tiles of 16 states)
+    // ---- H = exp(cs_end) H + W^T x  (channel block ph, state blocks nb0 + 2i)
     {
       const float fade = __builtin_amdgcn_exp2f(sCS[Q - 1] * kLog2eF);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
+      for (int i = 0; i < HT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) hacc[nt][j] *= fade;
+        for (int j = 0; j < 4; ++j) hacc[i][j] *= fade;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sXT[(16 * w + lr) * SQ + 32 * kk + 8 * lq]);
+        const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sXT[(16 * ph + lr) * SQ + 32 * kk + 8 * lq]);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&sB[(16 * nt + lr) * SQ + 32 * kk + 8 * lq]);
-          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&sWl[(16 * nt + lr) * SQ + 32 * kk + 8 * lq]);
-          hacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, hacc[nt], 0, 0, 0);
-          hacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, hacc[nt], 0, 0, 0);
+        for (int i = 0; i < HT; ++i) {
+          const int wr = (16 * (nb0 + 2 * i) + lr) * SQ + 32 * kk + 8 * lq;
+          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sWh[wr]);
+          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sWl[wr]);
+          hacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, hacc[i], 0, 0, 0);
+          hacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb, hacc[i], 0, 0, 0);
         }
       }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int idx = (16 * w + 4 * lq + j) * SN + 16 * nt + lr;
-          const unsigned short hi = bf16_bits_of(hacc[nt][j]);
-          sHT[idx] = hi;
-          sHl[idx] = bf16_bits_of(hacc[nt][j] - bf16_value(hi));
-        }
     }
-    __syncthreads();  // H^T is staged; x^T and W are free for the next chunk
+    __syncthreads();  // every read of H^T, x^T, W^T, C, B and M for this chunk is done
+    // ---- H^T for the next chunk: four consecutive states of one channel per lane
+#pragma unroll
+    for (int i = 0; i < HT; ++i) {
+      const float v[4] = {hacc[i][0], hacc[i][1], hacc[i][2], hacc[i][3]};
+      u32x2_t hi, lo;
+      split4(v, hi, lo);
+      const int idx = (16 * ph + lr) * SN + 16 * (nb0 + 2 * i) + 4 * lq;
+      *reinterpret_cast<u32x2_t*>(&sHh[idx]) = hi;
+      *reinterpret_cast<u32x2_t*>(&sHl[idx]) = lo;
+    }
   }
 
   if (p.final_state) {
     float* fs = p.final_state + ((b * H + h) * P) * N;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int i = 0; i < HT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fs[(16 * w + 4 * lq + j) * N + 16 * nt + lr] = hacc[nt][j];
+      for (int j = 0; j < 4; ++j) fs[(16 * ph + lr) * N + 16 * (nb0 + 2 * i) + 4 * lq + j] = hacc[i][j];
   }
 }
 

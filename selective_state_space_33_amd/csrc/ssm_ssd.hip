@@ -14,7 +14,7 @@ bool ssd_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_
 
 template <int N>
 hipError_t launch_ssd(const SsdParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((ssd_kernel<N>), dim3(static_cast<unsigned>(p.batch * p.H)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((ssd_kernel<N>), dim3(static_cast<unsigned>(p.batch * p.H)), dim3(kSsdThreads), 0, s, p);
   return hipGetLastError();
 }
 
