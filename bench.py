@@ -386,7 +386,8 @@ def main():
         out["ssd"] = {"workload": "mamba2_2p7b_bf16 (batch 4, L 4096, 80 heads x 64, state 128)", "op": "ssm_ssd_fwd",
                       "ms_per_step": sms, "value": supd / (sms * 1e-3), "unit": "updates/s",
                       "roofline": {"bound": "hbm", "achieved": sgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                   "frac": sgbs / HBM_PEAK_GBS, "algorithmic_bytes": sbytes},
+                                   "frac": sgbs / HBM_PEAK_GBS, "algorithmic_bytes": sbytes,
+                                   "traffic": measured_traffic("mamba2_2p7b_bf16")},
                       "mfma": {"achieved": stf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": stf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": sflops}}
         del gs, ys, fss
