@@ -199,7 +199,9 @@ ssm_status_t ssm_state_update(float* state, const void* u, const void* delta, co
  * 16-token block of every 64-channel tile (about batch * L * dim * dstate *
  * 4 / 16 bytes), and per-tile partial sums of dB and dC (about 2 * batch *
  * L * dim / 64 * dstate * 4 bytes) and of dA, dD and d(delta_bias) per batch
- * row.  Returns 0 for arguments ssm_scan_bwd would reject. */
+ * row (and per chunk slot, plus the adjoints handed between chunks, when
+ * there are between 1 and 1.5 tiles of 64 channels per compute unit).
+ * Returns 0 for arguments ssm_scan_bwd would reject. */
 size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt);
 
 /* Backward of ssm_scan_fwd (or of ssm_scan_fwd_ex from an initial state,

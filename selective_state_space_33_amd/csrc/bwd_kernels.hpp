@@ -38,6 +38,20 @@
 // dA, dD and dbias accumulate in registers over the whole sequence.  Partial
 // sums over tiles (dB, dC) and over batch rows (dA, dD, dbias) are added in
 // a fixed order by bwd_reduce_*; so every result is deterministic.
+//
+// Chained launches (more tiles than CUs, up to 1.5 per CU): one workgroup per
+// CU runs a whole tile, and the r left-over tiles are cut into Ks chunks of
+// blocks, spliced into the whole tiles in reverse order of time.  Ticket j
+// (the order workgroups start) owns whole tile j and, for j < r * Ks, chunk
+// c = Ks-1 - j / r of left-over tile j % r.  The last chunk in time goes first,
+// from the gradient reaching the final state; chunk c < Ks-1 starts from the
+// adjoint that chunk c+1 (an earlier ticket) leaves after its first token,
+// handed on through device-coherent stores and a ready flag, as the forward's
+// chained plan hands on states.  A workgroup runs about (Ks-1-c) chunk-lengths
+// of its whole tile before it polls for that flag, so nobody idles; the whole
+// tile's running sums wait in registers meanwhile.  dA, dD and dbias of a
+// chunk go to partial slot c (a whole tile's to slot 0, zeros to the others),
+// so the reduction stays a fixed-order sum.
 #pragma once
 
 #include <utility>
@@ -70,9 +84,25 @@ struct BwdParams {
   int64_t batch, L, Lp, dim, N, ckpt_blocks;
   int ntd;
   int softplus;
+  // Chained launches (n_split > 0): tiles 0 .. n_long-1 whole, n_long .. n_long+n_split-1
+  // cut into Ks chunks of chunk_blocks blocks; adjoints handed on through carry
+  // [n_split][Ks][64][NPL*G] and flags [n_split][Ks] (zeroed by the pack kernel).  The
+  // dA/dD/dbias partials then have Ks slots: row slot * batch + b.
+  int n_long, n_split, Ks;
+  int chunk_blocks;
+  float* carry;
+  unsigned* flags;
+  unsigned* ticket;
+  unsigned* status;
 };
 
 constexpr int kBwdTB = 16;  // tokens per block (the checkpoint spacing)
+// A chained chunk waits for the adjoint handed on to it for at most this many
+// polls (each after a short sleep); past that it records an error bit in the
+// status word and goes on from what it read, so the kernel always ends.
+constexpr unsigned kBwdSpinLimit = 1u << 18;
+// vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 s_waitcnt encoding).
+constexpr int kBwdWaitVm0 = 0x0F70;
 
 // Sums over each group of 4 lanes of four values at once, each left in the
 // group's last lane: two steps of x += x shifted right by 1, 2 lanes within
@@ -111,52 +141,75 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   __shared__ float sRB[TB][NPAD][16];        // dB partials: one sum per group of 4 lanes
   __shared__ float sRC[TB][NPAD][16];
   __shared__ float sAcc[2][G][64];
+  __shared__ unsigned sWord;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = w * NPL;
-  const int tile = blockIdx.x;
-  const int64_t b = tile / p.ntd;
-  const int64_t d0 = static_cast<int64_t>(tile % p.ntd) * 64;
-  const int64_t d = d0 + lane;
   const int64_t dim = p.dim, L = p.L, N = p.N;
-  const bool dvalid = d < dim;
-
-  float A2[NPL], An[NPL], dhn[NPL], dAacc[NPL];
-#pragma unroll
-  for (int j = 0; j < NPL; ++j) {
-    const int n = n0 + j;
-    const bool ok = dvalid && n < N;
-    An[j] = ok ? p.A[d * N + n] : 0.0f;
-    A2[j] = An[j] * kLog2e;
-    dhn[j] = (ok && p.dfs) ? p.dfs[(b * dim + d) * N + n] : 0.0f;
-    dAacc[j] = 0.0f;
-  }
-  const float Dd = (dvalid && p.D) ? p.D[d] : 0.0f;
-  const float bias_d = (dvalid && p.bias) ? p.bias[d] : 0.0f;
   const bool has_z = p.z != nullptr;
   const bool sp_on = p.softplus != 0;
-
-  // Token rows of the tile (channels d0 .. d0+63 of batch row b), through
-  // buffer resources: rows past L read as zero and their stores are dropped;
-  // lanes past dim are masked at the stores.  The host keeps L rows of the
-  // tensor within 2^31 bytes.
   const int row_bytes = static_cast<int>(dim * ES);
-  const int64_t base_off = (b * L * dim + d0) * ES;
-  const int64_t bytes = L * row_bytes - d0 * ES;
-  auto rs_of = [&](const void* ptr) {
-    return make_rsrc(ptr ? static_cast<const char*>(ptr) + base_off : nullptr, ptr ? bytes : 0);
-  };
-  const rsrc_t rs_u = rs_of(p.u), rs_d = rs_of(p.delta), rs_z = rs_of(p.z), rs_dy = rs_of(p.dy);
-  const rsrc_t rs_du = rs_of(p.du), rs_dd = rs_of(p.ddelta), rs_dz = rs_of(p.dz);
-  const float* bc_row = p.bc + ((b * G + w) * p.Lp) * (2 * NPL);
-  const rsrc_t rs_bc = make_rsrc(bc_row, (p.Lp + 32) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
   const int rec_voff = (lane & 15) * 4;
-  const float* ckpt_row = p.ckpt + (static_cast<int64_t>(tile) * p.ckpt_blocks * 64 + lane) * NPAD + n0;
-
-  float accD = 0.0f, accBias = 0.0f;
   const int nblk = static_cast<int>((L + TB - 1) / TB);
+
+  // ---- the tile (64 channels of one batch row) the blocks below work on
+  int tile = 0;
+  int64_t b = 0, d0 = 0, d = 0;
+  bool dvalid = false;
+  float A2[NPL], An[NPL];
+  float Dd = 0.0f, bias_d = 0.0f;
+  rsrc_t rs_u, rs_d, rs_z, rs_dy, rs_du, rs_dd, rs_dz, rs_bc;
+  const float* ckpt_row = p.ckpt;
+  auto set_tile = [&](int t) {
+    tile = t;
+    b = t / p.ntd;
+    d0 = static_cast<int64_t>(t % p.ntd) * 64;
+    d = d0 + lane;
+    dvalid = d < dim;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int n = n0 + j;
+      An[j] = (dvalid && n < N) ? p.A[d * N + n] : 0.0f;
+      A2[j] = An[j] * kLog2e;
+    }
+    Dd = (dvalid && p.D) ? p.D[d] : 0.0f;
+    bias_d = (dvalid && p.bias) ? p.bias[d] : 0.0f;
+    // Token rows of the tile (channels d0 .. d0+63 of batch row b), through
+    // buffer resources: rows past L read as zero and their stores are
+    // dropped; lanes past dim are masked at the stores.  The host keeps L
+    // rows of the tensor within 2^31 bytes.
+    const int64_t base_off = (b * L * dim + d0) * ES;
+    const int64_t bytes = L * row_bytes - d0 * ES;
+    auto rs_of = [&](const void* ptr) {
+      return make_rsrc(ptr ? static_cast<const char*>(ptr) + base_off : nullptr, ptr ? bytes : 0);
+    };
+    rs_u = rs_of(p.u);
+    rs_d = rs_of(p.delta);
+    rs_z = rs_of(p.z);
+    rs_dy = rs_of(p.dy);
+    rs_du = rs_of(p.du);
+    rs_dd = rs_of(p.ddelta);
+    rs_dz = rs_of(p.dz);
+    const float* bc_row = p.bc + ((b * G + w) * p.Lp) * (2 * NPL);
+    rs_bc = make_rsrc(bc_row, (p.Lp + 32) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
+    ckpt_row = p.ckpt + (static_cast<int64_t>(t) * p.ckpt_blocks * 64 + lane) * NPAD + n0;
+  };
+
+  // ---- running sums of the stretch being worked on: the adjoint entering the
+  // next block down, dA, and this lane's dD, dbias terms
+  float dhn[NPL], dAacc[NPL];
+  float accD = 0.0f, accBias = 0.0f;
+  auto start_from_final = [&]() {  // the gradient reaching the tile's final state
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int n = n0 + j;
+      dhn[j] = (dvalid && n < N && p.dfs) ? p.dfs[(b * dim + d) * N + n] : 0.0f;
+      dAacc[j] = 0.0f;
+    }
+    accD = accBias = 0.0f;
+  };
 
   // Two-slot pipeline over the blocks (last to first): the loads of block
   // k-1 are in flight while block k computes.  Unrolled by two so each slot
@@ -350,36 +403,156 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     }
     __syncthreads();
   };
-  load_block(IC<0>{}, nblk - 1);
-  for (int k = nblk - 1; k >= 0; k -= 2) {
-    if (k >= 1) load_block(IC<1>{}, k - 1);
-    process_block(IC<0>{}, k);
-    if (k < 1) break;
-    if (k >= 2) load_block(IC<0>{}, k - 2);
-    process_block(IC<1>{}, k - 1);
+
+  // Blocks ke-1 down to kb.  With a stop flag, the run also ends after a pair
+  // of blocks once at least k_stop blocks are done and the flag is set
+  // (thread 0 polls it, the workgroup reads it through LDS); returns the end
+  // of what is left, [kb, returned).
+  auto run_blocks = [&](int kb, int ke, const unsigned* stop_flag, int k_stop) -> int {
+    if (ke <= kb) return kb;
+    load_block(IC<0>{}, ke - 1);
+    for (int k = ke - 1; k >= kb; k -= 2) {
+      if (k - 1 >= kb) load_block(IC<1>{}, k - 1);
+      process_block(IC<0>{}, k);
+      if (k - 1 < kb) break;
+      if (k - 2 >= kb) load_block(IC<0>{}, k - 2);
+      process_block(IC<1>{}, k - 1);
+      if (stop_flag != nullptr && ke - (k - 1) >= k_stop && k - 1 > kb) {
+        if (tid == 0) sWord = __hip_atomic_load(stop_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        const bool stop = sWord != 0u;
+        __syncthreads();  // every wavefront has read the word before it is written again
+        if (stop) return k - 1;
+      }
+    }
+    return kb;
+  };
+
+  // dA, dD, dbias of the current stretch into partial slot `slot`; the other
+  // slots of a whole tile are zero.
+  auto write_partials = [&](int slot, bool zero_others) {
+    const int nslots = p.n_split > 0 ? p.Ks : 1;
+    if (dvalid) {
+      for (int s = 0; s < nslots; ++s) {
+        if (s != slot && !zero_others) continue;
+        const int64_t row = static_cast<int64_t>(s) * p.batch + b;
+#pragma unroll
+        for (int j = 0; j < NPL; ++j) p.dA_part[(row * dim + d) * NPAD + n0 + j] = s == slot ? dAacc[j] : 0.0f;
+      }
+    }
+    sAcc[0][w][lane] = accD;
+    sAcc[1][w][lane] = accBias;
+    __syncthreads();
+    if (w == 0 && dvalid) {
+      float sd = sAcc[0][0][lane], sb = sAcc[1][0][lane];
+#pragma unroll
+      for (int ww = 1; ww < G; ++ww) {
+        sd += sAcc[0][ww][lane];
+        sb += sAcc[1][ww][lane];
+      }
+      for (int s = 0; s < nslots; ++s) {
+        if (s != slot && !zero_others) continue;
+        const int64_t row = static_cast<int64_t>(s) * p.batch + b;
+        p.dD_part[row * dim + d] = s == slot ? sd : 0.0f;
+        p.dbias_part[row * dim + d] = s == slot ? sb : 0.0f;
+      }
+    }
+    __syncthreads();  // sAcc is free again
+  };
+  // the adjoint left after token 0 is the gradient of h_{-1}
+  auto write_dh0 = [&]() {
+    if (dvalid && p.dh0) {
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        if (n0 + j < N) p.dh0[(b * dim + d) * N + n0 + j] = dhn[j];
+    }
+  };
+
+  if (p.n_split == 0) {  // one workgroup per tile
+    set_tile(blockIdx.x);
+    start_from_final();
+    run_blocks(0, nblk, nullptr, 0);
+    write_dh0();
+    write_partials(0, false);
+    return;
   }
 
-  if (dvalid) {
-#pragma unroll
-    for (int j = 0; j < NPL; ++j) {
-      p.dA_part[(b * dim + d) * NPAD + n0 + j] = dAacc[j];
-      // the adjoint left after token 0 is the gradient of h_{-1}
-      if (p.dh0 && n0 + j < N) p.dh0[(b * dim + d) * N + n0 + j] = dhn[j];
-    }
-  }
-  sAcc[0][w][lane] = accD;
-  sAcc[1][w][lane] = accBias;
+  // ---- chained: whole tile j, and chunk c = Ks-1 - j / n_split of left-over tile j % n_split
+  if (tid == 0) sWord = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (w == 0 && dvalid) {
-    float sd = sAcc[0][0][lane], sb = sAcc[1][0][lane];
-#pragma unroll
-    for (int ww = 1; ww < G; ++ww) {
-      sd += sAcc[0][ww][lane];
-      sb += sAcc[1][ww][lane];
-    }
-    p.dD_part[b * dim + d] = sd;
-    p.dbias_part[b * dim + d] = sb;
+  const int j = static_cast<int>(__builtin_amdgcn_readfirstlane(sWord));
+  __syncthreads();
+  set_tile(j);
+  start_from_final();
+  if (j >= p.n_split * p.Ks) {
+    run_blocks(0, nblk, nullptr, 0);
+    write_dh0();
+    write_partials(0, true);
+    return;
   }
+  const int o = j / p.n_split, st = j % p.n_split, c = p.Ks - 1 - o;
+  const int kb = c * p.chunk_blocks < nblk ? c * p.chunk_blocks : nblk;
+  const int ke = (c + 1) * p.chunk_blocks < nblk ? (c + 1) * p.chunk_blocks : nblk;
+  unsigned* my_flag = p.flags + static_cast<int64_t>(st) * p.Ks + c;  // set once chunk c+1 is done
+  int rest = nblk;
+  if (o > 0) rest = run_blocks(0, nblk, my_flag, o * p.chunk_blocks);
+  float sdh[NPL], sdA[NPL];
+  const float sD = accD, sBias = accBias;
+#pragma unroll
+  for (int q = 0; q < NPL; ++q) {
+    sdh[q] = dhn[q];
+    sdA[q] = dAacc[q];
+  }
+  set_tile(p.n_long + st);
+  start_from_final();
+  const int64_t crow = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;  // carry row [n_split][Ks][64]
+  if (o > 0) {
+    // the adjoint after chunk c+1: wait for its flag, then read it coherently
+    if (tid == 0) {
+      unsigned polls = 0;
+      while (__hip_atomic_load(my_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        if (++polls > kBwdSpinLimit) {
+          __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+    }
+    __syncthreads();
+    if (dvalid) {
+#pragma unroll
+      for (int q = 0; q < NPL; ++q)
+        dhn[q] = __hip_atomic_load(p.carry + crow * NPAD + n0 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  run_blocks(kb, ke, nullptr, 0);
+  if (c > 0) {
+    if (dvalid) {
+#pragma unroll
+      for (int q = 0; q < NPL; ++q)
+        __hip_atomic_store(p.carry + (crow - 64) * NPAD + n0 + q, dhn[q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(kBwdWaitVm0);  // this thread's carry stores have completed
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(p.flags + static_cast<int64_t>(st) * p.Ks + c - 1, 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    write_dh0();
+  }
+  write_partials(c, false);
+  // back to the whole tile where it stopped
+  set_tile(j);
+#pragma unroll
+  for (int q = 0; q < NPL; ++q) {
+    dhn[q] = sdh[q];
+    dAacc[q] = sdA[q];
+  }
+  accD = sD;
+  accBias = sBias;
+  run_blocks(0, rest, nullptr, 0);
+  write_dh0();
+  write_partials(0, true);
 }
 
 // dB[b][t][n] (and dC) = sum over the tiles of batch row b of their partials,

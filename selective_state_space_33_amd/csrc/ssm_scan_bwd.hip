@@ -4,12 +4,18 @@
 // One call: pack B/C into the forward's records; a forward launch in
 // checkpoint mode leaves the state entering every 16-token block of every
 // tile; the backward kernel walks each tile's blocks from the last to the
-// first, recomputing the states it needs; two small kernels add the partial
-// sums over tiles (dB, dC) and batch rows (dA, dD, dbias) in a fixed order.
+// first, recomputing the states it needs (one workgroup per tile, or, with
+// between 1 and 1.5 tiles per CU, one per CU with the left-over tiles' chunks
+// chained in); two small kernels add the partial sums over tiles (dB, dC)
+// and batch rows and chunk slots (dA, dD, dbias) in a fixed order.
+//
+// SSM_BWD_CHAINED=0 (environment) keeps one workgroup per tile; for tests and
+// timing comparisons.
 #include "ssm_scan.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include "bwd_kernels.hpp"
 #include "scan_launch.hpp"
@@ -19,15 +25,19 @@ namespace {
 
 constexpr int64_t kBwdMaxBatch = 65535;
 constexpr int64_t kBwdMaxState = 32;
+constexpr int64_t kBwdNumCU = 256;  // MI355X compute units
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 bool is_aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 // Variant: 2 states per lane over 8 wavefronts up to 16 states, 4 per lane up to 32.
+// Chained plan (CUs < T <= 1.5 CUs): n_long = CUs whole tiles, the r = T - CUs
+// others in Ks = CUs / r chunks of blocks (at most 8).
 struct BwdPlan {
   int npl, G;
   int64_t Lp, ntd, T, ckpt_blocks;
+  int n_long, n_split, Ks, chunk_blocks;
 };
 
 BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
@@ -38,22 +48,44 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
   pl.ntd = cdiv(dim, 64);
   pl.T = batch * pl.ntd;
   pl.ckpt_blocks = pl.Lp / kBwdTB;
+  pl.n_long = 0;
+  pl.n_split = 0;
+  pl.Ks = 1;
+  pl.chunk_blocks = 0;
+  const char* env = getenv("SSM_BWD_CHAINED");
+  const bool chained_ok = !(env && atoi(env) == 0);
+  if (chained_ok && pl.T > kBwdNumCU && 2 * (pl.T - kBwdNumCU) <= kBwdNumCU) {
+    const int64_t r = pl.T - kBwdNumCU;
+    int64_t K = kBwdNumCU / r;
+    if (K > 8) K = 8;
+    pl.n_long = static_cast<int>(kBwdNumCU);
+    pl.n_split = static_cast<int>(r);
+    pl.Ks = static_cast<int>(K);
+    pl.chunk_blocks = static_cast<int>(cdiv(cdiv(L, kBwdTB), K));
+  }
   return pl;
 }
 
+// Workspace: [packed B/C][checkpoints][dB, dC partials][dA, dD, dbias
+// partials (Ks slots)][carried adjoints][flags, ticket, status].
 struct BwdLayout {
-  size_t bc, ckpt, bcpart, apart, dpart, total;
+  size_t bc, ckpt, bcpart, apart, dpart, carry, words, total;
+  int n_words;
 };
 
 BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t dim) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
+  const int64_t slots = pl.n_split > 0 ? pl.Ks : 1;
   BwdLayout l;
   l.bc = al256(static_cast<size_t>(batch * pl.Lp + kTBMax) * 2 * npad * sizeof(float));
   l.ckpt = al256(static_cast<size_t>(pl.T * pl.ckpt_blocks) * 64 * npad * sizeof(float));
   l.bcpart = al256(static_cast<size_t>(batch * pl.ntd * pl.Lp) * npad * sizeof(float));
-  l.apart = al256(static_cast<size_t>(batch * dim) * npad * sizeof(float));
-  l.dpart = al256(static_cast<size_t>(batch * dim) * sizeof(float));
-  l.total = l.bc + l.ckpt + 2 * l.bcpart + l.apart + 2 * l.dpart;
+  l.apart = al256(static_cast<size_t>(slots * batch * dim) * npad * sizeof(float));
+  l.dpart = al256(static_cast<size_t>(slots * batch * dim) * sizeof(float));
+  l.carry = al256(static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float));
+  l.n_words = pl.n_split > 0 ? pl.n_split * pl.Ks + 2 : 0;
+  l.words = al256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
+  l.total = l.bc + l.ckpt + 2 * l.bcpart + l.apart + 2 * l.dpart + l.carry + l.words;
   return l;
 }
 
@@ -62,24 +94,26 @@ BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t dim) {
 bool rows_fit(int64_t L, int64_t dim, int64_t es) { return L * dim * es < 0x7fffffffLL - kTrip * dim * es; }
 
 template <class IO>
-hipError_t run_bwd(const BwdPlan& pl, const void* B, const void* C, float* bc, ScanParams sp, BwdParams bp,
-                   void* dB, void* dC, float* dA, float* dD, float* dbias, int vw, hipStream_t s) {
+hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const void* C, float* bc, ScanParams sp,
+                   BwdParams bp, void* dB, void* dC, float* dA, float* dD, float* dbias, int vw, hipStream_t s) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
   const dim3 pgrid(static_cast<unsigned>(sp.batch * (pl.Lp / kPackT)));
+  // the pack also zeroes the chained launch's flags, ticket and status
   if (pl.npl == 2)
     hipLaunchKernelGGL((pack_bc_kernel<IO, 2>), pgrid, dim3(256), 0, s, B, C, bc, sp.batch, sp.L, pl.Lp, sp.N,
-                       pl.G, static_cast<unsigned*>(nullptr), 0, static_cast<float*>(nullptr));
+                       pl.G, bp.flags, lay.n_words, static_cast<float*>(nullptr));
   else
     hipLaunchKernelGGL((pack_bc_kernel<IO, 4>), pgrid, dim3(256), 0, s, B, C, bc, sp.batch, sp.L, pl.Lp, sp.N,
-                       pl.G, static_cast<unsigned*>(nullptr), 0, static_cast<float*>(nullptr));
+                       pl.G, bp.flags, lay.n_words, static_cast<float*>(nullptr));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   e = launch_scan<IO, kModeCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.T)), s);
   if (e != hipSuccess) return e;
+  const dim3 bgrid(static_cast<unsigned>(pl.n_split > 0 ? pl.n_long : pl.T));
   if (pl.npl == 2)
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, 2, 8>), dim3(static_cast<unsigned>(pl.T)), dim3(512), 0, s, bp);
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, 2, 8>), bgrid, dim3(512), 0, s, bp);
   else
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8>), dim3(static_cast<unsigned>(pl.T)), dim3(512), 0, s, bp);
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8>), bgrid, dim3(512), 0, s, bp);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nbc = sp.batch * sp.L * sp.N;
@@ -88,8 +122,10 @@ hipError_t run_bwd(const BwdPlan& pl, const void* B, const void* C, float* bc, S
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t npar = sp.dim * sp.N;
+  // the partial slots are further rows of the same sums
+  const int64_t rows = sp.batch * (pl.n_split > 0 ? pl.Ks : 1);
   hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3(static_cast<unsigned>(cdiv(npar, 256))), dim3(256), 0, s,
-                     bp.dA_part, bp.dD_part, bp.dbias_part, dA, dD, dbias, sp.batch, sp.dim, sp.N, npad);
+                     bp.dA_part, bp.dD_part, bp.dbias_part, dA, dD, dbias, rows, sp.dim, sp.N, npad);
   return hipGetLastError();
 }
 
@@ -152,6 +188,9 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   float* dA_part = reinterpret_cast<float*>(ws + lay.bc + lay.ckpt + 2 * lay.bcpart);
   float* dD_part = reinterpret_cast<float*>(ws + lay.bc + lay.ckpt + 2 * lay.bcpart + lay.apart);
   float* dbias_part = reinterpret_cast<float*>(ws + lay.bc + lay.ckpt + 2 * lay.bcpart + lay.apart + lay.dpart);
+  char* tail = ws + lay.bc + lay.ckpt + 2 * lay.bcpart + lay.apart + 2 * lay.dpart;
+  float* carry = lay.carry ? reinterpret_cast<float*>(tail) : nullptr;
+  unsigned* words = lay.n_words ? reinterpret_cast<unsigned*>(tail + lay.carry) : nullptr;
 
   ScanParams sp = {};
   sp.u = u;
@@ -173,7 +212,7 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   sp.ckpt_blocks = pl.ckpt_blocks;
   sp.h0 = initial_state;
 
-  BwdParams bp;
+  BwdParams bp = {};
   bp.u = u;
   bp.delta = delta;
   bp.A = A;
@@ -201,12 +240,20 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   bp.ckpt_blocks = pl.ckpt_blocks;
   bp.ntd = static_cast<int>(pl.ntd);
   bp.softplus = softplus_flag ? 1 : 0;
+  bp.n_long = pl.n_long;
+  bp.n_split = pl.n_split;
+  bp.Ks = pl.Ks;
+  bp.chunk_blocks = pl.chunk_blocks;
+  bp.carry = carry;
+  bp.flags = words;
+  bp.ticket = words ? words + static_cast<int64_t>(pl.n_split) * pl.Ks : nullptr;
+  bp.status = words ? bp.ticket + 1 : nullptr;
 
   float* dD_out = D ? dD : nullptr;
   float* dbias_out = delta_bias ? ddelta_bias : nullptr;
   const hipError_t e =
       dt == SSM_DTYPE_F32
-          ? run_bwd<F32>(pl, B, C, bc, sp, bp, dB, dC, dA, dD_out, dbias_out, vw, stream)
-          : run_bwd<BF16>(pl, B, C, bc, sp, bp, dB, dC, dA, dD_out, dbias_out, vw, stream);
+          ? run_bwd<F32>(pl, lay, B, C, bc, sp, bp, dB, dC, dA, dD_out, dbias_out, vw, stream)
+          : run_bwd<BF16>(pl, lay, B, C, bc, sp, bp, dB, dC, dA, dD_out, dbias_out, vw, stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }

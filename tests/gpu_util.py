@@ -146,3 +146,10 @@ class IndexOrder(_Env):
 
     def __init__(self):
         super().__init__("SSM_SCAN_ORDER", "0")
+
+
+class BwdChained(_Env):
+    """Temporarily allow (True) or forbid (False) the chained plan of the backward pass."""
+
+    def __init__(self, on):
+        super().__init__("SSM_BWD_CHAINED", "1" if on else "0")

@@ -14,7 +14,7 @@ from oracle import bwd as OB
 from selective_state_space_33_amd import inputs as I
 from selective_state_space_33_amd import ops
 
-from .gpu_util import TOL, rel_err, say, to_dev, to_dev_f32
+from .gpu_util import TOL, BwdChained, rel_err, say, to_dev, to_dev_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +117,31 @@ def test_bwd_is_deterministic():
     for k in g1:
         if g1[k] is not None:
             assert torch.equal(g1[k], g2[k]), k
+
+
+@pytest.mark.parametrize("L", [300, 40, 16])
+def test_bwd_chained_plan(L):
+    """320 tiles (5 rows x 64 tiles): 256 whole, 64 cut into 4 chunks of blocks handing the adjoint backwards
+    (L = 40 leaves the last chunk empty, L = 16 all but chunk 0)."""
+    rng = np.random.default_rng(470 + L)
+    x, dy, dfs = _case(rng, 5, L, 64 * 64, 16, "bf16")
+    h0 = np.asarray(rng.standard_normal((5, 64 * 64, 16)) * 0.5, np.float32).astype(np.float64)
+    with BwdChained(True):
+        _run_and_compare(x, dy, dfs, "bf16", label=f"chained L{L}", h0=h0)
+
+
+def test_bwd_chained_plan_fp32_and_deterministic():
+    rng = np.random.default_rng(480)
+    x, dy, dfs = _case(rng, 5, 200, 64 * 64, 16, "f32")
+    with BwdChained(True):
+        g1 = _run_and_compare(x, dy, dfs, "f32", label="chained fp32")
+        args = (to_dev(x["u"], "f32"), to_dev(x["delta"], "f32"), to_dev_f32(x["A"]), to_dev(x["B"], "f32"),
+                to_dev(x["C"], "f32"), to_dev(dy, "f32"))
+        kw = dict(D=to_dev_f32(x["D"]), z=to_dev(x["z"], "f32"), delta_bias=to_dev_f32(x["delta_bias"]),
+                  dfinal_state=to_dev_f32(dfs))
+        g2 = ops.ssm_scan_bwd(*args, **kw)
+        g3 = ops.ssm_scan_bwd(*args, **kw)
+        torch.cuda.synchronize()
+    for k in g2:
+        if g2[k] is not None:
+            assert torch.equal(g2[k], g3[k]), k
