@@ -177,11 +177,23 @@ ssm_status_t ssm_scan_trap_fwd(const void* u, const void* delta, const float* A,
  *   4-byte (else INVALID_ARG).  Supported: dt = BF16, headdim = 64 and
  *   dstate = 32, 64 or 128, with (L + 64) * heads * headdim * 2 bytes below
  *   2^31 (else UNSUPPORTED).  Arithmetic: bf16 matrix products with fp32
- *   accumulation, fp32 state.  No workspace; y must not alias an input. */
+ *   accumulation, fp32 state.  workspace: workspace_bytes >=
+ *   ssm_ssd_fwd_workspace_size() bytes of device memory, 256-byte aligned
+ *   (may be NULL when that size is 0), overwritten by the call and not to be
+ *   shared with a concurrent call.  y must not alias an input. */
 ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                          const float* D, const void* z, const float* delta_bias, int softplus_flag,
                          void* y, float* final_state, int64_t batch, int64_t L, int64_t heads, int64_t headdim,
-                         int64_t dstate, ssm_dtype_t dt, hipStream_t stream);
+                         int64_t dstate, ssm_dtype_t dt, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Bytes of device workspace ssm_ssd_fwd needs: 0 when there are at most as
+ * many (batch row, head) units as compute units (or more than 1.5 per CU);
+ * otherwise the states handed between the segments of the left-over units
+ * (about (batch * heads - 256) * 8 * headdim * dstate * 4 bytes at most) and a
+ * few words of flags.  Returns 0 also for arguments the call would reject. */
+size_t ssm_ssd_fwd_workspace_size(int64_t batch, int64_t L, int64_t heads, int64_t headdim, int64_t dstate,
+                                  ssm_dtype_t dt);
 
 /* One recurrent (decode) step: the same arithmetic as one token of the scan,
  * reading `state` as h_{t-1} and overwriting it in place with h_t

@@ -57,7 +57,29 @@ struct SsdParams {
   float* final_state;  // [batch][H][P][N] (nullable)
   int64_t batch, L, H;
   int softplus;
+  // Chained launches (n_split > 0): units (batch row, head) 0 .. n_long-1
+  // whole, n_long .. n_long+n_split-1 cut into Ks segments of seg_chunks
+  // chunks, states handed on through carry [n_split][Ks][P][N] and flags
+  // [n_split][Ks], with a workgroup ticket and a status word (all zeroed
+  // before the launch).
+  int n_long, n_split, Ks;
+  int64_t seg_chunks;
+  float* carry;
+  unsigned* flags;
+  unsigned* ticket;
+  unsigned* status;
 };
+
+// A chained segment waits for the state handed on to it for at most this
+// many polls (each after a short sleep); past that it records an error bit in
+// the status word and goes on, so the kernel always ends.
+constexpr unsigned kSsdSpinLimit = 1u << 18;
+constexpr int kSsdWaitVm0 = 0x0F70;  // vmcnt(0), other counters at their maxima (gfx9 s_waitcnt)
+
+// Zeroes the flags, ticket and status of a chained launch.
+__global__ void __launch_bounds__(256) ssd_zero_words_kernel(unsigned* words, int n) {
+  for (int e = threadIdx.x; e < n; e += 256) words[e] = 0u;
+}
 
 constexpr int kSsdQ = 64;         // tokens per chunk
 constexpr int kSsdP = 64;         // channels per head
@@ -117,21 +139,28 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
   const int lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
   const int64_t H = p.H, L = p.L;
-  const int64_t b = blockIdx.x / H, h = blockIdx.x % H;
   const int64_t rowe = H * P;  // elements between token rows of x, z, y
-  const float Ah = p.A[h];
-  const float Dh = p.D ? p.D[h] : 0.0f;
-  const float biash = p.bias ? p.bias[h] : 0.0f;
 
-  // Buffer resources: token rows past L read as zero and are not written.
-  const int64_t xbase = (b * L * H + h) * P;
-  const int64_t xbytes = (L * H - h) * P * 2;
-  const rsrc_t rs_x = make_rsrc(static_cast<const unsigned short*>(p.x) + xbase, xbytes);
-  const rsrc_t rs_z = make_rsrc(p.z ? static_cast<const unsigned short*>(p.z) + xbase : nullptr, p.z ? xbytes : 0);
-  const rsrc_t rs_y = make_rsrc(static_cast<unsigned short*>(p.y) + xbase, xbytes);
-  const rsrc_t rs_b = make_rsrc(static_cast<const unsigned short*>(p.B) + b * L * N, L * N * 2);
-  const rsrc_t rs_c = make_rsrc(static_cast<const unsigned short*>(p.C) + b * L * N, L * N * 2);
-  const rsrc_t rs_d = make_rsrc(static_cast<const unsigned short*>(p.delta) + b * L * H + h, (L * H - h) * 2);
+  // ---- the unit (batch row b, head h) being worked on
+  int64_t b = 0, h = 0;
+  float Ah = 0.0f, Dh = 0.0f, biash = 0.0f;
+  rsrc_t rs_x, rs_z, rs_y, rs_b, rs_c, rs_d;
+  auto set_unit = [&](int64_t unit) {
+    b = unit / H;
+    h = unit % H;
+    Ah = p.A[h];
+    Dh = p.D ? p.D[h] : 0.0f;
+    biash = p.bias ? p.bias[h] : 0.0f;
+    // Buffer resources: token rows past L read as zero and are not written.
+    const int64_t xbase = (b * L * H + h) * P;
+    const int64_t xbytes = (L * H - h) * P * 2;
+    rs_x = make_rsrc(static_cast<const unsigned short*>(p.x) + xbase, xbytes);
+    rs_z = make_rsrc(p.z ? static_cast<const unsigned short*>(p.z) + xbase : nullptr, p.z ? xbytes : 0);
+    rs_y = make_rsrc(static_cast<unsigned short*>(p.y) + xbase, xbytes);
+    rs_b = make_rsrc(static_cast<const unsigned short*>(p.B) + b * L * N, L * N * 2);
+    rs_c = make_rsrc(static_cast<const unsigned short*>(p.C) + b * L * N, L * N * 2);
+    rs_d = make_rsrc(static_cast<const unsigned short*>(p.delta) + b * L * H + h, (L * H - h) * 2);
+  };
 
   // Work of this wavefront.  Y tiles: token block ty, channel blocks py0, py0+1.
   const int ty = w & 3, py0 = 2 * (w >> 2);
@@ -187,15 +216,33 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
   };
 
   f32x4_t hacc[HT];
+  // H^T as bf16 pairs for the Y products, from the accumulators: four
+  // consecutive states of one channel per lane (this wavefront's tiles only)
+  auto stage_state = [&]() {
 #pragma unroll
-  for (int i = 0; i < HT; ++i) hacc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int e = tid; e < P * SN; e += NTH) sHh[e] = sHl[e] = 0;
+    for (int i = 0; i < HT; ++i) {
+      const float v[4] = {hacc[i][0], hacc[i][1], hacc[i][2], hacc[i][3]};
+      u32x2_t hi, lo;
+      split4(v, hi, lo);
+      const int idx = (16 * ph + lr) * SN + 16 * (nb0 + 2 * i) + 4 * lq;
+      *reinterpret_cast<u32x2_t*>(&sHh[idx]) = hi;
+      *reinterpret_cast<u32x2_t*>(&sHl[idx]) = lo;
+    }
+  };
+  // state element (channel, state) of this lane's tile i, entry q
+  auto state_index = [&](int i, int q) { return (16 * ph + lr) * N + 16 * (nb0 + 2 * i) + 4 * lq + q; };
+  __shared__ unsigned sWord;
 
-  const int64_t nchunks = (L + Q - 1) / Q;
-  load_c(0);
-  load_b(0);
-  load_x(0);
-  for (int64_t k = 0; k < nchunks; ++k) {
+  // Chunks kb .. ke-1 of the current unit, from the state in hacc (staged in
+  // LDS).  With a stop flag, the run also ends after a chunk once at least
+  // k_stop chunks are done and the flag is set (thread 0 polls it, the
+  // workgroup reads it through LDS); returns the first chunk not done.
+  auto run_chunks = [&](int64_t kb, int64_t ke, const unsigned* stop_flag, int64_t k_stop) -> int64_t {
+  if (ke <= kb) return kb;
+  load_c(kb * Q);
+  load_b(kb * Q);
+  load_x(kb * Q);
+  for (int64_t k = kb; k < ke; ++k) {
     const int64_t t0 = k * Q;
     load_z(t0);
     // ---- stage: C and B by token row, x transposed, the steps and their cumulative sums
@@ -234,7 +281,7 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
       sCS[lane] = cs;
     }
     __syncthreads();
-    if (k + 1 < nchunks) {  // in flight through the chunk's products
+    if (k + 1 < ke) {  // in flight through the chunk's products
       load_c(t0 + Q);
       load_x(t0 + Q);
     }
@@ -310,7 +357,7 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
       }
     }
     __syncthreads();
-    if (k + 1 < nchunks) load_b(t0 + Q);
+    if (k + 1 < ke) load_b(t0 + Q);
 
     // ---- Y = exp(cs_t) C H + M x  (token block ty, channel blocks py0, py0+1), then the epilogue
     {
@@ -385,25 +432,110 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
       }
     }
     __syncthreads();  // every read of H^T, x^T, W^T, C, B and M for this chunk is done
-    // ---- H^T for the next chunk: four consecutive states of one channel per lane
-#pragma unroll
-    for (int i = 0; i < HT; ++i) {
-      const float v[4] = {hacc[i][0], hacc[i][1], hacc[i][2], hacc[i][3]};
-      u32x2_t hi, lo;
-      split4(v, hi, lo);
-      const int idx = (16 * ph + lr) * SN + 16 * (nb0 + 2 * i) + 4 * lq;
-      *reinterpret_cast<u32x2_t*>(&sHh[idx]) = hi;
-      *reinterpret_cast<u32x2_t*>(&sHl[idx]) = lo;
+    stage_state();      // H^T for the next chunk
+    if (stop_flag != nullptr && k + 1 - kb >= k_stop && k + 1 < ke) {
+      if (tid == 0) sWord = __hip_atomic_load(stop_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const bool stop = sWord != 0u;
+      __syncthreads();  // every wavefront has read the word before it is written again
+      if (stop) return k + 1;
     }
   }
+  return ke;
+  };
+  auto write_final = [&]() {
+    if (p.final_state) {
+      float* fs = p.final_state + ((b * H + h) * P) * N;
+#pragma unroll
+      for (int i = 0; i < HT; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) fs[state_index(i, q)] = hacc[i][q];
+    }
+  };
 
-  if (p.final_state) {
-    float* fs = p.final_state + ((b * H + h) * P) * N;
+  const int64_t nchunks = (L + Q - 1) / Q;
+  if (p.n_split == 0) {  // one workgroup per unit
+    set_unit(blockIdx.x);
+#pragma unroll
+    for (int i = 0; i < HT; ++i) hacc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    stage_state();
+    run_chunks(0, nchunks, nullptr, 0);
+    write_final();
+    return;
+  }
+
+  // ---- chained: whole unit j, and segment sg = j / n_split of left-over unit j % n_split.
+  // Segment 0 goes first; segment sg > 0 is spliced in after about sg segment-lengths of the
+  // whole unit, once segment sg-1 (an earlier ticket) has handed on its state.
+  if (tid == 0) sWord = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int j = static_cast<int>(__builtin_amdgcn_readfirstlane(sWord));
+  __syncthreads();
+  set_unit(j);
+#pragma unroll
+  for (int i = 0; i < HT; ++i) hacc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  stage_state();
+  if (j >= p.n_split * p.Ks) {
+    run_chunks(0, nchunks, nullptr, 0);
+    write_final();
+    return;
+  }
+  const int sg = j / p.n_split, st = j % p.n_split;
+  const int64_t kb = sg * p.seg_chunks < nchunks ? sg * p.seg_chunks : nchunks;
+  const int64_t ke = (sg + 1) * p.seg_chunks < nchunks ? (sg + 1) * p.seg_chunks : nchunks;
+  unsigned* my_flag = p.flags + static_cast<int64_t>(st) * p.Ks + sg;  // set once segment sg-1 is done
+  int64_t rest = 0;
+  if (sg > 0) rest = run_chunks(0, nchunks, my_flag, sg * p.seg_chunks);
+  f32x4_t saved[HT];
+#pragma unroll
+  for (int i = 0; i < HT; ++i) saved[i] = hacc[i];
+  set_unit(p.n_long + st);
+  float* crow = p.carry + (static_cast<int64_t>(st) * p.Ks + sg) * P * N;  // [n_split][Ks][P][N]
+#pragma unroll
+  for (int i = 0; i < HT; ++i) hacc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  if (sg > 0) {
+    // the state after segment sg-1: wait for its flag, then read it coherently
+    if (tid == 0) {
+      unsigned polls = 0;
+      while (__hip_atomic_load(my_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        if (++polls > kSsdSpinLimit) {
+          __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(4);
+      }
+    }
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < HT; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fs[(16 * ph + lr) * N + 16 * (nb0 + 2 * i) + 4 * lq + j] = hacc[i][j];
+      for (int q = 0; q < 4; ++q)
+        hacc[i][q] = __hip_atomic_load(crow + state_index(i, q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  stage_state();
+  run_chunks(kb, ke, nullptr, 0);
+  if (sg + 1 < p.Ks) {
+    float* next = crow + P * N;
+#pragma unroll
+    for (int i = 0; i < HT; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __hip_atomic_store(next + state_index(i, q), hacc[i][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(kSsdWaitVm0);  // this thread's carry stores have completed
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(p.flags + static_cast<int64_t>(st) * p.Ks + sg + 1, 1u, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    write_final();
+  }
+  // back to the whole unit where it stopped
+  set_unit(j);
+#pragma unroll
+  for (int i = 0; i < HT; ++i) hacc[i] = saved[i];
+  stage_state();
+  run_chunks(rest, nchunks, nullptr, 0);
+  write_final();
 }
 
 }  // namespace ssm

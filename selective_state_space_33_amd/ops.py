@@ -22,7 +22,8 @@ SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 
 # Every symbol include/ssm_scan.h declares.
 EXPORTED = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_ex_workspace_size", "ssm_scan_fwd_ex",
-            "ssm_scan_trap_fwd_workspace_size", "ssm_scan_trap_fwd", "ssm_ssd_fwd", "ssm_state_update",
+            "ssm_scan_trap_fwd_workspace_size", "ssm_scan_trap_fwd", "ssm_ssd_fwd_workspace_size", "ssm_ssd_fwd",
+            "ssm_state_update",
             "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_status_string")
 
 _lib = None
@@ -60,7 +61,10 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_trap_fwd.restype = ctypes.c_int
         L.ssm_scan_trap_fwd.argtypes = L.ssm_scan_fwd_ex.argtypes
         L.ssm_ssd_fwd.restype = ctypes.c_int
-        L.ssm_ssd_fwd.argtypes = [_vp] * 8 + [ctypes.c_int, _vp, _vp] + [_i64] * 5 + [ctypes.c_int, _vp]
+        L.ssm_ssd_fwd.argtypes = ([_vp] * 8 + [ctypes.c_int, _vp, _vp] + [_i64] * 5 +
+                                  [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
+        L.ssm_ssd_fwd_workspace_size.restype = ctypes.c_size_t
+        L.ssm_ssd_fwd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int]
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_scan_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
         L.ssm_scan_bwd.restype = ctypes.c_int
@@ -212,8 +216,13 @@ def _fwd_rows(entry, u, delta, A, B, C, D, z, delta_bias, softplus, initial_stat
     return y, final_state
 
 
+def ssm_ssd_fwd_workspace_size(batch: int, L: int, heads: int, headdim: int, dstate: int,
+                               dtype: torch.dtype) -> int:
+    return int(lib().ssm_ssd_fwd_workspace_size(batch, L, heads, headdim, dstate, _dtype_code(dtype)))
+
+
 def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, y=None,
-                final_state=None, return_final_state: bool = True, stream=None):
+                final_state=None, return_final_state: bool = True, workspace=None, stream=None):
     """The Mamba-2 SSD layer on the GPU.
 
     x, z: [batch, L, heads, headdim]; delta: [batch, L, heads]; B, C: [batch, L, dstate] (bfloat16);
@@ -234,9 +243,13 @@ def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bo
     if final_state is None and return_final_state:
         final_state = torch.empty((batch, heads, headdim, dstate), dtype=torch.float32, device=dev)
     _check(final_state, "final_state", torch.float32, (batch, heads, headdim, dstate), dev)
+    need = ssm_ssd_fwd_workspace_size(batch, L, heads, headdim, dstate, dt)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                            1 if softplus else 0, _ptr(y), _ptr(final_state), batch, L, heads, headdim, dstate, code,
-                           _stream(dev, stream))
+                           _ptr(workspace), ws_bytes, _stream(dev, stream))
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_ssd_fwd")
     return y, final_state

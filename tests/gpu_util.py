@@ -153,3 +153,10 @@ class BwdChained(_Env):
 
     def __init__(self, on):
         super().__init__("SSM_BWD_CHAINED", "1" if on else "0")
+
+
+class SsdChained(_Env):
+    """Temporarily allow (True) or forbid (False) the chained plan of the SSD layer."""
+
+    def __init__(self, on):
+        super().__init__("SSM_SSD_CHAINED", "1" if on else "0")

@@ -213,10 +213,11 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 def _ssd(lib_, **kw):
     """Call ssm_ssd_fwd with fake (never dereferenced) pointers; only rejection paths are used."""
     a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, z=None, bias=None, sp=1, y=0x6000,
-             fs=None, batch=1, L=8, H=2, P=64, N=64, dt=BF16, stream=None)
+             fs=None, batch=1, L=8, H=2, P=64, N=64, dt=BF16, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib_.ssm_ssd_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["y"],
-                            a["fs"], a["batch"], a["L"], a["H"], a["P"], a["N"], a["dt"], a["stream"])
+                            a["fs"], a["batch"], a["L"], a["H"], a["P"], a["N"], a["dt"], a["ws"], a["wsb"],
+                            a["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -225,6 +226,15 @@ def _ssd(lib_, **kw):
     (dict(x=0x1008), INVALID), (dict(C=0x5004), INVALID), (dict(delta=0x2001), INVALID), (dict(fs=0x7002), INVALID),
     (dict(dt=F32), UNSUPPORTED), (dict(P=32), UNSUPPORTED), (dict(N=16), UNSUPPORTED), (dict(N=96), UNSUPPORTED),
     (dict(L=1 << 20, H=40), UNSUPPORTED),   # token rows past 2^31 bytes
+    (dict(batch=4, H=80), INVALID),           # 320 units: the chained plan needs its workspace
 ])
 def test_ssd_rejects_bad_arguments_without_launching(kw, expect):
     assert _ssd(ops.lib(), **kw) == expect
+
+
+def test_ssd_workspace_size():
+    L = ops.lib()
+    assert L.ssm_ssd_fwd_workspace_size(2, 1000, 3, 64, 64, BF16) == 0          # fewer units than CUs
+    ws = L.ssm_ssd_fwd_workspace_size(4, 4096, 80, 64, 128, BF16)             # 320 units: 64 left over, 4 segments
+    assert ws >= 64 * 4 * 64 * 128 * 4 and ws % 256 == 0
+    assert L.ssm_ssd_fwd_workspace_size(4, 4096, 80, 64, 128, F32) == 0        # rejected

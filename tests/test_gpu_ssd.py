@@ -15,7 +15,7 @@ from oracle import ssd as S
 from selective_state_space_33_amd import inputs as I
 from selective_state_space_33_amd import ops
 
-from .gpu_util import TOL, rel_err, say
+from .gpu_util import TOL, SsdChained, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -116,3 +116,17 @@ def test_ssd_deterministic():
     y1, f1 = _run(x)
     y2, f2 = _run(x)
     assert np.array_equal(y1, y2) and np.array_equal(f1, f2)
+
+
+@pytest.mark.parametrize("L", [700, 130])
+def test_ssd_chained_plan(L):
+    """270 units (3 rows x 90 heads): 256 whole, 14 cut into 8 segments chained through the workspace (L = 130
+    leaves most segments empty).  Equal to the oracle, and bitwise equal to one workgroup per unit (the state is
+    handed on exactly)."""
+    x = I.random_ssd_inputs(np.random.default_rng(770 + L), 3, L, 90, 64, 64)
+    with SsdChained(True):
+        _check(x, f"chained L={L}")
+        yc, fc = _run(x)
+    with SsdChained(False):
+        yu, fu = _run(x)
+    assert np.array_equal(yc, yu) and np.array_equal(fc, fu)
