@@ -14,7 +14,7 @@
 //           + sum_{s<=t} (C_t . B_s) exp(cs_t - cs_s) delta_s x_s        (intra)
 //     H_end = exp(cs_end) H_prev + sum_s exp(cs_end - cs_s) delta_s B_s x_s^T.
 //
-// One workgroup (8 wavefronts) per (batch row, head) walks the chunks in
+// One workgroup (16 wavefronts, 8 for dstate 32) per (batch row, head) walks the chunks in
 // order; the head's state stays in MFMA accumulators (fp32), so no chunk
 // state goes to HBM and x, z, y, B, C are each read or written once.  Per
 // chunk (v_mfma_f32_16x16x32_bf16, bf16 operands, fp32 accumulation):
@@ -83,7 +83,9 @@ __global__ void __launch_bounds__(256) ssd_zero_words_kernel(unsigned* words, in
 
 constexpr int kSsdQ = 64;         // tokens per chunk
 constexpr int kSsdP = 64;         // channels per head
-constexpr int kSsdThreads = 512;  // 8 wavefronts
+// Wavefronts per workgroup: 16 (four per SIMD) where the state has at least
+// 64 tiles of work to share, else 8.
+constexpr int ssd_waves(int N) { return N >= 64 ? 16 : 8; }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -108,18 +110,20 @@ __device__ __forceinline__ void split4(const float* v, u32x2_t& hi, u32x2_t& lo)
 }
 
 template <int N>
-__global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
-  constexpr int Q = kSsdQ, P = kSsdP, NTH = kSsdThreads;
+__global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
+  constexpr int Q = kSsdQ, P = kSsdP, NW = ssd_waves(N), NTH = 64 * NW;
   static_assert(N == 32 || N == 64 || N == 128, "dstate: 32, 64 or 128");
   constexpr int SN = N + 8;  // padded rows (elements) of the [.][N] arrays: 16-byte aligned, banks staggered
   constexpr int SQ = Q + 8;  // padded rows of the [.][Q] arrays
   constexpr int NT = N / 16;  // 16-wide state tiles
-  constexpr int HT = NT / 2;  // state tiles per wavefront (NT x 4 tiles over 8 wavefronts)
+  constexpr int HT = NT * 4 / NW;  // state tiles per wavefront (NT x 4 tiles over NW wavefronts)
+  constexpr int YT = 16 / NW;      // Y tiles per wavefront (4 x 4 over NW wavefronts)
+  constexpr int XI = (Q / 4) * (P / 2);  // x items (4 tokens x 2 channels), one per thread up to XI
   constexpr int C_PIECES = Q * N / 8;         // 16-byte pieces of a chunk's C
   constexpr int C_PER = (C_PIECES + NTH - 1) / NTH;
   constexpr int B_ITEMS = (Q / 4) * (N / 2);  // (4 tokens) x (2 states) items of a chunk's B
   constexpr int B_PER = (B_ITEMS + NTH - 1) / NTH;
-  static_assert((Q / 4) * (P / 2) == NTH, "one x item per thread");
+  static_assert(XI <= NTH && HT >= 1 && YT >= 1, "work split");
   constexpr float kLog2eF = 1.4426950408889634f;
 
   __shared__ __attribute__((aligned(16))) unsigned short sC[Q * SN];   // C [t][n]
@@ -131,15 +135,20 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned short sMl[Q * SQ];  // lo
   __shared__ __attribute__((aligned(16))) unsigned short sHh[P * SN];  // H^T [p][n], hi
   __shared__ __attribute__((aligned(16))) unsigned short sHl[P * SN];  // lo
-  __shared__ __attribute__((aligned(16))) float sCS[Q];                // A * (cumulative step) within the chunk
-  __shared__ __attribute__((aligned(16))) float sDL[Q];                // the step delta_t
+  // per chunk parity: A * (cumulative step) within the chunk, and the step delta_t; wavefront 0
+  // prepares the next chunk's while the others finish the current one
+  __shared__ __attribute__((aligned(16))) float sCS[2][Q];
+  __shared__ __attribute__((aligned(16))) float sDL[2][Q];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lr = lane & 15, lq = lane >> 4;
   const int64_t H = p.H, L = p.L;
-  const int64_t rowe = H * P;  // elements between token rows of x, z, y
+  // elements between token rows of x, z, y; the host keeps every token-row
+  // byte offset (one chunk past L included) below 2^31, so offsets are 32-bit
+  const int rowe = static_cast<int>(H * P);
+  const int H32 = static_cast<int>(H);
 
   // ---- the unit (batch row b, head h) being worked on
   int64_t b = 0, h = 0;
@@ -162,10 +171,11 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
     rs_d = make_rsrc(static_cast<const unsigned short*>(p.delta) + b * L * H + h, (L * H - h) * 2);
   };
 
-  // Work of this wavefront.  Y tiles: token block ty, channel blocks py0, py0+1.
-  const int ty = w & 3, py0 = 2 * (w >> 2);
-  // State tiles: channel block ph, state blocks nb0 + 2i.
+  // Work of this wavefront.  Y tiles: token block ty, channel blocks py0 .. py0+YT-1.
+  const int ty = w & 3, py0 = YT * (w >> 2);
+  // State tiles: channel block ph, state blocks nb0 + (NW/4) i.
   const int ph = w & 3, nb0 = w >> 2;
+  constexpr int NBS = NW / 4;
 
   // Chunk loads (registers): C in 16-byte pieces; B and x four token rows at a
   // time (4-byte pieces: two states / two channels); the raw step; z for this
@@ -173,18 +183,18 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
   u32x4_t gc[C_PER];
   uint32_t gb[B_PER][4], gx[4];
   float graw = 0.0f;
-  unsigned short gz[2][4];
-  auto load_c = [&](int64_t t0) {
+  unsigned short gz[YT][4];
+  auto load_c = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < C_PER; ++i) {
       const int e = tid + NTH * i;
       const int row = e / (N / 8), col = (e % (N / 8)) * 8;
       if (e < C_PIECES)
         gc[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rs_c, static_cast<int>(((t0 + row) * N + col) * 2), 0, 0));
+                                                rs_c, ((t0 + row) * N + col) * 2, 0, 0));
     }
   };
-  auto load_b = [&](int64_t t0) {
+  auto load_b = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
       const int e = tid + NTH * i;
@@ -192,27 +202,29 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
       if (e < B_ITEMS) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          gb[i][r] = __builtin_amdgcn_raw_buffer_load_b32(rs_b, static_cast<int>(((t0 + s0 + r) * N + 2 * np) * 2), 0, 0);
+          gb[i][r] = __builtin_amdgcn_raw_buffer_load_b32(rs_b, ((t0 + s0 + r) * N + 2 * np) * 2, 0, 0);
       }
     }
   };
   const int xpp = tid % (P / 2), xs0 = 4 * (tid / (P / 2));  // x item: channels 2xpp, 2xpp+1 of tokens xs0..xs0+3
-  auto load_x = [&](int64_t t0) {
+  auto load_x = [&](int t0) {
+    if (tid < XI) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      gx[r] = __builtin_amdgcn_raw_buffer_load_b32(rs_x, static_cast<int>(((t0 + xs0 + r) * rowe + 2 * xpp) * 2), 0, 0);
+      for (int r = 0; r < 4; ++r)
+        gx[r] = __builtin_amdgcn_raw_buffer_load_b32(rs_x, ((t0 + xs0 + r) * rowe + 2 * xpp) * 2, 0, 0);
+    }
     if (w == 0)
       graw = bf16_value(static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(
-          rs_d, static_cast<int>((t0 + lane) * H * 2), 0, 0)));
+          rs_d, (t0 + lane) * H32 * 2, 0, 0)));
   };
-  auto load_z = [&](int64_t t0) {
+  auto load_z = [&](int t0) {
     if (!p.z) return;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < YT; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         gz[c][j] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(
-            rs_z, static_cast<int>(((t0 + 16 * ty + 4 * lq + j) * rowe + 16 * (py0 + c) + lr) * 2), 0, 0));
+            rs_z, ((t0 + 16 * ty + 4 * lq + j) * rowe + 16 * (py0 + c) + lr) * 2, 0, 0));
   };
 
   f32x4_t hacc[HT];
@@ -224,28 +236,45 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
       const float v[4] = {hacc[i][0], hacc[i][1], hacc[i][2], hacc[i][3]};
       u32x2_t hi, lo;
       split4(v, hi, lo);
-      const int idx = (16 * ph + lr) * SN + 16 * (nb0 + 2 * i) + 4 * lq;
+      const int idx = (16 * ph + lr) * SN + 16 * (nb0 + NBS * i) + 4 * lq;
       *reinterpret_cast<u32x2_t*>(&sHh[idx]) = hi;
       *reinterpret_cast<u32x2_t*>(&sHl[idx]) = lo;
     }
   };
   // state element (channel, state) of this lane's tile i, entry q
-  auto state_index = [&](int i, int q) { return (16 * ph + lr) * N + 16 * (nb0 + 2 * i) + 4 * lq + q; };
+  auto state_index = [&](int i, int q) { return (16 * ph + lr) * N + 16 * (nb0 + NBS * i) + 4 * lq + q; };
   __shared__ unsigned sWord;
 
   // Chunks kb .. ke-1 of the current unit, from the state in hacc (staged in
   // LDS).  With a stop flag, the run also ends after a chunk once at least
   // k_stop chunks are done and the flag is set (thread 0 polls it, the
   // workgroup reads it through LDS); returns the first chunk not done.
-  auto run_chunks = [&](int64_t kb, int64_t ke, const unsigned* stop_flag, int64_t k_stop) -> int64_t {
+  // (wavefront 0) the steps of the chunk at token t0 from the raw values in
+  // graw, and their cumulative sum times A, into parity buffer `par`
+  auto steps = [&](int t0, int par) {
+    const float xv = graw + biash;
+    float dl = p.softplus ? softplus_f(xv) : xv;
+    dl = (t0 + lane < L) ? dl : 0.0f;  // past the end: no step, no input
+    float cs = dl * Ah;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float up = __shfl_up(cs, o, 64);
+      cs += lane >= o ? up : 0.0f;
+    }
+    sDL[par][lane] = dl;
+    sCS[par][lane] = cs;
+  };
+  auto run_chunks = [&](int kb, int ke, const unsigned* stop_flag, int k_stop) -> int {
   if (ke <= kb) return kb;
   load_c(kb * Q);
   load_b(kb * Q);
   load_x(kb * Q);
-  for (int64_t k = kb; k < ke; ++k) {
-    const int64_t t0 = k * Q;
+  if (w == 0) steps(kb * Q, kb & 1);
+  for (int k = kb; k < ke; ++k) {
+    const int t0 = k * Q;
+    const int par = k & 1;
     load_z(t0);
-    // ---- stage: C and B by token row, x transposed, the steps and their cumulative sums
+    // ---- stage: C and B by token row, x transposed (the steps are ready in parity buffer par)
 #pragma unroll
     for (int i = 0; i < C_PER; ++i) {
       const int e = tid + NTH * i;
@@ -260,25 +289,12 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
         for (int r = 0; r < 4; ++r) *reinterpret_cast<uint32_t*>(&sB[(s0 + r) * SN + 2 * np]) = gb[i][r];
       }
     }
-    {
+    if (tid < XI) {
       // x^T: channel 2xpp takes the low halves of the four rows, 2xpp+1 the high halves
       const u32x2_t even = {(gx[0] & 0xffffu) | (gx[1] << 16), (gx[2] & 0xffffu) | (gx[3] << 16)};
       const u32x2_t odd = {(gx[0] >> 16) | (gx[1] & 0xffff0000u), (gx[2] >> 16) | (gx[3] & 0xffff0000u)};
       *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp) * SQ + xs0]) = even;
       *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp + 1) * SQ + xs0]) = odd;
-    }
-    if (w == 0) {
-      const float xv = graw + biash;
-      float dl = p.softplus ? softplus_f(xv) : xv;
-      dl = (t0 + lane < L) ? dl : 0.0f;  // past the end: no step, no input
-      float cs = dl * Ah;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const float up = __shfl_up(cs, o, 64);
-        cs += lane >= o ? up : 0.0f;
-      }
-      sDL[lane] = dl;
-      sCS[lane] = cs;
     }
     __syncthreads();
     if (k + 1 < ke) {  // in flight through the chunk's products
@@ -289,7 +305,7 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
     // ---- M[t][s] = G[t][s] exp(cs_t - cs_s) delta_s on s <= t, from tiles of G^T = B C^T on or
     // below the diagonal (wavefronts 0 and 1 take two of the ten, the others one), and zero for the
     // two tiles above it that the Y products read
-    for (int gi = w; gi < 12; gi += 8) {
+    for (int gi = w; gi < 12; gi += NW) {
       int gs, gt;
       if (gi < 4) {
         gs = 0;
@@ -317,9 +333,9 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
           const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sC[(16 * gt + lr) * SN + 32 * kk + 8 * lq]);
           g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, g, 0, 0, 0);
         }
-        const float cst = sCS[t];
-        const f32x4_t css = *reinterpret_cast<const f32x4_t*>(&sCS[s0]);
-        const f32x4_t dls = *reinterpret_cast<const f32x4_t*>(&sDL[s0]);
+        const float cst = sCS[par][t];
+        const f32x4_t css = *reinterpret_cast<const f32x4_t*>(&sCS[par][s0]);
+        const f32x4_t dls = *reinterpret_cast<const f32x4_t*>(&sDL[par][s0]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           m[j] = (s0 + j <= t) ? g[j] * __builtin_amdgcn_exp2f((cst - css[j]) * kLog2eF) * dls[j] : 0.0f;
@@ -331,14 +347,14 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
     }
     // ---- W^T[n][s] = exp(cs_end - cs_s) delta_s B[s][n], from the B rows in registers
     {
-      const float cse = sCS[Q - 1];
+      const float cse = sCS[par][Q - 1];
 #pragma unroll
       for (int i = 0; i < B_PER; ++i) {
         const int e = tid + NTH * i;
         if (e < B_ITEMS) {
           const int np = e % (N / 2), s0 = 4 * (e / (N / 2));
-          const f32x4_t css = *reinterpret_cast<const f32x4_t*>(&sCS[s0]);
-          const f32x4_t dls = *reinterpret_cast<const f32x4_t*>(&sDL[s0]);
+          const f32x4_t css = *reinterpret_cast<const f32x4_t*>(&sCS[par][s0]);
+          const f32x4_t dls = *reinterpret_cast<const f32x4_t*>(&sDL[par][s0]);
           float v0[4], v1[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -361,14 +377,14 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
 
     // ---- Y = exp(cs_t) C H + M x  (token block ty, channel blocks py0, py0+1), then the epilogue
     {
-      f32x4_t yacc[2];
+      f32x4_t yacc[YT];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) yacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int c = 0; c < YT; ++c) yacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < N / 32; ++kk) {
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sC[(16 * ty + lr) * SN + 32 * kk + 8 * lq]);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < YT; ++c) {
           const int pr = (16 * (py0 + c) + lr) * SN + 32 * kk + 8 * lq;
           const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&sHh[pr]);
           const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&sHl[pr]);
@@ -376,9 +392,9 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
           yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, yacc[c], 0, 0, 0);
         }
       }
-      const f32x4_t cst = *reinterpret_cast<const f32x4_t*>(&sCS[16 * ty + 4 * lq]);
+      const f32x4_t cst = *reinterpret_cast<const f32x4_t*>(&sCS[par][16 * ty + 4 * lq]);
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < YT; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) yacc[c][j] *= __builtin_amdgcn_exp2f(cst[j] * kLog2eF);
 #pragma unroll
@@ -388,7 +404,7 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
         const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sMh[mr]);
         const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sMl[mr]);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < YT; ++c) {
           const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sXT[(16 * (py0 + c) + lr) * SQ + 32 * kk + 8 * lq]);
           yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, yacc[c], 0, 0, 0);
           yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb, yacc[c], 0, 0, 0);
@@ -396,7 +412,7 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
       }
       // + D x, times SiLU(z), rounded to bf16; x of four consecutive tokens is one 8-byte read of x^T
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < YT; ++c) {
         const int pch = 16 * (py0 + c) + lr;
         const u32x2_t xq = *reinterpret_cast<const u32x2_t*>(&sXT[pch * SQ + 16 * ty + 4 * lq]);
         const float xv[4] = {bf16_lo_of(xq[0]), bf16_hi_of(xq[0]), bf16_lo_of(xq[1]), bf16_hi_of(xq[1])};
@@ -405,15 +421,15 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
           const int t = 16 * ty + 4 * lq + j;
           float v = __builtin_fmaf(Dh, xv[j], yacc[c][j]);
           if (p.z) v *= silu_f(bf16_value(gz[c][j]));
-          __builtin_amdgcn_raw_buffer_store_b16(bf16_bits_of(v), rs_y, static_cast<int>(((t0 + t) * rowe + pch) * 2),
+          __builtin_amdgcn_raw_buffer_store_b16(bf16_bits_of(v), rs_y, ((t0 + t) * rowe + pch) * 2,
                                                 0, 0);
         }
       }
     }
 
-    // ---- H = exp(cs_end) H + W^T x  (channel block ph, state blocks nb0 + 2i)
+    // ---- H = exp(cs_end) H + W^T x  (channel block ph, state blocks nb0 + NBS i)
     {
-      const float fade = __builtin_amdgcn_exp2f(sCS[Q - 1] * kLog2eF);
+      const float fade = __builtin_amdgcn_exp2f(sCS[par][Q - 1] * kLog2eF);
 #pragma unroll
       for (int i = 0; i < HT; ++i)
 #pragma unroll
@@ -423,7 +439,7 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
         const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sXT[(16 * ph + lr) * SQ + 32 * kk + 8 * lq]);
 #pragma unroll
         for (int i = 0; i < HT; ++i) {
-          const int wr = (16 * (nb0 + 2 * i) + lr) * SQ + 32 * kk + 8 * lq;
+          const int wr = (16 * (nb0 + NBS * i) + lr) * SQ + 32 * kk + 8 * lq;
           const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sWh[wr]);
           const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sWl[wr]);
           hacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, hacc[i], 0, 0, 0);
@@ -431,6 +447,7 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
         }
       }
     }
+    if (w == 0 && k + 1 < ke) steps(t0 + Q, par ^ 1);  // the next chunk's raw steps arrived meanwhile
     __syncthreads();  // every read of H^T, x^T, W^T, C, B and M for this chunk is done
     stage_state();      // H^T for the next chunk
     if (stop_flag != nullptr && k + 1 - kb >= k_stop && k + 1 < ke) {
@@ -453,89 +470,87 @@ __global__ void __launch_bounds__(kSsdThreads) ssd_kernel(SsdParams p) {
     }
   };
 
-  const int64_t nchunks = (L + Q - 1) / Q;
-  if (p.n_split == 0) {  // one workgroup per unit
-    set_unit(blockIdx.x);
-#pragma unroll
-    for (int i = 0; i < HT; ++i) hacc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    stage_state();
-    run_chunks(0, nchunks, nullptr, 0);
-    write_final();
-    return;
+  const int nchunks = static_cast<int>((L + Q - 1) / Q);
+  // Which unit and chunks this workgroup runs, as up to three phases that
+  // share one copy of the chunk loop:
+  //   one workgroup per unit:  phase 2 only, unit blockIdx.x, all chunks;
+  //   chained, ticket j:       phase 0 (segment sg > 0 only): unit j from its
+  //                            start until segment sg-1 has handed on its state
+  //                            (after at least sg segment-lengths);
+  //                            phase 1 (left-over units only): segment sg of
+  //                            unit n_long + st, from the state handed on;
+  //                            phase 2: unit j, the rest.
+  // Segment 0 goes first; the whole unit's state waits in registers meanwhile.
+  int j = static_cast<int>(blockIdx.x), sg = 0, st = 0;
+  bool has_seg = false;
+  if (p.n_split > 0) {
+    if (tid == 0) sWord = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    j = static_cast<int>(__builtin_amdgcn_readfirstlane(sWord));
+    __syncthreads();
+    has_seg = j < p.n_split * p.Ks;
+    sg = has_seg ? j / p.n_split : 0;
+    st = has_seg ? j % p.n_split : 0;
   }
-
-  // ---- chained: whole unit j, and segment sg = j / n_split of left-over unit j % n_split.
-  // Segment 0 goes first; segment sg > 0 is spliced in after about sg segment-lengths of the
-  // whole unit, once segment sg-1 (an earlier ticket) has handed on its state.
-  if (tid == 0) sWord = __hip_atomic_fetch_add(p.ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  const int j = static_cast<int>(__builtin_amdgcn_readfirstlane(sWord));
-  __syncthreads();
-  set_unit(j);
-#pragma unroll
-  for (int i = 0; i < HT; ++i) hacc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  stage_state();
-  if (j >= p.n_split * p.Ks) {
-    run_chunks(0, nchunks, nullptr, 0);
-    write_final();
-    return;
-  }
-  const int sg = j / p.n_split, st = j % p.n_split;
-  const int64_t kb = sg * p.seg_chunks < nchunks ? sg * p.seg_chunks : nchunks;
-  const int64_t ke = (sg + 1) * p.seg_chunks < nchunks ? (sg + 1) * p.seg_chunks : nchunks;
-  unsigned* my_flag = p.flags + static_cast<int64_t>(st) * p.Ks + sg;  // set once segment sg-1 is done
-  int64_t rest = 0;
-  if (sg > 0) rest = run_chunks(0, nchunks, my_flag, sg * p.seg_chunks);
+  const int seg_chunks = static_cast<int>(p.seg_chunks);
+  const int kb = sg * seg_chunks < nchunks ? sg * seg_chunks : nchunks;
+  const int ke = (sg + 1) * seg_chunks < nchunks ? (sg + 1) * seg_chunks : nchunks;
+  unsigned* my_flag = has_seg ? p.flags + static_cast<int64_t>(st) * p.Ks + sg : nullptr;  // set once sg-1 is done
+  float* crow = has_seg ? p.carry + (static_cast<int64_t>(st) * p.Ks + sg) * P * N : nullptr;  // [n_split][Ks][P][N]
   f32x4_t saved[HT];
+  int rest = 0;
 #pragma unroll
-  for (int i = 0; i < HT; ++i) saved[i] = hacc[i];
-  set_unit(p.n_long + st);
-  float* crow = p.carry + (static_cast<int64_t>(st) * p.Ks + sg) * P * N;  // [n_split][Ks][P][N]
+  for (int i = 0; i < HT; ++i) saved[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int phase = 0; phase < 3; ++phase) {
+    if (phase == 0 && !(has_seg && sg > 0)) continue;
+    if (phase == 1 && !has_seg) continue;
+    // ---- before the phase: the unit and its starting state
+    set_unit(phase == 1 ? p.n_long + st : j);
 #pragma unroll
-  for (int i = 0; i < HT; ++i) hacc[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  if (sg > 0) {
-    // the state after segment sg-1: wait for its flag, then read it coherently
-    if (tid == 0) {
-      unsigned polls = 0;
-      while (__hip_atomic_load(my_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-        if (++polls > kSsdSpinLimit) {
-          __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
+    for (int i = 0; i < HT; ++i) hacc[i] = phase == 2 ? saved[i] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    if (phase == 1 && sg > 0) {
+      // the state after segment sg-1: wait for its flag, then read it coherently
+      if (tid == 0) {
+        unsigned polls = 0;
+        while (__hip_atomic_load(my_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+          if (++polls > kSsdSpinLimit) {
+            __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
         }
-        __builtin_amdgcn_s_sleep(4);
       }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < HT; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          hacc[i][q] = __hip_atomic_load(crow + state_index(i, q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __syncthreads();
+    stage_state();
+    const int r = run_chunks(phase == 0 ? 0 : (phase == 1 ? kb : rest), phase == 1 ? ke : nchunks,
+                             phase == 0 ? my_flag : nullptr, phase == 0 ? sg * seg_chunks : 0);
+    // ---- after the phase
+    if (phase == 0) {
+      rest = r;
 #pragma unroll
-    for (int i = 0; i < HT; ++i)
+      for (int i = 0; i < HT; ++i) saved[i] = hacc[i];
+    } else if (phase == 1 && sg + 1 < p.Ks) {
+      float* next = crow + P * N;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        hacc[i][q] = __hip_atomic_load(crow + state_index(i, q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < HT; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          __hip_atomic_store(next + state_index(i, q), hacc[i][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(kSsdWaitVm0);  // this thread's carry stores have completed
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_store(p.flags + static_cast<int64_t>(st) * p.Ks + sg + 1, 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      write_final();
+    }
   }
-  stage_state();
-  run_chunks(kb, ke, nullptr, 0);
-  if (sg + 1 < p.Ks) {
-    float* next = crow + P * N;
-#pragma unroll
-    for (int i = 0; i < HT; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        __hip_atomic_store(next + state_index(i, q), hacc[i][q], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(kSsdWaitVm0);  // this thread's carry stores have completed
-    __syncthreads();
-    if (tid == 0)
-      __hip_atomic_store(p.flags + static_cast<int64_t>(st) * p.Ks + sg + 1, 1u, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-  } else {
-    write_final();
-  }
-  // back to the whole unit where it stopped
-  set_unit(j);
-#pragma unroll
-  for (int i = 0; i < HT; ++i) hacc[i] = saved[i];
-  stage_state();
-  run_chunks(rest, nchunks, nullptr, 0);
-  write_final();
 }
 
 }  // namespace ssm

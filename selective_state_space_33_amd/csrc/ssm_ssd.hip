@@ -63,7 +63,7 @@ bool ssd_shape_ok(int64_t L, int64_t heads, int64_t headdim, int64_t dstate, ssm
 
 template <int N>
 hipError_t launch_ssd(const SsdParams& p, unsigned grid, hipStream_t s) {
-  hipLaunchKernelGGL((ssd_kernel<N>), dim3(grid), dim3(kSsdThreads), 0, s, p);
+  hipLaunchKernelGGL((ssd_kernel<N>), dim3(grid), dim3(64 * ssd_waves(N)), 0, s, p);
   return hipGetLastError();
 }
 
