@@ -109,6 +109,7 @@ constexpr int kModeFull = 0;     // whole tiles, and chunks of split tiles from 
 constexpr int kModeAgg = 1;      // chunk pairs (P, S) of chunks 0..Ks-2 of every split tile
 constexpr int kModeChained = 2;  // one workgroup per CU: a whole tile with one chunk of a left-over tile spliced in
 constexpr int kModeCkpt = 3;     // whole tiles, no readout: the state entering every block (for the backward pass)
+constexpr int kModeChainedCkpt = 4;  // kModeChained's plan with kModeCkpt's work (no readout, checkpoints)
 
 // Discretisation rules of scan_kernel.
 constexpr int kRuleEuler = 0;    // h_t = exp(delta_t A) h_{t-1} + delta_t B_t u_t
@@ -233,8 +234,11 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   static_assert(kRing % 2 == 0, "ring slots keep their block parity");
   constexpr int ES = __is_same(IO, F32) ? 4 : 2;  // bytes per stored element
   constexpr bool HAS_FULL = MODE == kModeFull || MODE == kModeChained;  // a readout pass runs in this launch
+  constexpr bool CHAINED = MODE == kModeChained || MODE == kModeChainedCkpt;
+  constexpr bool CKPT = MODE == kModeCkpt || MODE == kModeChainedCkpt;
+  static_assert(HAS_FULL || G <= TB_, "stop-flag words in the partial-readout buffer");
   constexpr bool TRAP = RULE == kRuleTrap;
-  static_assert(!TRAP || MODE != kModeCkpt, "the backward's checkpoints are of the two-term rule");
+  static_assert(!TRAP || !CKPT, "the backward's checkpoints are of the two-term rule");
 
   // Double-buffered by block parity.  (delta, delta*u) per token, channel;
   // (delta, u/2) with the trapezoidal rule.
@@ -289,8 +293,9 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     }
     // packed B/C records of this wavefront's state group, from the stretch's first token
     bc_row = p.bc + ((b * G + w) * p.Lp + t_begin) * (2 * NPL);
-    if constexpr (MODE == kModeCkpt)
-      ckpt_row = p.ckpt + (static_cast<int64_t>(tile) * p.ckpt_blocks * 64 + lane) * NPAD + n0;
+    if constexpr (CKPT)  // from the stretch's first block (a chunk starts on a block boundary)
+      ckpt_row = p.ckpt + (static_cast<int64_t>(tile) * p.ckpt_blocks * 64 + lane) * NPAD + n0 +
+                 (t_begin / TB) * 64 * NPAD;
     // the records run on for kTBMax rows of padding past Lp
     rs_bc = make_rsrc(bc_row, (p.Lp + kTBMax - t_begin) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
     pd = d0 + pcol;
@@ -587,7 +592,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       constexpr int Sp1 = (S + 1) % kRing;          // block k+1
       static_assert((S + kPD + 1) % kRing == Sm1, "ring");
       IC<P> parc;
-      if constexpr (MODE == kModeCkpt) {
+      if constexpr (CKPT) {
         // the state entering block k (the padding blocks at the end have room too)
 #pragma unroll
         for (int j = 0; j < NPL; ++j) ckpt_row[static_cast<int64_t>(k) * 64 * NPAD + j] = h[j];
@@ -626,22 +631,25 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       [&]<int... I>(std::integer_sequence<int, I...>) {
         (iteration(IC<I>{}, k + I), ...);
       }(std::make_integer_sequence<int, kRing>{});
-      if constexpr (HAS_FULL) {
-        if (poll) {
-          // Thread 0 hands the flag to every wavefront through that
-          // wavefront's own word of the parity-0 partial readouts: the buffer
-          // is free at a trip boundary (its last reader, the epilogue in the
-          // trip's last block, is behind the barrier), and wavefront w next
-          // writes its word in the following block's scan, after reading it.
-          if (tid == 0) {
+      if (poll) {
+        // Thread 0 hands the flag to every wavefront through that wavefront's
+        // own word of the parity-0 partial readouts: the buffer is free at a
+        // trip boundary (its last reader, the epilogue in the trip's last
+        // block, is behind the barrier), and wavefront w next writes its word
+        // in the following block's scan, after reading it.  Launches without
+        // a readout never write that buffer otherwise.
+        auto word = [&](int ww) -> float& {
+          if constexpr (HAS_FULL) return sY[0][ww][TB - 1][63];
+          else return sY[0][0][ww][63];
+        };
+        if (tid == 0) {
 #pragma unroll
-            for (int ww = 0; ww < G; ++ww) sY[0][ww][TB - 1][63] = __builtin_bit_cast(float, seen);
-          }
-          __syncthreads();
-          if (__builtin_bit_cast(unsigned, sY[0][w][TB - 1][63]) != 0u) {
-            k_end = k + kRing;
-            break;
-          }
+          for (int ww = 0; ww < G; ++ww) word(ww) = __builtin_bit_cast(float, seen);
+        }
+        __syncthreads();
+        if (__builtin_bit_cast(unsigned, word(w)) != 0u) {
+          k_end = k + kRing;
+          break;
         }
       }
     }
@@ -673,7 +681,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     }
   };
 
-  if constexpr (MODE == kModeChained) {
+  if constexpr (CHAINED) {
+    constexpr bool FULLC = MODE == kModeChained;  // the chained checkpoint pass has no readout
     // One workgroup per CU.  Ticket j (the order workgroups start) owns
     // whole tile j and, for j < n_split * Ks, chunk c = j / n_split of
     // left-over tile n_long + j % n_split.  Chunk 0 runs first; chunk c > 0
@@ -690,7 +699,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     int nb_whole = stretch_blocks();
     const bool has_chunk = j < p.n_split * p.Ks;
     if (!has_chunk) {
-      run_pass(IC<true>{}, 0, nb_whole);
+      run_pass(IC<FULLC>{}, 0, nb_whole);
       write_final_state(b);
       return;
     }
@@ -705,7 +714,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     unsigned* my_flag = p.flags + static_cast<int64_t>(st) * p.Ks + c;
     if (c > 0) {
       m = nb_whole;
-      run_pass(IC<true>{}, 0, m, my_flag, c * nb_chunk);
+      run_pass(IC<FULLC>{}, 0, m, my_flag, c * nb_chunk);
     }
     float hw[NPL];
 #pragma unroll
@@ -740,7 +749,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       }
     }
     int nbc = nb_chunk;
-    run_pass(IC<true>{}, 0, nbc);
+    run_pass(IC<FULLC>{}, 0, nbc);
     if (c + 1 < p.Ks) {
       if (dvalid) {
 #pragma unroll
@@ -759,7 +768,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     set_tile(j, 0, L);
 #pragma unroll
     for (int q = 0; q < NPL; ++q) h[q] = hw[q];
-    run_pass(IC<true>{}, m, nb_whole);
+    run_pass(IC<FULLC>{}, m, nb_whole);
     write_final_state(b);
   } else {
     // ---- which tile and which part of the sequence this workgroup scans

@@ -18,7 +18,7 @@ namespace ssm {
 template <class IO, int MODE, int RULE = kRuleEuler>
 hipError_t launch_scan(int npl, int G, int vw, int tb, const ScanParams& p, dim3 grid, hipStream_t s);
 
-// Instantiated (each in its own translation unit) for these fourteen combinations.
+// Instantiated (each in its own translation unit) for these sixteen combinations.
 extern template hipError_t launch_scan<F32, kModeFull>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<F32, kModeAgg>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<F32, kModeChained>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
@@ -26,6 +26,10 @@ extern template hipError_t launch_scan<BF16, kModeFull>(int, int, int, int, cons
 extern template hipError_t launch_scan<BF16, kModeAgg>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<F32, kModeCkpt>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<BF16, kModeCkpt>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
+extern template hipError_t launch_scan<F32, kModeChainedCkpt>(int, int, int, int, const ScanParams&, dim3,
+                                                             hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeChainedCkpt>(int, int, int, int, const ScanParams&, dim3,
+                                                              hipStream_t);
 extern template hipError_t launch_scan<BF16, kModeChained>(int, int, int, int, const ScanParams&,
                                                            dim3, hipStream_t);
 extern template hipError_t launch_scan<F32, kModeFull, kRuleTrap>(int, int, int, int, const ScanParams&, dim3,

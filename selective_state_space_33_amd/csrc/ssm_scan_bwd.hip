@@ -38,6 +38,9 @@ struct BwdPlan {
   int npl, G;
   int64_t Lp, ntd, T, ckpt_blocks;
   int n_long, n_split, Ks, chunk_blocks;
+  // the checkpoint pass, chained alike: Kc chunks of ck_len tokens per left-over tile
+  int Kc;
+  int64_t ck_len;
 };
 
 BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
@@ -52,6 +55,8 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
   pl.n_split = 0;
   pl.Ks = 1;
   pl.chunk_blocks = 0;
+  pl.Kc = 1;
+  pl.ck_len = 0;
   const char* env = getenv("SSM_BWD_CHAINED");
   const bool chained_ok = !(env && atoi(env) == 0);
   if (chained_ok && pl.T > kBwdNumCU && 2 * (pl.T - kBwdNumCU) <= kBwdNumCU) {
@@ -62,15 +67,19 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
     pl.n_split = static_cast<int>(r);
     pl.Ks = static_cast<int>(K);
     pl.chunk_blocks = static_cast<int>(cdiv(cdiv(L, kBwdTB), K));
+    // the forward's chained plan for the checkpoints: chunk lengths in whole trips of its loop
+    pl.Kc = static_cast<int>(kBwdNumCU / r);
+    pl.ck_len = cdiv(cdiv(L, pl.Kc), kTrip) * kTrip;
   }
   return pl;
 }
 
 // Workspace: [packed B/C][checkpoints][dB, dC partials][dA, dD, dbias
-// partials (Ks slots)][carried adjoints][flags, ticket, status].
+// partials (Ks slots)][carried adjoints][carried checkpoint-pass states]
+// [flags, ticket, status of the backward; the same of the checkpoint pass].
 struct BwdLayout {
-  size_t bc, ckpt, bcpart, apart, dpart, carry, words, total;
-  int n_words;
+  size_t bc, ckpt, bcpart, apart, dpart, carry, ckcarry, words, total;
+  int n_words, bwd_words;
 };
 
 BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t dim) {
@@ -83,9 +92,11 @@ BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t dim) {
   l.apart = al256(static_cast<size_t>(slots * batch * dim) * npad * sizeof(float));
   l.dpart = al256(static_cast<size_t>(slots * batch * dim) * sizeof(float));
   l.carry = al256(static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float));
-  l.n_words = pl.n_split > 0 ? pl.n_split * pl.Ks + 2 : 0;
+  l.ckcarry = al256(static_cast<size_t>(pl.n_split) * pl.Kc * 64 * npad * sizeof(float));
+  l.bwd_words = pl.n_split > 0 ? pl.n_split * pl.Ks + 2 : 0;
+  l.n_words = pl.n_split > 0 ? l.bwd_words + pl.n_split * pl.Kc + 2 : 0;
   l.words = al256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
-  l.total = l.bc + l.ckpt + 2 * l.bcpart + l.apart + 2 * l.dpart + l.carry + l.words;
+  l.total = l.bc + l.ckpt + 2 * l.bcpart + l.apart + 2 * l.dpart + l.carry + l.ckcarry + l.words;
   return l;
 }
 
@@ -107,7 +118,10 @@ hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const
                        pl.G, bp.flags, lay.n_words, static_cast<float*>(nullptr));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  e = launch_scan<IO, kModeCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.T)), s);
+  if (pl.n_split > 0)
+    e = launch_scan<IO, kModeChainedCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.n_long)), s);
+  else
+    e = launch_scan<IO, kModeCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.T)), s);
   if (e != hipSuccess) return e;
   const dim3 bgrid(static_cast<unsigned>(pl.n_split > 0 ? pl.n_long : pl.T));
   if (pl.npl == 2)
@@ -190,7 +204,8 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   float* dbias_part = reinterpret_cast<float*>(ws + lay.bc + lay.ckpt + 2 * lay.bcpart + lay.apart + lay.dpart);
   char* tail = ws + lay.bc + lay.ckpt + 2 * lay.bcpart + lay.apart + 2 * lay.dpart;
   float* carry = lay.carry ? reinterpret_cast<float*>(tail) : nullptr;
-  unsigned* words = lay.n_words ? reinterpret_cast<unsigned*>(tail + lay.carry) : nullptr;
+  float* ckcarry = lay.ckcarry ? reinterpret_cast<float*>(tail + lay.carry) : nullptr;
+  unsigned* words = lay.n_words ? reinterpret_cast<unsigned*>(tail + lay.carry + lay.ckcarry) : nullptr;
 
   ScanParams sp = {};
   sp.u = u;
@@ -211,6 +226,16 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   sp.ckpt = ckpt;
   sp.ckpt_blocks = pl.ckpt_blocks;
   sp.h0 = initial_state;
+  if (pl.n_split > 0) {  // the checkpoint pass chained like the forward
+    sp.n_long = pl.n_long;
+    sp.n_split = pl.n_split;
+    sp.Ks = pl.Kc;
+    sp.chunk_len = pl.ck_len;
+    sp.carry = ckcarry;
+    sp.flags = words + lay.bwd_words;
+    sp.ticket = sp.flags + static_cast<int64_t>(pl.n_split) * pl.Kc;
+    sp.status = sp.ticket + 1;
+  }
 
   BwdParams bp = {};
   bp.u = u;
