@@ -132,6 +132,45 @@ def time_calls(fn, steps, warmup, stream):
     return start.elapsed_time(end) / steps, wall / steps * 1e3
 
 
+def time_cold_calls(fn, calls, stream, flush_bytes=1 << 30):
+    """Per-call times (ms) with the caches flushed before every call.
+
+    A read over a 1 GiB buffer, outside the events, evicts the inputs from L2 and the 256 MB
+    Infinity Cache, so each call reads them from HBM.  It reads rather than writes so that the
+    call does not start with the flush's own dirty lines still waiting to be written back.
+    Returns min, p10, median, p90."""
+    import numpy as np
+    import torch
+
+    buf = torch.ones(flush_bytes // 4, dtype=torch.float32, device=stream.device)
+    fn()
+    times = []
+    for _ in range(calls):
+        buf.sum()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        fn()
+        end.record(stream)
+        end.synchronize()
+        times.append(start.elapsed_time(end))
+    del buf
+    t = np.asarray(times)
+    return {"calls": calls, "flush_bytes": flush_bytes, "ms_min": float(t.min()), "ms_p10": float(np.percentile(t, 10)),
+            "ms_median": float(np.median(t)), "ms_p90": float(np.percentile(t, 90))}
+
+
+def copy_bandwidth(dev, stream, nbytes=1 << 30, steps=20):
+    """Device-to-device copy rate of a plain 1 GiB copy, counting bytes read plus bytes written (GB/s)."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    ms, _ = time_calls(lambda: dst.copy_(src), steps, 5, stream)
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def cpu_baseline(w, x, budget_s):
     """The fp64 oracle on the first channels of every batch row (full sequence), sized to ~budget_s of wall time.
 
@@ -183,6 +222,7 @@ def main():
     ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--packed-mean-len", type=float, default=1024.0,
                     help="mean sequence length of the packed row (log-normal lengths, sigma 1)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the per-call timings with flushed caches")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the scan, time a plain device copy of this many MiB (calibrates HBM counters)")
     args = ap.parse_args()
@@ -259,6 +299,16 @@ def main():
                 "frac": achieved_gbs / HBM_PEAK_GBS},
     }
 
+    if not args.no_cold:
+        # Each call on its own, after a cache flush: the inputs come from HBM, never from the Infinity Cache.
+        cold = time_cold_calls(step, max(args.steps, 20), stream)
+        copy_gbs = copy_bandwidth(dev, stream)
+        med_gbs = nbytes / (cold["ms_median"] * 1e-3) / 1e9
+        out["cold"] = dict(cold, hbm_achieved=med_gbs, hbm_frac=med_gbs / HBM_PEAK_GBS,
+                           updates_per_s=w.updates / (cold["ms_median"] * 1e-3))
+        out["copy_bandwidth"] = {"achieved": copy_gbs, "unit": "GB/s", "bytes_each_way": 1 << 30,
+                                 "scan_frac_of_copy": achieved_gbs / copy_gbs}
+
     if not args.no_decode:
         wd = I.WORKLOADS["decode_bf16"]
         xd = I.make_inputs(wd, 0)
@@ -277,6 +327,12 @@ def main():
                          "roofline": {"bound": "hbm", "achieved": db / (dms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
                                       "unit": "GB/s", "frac": db / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                                       "algorithmic_bytes": db, "traffic": measured_traffic(wd.name)}}
+        if not args.no_cold:
+            # 179 MB fits the Infinity Cache, so back-to-back steps can hit it; flushed steps cannot
+            dcold = time_cold_calls(dstep, max(args.steps, 20), stream)
+            dgbs = db / (dcold["ms_median"] * 1e-3) / 1e9
+            out["decode"]["cold"] = dict(dcold, hbm_achieved=dgbs, hbm_frac=dgbs / HBM_PEAK_GBS,
+                                         frac_of_copy=dgbs / out["copy_bandwidth"]["achieved"])
         del gd, yd, state
 
     if not args.no_backward:
