@@ -174,7 +174,8 @@ def copy_bandwidth(dev, stream, nbytes=1 << 30, steps=20):
 def cpu_baseline(w, x, budget_s):
     """The fp64 oracle on the first channels of every batch row (full sequence), sized to ~budget_s of wall time.
 
-    When the whole workload fits in the budget it is run whole, once.
+    Timed with one thread per host core (up to 16) and, on a smaller sample, with one thread.  When the whole
+    workload fits in the budget it is run whole, repeatedly, and the median run is reported.
     """
     import numpy as np
 
@@ -182,28 +183,42 @@ def cpu_baseline(w, x, budget_s):
 
     threads = max(1, min(16, os.cpu_count() or 1))
 
-    def run(nch):
+    def run(nch, nthreads):
         sub = dict(u=x["u"][:, :, :nch], delta=x["delta"][:, :, :nch],
                    z=None if x["z"] is None else x["z"][:, :, :nch], B=x["B"], C=x["C"],
                    A=x["A"][:nch], D=x["D"][:nch], delta_bias=x["delta_bias"][:nch])
         sub = {k: (None if v is None else np.ascontiguousarray(v, dtype=np.float64)) for k, v in sub.items()}
         t0 = time.perf_counter()
         R.scan_fwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], D=sub["D"], z=sub["z"],
-                   delta_bias=sub["delta_bias"], nthreads=threads)
+                   delta_bias=sub["delta_bias"], nthreads=nthreads)
         return time.perf_counter() - t0
 
     per_channel = w.batch * w.L * w.dstate
     probe = min(w.dim, max(1, threads // max(1, w.batch)) * 4)
-    dt = run(probe)
+    dt = run(probe, threads)
     rate = probe * per_channel / dt
-    nch = int(min(w.dim, max(probe, budget_s * rate / per_channel)))
-    dt = run(nch)
+    nch = int(min(w.dim, max(probe, 0.8 * budget_s * rate / per_channel)))
+    runs = [run(nch, threads)]
+    while nch == w.dim and sum(runs) < 0.6 * budget_s and len(runs) < 50:
+        runs.append(run(nch, threads))
+    dt = float(np.median(runs))
     ups = nch * per_channel / dt
+    # one thread, on a sample sized to ~15% of the budget
+    nch1 = int(min(w.dim, max(1, 0.15 * budget_s * (rate / threads) / per_channel)))
+    dt1 = run(nch1, 1)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "")
+    except OSError:
+        pass
     what = "the whole workload" if nch == w.dim else f"channels 0..{nch - 1} of every batch row"
     return {"value": ups, "unit": "updates/s", "cores": threads, "kind": "oracle",
+            "single_thread_value": nch1 * per_channel / dt1, "cpu_model": model,
             "sample": f"{w.name}: {what}, all {w.L} tokens, dstate {w.dstate} "
-                      f"({nch * per_channel:.3e} updates in {dt:.2f} s; fp64 sequential recurrence, "
-                      f"{threads} threads over channels)"}
+                      f"({nch * per_channel:.3e} updates, median of {len(runs)} runs of {dt:.2f} s; fp64 "
+                      f"sequential recurrence, {threads} threads over channels); single thread: channels "
+                      f"0..{nch1 - 1} of every batch row ({nch1 * per_channel:.3e} updates in {dt1:.2f} s)"}
 
 
 def main():
