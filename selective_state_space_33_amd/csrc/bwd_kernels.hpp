@@ -138,8 +138,12 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   __shared__ float2 sDU[TB][64];             // (Delta, Delta*u)
   __shared__ float sDV[TB][64];              // dv
   __shared__ float2 sYS[G][TB][64];          // readout partials (.x), then (sum t_a A, sum dh B)
-  __shared__ float sRB[TB][NPAD][16];        // dB partials: one sum per group of 4 lanes
-  __shared__ float sRC[TB][NPAD][16];
+  // dB, dC partials: one sum per group of 4 lanes, 16 per (token, state), in
+  // rows of 20 floats where LDS allows (so that the 16-byte reads of
+  // consecutive rows in the reduction below fall on distinct banks)
+  constexpr int RROW = NPL <= 2 ? 20 : 16;
+  __shared__ float sRB[TB][NPAD][RROW];
+  __shared__ float sRC[TB][NPAD][RROW];
   __shared__ float sAcc[2][G][64];
   __shared__ unsigned sWord;
 
