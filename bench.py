@@ -114,12 +114,19 @@ def gpu_inputs(x, dtype, dev):
                 D=t(x["D"], True), delta_bias=t(x["delta_bias"], True), h0=t(x.get("h0"), True))
 
 
-def time_calls(fn, steps, warmup, stream):
+def time_calls(fn, steps, warmup, stream, min_warm_ms=150.0):
+    """Average ms per call of `steps` back-to-back calls, after `warmup` calls and at least
+    min_warm_ms of warm-up work (the GPU clock takes ~100 ms of load to settle)."""
     import torch
 
+    t_w = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while (time.perf_counter() - t_w) * 1e3 < min_warm_ms:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()

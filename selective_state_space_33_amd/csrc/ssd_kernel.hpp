@@ -131,6 +131,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned short sWh[N * SQ];  // W^T [n][s], hi
   __shared__ __attribute__((aligned(16))) unsigned short sWl[N * SQ];  // lo
   __shared__ __attribute__((aligned(16))) unsigned short sXT[P * SQ];  // x^T [p][s]
+  __shared__ __attribute__((aligned(16))) unsigned short sZT[P * SQ];  // z^T [p][t]
   __shared__ __attribute__((aligned(16))) unsigned short sMh[Q * SQ];  // M [t][s], hi
   __shared__ __attribute__((aligned(16))) unsigned short sMl[Q * SQ];  // lo
   __shared__ __attribute__((aligned(16))) unsigned short sHh[P * SN];  // H^T [p][n], hi
@@ -177,13 +178,13 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   const int ph = w & 3, nb0 = w >> 2;
   constexpr int NBS = NW / 4;
 
-  // Chunk loads (registers): C in 16-byte pieces; B and x four token rows at a
-  // time (4-byte pieces: two states / two channels); the raw step; z for this
-  // wavefront's Y tiles.
+  // Chunk loads (registers), one chunk ahead: C in 16-byte pieces; B, x and z
+  // four token rows at a time (4-byte pieces: two states / two channels); the
+  // raw step.  x and z are staged transposed, so that the epilogue reads the
+  // z of four consecutive tokens as one 8-byte piece.
   u32x4_t gc[C_PER];
-  uint32_t gb[B_PER][4], gx[4];
+  uint32_t gb[B_PER][4], gx[4], gzz[4];
   float graw = 0.0f;
-  unsigned short gz[YT][4];
   auto load_c = [&](int t0) {
 #pragma unroll
     for (int i = 0; i < C_PER; ++i) {
@@ -212,21 +213,16 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         gx[r] = __builtin_amdgcn_raw_buffer_load_b32(rs_x, ((t0 + xs0 + r) * rowe + 2 * xpp) * 2, 0, 0);
+      if (p.z) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          gzz[r] = __builtin_amdgcn_raw_buffer_load_b32(rs_z, ((t0 + xs0 + r) * rowe + 2 * xpp) * 2, 0, 0);
+      }
     }
     if (w == 0)
       graw = bf16_value(static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(
           rs_d, (t0 + lane) * H32 * 2, 0, 0)));
   };
-  auto load_z = [&](int t0) {
-    if (!p.z) return;
-#pragma unroll
-    for (int c = 0; c < YT; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        gz[c][j] = static_cast<unsigned short>(__builtin_amdgcn_raw_buffer_load_b16(
-            rs_z, ((t0 + 16 * ty + 4 * lq + j) * rowe + 16 * (py0 + c) + lr) * 2, 0, 0));
-  };
-
   f32x4_t hacc[HT];
   // H^T as bf16 pairs for the Y products, from the accumulators: four
   // consecutive states of one channel per lane (this wavefront's tiles only)
@@ -273,7 +269,6 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   for (int k = kb; k < ke; ++k) {
     const int t0 = k * Q;
     const int par = k & 1;
-    load_z(t0);
     // ---- stage: C and B by token row, x transposed (the steps are ready in parity buffer par)
 #pragma unroll
     for (int i = 0; i < C_PER; ++i) {
@@ -295,6 +290,12 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       const u32x2_t odd = {(gx[0] >> 16) | (gx[1] & 0xffff0000u), (gx[2] >> 16) | (gx[3] & 0xffff0000u)};
       *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp) * SQ + xs0]) = even;
       *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp + 1) * SQ + xs0]) = odd;
+      if (p.z) {
+        *reinterpret_cast<u32x2_t*>(&sZT[(2 * xpp) * SQ + xs0]) =
+            u32x2_t{(gzz[0] & 0xffffu) | (gzz[1] << 16), (gzz[2] & 0xffffu) | (gzz[3] << 16)};
+        *reinterpret_cast<u32x2_t*>(&sZT[(2 * xpp + 1) * SQ + xs0]) =
+            u32x2_t{(gzz[0] >> 16) | (gzz[1] & 0xffff0000u), (gzz[2] >> 16) | (gzz[3] & 0xffff0000u)};
+      }
     }
     __syncthreads();
     if (k + 1 < ke) {  // in flight through the chunk's products
@@ -416,11 +417,14 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
         const int pch = 16 * (py0 + c) + lr;
         const u32x2_t xq = *reinterpret_cast<const u32x2_t*>(&sXT[pch * SQ + 16 * ty + 4 * lq]);
         const float xv[4] = {bf16_lo_of(xq[0]), bf16_hi_of(xq[0]), bf16_lo_of(xq[1]), bf16_hi_of(xq[1])};
+        u32x2_t zq = {0u, 0u};
+        if (p.z) zq = *reinterpret_cast<const u32x2_t*>(&sZT[pch * SQ + 16 * ty + 4 * lq]);
+        const float zv[4] = {bf16_lo_of(zq[0]), bf16_hi_of(zq[0]), bf16_lo_of(zq[1]), bf16_hi_of(zq[1])};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = 16 * ty + 4 * lq + j;
           float v = __builtin_fmaf(Dh, xv[j], yacc[c][j]);
-          if (p.z) v *= silu_f(bf16_value(gz[c][j]));
+          if (p.z) v *= silu_f(zv[j]);
           __builtin_amdgcn_raw_buffer_store_b16(bf16_bits_of(v), rs_y, ((t0 + t) * rowe + pch) * 2,
                                                 0, 0);
         }
