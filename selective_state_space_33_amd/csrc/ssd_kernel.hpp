@@ -303,6 +303,25 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       load_x(t0 + Q);
     }
 
+    // ---- Y (inter-chunk part) = C H for token block ty, channel blocks py0.. (from the state
+    // staged at the end of the last chunk).  Issued ahead of the M and W work below, which does
+    // not depend on it, so that the matrix cores run under that vector work.
+    f32x4_t yacc[YT];
+#pragma unroll
+    for (int c = 0; c < YT; ++c) yacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < N / 32; ++kk) {
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sC[(16 * ty + lr) * SN + 32 * kk + 8 * lq]);
+#pragma unroll
+      for (int c = 0; c < YT; ++c) {
+        const int pr = (16 * (py0 + c) + lr) * SN + 32 * kk + 8 * lq;
+        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&sHh[pr]);
+        const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&sHl[pr]);
+        yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, yacc[c], 0, 0, 0);
+        yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, yacc[c], 0, 0, 0);
+      }
+    }
+
     // ---- M[t][s] = G[t][s] exp(cs_t - cs_s) delta_s on s <= t, from tiles of G^T = B C^T on or
     // below the diagonal (wavefronts 0 and 1 take two of the ten, the others one), and zero for the
     // two tiles above it that the Y products read
@@ -378,21 +397,6 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
 
     // ---- Y = exp(cs_t) C H + M x  (token block ty, channel blocks py0, py0+1), then the epilogue
     {
-      f32x4_t yacc[YT];
-#pragma unroll
-      for (int c = 0; c < YT; ++c) yacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kk = 0; kk < N / 32; ++kk) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sC[(16 * ty + lr) * SN + 32 * kk + 8 * lq]);
-#pragma unroll
-        for (int c = 0; c < YT; ++c) {
-          const int pr = (16 * (py0 + c) + lr) * SN + 32 * kk + 8 * lq;
-          const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&sHh[pr]);
-          const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&sHl[pr]);
-          yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, yacc[c], 0, 0, 0);
-          yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, yacc[c], 0, 0, 0);
-        }
-      }
       const f32x4_t cst = *reinterpret_cast<const f32x4_t*>(&sCS[par][16 * ty + 4 * lq]);
 #pragma unroll
       for (int c = 0; c < YT; ++c)
