@@ -137,7 +137,12 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
 
   __shared__ float2 sDU[TB][64];             // (Delta, Delta*u)
   __shared__ float sDV[TB][64];              // dv
-  __shared__ float2 sYS[G][TB][64];          // readout partials (.x), then (sum t_a A, sum dh B)
+  __shared__ float2 sYS[G][TB][64];          // (sum t_a A, sum dh B); the readout partials (.x) too unless SEP
+  // Where LDS allows (2 states per lane), the readout partials have an array of
+  // their own, so that the adjoint pass may overwrite sYS while v is still being
+  // summed: E1 and R then share one phase.
+  constexpr bool SEP = NPL <= 2;
+  __shared__ float sYP[SEP ? G : 1][SEP ? TB : 1][64];
   // dB, dC partials: one sum per group of 4 lanes, 16 per (token, state), in
   // rows of 20 floats where LDS allows (so that the 16-byte reads of
   // consecutive rows in the reduction below fall on distinct banks)
@@ -303,7 +308,8 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
               }()),
               ...);
            }(std::make_integer_sequence<int, NPL>{});
-           sYS[w][t][lane].x = yp;
+           if constexpr (SEP) sYP[w][t][lane] = yp;
+           else sYS[w][t][lane].x = yp;
          }()),
          ...);
       }(std::make_integer_sequence<int, TB>{});
@@ -314,9 +320,9 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = w + i * G;
-      float v = sYS[0][row][lane].x;
+      float v = SEP ? sYP[0][row][lane] : sYS[0][row][lane].x;
 #pragma unroll
-      for (int ww = 1; ww < G; ++ww) v += sYS[ww][row][lane].x;
+      for (int ww = 1; ww < G; ++ww) v += SEP ? sYP[ww][row][lane] : sYS[ww][row][lane].x;
       v = __builtin_fmaf(Dd, eu[i], v);
       if (has_z) {
         const float dzv = egz[i] * v;
@@ -324,7 +330,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
         buf_store<IO, 1>(rs_dz, off, 0, &dzv);
       }
     }
-    __syncthreads();
+    if constexpr (!SEP) __syncthreads();  // R overwrites the partials just read
 
     // ---- R: the adjoint back through the block
     [&]<int... T>(std::integer_sequence<int, T...>) {
@@ -405,7 +411,9 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       p.dB_part[o] = sb;
       p.dC_part[o] = sc;
     }
-    __syncthreads();
+    // No barrier here: the next block's P writes only sDU and sDV, whose last
+    // readers (R) finished at the barrier before E2, and its F writes the
+    // partials only after the barrier that follows P.
   };
 
   // Blocks ke-1 down to kb.  With a stop flag, the run also ends after a pair
