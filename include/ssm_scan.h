@@ -48,6 +48,12 @@
  *     Nothing is launched in either case.  A failed launch gives
  *     SSM_ERR_HIP.
  *     Input values are not inspected (NaN in gives NaN out).
+ *   - Where a plan chains pieces of one sequence through the workspace (a
+ *     piece starts from the state, or adjoint, that the piece before it
+ *     hands on), each wait is bounded (about a third of a second).  Past the
+ *     bound the piece goes on from NaN, so the outputs that depend on the
+ *     lost hand-off are NaN rather than silently wrong; it does not happen
+ *     on a GPU that runs the call's workgroups.
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H

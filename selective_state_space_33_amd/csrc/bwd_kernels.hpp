@@ -99,7 +99,8 @@ struct BwdParams {
 constexpr int kBwdTB = 16;  // tokens per block (the checkpoint spacing)
 // A chained chunk waits for the adjoint handed on to it for at most this many
 // polls (each after a short sleep); past that it records an error bit in the
-// status word and goes on from what it read, so the kernel always ends.
+// status word and goes on from a NaN adjoint, so the kernel always ends and
+// the gradients that depend on the lost hand-off show the failure.
 constexpr unsigned kBwdSpinLimit = 1u << 18;
 // vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 s_waitcnt encoding).
 constexpr int kBwdWaitVm0 = 0x0F70;
@@ -531,10 +532,12 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       }
     }
     __syncthreads();
+    const bool lost = __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
     if (dvalid) {
 #pragma unroll
       for (int q = 0; q < NPL; ++q)
-        dhn[q] = __hip_atomic_load(p.carry + crow * NPAD + n0 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        dhn[q] = lost ? __builtin_nanf("")
+                      : __hip_atomic_load(p.carry + crow * NPAD + n0 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   run_blocks(kb, ke, nullptr, 0);

@@ -117,7 +117,8 @@ constexpr int kRuleTrap = 1;     // the trapezoidal three-term recurrence (Mamba
 
 // A workgroup waits for the state carried into its chunk for at most this
 // many polls (each after a short sleep); past that it records an error in
-// the status word and goes on from a zero state, so the kernel always ends.
+// the status word and goes on from a NaN state, so the kernel always ends and
+// the outputs that depend on the lost hand-off show the failure.
 constexpr unsigned kSpinLimit = 1u << 18;
 constexpr unsigned kStatusCarryTimeout = 1u;
 
@@ -742,10 +743,12 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
         }
       }
       __syncthreads();
+      const bool lost = __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
       if (dvalid) {
 #pragma unroll
         for (int q = 0; q < NPL; ++q)
-          h[q] = __hip_atomic_load(p.carry + crow * NPAD + n0 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          h[q] = lost ? __builtin_nanf("")
+                      : __hip_atomic_load(p.carry + crow * NPAD + n0 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     int nbc = nb_chunk;

@@ -72,7 +72,8 @@ struct SsdParams {
 
 // A chained segment waits for the state handed on to it for at most this
 // many polls (each after a short sleep); past that it records an error bit in
-// the status word and goes on, so the kernel always ends.
+// the status word and goes on from a NaN state, so the kernel always ends and
+// the outputs that depend on the lost hand-off show the failure.
 constexpr unsigned kSsdSpinLimit = 1u << 18;
 constexpr int kSsdWaitVm0 = 0x0F70;  // vmcnt(0), other counters at their maxima (gfx9 s_waitcnt)
 
@@ -529,11 +530,13 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
         }
       }
       __syncthreads();
+      const bool lost = __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 #pragma unroll
       for (int i = 0; i < HT; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          hacc[i][q] = __hip_atomic_load(crow + state_index(i, q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          hacc[i][q] = lost ? __builtin_nanf("")
+                            : __hip_atomic_load(crow + state_index(i, q), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     stage_state();
     const int r = run_chunks(phase == 0 ? 0 : (phase == 1 ? kb : rest), phase == 1 ? ke : nchunks,
