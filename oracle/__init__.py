@@ -12,4 +12,11 @@ of its own transcription of the forward, pinned in ``tests/test_oracle_bwd.py``
 against the C oracle's forward and central finite differences of it.
 ``ssd.py`` is the Mamba-2 SSD layer in its quadratic masked-matrix form (numpy),
 pinned in ``tests/test_oracle_ssd.py`` against the C oracle's recurrence.
+
+Pin status.  The trapezoidal (Mamba-3) scan is partly pinned: its tests fix the
+step as read (impulse response, constant-input closed form, second-order
+convergence, the A = 0 cumulative trapezoid), but the pages leave its three
+coefficients undefined, so that this reading is the paper's is not checkable.
+Full-size outputs with random inputs have no printed value to compare with;
+they rest on the pinned functions.
 """

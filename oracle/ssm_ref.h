@@ -73,7 +73,9 @@ int ssm_ref_scan_fwd_ex(const double* u, const double* delta, const double* A,
  *       gamma_t = delta_t/2.
  *   At the first token of a recurrence (a batch row, or a packed sequence)
  *   the previous input is zero, also when an initial state is given.  The
- *   readout, skip and gate are those of ssm_ref_scan_fwd. */
+ *   readout, skip and gate are those of ssm_ref_scan_fwd.
+ *   Parity partly pinned: the tests fix this reading (impulse response,
+ *   closed form, second-order convergence), not that it is the paper's. */
 int ssm_ref_scan_trap_fwd_ex(const double* u, const double* delta, const double* A,
                              const double* B, const double* C, const double* D,
                              const double* z, const double* delta_bias, int softplus_flag,
