@@ -130,3 +130,30 @@ def test_ssd_chained_plan(L):
     with SsdChained(False):
         yu, fu = _run(x)
     assert np.array_equal(yc, yu) and np.array_equal(fc, fu)
+
+
+def test_ssd_then_decode_step_continues_it():
+    """An SSD layer is a selective scan whose channels share their head's step and A ([P4] "Mamba-2 and
+    Structured State Space Duality"), so its one-token continuation is ssm_state_update with the step and A
+    broadcast over the head's channels: the SSD over L-1 tokens, then one decode step from its final state,
+    equals the SSD over L tokens (y of the last token and the final state).  Two independent kernels (the
+    MFMA chunked form and the per-channel decode) must agree."""
+    rng = np.random.default_rng(790)
+    batch, L, H, P, N = 2, 130, 3, 64, 64
+    x = I.random_ssd_inputs(rng, batch, L, H, P, N)
+    say("ssd then decode")
+    y_full, f_full = _run(x)
+    head = {k: (v[:, :L - 1] if k in ("x", "delta", "B", "C", "z") else v) for k, v in x.items()}
+    _, f_head = _run(head)
+    t = L - 1
+    rep = lambda a: np.repeat(np.asarray(a, np.float32), P, axis=-1)  # per head -> per channel (h major, p minor)
+    state = torch.from_numpy(np.ascontiguousarray(f_head.reshape(batch, H * P, N), dtype=np.float32)).to("cuda:0")
+    yd = ops.ssm_state_update(state, _dev(x["x"][:, t].reshape(batch, H * P)), _dev(rep(x["delta"][:, t])),
+                              _dev(np.repeat(x["A"], P)[:, None] * np.ones((1, N), np.float32), True),
+                              _dev(x["B"][:, t]), _dev(x["C"][:, t]), D=_dev(rep(x["D"]), True),
+                              z=_dev(x["z"][:, t].reshape(batch, H * P)), delta_bias=_dev(rep(x["delta_bias"]), True))
+    torch.cuda.synchronize()
+    ey = rel_err(yd.float().cpu().numpy().astype(np.float64), y_full[:, t].reshape(batch, H * P))
+    ef = rel_err(state.cpu().numpy().astype(np.float64), f_full.reshape(batch, H * P, N))
+    print(f"[parity] ssd then decode: y {ey:.2e}  state {ef:.2e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= 1e-4, (ey, ef)
