@@ -43,7 +43,8 @@
  *   - Arguments are validated before any HIP call: a null required pointer,
  *     a size <= 0, an unknown dtype, a pointer not aligned to its element
  *     size, or a missing, too small or misaligned workspace gives
- *     SSM_ERR_INVALID_ARG; a dstate above 64, a batch above 65535 or a token
+ *     SSM_ERR_INVALID_ARG; a dstate above 64 (above 256 for the decode
+ *     step), a batch above 65535 or a token
  *     row (dim * element size) above 16 MiB gives SSM_ERR_UNSUPPORTED.
  *     Nothing is launched in either case.  A failed launch gives
  *     SSM_ERR_HIP.
@@ -206,6 +207,9 @@ size_t ssm_ssd_fwd_workspace_size(int64_t batch, int64_t L, int64_t heads, int64
  * ("Mamba: The State Space Models Challenging the Transformer", "What a
  * state space model actually is": each new token is one cheap state update).
  *   Required: state, u, delta, A, B, C, y.  Optional: D, z, delta_bias.
+ *   dstate up to 256.  A Mamba-2 (SSD) layer's step is this call with each
+ *   head's step and A repeated over its headdim channels (dim = heads *
+ *   headdim), continuing the state ssm_ssd_fwd leaves.
  *   state must not alias any other argument. */
 ssm_status_t ssm_state_update(float* state, const void* u, const void* delta, const float* A, const void* B,
                               const void* C, const float* D, const void* z, const float* delta_bias,

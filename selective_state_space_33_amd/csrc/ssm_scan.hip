@@ -306,6 +306,10 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
   return launch_scan<IO, kModeFull, RULE>(pl.npl, pl.G, pl.vw, pl.tb, p, grid_full, s);
 }
 
+// The decode step keeps no per-channel state across lanes beyond one
+// wavefront: 64 lanes of 4 states.
+constexpr int64_t kMaxDecodeDstate = 256;
+
 template <class IO>
 hipError_t run_decode(const DecodeParams& p, hipStream_t s) {
   const int nq = next_pow2(ceil_div(p.N, 4));
@@ -332,6 +336,8 @@ hipError_t run_decode(const DecodeParams& p, hipStream_t s) {
     SSM_DECV_CASE(4)
     SSM_DECV_CASE(8)
     SSM_DECV_CASE(16)
+    SSM_DECV_CASE(32)
+    SSM_DECV_CASE(64)
 #undef SSM_DECV_CASE
     return hipErrorInvalidValue;
   }
@@ -350,6 +356,8 @@ hipError_t run_decode(const DecodeParams& p, hipStream_t s) {
   SSM_DEC_CASE(4)
   SSM_DEC_CASE(8)
   SSM_DEC_CASE(16)
+  SSM_DEC_CASE(32)
+  SSM_DEC_CASE(64)
 #undef SSM_DEC_CASE
   return hipErrorInvalidValue;
 }
@@ -543,7 +551,8 @@ extern "C" ssm_status_t ssm_state_update(float* state, const void* u, const void
       (z && !aligned(z, es)) || !aligned(state, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
       (delta_bias && !aligned(delta_bias, 4)))
     return SSM_ERR_INVALID_ARG;
-  if (dstate > 64) return SSM_ERR_UNSUPPORTED;
+  // up to 64 lanes of 4 states per channel: the whole wavefront for dstate 256
+  if (dstate > kMaxDecodeDstate) return SSM_ERR_UNSUPPORTED;
   const int64_t threads = batch * dim * next_pow2(ceil_div(dstate, 4));
   if (ceil_div(threads, 256) > 0x7fffffff) return SSM_ERR_UNSUPPORTED;
   DecodeParams p;

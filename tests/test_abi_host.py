@@ -113,7 +113,7 @@ def _upd(lib_, **kw):
     (dict(state=None), INVALID), (dict(u=None), INVALID), (dict(B=None), INVALID), (dict(y=None), INVALID),
     (dict(batch=0), INVALID), (dict(dim=0), INVALID), (dict(N=-3), INVALID), (dict(dt=9), INVALID),
     (dict(state=0x1002), INVALID), (dict(dt=BF16, z=0x8001), INVALID),
-    (dict(N=100), UNSUPPORTED),
+    (dict(N=257), UNSUPPORTED),
 ])
 def test_state_update_rejects_bad_arguments_without_launching(kw, expect):
     assert _upd(ops.lib(), **kw) == expect

@@ -274,7 +274,8 @@ def test_decode_continues_scan(dtype):
 
 
 @pytest.mark.parametrize("dtype,N,batch", [("bf16", 16, 5), ("f32", 16, 5), ("f32", 3, 5), ("bf16", 64, 5), ("f32", 1, 5),
-                                           ("bf16", 15, 5), ("bf16", 16, 1), ("f32", 8, 2), ("f32", 16, 7)])
+                                           ("bf16", 15, 5), ("bf16", 16, 1), ("f32", 8, 2), ("f32", 16, 7),
+                                           ("bf16", 128, 5), ("f32", 256, 3), ("f32", 130, 2), ("bf16", 100, 1)])
 def test_decode_small_against_oracle(dtype, N, batch):
     """Odd batch sizes leave the last two-row group of the vector kernel half empty; batch 1 runs one row per thread."""
     rng = np.random.default_rng(35 + N + 100 * batch)

@@ -132,14 +132,15 @@ def test_ssd_chained_plan(L):
     assert np.array_equal(yc, yu) and np.array_equal(fc, fu)
 
 
-def test_ssd_then_decode_step_continues_it():
+@pytest.mark.parametrize("N", [64, 128])
+def test_ssd_then_decode_step_continues_it(N):
     """An SSD layer is a selective scan whose channels share their head's step and A ([P4] "Mamba-2 and
     Structured State Space Duality"), so its one-token continuation is ssm_state_update with the step and A
     broadcast over the head's channels: the SSD over L-1 tokens, then one decode step from its final state,
     equals the SSD over L tokens (y of the last token and the final state).  Two independent kernels (the
     MFMA chunked form and the per-channel decode) must agree."""
-    rng = np.random.default_rng(790)
-    batch, L, H, P, N = 2, 130, 3, 64, 64
+    rng = np.random.default_rng(790 + N)
+    batch, L, H, P = 2, 130, 3, 64
     x = I.random_ssd_inputs(rng, batch, L, H, P, N)
     say("ssd then decode")
     y_full, f_full = _run(x)
