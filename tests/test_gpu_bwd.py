@@ -145,3 +145,12 @@ def test_bwd_chained_plan_fp32_and_deterministic():
     for k in g2:
         if g2[k] is not None:
             assert torch.equal(g2[k], g3[k]), k
+
+
+@pytest.mark.parametrize("tiles", [257, 384])
+def test_bwd_planner_boundaries(tiles):
+    """The backward's chained plan at its edges, as the planner chooses it: one tile left over (cut into the most
+    chunks), and half as many tiles again as CUs (two chunks each); ragged L."""
+    rng = np.random.default_rng(490 + tiles)
+    x, dy, dfs = _case(rng, 1, 150, 64 * tiles, 16, "bf16")
+    _run_and_compare(x, dy, dfs, "bf16", label=f"planner boundary {tiles} tiles")

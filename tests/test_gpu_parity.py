@@ -227,6 +227,26 @@ def test_chained_plan_sampled_channels():
     assert ey <= TOL["bf16"] and ef <= 1e-5, (ey, ef)
 
 
+@pytest.mark.parametrize("tiles", [257, 384, 385])
+def test_planner_boundaries(tiles):
+    """At the edges of the chained plan: one tile left over (cut into the most chunks), half as many tiles
+    again as CUs (two chunks each), and one tile more (every tile whole, two rounds).  Channels of the first,
+    a middle and the last tiles, against the oracle."""
+    rng = np.random.default_rng(43 + tiles)
+    batch, L, dim = 1, 333, 64 * tiles
+    x = I.random_scan_inputs(rng, batch, L, dim, 16, dtype="bf16")
+    say(f"planner boundary tiles={tiles} L={L}")
+    y, fs = gpu_scan(x, "bf16")
+    samples = [(0, d) for d in (0, 63, 64 * (tiles // 2) + 7, dim - 64, dim - 1)]
+    samples += [(0, int(d)) for d in rng.integers(0, dim, 6)]
+    yo, fo = oracle_channels(x, samples)
+    yg = np.stack([y[b, :, d] for b, d in samples], axis=1)
+    fg = np.stack([fs[b, d] for b, d in samples], axis=0)
+    ey, ef = rel_err(yg, yo), rel_err(fg, fo)
+    print(f"[parity] planner boundary {tiles} tiles: y err {ey:.3e}  final-state err {ef:.3e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= 1e-5, (ey, ef)
+
+
 def test_chained_deterministic_and_matches_other_plans():
     rng = np.random.default_rng(42)
     x = I.random_scan_inputs(rng, 1, 3000, 64 * 12, 16, dtype="f32")
