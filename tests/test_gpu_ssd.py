@@ -158,3 +158,11 @@ def test_ssd_then_decode_step_continues_it(N):
     ef = rel_err(state.cpu().numpy().astype(np.float64), f_full.reshape(batch, H * P, N))
     print(f"[parity] ssd then decode: y {ey:.2e}  state {ef:.2e}", flush=True)
     assert ey <= TOL["bf16"] and ef <= 1e-4, (ey, ef)
+
+
+@pytest.mark.parametrize("batch,heads", [(1, 257), (4, 96)])
+def test_ssd_planner_boundaries(batch, heads):
+    """The SSD's chained plan at its edges, as the planner chooses it: one (row, head) unit left over (cut into
+    the most segments) and half as many units again as CUs (two segments each); ragged L."""
+    x = I.random_ssd_inputs(np.random.default_rng(800 + heads), batch, 200, heads, 64, 32)
+    _check(x, f"planner boundary {batch * heads} units")
