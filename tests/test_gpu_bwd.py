@@ -154,3 +154,12 @@ def test_bwd_planner_boundaries(tiles):
     rng = np.random.default_rng(490 + tiles)
     x, dy, dfs = _case(rng, 1, 150, 64 * tiles, 16, "bf16")
     _run_and_compare(x, dy, dfs, "bf16", label=f"planner boundary {tiles} tiles")
+
+
+def test_bwd_extreme_steps():
+    """Steps from ~1e-26 to ~60 (raw values spread over +-60): decays that underflow to 0 and decays of 1, with
+    softplus' saturating at 0 and 1, in every gradient."""
+    rng = np.random.default_rng(495)
+    x, dy, dfs = _case(rng, 2, 200, 136, 16, "f32")
+    x["delta"] = _round(np.asarray(x["delta"], np.float64) * 20.0, "f32")
+    _run_and_compare(x, dy, dfs, "f32", label="extreme steps")

@@ -328,3 +328,20 @@ def test_zero_input_gives_zero():
     say("zero input")
     y, fs = gpu_scan(x, "f32")
     assert np.all(y == 0.0) and np.all(fs == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_extreme_steps(dtype):
+    """Steps from ~1e-26 to ~60 (raw values spread over +-60): the decay underflows to 0 at the large end, so the
+    state is just the last input term, and stays at 1 at the small end, so the state is carried unchanged ([P4]
+    "The Selection Mechanism": a large step resets, a small one ignores the token)."""
+    rng = np.random.default_rng(37)
+    x = I.random_scan_inputs(rng, 2, 300, 136, 16, dtype=dtype)
+    raw = np.asarray(x["delta"], np.float64) * 20.0
+    x["delta"] = I.round_to_bf16(raw) if dtype == "bf16" else np.asarray(raw, np.float32).astype(np.float64)
+    say(f"extreme steps {dtype}")
+    y, fs = gpu_scan(x, dtype)
+    yo, fo = oracle_scan(x)
+    ey, ef = rel_err(y, yo), rel_err(fs, fo)
+    print(f"[parity] extreme steps {dtype}: y {ey:.2e}  final {ef:.2e}", flush=True)
+    assert np.all(np.isfinite(y)) and ey <= TOL[dtype] and ef <= TOL[dtype], (ey, ef)
