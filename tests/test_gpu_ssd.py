@@ -166,3 +166,11 @@ def test_ssd_planner_boundaries(batch, heads):
     the most segments) and half as many units again as CUs (two segments each); ragged L."""
     x = I.random_ssd_inputs(np.random.default_rng(800 + heads), batch, 200, heads, 64, 32)
     _check(x, f"planner boundary {batch * heads} units")
+
+
+def test_ssd_extreme_steps():
+    """Raw steps spread over +-60: within a chunk the cumulative decay underflows to 0 (the masked matrix and
+    the chunk's weights lose every term but the newest) or stays at 1."""
+    x = I.random_ssd_inputs(np.random.default_rng(810), 2, 300, 4, 64, 64)
+    x["delta"] = I.round_to_bf16(np.asarray(x["delta"], np.float64) * 20.0)
+    _check(x, "extreme steps")
