@@ -15,7 +15,7 @@ is a group of `headdim` channels sharing the step delta_t and the scalar A of
 the head; B_t and C_t (dstate each) are shared by all heads, as in the
 two-term scan.  Per batch row and head, with x_t the head's headdim inputs:
 
-    H_t = exp(delta_t A) H_{t-1} + delta_t x_t B_t^T      (H: headdim x dstate, H_{-1} = 0)
+    H_t = exp(delta_t A) H_{t-1} + delta_t x_t B_t^T      (H: headdim x dstate, H_{-1} = 0 or given)
     y_t = H_t C_t + D x_t,  then times SiLU(z_t) when z is given
 
 This oracle evaluates the other ordering of the same computation, the
@@ -24,6 +24,10 @@ quadratic "attention" form, literally:
     M[t, s] = (C_t . B_s) * exp(A * (cs_t - cs_s)) * delta_s   for s <= t, else 0,
     cs_t = delta_0 + ... + delta_t,
     y = M x + D x,   final state H_{L-1} = sum_s exp(A (cs_{L-1} - cs_s)) delta_s x_s B_s^T,
+
+and from a given H_{-1} the same plus its decay: exp(A cs_t) H_{-1} C_t in y_t and
+exp(A cs_{L-1}) H_{-1} in the final state (the state a previous call hands on,
+"Mamba is attention all you really need, part 2", "The relay"),
 
 with numpy matrix products.  delta_t = softplus(delta_raw + bias) with the
 exact log-add-exp, or delta_raw + bias when softplus is off.  The tests pin it
@@ -37,13 +41,13 @@ def _f64(a):
     return None if a is None else np.asarray(a, dtype=np.float64)
 
 
-def ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True):
+def ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, initial_state=None):
     """SSD layer in the masked-matrix form.
 
     x, z: [batch, L, heads, headdim]; delta: [batch, L, heads]; A, D, delta_bias: [heads];
-    B, C: [batch, L, dstate].  Returns (y [batch, L, heads, headdim],
-    final_state [batch, heads, headdim, dstate]) in float64."""
-    x, delta, A, B, C, D, z, bias = map(_f64, (x, delta, A, B, C, D, z, delta_bias))
+    B, C: [batch, L, dstate]; initial_state: [batch, heads, headdim, dstate] or None (zero).
+    Returns (y [batch, L, heads, headdim], final_state [batch, heads, headdim, dstate]) in float64."""
+    x, delta, A, B, C, D, z, bias, h0 = map(_f64, (x, delta, A, B, C, D, z, delta_bias, initial_state))
     batch, L, H, P = x.shape
     N = B.shape[2]
     assert delta.shape == (batch, L, H) and A.shape == (H,)
@@ -64,6 +68,9 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True):
                 y[b, :, h] += D[h] * x[b, :, h]
             w = np.exp(A[h] * (cs[-1] - cs)) * dl[b, :, h]                  # weight of token s in H_{L-1}
             fs[b, h] = (x[b, :, h] * w[:, None]).T @ B[b]
+            if h0 is not None:
+                y[b, :, h] += np.exp(A[h] * cs)[:, None] * (C[b] @ h0[b, h].T)   # [t, p]: e^{A cs_t} H_{-1} C_t
+                fs[b, h] += np.exp(A[h] * cs[-1]) * h0[b, h]
     if z is not None:
         y = y * (z / (1.0 + np.exp(-z)))
     return y, fs

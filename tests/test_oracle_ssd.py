@@ -53,6 +53,23 @@ def test_masked_form_equals_the_recurrent_scan(gate, softplus):
     np.testing.assert_allclose(fs.reshape(batch, H * P, -1), fr, rtol=1e-10, atol=1e-12)
 
 
+@pytest.mark.parametrize("gate", [True, False])
+def test_initial_state_equals_the_recurrent_scan_from_it(gate):
+    """From a given state: the masked form plus the state's decay equals the recurrent oracle started from that
+    state (pinned separately in test_oracle_ex.py), head-broadcast as above."""
+    x, dl, A, B, C, D, z, bias = _case(5, 2, 29, 3, 4, 5, gate)
+    rng = np.random.default_rng(6)
+    h0 = rng.standard_normal((2, 3, 4, 5))
+    y, fs = S.ssd_fwd(x, dl, A, B, C, D=D, z=z, delta_bias=bias, initial_state=h0)
+    batch, L, H, P = x.shape
+    rep = lambda a: np.repeat(a, P, axis=-1)
+    yr, fr = R.scan_fwd_ex(x.reshape(batch, L, H * P), rep(dl), np.repeat(A, P)[:, None] * np.ones((1, 5)), B, C,
+                           D=rep(D), z=None if z is None else z.reshape(batch, L, H * P), delta_bias=rep(bias),
+                           initial_state=h0.reshape(batch, H * P, 5))
+    np.testing.assert_allclose(y.reshape(batch, L, H * P), yr, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(fs.reshape(batch, H * P, -1), fr, rtol=1e-10, atol=1e-12)
+
+
 def test_no_decay_unit_step_is_causal_linear_attention():
     rng = np.random.default_rng(2)
     batch, L, H, P, N = 1, 9, 2, 3, 4
@@ -105,6 +122,8 @@ SSD_MUTANTS = {
     "skip_dropped": ("y[b, :, h] += D[h] * x[b, :, h]", "y[b, :, h] += 0.0"),
     "final_state_without_decay": ("w = np.exp(A[h] * (cs[-1] - cs)) * dl[b, :, h]", "w = dl[b, :, h]"),
     "gate_is_sigmoid": ("y = y * (z / (1.0 + np.exp(-z)))", "y = y * (1.0 / (1.0 + np.exp(-z)))"),
+    "initial_state_readout_without_decay": ("np.exp(A[h] * cs)[:, None] * (C[b] @ h0[b, h].T)", "(C[b] @ h0[b, h].T)"),
+    "initial_state_not_handed_on": ("fs[b, h] += np.exp(A[h] * cs[-1]) * h0[b, h]", "fs[b, h] += 0.0"),
 }
 
 
@@ -119,6 +138,7 @@ def test_ssd_mutant_is_caught(name, monkeypatch):
     exec(compile(src.replace(old, new), "ssd_mutant", "exec"), mod.__dict__)
     monkeypatch.setattr(S, "ssd_fwd", mod.ssd_fwd)
     pins = [lambda: test_masked_form_equals_the_recurrent_scan(True, True),
+            lambda: test_initial_state_equals_the_recurrent_scan_from_it(True),
             test_no_decay_unit_step_is_causal_linear_attention, test_decay_mask_is_one_semiseparable]
     caught = 0
     for pin in pins:
