@@ -171,7 +171,7 @@ ssm_status_t ssm_scan_trap_fwd(const void* u, const void* delta, const float* A,
  * 1-semiseparable matrix computed blockwise with matrix products.  Per batch
  * row and head (headdim channels sharing the step and A; B_t, C_t shared by
  * all heads) the state H (headdim x dstate) runs
- *     H_t = exp(delta_t A) H_{t-1} + delta_t x_t B_t^T,   H_{-1} = 0,
+ *     H_t = exp(delta_t A) H_{t-1} + delta_t x_t B_t^T,   H_{-1} = initial_state or 0,
  *     y_t = (H_t C_t + D x_t) * SiLU(z_t)   (skip and gate optional),
  * with delta_t = softplus(delta_raw + bias) (or raw + bias when
  * softplus_flag = 0).  This equals ssm_scan_fwd with dim = heads * headdim,
@@ -179,7 +179,12 @@ ssm_status_t ssm_scan_trap_fwd(const void* u, const void* delta, const float* A,
  *   x, z, y: [batch, L, heads, headdim]; delta: [batch, L, heads]; B, C:
  *   [batch, L, dstate] (all bf16); A, D, delta_bias: [heads] fp32;
  *   final_state (nullable): [batch, heads, headdim, dstate] fp32.
- *   Required: x, delta, A, B, C, y; optional: D, z, delta_bias, final_state.
+ *   initial_state (nullable): the same layout, the state before token 0 of
+ *   each (row, head), e.g. the final_state of the call over the tokens before
+ *   ("Mamba is attention all you really need, part 2", "The relay"); it may
+ *   be the same buffer as final_state.
+ *   Required: x, delta, A, B, C, y; optional: D, z, delta_bias,
+ *   initial_state, final_state.
  *   x, B, C must be 16-byte aligned, delta, z, y 2-byte, the fp32 arrays
  *   4-byte (else INVALID_ARG).  Supported: dt = BF16, headdim = 64 and
  *   dstate = 32, 64 or 128, with (L + 64) * heads * headdim * 2 bytes below
@@ -190,7 +195,7 @@ ssm_status_t ssm_scan_trap_fwd(const void* u, const void* delta, const float* A,
  *   shared with a concurrent call.  y must not alias an input. */
 ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                          const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                         void* y, float* final_state, int64_t batch, int64_t L, int64_t heads, int64_t headdim,
+                         const float* initial_state, void* y, float* final_state, int64_t batch, int64_t L, int64_t heads, int64_t headdim,
                          int64_t dstate, ssm_dtype_t dt, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 

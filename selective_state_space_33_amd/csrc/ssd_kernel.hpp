@@ -55,6 +55,7 @@ struct SsdParams {
   const float* bias;   // [H] (nullable)
   void* y;             // [batch][L][H][P] bf16
   float* final_state;  // [batch][H][P][N] (nullable)
+  const float* h0;     // [batch][H][P][N]: the state before token 0 (nullable: zero)
   int64_t batch, L, H;
   int softplus;
   // Chained launches (n_split > 0): units (batch row, head) 0 .. n_long-1
@@ -506,17 +507,34 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   const int ke = (sg + 1) * seg_chunks < nchunks ? (sg + 1) * seg_chunks : nchunks;
   unsigned* my_flag = has_seg ? p.flags + static_cast<int64_t>(st) * p.Ks + sg : nullptr;  // set once sg-1 is done
   float* crow = has_seg ? p.carry + (static_cast<int64_t>(st) * p.Ks + sg) * P * N : nullptr;  // [n_split][Ks][P][N]
+  // the state of unit `unit` before its token 0: zero, or the given one
+  auto initial = [&](int unit, f32x4_t* dst) {
+#pragma unroll
+    for (int i = 0; i < HT; ++i) {
+      dst[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      if (p.h0) {
+        const float* src = p.h0 + static_cast<int64_t>(unit) * P * N;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) dst[i][q] = src[state_index(i, q)];
+      }
+    }
+  };
+  // unit j's starting state, kept here while a segment runs first (phase 0)
   f32x4_t saved[HT];
   int rest = 0;
-#pragma unroll
-  for (int i = 0; i < HT; ++i) saved[i] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  initial(j, saved);
   for (int phase = 0; phase < 3; ++phase) {
     if (phase == 0 && !(has_seg && sg > 0)) continue;
     if (phase == 1 && !has_seg) continue;
-    // ---- before the phase: the unit and its starting state
+    // ---- before the phase: the unit and its starting state (a segment past the first takes its state
+    // from the segment before it, below)
     set_unit(phase == 1 ? p.n_long + st : j);
+    if (phase == 1) {
+      initial(p.n_long + st, hacc);
+    } else {
 #pragma unroll
-    for (int i = 0; i < HT; ++i) hacc[i] = phase == 2 ? saved[i] : f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int i = 0; i < HT; ++i) hacc[i] = saved[i];
+    }
     if (phase == 1 && sg > 0) {
       // the state after segment sg-1: wait for its flag, then read it coherently
       if (tid == 0) {

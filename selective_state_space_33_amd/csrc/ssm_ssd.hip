@@ -81,7 +81,7 @@ extern "C" size_t ssm_ssd_fwd_workspace_size(int64_t batch, int64_t L, int64_t h
 
 extern "C" ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                                     const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                                    void* y, float* final_state, int64_t batch, int64_t L, int64_t heads,
+                                    const float* initial_state, void* y, float* final_state, int64_t batch, int64_t L, int64_t heads,
                                     int64_t headdim, int64_t dstate, ssm_dtype_t dt, void* workspace,
                                     size_t workspace_bytes, hipStream_t stream) {
   if (!x || !delta || !A || !B || !C || !y) return SSM_ERR_INVALID_ARG;
@@ -91,7 +91,7 @@ extern "C" ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const floa
   if (!ssd_aligned(x, 16) || !ssd_aligned(B, 16) || !ssd_aligned(C, 16) || !ssd_aligned(delta, 2) ||
       !ssd_aligned(y, 2) || (z && !ssd_aligned(z, 2)))
     return SSM_ERR_INVALID_ARG;
-  const float* f32s[] = {A, D, delta_bias, final_state};
+  const float* f32s[] = {A, D, delta_bias, final_state, initial_state};
   for (const float* q : f32s)
     if (q && !ssd_aligned(q, 4)) return SSM_ERR_INVALID_ARG;
   if (!ssd_shape_ok(L, heads, headdim, dstate, dt) || batch * heads > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
@@ -109,6 +109,7 @@ extern "C" ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const floa
   p.bias = delta_bias;
   p.y = y;
   p.final_state = final_state;
+  p.h0 = initial_state;
   p.batch = batch;
   p.L = L;
   p.H = heads;

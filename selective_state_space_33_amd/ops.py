@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_trap_fwd.restype = ctypes.c_int
         L.ssm_scan_trap_fwd.argtypes = L.ssm_scan_fwd_ex.argtypes
         L.ssm_ssd_fwd.restype = ctypes.c_int
-        L.ssm_ssd_fwd.argtypes = ([_vp] * 8 + [ctypes.c_int, _vp, _vp] + [_i64] * 5 +
+        L.ssm_ssd_fwd.argtypes = ([_vp] * 8 + [ctypes.c_int, _vp, _vp, _vp] + [_i64] * 5 +
                                   [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
         L.ssm_ssd_fwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_ssd_fwd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int]
@@ -221,12 +221,13 @@ def ssm_ssd_fwd_workspace_size(batch: int, L: int, heads: int, headdim: int, dst
     return int(lib().ssm_ssd_fwd_workspace_size(batch, L, heads, headdim, dstate, _dtype_code(dtype)))
 
 
-def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, y=None,
-                final_state=None, return_final_state: bool = True, workspace=None, stream=None):
+def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, initial_state=None,
+                y=None, final_state=None, return_final_state: bool = True, workspace=None, stream=None):
     """The Mamba-2 SSD layer on the GPU.
 
     x, z: [batch, L, heads, headdim]; delta: [batch, L, heads]; B, C: [batch, L, dstate] (bfloat16);
-    A, D, delta_bias: [heads] (float32).  Returns (y, final_state [batch, heads, headdim, dstate] or None)."""
+    A, D, delta_bias: [heads] (float32); initial_state: [batch, heads, headdim, dstate] (float32) or None.
+    Returns (y, final_state [batch, heads, headdim, dstate] or None)."""
     batch, L, heads, headdim = x.shape
     dstate = B.shape[2]
     dev, dt = x.device, x.dtype
@@ -237,6 +238,7 @@ def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bo
         _check(t, name, dt, shp, dev)
     for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias)):
         _check(t, name, torch.float32, (heads,), dev)
+    _check(initial_state, "initial_state", torch.float32, (batch, heads, headdim, dstate), dev)
     if y is None:
         y = torch.empty_like(x)
     _check(y, "y", dt, (batch, L, heads, headdim), dev)
@@ -248,7 +250,8 @@ def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bo
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                           1 if softplus else 0, _ptr(y), _ptr(final_state), batch, L, heads, headdim, dstate, code,
+                           1 if softplus else 0, _ptr(initial_state), _ptr(y), _ptr(final_state), batch, L, heads,
+                           headdim, dstate, code,
                            _ptr(workspace), ws_bytes, _stream(dev, stream))
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_ssd_fwd")

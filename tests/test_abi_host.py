@@ -212,11 +212,11 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 
 def _ssd(lib_, **kw):
     """Call ssm_ssd_fwd with fake (never dereferenced) pointers; only rejection paths are used."""
-    a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, z=None, bias=None, sp=1, y=0x6000,
-             fs=None, batch=1, L=8, H=2, P=64, N=64, dt=BF16, ws=None, wsb=0, stream=None)
+    a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, z=None, bias=None, sp=1, h0=None,
+             y=0x6000, fs=None, batch=1, L=8, H=2, P=64, N=64, dt=BF16, ws=None, wsb=0, stream=None)
     a.update(kw)
-    return lib_.ssm_ssd_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["y"],
-                            a["fs"], a["batch"], a["L"], a["H"], a["P"], a["N"], a["dt"], a["ws"], a["wsb"],
+    return lib_.ssm_ssd_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["h0"],
+                            a["y"], a["fs"], a["batch"], a["L"], a["H"], a["P"], a["N"], a["dt"], a["ws"], a["wsb"],
                             a["stream"])
 
 
@@ -224,6 +224,7 @@ def _ssd(lib_, **kw):
     (dict(x=None), INVALID), (dict(B=None), INVALID), (dict(y=None), INVALID), (dict(L=0), INVALID),
     (dict(H=-1), INVALID), (dict(dt=7), INVALID),
     (dict(x=0x1008), INVALID), (dict(C=0x5004), INVALID), (dict(delta=0x2001), INVALID), (dict(fs=0x7002), INVALID),
+    (dict(h0=0x8002), INVALID),
     (dict(dt=F32), UNSUPPORTED), (dict(P=32), UNSUPPORTED), (dict(N=16), UNSUPPORTED), (dict(N=96), UNSUPPORTED),
     (dict(L=1 << 20, H=40), UNSUPPORTED),   # token rows past 2^31 bytes
     (dict(batch=4, H=80), INVALID),           # 320 units: the chained plan needs its workspace

@@ -27,19 +27,19 @@ def _dev(a, f32=False):
     return t if f32 else t.to(torch.bfloat16)
 
 
-def _run(x, softplus=True):
+def _run(x, softplus=True, h0=None):
     y, fs = ops.ssm_ssd_fwd(_dev(x["x"]), _dev(x["delta"]), _dev(x["A"], True), _dev(x["B"]), _dev(x["C"]),
                             D=_dev(x["D"], True), z=_dev(x["z"]), delta_bias=_dev(x["delta_bias"], True),
-                            softplus=softplus)
+                            softplus=softplus, initial_state=_dev(h0, True))
     torch.cuda.synchronize()
     return y.float().cpu().numpy().astype(np.float64), fs.cpu().numpy().astype(np.float64)
 
 
-def _check(x, label, softplus=True, tol=TOL["bf16"]):
+def _check(x, label, softplus=True, tol=TOL["bf16"], h0=None):
     say(f"ssd {label} x={x['x'].shape} N={x['B'].shape[2]}")
-    yg, fg = _run(x, softplus)
+    yg, fg = _run(x, softplus, h0)
     yo, fo = S.ssd_fwd(x["x"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
-                       softplus=softplus)
+                       softplus=softplus, initial_state=h0)
     ey, ef = rel_err(yg, yo), rel_err(fg, fo)
     print(f"[parity] ssd {label}: y {ey:.2e}  final {ef:.2e}", flush=True)
     assert ey <= tol and ef <= tol, (ey, ef)
@@ -174,3 +174,33 @@ def test_ssd_extreme_steps():
     x = I.random_ssd_inputs(np.random.default_rng(810), 2, 300, 4, 64, 64)
     x["delta"] = I.round_to_bf16(np.asarray(x["delta"], np.float64) * 20.0)
     _check(x, "extreme steps")
+
+
+@pytest.mark.parametrize("chained", [False, True])
+def test_ssd_initial_state(chained):
+    """From a given state per (row, head): on one workgroup per unit, and on the chained plan (270 units), where
+    a unit's first segment starts from it."""
+    rng = np.random.default_rng(820 + chained)
+    batch, heads = (2, 5) if not chained else (3, 90)
+    x = I.random_ssd_inputs(rng, batch, 200, heads, 64, 64)
+    h0 = np.asarray(rng.standard_normal((batch, heads, 64, 64)) * 0.5, np.float32).astype(np.float64)
+    with SsdChained(chained):
+        _check(x, f"initial state chained={chained}", h0=h0)
+
+
+def test_ssd_continues_from_its_final_state():
+    """Two calls, the second from the first's final state, equal one call over all the tokens (chunked prefill;
+    [P1] "The relay")."""
+    rng = np.random.default_rng(830)
+    x = I.random_ssd_inputs(rng, 2, 300, 3, 64, 128)
+    say("ssd continuation")
+    y_all, f_all = _run(x)
+    cut = 137
+    first = {k: (v[:, :cut] if k in ("x", "delta", "B", "C", "z") else v) for k, v in x.items()}
+    second = {k: (v[:, cut:] if k in ("x", "delta", "B", "C", "z") else v) for k, v in x.items()}
+    y1, f1 = _run(first)
+    y2, f2 = _run(second, h0=f1)
+    ey = rel_err(np.concatenate([y1, y2], axis=1), y_all)
+    ef = rel_err(f2, f_all)
+    print(f"[parity] ssd continuation: y {ey:.2e}  final {ef:.2e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= 1e-4, (ey, ef)
