@@ -1,5 +1,7 @@
 """The build's DPP hazard scan (selective_state_space_33_amd/build.py, dpp_hazards) on small
 assembly fragments: every planted hazard is found, and correctly separated code passes."""
+import os
+
 from selective_state_space_33_amd.build import dpp_hazards
 
 ASM_DPP = ";;#ASMSTART\n\tv_fmac_f32_dpp v0, v5, v2 row_newbcast:3 row_mask:0xf bank_mask:0xf\n;;#ASMEND\n"
@@ -39,3 +41,14 @@ def test_inline_asm_dpp_right_after_a_label_is_found():
     assert dpp_hazards(".LBB0_3:\n\ts_nop 4\n" + ASM_DPP) == []
     # compiler-emitted DPP after a label is the compiler's to protect
     assert dpp_hazards(".LBB0_3:\n\tv_mul_f32_dpp v1, v5, v2 row_newbcast:1 row_mask:0xf bank_mask:0xf\n") == []
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: asked for more it exits non-zero with a message, before touching a device."""
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
