@@ -239,3 +239,19 @@ def test_ssd_workspace_size():
     ws = L.ssm_ssd_fwd_workspace_size(4, 4096, 80, 64, 128, BF16)             # 320 units: 64 left over, 4 segments
     assert ws >= 64 * 4 * 64 * 128 * 4 and ws % 256 == 0
     assert L.ssm_ssd_fwd_workspace_size(4, 4096, 80, 64, 128, F32) == 0        # rejected
+
+
+def test_binding_argument_counts_match_the_header():
+    """Every entry point's ctypes signature has as many arguments as its declaration in include/ssm_scan.h (the
+    binding and the header cannot drift apart unnoticed)."""
+    import os
+    import re
+
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "ssm_scan.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    L = ops.lib()
+    for name in ops.EXPORTED:
+        m = re.search(r"\b" + name + r"\s*\(([^;]*?)\)\s*;", hdr, flags=re.S)
+        assert m, name
+        params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
+        assert len(getattr(L, name).argtypes) == len(params), name
