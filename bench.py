@@ -14,12 +14,21 @@ with the Mamba-3 trapezoidal three-term recurrence (ssm_scan_trap_fwd) under
 "trapezoid".  The Mamba-2 SSD layer (ssm_ssd_fwd, MFMA) on a 2.7B-shaped layer
 (batch 4, L 4096, 80 heads of 64 channels, state 128, bf16) is under "ssd".
 
+Timing: inputs are resident in HBM; every timed call is preceded, outside
+its HIP events, by a read of a 1 GiB buffer that evicts L2 and the Infinity
+Cache, so each call reads its inputs from HBM.  ms_per_step is the median of
+the timed calls (p10/p90/min beside it); back-to-back timing is reported
+under "back_to_back".
+
 Prints ONE JSON line.  Fields beyond the common ones:
-  roofline      the dominant kernel against its binding roofline (VALU issue:
-                the scan needs 4 fp32 VALU ops + 1 exp per state update, which
-                takes longer at the chip's issue rate than moving its bytes);
-  hbm           the same launch against the 8 TB/s HBM roofline (the metric's
-                second half);
+  roofline      the step's algorithmic HBM bytes (every input read once, y and
+                the final state written once) per call time against the
+                8 TB/s HBM peak -- the metric's second half.  The step is the
+                packing of B and C (~1% of it) and the scan kernel; the
+                scan's rocprofv3 duration is in profiles/;
+  alu_issue     the same time against the chip's fp32 VALU issue rate: the
+                scan needs 4 fp32 VALU ops + 1 exp per state update, more issue
+                time than byte time, so this fraction is the higher one;
   cpu_baseline  the fp64 CPU oracle on a bounded sample of the same workload.
 """
 import argparse
@@ -72,6 +81,15 @@ def decode_bytes(w):
     s = 2 if w.dtype == "bf16" else 4
     return (2 * w.batch * w.dim * w.dstate * 4 + w.batch * w.dim * 4 * s + w.batch * w.dstate * 2 * s
             + w.dim * w.dstate * 4 + 2 * w.dim * 4)
+
+
+def bwd_bytes(w):
+    """Algorithmic bytes of the backward: u, delta, z, B, C, dy read and du, ddelta, dz, dB, dC written once,
+    A/D/bias read and dA/dD/dbias written once."""
+    s = 2 if w.dtype == "bf16" else 4
+    n_io = 7 if w.gate else 5  # u, delta, dy (+ z) read; du, ddelta (+ dz) written
+    return (w.batch * w.L * w.dim * n_io * s + w.batch * w.L * w.dstate * 4 * s
+            + 2 * (w.dim * w.dstate * 4 + 2 * w.dim * 4))
 
 
 def scan_slots(w):
@@ -139,32 +157,42 @@ def time_calls(fn, steps, warmup, stream, min_warm_ms=150.0):
     return start.elapsed_time(end) / steps, wall / steps * 1e3
 
 
-def time_cold_calls(fn, calls, stream, flush_bytes=1 << 30):
+def time_cold_calls(fn, calls, stream, warmup=0, flush_bytes=1 << 30, min_warm_ms=150.0):
     """Per-call times (ms) with the caches flushed before every call.
 
     A read over a 1 GiB buffer, outside the events, evicts the inputs from L2 and the 256 MB
     Infinity Cache, so each call reads them from HBM.  It reads rather than writes so that the
     call does not start with the flush's own dirty lines still waiting to be written back.
-    Returns min, p10, median, p90."""
+    `warmup` untimed flushed calls (and at least min_warm_ms of them: the clock takes ~100 ms of
+    load to settle) come first; the timed calls are bracketed by device synchronisations.
+    Returns min, p10, median, p90 and the wall time of the timed region."""
     import numpy as np
     import torch
 
     buf = torch.ones(flush_bytes // 4, dtype=torch.float32, device=stream.device)
-    fn()
-    times = []
-    for _ in range(calls):
+    t_w = time.perf_counter()
+    n_w = 0
+    while n_w < max(warmup, 1) or (time.perf_counter() - t_w) * 1e3 < min_warm_ms:
         buf.sum()
-        start = torch.cuda.Event(enable_timing=True)
-        end = torch.cuda.Event(enable_timing=True)
+        fn()
+        n_w += 1
+        if n_w % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    t0 = time.perf_counter()
+    for start, end in evs:
+        buf.sum()
         start.record(stream)
         fn()
         end.record(stream)
-        end.synchronize()
-        times.append(start.elapsed_time(end))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     del buf
-    t = np.asarray(times)
-    return {"calls": calls, "flush_bytes": flush_bytes, "ms_min": float(t.min()), "ms_p10": float(np.percentile(t, 10)),
-            "ms_median": float(np.median(t)), "ms_p90": float(np.percentile(t, 90))}
+    t = np.asarray([s_.elapsed_time(e_) for s_, e_ in evs])
+    return {"calls": calls, "warmup_calls": n_w, "flush_bytes": flush_bytes, "ms_min": float(t.min()),
+            "ms_p10": float(np.percentile(t, 10)), "ms_median": float(np.median(t)),
+            "ms_p90": float(np.percentile(t, 90)), "wall_s": wall}
 
 
 def copy_bandwidth(dev, stream, nbytes=1 << 30, steps=20):
@@ -178,17 +206,31 @@ def copy_bandwidth(dev, stream, nbytes=1 << 30, steps=20):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+def host_cores():
+    """Cores this process may run on: its CPU affinity, further limited by a cgroup CPU quota if one is set."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            quota, period = f.read().split()[:2]
+        if quota != "max":
+            n = min(n, max(1, int(int(quota) / int(period))))
+    except (OSError, ValueError):
+        pass
+    return max(1, n)
+
+
 def cpu_baseline(w, x, budget_s):
     """The fp64 oracle on the first channels of every batch row (full sequence), sized to ~budget_s of wall time.
 
-    Timed with one thread per host core (up to 16) and, on a smaller sample, with one thread.  When the whole
-    workload fits in the budget it is run whole, repeatedly, and the median run is reported.
+    Timed with one thread per core this process may use (host_cores) and, on a smaller sample, with one
+    thread.  When the whole workload fits in the budget it is run whole, repeatedly, and the median run is
+    reported.
     """
     import numpy as np
 
     from oracle import ref as R
 
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads = host_cores()
 
     def run(nch, nthreads):
         sub = dict(u=x["u"][:, :, :nch], delta=x["delta"][:, :, :nch],
@@ -221,7 +263,7 @@ def cpu_baseline(w, x, budget_s):
         pass
     what = "the whole workload" if nch == w.dim else f"channels 0..{nch - 1} of every batch row"
     return {"value": ups, "unit": "updates/s", "cores": threads, "kind": "oracle",
-            "single_thread_value": nch1 * per_channel / dt1, "cpu_model": model,
+            "host_cpu_count": os.cpu_count(), "single_thread_value": nch1 * per_channel / dt1, "cpu_model": model,
             "sample": f"{w.name}: {what}, all {w.L} tokens, dstate {w.dstate} "
                       f"({nch * per_channel:.3e} updates, median of {len(runs)} runs of {dt:.2f} s; fp64 "
                       f"sequential recurrence, {threads} threads over channels); single thread: channels "
@@ -244,7 +286,7 @@ def main():
     ap.add_argument("--no-ssd", action="store_true")
     ap.add_argument("--packed-mean-len", type=float, default=1024.0,
                     help="mean sequence length of the packed row (log-normal lengths, sigma 1)")
-    ap.add_argument("--no-cold", action="store_true", help="skip the per-call timings with flushed caches")
+    ap.add_argument("--no-copy", action="store_true", help="skip the plain-copy bandwidth reference")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="instead of the scan, time a plain device copy of this many MiB (calibrates HBM counters)")
     args = ap.parse_args()
@@ -288,13 +330,17 @@ def main():
         ops.ssm_scan_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"], delta_bias=g["delta_bias"],
                          y=y, final_state=fs, workspace=ws, stream=stream)
 
-    ms, wall_ms = time_calls(step, args.steps, args.warmup, stream)
+    # the contract's timing: each call from HBM (caches flushed before it), median of the timed calls
+    cold = time_cold_calls(step, args.steps, stream, warmup=args.warmup)
+    ms = cold["ms_median"]
     ups = w.updates / (ms * 1e-3)
     nbytes = scan_bytes(w)
     slots = scan_slots(w)
     achieved_tf = 2.0 * slots / (ms * 1e-3) / 1e12
     achieved_gbs = nbytes / (ms * 1e-3) / 1e9
     traffic = measured_traffic(w.name)
+    # back to back, for comparison (inputs may partly hit the Infinity Cache)
+    bb_ms, bb_wall_ms = time_calls(step, args.steps, 5, stream)
 
     out = {
         "metric": "selective-scan state updates/s (B*L*D*N) and % of MI355X HBM roofline",
@@ -307,27 +353,27 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {"workload": w.name, "op": "ssm_scan_fwd", "batch": w.batch, "seq_len": w.L, "dim": w.dim,
-                   "dstate": w.dstate, "storage_dtype": w.dtype, "z_gate": w.gate, "final_state": True,
-                   "workspace_bytes": need, "seed": 0, "wall_ms_per_step": wall_ms},
-        "roofline": {"bound": "alu", "achieved": achieved_tf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved_tf / VALU_PEAK_TFLOPS, "traffic": traffic,
-                     "counted": f"algorithmic fp32 VALU issue slots x 2 flops: {SLOTS_PER_UPDATE} per state update, "
-                                f"{SLOTS_PER_TOKEN_CHANNEL} per (token, channel), a transcendental = {TRANS_SLOTS} "
-                                f"slots; peak = non-packed fp32 issue rate"},
-        "hbm": {"algorithmic_bytes": nbytes, "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": achieved_gbs / HBM_PEAK_GBS},
+                   "dstate": w.dstate, "storage_dtype": w.dtype, "compute_dtype": "f32", "z_gate": w.gate,
+                   "final_state": True, "workspace_bytes": need, "seed": 0},
+        "timing": dict(cold, protocol="1 GiB read before every timed call, outside its HIP events; "
+                                      "median of the timed calls"),
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic, "algorithmic_bytes": nbytes,
+                     "kernels": "pack_bc_kernel + scan_kernel (one ssm_scan_fwd call)"},
+        "alu_issue": {"achieved": achieved_tf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": achieved_tf / VALU_PEAK_TFLOPS,
+                      "counted": f"algorithmic fp32 VALU issue slots x 2 flops: {SLOTS_PER_UPDATE} per state update, "
+                                 f"{SLOTS_PER_TOKEN_CHANNEL} per (token, channel), a transcendental = {TRANS_SLOTS} "
+                                 f"slots; peak = non-packed fp32 issue rate"},
+        "back_to_back": {"ms_per_step": bb_ms, "wall_ms_per_step": bb_wall_ms, "value": w.updates / (bb_ms * 1e-3),
+                         "hbm_frac": nbytes / (bb_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
     }
 
-    if not args.no_cold:
-        # Each call on its own, after a cache flush: the inputs come from HBM, never from the Infinity Cache.
-        cold = time_cold_calls(step, max(args.steps, 20), stream)
+    if not args.no_copy:
         copy_gbs = copy_bandwidth(dev, stream)
-        med_gbs = nbytes / (cold["ms_median"] * 1e-3) / 1e9
-        out["cold"] = dict(cold, hbm_achieved=med_gbs, hbm_frac=med_gbs / HBM_PEAK_GBS,
-                           updates_per_s=w.updates / (cold["ms_median"] * 1e-3))
         out["copy_bandwidth"] = {"achieved": copy_gbs, "unit": "GB/s", "bytes_each_way": 1 << 30,
                                  "scan_frac_of_copy": achieved_gbs / copy_gbs}
 
@@ -342,19 +388,20 @@ def main():
             ops.ssm_state_update(state, gd["u"], gd["delta"], gd["A"], gd["B"], gd["C"], D=gd["D"], z=gd["z"],
                                  delta_bias=gd["delta_bias"], y=yd, stream=stream)
 
-        dms, _ = time_calls(dstep, max(args.steps, 20), args.warmup, stream)
+        # 179 MB fits the Infinity Cache, so back-to-back steps can hit it; flushed steps cannot
+        dcold = time_cold_calls(dstep, max(args.steps, 20), stream, warmup=20)
+        dms = dcold["ms_median"]
         db = decode_bytes(wd)
+        dgbs = db / (dms * 1e-3) / 1e9
+        dbb, _ = time_calls(dstep, max(args.steps, 20), 20, stream)
         out["decode"] = {"workload": wd.name, "op": "ssm_state_update", "ms_per_step": dms,
-                         "value": wd.updates / (dms * 1e-3), "unit": "updates/s",
-                         "roofline": {"bound": "hbm", "achieved": db / (dms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
-                                      "unit": "GB/s", "frac": db / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                                      "algorithmic_bytes": db, "traffic": measured_traffic(wd.name)}}
-        if not args.no_cold:
-            # 179 MB fits the Infinity Cache, so back-to-back steps can hit it; flushed steps cannot
-            dcold = time_cold_calls(dstep, max(args.steps, 20), stream)
-            dgbs = db / (dcold["ms_median"] * 1e-3) / 1e9
-            out["decode"]["cold"] = dict(dcold, hbm_achieved=dgbs, hbm_frac=dgbs / HBM_PEAK_GBS,
-                                         frac_of_copy=dgbs / out["copy_bandwidth"]["achieved"])
+                         "value": wd.updates / (dms * 1e-3), "unit": "updates/s", "timing": dcold,
+                         "roofline": {"bound": "hbm", "achieved": dgbs, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "frac": dgbs / HBM_PEAK_GBS,
+                                      "algorithmic_bytes": db, "traffic": measured_traffic(wd.name)},
+                         "back_to_back": {"ms_per_step": dbb, "hbm_frac": db / (dbb * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+        if "copy_bandwidth" in out:
+            out["decode"]["frac_of_copy"] = dgbs / out["copy_bandwidth"]["achieved"]
         del gd, yd, state
 
     if not args.no_backward:
@@ -366,16 +413,21 @@ def main():
             ops.ssm_scan_bwd(g["u"], g["delta"], g["A"], g["B"], g["C"], dy, D=g["D"], z=g["z"],
                              delta_bias=g["delta_bias"], workspace=wsb, stream=stream)
 
-        bms, _ = time_calls(bstep, max(args.steps // 5, 5), max(args.warmup // 10, 5), stream)
+        bt = time_cold_calls(bstep, max(args.steps // 5, 10), stream, warmup=5)
+        bms = bt["ms_median"]
         bslots = w.updates * BWD_SLOTS_PER_UPDATE + w.batch * w.L * w.dim * BWD_SLOTS_PER_TOKEN_CHANNEL
         btf = 2.0 * bslots / (bms * 1e-3) / 1e12
-        out["backward"] = {"workload": w.name, "op": "ssm_scan_bwd", "ms_per_step": bms,
+        bbytes = bwd_bytes(w)
+        out["backward"] = {"workload": w.name, "op": "ssm_scan_bwd", "ms_per_step": bms, "timing": bt,
                            "value": w.updates / (bms * 1e-3), "unit": "updates/s", "workspace_bytes": needb,
-                           "roofline": {"bound": "alu", "achieved": btf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                        "frac": btf / VALU_PEAK_TFLOPS,
-                                        "counted": f"algorithmic fp32 VALU issue slots x 2 flops, states recomputed "
-                                                   f"once: {BWD_SLOTS_PER_UPDATE} per state update, "
-                                                   f"{BWD_SLOTS_PER_TOKEN_CHANNEL} per (token, channel)"}}
+                           "roofline": {"bound": "hbm", "achieved": bbytes / (bms * 1e-3) / 1e9,
+                                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "algorithmic_bytes": bbytes,
+                                        "frac": bbytes / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                           "alu_issue": {"achieved": btf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                         "frac": btf / VALU_PEAK_TFLOPS,
+                                         "counted": f"algorithmic fp32 VALU issue slots x 2 flops, states "
+                                                    f"recomputed once: {BWD_SLOTS_PER_UPDATE} per state update, "
+                                                    f"{BWD_SLOTS_PER_TOKEN_CHANNEL} per (token, channel)"}}
         del dy, wsb
 
     if not args.no_packed:
@@ -400,15 +452,21 @@ def main():
                                 initial_state=h0, cu_seqlens=cu_t, y=py, final_state=pfs, workspace=wsp,
                                 stream=stream)
 
-        pms, _ = time_calls(pstep, args.steps, max(args.warmup // 4, 5), stream)
+        pt = time_cold_calls(pstep, args.steps, stream, warmup=10)
+        pms = pt["ms_median"]
         lens = np.diff(cu)
         ptf = 2.0 * slots / (pms * 1e-3) / 1e12
+        # the same bytes as the batch layer, plus the initial states read
+        pbytes = scan_bytes(w) - w.batch * w.dim * w.dstate * 4 + 2 * nseq * w.dim * w.dstate * 4
         out["packed"] = {"workload": f"{w.name} as 1 x {w.batch * w.L} packed tokens", "op": "ssm_scan_fwd_ex",
                          "sequences": nseq, "len_min": int(lens.min()), "len_median": float(np.median(lens)),
-                         "len_max": int(lens.max()), "initial_state": True, "ms_per_step": pms,
+                         "len_max": int(lens.max()), "initial_state": True, "ms_per_step": pms, "timing": pt,
                          "value": w.updates / (pms * 1e-3), "unit": "updates/s",
-                         "roofline": {"bound": "alu", "achieved": ptf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                      "frac": ptf / VALU_PEAK_TFLOPS}}
+                         "roofline": {"bound": "hbm", "achieved": pbytes / (pms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS,
+                                      "unit": "GB/s", "algorithmic_bytes": pbytes,
+                                      "frac": pbytes / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                         "alu_issue": {"achieved": ptf, "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                       "frac": ptf / VALU_PEAK_TFLOPS}}
         del py, pfs, wsp, h0
 
     if not args.no_trapezoid:
@@ -419,15 +477,19 @@ def main():
             ops.ssm_scan_trap_fwd(g["u"], g["delta"], g["A"], g["B"], g["C"], D=g["D"], z=g["z"],
                                   delta_bias=g["delta_bias"], y=y, final_state=fs, workspace=wst, stream=stream)
 
-        tms, _ = time_calls(tstep, args.steps, max(args.warmup // 4, 5), stream)
+        tt = time_cold_calls(tstep, args.steps, stream, warmup=10)
+        tms = tt["ms_median"]
         tslots = w.updates * SLOTS_PER_UPDATE + w.batch * w.L * w.dim * TRAP_SLOTS_PER_TOKEN_CHANNEL
         ttf = 2.0 * tslots / (tms * 1e-3) / 1e12
-        out["trapezoid"] = {"workload": w.name, "op": "ssm_scan_trap_fwd", "ms_per_step": tms,
+        out["trapezoid"] = {"workload": w.name, "op": "ssm_scan_trap_fwd", "ms_per_step": tms, "timing": tt,
                             "value": w.updates / (tms * 1e-3), "unit": "updates/s", "workspace_bytes": needt,
-                            "roofline": {"bound": "alu", "achieved": ttf, "peak": VALU_PEAK_TFLOPS,
-                                         "unit": "TFLOP/s", "frac": ttf / VALU_PEAK_TFLOPS,
-                                         "counted": f"{SLOTS_PER_UPDATE} slots per state update, "
-                                                    f"{TRAP_SLOTS_PER_TOKEN_CHANNEL} per (token, channel)"}}
+                            "roofline": {"bound": "hbm", "achieved": nbytes / (tms * 1e-3) / 1e9,
+                                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "algorithmic_bytes": nbytes,
+                                         "frac": nbytes / (tms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+                            "alu_issue": {"achieved": ttf, "peak": VALU_PEAK_TFLOPS,
+                                          "unit": "TFLOP/s", "frac": ttf / VALU_PEAK_TFLOPS,
+                                          "counted": f"{SLOTS_PER_UPDATE} slots per state update, "
+                                                     f"{TRAP_SLOTS_PER_TOKEN_CHANNEL} per (token, channel)"}}
         del wst
 
     if not args.no_ssd:
@@ -444,12 +506,15 @@ def main():
         del xs
         ys = torch.empty_like(gs["x"])
         fss = torch.empty((sb, sH, sP, sN), dtype=torch.float32, device=dev)
+        needs = ops.ssm_ssd_fwd_workspace_size(sb, sL, sH, sP, sN, gs["x"].dtype)
+        wss = torch.empty(needs, dtype=torch.uint8, device=dev) if needs else None
 
         def sstep():
             ops.ssm_ssd_fwd(gs["x"], gs["delta"], gs["A"], gs["B"], gs["C"], D=gs["D"], z=gs["z"],
-                            delta_bias=gs["bias"], y=ys, final_state=fss, stream=stream)
+                            delta_bias=gs["bias"], y=ys, final_state=fss, workspace=wss, stream=stream)
 
-        sms, _ = time_calls(sstep, max(args.steps // 2, 5), max(args.warmup // 10, 5), stream)
+        st_ = time_cold_calls(sstep, max(args.steps // 2, 10), stream, warmup=5)
+        sms = st_["ms_median"]
         supd = sb * sL * sH * sP * sN
         # algorithmic bytes: x, z, y, B, C, delta once each (bf16), A, D, bias, the final state (fp32)
         sbytes = sb * sL * sH * sP * 2 * 3 + sb * sL * sN * 2 * 2 + sb * sL * sH * 2 + sb * sH * sP * sN * 4 + sH * 12
@@ -462,13 +527,13 @@ def main():
         sgbs = sbytes / (sms * 1e-3) / 1e9
         stf = sflops / (sms * 1e-3) / 1e12
         out["ssd"] = {"workload": "mamba2_2p7b_bf16 (batch 4, L 4096, 80 heads x 64, state 128)", "op": "ssm_ssd_fwd",
-                      "ms_per_step": sms, "value": supd / (sms * 1e-3), "unit": "updates/s",
+                      "ms_per_step": sms, "timing": st_, "value": supd / (sms * 1e-3), "unit": "updates/s",
                       "roofline": {"bound": "hbm", "achieved": sgbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                    "frac": sgbs / HBM_PEAK_GBS, "algorithmic_bytes": sbytes,
                                    "traffic": measured_traffic("mamba2_2p7b_bf16")},
                       "mfma": {"achieved": stf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": stf / MFMA_BF16_PEAK_TFLOPS, "algorithmic_flops": sflops}}
-        del gs, ys, fss
+        del gs, ys, fss, wss
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_budget)

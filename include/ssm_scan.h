@@ -26,8 +26,14 @@
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the
- *     library allocates and frees nothing and keeps no state between calls,
- *     so concurrent calls on different streams are safe.
+ *     library allocates and frees nothing and keeps no state between calls
+ *     (beyond each device's compute-unit count, looked up once), so
+ *     concurrent calls on different streams with their own workspaces are
+ *     safe.
+ *   - Launch plans balance the work over the current device's compute units;
+ *     workspace sizes therefore depend on the device current when they are
+ *     queried (the same device must be current for the call).  SSM_NUM_CU
+ *     in the environment overrides the count (for tests of the plans).
  *   - Layouts are contiguous row-major:
  *       u, delta, z, y        [batch, L, dim]     (decode: [batch, dim])
  *       B, C                  [batch, L, dstate]  (decode: [batch, dstate]),
@@ -53,8 +59,11 @@
  *     piece starts from the state, or adjoint, that the piece before it
  *     hands on), each wait is bounded (about a third of a second).  Past the
  *     bound the piece goes on from NaN, so the outputs that depend on the
- *     lost hand-off are NaN rather than silently wrong; it does not happen
- *     on a GPU that runs the call's workgroups.
+ *     lost hand-off are NaN rather than silently wrong, and the call's
+ *     workspace records the time-out: ssm_workspace_status then returns
+ *     SSM_ERR_HANDOFF_TIMEOUT.  It does not happen on a GPU that runs the
+ *     call's workgroups.  Every workspace starts with a 256-byte header
+ *     (status word, tickets, ready flags) that each call resets.
  */
 #ifndef SSM_SCAN_H
 #define SSM_SCAN_H
@@ -72,7 +81,8 @@ typedef enum {
   SSM_OK = 0,
   SSM_ERR_INVALID_ARG = 1,
   SSM_ERR_UNSUPPORTED = 2,
-  SSM_ERR_HIP = 3
+  SSM_ERR_HIP = 3,
+  SSM_ERR_HANDOFF_TIMEOUT = 4
 } ssm_status_t;
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
@@ -262,6 +272,17 @@ ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, cons
                           float* ddelta_bias, float* dinitial_state,
                           int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Outcome of the kernels of the last call that used `workspace` (any entry
+ * point taking a workspace): SSM_OK, or SSM_ERR_HANDOFF_TIMEOUT when a chained
+ * hand-off wait of that call ran out (its dependent outputs are then NaN).
+ * Enqueues a 4-byte device-to-host copy of the workspace's status word on
+ * `stream` and synchronises the stream, so it returns after the call's
+ * kernels.  workspace NULL or workspace_bytes 0 (an SSD call that needed no
+ * workspace): SSM_OK.  A workspace below 16 bytes or not 256-byte aligned:
+ * SSM_ERR_INVALID_ARG; a failed copy: SSM_ERR_HIP.  Meaningless for a
+ * workspace no call has used yet. */
+ssm_status_t ssm_workspace_status(const void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable name of a status code (never NULL). */
 const char* ssm_status_string(ssm_status_t s);

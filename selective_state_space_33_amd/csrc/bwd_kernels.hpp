@@ -94,14 +94,15 @@ struct BwdParams {
   unsigned* flags;
   unsigned* ticket;
   unsigned* status;
+  unsigned spin_limit;             // polls per wait (poll_ready)
+  const unsigned* wait_override;   // test hook: a word no one sets, polled instead of every flag
 };
 
 constexpr int kBwdTB = 16;  // tokens per block (the checkpoint spacing)
-// A chained chunk waits for the adjoint handed on to it for at most this many
-// polls (each after a short sleep); past that it records an error bit in the
-// status word and goes on from a NaN adjoint, so the kernel always ends and
-// the gradients that depend on the lost hand-off show the failure.
-constexpr unsigned kBwdSpinLimit = 1u << 18;
+// A chained chunk waits for the adjoint handed on to it with poll_ready; past
+// the limit it sets the status word and goes on from a NaN adjoint, so the
+// kernel always ends and the gradients that depend on the lost hand-off show
+// the failure.
 // vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 s_waitcnt encoding).
 constexpr int kBwdWaitVm0 = 0x0F70;
 
@@ -506,7 +507,8 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   const int o = j / p.n_split, st = j % p.n_split, c = p.Ks - 1 - o;
   const int kb = c * p.chunk_blocks < nblk ? c * p.chunk_blocks : nblk;
   const int ke = (c + 1) * p.chunk_blocks < nblk ? (c + 1) * p.chunk_blocks : nblk;
-  unsigned* my_flag = p.flags + static_cast<int64_t>(st) * p.Ks + c;  // set once chunk c+1 is done
+  // set once chunk c+1 is done
+  const unsigned* my_flag = p.wait_override ? p.wait_override : p.flags + static_cast<int64_t>(st) * p.Ks + c;
   int rest = nblk;
   if (o > 0) rest = run_blocks(0, nblk, my_flag, o * p.chunk_blocks);
   float sdh[NPL], sdA[NPL];
@@ -522,17 +524,13 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   if (o > 0) {
     // the adjoint after chunk c+1: wait for its flag, then read it coherently
     if (tid == 0) {
-      unsigned polls = 0;
-      while (__hip_atomic_load(my_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-        if (++polls > kBwdSpinLimit) {
-          __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(4);
-      }
+      const bool ok = poll_ready(my_flag, p.spin_limit);
+      if (!ok) __hip_atomic_fetch_or(p.status, kStatusHandoffTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sWord = ok ? 1u : 0u;
     }
     __syncthreads();
-    const bool lost = __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+    const bool lost = sWord == 0u;  // this wait ran out (not another's)
+    __syncthreads();                // read by every wavefront before the word is written again
     if (dvalid) {
 #pragma unroll
       for (int q = 0; q < NPL; ++q)

@@ -195,6 +195,34 @@ __device__ __forceinline__ float log1p_exp_neg_abs(float x) {
 }
 __device__ __forceinline__ float softplus_f(float x) { return __builtin_fmaxf(x, 0.0f) + log1p_exp_neg_abs(x); }
 
+// The step from x = delta_raw + bias: softplus(x) with (sp_k, sp_lo) = (1, 0),
+// x itself with (0, -inf); one expression either way, so no branch.
+__device__ __forceinline__ float step_of(float x, float sp_k, float sp_lo) {
+  return __builtin_fmaf(sp_k, log1p_exp_neg_abs(x), __builtin_fmaxf(x, sp_lo));
+}
+
+// Chained launches hand a state (or an adjoint) from one piece of a sequence
+// to the next through the workspace: a ready flag per piece, set by the
+// workgroup that finished the piece before it.  A waiting workgroup's thread 0
+// polls the flag at most `limit` times, each after a short sleep; the default
+// limit (kSpinLimit polls of ~256 clocks) is about a third of a second.  On a
+// time-out the kernel sets kStatusHandoffTimeout in the workspace's status word
+// (word 0, which the host reads back with ssm_workspace_status) and the piece
+// goes on from NaN, so every kernel ends and the outputs that depend on the
+// lost hand-off show the failure.
+constexpr unsigned kSpinLimit = 1u << 18;
+constexpr unsigned kStatusHandoffTimeout = 1u;
+
+// True once *flag is non-zero, false after `limit` polls without it.
+__device__ __forceinline__ bool poll_ready(const unsigned* flag, unsigned limit) {
+  unsigned polls = 0;
+  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+    if (++polls > limit) return false;
+    __builtin_amdgcn_s_sleep(4);
+  }
+  return true;
+}
+
 // A compile-time int as a type (for unrolled steps written as lambdas).
 template <int I> struct IC { static constexpr int value = I; };
 

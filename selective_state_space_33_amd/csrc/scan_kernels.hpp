@@ -75,10 +75,14 @@ struct ScanParams {
   float* aggS;
   float* carry;
   // Chained launches: one ready flag per (split tile, chunk), the workgroup
-  // ticket and a status word (all zeroed by pack_bc_kernel).
+  // ticket and the status word (all zeroed by pack_bc_kernel).  spin_limit
+  // bounds each wait; wait_override (a test hook, normally null) is a word no
+  // one sets, polled instead of every flag, so every wait runs out.
   unsigned* flags;
   unsigned* ticket;
   unsigned* status;
+  unsigned spin_limit;
+  const unsigned* wait_override;
   int64_t batch, L, Lp, dim, N;
   int64_t chunk_len;   // tokens per chunk of a split tile
   int ntd;             // 64-channel tiles per batch row
@@ -114,13 +118,6 @@ constexpr int kModeChainedCkpt = 4;  // kModeChained's plan with kModeCkpt's wor
 // Discretisation rules of scan_kernel.
 constexpr int kRuleEuler = 0;    // h_t = exp(delta_t A) h_{t-1} + delta_t B_t u_t
 constexpr int kRuleTrap = 1;     // the trapezoidal three-term recurrence (Mamba-3), see scan_kernel
-
-// A workgroup waits for the state carried into its chunk for at most this
-// many polls (each after a short sleep); past that it records an error in
-// the status word and goes on from a NaN state, so the kernel always ends and
-// the outputs that depend on the lost hand-off show the failure.
-constexpr unsigned kSpinLimit = 1u << 18;
-constexpr unsigned kStatusCarryTimeout = 1u;
 
 // Tokens per staged block: 16, or 32 where one workgroup has the CU to
 // itself (the block's barrier is then paid half as often, and the staging
@@ -338,11 +335,17 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   // at or past block k_stop once the flag is set (k_end then returns the
   // block it stopped at); the flag is polled once per trip, its load in
   // flight while the trip computes.
+  // Trapezoidal rule: a pass ends with h, except one stopped by its flag,
+  // which leaves the shifted state s for the same workgroup to resume with
+  // resume_s = true; that pass re-derives the previous token's step exactly
+  // as the prologue did, so a tile split at a point that depends on timing
+  // gives the same bits as one pass over it.
   auto run_pass = [&](auto fullc, int k_begin, int& k_end, const unsigned* stop_flag = nullptr,
-                      int k_stop = 0) -> float {
+                      int k_stop = 0, bool resume_s = false) -> float {
     constexpr bool FULL = decltype(fullc)::value;
     static_assert(!FULL || HAS_FULL, "a readout pass needs the partial-readout buffers");
     float delta_total = 0.0f;
+    bool stopped = false;
     if (k_begin >= k_end) return delta_total;
 
     // Raw u, delta_raw, z of kRing blocks (slot = block % kRing).
@@ -364,6 +367,9 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       const int prev_row = k_begin * TB - 1;  // relative to the stretch
       if (!(row_start && k_begin == 0) && t_begin + prev_row >= 0 && prev_row < rows32) {
         if (dvalid) pv_hx = 0.5f * load_elem<IO>(p.u, (b * L + t_begin + prev_row) * dim + d);
+        if (resume_s && dvalid)  // h holds s: the previous token's step, as the prologue computed it
+          pv_d = step_of(load_elem<IO>(p.delta, (b * L + t_begin + prev_row) * dim + d) +
+                             (p.bias ? p.bias[d] : 0.0f), sp_k, sp_lo);
 #pragma unroll
         for (int j = 0; j < NPL; ++j) Bprev[j] = bc_row[static_cast<int64_t>(prev_row) * (2 * NPL) + j];
       }
@@ -410,9 +416,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
         float2 out[VW];
 #pragma unroll
         for (int e = 0; e < VW; ++e) {
-          const float x = df[e] + biasv[e];
           // evaluated either way, so no branch splits the loop body
-          float dl = __builtin_fmaf(sp_k, log1p_exp_neg_abs(x), __builtin_fmaxf(x, sp_lo));
+          float dl = step_of(df[e] + biasv[e], sp_k, sp_lo);
           dl = live ? dl : 0.0f;  // padding token: the identity step (1, 0)
           if constexpr (TRAP) out[e] = make_float2(dl, live ? 0.5f * uf[e] : 0.0f);
           else out[e] = make_float2(dl, dl * uf[e]);
@@ -650,13 +655,14 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
         __syncthreads();
         if (__builtin_bit_cast(unsigned, word(w)) != 0u) {
           k_end = k + kRing;
+          stopped = true;
           break;
         }
       }
     }
     epilogue(IC<1>{}, IC<kRing - 1>{}, k_end - 1);  // k_end is a multiple of kRing (even)
     __syncthreads();  // the staging buffers are free for whatever runs next
-    if constexpr (TRAP) {
+    if (TRAP && !stopped) {
       // back from s to h: h = s + delta (u/2) B of the last token scanned (zero
       // after a padding token, whose step already made the same correction)
       const float e = pv_d * pv_hx;
@@ -712,7 +718,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     // c-1 has handed on its state (chunk 0 goes first).
     int m = c * nb_chunk;
     if (m > nb_whole) m = nb_whole;
-    unsigned* my_flag = p.flags + static_cast<int64_t>(st) * p.Ks + c;
+    const unsigned* my_flag = p.wait_override ? p.wait_override : p.flags + static_cast<int64_t>(st) * p.Ks + c;
     if (c > 0) {
       m = nb_whole;
       run_pass(IC<FULLC>{}, 0, m, my_flag, c * nb_chunk);
@@ -732,18 +738,15 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     // (Release/acquire fences would instead write back or invalidate the
     // whole L2, slowing every workgroup on the XCD.)
     if (c > 0) {
+      // the staging buffer is free between passes: its first word carries the outcome of the wait
       if (tid == 0) {
-        unsigned polls = 0;
-        while (__hip_atomic_load(my_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-          if (++polls > kSpinLimit) {
-            __hip_atomic_fetch_or(p.status, kStatusCarryTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(4);
-        }
+        const bool ok = poll_ready(my_flag, p.spin_limit);
+        if (!ok) __hip_atomic_fetch_or(p.status, kStatusHandoffTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *sTicket = ok ? 1u : 0u;
       }
       __syncthreads();
-      const bool lost = __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+      const bool lost = *sTicket == 0u;  // this wait ran out (not another's)
+      __syncthreads();  // read by every wavefront before the pass stages into the buffer
       if (dvalid) {
 #pragma unroll
         for (int q = 0; q < NPL; ++q)
@@ -771,7 +774,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     set_tile(j, 0, L);
 #pragma unroll
     for (int q = 0; q < NPL; ++q) h[q] = hw[q];
-    run_pass(IC<FULLC>{}, m, nb_whole);
+    run_pass(IC<FULLC>{}, m, nb_whole, nullptr, 0, true);  // resumes h as the first part left it
     write_final_state(b);
   } else {
     // ---- which tile and which part of the sequence this workgroup scans

@@ -69,13 +69,14 @@ struct SsdParams {
   unsigned* flags;
   unsigned* ticket;
   unsigned* status;
+  unsigned spin_limit;             // polls per wait (poll_ready)
+  const unsigned* wait_override;   // test hook: a word no one sets, polled instead of every flag
 };
 
-// A chained segment waits for the state handed on to it for at most this
-// many polls (each after a short sleep); past that it records an error bit in
-// the status word and goes on from a NaN state, so the kernel always ends and
-// the outputs that depend on the lost hand-off show the failure.
-constexpr unsigned kSsdSpinLimit = 1u << 18;
+// A chained segment waits for the state handed on to it with poll_ready; past
+// the limit it sets the status word and goes on from a NaN state, so the
+// kernel always ends and the outputs that depend on the lost hand-off show the
+// failure.
 constexpr int kSsdWaitVm0 = 0x0F70;  // vmcnt(0), other counters at their maxima (gfx9 s_waitcnt)
 
 // Zeroes the flags, ticket and status of a chained launch.
@@ -505,7 +506,9 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   const int seg_chunks = static_cast<int>(p.seg_chunks);
   const int kb = sg * seg_chunks < nchunks ? sg * seg_chunks : nchunks;
   const int ke = (sg + 1) * seg_chunks < nchunks ? (sg + 1) * seg_chunks : nchunks;
-  unsigned* my_flag = has_seg ? p.flags + static_cast<int64_t>(st) * p.Ks + sg : nullptr;  // set once sg-1 is done
+  // set once segment sg-1 is done
+  const unsigned* my_flag =
+      has_seg ? (p.wait_override ? p.wait_override : p.flags + static_cast<int64_t>(st) * p.Ks + sg) : nullptr;
   float* crow = has_seg ? p.carry + (static_cast<int64_t>(st) * p.Ks + sg) * P * N : nullptr;  // [n_split][Ks][P][N]
   // the state of unit `unit` before its token 0: zero, or the given one
   auto initial = [&](int unit, f32x4_t* dst) {
@@ -538,17 +541,13 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
     if (phase == 1 && sg > 0) {
       // the state after segment sg-1: wait for its flag, then read it coherently
       if (tid == 0) {
-        unsigned polls = 0;
-        while (__hip_atomic_load(my_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-          if (++polls > kSsdSpinLimit) {
-            __hip_atomic_fetch_or(p.status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(4);
-        }
+        const bool ok = poll_ready(my_flag, p.spin_limit);
+        if (!ok) __hip_atomic_fetch_or(p.status, kStatusHandoffTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        sWord = ok ? 1u : 0u;
       }
       __syncthreads();
-      const bool lost = __hip_atomic_load(p.status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+      const bool lost = sWord == 0u;  // this wait ran out (not another's)
+      __syncthreads();                // read by every wavefront before the word is written again
 #pragma unroll
       for (int i = 0; i < HT; ++i)
 #pragma unroll

@@ -5,7 +5,7 @@
 // (states per lane, wavefronts per workgroup, which tiles are cut into
 // sequence chunks) and enqueues the kernels of scan_kernels.hpp and
 // decode_kernel.hpp on the caller's stream.  It allocates nothing and keeps
-// no state.
+// no state beyond each device's compute-unit count, looked up once.
 #include "ssm_scan.h"
 
 #include <hip/hip_runtime.h>
@@ -13,8 +13,10 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+
 #include "carry_kernel.hpp"
 #include "decode_kernel.hpp"
+#include "host_common.hpp"
 #include "order_kernel.hpp"
 #include "scan_launch.hpp"
 
@@ -24,7 +26,6 @@ namespace {
 constexpr int64_t kMaxBatch = 65535;
 constexpr int64_t kChunkQuantum = kTrip;  // chunk lengths are multiples of the main loop trip
 constexpr int64_t kMinChunk = 256;        // never cut the sequence finer than this
-constexpr int64_t kNumCU = 256;           // MI355X compute units: the work is balanced over these
 constexpr int64_t kMaxChunks = 4096;      // chunks per split tile
 constexpr int64_t kMaxChained = 8;        // chunks per tile in a chained launch (the carry hops in series)
 
@@ -56,12 +57,12 @@ struct Plan {
   bool trap;     // trapezoidal rule: also C_t . B_t per token
 };
 
-// Workspace layout: [packed B/C][chunk fades P][chunk states S][carried-in
-// states][flags, ticket, status][sequence order][C_t . B_t].  The chained
-// plan needs no P, S; the others no flags; only the packed plan has an
-// order, only the trapezoidal rule C . B.
+// Workspace layout: [header words (status, ticket, ...) and ready flags]
+// [packed B/C][chunk fades P][chunk states S][carried-in states][sequence
+// order][C_t . B_t].  The chained plan needs no P, S and has a flag per
+// chunk; only the packed plan has an order, only the trapezoidal rule C . B.
 struct Layout {
-  size_t bc, pairs, carry, words, order, cb, total;
+  size_t words, bc, pairs, carry, order, cb, total;
   int n_words;
 };
 
@@ -69,14 +70,14 @@ Layout layout_for(const Plan& pl, int64_t batch) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
   const size_t per = static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float);
   Layout l;
+  l.n_words = kHeaderWords + (pl.chained ? pl.n_split * pl.Ks : 0);
+  l.words = align256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
   l.bc = align256((static_cast<size_t>(batch) * pl.Lp + kTBMax) * 2 * npad * sizeof(float));
   l.pairs = (pl.n_split > 0 && !pl.chained && !pl.packed) ? align256(per) : 0;
   l.carry = (pl.n_split > 0 && !pl.packed) ? align256(per) : 0;
-  l.n_words = pl.chained ? pl.n_split * pl.Ks + 2 : 0;
-  l.words = align256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
   l.order = pl.packed ? align256(static_cast<size_t>(pl.Ks) * sizeof(int)) : 0;
   l.cb = pl.trap ? align256(static_cast<size_t>(batch) * (pl.Lp + kTBMax) * sizeof(float)) : 0;
-  l.total = l.bc + 2 * l.pairs + l.carry + l.words + l.order + l.cb;
+  l.total = l.words + l.bc + 2 * l.pairs + l.carry + l.order + l.cb;
   return l;
 }
 
@@ -136,6 +137,7 @@ int env_flag(const char* name) {  // -1 when unset
 // vw_ok: the widest token-row access the pointers and dim allow (4, 2 or 1);
 // it decides the prologue width, not the split.
 void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int vw_ok, Plan* pl) {
+  const int64_t kNumCU = device_cu_count();
   int npl, G, Kreq = 0;
   if (N == 16) {
     // 2 states per lane over 8 wavefronts: 80 KB of LDS, two workgroups per CU.
@@ -225,6 +227,7 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
 // sequence) is one readout-pass unit from its own initial state, with no
 // chunking of a sequence.
 void plan_packed(int64_t L, int64_t dim, int64_t N, int vw_ok, int64_t nseq, Plan* pl) {
+  const int64_t kNumCU = device_cu_count();
   int npl, G;
   if (N == 16) {
     npl = 2;
@@ -273,7 +276,7 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
 #define SSM_PACK_CASE(NPL_)                                                                                  \
   if (pl.npl == NPL_)                                                                                       \
     hipLaunchKernelGGL((pack_bc_kernel<IO, NPL_>), pgrid, dim3(256), 0, s, B, C, bc, p.batch, p.L, pl.Lp, p.N, \
-                       pl.G, p.flags, lay.n_words, const_cast<float*>(p.cb));
+                       pl.G, p.status, lay.n_words, const_cast<float*>(p.cb));
   SSM_PACK_CASE(1)
   SSM_PACK_CASE(2)
   SSM_PACK_CASE(4)
@@ -434,6 +437,7 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
   if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256)) return SSM_ERR_INVALID_ARG;
 
   char* ws = static_cast<char*>(workspace);
+  unsigned* words = reinterpret_cast<unsigned*>(ws);
   ScanParams p = {};
   p.u = u;
   p.delta = delta;
@@ -441,14 +445,18 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
   p.D = D;
   p.z = z;
   p.bias = delta_bias;
-  p.bc = reinterpret_cast<const float*>(ws);
+  p.bc = reinterpret_cast<const float*>(ws + lay.words);
   p.y = y;
   p.final_state = final_state;
   p.aggP = p.aggS = p.carry = nullptr;
-  p.flags = p.ticket = p.status = nullptr;
+  p.status = words + kWordStatus;
+  p.ticket = words + kWordTicket;
+  p.flags = pl.chained ? words + kHeaderWords : nullptr;  // [n_split][Ks]
+  p.spin_limit = wait_spin_limit();
+  p.wait_override = wait_override(words);
   p.h0 = h0;
   p.cu = cu_seqlens;
-  size_t off = lay.bc;
+  size_t off = lay.words + lay.bc;
   if (lay.pairs) {
     p.aggP = reinterpret_cast<float*>(ws + off);
     p.aggS = reinterpret_cast<float*>(ws + off + lay.pairs);
@@ -457,13 +465,6 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
   if (lay.carry) {
     p.carry = reinterpret_cast<float*>(ws + off);
     off += lay.carry;
-  }
-  if (lay.n_words) {
-    unsigned* words = reinterpret_cast<unsigned*>(ws + off);
-    p.flags = words;                                           // [n_split][Ks]
-    p.ticket = words + static_cast<int64_t>(pl.n_split) * pl.Ks;
-    p.status = p.ticket + 1;
-    off += lay.words;
   }
   const char* oe = getenv("SSM_SCAN_ORDER");
   p.order = (lay.order && !(oe && atoi(oe) == 0)) ? reinterpret_cast<const int*>(ws + off) : nullptr;
@@ -480,7 +481,7 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
   p.n_split = pl.n_split;
   p.Ks = pl.Ks;
   p.softplus = softplus_flag ? 1 : 0;
-  float* bc = reinterpret_cast<float*>(ws);
+  float* bc = reinterpret_cast<float*>(ws + lay.words);
   hipError_t e;
   if (pl.trap)
     e = dt == SSM_DTYPE_F32 ? run_scan<F32, kRuleTrap>(pl, lay, B, C, bc, p, stream)
@@ -574,12 +575,24 @@ extern "C" ssm_status_t ssm_state_update(float* state, const void* u, const void
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+extern "C" ssm_status_t ssm_workspace_status(const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace || workspace_bytes == 0) return SSM_OK;  // no workspace: no chained plan ran
+  if (workspace_bytes < kHeaderWords * sizeof(unsigned) || !aligned(workspace, 256)) return SSM_ERR_INVALID_ARG;
+  unsigned status = 0;
+  if (hipMemcpyAsync(&status, static_cast<const unsigned*>(workspace) + kWordStatus, sizeof(status),
+                     hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return SSM_ERR_HIP;
+  return (status & kStatusHandoffTimeout) ? SSM_ERR_HANDOFF_TIMEOUT : SSM_OK;
+}
+
 extern "C" const char* ssm_status_string(ssm_status_t s) {
   switch (s) {
     case SSM_OK: return "SSM_OK";
     case SSM_ERR_INVALID_ARG: return "SSM_ERR_INVALID_ARG";
     case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED";
     case SSM_ERR_HIP: return "SSM_ERR_HIP";
+    case SSM_ERR_HANDOFF_TIMEOUT: return "SSM_ERR_HANDOFF_TIMEOUT";
   }
   return "SSM_ERR_UNKNOWN";
 }

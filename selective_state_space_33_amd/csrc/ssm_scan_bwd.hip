@@ -18,6 +18,7 @@
 #include <stdlib.h>
 
 #include "bwd_kernels.hpp"
+#include "host_common.hpp"
 #include "scan_launch.hpp"
 
 namespace ssm {
@@ -25,7 +26,8 @@ namespace {
 
 constexpr int64_t kBwdMaxBatch = 65535;
 constexpr int64_t kBwdMaxState = 32;
-constexpr int64_t kBwdNumCU = 256;  // MI355X compute units
+constexpr int64_t kBwdMaxChained = 8;  // chunks per left-over tile (the hand-offs run in series)
+constexpr int64_t kBwdMinChunk = 256;   // tokens: the checkpoint pass never cuts the sequence finer
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -33,7 +35,9 @@ bool is_aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p
 
 // Variant: 2 states per lane over 8 wavefronts up to 16 states, 4 per lane up to 32.
 // Chained plan (CUs < T <= 1.5 CUs): n_long = CUs whole tiles, the r = T - CUs
-// others in Ks = CUs / r chunks of blocks (at most 8).
+// others in Ks = CUs / r chunks of blocks (at most 8); the checkpoint pass is
+// chained the same way, as the forward plans it: Kc = CUs / r chunks, at most
+// 8 and no shorter than 256 tokens, in whole trips of its loop.
 struct BwdPlan {
   int npl, G;
   int64_t Lp, ntd, T, ckpt_blocks;
@@ -59,26 +63,32 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
   pl.ck_len = 0;
   const char* env = getenv("SSM_BWD_CHAINED");
   const bool chained_ok = !(env && atoi(env) == 0);
+  const int64_t kBwdNumCU = device_cu_count();
   if (chained_ok && pl.T > kBwdNumCU && 2 * (pl.T - kBwdNumCU) <= kBwdNumCU) {
     const int64_t r = pl.T - kBwdNumCU;
     int64_t K = kBwdNumCU / r;
-    if (K > 8) K = 8;
+    if (K > kBwdMaxChained) K = kBwdMaxChained;
     pl.n_long = static_cast<int>(kBwdNumCU);
     pl.n_split = static_cast<int>(r);
     pl.Ks = static_cast<int>(K);
     pl.chunk_blocks = static_cast<int>(cdiv(cdiv(L, kBwdTB), K));
     // the forward's chained plan for the checkpoints: chunk lengths in whole trips of its loop
-    pl.Kc = static_cast<int>(kBwdNumCU / r);
-    pl.ck_len = cdiv(cdiv(L, pl.Kc), kTrip) * kTrip;
+    int64_t Kc = kBwdNumCU / r;
+    if (Kc > kBwdMaxChained) Kc = kBwdMaxChained;
+    if (Kc > cdiv(L, kBwdMinChunk)) Kc = cdiv(L, kBwdMinChunk);
+    if (Kc < 1) Kc = 1;
+    pl.ck_len = cdiv(cdiv(L, Kc), kTrip) * kTrip;
+    pl.Kc = static_cast<int>(cdiv(L, pl.ck_len));
   }
   return pl;
 }
 
-// Workspace: [packed B/C][checkpoints][dB, dC partials][dA, dD, dbias
-// partials (Ks slots)][carried adjoints][carried checkpoint-pass states]
-// [flags, ticket, status of the backward; the same of the checkpoint pass].
+// Workspace: [header words (status, the two launches' tickets, ...), ready
+// flags of the backward, then of the checkpoint pass][packed B/C]
+// [checkpoints][dB, dC partials][dA, dD, dbias partials (Ks slots)][carried
+// adjoints][carried checkpoint-pass states].
 struct BwdLayout {
-  size_t bc, ckpt, bcpart, apart, dpart, carry, ckcarry, words, total;
+  size_t words, bc, ckpt, bcpart, apart, dpart, carry, ckcarry, total;
   int n_words, bwd_words;
 };
 
@@ -86,6 +96,9 @@ BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t dim) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
   const int64_t slots = pl.n_split > 0 ? pl.Ks : 1;
   BwdLayout l;
+  l.bwd_words = pl.n_split > 0 ? pl.n_split * pl.Ks : 0;
+  l.n_words = kHeaderWords + l.bwd_words + (pl.n_split > 0 ? pl.n_split * pl.Kc : 0);
+  l.words = al256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
   l.bc = al256(static_cast<size_t>(batch * pl.Lp + kTBMax) * 2 * npad * sizeof(float));
   l.ckpt = al256(static_cast<size_t>(pl.T * pl.ckpt_blocks) * 64 * npad * sizeof(float));
   l.bcpart = al256(static_cast<size_t>(batch * pl.ntd * pl.Lp) * npad * sizeof(float));
@@ -93,10 +106,7 @@ BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t dim) {
   l.dpart = al256(static_cast<size_t>(slots * batch * dim) * sizeof(float));
   l.carry = al256(static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float));
   l.ckcarry = al256(static_cast<size_t>(pl.n_split) * pl.Kc * 64 * npad * sizeof(float));
-  l.bwd_words = pl.n_split > 0 ? pl.n_split * pl.Ks + 2 : 0;
-  l.n_words = pl.n_split > 0 ? l.bwd_words + pl.n_split * pl.Kc + 2 : 0;
-  l.words = al256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
-  l.total = l.bc + l.ckpt + 2 * l.bcpart + l.apart + 2 * l.dpart + l.carry + l.ckcarry + l.words;
+  l.total = l.words + l.bc + l.ckpt + 2 * l.bcpart + l.apart + 2 * l.dpart + l.carry + l.ckcarry;
   return l;
 }
 
@@ -109,13 +119,13 @@ hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const
                    BwdParams bp, void* dB, void* dC, float* dA, float* dD, float* dbias, int vw, hipStream_t s) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
   const dim3 pgrid(static_cast<unsigned>(sp.batch * (pl.Lp / kPackT)));
-  // the pack also zeroes the chained launch's flags, ticket and status
+  // the pack also zeroes the header words and the chained launches' flags
   if (pl.npl == 2)
     hipLaunchKernelGGL((pack_bc_kernel<IO, 2>), pgrid, dim3(256), 0, s, B, C, bc, sp.batch, sp.L, pl.Lp, sp.N,
-                       pl.G, bp.flags, lay.n_words, static_cast<float*>(nullptr));
+                       pl.G, bp.status, lay.n_words, static_cast<float*>(nullptr));
   else
     hipLaunchKernelGGL((pack_bc_kernel<IO, 4>), pgrid, dim3(256), 0, s, B, C, bc, sp.batch, sp.L, pl.Lp, sp.N,
-                       pl.G, bp.flags, lay.n_words, static_cast<float*>(nullptr));
+                       pl.G, bp.status, lay.n_words, static_cast<float*>(nullptr));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (pl.n_split > 0)
@@ -194,7 +204,8 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   }
   const int vw = preferred_vw(pl.G) <= vw_ok ? preferred_vw(pl.G) : 1;
 
-  char* ws = static_cast<char*>(workspace);
+  unsigned* words = static_cast<unsigned*>(workspace);
+  char* ws = static_cast<char*>(workspace) + lay.words;
   float* bc = reinterpret_cast<float*>(ws);
   float* ckpt = reinterpret_cast<float*>(ws + lay.bc);
   float* dB_part = reinterpret_cast<float*>(ws + lay.bc + lay.ckpt);
@@ -205,7 +216,8 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   char* tail = ws + lay.bc + lay.ckpt + 2 * lay.bcpart + lay.apart + 2 * lay.dpart;
   float* carry = lay.carry ? reinterpret_cast<float*>(tail) : nullptr;
   float* ckcarry = lay.ckcarry ? reinterpret_cast<float*>(tail + lay.carry) : nullptr;
-  unsigned* words = lay.n_words ? reinterpret_cast<unsigned*>(tail + lay.carry + lay.ckcarry) : nullptr;
+  const unsigned spin = wait_spin_limit();
+  const unsigned* never = wait_override(words);
 
   ScanParams sp = {};
   sp.u = u;
@@ -232,9 +244,11 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
     sp.Ks = pl.Kc;
     sp.chunk_len = pl.ck_len;
     sp.carry = ckcarry;
-    sp.flags = words + lay.bwd_words;
-    sp.ticket = sp.flags + static_cast<int64_t>(pl.n_split) * pl.Kc;
-    sp.status = sp.ticket + 1;
+    sp.flags = words + kHeaderWords + lay.bwd_words;  // [n_split][Kc]
+    sp.ticket = words + kWordTicket2;
+    sp.status = words + kWordStatus;
+    sp.spin_limit = spin;
+    sp.wait_override = never;
   }
 
   BwdParams bp = {};
@@ -270,9 +284,11 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   bp.Ks = pl.Ks;
   bp.chunk_blocks = pl.chunk_blocks;
   bp.carry = carry;
-  bp.flags = words;
-  bp.ticket = words ? words + static_cast<int64_t>(pl.n_split) * pl.Ks : nullptr;
-  bp.status = words ? bp.ticket + 1 : nullptr;
+  bp.flags = pl.n_split > 0 ? words + kHeaderWords : nullptr;  // [n_split][Ks]
+  bp.ticket = words + kWordTicket;
+  bp.status = words + kWordStatus;
+  bp.spin_limit = spin;
+  bp.wait_override = never;
 
   float* dD_out = D ? dD : nullptr;
   float* dbias_out = delta_bias ? ddelta_bias : nullptr;

@@ -13,17 +13,18 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+#include "host_common.hpp"
 #include "ssd_kernel.hpp"
 #include "ssm_scan.h"
 
 namespace ssm {
 namespace {
 
-constexpr int64_t kSsdNumCU = 256;  // MI355X compute units
-
 bool ssd_aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 size_t ssd_al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
+// Workspace of the chained plan: [header words (status, ticket, ...) and
+// ready flags][carried states]; none otherwise.
 struct SsdPlan {
   int n_long, n_split, Ks;
   int64_t seg_chunks;
@@ -35,6 +36,7 @@ SsdPlan plan_ssd(int64_t batch, int64_t L, int64_t heads, int64_t dstate) {
   SsdPlan pl = {};
   pl.Ks = 1;
   const int64_t T = batch * heads;
+  const int64_t kSsdNumCU = device_cu_count();
   const char* env = getenv("SSM_SSD_CHAINED");
   const bool chained_ok = !(env && atoi(env) == 0);
   if (chained_ok && T > kSsdNumCU && 2 * (T - kSsdNumCU) <= kSsdNumCU) {
@@ -47,7 +49,7 @@ SsdPlan plan_ssd(int64_t batch, int64_t L, int64_t heads, int64_t dstate) {
     pl.Ks = static_cast<int>(K);
     pl.seg_chunks = (nchunks + K - 1) / K;
     pl.carry_bytes = ssd_al256(static_cast<size_t>(r * K) * kSsdP * dstate * sizeof(float));
-    pl.n_words = static_cast<int>(r * K + 2);
+    pl.n_words = static_cast<int>(kHeaderWords + r * K);
     pl.word_bytes = ssd_al256(static_cast<size_t>(pl.n_words) * sizeof(unsigned));
   }
   pl.total = pl.carry_bytes + pl.word_bytes;
@@ -119,12 +121,14 @@ extern "C" ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const floa
   p.Ks = pl.Ks;
   p.seg_chunks = pl.seg_chunks;
   if (pl.n_split > 0) {
-    char* ws = static_cast<char*>(workspace);
-    p.carry = reinterpret_cast<float*>(ws);
-    p.flags = reinterpret_cast<unsigned*>(ws + pl.carry_bytes);  // [n_split][Ks], then the ticket and status
-    p.ticket = p.flags + static_cast<int64_t>(pl.n_split) * pl.Ks;
-    p.status = p.ticket + 1;
-    hipLaunchKernelGGL(ssd_zero_words_kernel, dim3(1), dim3(256), 0, stream, p.flags, pl.n_words);
+    unsigned* words = static_cast<unsigned*>(workspace);
+    p.status = words + kWordStatus;
+    p.ticket = words + kWordTicket;
+    p.flags = words + kHeaderWords;  // [n_split][Ks]
+    p.carry = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.word_bytes);
+    p.spin_limit = wait_spin_limit();
+    p.wait_override = wait_override(words);
+    hipLaunchKernelGGL(ssd_zero_words_kernel, dim3(1), dim3(256), 0, stream, words, pl.n_words);
     const hipError_t ez = hipGetLastError();
     if (ez != hipSuccess) return SSM_ERR_HIP;
   }

@@ -2,9 +2,17 @@
 
 The functions carry the names of the C entry points and only marshal
 arguments: tensor checks, default outputs/workspace allocated with torch on
-the inputs' device, and the raw device pointers plus the current HIP stream
-handed to the library.  Every step of the computation runs in the HIP
-kernels; there is no fallback.  If the library is missing, ``lib()`` raises.
+the inputs' device, and the raw device pointers plus the HIP stream handed
+to the library.  Every step of the computation runs in the HIP kernels;
+there is no fallback.  If the library is missing, ``lib()`` raises.
+
+Streams: the kernels run on ``stream`` (default: the device's current
+stream).  Outputs and workspaces allocated here are allocated while that
+stream is current, so torch's caching allocator ties their memory to it and
+does not hand it to other streams' work while the kernels may still use it.
+``check_status=True`` reads the workspace's status word back after the call
+(ssm_workspace_status, which synchronises the stream) and raises if a chained
+hand-off wait ran out.
 """
 from __future__ import annotations
 
@@ -17,14 +25,14 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 
-SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP = 0, 1, 2, 3
+SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP, SSM_ERR_HANDOFF_TIMEOUT = 0, 1, 2, 3, 4
 SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 
 # Every symbol include/ssm_scan.h declares.
 EXPORTED = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_ex_workspace_size", "ssm_scan_fwd_ex",
             "ssm_scan_trap_fwd_workspace_size", "ssm_scan_trap_fwd", "ssm_ssd_fwd_workspace_size", "ssm_ssd_fwd",
             "ssm_state_update",
-            "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_status_string")
+            "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_workspace_status", "ssm_status_string")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -70,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_bwd.restype = ctypes.c_int
         L.ssm_scan_bwd.argtypes = ([_vp] * 8 + [ctypes.c_int] + [_vp] * 12 + [_i64] * 4 +
                                    [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
+        L.ssm_workspace_status.restype = ctypes.c_int
+        L.ssm_workspace_status.argtypes = [_vp, ctypes.c_size_t, _vp]
         L.ssm_status_string.restype = ctypes.c_char_p
         L.ssm_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -107,10 +117,27 @@ def _check(t: Optional[torch.Tensor], name: str, dtype, shape, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _stream(device, stream) -> int:
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return stream.cuda_stream
+def _resolve(device, stream):
+    """The torch stream the kernels run on: `stream`, or the device's current stream."""
+    return torch.cuda.current_stream(device) if stream is None else stream
+
+
+def _ws_bytes(workspace) -> int:
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def ssm_workspace_status(workspace, stream=None) -> int:
+    """Status code the last call that used `workspace` left in it (synchronises `stream`):
+    SSM_OK, or SSM_ERR_HANDOFF_TIMEOUT if a chained hand-off wait ran out."""
+    dev = workspace.device if workspace is not None else torch.device("cuda", torch.cuda.current_device())
+    s = _resolve(dev, stream)
+    return int(lib().ssm_workspace_status(_ptr(workspace), _ws_bytes(workspace), s.cuda_stream))
+
+
+def _check_status(workspace, stream, where):
+    rc = ssm_workspace_status(workspace, stream)
+    if rc != SSM_OK:
+        raise SSMError(rc, where)
 
 
 def ssm_scan_workspace_size(batch: int, L: int, dim: int, dstate: int, dtype: torch.dtype) -> int:
@@ -118,7 +145,8 @@ def ssm_scan_workspace_size(batch: int, L: int, dim: int, dstate: int, dtype: to
 
 
 def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
-                 y=None, final_state=None, workspace=None, return_final_state: bool = True, stream=None):
+                 y=None, final_state=None, workspace=None, return_final_state: bool = True, stream=None,
+                 check_status: bool = False):
     """Selective scan from a zero state on the GPU.
 
     u, delta, z: [batch, L, dim]; B, C: [batch, L, dstate] (float32 or bfloat16,
@@ -135,33 +163,37 @@ def ssm_scan_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: b
     _check(A, "A", torch.float32, (dim, dstate), dev)
     _check(D, "D", torch.float32, (dim,), dev)
     _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
-    if y is None:
-        y = torch.empty((batch, L, dim), dtype=dt, device=dev)
+    s = _resolve(dev, stream)
+    with torch.cuda.stream(s):
+        if y is None:
+            y = torch.empty((batch, L, dim), dtype=dt, device=dev)
+        if final_state is None and return_final_state:
+            final_state = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+        need = ssm_scan_workspace_size(batch, L, dim, dstate, dt)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(y, "y", dt, (batch, L, dim), dev)
-    if final_state is None and return_final_state:
-        final_state = torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
     _check(final_state, "final_state", torch.float32, (batch, dim, dstate), dev)
-    need = ssm_scan_workspace_size(batch, L, dim, dstate, dt)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().ssm_scan_fwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                             1 if softplus else 0, _ptr(y), _ptr(final_state), batch, L, dim, dstate, code,
-                            _ptr(workspace), ws_bytes, _stream(dev, stream))
+                            _ptr(workspace), _ws_bytes(workspace), s.cuda_stream)
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_scan_fwd")
+    if check_status:
+        _check_status(workspace, s, "ssm_scan_fwd")
     return y, final_state
 
 
 def ssm_scan_fwd_ex(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
-                    initial_state=None, cu_seqlens=None, y=None, final_state=None, workspace=None, stream=None):
+                    initial_state=None, cu_seqlens=None, y=None, final_state=None, workspace=None, stream=None,
+                    check_status: bool = False):
     """ssm_scan_fwd from given initial states and/or over packed sequences.
 
     initial_state: [rows, dim, dstate] float32 (rows = batch, or the number of sequences).
     cu_seqlens: int64 device tensor of nseq + 1 offsets into the L axis of batch row 0 (batch must be 1).
     Returns (y, final_state [rows, dim, dstate])."""
     return _fwd_rows("ssm_scan_fwd_ex", u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, cu_seqlens,
-                     y, final_state, workspace, stream)
+                     y, final_state, workspace, stream, check_status)
 
 
 def ssm_scan_trap_fwd_workspace_size(batch: int, L: int, dim: int, dstate: int, nseq: int,
@@ -170,14 +202,15 @@ def ssm_scan_trap_fwd_workspace_size(batch: int, L: int, dim: int, dstate: int, 
 
 
 def ssm_scan_trap_fwd(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True,
-                      initial_state=None, cu_seqlens=None, y=None, final_state=None, workspace=None, stream=None):
+                      initial_state=None, cu_seqlens=None, y=None, final_state=None, workspace=None, stream=None,
+                      check_status: bool = False):
     """The Mamba-3 trapezoidal three-term scan; arguments and results as ssm_scan_fwd_ex."""
     return _fwd_rows("ssm_scan_trap_fwd", u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, cu_seqlens,
-                     y, final_state, workspace, stream)
+                     y, final_state, workspace, stream, check_status)
 
 
 def _fwd_rows(entry, u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, cu_seqlens, y, final_state,
-              workspace, stream):
+              workspace, stream, check_status=False):
     batch, L, dim = u.shape
     dstate = A.shape[1]
     dev, dt = u.device, u.dtype
@@ -197,22 +230,25 @@ def _fwd_rows(entry, u, delta, A, B, C, D, z, delta_bias, softplus, initial_stat
     _check(D, "D", torch.float32, (dim,), dev)
     _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
     _check(initial_state, "initial_state", torch.float32, (rows, dim, dstate), dev)
-    if y is None:
-        y = torch.empty((batch, L, dim), dtype=dt, device=dev)
+    s = _resolve(dev, stream)
+    with torch.cuda.stream(s):
+        if y is None:
+            y = torch.empty((batch, L, dim), dtype=dt, device=dev)
+        if final_state is None:
+            final_state = torch.empty((rows, dim, dstate), dtype=torch.float32, device=dev)
+        need = int(getattr(lib(), entry + "_workspace_size")(batch, L, dim, dstate, nseq, code))
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(y, "y", dt, (batch, L, dim), dev)
-    if final_state is None:
-        final_state = torch.empty((rows, dim, dstate), dtype=torch.float32, device=dev)
     _check(final_state, "final_state", torch.float32, (rows, dim, dstate), dev)
-    need = int(getattr(lib(), entry + "_workspace_size")(batch, L, dim, dstate, nseq, code))
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = getattr(lib(), entry)(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                                1 if softplus else 0, _ptr(initial_state), _ptr(cu_seqlens), nseq, _ptr(y),
-                               _ptr(final_state), batch, L, dim, dstate, code, _ptr(workspace), ws_bytes,
-                               _stream(dev, stream))
+                               _ptr(final_state), batch, L, dim, dstate, code, _ptr(workspace),
+                               _ws_bytes(workspace), s.cuda_stream)
     if rc != SSM_OK:
         raise SSMError(rc, entry)
+    if check_status:
+        _check_status(workspace, s, entry)
     return y, final_state
 
 
@@ -222,7 +258,8 @@ def ssm_ssd_fwd_workspace_size(batch: int, L: int, heads: int, headdim: int, dst
 
 
 def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bool = True, initial_state=None,
-                y=None, final_state=None, return_final_state: bool = True, workspace=None, stream=None):
+                y=None, final_state=None, return_final_state: bool = True, workspace=None, stream=None,
+                check_status: bool = False):
     """The Mamba-2 SSD layer on the GPU.
 
     x, z: [batch, L, heads, headdim]; delta: [batch, L, heads]; B, C: [batch, L, dstate] (bfloat16);
@@ -239,22 +276,24 @@ def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bo
     for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias)):
         _check(t, name, torch.float32, (heads,), dev)
     _check(initial_state, "initial_state", torch.float32, (batch, heads, headdim, dstate), dev)
-    if y is None:
-        y = torch.empty_like(x)
+    s = _resolve(dev, stream)
+    with torch.cuda.stream(s):
+        if y is None:
+            y = torch.empty_like(x)
+        if final_state is None and return_final_state:
+            final_state = torch.empty((batch, heads, headdim, dstate), dtype=torch.float32, device=dev)
+        need = ssm_ssd_fwd_workspace_size(batch, L, heads, headdim, dstate, dt)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(y, "y", dt, (batch, L, heads, headdim), dev)
-    if final_state is None and return_final_state:
-        final_state = torch.empty((batch, heads, headdim, dstate), dtype=torch.float32, device=dev)
     _check(final_state, "final_state", torch.float32, (batch, heads, headdim, dstate), dev)
-    need = ssm_ssd_fwd_workspace_size(batch, L, heads, headdim, dstate, dt)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                            1 if softplus else 0, _ptr(initial_state), _ptr(y), _ptr(final_state), batch, L, heads,
-                           headdim, dstate, code,
-                           _ptr(workspace), ws_bytes, _stream(dev, stream))
+                           headdim, dstate, code, _ptr(workspace), _ws_bytes(workspace), s.cuda_stream)
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_ssd_fwd")
+    if check_status:
+        _check_status(workspace, s, "ssm_ssd_fwd")
     return y, final_state
 
 
@@ -275,12 +314,14 @@ def ssm_state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, 
     _check(A, "A", torch.float32, (dim, dstate), dev)
     _check(D, "D", torch.float32, (dim,), dev)
     _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
+    s = _resolve(dev, stream)
     if y is None:
-        y = torch.empty((batch, dim), dtype=dt, device=dev)
+        with torch.cuda.stream(s):
+            y = torch.empty((batch, dim), dtype=dt, device=dev)
     _check(y, "y", dt, (batch, dim), dev)
     rc = lib().ssm_state_update(_ptr(state), _ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
                                 _ptr(delta_bias), 1 if softplus else 0, _ptr(y), batch, dim, dstate, code,
-                                _stream(dev, stream))
+                                s.cuda_stream)
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_state_update")
     return y
@@ -296,7 +337,7 @@ def ssm_scan_bwd_workspace_size(batch: int, L: int, dim: int, dstate: int, dtype
 
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus: bool = True,
                  dfinal_state=None, initial_state=None, want_dinitial_state: bool = False, workspace=None,
-                 stream=None):
+                 stream=None, check_status: bool = False):
     """Backward of ssm_scan_fwd on the GPU: gradients of sum(y*dy) + sum(final_state*dfinal_state).
 
     Same inputs as ssm_scan_fwd plus dy [batch, L, dim] (storage dtype) and dfinal_state
@@ -316,22 +357,24 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
     _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
     _check(dfinal_state, "dfinal_state", torch.float32, (batch, dim, dstate), dev)
     _check(initial_state, "initial_state", torch.float32, (batch, dim, dstate), dev)
-    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(delta), dB=torch.empty_like(B),
-             dC=torch.empty_like(C), dA=torch.empty_like(A),
-             dD=None if D is None else torch.empty_like(D), dz=None if z is None else torch.empty_like(z),
-             ddelta_bias=None if delta_bias is None else torch.empty_like(delta_bias),
-             dinitial_state=(torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
-                             if (initial_state is not None or want_dinitial_state) else None))
-    need = ssm_scan_bwd_workspace_size(batch, L, dim, dstate, dt)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    s = _resolve(dev, stream)
+    with torch.cuda.stream(s):
+        g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(delta), dB=torch.empty_like(B),
+                 dC=torch.empty_like(C), dA=torch.empty_like(A),
+                 dD=None if D is None else torch.empty_like(D), dz=None if z is None else torch.empty_like(z),
+                 ddelta_bias=None if delta_bias is None else torch.empty_like(delta_bias),
+                 dinitial_state=(torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+                                 if (initial_state is not None or want_dinitial_state) else None))
+        need = ssm_scan_bwd_workspace_size(batch, L, dim, dstate, dt)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     rc = lib().ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                             1 if softplus else 0, _ptr(dy), _ptr(dfinal_state), _ptr(initial_state), _ptr(g["du"]),
                             _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
                             _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dinitial_state"]), batch, L, dim, dstate,
-                            code, _ptr(workspace), ws_bytes,
-                            _stream(dev, stream))
+                            code, _ptr(workspace), _ws_bytes(workspace), s.cuda_stream)
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_scan_bwd")
+    if check_status:
+        _check_status(workspace, s, "ssm_scan_bwd")
     return g

@@ -46,7 +46,18 @@ def test_status_strings():
     assert ops.ssm_status_string(1) == "SSM_ERR_INVALID_ARG"
     assert ops.ssm_status_string(2) == "SSM_ERR_UNSUPPORTED"
     assert ops.ssm_status_string(3) == "SSM_ERR_HIP"
+    assert ops.ssm_status_string(4) == "SSM_ERR_HANDOFF_TIMEOUT"
     assert ops.ssm_status_string(77) == "SSM_ERR_UNKNOWN"
+
+
+def test_workspace_status_host_paths():
+    """No workspace: nothing chained ran, so OK without any HIP call; a workspace too small for the header or
+    misaligned is rejected before any HIP call."""
+    L = ops.lib()
+    assert L.ssm_workspace_status(None, 0, None) == ops.SSM_OK
+    assert L.ssm_workspace_status(0x100000, 0, None) == ops.SSM_OK
+    assert L.ssm_workspace_status(0x100000, 8, None) == INVALID
+    assert L.ssm_workspace_status(0x100004, 4096, None) == INVALID
 
 
 def test_workspace_size():

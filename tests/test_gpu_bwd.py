@@ -163,3 +163,51 @@ def test_bwd_extreme_steps():
     x, dy, dfs = _case(rng, 2, 200, 136, 16, "f32")
     x["delta"] = _round(np.asarray(x["delta"], np.float64) * 20.0, "f32")
     _run_and_compare(x, dy, dfs, "f32", label="extreme steps")
+
+
+def test_bwd_full_size_sampled_channels():
+    """The backward at the shape the benchmark times (4 x 4096 x 5120 x 16 bf16, z, D, bias, softplus on, the
+    chained plan: 256 whole tiles and 64 cut into 4 chunks of blocks, the checkpoint pass chained alike), with a
+    gradient on the final state.  du, d delta and dz of 12 sampled channels in every batch row (48 (row, channel)
+    recurrences) and dA, dD, d bias of those channels -- each a sum over all 16384 (row, token) terms -- against
+    the oracle run on those channels (a channel's gradients depend on its own inputs, B, C and dy only)."""
+    w = I.WORKLOADS["mamba2p8b_bf16"]
+    x = I.make_inputs(w, 0)
+    rng = np.random.default_rng(4242)
+    dy = I.round_to_bf16(rng.standard_normal((w.batch, w.L, w.dim)))
+    dfs = np.asarray(rng.standard_normal((w.batch, w.dim, w.dstate)), np.float32).astype(np.float64)
+    say(f"bwd full size {w}")
+    g = ops.ssm_scan_bwd(to_dev(x["u"], "bf16"), to_dev(x["delta"], "bf16"), to_dev_f32(x["A"]),
+                         to_dev(x["B"], "bf16"), to_dev(x["C"], "bf16"), to_dev(dy, "bf16"), D=to_dev_f32(x["D"]),
+                         z=to_dev(x["z"], "bf16"), delta_bias=to_dev_f32(x["delta_bias"]),
+                         dfinal_state=to_dev_f32(dfs), check_status=True)
+    torch.cuda.synchronize()
+    ds = np.sort(rng.choice(w.dim, size=12, replace=False))
+    ds[0], ds[-1] = 0, w.dim - 1   # tile edges of the first and last tile
+    dsel = torch.from_numpy(ds).to(g["du"].device)
+    got = {k: g[k].index_select(-1, dsel).float().cpu().numpy().astype(np.float64) for k in ("du", "ddelta", "dz")}
+    for k in ("dD", "ddelta_bias"):
+        got[k] = g[k][dsel].cpu().numpy().astype(np.float64)
+    got["dA"] = g["dA"][dsel].cpu().numpy().astype(np.float64)
+    del g
+    o = OB.scan_bwd(x["u"][:, :, ds], x["delta"][:, :, ds], x["A"][ds], x["B"], x["C"], dy[:, :, ds], D=x["D"][ds],
+                    z=x["z"][:, :, ds], delta_bias=x["delta_bias"][ds], dfinal_state=dfs[:, ds])
+    errs = {k: rel_err(got[k], o[k]) for k in got}
+    print("[parity] bwd full size, 48 sampled (row, channel) pairs: " +
+          "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k in ("du", "ddelta", "dz"):
+        assert errs[k] <= TOL["bf16"], (k, errs[k])
+    for k in ("dA", "dD", "ddelta_bias"):
+        assert errs[k] <= TOL["f32"], (k, errs[k])
+
+
+def test_bwd_db_dc_full_length_chained(monkeypatch):
+    """dB and dC (sums over every channel of a row) at the full 4096 tokens, in the chained plan the benchmark
+    runs, on a layer the oracle can finish: 5 tiles (320 channels) planned for a 4-CU device, so 4 whole tiles and
+    1 cut into 4 chunks of blocks (and the checkpoint pass into 4 chunks of 1024 tokens).  Every gradient against
+    the oracle."""
+    monkeypatch.setenv("SSM_NUM_CU", "4")
+    rng = np.random.default_rng(4343)
+    x, dy, dfs = _case(rng, 1, 4096, 320, 16, "bf16")
+    x["A"] = np.tile(-np.arange(1, 17, dtype=np.float64), (320, 1))   # the benchmark's A[d, n] = -(n + 1)
+    _run_and_compare(x, dy, dfs, "bf16", label="1 x 4096 x 320 chained for 4 CUs")
