@@ -82,7 +82,8 @@ typedef enum {
   SSM_ERR_INVALID_ARG = 1,
   SSM_ERR_UNSUPPORTED = 2,
   SSM_ERR_HIP = 3,
-  SSM_ERR_HANDOFF_TIMEOUT = 4
+  SSM_ERR_HANDOFF_TIMEOUT = 4,
+  SSM_ERR_SCRATCH_TOO_SMALL = 5
 } ssm_status_t;
 
 typedef enum { SSM_DTYPE_F32 = 0, SSM_DTYPE_BF16 = 1 } ssm_dtype_t;
@@ -111,6 +112,30 @@ ssm_status_t ssm_scan_fwd(const void* u, const void* delta, const float* A, cons
                           void* y, float* final_state,
                           int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ssm_scan_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation, kernels and plan as ssm_scan_fwd with the same
+ * arguments, bitwise the same outputs, but no workspace argument.  The
+ * workspace is a static 32 MiB device array of the library, one per GPU
+ * (each GPU holds it until the process ends); its device address is looked
+ * up once per device, on the first call with that device current.  The call
+ * itself allocates nothing: no hipMalloc, no hipFree, no allocating library
+ * routine.  Every call on one GPU shares that GPU's array, so calls that
+ * overlap in time on one GPU (other streams, other threads) race and must
+ * be serialised by the caller; sequential calls need nothing (each call
+ * resets what must start at zero).  The stream must belong to the current
+ * device.  ssm_workspace_status does not apply (there is no workspace to
+ * pass); a lost hand-off still shows as NaN outputs.
+ * Errors: as ssm_scan_fwd for the arguments; SSM_ERR_SCRATCH_TOO_SMALL when
+ * the shape needs more than 32 MiB of workspace (ssm_scan_workspace_size
+ * above 32 MiB: about batch * L above 250,000 tokens at dstate 16), nothing
+ * launched; SSM_ERR_HIP if the array's address cannot be looked up. */
+ssm_status_t ssm_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                  const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                  void* y, float* final_state,
+                                  int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
+                                  hipStream_t stream);
 
 /* Workspace for ssm_scan_fwd_ex: for nseq <= 0 (no packed sequences) the same
  * as ssm_scan_workspace_size; for nseq > 0 packed sequences (batch must be 1)

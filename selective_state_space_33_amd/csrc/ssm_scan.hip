@@ -13,6 +13,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
 
 #include "carry_kernel.hpp"
 #include "decode_kernel.hpp"
@@ -575,6 +576,63 @@ extern "C" ssm_status_t ssm_state_update(float* state, const void* u, const void
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+// ---- the allocation-free forward
+//
+// Its workspace is this static device array: every GPU the library runs on
+// holds its own copy, at its own address, until the process ends.  In host
+// code the array's name stands for a host-side shadow, not device memory, so
+// the host never passes it anywhere: scratch_address() looks up each device's
+// address once (hipGetSymbolAddress, with that device current) and the calls
+// use that.  Every call on a device shares the array; the first kernel of each
+// call resets the words that must start at zero (status, ticket, ready
+// flags), and everything else is written before it is read.
+namespace ssm {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// The device address of the current device's array, or null on failure.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace ssm
+
+extern "C" ssm_status_t ssm_scan_fwd_noalloc(const void* u, const void* delta, const float* A, const void* B,
+                                             const void* C, const float* D, const void* z, const float* delta_bias,
+                                             int softplus_flag, void* y, float* final_state, int64_t batch,
+                                             int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
+                                             hipStream_t stream) {
+  const ssm_status_t st =
+      check_scan_args(u, delta, A, B, C, D, z, delta_bias, y, final_state, batch, L, dim, dstate, dt);
+  if (st != SSM_OK) return st;
+  const size_t need = fwd_workspace(batch, L, dim, dstate, 0, dt, false);
+  if (need == 0) return SSM_ERR_UNSUPPORTED;      // a shape ssm_scan_fwd rejects as well
+  if (need > kScratchBytes) return SSM_ERR_SCRATCH_TOO_SMALL;
+  void* ws = scratch_address();
+  if (!ws) return SSM_ERR_HIP;
+  return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus_flag, nullptr, nullptr, 0, y, final_state,
+                       batch, L, dim, dstate, dt, ws, kScratchBytes, stream, kRuleEuler);
+}
+
 extern "C" ssm_status_t ssm_workspace_status(const void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!workspace || workspace_bytes == 0) return SSM_OK;  // no workspace: no chained plan ran
   if (workspace_bytes < kHeaderWords * sizeof(unsigned) || !aligned(workspace, 256)) return SSM_ERR_INVALID_ARG;
@@ -593,6 +651,7 @@ extern "C" const char* ssm_status_string(ssm_status_t s) {
     case SSM_ERR_UNSUPPORTED: return "SSM_ERR_UNSUPPORTED";
     case SSM_ERR_HIP: return "SSM_ERR_HIP";
     case SSM_ERR_HANDOFF_TIMEOUT: return "SSM_ERR_HANDOFF_TIMEOUT";
+    case SSM_ERR_SCRATCH_TOO_SMALL: return "SSM_ERR_SCRATCH_TOO_SMALL";
   }
   return "SSM_ERR_UNKNOWN";
 }

@@ -26,10 +26,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libssmscan.so")
 
 SSM_OK, SSM_ERR_INVALID_ARG, SSM_ERR_UNSUPPORTED, SSM_ERR_HIP, SSM_ERR_HANDOFF_TIMEOUT = 0, 1, 2, 3, 4
+SSM_ERR_SCRATCH_TOO_SMALL = 5
 SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 
 # Every symbol include/ssm_scan.h declares.
-EXPORTED = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_ex_workspace_size", "ssm_scan_fwd_ex",
+EXPORTED = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_ex_workspace_size", "ssm_scan_fwd_ex",
             "ssm_scan_trap_fwd_workspace_size", "ssm_scan_trap_fwd", "ssm_ssd_fwd_workspace_size", "ssm_ssd_fwd",
             "ssm_state_update",
             "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_workspace_status", "ssm_status_string")
@@ -57,6 +58,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_fwd.restype = ctypes.c_int
         L.ssm_scan_fwd.argtypes = ([_vp] * 8 + [ctypes.c_int, _vp, _vp] + [_i64] * 4 +
                                    [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
+        L.ssm_scan_fwd_noalloc.restype = ctypes.c_int
+        L.ssm_scan_fwd_noalloc.argtypes = [_vp] * 8 + [ctypes.c_int, _vp, _vp] + [_i64] * 4 + [ctypes.c_int, _vp]
         L.ssm_state_update.restype = ctypes.c_int
         L.ssm_state_update.argtypes = [_vp] * 9 + [ctypes.c_int, _vp] + [_i64] * 3 + [ctypes.c_int, _vp]
         L.ssm_scan_fwd_ex_workspace_size.restype = ctypes.c_size_t
