@@ -68,6 +68,8 @@ struct ScanParams {
   const void* z;       // nullable
   const float* bias;   // nullable
   const float* bc;     // packed B/C records [batch][G][Lp][2*NPL]
+  const void* Braw;    // the caller's B and C [batch][L][N]: read directly where the records are not packed
+  const void* Craw;
   void* y;
   float* final_state;  // nullable
   // Chunk pairs and carried-in states of the split tiles: [n_split][Ks][64][Npad].
@@ -237,6 +239,12 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   static_assert(HAS_FULL || G <= TB_, "stop-flag words in the partial-readout buffer");
   constexpr bool TRAP = RULE == kRuleTrap;
   static_assert(!TRAP || !CKPT, "the backward's checkpoints are of the two-term rule");
+  // fp32 storage, two-term rule, outside the backward's checkpoint launches:
+  // B and C come straight from the caller's rows, B_t[n] at float t*N + n,
+  // instead of from packed records.  A block's record registers then hold its
+  // B floats (16 per register: 16/NPL tokens of this wavefront's NPL states)
+  // followed by its C floats, and need the host to have made N = NPL * G.
+  constexpr bool DIRECT = __is_same(IO, F32) && RULE == kRuleEuler && !CKPT;
 
   // Double-buffered by block parity.  (delta, delta*u) per token, channel;
   // (delta, u/2) with the trapezoidal rule.
@@ -273,6 +281,13 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   rsrc_t rs_bc;                            // this wavefront's packed B/C records of the stretch
   float* ckpt_row = nullptr;               // checkpoint launches: this lane's states at the stretch's first block
   const int rec_voff = (lane & 15) * 4;    // lane l holds float l % 16 of a group's 16
+  // direct B/C: lane l's float of a register is token (l%16)/NPL, state n0 + (l%16)%NPL of its 16/NPL tokens;
+  // a state past N gets an offset at or above 2^31, past every resource's range (which the stretch keeps below
+  // 2^31 bytes), so it reads zero like a packed record's padding
+  rsrc_t rs_B, rs_C;
+  const unsigned dir_voff = (n0 + (lane & 15) % NPL < N)
+                                ? static_cast<unsigned>((((lane & 15) / NPL) * N + n0 + (lane & 15) % NPL) * 4)
+                                : 0x80000000u;
 
   auto set_tile = [&](int tile, int64_t tb, int64_t te) {
     b = tile / p.ntd;
@@ -295,7 +310,17 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       ckpt_row = p.ckpt + (static_cast<int64_t>(tile) * p.ckpt_blocks * 64 + lane) * NPAD + n0 +
                  (t_begin / TB) * 64 * NPAD;
     // the records run on for kTBMax rows of padding past Lp
-    rs_bc = make_rsrc(bc_row, (p.Lp + kTBMax - t_begin) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
+    if constexpr (DIRECT) {
+      // rows of B and C from the stretch's first token to the end of the batch row (the host keeps the
+      // stretch's offsets below 2^31 bytes)
+      const int64_t rb = (b * L + t_begin) * N * static_cast<int64_t>(sizeof(float));
+      int64_t rbytes = (L - t_begin) * N * static_cast<int64_t>(sizeof(float));
+      if (rbytes > 0x7fffffffLL) rbytes = 0x7fffffffLL;
+      rs_B = make_rsrc(static_cast<const char*>(p.Braw) + rb, rbytes);
+      rs_C = make_rsrc(static_cast<const char*>(p.Craw) + rb, rbytes);
+    } else {
+      rs_bc = make_rsrc(bc_row, (p.Lp + kTBMax - t_begin) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
+    }
     pd = d0 + pcol;
     pvalid = pd < dim;  // dim is a multiple of VW
 #pragma unroll
@@ -377,11 +402,25 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
 
     auto load_records = [&](auto parc, int blk) {
       constexpr int P = decltype(parc)::value;
-      const int bo = blk * (TB * 2 * NPL * 4);
+      if constexpr (DIRECT) {
+        const unsigned bo = static_cast<unsigned>(blk) * TB * static_cast<unsigned>(N) * 4u + dir_voff;
+        const unsigned rstep = (16 / NPL) * static_cast<unsigned>(N) * 4u;  // bytes of B per register
 #pragma unroll
-      for (int v = 0; v < NRV; ++v)
-        rv[P][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bc, rec_voff + bo + v * 64, 0, 0));
+        for (int v = 0; v < NRV / 2; ++v) {
+          const int off = static_cast<int>(bo + v * rstep);
+          rv[P][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_B, off, 0, 0));
+          rv[P][NRV / 2 + v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_C, off, 0, 0));
+        }
+      } else {
+        const int bo = blk * (TB * 2 * NPL * 4);
+#pragma unroll
+        for (int v = 0; v < NRV; ++v)
+          rv[P][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bc, rec_voff + bo + v * 64, 0, 0));
+      }
     };
+    // float index within a block's records of B_t[n0 + j] and C_t[n0 + j], t = token q of the block
+    auto bidx = [](int q, int j) constexpr { return DIRECT ? q * NPL + j : q * 2 * NPL + j; };
+    auto cidx = [](int q, int j) constexpr { return DIRECT ? TB * NPL + q * NPL + j : q * 2 * NPL + NPL + j; };
 
     auto issue_loads = [&](auto slotc, int blk) {
       constexpr int S = decltype(slotc)::value;
@@ -511,7 +550,6 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     auto update = [&](auto parc, auto gc, auto qc, const float2 dd, float& block_delta) {
       constexpr int P = decltype(parc)::value;
       constexpr int TQ = decltype(gc)::value * SUB + decltype(qc)::value;  // token within the block
-      constexpr int F = TQ * 2 * NPL;
       float yp = 0.0f;
       if constexpr (TRAP) {
         const float cw = (pv_d + dd.x) * pv_hx;
@@ -523,12 +561,12 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
              if constexpr (TQ == 0) {
                g = __builtin_fmaf(cw, Bprev[j], h[j]);
              } else {
-               constexpr int fp = F - 2 * NPL + j;  // B_{t-1}[n0 + j]
+               constexpr int fp = bidx(TQ - 1, j);  // B_{t-1}[n0 + j]
                g = fmac_row_bcast<fp % 16>(h[j], rv[P][fp / 16], cw);
              }
              h[j] = a * g;
              if constexpr (FULL) {
-               constexpr int fc = F + NPL + j;
+               constexpr int fc = cidx(TQ, j);
                if constexpr (j == 0) yp = row_bcast<fc % 16>(rv[P][fc / 16]) * h[0];
                else yp = fmac_row_bcast<fc % 16>(yp, rv[P][fc / 16], h[j]);
              } else {
@@ -546,11 +584,12 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       [&]<int... J>(std::integer_sequence<int, J...>) {
         (([&] {
            constexpr int j = J;
-           const float Bj = row_bcast<(F + j) % 16>(rv[P][(F + j) / 16]);
+           constexpr int fb = bidx(TQ, j);
+           const float Bj = row_bcast<fb % 16>(rv[P][fb / 16]);
            const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
            h[j] = __builtin_fmaf(a, h[j], dd.y * Bj);
            if constexpr (FULL) {
-             constexpr int fc = F + NPL + j;
+             constexpr int fc = cidx(TQ, j);
              if constexpr (j == 0) yp = row_bcast<fc % 16>(rv[P][fc / 16]) * h[0];
              else yp = fmac_row_bcast<fc % 16>(yp, rv[P][fc / 16], h[j]);
            } else {
@@ -614,9 +653,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       }(std::make_integer_sequence<int, NG>{});
       if constexpr (TRAP) {
         // B of the block's last token, for the next block's first update
-        constexpr int LF = (TB - 1) * 2 * NPL;
         [&]<int... J>(std::integer_sequence<int, J...>) {
-          ((Bprev[J] = row_bcast<(LF + J) % 16>(rv[P][(LF + J) / 16])), ...);
+          ((Bprev[J] = row_bcast<bidx(TB - 1, J) % 16>(rv[P][bidx(TB - 1, J) / 16])), ...);
         }(std::make_integer_sequence<int, NPL>{});
       }
       delta_total += block_delta;

@@ -56,12 +56,14 @@ struct Plan {
   int tb;        // tokens per block of the readout scan (16, or 32 with a CU per workgroup)
   bool packed;   // packed sequences: "chunk" c of a tile column is sequence c (no pairs, no carries)
   bool trap;     // trapezoidal rule: also C_t . B_t per token
+  bool direct;   // fp32 storage, two-term rule: the scan reads B and C directly (no packed records)
 };
 
 // Workspace layout: [header words (status, ticket, ...) and ready flags]
 // [packed B/C][chunk fades P][chunk states S][carried-in states][sequence
 // order][C_t . B_t].  The chained plan needs no P, S and has a flag per
-// chunk; only the packed plan has an order, only the trapezoidal rule C . B.
+// chunk; only the packed plan has an order, only the trapezoidal rule C . B;
+// fp32 storage with the two-term rule packs no B/C.
 struct Layout {
   size_t words, bc, pairs, carry, order, cb, total;
   int n_words;
@@ -73,7 +75,7 @@ Layout layout_for(const Plan& pl, int64_t batch) {
   Layout l;
   l.n_words = kHeaderWords + (pl.chained ? pl.n_split * pl.Ks : 0);
   l.words = align256(static_cast<size_t>(l.n_words) * sizeof(unsigned));
-  l.bc = align256((static_cast<size_t>(batch) * pl.Lp + kTBMax) * 2 * npad * sizeof(float));
+  l.bc = pl.direct ? 0 : align256((static_cast<size_t>(batch) * pl.Lp + kTBMax) * 2 * npad * sizeof(float));
   l.pairs = (pl.n_split > 0 && !pl.chained && !pl.packed) ? align256(per) : 0;
   l.carry = (pl.n_split > 0 && !pl.packed) ? align256(per) : 0;
   l.order = pl.packed ? align256(static_cast<size_t>(pl.Ks) * sizeof(int)) : 0;
@@ -112,9 +114,14 @@ void generic_variant(int64_t N, int* npl, int* G) {
 
 // The kernels address a chunk's token rows with 32-bit byte offsets: a chunk
 // (plus one trip of padding) must stay below 2^31 bytes per tensor, so very
-// long rows force every tile to be cut.
-int64_t max_chunk_len(int64_t dim, int64_t es) {
-  return (0x7fffffffLL / (dim * es) - kTrip) / kTrip * kTrip;
+// long rows force every tile to be cut.  row_bytes: the larger of a token row
+// of u (dim * element size) and, where the scan reads B and C directly, of B
+// (dstate * 4).
+int64_t max_chunk_len(int64_t row_bytes) {
+  return (0x7fffffffLL / row_bytes - kTrip) / kTrip * kTrip;
+}
+int64_t token_row_bytes(int64_t dim, int64_t N, int64_t es, bool direct) {
+  return (direct && N * 4 > dim * es) ? N * 4 : dim * es;
 }
 
 int env_flag(const char* name) {  // -1 when unset
@@ -136,9 +143,11 @@ int env_flag(const char* name) {  // -1 when unset
 //   - with fewer tiles, every tile is cut so that each CU gets about two
 //     chunks, through the separate pair and carry passes.
 // vw_ok: the widest token-row access the pointers and dim allow (4, 2 or 1);
-// it decides the prologue width, not the split.
-void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int vw_ok, Plan* pl) {
+// it decides the prologue width, not the split.  rule: the discretisation
+// (fp32 storage with the two-term rule reads B and C without packing them).
+void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int vw_ok, int rule, Plan* pl) {
   const int64_t kNumCU = device_cu_count();
+  const bool direct = es == 4 && rule == kRuleEuler;
   int npl, G, Kreq = 0;
   if (N == 16) {
     // 2 states per lane over 8 wavefronts: 80 KB of LDS, two workgroups per CU.
@@ -192,7 +201,7 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
     if (K > kmax) K = kmax;
   }
   if (K < 1) K = 1;
-  const int64_t kmin = ceil_div(L, max_chunk_len(dim, es));
+  const int64_t kmin = ceil_div(L, max_chunk_len(token_row_bytes(dim, N, es, direct)));
   if (kmin > 1) {
     n_long = 0;
     chained = false;
@@ -221,13 +230,14 @@ void plan_scan(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, int
   const char* te = getenv("SSM_SCAN_TB");
   if (te && tb32_ok && (atoi(te) == 16 || atoi(te) == 32)) pl->tb = atoi(te);
   pl->packed = false;
-  pl->trap = false;
+  pl->trap = rule == kRuleTrap;
+  pl->direct = direct;
 }
 
 // Packed sequences (batch row 0 holds nseq of them): every (tile column,
 // sequence) is one readout-pass unit from its own initial state, with no
 // chunking of a sequence.
-void plan_packed(int64_t L, int64_t dim, int64_t N, int vw_ok, int64_t nseq, Plan* pl) {
+void plan_packed(int64_t L, int64_t dim, int64_t N, int64_t es, int vw_ok, int64_t nseq, int rule, Plan* pl) {
   const int64_t kNumCU = device_cu_count();
   int npl, G;
   if (N == 16) {
@@ -247,7 +257,8 @@ void plan_packed(int64_t L, int64_t dim, int64_t N, int vw_ok, int64_t nseq, Pla
   pl->Lp = ceil_div(L, kTrip) * kTrip;
   pl->chained = false;
   pl->packed = true;
-  pl->trap = false;
+  pl->trap = rule == kRuleTrap;
+  pl->direct = es == 4 && rule == kRuleEuler;
   const bool tb32_ok = variant_has_tb32(npl, G, pl->vw, kModeFull);
   pl->tb = (tb32_ok && static_cast<int64_t>(pl->ntd) * nseq <= kNumCU) ? 32 : 16;
 }
@@ -269,6 +280,12 @@ ssm_status_t check_scan_args(const void* u, const void* delta, const float* A, c
   return SSM_OK;
 }
 
+// Zeroes the header words (status, tickets) and ready flags of a call whose
+// B and C need no packing (pack_bc_kernel zeroes them otherwise).
+__global__ void __launch_bounds__(256) zero_words_kernel(unsigned* words, int n) {
+  for (int e = threadIdx.x; e < n; e += 256) words[e] = 0u;
+}
+
 template <class IO, int RULE>
 hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void* C, float* bc, ScanParams p,
                     hipStream_t s) {
@@ -278,11 +295,16 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
   if (pl.npl == NPL_)                                                                                       \
     hipLaunchKernelGGL((pack_bc_kernel<IO, NPL_>), pgrid, dim3(256), 0, s, B, C, bc, p.batch, p.L, pl.Lp, p.N, \
                        pl.G, p.status, lay.n_words, const_cast<float*>(p.cb));
-  SSM_PACK_CASE(1)
-  SSM_PACK_CASE(2)
-  SSM_PACK_CASE(4)
-  SSM_PACK_CASE(8)
-  SSM_PACK_CASE(16)
+  if (pl.direct) {
+    // the scan reads B and C itself: only the header words and flags need zeroing
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, s, p.status, lay.n_words);
+  } else {
+    SSM_PACK_CASE(1)
+    SSM_PACK_CASE(2)
+    SSM_PACK_CASE(4)
+    SSM_PACK_CASE(8)
+    SSM_PACK_CASE(16)
+  }
 #undef SSM_PACK_CASE
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -383,17 +405,18 @@ size_t fwd_workspace(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int6
   if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 64 || batch > kMaxBatch) return 0;
   if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return 0;
   const int64_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
+  const int rule = trap ? kRuleTrap : kRuleEuler;
+  const int64_t row = token_row_bytes(dim, dstate, es, es == 4 && !trap);
   Plan p4, p1;
   if (nseq > 0) {
-    if (batch != 1 || max_chunk_len(dim, es) < ceil_div(L, kChunkQuantum) * kChunkQuantum) return 0;
-    plan_packed(L, dim, dstate, 4, nseq, &p4);
-    plan_packed(L, dim, dstate, 1, nseq, &p1);
+    if (batch != 1 || max_chunk_len(row) < ceil_div(L, kChunkQuantum) * kChunkQuantum) return 0;
+    plan_packed(L, dim, dstate, es, 4, nseq, rule, &p4);
+    plan_packed(L, dim, dstate, es, 1, nseq, rule, &p1);
   } else {
-    if (max_chunk_len(dim, es) < kChunkQuantum) return 0;
-    plan_scan(batch, L, dim, dstate, es, 4, &p4);
-    plan_scan(batch, L, dim, dstate, es, 1, &p1);
+    if (max_chunk_len(row) < kChunkQuantum) return 0;
+    plan_scan(batch, L, dim, dstate, es, 4, rule, &p4);
+    plan_scan(batch, L, dim, dstate, es, 1, rule, &p1);
   }
-  p4.trap = p1.trap = trap;
   const size_t a = layout_for(p4, batch).total, b = layout_for(p1, batch).total;
   return a > b ? a : b;
 }
@@ -420,20 +443,19 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
       break;
     }
   }
-  if (max_chunk_len(dim, static_cast<int64_t>(es)) < kChunkQuantum) return SSM_ERR_UNSUPPORTED;
+  const int64_t row = token_row_bytes(dim, dstate, static_cast<int64_t>(es), es == 4 && rule == kRuleEuler);
+  if (max_chunk_len(row) < kChunkQuantum) return SSM_ERR_UNSUPPORTED;
   Plan pl;
   if (cu_seqlens) {
     // a sequence is never cut, so the whole row of tokens must stay within the 32-bit offsets
-    if (ceil_div(L, kChunkQuantum) * kChunkQuantum > max_chunk_len(dim, static_cast<int64_t>(es)))
-      return SSM_ERR_UNSUPPORTED;
-    plan_packed(L, dim, dstate, vw_ok, nseq, &pl);
+    if (ceil_div(L, kChunkQuantum) * kChunkQuantum > max_chunk_len(row)) return SSM_ERR_UNSUPPORTED;
+    plan_packed(L, dim, dstate, static_cast<int64_t>(es), vw_ok, nseq, rule, &pl);
   } else {
-    plan_scan(batch, L, dim, dstate, static_cast<int64_t>(es), vw_ok, &pl);
+    plan_scan(batch, L, dim, dstate, static_cast<int64_t>(es), vw_ok, rule, &pl);
   }
   if (static_cast<int64_t>(pl.n_long) + static_cast<int64_t>(pl.n_split) * pl.Ks > 0x7fffffffLL ||
       batch * (pl.Lp / kPackT) > 0x7fffffffLL)
     return SSM_ERR_UNSUPPORTED;
-  pl.trap = rule == kRuleTrap;
   const Layout lay = layout_for(pl, batch);
   if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256)) return SSM_ERR_INVALID_ARG;
 
@@ -447,6 +469,8 @@ ssm_status_t scan_fwd_impl(const void* u, const void* delta, const float* A, con
   p.z = z;
   p.bias = delta_bias;
   p.bc = reinterpret_cast<const float*>(ws + lay.words);
+  p.Braw = B;
+  p.Craw = C;
   p.y = y;
   p.final_state = final_state;
   p.aggP = p.aggS = p.carry = nullptr;

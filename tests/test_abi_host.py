@@ -67,9 +67,12 @@ def test_workspace_size():
     ws = L.ssm_scan_workspace_size(64, 256, 8192, 16, BF16)
     assert ws >= 64 * 256 * 2 * 16 * 4 and ws % 256 == 0
     # few channels, long sequence: the tile is cut into chunks, which adds
-    # chunk pairs and carried-in states on top of the packed B/C
-    ws_long = L.ssm_scan_workspace_size(1, 1 << 20, 64, 16, F32)
+    # chunk pairs and carried-in states on top of the packed B/C (bf16); fp32
+    # storage packs nothing, the scan reads B and C directly
+    ws_long = L.ssm_scan_workspace_size(1, 1 << 20, 64, 16, BF16)
     assert ws_long > (1 << 20) * 2 * 16 * 4 and ws_long % 256 == 0
+    ws_long32 = L.ssm_scan_workspace_size(1, 1 << 20, 64, 16, F32)
+    assert ws_long32 == ws_long - ((((1 << 20) + 32) * 2 * 16 * 4 + 255) // 256 * 256)
     # rejected shapes report 0
     assert L.ssm_scan_workspace_size(0, 10, 10, 16, F32) == 0
     assert L.ssm_scan_workspace_size(1, 10, 10, 65, F32) == 0
@@ -266,3 +269,16 @@ def test_binding_argument_counts_match_the_header():
         assert m, name
         params = [p for p in m.group(1).split(",") if p.strip() and p.strip() != "void"]
         assert len(getattr(L, name).argtypes) == len(params), name
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch():
+    """ssm_scan_fwd_noalloc on a shape whose workspace exceeds its 32 MiB static array: a clear error before any
+    HIP call (fake pointers, never dereferenced).  The shape is bf16, whose B/C records are always packed (128 MB
+    here); the guard keeps the call from ever being made with a shape that would fit."""
+    lib = ops.lib()
+    shape = (1, 1 << 20, 64, 16)
+    assert lib.ssm_scan_workspace_size(*shape, BF16) > (32 << 20)
+    a = (0x1000, 0x2000, 0x3000, 0x4000, 0x5000, None, None, None, 1, 0x6000, None)
+    assert lib.ssm_scan_fwd_noalloc(*a, *shape, BF16, None) == ops.SSM_ERR_SCRATCH_TOO_SMALL
+    assert lib.ssm_scan_fwd_noalloc(*a, 0, 10, 64, 16, F32, None) == INVALID
+    assert lib.ssm_scan_fwd_noalloc(*a, 1, 10, 64, 65, F32, None) == UNSUPPORTED

@@ -19,13 +19,14 @@ def a256(x):
     return (x + 255) // 256 * 256
 
 
-def fwd_expected(batch, L, dim, N, chained_chunks=0, split_tiles=0, pair_chunks=0):
+def fwd_expected(batch, L, dim, N, chained_chunks=0, split_tiles=0, pair_chunks=0, direct=False):
     """Workspace of the two-state-per-lane, 8-wavefront variant (N = 16): header words (+ flags), packed B/C
-    records of whole 128-token trips (+ 32 rows of padding), and the chunk pairs and carries."""
+    records of whole 128-token trips (+ 32 rows of padding; none for fp32 storage, whose B and C the scan reads
+    directly), and the chunk pairs and carries."""
     Lp = (L + 127) // 128 * 128
     npad = 16
     words = 4 + split_tiles * chained_chunks
-    ws = a256(words * 4) + a256((batch * Lp + 32) * 2 * npad * 4)
+    ws = a256(words * 4) + (0 if direct else a256((batch * Lp + 32) * 2 * npad * 4))
     K = chained_chunks or pair_chunks
     per = a256(split_tiles * K * 64 * npad * 4) if split_tiles else 0
     if chained_chunks:
@@ -62,6 +63,9 @@ def test_forward_plan_small_device(monkeypatch):
     """A 10-tile layer on an 8-CU device: 8 whole tiles, 2 left over in 4 chunks of the 1024 tokens."""
     monkeypatch.setenv("SSM_NUM_CU", "8")
     got = ops.lib().ssm_scan_workspace_size(1, 1024, 640, 16, F32)
+    assert got == fwd_expected(1, 1024, 640, 16, chained_chunks=4, split_tiles=2, direct=True)
+    # the same plan in bf16 packs B and C into records
+    got = ops.lib().ssm_scan_workspace_size(1, 1024, 640, 16, BF16)
     assert got == fwd_expected(1, 1024, 640, 16, chained_chunks=4, split_tiles=2)
 
 
