@@ -33,6 +33,13 @@ with numpy matrix products.  delta_t = softplus(delta_raw + bias) with the
 exact log-add-exp, or delta_raw + bias when softplus is off.  The tests pin it
 to the recurrent oracle (ssm_ref.c) on head-broadcast inputs and to plain
 causal linear attention at A = 0, delta = 1.
+
+Groups.  The page's equivalence casts B_t as the keys and C_t as the queries
+of masked linear attention, shared by the heads; letting groups of heads
+share them, as grouped attention shares keys and queries, is the reading taken
+for B, C of shape [batch, L, ngroups, dstate]: heads are split into ngroups
+runs of heads / ngroups consecutive heads, and run g uses B[..., g, :] and
+C[..., g, :].  One group is the shape [batch, L, dstate] above.
 """
 import numpy as np
 
@@ -45,21 +52,27 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, i
     """SSD layer in the masked-matrix form.
 
     x, z: [batch, L, heads, headdim]; delta: [batch, L, heads]; A, D, delta_bias: [heads];
-    B, C: [batch, L, dstate]; initial_state: [batch, heads, headdim, dstate] or None (zero).
+    B, C: [batch, L, dstate], or [batch, L, ngroups, dstate] with heads a multiple of ngroups;
+    initial_state: [batch, heads, headdim, dstate] or None (zero).
     Returns (y [batch, L, heads, headdim], final_state [batch, heads, headdim, dstate]) in float64."""
     x, delta, A, B, C, D, z, bias, h0 = map(_f64, (x, delta, A, B, C, D, z, delta_bias, initial_state))
     batch, L, H, P = x.shape
-    N = B.shape[2]
-    assert delta.shape == (batch, L, H) and A.shape == (H,)
-    assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+    if B.ndim == 3:
+        B, C = B[:, :, None, :], C[:, :, None, :]
+    ngroups, N = B.shape[2], B.shape[3]
+    assert delta.shape == (batch, L, H) and A.shape == (H,) and H % ngroups == 0
+    assert B.shape == (batch, L, ngroups, N) and C.shape == (batch, L, ngroups, N)
+    per_group = H // ngroups
     raw = delta if bias is None else delta + bias
     dl = np.logaddexp(raw, 0.0) if softplus else raw                       # [batch, L, H]
     y = np.empty((batch, L, H, P))
     fs = np.empty((batch, H, P, N))
     causal = np.tril(np.ones((L, L), dtype=bool))
     for b in range(batch):
-        G = C[b] @ B[b].T                                                   # [t, s] = C_t . B_s
         for h in range(H):
+            g = h // per_group
+            Bg, Cg = B[b, :, g], C[b, :, g]                                 # [L, N] of the head's group
+            G = Cg @ Bg.T                                                   # [t, s] = C_t . B_s
             cs = np.cumsum(dl[b, :, h])
             decay = np.exp(np.where(causal, A[h] * (cs[:, None] - cs[None, :]), -np.inf))
             M = G * decay * dl[b, None, :, h]                               # [t, s]
@@ -67,9 +80,9 @@ def ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, i
             if D is not None:
                 y[b, :, h] += D[h] * x[b, :, h]
             w = np.exp(A[h] * (cs[-1] - cs)) * dl[b, :, h]                  # weight of token s in H_{L-1}
-            fs[b, h] = (x[b, :, h] * w[:, None]).T @ B[b]
+            fs[b, h] = (x[b, :, h] * w[:, None]).T @ Bg
             if h0 is not None:
-                y[b, :, h] += np.exp(A[h] * cs)[:, None] * (C[b] @ h0[b, h].T)   # [t, p]: e^{A cs_t} H_{-1} C_t
+                y[b, :, h] += np.exp(A[h] * cs)[:, None] * (Cg @ h0[b, h].T)     # [t, p]: e^{A cs_t} H_{-1} C_t
                 fs[b, h] += np.exp(A[h] * cs[-1]) * h0[b, h]
     if z is not None:
         y = y * (z / (1.0 + np.exp(-z)))

@@ -116,13 +116,14 @@ SSD_MUTANTS = {
     "decay_includes_own_step": ("A[h] * (cs[:, None] - cs[None, :])",
                                 "A[h] * (cs[:, None] - cs[None, :] + dl[b, None, :, h])"),
     "step_weight_dropped": ("M = G * decay * dl[b, None, :, h]", "M = G * decay"),
-    "B_and_C_swapped": ("G = C[b] @ B[b].T", "G = B[b] @ C[b].T"),
+    "B_and_C_swapped": ("G = Cg @ Bg.T", "G = Bg @ Cg.T"),
+    "group_of_head_interleaved": ("g = h // per_group", "g = h % ngroups"),
     "mask_not_causal": ("np.where(causal, A[h] * (cs[:, None] - cs[None, :]), -np.inf)",
                         "A[h] * np.abs(cs[:, None] - cs[None, :])"),
     "skip_dropped": ("y[b, :, h] += D[h] * x[b, :, h]", "y[b, :, h] += 0.0"),
     "final_state_without_decay": ("w = np.exp(A[h] * (cs[-1] - cs)) * dl[b, :, h]", "w = dl[b, :, h]"),
     "gate_is_sigmoid": ("y = y * (z / (1.0 + np.exp(-z)))", "y = y * (1.0 / (1.0 + np.exp(-z)))"),
-    "initial_state_readout_without_decay": ("np.exp(A[h] * cs)[:, None] * (C[b] @ h0[b, h].T)", "(C[b] @ h0[b, h].T)"),
+    "initial_state_readout_without_decay": ("np.exp(A[h] * cs)[:, None] * (Cg @ h0[b, h].T)", "(Cg @ h0[b, h].T)"),
     "initial_state_not_handed_on": ("fs[b, h] += np.exp(A[h] * cs[-1]) * h0[b, h]", "fs[b, h] += 0.0"),
 }
 
@@ -139,7 +140,8 @@ def test_ssd_mutant_is_caught(name, monkeypatch):
     monkeypatch.setattr(S, "ssd_fwd", mod.ssd_fwd)
     pins = [lambda: test_masked_form_equals_the_recurrent_scan(True, True),
             lambda: test_initial_state_equals_the_recurrent_scan_from_it(True),
-            test_no_decay_unit_step_is_causal_linear_attention, test_decay_mask_is_one_semiseparable]
+            test_no_decay_unit_step_is_causal_linear_attention, test_decay_mask_is_one_semiseparable,
+            lambda: test_groups_equal_the_recurrent_scan_per_group(2, True)]
     caught = 0
     for pin in pins:
         try:
@@ -147,3 +149,40 @@ def test_ssd_mutant_is_caught(name, monkeypatch):
         except AssertionError:
             caught += 1
     assert caught, f"no pin caught {name}"
+
+
+@pytest.mark.parametrize("ngroups,gate", [(2, True), (3, False), (6, True)])
+def test_groups_equal_the_recurrent_scan_per_group(ngroups, gate):
+    """B, C of shape [batch, L, ngroups, dstate]: run g of H / ngroups consecutive heads uses group g's B_t, C_t.
+    Each run equals the recurrent C oracle over that run's channels with that group's B and C (head-broadcast as
+    in test_masked_form_equals_the_recurrent_scan), y and the final state, from a given state too."""
+    batch, L, H, P, N = 2, 23, 6, 3, 4
+    rng = np.random.default_rng(40 + ngroups)
+    x = rng.standard_normal((batch, L, H, P))
+    z = rng.standard_normal((batch, L, H, P)) if gate else None
+    dl = rng.standard_normal((batch, L, H))
+    A = -rng.uniform(0.2, 3.0, H)
+    B = rng.standard_normal((batch, L, ngroups, N))
+    C = rng.standard_normal((batch, L, ngroups, N))
+    D = rng.uniform(0.5, 1.5, H)
+    bias = np.log(np.expm1(rng.uniform(1e-3, 0.2, H)))
+    h0 = rng.standard_normal((batch, H, P, N))
+    y, fs = S.ssd_fwd(x, dl, A, B, C, D=D, z=z, delta_bias=bias, initial_state=h0)
+    per = H // ngroups
+    rep = lambda a: np.repeat(a, P, axis=-1)
+    for g in range(ngroups):
+        hs = slice(g * per, (g + 1) * per)
+        xr = x[:, :, hs].reshape(batch, L, per * P)
+        yr, fr = R.scan_fwd_ex(xr, rep(dl[:, :, hs]), np.repeat(A[hs], P)[:, None] * np.ones((1, N)),
+                               B[:, :, g], C[:, :, g], D=rep(D[hs]),
+                               z=None if z is None else z[:, :, hs].reshape(batch, L, per * P),
+                               delta_bias=rep(bias[hs]), initial_state=h0[:, hs].reshape(batch, per * P, N))
+        np.testing.assert_allclose(y[:, :, hs].reshape(batch, L, per * P), yr, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(fs[:, hs].reshape(batch, per * P, N), fr, rtol=1e-10, atol=1e-12)
+
+
+def test_one_group_is_the_shared_shape():
+    x, dl, A, B, C, D, z, bias = _case(7, 2, 19, 3, 4, 5)
+    y1, f1 = S.ssd_fwd(x, dl, A, B, C, D=D, z=z, delta_bias=bias)
+    y2, f2 = S.ssd_fwd(x, dl, A, B[:, :, None, :], C[:, :, None, :], D=D, z=z, delta_bias=bias)
+    assert np.array_equal(y1, y2) and np.array_equal(f1, f2)
