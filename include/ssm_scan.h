@@ -205,14 +205,20 @@ ssm_status_t ssm_scan_trap_fwd(const void* u, const void* delta, const float* A,
  * state matrix A (times the identity), which makes the sequence map a causal
  * 1-semiseparable matrix computed blockwise with matrix products.  Per batch
  * row and head (headdim channels sharing the step and A; B_t, C_t shared by
- * all heads) the state H (headdim x dstate) runs
+ * the heads of a group) the state H (headdim x dstate) runs
  *     H_t = exp(delta_t A) H_{t-1} + delta_t x_t B_t^T,   H_{-1} = initial_state or 0,
  *     y_t = (H_t C_t + D x_t) * SiLU(z_t)   (skip and gate optional),
  * with delta_t = softplus(delta_raw + bias) (or raw + bias when
- * softplus_flag = 0).  This equals ssm_scan_fwd with dim = heads * headdim,
- * A[d][n] = A[head of d] and the head's step on each of its channels.
+ * softplus_flag = 0).  With one group this equals ssm_scan_fwd with dim =
+ * heads * headdim, A[d][n] = A[head of d] and the head's step on each of its
+ * channels.  Groups: the page casts B_t as the keys and C_t as the queries of
+ * masked linear attention; as grouped attention shares keys and queries among
+ * heads, runs of heads / ngroups consecutive heads share a group's B_t, C_t
+ * (head h reads group h / (heads / ngroups)); each group is then the
+ * one-group layer over its heads.
  *   x, z, y: [batch, L, heads, headdim]; delta: [batch, L, heads]; B, C:
- *   [batch, L, dstate] (all bf16); A, D, delta_bias: [heads] fp32;
+ *   [batch, L, ngroups, dstate] (all bf16); ngroups >= 1 divides heads (else
+ *   INVALID_ARG); A, D, delta_bias: [heads] fp32;
  *   final_state (nullable): [batch, heads, headdim, dstate] fp32.
  *   initial_state (nullable): the same layout, the state before token 0 of
  *   each (row, head), e.g. the final_state of the call over the tokens before
@@ -222,17 +228,17 @@ ssm_status_t ssm_scan_trap_fwd(const void* u, const void* delta, const float* A,
  *   initial_state, final_state.
  *   x, B, C must be 16-byte aligned, delta, z, y 2-byte, the fp32 arrays
  *   4-byte (else INVALID_ARG).  Supported: dt = BF16, headdim = 64 and
- *   dstate = 32, 64 or 128, with (L + 64) * heads * headdim * 2 bytes below
- *   2^31 (else UNSUPPORTED).  Arithmetic: bf16 matrix products with fp32
+ *   dstate = 32, 64 or 128, with (L + 64) * heads * headdim * 2 and
+ *   (L + 64) * ngroups * dstate * 2 bytes below 2^31 (else UNSUPPORTED).  Arithmetic: bf16 matrix products with fp32
  *   accumulation, fp32 state.  workspace: workspace_bytes >=
  *   ssm_ssd_fwd_workspace_size() bytes of device memory, 256-byte aligned
  *   (may be NULL when that size is 0), overwritten by the call and not to be
  *   shared with a concurrent call.  y must not alias an input. */
 ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                          const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                         const float* initial_state, void* y, float* final_state, int64_t batch, int64_t L, int64_t heads, int64_t headdim,
-                         int64_t dstate, ssm_dtype_t dt, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream);
+                         const float* initial_state, void* y, float* final_state, int64_t batch, int64_t L,
+                         int64_t heads, int64_t headdim, int64_t ngroups, int64_t dstate, ssm_dtype_t dt,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Bytes of device workspace ssm_ssd_fwd needs: 0 when there are at most as
  * many (batch row, head) units as compute units (or more than 1.5 per CU);

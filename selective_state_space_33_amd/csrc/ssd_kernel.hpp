@@ -48,8 +48,8 @@ struct SsdParams {
   const void* x;       // [batch][L][H][P] bf16
   const void* delta;   // [batch][L][H] bf16 (raw)
   const float* A;      // [H]
-  const void* B;       // [batch][L][N] bf16
-  const void* C;       // [batch][L][N] bf16
+  const void* B;       // [batch][L][ngroups][N] bf16
+  const void* C;       // [batch][L][ngroups][N] bf16
   const float* D;      // [H] (nullable)
   const void* z;       // [batch][L][H][P] bf16 (nullable)
   const float* bias;   // [H] (nullable)
@@ -57,6 +57,7 @@ struct SsdParams {
   float* final_state;  // [batch][H][P][N] (nullable)
   const float* h0;     // [batch][H][P][N]: the state before token 0 (nullable: zero)
   int64_t batch, L, H;
+  int64_t ngroups;     // head h reads group h / (H / ngroups) of B and C
   int softplus;
   // Chained launches (n_split > 0): units (batch row, head) 0 .. n_long-1
   // whole, n_long .. n_long+n_split-1 cut into Ks segments of seg_chunks
@@ -153,6 +154,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   // byte offset (one chunk past L included) below 2^31, so offsets are 32-bit
   const int rowe = static_cast<int>(H * P);
   const int H32 = static_cast<int>(H);
+  const int BS = static_cast<int>(p.ngroups) * N;  // elements per token row of B and C
 
   // ---- the unit (batch row b, head h) being worked on
   int64_t b = 0, h = 0;
@@ -170,8 +172,11 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
     rs_x = make_rsrc(static_cast<const unsigned short*>(p.x) + xbase, xbytes);
     rs_z = make_rsrc(p.z ? static_cast<const unsigned short*>(p.z) + xbase : nullptr, p.z ? xbytes : 0);
     rs_y = make_rsrc(static_cast<unsigned short*>(p.y) + xbase, xbytes);
-    rs_b = make_rsrc(static_cast<const unsigned short*>(p.B) + b * L * N, L * N * 2);
-    rs_c = make_rsrc(static_cast<const unsigned short*>(p.C) + b * L * N, L * N * 2);
+    // B and C of the head's group: token rows of BS elements, the group's N at offset g * N
+    const int64_t g = h / (H / p.ngroups);
+    const int64_t bcbase = (b * L * p.ngroups + g) * N;
+    rs_b = make_rsrc(static_cast<const unsigned short*>(p.B) + bcbase, (L * p.ngroups - g) * N * 2);
+    rs_c = make_rsrc(static_cast<const unsigned short*>(p.C) + bcbase, (L * p.ngroups - g) * N * 2);
     rs_d = make_rsrc(static_cast<const unsigned short*>(p.delta) + b * L * H + h, (L * H - h) * 2);
   };
 
@@ -195,7 +200,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       const int row = e / (N / 8), col = (e % (N / 8)) * 8;
       if (e < C_PIECES)
         gc[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rs_c, ((t0 + row) * N + col) * 2, 0, 0));
+                                                rs_c, ((t0 + row) * BS + col) * 2, 0, 0));
     }
   };
   auto load_b = [&](int t0) {
@@ -206,7 +211,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       if (e < B_ITEMS) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          gb[i][r] = __builtin_amdgcn_raw_buffer_load_b32(rs_b, ((t0 + s0 + r) * N + 2 * np) * 2, 0, 0);
+          gb[i][r] = __builtin_amdgcn_raw_buffer_load_b32(rs_b, ((t0 + s0 + r) * BS + 2 * np) * 2, 0, 0);
       }
     }
   };

@@ -56,11 +56,11 @@ SsdPlan plan_ssd(int64_t batch, int64_t L, int64_t heads, int64_t dstate) {
   return pl;
 }
 
-bool ssd_shape_ok(int64_t L, int64_t heads, int64_t headdim, int64_t dstate, ssm_dtype_t dt) {
+bool ssd_shape_ok(int64_t L, int64_t heads, int64_t headdim, int64_t ngroups, int64_t dstate, ssm_dtype_t dt) {
   if (dt != SSM_DTYPE_BF16 || headdim != kSsdP || (dstate != 32 && dstate != 64 && dstate != 128)) return false;
   // token rows are addressed with 32-bit byte offsets (up to one chunk past L)
   const int64_t rows = L + kSsdQ;
-  return rows * heads * headdim * 2 < 0x7fffffffLL && rows * dstate * 2 < 0x7fffffffLL;
+  return rows * heads * headdim * 2 < 0x7fffffffLL && rows * ngroups * dstate * 2 < 0x7fffffffLL;
 }
 
 template <int N>
@@ -77,17 +77,18 @@ using namespace ssm;
 extern "C" size_t ssm_ssd_fwd_workspace_size(int64_t batch, int64_t L, int64_t heads, int64_t headdim,
                                              int64_t dstate, ssm_dtype_t dt) {
   if (batch <= 0 || L <= 0 || heads <= 0 || headdim <= 0 || dstate <= 0) return 0;
-  if (!ssd_shape_ok(L, heads, headdim, dstate, dt) || batch * heads > 0x7fffffffLL) return 0;
+  if (!ssd_shape_ok(L, heads, headdim, 1, dstate, dt) || batch * heads > 0x7fffffffLL) return 0;
   return plan_ssd(batch, L, heads, dstate).total;
 }
 
 extern "C" ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const float* A, const void* B, const void* C,
                                     const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                                    const float* initial_state, void* y, float* final_state, int64_t batch, int64_t L, int64_t heads,
-                                    int64_t headdim, int64_t dstate, ssm_dtype_t dt, void* workspace,
-                                    size_t workspace_bytes, hipStream_t stream) {
+                                    const float* initial_state, void* y, float* final_state, int64_t batch,
+                                    int64_t L, int64_t heads, int64_t headdim, int64_t ngroups, int64_t dstate,
+                                    ssm_dtype_t dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!x || !delta || !A || !B || !C || !y) return SSM_ERR_INVALID_ARG;
   if (batch <= 0 || L <= 0 || heads <= 0 || headdim <= 0 || dstate <= 0) return SSM_ERR_INVALID_ARG;
+  if (ngroups <= 0 || heads % ngroups != 0) return SSM_ERR_INVALID_ARG;
   if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return SSM_ERR_INVALID_ARG;
   // 16-byte pieces of token rows are loaded; scalars and states are fp32
   if (!ssd_aligned(x, 16) || !ssd_aligned(B, 16) || !ssd_aligned(C, 16) || !ssd_aligned(delta, 2) ||
@@ -96,7 +97,8 @@ extern "C" ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const floa
   const float* f32s[] = {A, D, delta_bias, final_state, initial_state};
   for (const float* q : f32s)
     if (q && !ssd_aligned(q, 4)) return SSM_ERR_INVALID_ARG;
-  if (!ssd_shape_ok(L, heads, headdim, dstate, dt) || batch * heads > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
+  if (!ssd_shape_ok(L, heads, headdim, ngroups, dstate, dt) || batch * heads > 0x7fffffffLL)
+    return SSM_ERR_UNSUPPORTED;
   const SsdPlan pl = plan_ssd(batch, L, heads, dstate);
   if (pl.total > 0 && (!workspace || workspace_bytes < pl.total || !ssd_aligned(workspace, 256)))
     return SSM_ERR_INVALID_ARG;
@@ -115,6 +117,7 @@ extern "C" ssm_status_t ssm_ssd_fwd(const void* x, const void* delta, const floa
   p.batch = batch;
   p.L = L;
   p.H = heads;
+  p.ngroups = ngroups;
   p.softplus = softplus_flag ? 1 : 0;
   p.n_long = pl.n_long;
   p.n_split = pl.n_split;

@@ -183,17 +183,18 @@ SSD_WORKLOADS = {
 
 
 def random_ssd_inputs(rng: np.random.Generator, batch: int, L: int, heads: int, headdim: int, dstate: int,
-                      dtype: str = "bf16", gate: bool = True) -> dict:
+                      dtype: str = "bf16", gate: bool = True, ngroups: int = 0) -> dict:
     """Seeded inputs of the SSD layer (float32 arrays, bf16-representable where stored as bf16).
 
     x, z: [batch, L, heads, headdim] ~ N(0, 1); delta (raw): [batch, L, heads] ~ N(0, 1); B, C: [batch, L, dstate]
-    ~ N(0, 1); A: [heads] = -U[1, 16] (a scalar per head); D = 1; delta_bias = log(expm1(U[1e-3, 0.1])), so
-    softplus(bias) is uniform in [1e-3, 0.1]."""
+    (ngroups = 0) or [batch, L, ngroups, dstate] ~ N(0, 1); A: [heads] = -U[1, 16] (a scalar per head); D = 1;
+    delta_bias = log(expm1(U[1e-3, 0.1])), so softplus(bias) is uniform in [1e-3, 0.1]."""
     x = rng.standard_normal((batch, L, heads, headdim), dtype=np.float32)
     z = rng.standard_normal((batch, L, heads, headdim), dtype=np.float32) if gate else None
     delta = rng.standard_normal((batch, L, heads), dtype=np.float32)
-    B = rng.standard_normal((batch, L, dstate), dtype=np.float32)
-    C = rng.standard_normal((batch, L, dstate), dtype=np.float32)
+    bc_shape = (batch, L, dstate) if ngroups == 0 else (batch, L, ngroups, dstate)
+    B = rng.standard_normal(bc_shape, dtype=np.float32)
+    C = rng.standard_normal(bc_shape, dtype=np.float32)
     A = -rng.uniform(1.0, 16.0, size=heads).astype(np.float32)
     bias = np.log(np.expm1(rng.uniform(1e-3, 0.1, size=heads))).astype(np.float32)
     return {

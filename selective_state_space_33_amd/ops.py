@@ -72,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_trap_fwd.restype = ctypes.c_int
         L.ssm_scan_trap_fwd.argtypes = L.ssm_scan_fwd_ex.argtypes
         L.ssm_ssd_fwd.restype = ctypes.c_int
-        L.ssm_ssd_fwd.argtypes = ([_vp] * 8 + [ctypes.c_int, _vp, _vp, _vp] + [_i64] * 5 +
+        L.ssm_ssd_fwd.argtypes = ([_vp] * 8 + [ctypes.c_int, _vp, _vp, _vp] + [_i64] * 6 +
                                   [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
         L.ssm_ssd_fwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_ssd_fwd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int]
@@ -265,16 +265,18 @@ def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bo
                 check_status: bool = False):
     """The Mamba-2 SSD layer on the GPU.
 
-    x, z: [batch, L, heads, headdim]; delta: [batch, L, heads]; B, C: [batch, L, dstate] (bfloat16);
-    A, D, delta_bias: [heads] (float32); initial_state: [batch, heads, headdim, dstate] (float32) or None.
+    x, z: [batch, L, heads, headdim]; delta: [batch, L, heads]; B, C: [batch, L, dstate] or
+    [batch, L, ngroups, dstate] (bfloat16; heads a multiple of ngroups); A, D, delta_bias: [heads] (float32);
+    initial_state: [batch, heads, headdim, dstate] (float32) or None.
     Returns (y, final_state [batch, heads, headdim, dstate] or None)."""
     batch, L, heads, headdim = x.shape
-    dstate = B.shape[2]
+    ngroups = 1 if B.dim() == 3 else B.shape[2]
+    dstate = B.shape[-1]
+    bc_shape = (batch, L, dstate) if B.dim() == 3 else (batch, L, ngroups, dstate)
     dev, dt = x.device, x.dtype
     code = _dtype_code(dt)
     for name, t, shp in (("x", x, (batch, L, heads, headdim)), ("z", z, (batch, L, heads, headdim)),
-                         ("delta", delta, (batch, L, heads)), ("B", B, (batch, L, dstate)),
-                         ("C", C, (batch, L, dstate))):
+                         ("delta", delta, (batch, L, heads)), ("B", B, bc_shape), ("C", C, bc_shape)):
         _check(t, name, dt, shp, dev)
     for name, t in (("A", A), ("D", D), ("delta_bias", delta_bias)):
         _check(t, name, torch.float32, (heads,), dev)
@@ -292,7 +294,7 @@ def ssm_ssd_fwd(x, delta, A, B, C, D=None, z=None, delta_bias=None, softplus: bo
     _check(final_state, "final_state", torch.float32, (batch, heads, headdim, dstate), dev)
     rc = lib().ssm_ssd_fwd(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                            1 if softplus else 0, _ptr(initial_state), _ptr(y), _ptr(final_state), batch, L, heads,
-                           headdim, dstate, code, _ptr(workspace), _ws_bytes(workspace), s.cuda_stream)
+                           headdim, ngroups, dstate, code, _ptr(workspace), _ws_bytes(workspace), s.cuda_stream)
     if rc != SSM_OK:
         raise SSMError(rc, "ssm_ssd_fwd")
     if check_status:

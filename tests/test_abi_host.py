@@ -227,11 +227,11 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 def _ssd(lib_, **kw):
     """Call ssm_ssd_fwd with fake (never dereferenced) pointers; only rejection paths are used."""
     a = dict(x=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, z=None, bias=None, sp=1, h0=None,
-             y=0x6000, fs=None, batch=1, L=8, H=2, P=64, N=64, dt=BF16, ws=None, wsb=0, stream=None)
+             y=0x6000, fs=None, batch=1, L=8, H=2, P=64, G=1, N=64, dt=BF16, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib_.ssm_ssd_fwd(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["h0"],
-                            a["y"], a["fs"], a["batch"], a["L"], a["H"], a["P"], a["N"], a["dt"], a["ws"], a["wsb"],
-                            a["stream"])
+                            a["y"], a["fs"], a["batch"], a["L"], a["H"], a["P"], a["G"], a["N"], a["dt"], a["ws"],
+                            a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,expect", [
@@ -241,6 +241,8 @@ def _ssd(lib_, **kw):
     (dict(h0=0x8002), INVALID),
     (dict(dt=F32), UNSUPPORTED), (dict(P=32), UNSUPPORTED), (dict(N=16), UNSUPPORTED), (dict(N=96), UNSUPPORTED),
     (dict(L=1 << 20, H=40), UNSUPPORTED),   # token rows past 2^31 bytes
+    (dict(G=0), INVALID), (dict(H=6, G=4), INVALID),   # ngroups must divide heads
+    (dict(L=1 << 22, H=2, G=2, N=128), UNSUPPORTED),    # B/C rows past 2^31 bytes
     (dict(batch=4, H=80), INVALID),           # 320 units: the chained plan needs its workspace
 ])
 def test_ssd_rejects_bad_arguments_without_launching(kw, expect):

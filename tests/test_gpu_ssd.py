@@ -36,7 +36,7 @@ def _run(x, softplus=True, h0=None):
 
 
 def _check(x, label, softplus=True, tol=TOL["bf16"], h0=None):
-    say(f"ssd {label} x={x['x'].shape} N={x['B'].shape[2]}")
+    say(f"ssd {label} x={x['x'].shape} B={x['B'].shape}")
     yg, fg = _run(x, softplus, h0)
     yo, fo = S.ssd_fwd(x["x"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
                        softplus=softplus, initial_state=h0)
@@ -204,3 +204,20 @@ def test_ssd_continues_from_its_final_state():
     ef = rel_err(f2, f_all)
     print(f"[parity] ssd continuation: y {ey:.2e}  final {ef:.2e}", flush=True)
     assert ey <= TOL["bf16"] and ef <= 1e-4, (ey, ef)
+
+
+@pytest.mark.parametrize("ngroups,heads,N", [(2, 4, 64), (4, 8, 32), (3, 6, 128), (8, 8, 64)])
+def test_ssd_groups_match_oracle(ngroups, heads, N):
+    """B, C of shape [batch, L, ngroups, dstate]: runs of heads / ngroups heads share a group (the oracle pinned per
+    group to the recurrent scan); ragged L, from a given state."""
+    rng = np.random.default_rng(790 + ngroups * 10 + heads)
+    x = I.random_ssd_inputs(rng, 2, 333, heads, 64, N, ngroups=ngroups)
+    h0 = (rng.standard_normal((2, heads, 64, N)) * 0.5).astype(np.float32)
+    _check(x, f"{ngroups} groups of {heads // ngroups} heads N={N}", h0=h0)
+
+
+def test_ssd_groups_chained_plan(monkeypatch):
+    """Groups on the chained plan: 10 (row, head) units on a plan for 8 CUs (8 whole, 2 cut into 4 segments)."""
+    monkeypatch.setenv("SSM_NUM_CU", "8")
+    x = I.random_ssd_inputs(np.random.default_rng(799), 1, 700, 10, 64, 64, ngroups=5)
+    _check(x, "5 groups, chained for 8 CUs")
