@@ -24,6 +24,12 @@ dfinal_state, the gradient reaching the final state, if any).
 
 The transcription is independent of the C oracle (ssm_ref.c); the tests pin
 it to that oracle's forward and to central finite differences of it.
+
+Packed sequences (cu_seqlens, batch 1): sequence s is tokens cu[s] ..
+cu[s+1]-1 of the row, run on its own from initial_state[s] (zero if none)
+with its own final state, as the forward's packed scan defines it; the
+scalar differentiated sums y*dy over the row and final_state[s] *
+dfinal_state[s] over the sequences.
 """
 import numpy as np
 import torch
@@ -55,10 +61,32 @@ def forward_torch(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=T
     return y, h
 
 
+def forward_packed_torch(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, cu_seqlens):
+    """forward_torch over each packed sequence of batch row 0, from its own initial state (None: zero).
+    Returns (y [1, L, dim], final_state [nseq, dim, N])."""
+    nseq = len(cu_seqlens) - 1
+    dim, N = A.shape
+    ys, fss = [], []
+    for s in range(nseq):
+        a, b = int(cu_seqlens[s]), int(cu_seqlens[s + 1])
+        sl = lambda t: None if t is None else t[:, a:b]  # noqa: E731
+        h0 = None if initial_state is None else initial_state[s:s + 1]
+        if b > a:
+            y, fs = forward_torch(sl(u), sl(delta), A, sl(B), sl(C), D=D, z=sl(z), delta_bias=delta_bias,
+                                  softplus=softplus, initial_state=h0)
+            ys.append(y)
+        else:
+            fs = torch.zeros((1, dim, N), dtype=torch.float64) if h0 is None else h0
+        fss.append(fs)
+    return torch.cat(ys, dim=1), torch.cat(fss, dim=0)
+
+
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, dfinal_state=None,
-             initial_state=None):
+             initial_state=None, cu_seqlens=None):
     """Gradients of sum(y*dy) + sum(final_state*dfinal_state) with respect to every input.
 
+    With cu_seqlens (batch 1) the row holds packed sequences: initial_state, dfinal_state and the returned
+    dinitial_state are [nseq, dim, N].
     Returns a dict of float64 numpy arrays: du, ddelta, dA, dB, dC, and dD, dz,
     ddelta_bias, dinitial_state for the optional inputs that were given (None otherwise)."""
     names = ["u", "delta", "A", "B", "C", "D", "z", "delta_bias", "initial_state"]
@@ -69,8 +97,12 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
         if tv is not None:
             tv.requires_grad_(True)
         ts[n] = tv
-    y, fs = forward_torch(ts["u"], ts["delta"], ts["A"], ts["B"], ts["C"], D=ts["D"], z=ts["z"],
-                          delta_bias=ts["delta_bias"], softplus=softplus, initial_state=ts["initial_state"])
+    if cu_seqlens is not None:
+        y, fs = forward_packed_torch(ts["u"], ts["delta"], ts["A"], ts["B"], ts["C"], ts["D"], ts["z"],
+                                     ts["delta_bias"], softplus, ts["initial_state"], list(cu_seqlens))
+    else:
+        y, fs = forward_torch(ts["u"], ts["delta"], ts["A"], ts["B"], ts["C"], D=ts["D"], z=ts["z"],
+                              delta_bias=ts["delta_bias"], softplus=softplus, initial_state=ts["initial_state"])
     obj = (y * _t(dy)).sum()
     if dfinal_state is not None:
         obj = obj + (fs * _t(dfinal_state)).sum()

@@ -145,3 +145,46 @@ def test_relay_example_gradients_by_hand():
     np.testing.assert_allclose(g["ddelta"].ravel(), [(0.4 / d1) * (1 + a2), -a2 * b1 + 1.0 / d2], rtol=1e-13)
     # dA: a2 = exp(Delta_2 A), da2/dA = Delta_2 a2, times d(obj)/da2 = b1
     np.testing.assert_allclose(g["dA"].ravel(), [d2 * a2 * b1], rtol=1e-13)
+
+
+@pytest.mark.parametrize("cuts", [[0, 3, 3, 9, 10], [0, 10], [0, 1, 5, 10]])
+def test_packed_gradients_match_central_differences(cuts):
+    """Packed sequences (an empty and a one-token sequence among them): every gradient, d initial_state per
+    sequence included, matches central differences of the C oracle's packed forward (scan_fwd_ex with
+    cu_seqlens, pinned in test_oracle_ex.py to independent scans of the slices)."""
+    rng = np.random.default_rng(31 + len(cuts))
+    L, dim, N = cuts[-1], 3, 4
+    x = _inputs(rng, 1, L, dim, N)
+    nseq = len(cuts) - 1
+    h0 = rng.standard_normal((nseq, dim, N))
+    dy = rng.standard_normal((1, L, dim))
+    dfs = rng.standard_normal((nseq, dim, N))
+    cu = np.asarray(cuts, dtype=np.int64)
+
+    def obj():
+        y, fs = R.scan_fwd_ex(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                              delta_bias=x["delta_bias"], initial_state=h0, cu_seqlens=cu)
+        return float(np.sum(y * dy) + np.sum(fs * dfs))
+
+    g = OB.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                    dfinal_state=dfs, initial_state=h0, cu_seqlens=cu)
+    checked = 0
+    for arr, name in [(h0, "dinitial_state"), (x["u"], "du"), (x["delta"], "ddelta"), (x["A"], "dA"),
+                      (x["B"], "dB"), (x["C"], "dC"), (x["D"], "dD"), (x["z"], "dz"), (x["delta_bias"], "ddelta_bias")]:
+        flat = arr.reshape(-1)
+        for i in rng.choice(flat.size, size=min(6, flat.size), replace=False):
+            e = 1e-6 * max(1.0, abs(flat[i]))
+            o = flat[i]
+            flat[i] = o + e
+            fp = obj()
+            flat[i] = o - e
+            fm = obj()
+            flat[i] = o
+            fd = (fp - fm) / (2 * e)
+            assert abs(g[name].reshape(-1)[i] - fd) <= 2e-7 * max(1.0, abs(fd)), (name, i)
+            checked += 1
+    assert checked >= 40
+    # an empty sequence hands its final-state gradient straight to its initial state
+    for s in range(nseq):
+        if cuts[s + 1] == cuts[s]:
+            np.testing.assert_array_equal(g["dinitial_state"][s], dfs[s])
