@@ -268,12 +268,15 @@ ssm_status_t ssm_state_update(float* state, const void* u, const void* delta, co
  * 4 / 16 bytes), and per-tile partial sums of dB and dC (about 2 * batch *
  * L * dim / 64 * dstate * 4 bytes) and of dA, dD and d(delta_bias) per batch
  * row (and per chunk slot, plus the adjoints handed between chunks, when
- * there are between 1 and 1.5 tiles of 64 channels per compute unit).
- * Returns 0 for arguments ssm_scan_bwd would reject. */
-size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt);
+ * there are between 1 and 1.5 tiles of 64 channels per compute unit).  With
+ * nseq > 0 packed sequences (batch 1): partial rows per sequence, a few more
+ * checkpoints per sequence and the launch order.  Returns 0 for arguments
+ * ssm_scan_bwd would reject. */
+size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int64_t nseq,
+                                   ssm_dtype_t dt);
 
-/* Backward of ssm_scan_fwd (or of ssm_scan_fwd_ex from an initial state,
- * without packed sequences): the gradients of
+/* Backward of ssm_scan_fwd, or of ssm_scan_fwd_ex from initial states and
+ * over packed sequences: the gradients of
  *     sum(y * dy) + sum(final_state * dfinal_state)
  * with respect to u, delta, A, B, C, D, z, delta_bias and the initial
  * state, for the same inputs and flags as the forward call.  The states are recomputed from the
@@ -293,12 +296,19 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_
  *   is the one of the raw input (through softplus and the bias when on).
  *   dA, dD and ddelta_bias sum over the batch and the sequence, dB and dC
  *   over the channels, in a fixed order (results are deterministic).
+ *   cu_seqlens (NULL: none), nseq: packed sequences as in ssm_scan_fwd_ex
+ *   (batch 1, nseq + 1 int64 device offsets, 8-byte aligned, clamped into
+ *   [0, L] on the device); each sequence runs from initial_state[s] with
+ *   its own final state, so initial_state, dfinal_state and dinitial_state
+ *   are then [nseq, dim, dstate], and an empty sequence hands
+ *   dfinal_state[s] to dinitial_state[s] unchanged.
  *   No output may alias an input or another output.  workspace must hold
  *   ssm_scan_bwd_workspace_size() bytes of device memory, 256-byte aligned.
  *   UNSUPPORTED for dstate > 32 or batch > 65535. */
 ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                           const float* D, const void* z, const float* delta_bias, int softplus_flag,
                           const void* dy, const float* dfinal_state, const float* initial_state,
+                          const int64_t* cu_seqlens, int64_t nseq,
                           void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
                           float* ddelta_bias, float* dinitial_state,
                           int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,

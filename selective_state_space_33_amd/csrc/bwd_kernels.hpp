@@ -90,6 +90,13 @@ struct BwdParams {
   // dA/dD/dbias partials then have Ks slots: row slot * batch + b.
   int n_long, n_split, Ks;
   int chunk_blocks;
+  // Packed sequences (cu non-null, batch row 0, no chained plan): unit j is tile
+  // column j % ntd of sequence order[j / ntd] (index order when order is null),
+  // tokens cu[s] .. cu[s+1]-1 (clamped into [0, L]); the final-state and
+  // initial-state gradients and the dA/dD/dbias partial rows are per sequence,
+  // and the sequence's checkpoints start at block cu[s] / 16 + kPackedCkptSlack * s.
+  const int64_t* cu;
+  const int* order;
   float* carry;
   unsigned* flags;
   unsigned* ticket;
@@ -163,19 +170,26 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   const bool sp_on = p.softplus != 0;
   const int row_bytes = static_cast<int>(dim * ES);
   const int rec_voff = (lane & 15) * 4;
-  const int nblk = static_cast<int>((L + TB - 1) / TB);
+  int nblk = static_cast<int>((L + TB - 1) / TB);  // blocks of the unit's stretch
 
-  // ---- the tile (64 channels of one batch row) the blocks below work on
+  // ---- the tile (64 channels of one batch row) the blocks below work on, and
+  // the stretch of its row: tokens t_begin .. t_begin+len-1 (the whole row,
+  // or a packed sequence); srow indexes the final-state and initial-state
+  // gradients and the dA/dD/dbias partial rows (the batch row, or the sequence)
   int tile = 0;
-  int64_t b = 0, d0 = 0, d = 0;
+  int64_t b = 0, d0 = 0, d = 0, t_begin = 0, len = L, srow = 0;
   bool dvalid = false;
   float A2[NPL], An[NPL];
   float Dd = 0.0f, bias_d = 0.0f;
   rsrc_t rs_u, rs_d, rs_z, rs_dy, rs_du, rs_dd, rs_dz, rs_bc;
   const float* ckpt_row = p.ckpt;
-  auto set_tile = [&](int t) {
+  auto set_tile = [&](int t, int64_t tb = 0, int64_t tl = -1, int64_t sr = -1, int64_t ckpt_slot0 = 0) {
     tile = t;
     b = t / p.ntd;
+    t_begin = tb;
+    len = tl < 0 ? L : tl;
+    srow = sr < 0 ? b : sr;
+    nblk = static_cast<int>((len + TB - 1) / TB);
     d0 = static_cast<int64_t>(t % p.ntd) * 64;
     d = d0 + lane;
     dvalid = d < dim;
@@ -191,8 +205,8 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     // buffer resources: rows past L read as zero and their stores are
     // dropped; lanes past dim are masked at the stores.  The host keeps L
     // rows of the tensor within 2^31 bytes.
-    const int64_t base_off = (b * L * dim + d0) * ES;
-    const int64_t bytes = L * row_bytes - d0 * ES;
+    const int64_t base_off = ((b * L + t_begin) * dim + d0) * ES;
+    const int64_t bytes = len * row_bytes - d0 * ES;
     auto rs_of = [&](const void* ptr) {
       return make_rsrc(ptr ? static_cast<const char*>(ptr) + base_off : nullptr, ptr ? bytes : 0);
     };
@@ -203,9 +217,9 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     rs_du = rs_of(p.du);
     rs_dd = rs_of(p.ddelta);
     rs_dz = rs_of(p.dz);
-    const float* bc_row = p.bc + ((b * G + w) * p.Lp) * (2 * NPL);
-    rs_bc = make_rsrc(bc_row, (p.Lp + 32) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
-    ckpt_row = p.ckpt + (static_cast<int64_t>(t) * p.ckpt_blocks * 64 + lane) * NPAD + n0;
+    const float* bc_row = p.bc + ((b * G + w) * p.Lp + t_begin) * (2 * NPL);
+    rs_bc = make_rsrc(bc_row, (p.Lp + 32 - t_begin) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
+    ckpt_row = p.ckpt + ((static_cast<int64_t>(t) * p.ckpt_blocks + ckpt_slot0) * 64 + lane) * NPAD + n0;
   };
 
   // ---- running sums of the stretch being worked on: the adjoint entering the
@@ -216,7 +230,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
       const int n = n0 + j;
-      dhn[j] = (dvalid && n < N && p.dfs) ? p.dfs[(b * dim + d) * N + n] : 0.0f;
+      dhn[j] = (dvalid && n < N && p.dfs) ? p.dfs[(srow * dim + d) * N + n] : 0.0f;
       dAacc[j] = 0.0f;
     }
     accD = accBias = 0.0f;
@@ -257,7 +271,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = w + i * G;
-      const bool live = t0 + row < L && dvalid;  // lanes past dim read the next row: keep them at zero
+      const bool live = t0 + row < len && dvalid;  // lanes past dim read the next row: keep them at zero
       float uf, df, zf, gf;
       unpack<IO, 1>(qu[S][i], &uf);
       unpack<IO, 1>(qd[S][i], &df);
@@ -403,13 +417,14 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     }
     for (int q = tid; q < TB * NPAD; q += 64 * G) {
       const int t = q / NPAD, n = q % NPAD;
+      if (t0 + t >= len) continue;  // past the stretch: the next packed sequence's tokens
       float sb = 0.0f, sc = 0.0f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         sb += sRB[t][n][r];
         sc += sRC[t][n][r];
       }
-      const int64_t o = ((b * p.ntd + tile % p.ntd) * p.Lp + t0 + t) * NPAD + n;
+      const int64_t o = ((b * p.ntd + tile % p.ntd) * p.Lp + t_begin + t0 + t) * NPAD + n;
       p.dB_part[o] = sb;
       p.dC_part[o] = sc;
     }
@@ -449,7 +464,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     if (dvalid) {
       for (int s = 0; s < nslots; ++s) {
         if (s != slot && !zero_others) continue;
-        const int64_t row = static_cast<int64_t>(s) * p.batch + b;
+        const int64_t row = static_cast<int64_t>(s) * p.batch + srow;
 #pragma unroll
         for (int j = 0; j < NPL; ++j) p.dA_part[(row * dim + d) * NPAD + n0 + j] = s == slot ? dAacc[j] : 0.0f;
       }
@@ -466,7 +481,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       }
       for (int s = 0; s < nslots; ++s) {
         if (s != slot && !zero_others) continue;
-        const int64_t row = static_cast<int64_t>(s) * p.batch + b;
+        const int64_t row = static_cast<int64_t>(s) * p.batch + srow;
         p.dD_part[row * dim + d] = s == slot ? sd : 0.0f;
         p.dbias_part[row * dim + d] = s == slot ? sb : 0.0f;
       }
@@ -478,10 +493,23 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     if (dvalid && p.dh0) {
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
-        if (n0 + j < N) p.dh0[(b * dim + d) * N + n0 + j] = dhn[j];
+        if (n0 + j < N) p.dh0[(srow * dim + d) * N + n0 + j] = dhn[j];
     }
   };
 
+  if (p.cu != nullptr) {  // packed: one workgroup per (tile column, sequence)
+    const int col = static_cast<int>(blockIdx.x % p.ntd);
+    const int s = p.order ? p.order[blockIdx.x / p.ntd] : static_cast<int>(blockIdx.x / p.ntd);
+    int64_t tb = p.cu[s], te = p.cu[s + 1];
+    tb = tb < 0 ? 0 : (tb > L ? L : tb);
+    te = te < tb ? tb : (te > L ? L : te);
+    set_tile(col, tb, te - tb, s, tb / TB + static_cast<int64_t>(kPackedCkptSlack) * s);
+    start_from_final();
+    run_blocks(0, nblk, nullptr, 0);
+    write_dh0();
+    write_partials(0, false);
+    return;
+  }
   if (p.n_split == 0) {  // one workgroup per tile
     set_tile(blockIdx.x);
     start_from_final();

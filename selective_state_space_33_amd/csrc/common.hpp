@@ -223,6 +223,12 @@ __device__ __forceinline__ bool poll_ready(const unsigned* flag, unsigned limit)
   return true;
 }
 
+// The backward over packed sequences: sequence s's checkpoints (the state
+// entering each of its 16-token blocks) start at block cu[s] / 16 +
+// kPackedCkptSlack * s of its tile column, which leaves room for the whole
+// trips of blocks the checkpoint pass writes (up to 3 past the last).
+constexpr int kPackedCkptSlack = 5;
+
 // A compile-time int as a type (for unrolled steps written as lambdas).
 template <int I> struct IC { static constexpr int value = I; };
 

@@ -19,7 +19,7 @@ constexpr int kOrderBins = 1024;
 
 // order[0 .. nseq) = a permutation of the sequences 0 .. nseq-1, longest
 // (offsets clamped into [0, L] as the scan clamps them) first.
-__global__ __launch_bounds__(kOrderBins) void packed_order_kernel(const int64_t* __restrict__ cu, int nseq,
+static __global__ __launch_bounds__(kOrderBins) void packed_order_kernel(const int64_t* __restrict__ cu, int nseq,
                                                                   int64_t L, int* __restrict__ order) {
   __shared__ int bins[kOrderBins];
   __shared__ int longest;

@@ -819,7 +819,8 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     const int unit = blockIdx.x;
     int tile, c, st;
     bool split;
-    if (MODE == kModeCkpt || (MODE == kModeFull && unit < p.n_long)) {
+    constexpr bool PACKABLE = MODE == kModeFull || MODE == kModeCkpt;  // modes that run packed sequences
+    if ((MODE == kModeCkpt && p.cu == nullptr) || (MODE == kModeFull && unit < p.n_long)) {
       tile = unit;
       c = 0;
       st = 0;
@@ -827,7 +828,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     } else {
       const int per = MODE == kModeFull ? p.Ks : p.Ks - 1;
       const int jj = MODE == kModeFull ? unit - p.n_long : unit;
-      if (MODE == kModeFull && p.cu != nullptr) {  // packed: every tile column of a sequence together
+      if (PACKABLE && p.cu != nullptr) {  // packed: every tile column of a sequence together
         st = jj % p.n_split;
         c = p.order ? p.order[jj / p.n_split] : jj / p.n_split;
       } else {
@@ -839,7 +840,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     }
     int64_t tb = split ? static_cast<int64_t>(c) * p.chunk_len : 0;
     int64_t te = split ? ((tb + p.chunk_len < L) ? tb + p.chunk_len : L) : L;
-    const bool packed = MODE == kModeFull && split && p.cu != nullptr;
+    const bool packed = PACKABLE && split && p.cu != nullptr;
     if (packed) {  // sequence c of batch row 0, offsets clamped into [0, L]
       tb = p.cu[c];
       tb = tb < 0 ? 0 : (tb > L ? L : tb);
@@ -848,9 +849,10 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     }
     set_tile(tile, tb, te);
     if (packed) row_start = true;  // a packed sequence has no input before its first token
+    if (CKPT && packed) ckpt_row += static_cast<int64_t>(kPackedCkptSlack) * c * 64 * NPAD;
     const int64_t pair_row = (static_cast<int64_t>(st) * p.Ks + c) * 64 + lane;   // row of [n_split][Ks][64]
     if constexpr (MODE == kModeCkpt) {
-      init_state(b);
+      init_state(packed ? c : b);
       int nb = stretch_blocks();
       run_pass(IC<false>{}, 0, nb);
     } else if constexpr (MODE == kModeAgg) {

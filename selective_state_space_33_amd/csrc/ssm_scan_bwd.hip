@@ -19,6 +19,7 @@
 
 #include "bwd_kernels.hpp"
 #include "host_common.hpp"
+#include "order_kernel.hpp"
 #include "scan_launch.hpp"
 
 namespace ssm {
@@ -40,6 +41,7 @@ bool is_aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p
 // 8 and no shorter than 256 tokens, in whole trips of its loop.
 struct BwdPlan {
   int npl, G;
+  int64_t nseq;  // packed sequences of batch row 0 (0: none)
   int64_t Lp, ntd, T, ckpt_blocks;
   int n_long, n_split, Ks, chunk_blocks;
   // the checkpoint pass, chained alike: Kc chunks of ck_len tokens per left-over tile
@@ -47,14 +49,19 @@ struct BwdPlan {
   int64_t ck_len;
 };
 
-BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
+// Packed sequences (nseq > 0, batch 1): one unit per (tile column, sequence),
+// no chained plan; each sequence's checkpoints start kPackedCkptSlack blocks
+// further per sequence before it, so a tile column holds Lp / 16 +
+// kPackedCkptSlack * nseq of them.
+BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t nseq) {
   BwdPlan pl;
   pl.npl = N <= 16 ? 2 : 4;
   pl.G = 8;
+  pl.nseq = nseq > 0 ? nseq : 0;
   pl.Lp = cdiv(L, kTrip) * kTrip;  // whole trips of the checkpoint launch
   pl.ntd = cdiv(dim, 64);
-  pl.T = batch * pl.ntd;
-  pl.ckpt_blocks = pl.Lp / kBwdTB;
+  pl.T = (pl.nseq > 0 ? pl.nseq : batch) * pl.ntd;
+  pl.ckpt_blocks = pl.Lp / kBwdTB + kPackedCkptSlack * pl.nseq;
   pl.n_long = 0;
   pl.n_split = 0;
   pl.Ks = 1;
@@ -62,7 +69,7 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
   pl.Kc = 1;
   pl.ck_len = 0;
   const char* env = getenv("SSM_BWD_CHAINED");
-  const bool chained_ok = !(env && atoi(env) == 0);
+  const bool chained_ok = !(env && atoi(env) == 0) && pl.nseq == 0;
   const int64_t kBwdNumCU = device_cu_count();
   if (chained_ok && pl.T > kBwdNumCU && 2 * (pl.T - kBwdNumCU) <= kBwdNumCU) {
     const int64_t r = pl.T - kBwdNumCU;
@@ -85,16 +92,18 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N) {
 
 // Workspace: [header words (status, the two launches' tickets, ...), ready
 // flags of the backward, then of the checkpoint pass][packed B/C]
-// [checkpoints][dB, dC partials][dA, dD, dbias partials (Ks slots)][carried
-// adjoints][carried checkpoint-pass states].
+// [checkpoints][dB, dC partials][dA, dD, dbias partials (Ks slots of batch
+// rows, or one per packed sequence)][carried adjoints][carried
+// checkpoint-pass states][packed sequences' launch order].
 struct BwdLayout {
-  size_t words, bc, ckpt, bcpart, apart, dpart, carry, ckcarry, total;
+  size_t words, bc, ckpt, bcpart, apart, dpart, carry, ckcarry, order, total;
   int n_words, bwd_words;
 };
 
 BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t dim) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
   const int64_t slots = pl.n_split > 0 ? pl.Ks : 1;
+  const int64_t prow = pl.nseq > 0 ? pl.nseq : batch;  // partial rows per slot
   BwdLayout l;
   l.bwd_words = pl.n_split > 0 ? pl.n_split * pl.Ks : 0;
   l.n_words = kHeaderWords + l.bwd_words + (pl.n_split > 0 ? pl.n_split * pl.Kc : 0);
@@ -102,11 +111,12 @@ BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t dim) {
   l.bc = al256(static_cast<size_t>(batch * pl.Lp + kTBMax) * 2 * npad * sizeof(float));
   l.ckpt = al256(static_cast<size_t>(pl.T * pl.ckpt_blocks) * 64 * npad * sizeof(float));
   l.bcpart = al256(static_cast<size_t>(batch * pl.ntd * pl.Lp) * npad * sizeof(float));
-  l.apart = al256(static_cast<size_t>(slots * batch * dim) * npad * sizeof(float));
-  l.dpart = al256(static_cast<size_t>(slots * batch * dim) * sizeof(float));
+  l.apart = al256(static_cast<size_t>(slots * prow * dim) * npad * sizeof(float));
+  l.dpart = al256(static_cast<size_t>(slots * prow * dim) * sizeof(float));
   l.carry = al256(static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float));
   l.ckcarry = al256(static_cast<size_t>(pl.n_split) * pl.Kc * 64 * npad * sizeof(float));
-  l.total = l.words + l.bc + l.ckpt + 2 * l.bcpart + l.apart + 2 * l.dpart + l.carry + l.ckcarry;
+  l.order = al256(static_cast<size_t>(pl.nseq) * sizeof(int));
+  l.total = l.words + l.bc + l.ckpt + 2 * l.bcpart + l.apart + 2 * l.dpart + l.carry + l.ckcarry + l.order;
   return l;
 }
 
@@ -128,6 +138,12 @@ hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const
                        pl.G, bp.status, lay.n_words, static_cast<float*>(nullptr));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (pl.nseq > 0) {  // packed sequences, longest first (the units of a sequence run together)
+    hipLaunchKernelGGL(packed_order_kernel, dim3(1), dim3(kOrderBins), 0, s, sp.cu, static_cast<int>(pl.nseq), sp.L,
+                       const_cast<int*>(sp.order));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (pl.n_split > 0)
     e = launch_scan<IO, kModeChainedCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.n_long)), s);
   else
@@ -147,7 +163,7 @@ hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const
   if (e != hipSuccess) return e;
   const int64_t npar = sp.dim * sp.N;
   // the partial slots are further rows of the same sums
-  const int64_t rows = sp.batch * (pl.n_split > 0 ? pl.Ks : 1);
+  const int64_t rows = (pl.nseq > 0 ? pl.nseq : sp.batch) * (pl.n_split > 0 ? pl.Ks : 1);
   hipLaunchKernelGGL(bwd_reduce_param_kernel, dim3(static_cast<unsigned>(cdiv(npar, 256))), dim3(256), 0, s,
                      bp.dA_part, bp.dD_part, bp.dbias_part, dA, dD, dbias, rows, sp.dim, sp.N, npad);
   return hipGetLastError();
@@ -158,19 +174,21 @@ hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const
 
 using namespace ssm;
 
-extern "C" size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate,
+extern "C" size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int64_t nseq,
                                                ssm_dtype_t dt) {
   if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > kBwdMaxState || batch > kBwdMaxBatch) return 0;
   if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return 0;
+  if (nseq > 0 && batch != 1) return 0;
   const int64_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
   if (!rows_fit(L, dim, es)) return 0;
-  const BwdPlan pl = plan_bwd(batch, L, dim, dstate);
+  const BwdPlan pl = plan_bwd(batch, L, dim, dstate, nseq);
   return bwd_layout(pl, batch, dim).total;
 }
 
 extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                                      const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                                     const void* dy, const float* dfinal_state, const float* initial_state, void* du,
+                                     const void* dy, const float* dfinal_state, const float* initial_state,
+                                     const int64_t* cu_seqlens, int64_t nseq, void* du,
                                      void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
                                      float* ddelta_bias, float* dinitial_state, int64_t batch,
                                      int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt, void* workspace,
@@ -185,9 +203,10 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   const float* f32s[] = {A, D, delta_bias, dfinal_state, initial_state, dA, dD, ddelta_bias, dinitial_state};
   for (const float* q : f32s)
     if (q && !is_aligned(q, 4)) return SSM_ERR_INVALID_ARG;
+  if (cu_seqlens && (!is_aligned(cu_seqlens, 8) || batch != 1 || nseq <= 0)) return SSM_ERR_INVALID_ARG;
   if (dstate > kBwdMaxState || batch > kBwdMaxBatch) return SSM_ERR_UNSUPPORTED;
   if (!rows_fit(L, dim, static_cast<int64_t>(es))) return SSM_ERR_UNSUPPORTED;
-  const BwdPlan pl = plan_bwd(batch, L, dim, dstate);
+  const BwdPlan pl = plan_bwd(batch, L, dim, dstate, cu_seqlens ? nseq : 0);
   if (pl.T > 0x7fffffffLL || batch * (pl.Lp / kPackT) > 0x7fffffffLL || batch * L * dstate / 256 > 0x7fffffffLL)
     return SSM_ERR_UNSUPPORTED;
   const BwdLayout lay = bwd_layout(pl, batch, dim);
@@ -216,6 +235,7 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   char* tail = ws + lay.bc + lay.ckpt + 2 * lay.bcpart + lay.apart + 2 * lay.dpart;
   float* carry = lay.carry ? reinterpret_cast<float*>(tail) : nullptr;
   float* ckcarry = lay.ckcarry ? reinterpret_cast<float*>(tail + lay.carry) : nullptr;
+  int* order = lay.order ? reinterpret_cast<int*>(tail + lay.carry + lay.ckcarry) : nullptr;
   const unsigned spin = wait_spin_limit();
   const unsigned* never = wait_override(words);
 
@@ -238,6 +258,13 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   sp.ckpt = ckpt;
   sp.ckpt_blocks = pl.ckpt_blocks;
   sp.h0 = initial_state;
+  if (pl.nseq > 0) {  // the checkpoint pass over every (tile column, sequence)
+    sp.n_long = 0;
+    sp.n_split = static_cast<int>(pl.ntd);
+    sp.Ks = static_cast<int>(pl.nseq);
+    sp.cu = cu_seqlens;
+    sp.order = order;
+  }
   if (pl.n_split > 0) {  // the checkpoint pass chained like the forward
     sp.n_long = pl.n_long;
     sp.n_split = pl.n_split;
@@ -271,7 +298,9 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   bp.dbias_part = dbias_part;
   bp.dB_part = dB_part;
   bp.dC_part = dC_part;
-  bp.batch = batch;
+  bp.batch = pl.nseq > 0 ? pl.nseq : batch;  // partial rows of dA, dD, dbias
+  bp.cu = cu_seqlens;
+  bp.order = order;
   bp.L = L;
   bp.Lp = pl.Lp;
   bp.dim = dim;

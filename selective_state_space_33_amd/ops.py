@@ -77,9 +77,9 @@ def lib() -> ctypes.CDLL:
         L.ssm_ssd_fwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_ssd_fwd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int]
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
-        L.ssm_scan_bwd_workspace_size.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int]
+        L.ssm_scan_bwd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int]
         L.ssm_scan_bwd.restype = ctypes.c_int
-        L.ssm_scan_bwd.argtypes = ([_vp] * 8 + [ctypes.c_int] + [_vp] * 12 + [_i64] * 4 +
+        L.ssm_scan_bwd.argtypes = ([_vp] * 8 + [ctypes.c_int] + [_vp] * 4 + [_i64] + [_vp] * 9 + [_i64] * 4 +
                                    [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
         L.ssm_workspace_status.restype = ctypes.c_int
         L.ssm_workspace_status.argtypes = [_vp, ctypes.c_size_t, _vp]
@@ -336,45 +336,54 @@ def ssm_scan_fwd_ex_workspace_size(batch: int, L: int, dim: int, dstate: int, ns
     return int(lib().ssm_scan_fwd_ex_workspace_size(batch, L, dim, dstate, nseq, _dtype_code(dtype)))
 
 
-def ssm_scan_bwd_workspace_size(batch: int, L: int, dim: int, dstate: int, dtype: torch.dtype) -> int:
-    return int(lib().ssm_scan_bwd_workspace_size(batch, L, dim, dstate, _dtype_code(dtype)))
+def ssm_scan_bwd_workspace_size(batch: int, L: int, dim: int, dstate: int, dtype: torch.dtype, nseq: int = 0) -> int:
+    return int(lib().ssm_scan_bwd_workspace_size(batch, L, dim, dstate, nseq, _dtype_code(dtype)))
 
 
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus: bool = True,
-                 dfinal_state=None, initial_state=None, want_dinitial_state: bool = False, workspace=None,
-                 stream=None, check_status: bool = False):
-    """Backward of ssm_scan_fwd on the GPU: gradients of sum(y*dy) + sum(final_state*dfinal_state).
+                 dfinal_state=None, initial_state=None, want_dinitial_state: bool = False, cu_seqlens=None,
+                 workspace=None, stream=None, check_status: bool = False):
+    """Backward of ssm_scan_fwd (or ssm_scan_fwd_ex) on the GPU: gradients of sum(y*dy) +
+    sum(final_state*dfinal_state).
 
     Same inputs as ssm_scan_fwd plus dy [batch, L, dim] (storage dtype) and dfinal_state
-    [batch, dim, dstate] (float32, optional).  Returns a dict with du, ddelta, dB, dC (storage
+    [rows, dim, dstate] (float32, optional); cu_seqlens: int64 device offsets of packed sequences of batch
+    row 0 (rows = nseq; otherwise rows = batch).  Returns a dict with du, ddelta, dB, dC (storage
     dtype), dA (float32), and dD, dz, ddelta_bias for the optional inputs given (None otherwise);
-    dinitial_state [batch, dim, dstate] when an initial state is given or want_dinitial_state.
+    dinitial_state [rows, dim, dstate] when an initial state is given or want_dinitial_state.
     """
     batch, L, dim = u.shape
     dstate = A.shape[1]
     dev, dt = u.device, u.dtype
     code = _dtype_code(dt)
+    nseq, rows = 0, batch
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int64 or cu_seqlens.device != dev or cu_seqlens.dim() != 1:
+            raise TypeError("cu_seqlens must be a 1-d int64 tensor on the device of u")
+        nseq = rows = cu_seqlens.numel() - 1
+        _check(cu_seqlens, "cu_seqlens", torch.int64, (nseq + 1,), dev)
     for name, t, shp in (("u", u, (batch, L, dim)), ("delta", delta, (batch, L, dim)), ("z", z, (batch, L, dim)),
                          ("dy", dy, (batch, L, dim)), ("B", B, (batch, L, dstate)), ("C", C, (batch, L, dstate))):
         _check(t, name, dt, shp, dev)
     _check(A, "A", torch.float32, (dim, dstate), dev)
     _check(D, "D", torch.float32, (dim,), dev)
     _check(delta_bias, "delta_bias", torch.float32, (dim,), dev)
-    _check(dfinal_state, "dfinal_state", torch.float32, (batch, dim, dstate), dev)
-    _check(initial_state, "initial_state", torch.float32, (batch, dim, dstate), dev)
+    _check(dfinal_state, "dfinal_state", torch.float32, (rows, dim, dstate), dev)
+    _check(initial_state, "initial_state", torch.float32, (rows, dim, dstate), dev)
     s = _resolve(dev, stream)
     with torch.cuda.stream(s):
         g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(delta), dB=torch.empty_like(B),
                  dC=torch.empty_like(C), dA=torch.empty_like(A),
                  dD=None if D is None else torch.empty_like(D), dz=None if z is None else torch.empty_like(z),
                  ddelta_bias=None if delta_bias is None else torch.empty_like(delta_bias),
-                 dinitial_state=(torch.empty((batch, dim, dstate), dtype=torch.float32, device=dev)
+                 dinitial_state=(torch.empty((rows, dim, dstate), dtype=torch.float32, device=dev)
                                  if (initial_state is not None or want_dinitial_state) else None))
-        need = ssm_scan_bwd_workspace_size(batch, L, dim, dstate, dt)
+        need = ssm_scan_bwd_workspace_size(batch, L, dim, dstate, dt, nseq)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     rc = lib().ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                            1 if softplus else 0, _ptr(dy), _ptr(dfinal_state), _ptr(initial_state), _ptr(g["du"]),
+                            1 if softplus else 0, _ptr(dy), _ptr(dfinal_state), _ptr(initial_state),
+                            _ptr(cu_seqlens), nseq, _ptr(g["du"]),
                             _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
                             _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dinitial_state"]), batch, L, dim, dstate,
                             code, _ptr(workspace), _ws_bytes(workspace), s.cuda_stream)

@@ -181,23 +181,28 @@ def test_scan_ex_workspace_size():
 def test_bwd_workspace_size():
     L = ops.lib()
     # at least the state entering every 16-token block of every 64-channel tile
-    ws = L.ssm_scan_bwd_workspace_size(2, 1000, 136, 16, BF16)
+    ws = L.ssm_scan_bwd_workspace_size(2, 1000, 136, 16, 0, BF16)
     assert ws >= 2 * 3 * (1024 // 16) * 64 * 16 * 4 and ws % 256 == 0
-    assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 32, F32) > ws
-    assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 33, F32) == 0   # backward: dstate <= 32
-    assert L.ssm_scan_bwd_workspace_size(0, 10, 10, 16, F32) == 0
-    assert L.ssm_scan_bwd_workspace_size(1, 10, 10, 16, 7) == 0
-    assert L.ssm_scan_bwd_workspace_size(1, 1 << 24, 1024, 16, F32) == 0  # rows past 2^31 bytes
+    assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 32, 0, F32) > ws
+    assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 33, 0, F32) == 0   # backward: dstate <= 32
+    assert L.ssm_scan_bwd_workspace_size(0, 10, 10, 16, 0, F32) == 0
+    assert L.ssm_scan_bwd_workspace_size(1, 10, 10, 16, 0, 7) == 0
+    assert L.ssm_scan_bwd_workspace_size(1, 1 << 24, 1024, 16, 0, F32) == 0  # rows past 2^31 bytes
+    # packed sequences: batch 1 only; partial rows per sequence and a few more checkpoints per sequence
+    assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 16, 3, F32) == 0
+    assert L.ssm_scan_bwd_workspace_size(1, 1000, 136, 16, 7, F32) > L.ssm_scan_bwd_workspace_size(1, 1000, 136, 16,
+                                                                                                   0, F32)
 
 
 def _bwd(lib_, **kw):
     """Call ssm_scan_bwd with fake (never dereferenced) pointers; only rejection paths are used."""
     a = dict(u=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, z=None, bias=None, sp=1, dy=0x6000,
-             dfs=None, h0=None, du=0x7000, dd=0x8000, dA=0x9000, dB=0xa000, dC=0xb000, dD=None, dz=None, dbias=None,
-             dh0=None, batch=1, L=8, dim=8, N=16, dt=F32, ws=None, wsb=0, stream=None)
+             dfs=None, h0=None, cu=None, nseq=0, du=0x7000, dd=0x8000, dA=0x9000, dB=0xa000, dC=0xb000, dD=None,
+             dz=None, dbias=None, dh0=None, batch=1, L=8, dim=8, N=16, dt=F32, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib_.ssm_scan_bwd(a["u"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["z"], a["bias"], a["sp"], a["dy"],
-                             a["dfs"], a["h0"], a["du"], a["dd"], a["dA"], a["dB"], a["dC"], a["dD"], a["dz"],
+                             a["dfs"], a["h0"], a["cu"], a["nseq"], a["du"], a["dd"], a["dA"], a["dB"], a["dC"],
+                             a["dD"], a["dz"],
                              a["dbias"], a["dh0"], a["batch"], a["L"], a["dim"], a["N"], a["dt"], a["ws"], a["wsb"],
                              a["stream"])
 
@@ -212,6 +217,9 @@ def _bwd(lib_, **kw):
     (dict(L=1 << 24, dim=1024), UNSUPPORTED),
     (dict(), INVALID),                                  # no workspace
     (dict(ws=0x100000, wsb=256), INVALID),              # too small
+    (dict(cu=0x8000, nseq=2, batch=2), INVALID),        # packed sequences need batch 1
+    (dict(cu=0x8004, nseq=2), INVALID),                 # offsets 8-byte aligned
+    (dict(cu=0x8000, nseq=0), INVALID),
 ])
 def test_bwd_rejects_bad_arguments_without_launching(kw, expect):
     assert _bwd(ops.lib(), **kw) == expect

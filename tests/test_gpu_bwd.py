@@ -211,3 +211,72 @@ def test_bwd_db_dc_full_length_chained(monkeypatch):
     x, dy, dfs = _case(rng, 1, 4096, 320, 16, "bf16")
     x["A"] = np.tile(-np.arange(1, 17, dtype=np.float64), (320, 1))   # the benchmark's A[d, n] = -(n + 1)
     _run_and_compare(x, dy, dfs, "bf16", label="1 x 4096 x 320 chained for 4 CUs")
+
+
+def _packed_case(rng, L, dim, N, dtype, cuts):
+    x = I.random_scan_inputs(rng, 1, L, dim, N, dtype=dtype)
+    nseq = len(cuts) - 1
+    dy = _round(rng.standard_normal((1, L, dim)), dtype)
+    dfs = np.asarray(rng.standard_normal((nseq, dim, N)), np.float32).astype(np.float64)
+    h0 = np.asarray(rng.standard_normal((nseq, dim, N)) * 0.5, np.float32).astype(np.float64)
+    return x, dy, dfs, h0, np.asarray(cuts, dtype=np.int64)
+
+
+def _run_packed(x, dy, dfs, h0, cu, dtype, label):
+    say(f"bwd packed {label} L={x['u'].shape[1]} dim={x['u'].shape[2]} nseq={len(cu) - 1} {dtype}")
+    g = ops.ssm_scan_bwd(to_dev(x["u"], dtype), to_dev(x["delta"], dtype), to_dev_f32(x["A"]), to_dev(x["B"], dtype),
+                         to_dev(x["C"], dtype), to_dev(dy, dtype), D=to_dev_f32(x["D"]), z=to_dev(x["z"], dtype),
+                         delta_bias=to_dev_f32(x["delta_bias"]), dfinal_state=to_dev_f32(dfs),
+                         initial_state=to_dev_f32(h0), cu_seqlens=torch.tensor(cu, device="cuda:0"),
+                         check_status=True)
+    torch.cuda.synchronize()
+    o = OB.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                    dfinal_state=dfs, initial_state=h0, cu_seqlens=cu)
+    errs = {k: rel_err(g[k].float().cpu().numpy().astype(np.float64), o[k]) for k in SEQ_OUT + F32_OUT}
+    print(f"[parity] bwd packed {label}: " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k, e in errs.items():
+        tol = TOL[dtype] if k in SEQ_OUT else TOL["f32"]
+        assert e <= tol, (k, e, tol)
+    return g
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 32])
+def test_bwd_packed_sequences(N, dtype):
+    """Packed sequences of one row (an empty one, a one-token one, lengths not multiples of the 16-token block),
+    each from its own initial state with its own final-state gradient; every gradient and d initial_state per
+    sequence against the oracle over packed sequences (pinned by central differences)."""
+    cuts = [0, 37, 37, 38, 150, 151, 300]
+    rng = np.random.default_rng(860 + N + (1 if dtype == "bf16" else 0))
+    x, dy, dfs, h0, cu = _packed_case(rng, 300, 136, N, dtype, cuts)
+    _run_packed(x, dy, dfs, h0, cu, dtype, f"N{N}")
+
+
+def test_bwd_packed_many_sequences_and_deterministic():
+    """40 sequences x 3 tile columns (120 units, longest first): every gradient; two runs bitwise equal."""
+    rng = np.random.default_rng(870)
+    lens = rng.integers(1, 60, size=40)
+    cuts = np.concatenate([[0], np.cumsum(lens)]).tolist()
+    x, dy, dfs, h0, cu = _packed_case(rng, cuts[-1], 136, 16, "f32", cuts)
+    g1 = _run_packed(x, dy, dfs, h0, cu, "f32", "40 sequences")
+    g2 = _run_packed(x, dy, dfs, h0, cu, "f32", "40 sequences again")
+    for k in g1:
+        if g1[k] is not None:
+            assert torch.equal(g1[k], g2[k]), k
+
+
+def test_bwd_packed_one_sequence_equals_unpacked():
+    """One packed sequence over the whole row is the plain backward from that initial state (bitwise)."""
+    rng = np.random.default_rng(880)
+    x, dy, dfs, h0, cu = _packed_case(rng, 200, 72, 16, "f32", [0, 200])
+    args = (to_dev(x["u"], "f32"), to_dev(x["delta"], "f32"), to_dev_f32(x["A"]), to_dev(x["B"], "f32"),
+            to_dev(x["C"], "f32"), to_dev(dy, "f32"))
+    kw = dict(D=to_dev_f32(x["D"]), z=to_dev(x["z"], "f32"), delta_bias=to_dev_f32(x["delta_bias"]),
+              dfinal_state=to_dev_f32(dfs), initial_state=to_dev_f32(h0))
+    say("bwd one packed sequence vs unpacked")
+    g1 = ops.ssm_scan_bwd(*args, cu_seqlens=torch.tensor(cu, device="cuda:0"), **kw)
+    g2 = ops.ssm_scan_bwd(*args, **kw)
+    torch.cuda.synchronize()
+    for k in g1:
+        if g1[k] is not None:
+            assert torch.equal(g1[k], g2[k]), k

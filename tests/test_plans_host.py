@@ -88,9 +88,9 @@ def test_bwd_plan_follows_the_cu_count(monkeypatch):
     lib = ops.lib()
     monkeypatch.setenv("SSM_NUM_CU", "256")
     # 320 tiles: 64 left over; the backward's 4 chunks of blocks, the checkpoint pass's 4 chunks of 1024 tokens
-    assert lib.ssm_scan_bwd_workspace_size(4, 4096, 5120, 16, BF16) == bwd_expected(4, 4096, 5120, r=64, Ks=4, Kc=4)
+    assert lib.ssm_scan_bwd_workspace_size(4, 4096, 5120, 16, 0, BF16) == bwd_expected(4, 4096, 5120, r=64, Ks=4, Kc=4)
     monkeypatch.setenv("SSM_NUM_CU", "320")
-    assert lib.ssm_scan_bwd_workspace_size(4, 4096, 5120, 16, BF16) == bwd_expected(4, 4096, 5120)
+    assert lib.ssm_scan_bwd_workspace_size(4, 4096, 5120, 16, 0, BF16) == bwd_expected(4, 4096, 5120)
 
 
 def test_bwd_checkpoint_chunks_are_clamped(monkeypatch):
@@ -98,9 +98,9 @@ def test_bwd_checkpoint_chunks_are_clamped(monkeypatch):
     pass into no more than 8 chunks of at least 256 tokens -- one chunk for 150 tokens, 8 for 4096 (not 256)."""
     monkeypatch.setenv("SSM_NUM_CU", "256")
     lib = ops.lib()
-    assert lib.ssm_scan_bwd_workspace_size(1, 150, 64 * 257, 16, BF16) == bwd_expected(1, 150, 64 * 257, r=1, Ks=8,
+    assert lib.ssm_scan_bwd_workspace_size(1, 150, 64 * 257, 16, 0, BF16) == bwd_expected(1, 150, 64 * 257, r=1, Ks=8,
                                                                                          Kc=1)
-    assert lib.ssm_scan_bwd_workspace_size(1, 4096, 64 * 257, 16, BF16) == bwd_expected(1, 4096, 64 * 257, r=1,
+    assert lib.ssm_scan_bwd_workspace_size(1, 4096, 64 * 257, 16, 0, BF16) == bwd_expected(1, 4096, 64 * 257, r=1,
                                                                                           Ks=8, Kc=8)
 
 
