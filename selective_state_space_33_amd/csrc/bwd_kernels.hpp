@@ -97,6 +97,17 @@ struct BwdParams {
   // and the sequence's checkpoints start at block cu[s] / 16 + kPackedCkptSlack * s.
   const int64_t* cu;
   const int* order;
+  // States beyond one launch's NPL * G (wide states, up to 2 * NPL * G): the
+  // kernel runs twice, on states n_base .. n_base + NPL*G - 1 of a layout of
+  // g_total state groups (records, checkpoints and the dA, dB, dC partials are
+  // laid out for all of them).  The first launch leaves its readout partial v
+  // and its partial sums of t_a A and dh B per (row, token, channel) in
+  // part_v, part_s1, part_s2 ([batch][L][dim] fp32); the second adds them to
+  // its own and writes du, ddelta_raw and dz.  n_base 0, g_total G otherwise.
+  int n_base, g_total;
+  float* part_v;
+  float* part_s1;
+  float* part_s2;
   float* carry;
   unsigned* flags;
   unsigned* ticket;
@@ -131,7 +142,9 @@ __device__ __forceinline__ void quad_sums4_to_last(float& a, float& b, float& c,
 #undef SSM_ROW_STEP
 }
 
-template <class IO, int NPL, int G>
+// WIDE: 0 for all states in one launch; 1 for the first half of wide states
+// (partials out), 2 for the second (partials in, finished gradients out).
+template <class IO, int NPL, int G, int WIDE = 0>
 __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   constexpr int TB = kBwdTB;
   constexpr int NPAD = NPL * G;
@@ -165,6 +178,8 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = w * NPL;
+  const int nb = p.n_base;                 // first state of this launch
+  const int npg = NPL * p.g_total;         // states of the global layouts (records, checkpoints, partials)
   const int64_t dim = p.dim, L = p.L, N = p.N;
   const bool has_z = p.z != nullptr;
   const bool sp_on = p.softplus != 0;
@@ -195,7 +210,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     dvalid = d < dim;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      const int n = n0 + j;
+      const int n = nb + n0 + j;
       An[j] = (dvalid && n < N) ? p.A[d * N + n] : 0.0f;
       A2[j] = An[j] * kLog2e;
     }
@@ -217,9 +232,9 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     rs_du = rs_of(p.du);
     rs_dd = rs_of(p.ddelta);
     rs_dz = rs_of(p.dz);
-    const float* bc_row = p.bc + ((b * G + w) * p.Lp + t_begin) * (2 * NPL);
+    const float* bc_row = p.bc + ((b * p.g_total + nb / NPL + w) * p.Lp + t_begin) * (2 * NPL);
     rs_bc = make_rsrc(bc_row, (p.Lp + 32 - t_begin) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
-    ckpt_row = p.ckpt + ((static_cast<int64_t>(t) * p.ckpt_blocks + ckpt_slot0) * 64 + lane) * NPAD + n0;
+    ckpt_row = p.ckpt + ((static_cast<int64_t>(t) * p.ckpt_blocks + ckpt_slot0) * 64 + lane) * npg + nb + n0;
   };
 
   // ---- running sums of the stretch being worked on: the adjoint entering the
@@ -229,7 +244,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   auto start_from_final = [&]() {  // the gradient reaching the tile's final state
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      const int n = n0 + j;
+      const int n = nb + n0 + j;
       dhn[j] = (dvalid && n < N && p.dfs) ? p.dfs[(srow * dim + d) * N + n] : 0.0f;
       dAacc[j] = 0.0f;
     }
@@ -249,7 +264,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       qrv[S][v] = __uint_as_float(
           __builtin_amdgcn_raw_buffer_load_b32(rs_bc, rec_voff + t0 * (2 * NPL * 4) + v * 64, 0, 0));
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) qhs[S][j] = dvalid ? ckpt_row[static_cast<int64_t>(k) * 64 * NPAD + j] : 0.0f;
+    for (int j = 0; j < NPL; ++j) qhs[S][j] = dvalid ? ckpt_row[static_cast<int64_t>(k) * 64 * npg + j] : 0.0f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int off = (t0 + w + i * G) * row_bytes + lane * ES;
@@ -339,6 +354,12 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       float v = SEP ? sYP[0][row][lane] : sYS[0][row][lane].x;
 #pragma unroll
       for (int ww = 1; ww < G; ++ww) v += SEP ? sYP[ww][row][lane] : sYS[ww][row][lane].x;
+      const int64_t pidx = ((b * L + t_begin + t0 + row) * dim + d);  // (row, token, channel) of the partials
+      if constexpr (WIDE == 1) {
+        if (elive[i]) p.part_v[pidx] = v;  // the other half finishes v
+        continue;
+      }
+      if constexpr (WIDE == 2) v += elive[i] ? p.part_v[pidx] : 0.0f;
       v = __builtin_fmaf(Dd, eu[i], v);
       if (has_z) {
         const float dzv = egz[i] * v;
@@ -404,6 +425,20 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
         S1 += sYS[ww][row][lane].x;
         S2 += sYS[ww][row][lane].y;
       }
+      const int64_t pidx = ((b * L + t_begin + t0 + row) * dim + d);
+      if constexpr (WIDE == 1) {
+        if (elive[i]) {
+          p.part_s1[pidx] = S1;
+          p.part_s2[pidx] = S2;
+        }
+        continue;
+      }
+      if constexpr (WIDE == 2) {
+        if (elive[i]) {
+          S1 += p.part_s1[pidx];
+          S2 += p.part_s2[pidx];
+        }
+      }
       const float dDelta = __builtin_fmaf(eu[i], S2, S1);
       const float duv = __builtin_fmaf(edl[i], S2, Dd * edv[i]);
       const float ddr = dDelta * esx[i];
@@ -424,7 +459,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
         sb += sRB[t][n][r];
         sc += sRC[t][n][r];
       }
-      const int64_t o = ((b * p.ntd + tile % p.ntd) * p.Lp + t_begin + t0 + t) * NPAD + n;
+      const int64_t o = ((b * p.ntd + tile % p.ntd) * p.Lp + t_begin + t0 + t) * npg + nb + n;
       p.dB_part[o] = sb;
       p.dC_part[o] = sc;
     }
@@ -466,7 +501,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
         if (s != slot && !zero_others) continue;
         const int64_t row = static_cast<int64_t>(s) * p.batch + srow;
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) p.dA_part[(row * dim + d) * NPAD + n0 + j] = s == slot ? dAacc[j] : 0.0f;
+        for (int j = 0; j < NPL; ++j) p.dA_part[(row * dim + d) * npg + nb + n0 + j] = s == slot ? dAacc[j] : 0.0f;
       }
     }
     sAcc[0][w][lane] = accD;
@@ -493,7 +528,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     if (dvalid && p.dh0) {
 #pragma unroll
       for (int j = 0; j < NPL; ++j)
-        if (n0 + j < N) p.dh0[(srow * dim + d) * N + n0 + j] = dhn[j];
+        if (nb + n0 + j < N) p.dh0[(srow * dim + d) * N + nb + n0 + j] = dhn[j];
     }
   };
 

@@ -26,7 +26,8 @@ namespace ssm {
 namespace {
 
 constexpr int64_t kBwdMaxBatch = 65535;
-constexpr int64_t kBwdMaxState = 32;
+constexpr int64_t kBwdMaxState = 64;
+constexpr int64_t kBwdOneLaunchState = 32;  // states one backward launch covers (4 per lane, 8 wavefronts)
 constexpr int64_t kBwdMaxChained = 8;  // chunks per left-over tile (the hand-offs run in series)
 constexpr int64_t kBwdMinChunk = 256;   // tokens: the checkpoint pass never cuts the sequence finer
 
@@ -34,13 +35,18 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t al256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 bool is_aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Variant: 2 states per lane over 8 wavefronts up to 16 states, 4 per lane up to 32.
+// Variant: 2 states per lane over 8 wavefronts up to 16 states, 4 per lane up to 32;
+// above 32 (wide states, up to 64) two launches of the 4-per-lane kernel, one
+// per half of the states, over records and checkpoints laid out for 16 groups
+// of 4 (the checkpoint pass runs the forward's 16-wavefront variant).
 // Chained plan (CUs < T <= 1.5 CUs): n_long = CUs whole tiles, the r = T - CUs
 // others in Ks = CUs / r chunks of blocks (at most 8); the checkpoint pass is
 // chained the same way, as the forward plans it: Kc = CUs / r chunks, at most
 // 8 and no shorter than 256 tokens, in whole trips of its loop.
 struct BwdPlan {
   int npl, G;
+  int g_total;   // state groups of the records and checkpoints (G, or 2G for wide states)
+  bool wide;
   int64_t nseq;  // packed sequences of batch row 0 (0: none)
   int64_t Lp, ntd, T, ckpt_blocks;
   int n_long, n_split, Ks, chunk_blocks;
@@ -57,6 +63,8 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t nseq)
   BwdPlan pl;
   pl.npl = N <= 16 ? 2 : 4;
   pl.G = 8;
+  pl.wide = N > kBwdOneLaunchState;
+  pl.g_total = pl.wide ? 2 * pl.G : pl.G;
   pl.nseq = nseq > 0 ? nseq : 0;
   pl.Lp = cdiv(L, kTrip) * kTrip;  // whole trips of the checkpoint launch
   pl.ntd = cdiv(dim, 64);
@@ -69,7 +77,7 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t nseq)
   pl.Kc = 1;
   pl.ck_len = 0;
   const char* env = getenv("SSM_BWD_CHAINED");
-  const bool chained_ok = !(env && atoi(env) == 0) && pl.nseq == 0;
+  const bool chained_ok = !(env && atoi(env) == 0) && pl.nseq == 0 && !pl.wide;
   const int64_t kBwdNumCU = device_cu_count();
   if (chained_ok && pl.T > kBwdNumCU && 2 * (pl.T - kBwdNumCU) <= kBwdNumCU) {
     const int64_t r = pl.T - kBwdNumCU;
@@ -96,12 +104,12 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t nseq)
 // rows, or one per packed sequence)][carried adjoints][carried
 // checkpoint-pass states][packed sequences' launch order].
 struct BwdLayout {
-  size_t words, bc, ckpt, bcpart, apart, dpart, carry, ckcarry, order, total;
+  size_t words, bc, ckpt, bcpart, apart, dpart, carry, ckcarry, order, part, total;
   int n_words, bwd_words;
 };
 
-BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t dim) {
-  const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
+BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t L, int64_t dim) {
+  const int64_t npad = static_cast<int64_t>(pl.npl) * pl.g_total;
   const int64_t slots = pl.n_split > 0 ? pl.Ks : 1;
   const int64_t prow = pl.nseq > 0 ? pl.nseq : batch;  // partial rows per slot
   BwdLayout l;
@@ -116,7 +124,10 @@ BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t dim) {
   l.carry = al256(static_cast<size_t>(pl.n_split) * pl.Ks * 64 * npad * sizeof(float));
   l.ckcarry = al256(static_cast<size_t>(pl.n_split) * pl.Kc * 64 * npad * sizeof(float));
   l.order = al256(static_cast<size_t>(pl.nseq) * sizeof(int));
-  l.total = l.words + l.bc + l.ckpt + 2 * l.bcpart + l.apart + 2 * l.dpart + l.carry + l.ckcarry + l.order;
+  // wide states: the first half's v, sum t_a A and sum dh B per (row, token, channel)
+  l.part = pl.wide ? al256(static_cast<size_t>(batch * L * dim) * sizeof(float)) : 0;
+  l.total = l.words + l.bc + l.ckpt + 2 * l.bcpart + l.apart + 2 * l.dpart + l.carry + l.ckcarry + l.order +
+            3 * l.part;
   return l;
 }
 
@@ -127,7 +138,7 @@ bool rows_fit(int64_t L, int64_t dim, int64_t es) { return L * dim * es < 0x7fff
 template <class IO>
 hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const void* C, float* bc, ScanParams sp,
                    BwdParams bp, void* dB, void* dC, float* dA, float* dD, float* dbias, int vw, hipStream_t s) {
-  const int64_t npad = static_cast<int64_t>(pl.npl) * pl.G;
+  const int64_t npad = static_cast<int64_t>(pl.npl) * pl.g_total;
   const dim3 pgrid(static_cast<unsigned>(sp.batch * (pl.Lp / kPackT)));
   // the pack also zeroes the header words and the chained launches' flags
   if (pl.npl == 2)
@@ -135,7 +146,7 @@ hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const
                        pl.G, bp.status, lay.n_words, static_cast<float*>(nullptr));
   else
     hipLaunchKernelGGL((pack_bc_kernel<IO, 4>), pgrid, dim3(256), 0, s, B, C, bc, sp.batch, sp.L, pl.Lp, sp.N,
-                       pl.G, bp.status, lay.n_words, static_cast<float*>(nullptr));
+                       pl.g_total, bp.status, lay.n_words, static_cast<float*>(nullptr));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (pl.nseq > 0) {  // packed sequences, longest first (the units of a sequence run together)
@@ -146,14 +157,22 @@ hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const
   }
   if (pl.n_split > 0)
     e = launch_scan<IO, kModeChainedCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.n_long)), s);
+  else if (pl.wide)  // the forward's 4-per-lane, 16-wavefront variant covers all 64 states
+    e = launch_scan<IO, kModeCkpt>(pl.npl, pl.g_total, 1, kBwdTB, sp, dim3(static_cast<unsigned>(pl.T)), s);
   else
     e = launch_scan<IO, kModeCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.T)), s);
   if (e != hipSuccess) return e;
   const dim3 bgrid(static_cast<unsigned>(pl.n_split > 0 ? pl.n_long : pl.T));
-  if (pl.npl == 2)
+  if (pl.wide) {  // one launch per half of the states; the second finishes the per-(token, channel) gradients
+    bp.n_base = 0;
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8, 1>), bgrid, dim3(512), 0, s, bp);
+    bp.n_base = static_cast<int>(kBwdOneLaunchState);
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8, 2>), bgrid, dim3(512), 0, s, bp);
+  } else if (pl.npl == 2) {
     hipLaunchKernelGGL((scan_bwd_kernel<IO, 2, 8>), bgrid, dim3(512), 0, s, bp);
-  else
+  } else {
     hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8>), bgrid, dim3(512), 0, s, bp);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t nbc = sp.batch * sp.L * sp.N;
@@ -182,7 +201,7 @@ extern "C" size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t 
   const int64_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
   if (!rows_fit(L, dim, es)) return 0;
   const BwdPlan pl = plan_bwd(batch, L, dim, dstate, nseq);
-  return bwd_layout(pl, batch, dim).total;
+  return bwd_layout(pl, batch, L, dim).total;
 }
 
 extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
@@ -209,7 +228,7 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   const BwdPlan pl = plan_bwd(batch, L, dim, dstate, cu_seqlens ? nseq : 0);
   if (pl.T > 0x7fffffffLL || batch * (pl.Lp / kPackT) > 0x7fffffffLL || batch * L * dstate / 256 > 0x7fffffffLL)
     return SSM_ERR_UNSUPPORTED;
-  const BwdLayout lay = bwd_layout(pl, batch, dim);
+  const BwdLayout lay = bwd_layout(pl, batch, L, dim);
   if (!workspace || workspace_bytes < lay.total || !is_aligned(workspace, 256)) return SSM_ERR_INVALID_ARG;
 
   // The checkpoint launch's prologue width: dim % vw == 0 and rows aligned to vw elements.
@@ -236,6 +255,7 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   float* carry = lay.carry ? reinterpret_cast<float*>(tail) : nullptr;
   float* ckcarry = lay.ckcarry ? reinterpret_cast<float*>(tail + lay.carry) : nullptr;
   int* order = lay.order ? reinterpret_cast<int*>(tail + lay.carry + lay.ckcarry) : nullptr;
+  float* part = lay.part ? reinterpret_cast<float*>(tail + lay.carry + lay.ckcarry + lay.order) : nullptr;
   const unsigned spin = wait_spin_limit();
   const unsigned* never = wait_override(words);
 
@@ -299,6 +319,14 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   bp.dB_part = dB_part;
   bp.dC_part = dC_part;
   bp.batch = pl.nseq > 0 ? pl.nseq : batch;  // partial rows of dA, dD, dbias
+  bp.n_base = 0;
+  bp.g_total = pl.g_total;
+  if (part) {
+    const size_t pn = lay.part / sizeof(float);
+    bp.part_v = part;
+    bp.part_s1 = part + pn;
+    bp.part_s2 = part + 2 * pn;
+  }
   bp.cu = cu_seqlens;
   bp.order = order;
   bp.L = L;

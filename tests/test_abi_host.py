@@ -184,7 +184,8 @@ def test_bwd_workspace_size():
     ws = L.ssm_scan_bwd_workspace_size(2, 1000, 136, 16, 0, BF16)
     assert ws >= 2 * 3 * (1024 // 16) * 64 * 16 * 4 and ws % 256 == 0
     assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 32, 0, F32) > ws
-    assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 33, 0, F32) == 0   # backward: dstate <= 32
+    assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 33, 0, F32) > 0    # wide states: two halves
+    assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 65, 0, F32) == 0   # backward: dstate <= 64
     assert L.ssm_scan_bwd_workspace_size(0, 10, 10, 16, 0, F32) == 0
     assert L.ssm_scan_bwd_workspace_size(1, 10, 10, 16, 0, 7) == 0
     assert L.ssm_scan_bwd_workspace_size(1, 1 << 24, 1024, 16, 0, F32) == 0  # rows past 2^31 bytes
@@ -213,7 +214,7 @@ def _bwd(lib_, **kw):
     (dict(batch=0), INVALID), (dict(L=0), INVALID), (dict(N=0), INVALID), (dict(dt=3), INVALID),
     (dict(dy=0x6001), INVALID), (dict(dt=BF16, dB=0xa001), INVALID), (dict(dfs=0xc002), INVALID),
     (dict(h0=0xc002), INVALID), (dict(dh0=0xd001), INVALID),
-    (dict(N=33), UNSUPPORTED), (dict(batch=70000), UNSUPPORTED),
+    (dict(N=65), UNSUPPORTED), (dict(batch=70000), UNSUPPORTED),
     (dict(L=1 << 24, dim=1024), UNSUPPORTED),
     (dict(), INVALID),                                  # no workspace
     (dict(ws=0x100000, wsb=256), INVALID),              # too small

@@ -69,7 +69,7 @@ def _run_and_compare(x, dy, dfs, dtype, softplus=True, label="", h0=None):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [16, 32, 4, 1])
+@pytest.mark.parametrize("N", [16, 32, 4, 1, 33, 48, 64])
 def test_bwd_matches_oracle(N, dtype):
     rng = np.random.default_rng(100 + N + (7 if dtype == "bf16" else 0))
     x, dy, dfs = _case(rng, 2, 150, 64 * 2 + 8, N, dtype)
@@ -94,7 +94,7 @@ def test_bwd_optional_inputs(opts):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [16, 32])
+@pytest.mark.parametrize("N", [16, 32, 64])
 def test_bwd_with_initial_state(N, dtype):
     """From an initial state h0: every gradient, and d h0 (the adjoint reaching h_{-1})."""
     rng = np.random.default_rng(450 + N + (5 if dtype == "bf16" else 0))
@@ -241,7 +241,7 @@ def _run_packed(x, dy, dfs, h0, cu, dtype, label):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [16, 32])
+@pytest.mark.parametrize("N", [16, 32, 64])
 def test_bwd_packed_sequences(N, dtype):
     """Packed sequences of one row (an empty one, a one-token one, lengths not multiples of the 16-token block),
     each from its own initial state with its own final-state gradient; every gradient and d initial_state per
