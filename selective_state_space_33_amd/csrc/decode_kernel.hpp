@@ -114,6 +114,23 @@ template <> struct Vec4In<BF16> {
   }
 };
 
+// Sum of v over each aligned group of NQ lanes, left in every lane of the
+// group: DPP quad permutations (lane i ^ 1, then i ^ 2) and, for eight lanes,
+// the half-row mirror (lane i with 7 - i, which after the quad sums holds the
+// other quad's sum); wider groups use cross-lane shuffles.
+template <int NQ> __device__ __forceinline__ float group_sum(float v) {
+  auto dpp = [](float x, auto ctrl) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), decltype(ctrl)::value,
+                                                              0xf, 0xf, false));
+  };
+  if constexpr (NQ >= 2) v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm(1, 0, 3, 2)
+  if constexpr (NQ >= 4) v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm(2, 3, 0, 1)
+  if constexpr (NQ >= 8) v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+#pragma unroll
+  for (int off = 8; off < NQ; off <<= 1) v += __shfl_xor(v, off, NQ);
+  return v;
+}
+
 template <class IO, int NQ, int R>
 __global__ void __launch_bounds__(256) state_update_vec_kernel(DecodeParams p) {
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
@@ -126,38 +143,36 @@ __global__ void __launch_bounds__(256) state_update_vec_kernel(DecodeParams p) {
   const int64_t b0 = valid ? (dq / dim) * R : 0;
   const int n0 = 4 * q;
   const bool qok = valid && n0 < N;
+  const int64_t nc = qok ? n0 : 0;
 
-  float A2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (qok) {
-    const float4 av = *reinterpret_cast<const float4*>(p.A + d * N + n0);
-    A2[0] = av.x * kLog2e; A2[1] = av.y * kLog2e; A2[2] = av.z * kLog2e; A2[3] = av.w * kLog2e;
-  }
-  const float bias = (valid && p.bias) ? p.bias[d] : 0.0f;
-  const float Dd = (valid && p.D) ? p.D[d] : 0.0f;
-
+  // Every load is issued up front and unconditionally, from an address clamped
+  // into its array (a missing bias, D or z reads a same-sized array in its
+  // place, and the value is then dropped); the invalid lanes' values are masked
+  // after the loads.  Loads under divergent branches would each be waited for
+  // before the next one issues: a memory round trip apiece.
+  const float4 av = *reinterpret_cast<const float4*>(p.A + d * N + nc);
+  const float bias_v = (p.bias ? p.bias : p.A)[d];
+  const float D_v = (p.D ? p.D : p.A)[d];
   float h[R][4], Bv[R][4], Cv[R][4], uu[R], xr[R], zz[R];
-  bool ok[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int64_t b = b0 + r;
-    ok[r] = qok && b < p.batch;
-    const bool cok = valid && b < p.batch;  // channel-level values (all NQ lanes need them)
-    if (ok[r]) {
-      const float4 hv = *reinterpret_cast<const float4*>(p.state + (b * dim + d) * N + n0);
-      h[r][0] = hv.x; h[r][1] = hv.y; h[r][2] = hv.z; h[r][3] = hv.w;
-      Vec4In<IO>::load(p.B, b * N + n0, Bv[r]);
-      Vec4In<IO>::load(p.C, b * N + n0, Cv[r]);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) h[r][j] = Bv[r][j] = Cv[r][j] = 0.0f;
-    }
-    uu[r] = cok ? load_elem<IO>(p.u, b * dim + d) : 0.0f;
-    xr[r] = cok ? load_elem<IO>(p.delta, b * dim + d) : 0.0f;
-    zz[r] = (cok && p.z) ? load_elem<IO>(p.z, b * dim + d) : 0.0f;
+    const int64_t bc = (b0 + r < p.batch) ? b0 + r : p.batch - 1;
+    const float4 hv = *reinterpret_cast<const float4*>(p.state + (bc * dim + d) * N + nc);
+    h[r][0] = hv.x; h[r][1] = hv.y; h[r][2] = hv.z; h[r][3] = hv.w;
+    Vec4In<IO>::load(p.B, bc * N + nc, Bv[r]);
+    Vec4In<IO>::load(p.C, bc * N + nc, Cv[r]);
+    uu[r] = load_elem<IO>(p.u, bc * dim + d);
+    xr[r] = load_elem<IO>(p.delta, bc * dim + d);
+    zz[r] = load_elem<IO>(p.z ? p.z : p.u, bc * dim + d);
   }
+  const float A2[4] = {av.x * kLog2e, av.y * kLog2e, av.z * kLog2e, av.w * kLog2e};
+  const float bias = p.bias ? bias_v : 0.0f;
+  const float Dd = p.D ? D_v : 0.0f;
+
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t b = b0 + r;
+    const bool ok = qok && b < p.batch;
     const float x = xr[r] + bias;
     float dl = softplus_f(x);
     dl = p.softplus ? dl : x;
@@ -169,10 +184,9 @@ __global__ void __launch_bounds__(256) state_update_vec_kernel(DecodeParams p) {
       h[r][j] = __builtin_fmaf(a, h[r][j], du * Bv[r][j]);
       yp = __builtin_fmaf(Cv[r][j], h[r][j], yp);
     }
-    if (ok[r])
+    if (ok)
       *reinterpret_cast<float4*>(p.state + (b * dim + d) * N + n0) = make_float4(h[r][0], h[r][1], h[r][2], h[r][3]);
-#pragma unroll
-    for (int off = 1; off < NQ; off <<= 1) yp += __shfl_xor(yp, off, NQ);
+    yp = group_sum<NQ>(qok ? yp : 0.0f);  // quads past N read a clamped quad: they add nothing
     if (valid && b < p.batch && q == 0) {
       float v = __builtin_fmaf(Dd, uu[r], yp);
       if (p.z) v *= silu_f(zz[r]);

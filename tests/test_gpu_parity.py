@@ -299,9 +299,11 @@ def test_decode_continues_scan(dtype):
 
 @pytest.mark.parametrize("dtype,N,batch", [("bf16", 16, 5), ("f32", 16, 5), ("f32", 3, 5), ("bf16", 64, 5), ("f32", 1, 5),
                                            ("bf16", 15, 5), ("bf16", 16, 1), ("f32", 8, 2), ("f32", 16, 7),
-                                           ("bf16", 128, 5), ("f32", 256, 3), ("f32", 130, 2), ("bf16", 100, 1)])
+                                           ("bf16", 128, 5), ("f32", 256, 3), ("f32", 130, 2), ("bf16", 100, 1),
+                                           ("bf16", 20, 3), ("f32", 32, 4)])
 def test_decode_small_against_oracle(dtype, N, batch):
-    """Odd batch sizes leave the last two-row group of the vector kernel half empty; batch 1 runs one row per thread."""
+    """Odd batch sizes leave the last two-row group of the vector kernel half empty; batch 1 runs one row per thread.
+    N = 20 gives groups of eight lanes of which the last three hold no states."""
     rng = np.random.default_rng(35 + N + 100 * batch)
     dim = 77
     u = rng.standard_normal((batch, dim)).astype(np.float32)
@@ -321,6 +323,29 @@ def test_decode_small_against_oracle(dtype, N, batch):
                              to_dev(C, dtype), D=to_dev_f32(D), z=to_dev(z, dtype), delta_bias=to_dev_f32(bias))
     torch.cuda.synchronize()
     so, yo = R.state_update(h0, u, dr, A, B, C, D=D, z=z, delta_bias=bias)
+    assert rel_err(st.cpu().numpy(), so) <= 1e-5
+    assert rel_err(y.float().cpu().numpy(), yo) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_optional_inputs_off(dtype):
+    """No D, z or bias, softplus off: the step is delta_raw itself, y = C . h."""
+    rng = np.random.default_rng(37)
+    batch, dim, N = 5, 130, 16
+    u = rng.standard_normal((batch, dim)).astype(np.float32)
+    dr = rng.uniform(0.01, 0.5, size=(batch, dim)).astype(np.float32)
+    B = rng.standard_normal((batch, N)).astype(np.float32)
+    C = rng.standard_normal((batch, N)).astype(np.float32)
+    if dtype == "bf16":
+        u, dr, B, C = (I.round_to_bf16(a) for a in (u, dr, B, C))
+    A = -rng.uniform(0.05, 3.0, size=(dim, N)).astype(np.float32)
+    h0 = rng.standard_normal((batch, dim, N)).astype(np.float32)
+    say(f"decode optional inputs off {dtype}")
+    st = to_dev_f32(h0)
+    y = ops.ssm_state_update(st, to_dev(u, dtype), to_dev(dr, dtype), to_dev_f32(A), to_dev(B, dtype),
+                             to_dev(C, dtype), softplus=False)
+    torch.cuda.synchronize()
+    so, yo = R.state_update(h0, u, dr, A, B, C, softplus=False)
     assert rel_err(st.cpu().numpy(), so) <= 1e-5
     assert rel_err(y.float().cpu().numpy(), yo) <= TOL[dtype]
 
