@@ -304,10 +304,12 @@ size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_
  *   dfinal_state[s] to dinitial_state[s] unchanged.
  *   No output may alias an input or another output.  workspace must hold
  *   ssm_scan_bwd_workspace_size() bytes of device memory, 256-byte aligned.
- *   UNSUPPORTED for dstate > 64 or batch > 65535.  Above 32 states the
- *   states are taken in two halves, the first leaving its per-(token,
- *   channel) partial sums in the workspace (3 * batch * L * dim * 4 more
- *   bytes). */
+ *   UNSUPPORTED for dstate > 64 or batch > 65535, and where a tile's dB/dC
+ *   partial row ((L + 128) * dstate * 4 bytes, dstate rounded up to the
+ *   kernel's state count) or, above 32 states, an fp32 row of L * dim
+ *   partials reaches 2^31 bytes.  Above 32 states the states are taken in two
+ *   halves, the first leaving its per-(token, channel) partial sums in the
+ *   workspace (3 * batch * L * dim * 4 more bytes). */
 ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
                           const float* D, const void* z, const float* delta_bias, int softplus_flag,
                           const void* dy, const float* dfinal_state, const float* initial_state,

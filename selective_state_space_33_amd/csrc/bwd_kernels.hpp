@@ -124,22 +124,22 @@ constexpr int kBwdTB = 16;  // tokens per block (the checkpoint spacing)
 // vmcnt(0) with expcnt and lgkmcnt left at their maxima (gfx9 s_waitcnt encoding).
 constexpr int kBwdWaitVm0 = 0x0F70;
 
-// Sums over each group of 4 lanes of four values at once, each left in the
-// group's last lane: two steps of x += x shifted right by 1, 2 lanes within
-// the 16-lane row (lanes shifted in from outside the row add zero, and lane
-// 4g+3 only ever takes lanes 4g .. 4g+2).  One asm block, so the order is
-// fixed: each value's next step comes four instructions after its last, past
-// the two wait states a DPP read of a VALU result needs; the leading s_nop
-// covers the inputs' own writes.
-__device__ __forceinline__ void quad_sums4_to_last(float& a, float& b, float& c, float& d) {
-#define SSM_ROW_STEP(K)                                                                 \
-  "v_add_f32_dpp %0, %0, %0 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-  "v_add_f32_dpp %1, %1, %1 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-  "v_add_f32_dpp %2, %2, %2 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
-  "v_add_f32_dpp %3, %3, %3 row_shr:" #K " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
-  asm("s_nop 1\n\t" SSM_ROW_STEP(1) SSM_ROW_STEP(2)
+// Sums over each group of 4 lanes of four values at once, left in all four
+// lanes of the group: a butterfly of two quad permutations (lane i ^ 1, then
+// lane i ^ 2).  Every lane ends with (x0 + x1) + (x2 + x3), the same bits, so
+// all four may store it to the same address and no lane needs a branch.  One
+// asm block, so the order is fixed: each value's next step comes four
+// instructions after its last, past the two wait states a DPP read of a VALU
+// result needs; the leading s_nop covers the inputs' own writes.
+__device__ __forceinline__ void quad_allsums4(float& a, float& b, float& c, float& d) {
+#define SSM_QUAD_STEP(P)                                                          \
+  "v_add_f32_dpp %0, %0, %0 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t"        \
+  "v_add_f32_dpp %1, %1, %1 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t"        \
+  "v_add_f32_dpp %2, %2, %2 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t"        \
+  "v_add_f32_dpp %3, %3, %3 quad_perm:" P " row_mask:0xf bank_mask:0xf\n\t"
+  asm("s_nop 1\n\t" SSM_QUAD_STEP("[1,0,3,2]") SSM_QUAD_STEP("[2,3,0,1]")
       : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-#undef SSM_ROW_STEP
+#undef SSM_QUAD_STEP
 }
 
 // WIDE: 0 for all states in one launch; 1 for the first half of wide states
@@ -197,6 +197,8 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   float A2[NPL], An[NPL];
   float Dd = 0.0f, bias_d = 0.0f;
   rsrc_t rs_u, rs_d, rs_z, rs_dy, rs_du, rs_dd, rs_dz, rs_bc;
+  rsrc_t rs_dbp, rs_dcp;                   // the tile's dB, dC partial rows from the stretch's first token
+  rsrc_t rs_pv, rs_ps1, rs_ps2;            // wide states: the per-(token, channel) partial sums
   const float* ckpt_row = p.ckpt;
   auto set_tile = [&](int t, int64_t tb = 0, int64_t tl = -1, int64_t sr = -1, int64_t ckpt_slot0 = 0) {
     tile = t;
@@ -235,6 +237,17 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     const float* bc_row = p.bc + ((b * p.g_total + nb / NPL + w) * p.Lp + t_begin) * (2 * NPL);
     rs_bc = make_rsrc(bc_row, (p.Lp + 32 - t_begin) * 2 * NPL * static_cast<int64_t>(sizeof(float)));
     ckpt_row = p.ckpt + ((static_cast<int64_t>(t) * p.ckpt_blocks + ckpt_slot0) * 64 + lane) * npg + nb + n0;
+    const int64_t prow = ((b * p.ntd + t % p.ntd) * p.Lp + t_begin) * npg;  // (the host keeps Lp * npg * 4 < 2^31)
+    const int64_t pbytes = (p.Lp - t_begin) * npg * static_cast<int64_t>(sizeof(float));
+    rs_dbp = make_rsrc(p.dB_part + prow, pbytes);
+    rs_dcp = make_rsrc(p.dC_part + prow, pbytes);
+    if constexpr (WIDE != 0) {  // fp32 rows like the tile's token rows (the host keeps L * dim * 4 < 2^31)
+      const int64_t fo = (b * L + t_begin) * dim + d0;
+      const int64_t fbytes = (len * dim - d0) * static_cast<int64_t>(sizeof(float));
+      rs_pv = make_rsrc(p.part_v + fo, fbytes);
+      rs_ps1 = make_rsrc(p.part_s1 + fo, fbytes);
+      rs_ps2 = make_rsrc(p.part_s2 + fo, fbytes);
+    }
   };
 
   // ---- running sums of the stretch being worked on: the adjoint entering the
@@ -254,9 +267,16 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   // Two-slot pipeline over the blocks (last to first): the loads of block
   // k-1 are in flight while block k computes.  Unrolled by two so each slot
   // keeps fixed registers (no copies, so no early waits on loads in flight).
+  // Every vector-memory operation of the loop is unconditional, so that the
+  // compiler can count them: loads and stores share one counter, and a wait
+  // for block k's data must not wait for the loads of block k-1 issued after
+  // them.  (With a load or store under a branch, the count the compiler can
+  // prove on every path is too low, and each block waited for the next one's
+  // loads.)  Block k-1 may be the one before the stretch: its buffer loads are
+  // then out of range or unused, and its checkpoint index is clamped.
   Raw<IO, 1> qu[2][RPT], qd[2][RPT], qz[2][RPT], qg[2][RPT];
   float qrv[2][NRV], qhs[2][NPL];
-  auto load_block = [&](auto slotc, int k) {
+  auto load_block = [&](auto slotc, int k) __attribute__((always_inline)) {
     constexpr int S = decltype(slotc)::value;
     const int t0 = k * TB;
 #pragma unroll
@@ -264,7 +284,8 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       qrv[S][v] = __uint_as_float(
           __builtin_amdgcn_raw_buffer_load_b32(rs_bc, rec_voff + t0 * (2 * NPL * 4) + v * 64, 0, 0));
 #pragma unroll
-    for (int j = 0; j < NPL; ++j) qhs[S][j] = dvalid ? ckpt_row[static_cast<int64_t>(k) * 64 * npg + j] : 0.0f;
+    for (int j = 0; j < NPL; ++j)  // every lane has a checkpoint row (see P for lanes past dim)
+      qhs[S][j] = ckpt_row[static_cast<int64_t>(k < 0 ? 0 : k) * 64 * npg + j];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int off = (t0 + w + i * G) * row_bytes + lane * ES;
@@ -274,7 +295,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       qg[S][i] = buf_load<IO, 1>(rs_dy, off, 0);
     }
   };
-  auto process_block = [&](auto slotc, int k) {
+  auto process_block = [&](auto slotc, int k) __attribute__((always_inline)) {
     constexpr int S = decltype(slotc)::value;
     const int t0 = k * TB;
     const float* rv = qrv[S];
@@ -286,7 +307,10 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int row = w + i * G;
-      const bool live = t0 + row < len && dvalid;  // lanes past dim read the next row: keep them at zero
+      // lanes past dim read the next row (and their checkpoints hold whatever the checkpoint pass scanned
+      // there): a zero step and dv make every term they add to the dB, dC sums zero, and their own
+      // outputs are not stored
+      const bool live = t0 + row < len && dvalid;
       float uf, df, zf, gf;
       unpack<IO, 1>(qu[S][i], &uf);
       unpack<IO, 1>(qd[S][i], &df);
@@ -354,18 +378,18 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       float v = SEP ? sYP[0][row][lane] : sYS[0][row][lane].x;
 #pragma unroll
       for (int ww = 1; ww < G; ++ww) v += SEP ? sYP[ww][row][lane] : sYS[ww][row][lane].x;
-      const int64_t pidx = ((b * L + t_begin + t0 + row) * dim + d);  // (row, token, channel) of the partials
+      // fp32 partial of this element in the wide-state arrays (out of range when not live: dropped or zero)
+      const int poff = elive[i] ? ((t0 + row) * static_cast<int>(dim) + lane) * 4 : 0x7ffffff0;
       if constexpr (WIDE == 1) {
-        if (elive[i]) p.part_v[pidx] = v;  // the other half finishes v
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs_pv, poff, 0, 0);  // the other half finishes v
         continue;
       }
-      if constexpr (WIDE == 2) v += elive[i] ? p.part_v[pidx] : 0.0f;
+      if constexpr (WIDE == 2) v += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_pv, poff, 0, 0));
       v = __builtin_fmaf(Dd, eu[i], v);
-      if (has_z) {
-        const float dzv = egz[i] * v;
-        const int off = elive[i] ? (t0 + row) * row_bytes + lane * ES : 0x7ffffff0;
-        buf_store<IO, 1>(rs_dz, off, 0, &dzv);
-      }
+      // without z the store's resource has no range (dropped) and egz is zero
+      const float dzv = egz[i] * v;
+      const int off = elive[i] ? (t0 + row) * row_bytes + lane * ES : 0x7ffffff0;
+      buf_store<IO, 1>(rs_dz, off, 0, &dzv);
     }
     if constexpr (!SEP) __syncthreads();  // R overwrites the partials just read
 
@@ -401,13 +425,14 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
             ...);
          }(std::make_integer_sequence<int, NPL>{});
 #pragma unroll
-         for (int j = 0; j < NPL; j += 2) quad_sums4_to_last(pb[j], pb[j + 1], pc[j], pc[j + 1]);
-         if ((lane & 3) == 3) {
+         for (int j = 0; j < NPL; j += 2) quad_allsums4(pb[j], pb[j + 1], pc[j], pc[j + 1]);
+         // the four lanes of a group store the same sum to the same word: no
+         // branch, so the block's adjoint steps stay one straight run that the
+         // compiler can schedule across (its LDS reads issued early)
 #pragma unroll
-           for (int j = 0; j < NPL; ++j) {
-             sRB[t][n0 + j][lane >> 2] = pb[j];
-             sRC[t][n0 + j][lane >> 2] = pc[j];
-           }
+         for (int j = 0; j < NPL; ++j) {
+           sRB[t][n0 + j][lane >> 2] = pb[j];
+           sRC[t][n0 + j][lane >> 2] = pc[j];
          }
          sYS[w][t][lane] = make_float2(s1, s2);
        }()),
@@ -425,19 +450,15 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
         S1 += sYS[ww][row][lane].x;
         S2 += sYS[ww][row][lane].y;
       }
-      const int64_t pidx = ((b * L + t_begin + t0 + row) * dim + d);
+      const int poff = elive[i] ? ((t0 + row) * static_cast<int>(dim) + lane) * 4 : 0x7ffffff0;
       if constexpr (WIDE == 1) {
-        if (elive[i]) {
-          p.part_s1[pidx] = S1;
-          p.part_s2[pidx] = S2;
-        }
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S1), rs_ps1, poff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S2), rs_ps2, poff, 0, 0);
         continue;
       }
       if constexpr (WIDE == 2) {
-        if (elive[i]) {
-          S1 += p.part_s1[pidx];
-          S2 += p.part_s2[pidx];
-        }
+        S1 += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_ps1, poff, 0, 0));
+        S2 += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_ps2, poff, 0, 0));
       }
       const float dDelta = __builtin_fmaf(eu[i], S2, S1);
       const float duv = __builtin_fmaf(edl[i], S2, Dd * edv[i]);
@@ -450,18 +471,26 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
         accBias += ddr;
       }
     }
-    for (int q = tid; q < TB * NPAD; q += 64 * G) {
-      const int t = q / NPAD, n = q % NPAD;
-      if (t0 + t >= len) continue;  // past the stretch: the next packed sequence's tokens
-      float sb = 0.0f, sc = 0.0f;
+    // (token, state) items of the block's dB, dC partials, a fixed number per
+    // thread; a token past the stretch (the next packed sequence's) stores out
+    // of range.  TB * NPAD is a multiple of 64, so `inb` is wave-uniform.
+    constexpr int NITEMS = TB * NPAD, NTH = 64 * G;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sb += sRB[t][n][r];
-        sc += sRC[t][n][r];
+    for (int it = 0; it < (NITEMS + NTH - 1) / NTH; ++it) {
+      const int q = tid + it * NTH;
+      const bool inb = q < NITEMS;
+      const int t = inb ? q / NPAD : 0, n = inb ? q % NPAD : 0;
+      float sb = 0.0f, sc = 0.0f;
+      if (inb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sb += sRB[t][n][r];
+          sc += sRC[t][n][r];
+        }
       }
-      const int64_t o = ((b * p.ntd + tile % p.ntd) * p.Lp + t_begin + t0 + t) * npg + nb + n;
-      p.dB_part[o] = sb;
-      p.dC_part[o] = sc;
+      const int o = (inb && t0 + t < len) ? ((t0 + t) * npg + nb + n) * 4 : 0x7ffffff0;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sb), rs_dbp, o, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sc), rs_dcp, o, 0, 0);
     }
     // No barrier here: the next block's P writes only sDU and sDV, whose last
     // readers (R) finished at the barrier before E2, and its F writes the
@@ -472,17 +501,27 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   // of blocks once at least k_stop blocks are done and the flag is set
   // (thread 0 polls it, the workgroup reads it through LDS); returns the end
   // of what is left, [kb, returned).
-  auto run_blocks = [&](int kb, int ke, const unsigned* stop_flag, int k_stop) -> int {
+  // POLL (a run with a stop flag): every thread loads the flag once per pair
+  // of blocks, unconditionally, and thread 0's value decides; runs without a
+  // flag issue no load at all (an unused load would still be waited for
+  // before its register is reused).  This lambda and the two above are always
+  // inlined: as a called function a block would take the buffer descriptors in
+  // vector registers (a loop per access) and a stack frame.
+  auto run_blocks = [&](auto pollc, int kb, int ke, const unsigned* stop_flag,
+                        int k_stop) __attribute__((always_inline)) -> int {
+    constexpr bool POLL = decltype(pollc)::value;
     if (ke <= kb) return kb;
     load_block(IC<0>{}, ke - 1);
     for (int k = ke - 1; k >= kb; k -= 2) {
-      if (k - 1 >= kb) load_block(IC<1>{}, k - 1);
+      unsigned seen = 0u;
+      if constexpr (POLL) seen = __hip_atomic_load(stop_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      load_block(IC<1>{}, k - 1);
       process_block(IC<0>{}, k);
       if (k - 1 < kb) break;
-      if (k - 2 >= kb) load_block(IC<0>{}, k - 2);
+      load_block(IC<0>{}, k - 2);
       process_block(IC<1>{}, k - 1);
-      if (stop_flag != nullptr && ke - (k - 1) >= k_stop && k - 1 > kb) {
-        if (tid == 0) sWord = __hip_atomic_load(stop_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (POLL && ke - (k - 1) >= k_stop && k - 1 > kb) {
+        if (tid == 0) sWord = seen;
         __syncthreads();
         const bool stop = sWord != 0u;
         __syncthreads();  // every wavefront has read the word before it is written again
@@ -540,7 +579,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
     te = te < tb ? tb : (te > L ? L : te);
     set_tile(col, tb, te - tb, s, tb / TB + static_cast<int64_t>(kPackedCkptSlack) * s);
     start_from_final();
-    run_blocks(0, nblk, nullptr, 0);
+    run_blocks(IC<false>{}, 0, nblk, nullptr, 0);
     write_dh0();
     write_partials(0, false);
     return;
@@ -548,7 +587,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   if (p.n_split == 0) {  // one workgroup per tile
     set_tile(blockIdx.x);
     start_from_final();
-    run_blocks(0, nblk, nullptr, 0);
+    run_blocks(IC<false>{}, 0, nblk, nullptr, 0);
     write_dh0();
     write_partials(0, false);
     return;
@@ -562,7 +601,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   set_tile(j);
   start_from_final();
   if (j >= p.n_split * p.Ks) {
-    run_blocks(0, nblk, nullptr, 0);
+    run_blocks(IC<false>{}, 0, nblk, nullptr, 0);
     write_dh0();
     write_partials(0, true);
     return;
@@ -573,7 +612,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   // set once chunk c+1 is done
   const unsigned* my_flag = p.wait_override ? p.wait_override : p.flags + static_cast<int64_t>(st) * p.Ks + c;
   int rest = nblk;
-  if (o > 0) rest = run_blocks(0, nblk, my_flag, o * p.chunk_blocks);
+  if (o > 0) rest = run_blocks(IC<true>{}, 0, nblk, my_flag, o * p.chunk_blocks);
   float sdh[NPL], sdA[NPL];
   const float sD = accD, sBias = accBias;
 #pragma unroll
@@ -601,7 +640,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
                       : __hip_atomic_load(p.carry + crow * NPAD + n0 + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  run_blocks(kb, ke, nullptr, 0);
+  run_blocks(IC<false>{}, kb, ke, nullptr, 0);
   if (c > 0) {
     if (dvalid) {
 #pragma unroll
@@ -626,7 +665,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   }
   accD = sD;
   accBias = sBias;
-  run_blocks(0, rest, nullptr, 0);
+  run_blocks(IC<false>{}, 0, rest, nullptr, 0);
   write_dh0();
   write_partials(0, true);
 }

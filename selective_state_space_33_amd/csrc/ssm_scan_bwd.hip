@@ -134,6 +134,14 @@ BwdLayout bwd_layout(const BwdPlan& pl, int64_t batch, int64_t L, int64_t dim) {
 // The kernels address a tile's token rows with 32-bit byte offsets from the
 // row block's start.
 bool rows_fit(int64_t L, int64_t dim, int64_t es) { return L * dim * es < 0x7fffffffLL - kTrip * dim * es; }
+// The kernel reaches a tile's dB/dC partial row ([Lp][states] fp32) and, for
+// wide states, the fp32 per-(token, channel) partials of a row through buffer
+// resources with 32-bit offsets.
+bool plan_fits(const BwdPlan& pl, int64_t L, int64_t dim) {
+  const int64_t npad = static_cast<int64_t>(pl.npl) * pl.g_total;
+  if (pl.Lp * npad * 4 >= 0x7fffffffLL) return false;
+  return !pl.wide || rows_fit(L, dim, 4);
+}
 
 template <class IO>
 hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const void* C, float* bc, ScanParams sp,
@@ -201,6 +209,7 @@ extern "C" size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t 
   const int64_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
   if (!rows_fit(L, dim, es)) return 0;
   const BwdPlan pl = plan_bwd(batch, L, dim, dstate, nseq);
+  if (!plan_fits(pl, L, dim)) return 0;
   return bwd_layout(pl, batch, L, dim).total;
 }
 
@@ -226,6 +235,7 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   if (dstate > kBwdMaxState || batch > kBwdMaxBatch) return SSM_ERR_UNSUPPORTED;
   if (!rows_fit(L, dim, static_cast<int64_t>(es))) return SSM_ERR_UNSUPPORTED;
   const BwdPlan pl = plan_bwd(batch, L, dim, dstate, cu_seqlens ? nseq : 0);
+  if (!plan_fits(pl, L, dim)) return SSM_ERR_UNSUPPORTED;
   if (pl.T > 0x7fffffffLL || batch * (pl.Lp / kPackT) > 0x7fffffffLL || batch * L * dstate / 256 > 0x7fffffffLL)
     return SSM_ERR_UNSUPPORTED;
   const BwdLayout lay = bwd_layout(pl, batch, L, dim);

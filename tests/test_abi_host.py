@@ -189,6 +189,12 @@ def test_bwd_workspace_size():
     assert L.ssm_scan_bwd_workspace_size(0, 10, 10, 16, 0, F32) == 0
     assert L.ssm_scan_bwd_workspace_size(1, 10, 10, 16, 0, 7) == 0
     assert L.ssm_scan_bwd_workspace_size(1, 1 << 24, 1024, 16, 0, F32) == 0  # rows past 2^31 bytes
+    # a tile's dB/dC partial row past 2^31 bytes: 40M tokens x 16 states x 4 bytes
+    assert L.ssm_scan_bwd_workspace_size(1, 40_000_000, 1, 16, 0, F32) == 0
+    assert L.ssm_scan_bwd_workspace_size(1, 20_000_000, 1, 16, 0, F32) > 0
+    # wide states keep fp32 partial rows of L * dim: allowed for 16 states, not for 64, at bf16 rows of 1.6 GB
+    assert L.ssm_scan_bwd_workspace_size(1, 200_000, 4096, 16, 0, BF16) > 0
+    assert L.ssm_scan_bwd_workspace_size(1, 200_000, 4096, 64, 0, BF16) == 0
     # packed sequences: batch 1 only; partial rows per sequence and a few more checkpoints per sequence
     assert L.ssm_scan_bwd_workspace_size(2, 1000, 136, 16, 3, F32) == 0
     assert L.ssm_scan_bwd_workspace_size(1, 1000, 136, 16, 7, F32) > L.ssm_scan_bwd_workspace_size(1, 1000, 136, 16,
@@ -216,6 +222,8 @@ def _bwd(lib_, **kw):
     (dict(h0=0xc002), INVALID), (dict(dh0=0xd001), INVALID),
     (dict(N=65), UNSUPPORTED), (dict(batch=70000), UNSUPPORTED),
     (dict(L=1 << 24, dim=1024), UNSUPPORTED),
+    (dict(L=40_000_000, dim=1), UNSUPPORTED),           # the dB/dC partial row of a tile past 2^31 bytes
+    (dict(L=200_000, dim=4096, N=64, dt=BF16), UNSUPPORTED),  # wide states' fp32 partial rows past 2^31 bytes
     (dict(), INVALID),                                  # no workspace
     (dict(ws=0x100000, wsb=256), INVALID),              # too small
     (dict(cu=0x8000, nseq=2, batch=2), INVALID),        # packed sequences need batch 1
