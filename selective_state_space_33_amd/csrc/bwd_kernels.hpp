@@ -341,6 +341,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
 
     // ---- F: recompute the block's states from the checkpoint
     float hs[TB][NPL], as[KEEP_A ? TB : 1][NPL];
+    float2 kdd[KEEP_A ? TB : 1];  // (delta, delta*u) of the block's tokens, kept from F for R where registers allow
     {
       float h[NPL];
 #pragma unroll
@@ -349,6 +350,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
         (([&] {
            constexpr int t = T;
            const float2 dd = sDU[t][lane];
+           if constexpr (KEEP_A) kdd[t] = dd;
            float yp = 0.0f;
            [&]<int... J>(std::integer_sequence<int, J...>) {
              (([&] {
@@ -398,7 +400,9 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       (([&] {
          constexpr int t = TB - 1 - T;
          const float dv = sDV[t][lane];
-         const float2 dd = sDU[t][lane];
+         float2 dd;
+         if constexpr (KEEP_A) dd = kdd[t];
+         else dd = sDU[t][lane];
          float s1 = 0.0f, s2 = 0.0f;
          float pb[NPL], pc[NPL];
          static_assert(NPL % 2 == 0, "row sums go four values at a time");
