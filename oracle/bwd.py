@@ -25,6 +25,17 @@ dfinal_state, the gradient reaching the final state, if any).
 The transcription is independent of the C oracle (ssm_ref.c); the tests pin
 it to that oracle's forward and to central finite differences of it.
 
+With rule="trap" the transcribed forward is Mamba-3's trapezoidal
+three-term recurrence ("The State That Must Remember Everything", Part 7,
+"Mamba-3 (2026)", item 1) with the coefficients as this library reads them
+(alpha_t = exp(Delta_t A), beta_t = Delta_t/2 alpha_t, gamma_t = Delta_t/2,
+and no previous input at the first token of a recurrence):
+
+    h_t = alpha_t * h_{t-1} + beta_t * B_{t-1} u_{t-1} + gamma_t * B_t u_t
+
+with the same readout, skip and gate.  The tests pin it to central finite
+differences of the C oracle's trapezoidal forward.
+
 Packed sequences (cu_seqlens, batch 1): sequence s is tokens cu[s] ..
 cu[s+1]-1 of the row, run on its own from initial_state[s] (zero if none)
 with its own final state, as the forward's packed scan defines it; the
@@ -61,8 +72,36 @@ def forward_torch(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=T
     return y, h
 
 
-def forward_packed_torch(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, cu_seqlens):
-    """forward_torch over each packed sequence of batch row 0, from its own initial state (None: zero).
+def forward_trap_torch(u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True, initial_state=None):
+    """The trapezoidal three-term recurrence on float64 torch tensors; returns (y, final_state)."""
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    x = delta if delta_bias is None else delta + delta_bias
+    dl = torch.logaddexp(x, torch.zeros_like(x)) if softplus else x
+    h = torch.zeros((batch, dim, N), dtype=torch.float64) if initial_state is None else initial_state
+    ys = []
+    for t in range(L):
+        step = dl[:, t, :, None]                                     # [batch, dim, 1]
+        alpha = torch.exp(step * A[None, :, :])
+        beta = 0.5 * step * alpha
+        gamma = 0.5 * step
+        cur = u[:, t, :, None] * B[:, t, None, :]                    # B_t u_t
+        h = alpha * h + gamma * cur
+        if t > 0:
+            h = h + beta * (u[:, t - 1, :, None] * B[:, t - 1, None, :])
+        v = (h * C[:, t, None, :]).sum(-1)
+        if D is not None:
+            v = v + D[None, :] * u[:, t, :]
+        ys.append(v)
+    y = torch.stack(ys, dim=1)
+    if z is not None:
+        y = y * (z * torch.sigmoid(z))
+    return y, h
+
+
+def forward_packed_torch(u, delta, A, B, C, D, z, delta_bias, softplus, initial_state, cu_seqlens,
+                         forward=forward_torch):
+    """`forward` over each packed sequence of batch row 0, from its own initial state (None: zero).
     Returns (y [1, L, dim], final_state [nseq, dim, N])."""
     nseq = len(cu_seqlens) - 1
     dim, N = A.shape
@@ -72,8 +111,8 @@ def forward_packed_torch(u, delta, A, B, C, D, z, delta_bias, softplus, initial_
         sl = lambda t: None if t is None else t[:, a:b]  # noqa: E731
         h0 = None if initial_state is None else initial_state[s:s + 1]
         if b > a:
-            y, fs = forward_torch(sl(u), sl(delta), A, sl(B), sl(C), D=D, z=sl(z), delta_bias=delta_bias,
-                                  softplus=softplus, initial_state=h0)
+            y, fs = forward(sl(u), sl(delta), A, sl(B), sl(C), D=D, z=sl(z), delta_bias=delta_bias,
+                            softplus=softplus, initial_state=h0)
             ys.append(y)
         else:
             fs = torch.zeros((1, dim, N), dtype=torch.float64) if h0 is None else h0
@@ -82,8 +121,10 @@ def forward_packed_torch(u, delta, A, B, C, D, z, delta_bias, softplus, initial_
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, dfinal_state=None,
-             initial_state=None, cu_seqlens=None):
+             initial_state=None, cu_seqlens=None, rule="euler"):
     """Gradients of sum(y*dy) + sum(final_state*dfinal_state) with respect to every input.
+
+    rule: "euler" (the two-term recurrence) or "trap" (the trapezoidal three-term one).
 
     With cu_seqlens (batch 1) the row holds packed sequences: initial_state, dfinal_state and the returned
     dinitial_state are [nseq, dim, N].
@@ -97,12 +138,13 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
         if tv is not None:
             tv.requires_grad_(True)
         ts[n] = tv
+    fwd = {"euler": forward_torch, "trap": forward_trap_torch}[rule]
     if cu_seqlens is not None:
         y, fs = forward_packed_torch(ts["u"], ts["delta"], ts["A"], ts["B"], ts["C"], ts["D"], ts["z"],
-                                     ts["delta_bias"], softplus, ts["initial_state"], list(cu_seqlens))
+                                     ts["delta_bias"], softplus, ts["initial_state"], list(cu_seqlens), forward=fwd)
     else:
-        y, fs = forward_torch(ts["u"], ts["delta"], ts["A"], ts["B"], ts["C"], D=ts["D"], z=ts["z"],
-                              delta_bias=ts["delta_bias"], softplus=softplus, initial_state=ts["initial_state"])
+        y, fs = fwd(ts["u"], ts["delta"], ts["A"], ts["B"], ts["C"], D=ts["D"], z=ts["z"],
+                    delta_bias=ts["delta_bias"], softplus=softplus, initial_state=ts["initial_state"])
     obj = (y * _t(dy)).sum()
     if dfinal_state is not None:
         obj = obj + (fs * _t(dfinal_state)).sum()

@@ -188,3 +188,104 @@ def test_packed_gradients_match_central_differences(cuts):
     for s in range(nseq):
         if cuts[s + 1] == cuts[s]:
             np.testing.assert_array_equal(g["dinitial_state"][s], dfs[s])
+
+
+# ---- the trapezoidal rule (oracle/bwd.py rule="trap"): its own transcription of the three-term recurrence,
+# pinned to the C oracle's trapezoidal forward (itself pinned in test_oracle_trap.py) and to central
+# differences of it
+
+@pytest.mark.parametrize("softplus,gated,h0", [(True, True, False), (False, False, True), (True, False, True)])
+def test_trap_transcription_forward_equals_c_oracle(softplus, gated, h0):
+    import torch
+    rng = np.random.default_rng(70 + softplus + 2 * gated + 4 * h0)
+    x = _inputs(rng, 2, 9, 5, 3, gated=gated)
+    if not softplus:
+        x["delta"] = np.abs(x["delta"]) + 0.05
+    init = rng.standard_normal((2, 5, 3)) if h0 else None
+    t = {k: (None if v is None else torch.tensor(v)) for k, v in x.items()}
+    y, fs = OB.forward_trap_torch(t["u"], t["delta"], t["A"], t["B"], t["C"], D=t["D"], z=t["z"],
+                                  delta_bias=t["delta_bias"], softplus=softplus,
+                                  initial_state=None if init is None else torch.tensor(init))
+    yo, fo = R.scan_trap_fwd_ex(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                                delta_bias=x["delta_bias"], softplus=softplus, initial_state=init)
+    assert _rel(y.numpy(), yo) < 1e-13 and _rel(fs.numpy(), fo) < 1e-13
+
+
+def _fd_check(rng, x, names, grads, obj, count=6, tol=2e-7):
+    checked = 0
+    for name in names:
+        arr = x[name]
+        flat = arr.reshape(-1)
+        for i in rng.choice(flat.size, size=min(count, flat.size), replace=False):
+            e = 1e-6 * max(1.0, abs(flat[i]))
+            o = flat[i]
+            flat[i] = o + e
+            fp = obj()
+            flat[i] = o - e
+            fm = obj()
+            flat[i] = o
+            fd = (fp - fm) / (2 * e)
+            an = grads["d" + name].reshape(-1)[i]
+            assert abs(an - fd) <= tol * max(1.0, abs(fd)), (name, i, an, fd)
+            checked += 1
+    return checked
+
+
+@pytest.mark.parametrize("softplus,gated,with_fs", [(True, True, True), (False, False, False), (True, False, True)])
+def test_trap_gradients_match_central_differences_of_c_oracle(softplus, gated, with_fs):
+    rng = np.random.default_rng(80 + softplus + 2 * gated + 4 * with_fs)
+    batch, L, dim, N = 2, 7, 3, 4
+    x = _inputs(rng, batch, L, dim, N, gated=gated)
+    if not gated:
+        x["D"] = None
+        x["delta_bias"] = None
+    if not softplus:
+        x["delta"] = np.abs(x["delta"]) + 0.05
+    x["initial_state"] = rng.standard_normal((batch, dim, N))
+    dy = rng.standard_normal((batch, L, dim))
+    dfs = rng.standard_normal((batch, dim, N)) if with_fs else None
+
+    def obj():
+        y, fs = R.scan_trap_fwd_ex(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                                   delta_bias=x["delta_bias"], softplus=softplus, initial_state=x["initial_state"])
+        return float(np.sum(y * dy) + (0.0 if dfs is None else np.sum(fs * dfs)))
+
+    g = OB.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                    softplus=softplus, dfinal_state=dfs, initial_state=x["initial_state"], rule="trap")
+    names = [n for n in ["u", "delta", "A", "B", "C", "D", "z", "delta_bias", "initial_state"] if x.get(n) is not None]
+    assert _fd_check(rng, x, names, g, obj) >= 30
+
+
+@pytest.mark.parametrize("cuts", [[0, 3, 3, 9, 10], [0, 1, 5, 10]])
+def test_trap_packed_gradients_match_central_differences(cuts):
+    """Packed sequences under the trapezoidal rule: each sequence's first token has no previous input."""
+    rng = np.random.default_rng(90 + len(cuts))
+    L, dim, N = 10, 3, 4
+    x = _inputs(rng, 1, L, dim, N)
+    nseq = len(cuts) - 1
+    x["initial_state"] = rng.standard_normal((nseq, dim, N))
+    dy = rng.standard_normal((1, L, dim))
+    dfs = rng.standard_normal((nseq, dim, N))
+    cu = np.asarray(cuts, dtype=np.int64)
+
+    def obj():
+        y, fs = R.scan_trap_fwd_ex(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                                   delta_bias=x["delta_bias"], initial_state=x["initial_state"], cu_seqlens=cu)
+        return float(np.sum(y * dy) + np.sum(fs * dfs))
+
+    g = OB.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                    dfinal_state=dfs, initial_state=x["initial_state"], cu_seqlens=cu, rule="trap")
+    names = ["u", "delta", "A", "B", "C", "D", "z", "delta_bias", "initial_state"]
+    assert _fd_check(rng, x, names, g, obj) >= 40
+
+
+def test_trap_differs_from_euler_gradients():
+    """The rule matters: the two recurrences' gradients differ on the same inputs (a guard against the
+    rule argument being ignored)."""
+    rng = np.random.default_rng(95)
+    x = _inputs(rng, 1, 6, 2, 3)
+    dy = rng.standard_normal((1, 6, 2))
+    ge = OB.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"])
+    gt = OB.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                     rule="trap")
+    assert _rel(gt["du"], ge["du"]) > 1e-3 and _rel(gt["dB"], ge["dB"]) > 1e-3
