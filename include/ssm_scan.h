@@ -319,6 +319,33 @@ ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, cons
                           int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bytes of device workspace that ssm_scan_trap_bwd needs (arguments as
+ * ssm_scan_bwd_workspace_size; there is no chained plan, so no carried
+ * adjoints).  Returns 0 for arguments ssm_scan_trap_bwd would reject. */
+size_t ssm_scan_trap_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int64_t nseq,
+                                        ssm_dtype_t dt);
+
+/* Backward of ssm_scan_trap_fwd: the gradients of
+ *     sum(y * dy) + sum(final_state * dfinal_state)
+ * for Mamba-3's trapezoidal three-term recurrence ("The State That Must
+ * Remember Everything", Part 7, "Mamba-3 (2026)", item 1) with the
+ * coefficients ssm_scan_trap_fwd uses (alpha_t = exp(delta_t A), beta_t =
+ * delta_t/2 alpha_t, gamma_t = delta_t/2, no previous input at the first
+ * token of a batch row or packed sequence).  The states are recomputed from
+ * checkpoints of the same recurrence, not stored by the forward.  Arguments,
+ * outputs, layouts, packed sequences, dstate range and errors as
+ * ssm_scan_bwd; the workspace must hold ssm_scan_trap_bwd_workspace_size()
+ * bytes.  Every tile of 64 channels runs in one workgroup (no chained
+ * plan). */
+ssm_status_t ssm_scan_trap_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                               const void* dy, const float* dfinal_state, const float* initial_state,
+                               const int64_t* cu_seqlens, int64_t nseq,
+                               void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                               float* ddelta_bias, float* dinitial_state,
+                               int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Outcome of the kernels of the last call that used `workspace` (any entry
  * point taking a workspace): SSM_OK, or SSM_ERR_HANDOFF_TIMEOUT when a chained
  * hand-off wait of that call ran out (its dependent outputs are then NaN).

@@ -144,8 +144,20 @@ __device__ __forceinline__ void quad_allsums4(float& a, float& b, float& c, floa
 
 // WIDE: 0 for all states in one launch; 1 for the first half of wide states
 // (partials out), 2 for the second (partials in, finished gradients out).
-template <class IO, int NPL, int G, int WIDE = 0>
+//
+// RULE = kRuleTrap: the backward of the trapezoidal recurrence
+//   h_t = alpha_t q_t + (delta_t/2) u_t B_t,  q_t = h_{t-1} + (delta_t/2) u_{t-1} B_{t-1}
+// (alpha_t = exp(delta_t A); no previous input at a recurrence's first
+// token).  With g_t = C_t dv_t + alpha_{t+1} g_{t+1} the adjoint of h_t:
+//   d delta_t = sum_n g_t (A alpha_t q_t + alpha_t (u_{t-1}/2) B_{t-1} + (u_t/2) B_t)
+//   dA       += g_t delta_t alpha_t q_t
+//   e_t       = (delta_t/2) g_t + (delta_{t+1}/2) alpha_{t+1} g_{t+1}
+//   du_t      = sum_n B_t e_t,   dB_t += u_t e_t,   dC_t += dv_t h_t
+// The staged pair per token is (delta, u); R forms the whole d delta and du
+// partials of its states, since they need the neighbouring tokens.
+template <class IO, int NPL, int G, int WIDE = 0, int RULE = kRuleEuler>
 __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
+  constexpr bool TRAP = RULE == kRuleTrap;
   constexpr int TB = kBwdTB;
   constexpr int NPAD = NPL * G;
   constexpr int RPT = TB / G;               // element rows per thread
@@ -254,6 +266,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   // next block down, dA, and this lane's dD, dbias terms
   float dhn[NPL], dAacc[NPL];
   float accD = 0.0f, accBias = 0.0f;
+  float nxt_d = 0.0f;  // trapezoidal rule: the step of the token after the block (zero past the stretch)
   auto start_from_final = [&]() {  // the gradient reaching the tile's final state
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
@@ -262,6 +275,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       dAacc[j] = 0.0f;
     }
     accD = accBias = 0.0f;
+    nxt_d = 0.0f;
   };
 
   // Two-slot pipeline over the blocks (last to first): the loads of block
@@ -276,6 +290,11 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
   // then out of range or unused, and its checkpoint index is clamped.
   Raw<IO, 1> qu[2][RPT], qd[2][RPT], qz[2][RPT], qg[2][RPT];
   float qrv[2][NRV], qhs[2][NPL];
+  // trapezoidal rule: u and B (this lane's states) of the token before the
+  // block; before the stretch they read zero (a recurrence's first token has
+  // no previous input)
+  Raw<IO, 1> qpu[TRAP ? 2 : 1];
+  float qpb[TRAP ? 2 : 1][NPL];
   auto load_block = [&](auto slotc, int k) __attribute__((always_inline)) {
     constexpr int S = decltype(slotc)::value;
     const int t0 = k * TB;
@@ -293,6 +312,12 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
       qd[S][i] = buf_load<IO, 1>(rs_d, off, 0);
       qz[S][i] = buf_load<IO, 1>(rs_z, off, 0);
       qg[S][i] = buf_load<IO, 1>(rs_dy, off, 0);
+    }
+    if constexpr (TRAP) {
+      qpu[S] = buf_load<IO, 1>(rs_u, (t0 - 1) * row_bytes + lane * ES, 0);
+#pragma unroll
+      for (int j = 0; j < NPL; ++j)
+        qpb[S][j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bc, ((t0 - 1) * 2 * NPL + j) * 4, 0, 0));
     }
   };
   auto process_block = [&](auto slotc, int k) __attribute__((always_inline)) {
@@ -328,7 +353,8 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
         gp = sz * __builtin_fmaf(zf, 1.0f - sz, 1.0f);  // SiLU'(z) = s (1 + z (1 - s))
       }
       const float dv = live ? gf * g : 0.0f;
-      sDU[row][lane] = make_float2(dl, dl * uf);
+      // (delta, delta*u), or (delta, u) under the trapezoidal rule (u zero past the stretch)
+      sDU[row][lane] = make_float2(dl, TRAP ? (live ? uf : 0.0f) : dl * uf);
       sDV[row][lane] = dv;
       eu[i] = uf;
       edl[i] = dl;
@@ -341,11 +367,14 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
 
     // ---- F: recompute the block's states from the checkpoint
     float hs[TB][NPL], as[KEEP_A ? TB : 1][NPL];
-    float2 kdd[KEEP_A ? TB : 1];  // (delta, delta*u) of the block's tokens, kept from F for R where registers allow
+    float2 kdd[KEEP_A ? TB : 1];  // the block's staged pairs, kept from F for R where registers allow
+    float u_before = 0.0f;        // trapezoidal rule: u of the token before the block
+    if constexpr (TRAP) unpack<IO, 1>(qpu[S], &u_before);
     {
       float h[NPL];
 #pragma unroll
       for (int j = 0; j < NPL; ++j) h[j] = hst[j];
+      float up = u_before;  // trapezoidal rule: the previous token's u
       [&]<int... T>(std::integer_sequence<int, T...>) {
         (([&] {
            constexpr int t = T;
@@ -357,7 +386,16 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
                 constexpr int j = J;
                 constexpr int fb = t * 2 * NPL + j, fc = fb + NPL;
                 const float a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
-                h[j] = __builtin_fmaf(a, h[j], dd.y * row_bcast<fb % 16>(rv[fb / 16]));
+                if constexpr (TRAP) {
+                  // q = h_{t-1} + (delta_t/2) u_{t-1} B_{t-1};  h_t = alpha q + (delta_t/2) u_t B_t
+                  const float w1 = 0.5f * dd.x * up;
+                  float q;
+                  if constexpr (t > 0) q = fmac_row_bcast<(fb - 2 * NPL) % 16>(h[j], rv[(fb - 2 * NPL) / 16], w1);
+                  else q = __builtin_fmaf(w1, qpb[S][j], h[j]);
+                  h[j] = __builtin_fmaf(a, q, (0.5f * dd.x * dd.y) * row_bcast<fb % 16>(rv[fb / 16]));
+                } else {
+                  h[j] = __builtin_fmaf(a, h[j], dd.y * row_bcast<fb % 16>(rv[fb / 16]));
+                }
                 hs[t][j] = h[j];
                 if constexpr (KEEP_A) as[t][j] = a;
                 if constexpr (j == 0) yp = row_bcast<fc % 16>(rv[fc / 16]) * h[0];
@@ -367,6 +405,7 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
            }(std::make_integer_sequence<int, NPL>{});
            if constexpr (SEP) sYP[w][t][lane] = yp;
            else sYS[w][t][lane].x = yp;
+           up = dd.y;
          }()),
          ...);
       }(std::make_integer_sequence<int, TB>{});
@@ -405,6 +444,14 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
          else dd = sDU[t][lane];
          float s1 = 0.0f, s2 = 0.0f;
          float pb[NPL], pc[NPL];
+         // trapezoidal rule: u of the token before, the step of the token after
+         float up = 0.0f, dn = 0.0f, s3 = 0.0f, s5 = 0.0f;
+         if constexpr (TRAP) {
+           if constexpr (t > 0) up = KEEP_A ? kdd[t - 1].y : sDU[t - 1][lane].y;
+           else up = u_before;
+           if constexpr (t + 1 < TB) dn = KEEP_A ? kdd[t + 1].x : sDU[t + 1][lane].x;
+           else dn = nxt_d;
+         }
          static_assert(NPL % 2 == 0, "row sums go four values at a time");
          [&]<int... J>(std::integer_sequence<int, J...>) {
            (([&] {
@@ -418,13 +465,33 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
               float a;
               if constexpr (KEEP_A) a = as[t][j];
               else a = __builtin_amdgcn_exp2f(dd.x * A2[j]);
-              const float ta = dh * hp * a;
-              s1 = __builtin_fmaf(ta, An[j], s1);
-              s2 = fmac_row_bcast<fb % 16>(s2, rv[fb / 16], dh);
-              dAacc[j] = __builtin_fmaf(ta, dd.x, dAacc[j]);
-              pb[j] = dh * dd.y;
-              pc[j] = dv * hs[t][j];
-              dhn[j] = a * dh;
+              if constexpr (TRAP) {
+                // dh is g_t; dhn[j] still holds alpha_{t+1} g_{t+1}
+                constexpr int fp = fb - 2 * NPL;  // B_{t-1} within the block's records (t > 0)
+                const float w1 = 0.5f * dd.x * up;
+                float q;
+                if constexpr (t > 0) q = fmac_row_bcast<fp % 16>(hp, rv[fp / 16], w1);
+                else q = __builtin_fmaf(w1, qpb[S][j], hp);
+                const float ga = dh * a;
+                const float ta = ga * q;
+                s1 = __builtin_fmaf(ta, An[j], s1);
+                dAacc[j] = __builtin_fmaf(ta, dd.x, dAacc[j]);
+                if constexpr (t > 0) s3 = fmac_row_bcast<fp % 16>(s3, rv[fp / 16], ga);
+                else s3 = __builtin_fmaf(ga, qpb[S][j], s3);
+                s2 = fmac_row_bcast<fb % 16>(s2, rv[fb / 16], dh);
+                s5 = fmac_row_bcast<fb % 16>(s5, rv[fb / 16], dhn[j]);
+                pb[j] = __builtin_fmaf(0.5f * dn * dd.y, dhn[j], (0.5f * dd.x * dd.y) * dh);
+                pc[j] = dv * hs[t][j];
+                dhn[j] = ga;
+              } else {
+                const float ta = dh * hp * a;
+                s1 = __builtin_fmaf(ta, An[j], s1);
+                s2 = fmac_row_bcast<fb % 16>(s2, rv[fb / 16], dh);
+                dAacc[j] = __builtin_fmaf(ta, dd.x, dAacc[j]);
+                pb[j] = dh * dd.y;
+                pc[j] = dv * hs[t][j];
+                dhn[j] = a * dh;
+              }
             }()),
             ...);
          }(std::make_integer_sequence<int, NPL>{});
@@ -438,10 +505,14 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
            sRB[t][n0 + j][lane >> 2] = pb[j];
            sRC[t][n0 + j][lane >> 2] = pc[j];
          }
-         sYS[w][t][lane] = make_float2(s1, s2);
+         if constexpr (TRAP)  // this wavefront's parts of d delta_t and du_t
+           sYS[w][t][lane] = make_float2(s1 + 0.5f * (up * s3 + dd.y * s2), 0.5f * (dd.x * s2 + dn * s5));
+         else
+           sYS[w][t][lane] = make_float2(s1, s2);
        }()),
        ...);
     }(std::make_integer_sequence<int, TB>{});
+    if constexpr (TRAP) nxt_d = KEEP_A ? kdd[0].x : sDU[0][lane].x;  // for the block before this one
     __syncthreads();
 
     // ---- E2: du, ddelta_raw of the elements; the tile's dB, dC partials
@@ -464,8 +535,10 @@ __global__ void __launch_bounds__(64 * G) scan_bwd_kernel(BwdParams p) {
         S1 += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_ps1, poff, 0, 0));
         S2 += __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_ps2, poff, 0, 0));
       }
-      const float dDelta = __builtin_fmaf(eu[i], S2, S1);
-      const float duv = __builtin_fmaf(edl[i], S2, Dd * edv[i]);
+      // two-term rule: d delta = sum t_a A + u sum dh B, du = delta sum dh B + D dv;
+      // trapezoidal rule: R summed the whole parts
+      const float dDelta = TRAP ? S1 : __builtin_fmaf(eu[i], S2, S1);
+      const float duv = TRAP ? __builtin_fmaf(Dd, edv[i], S2) : __builtin_fmaf(edl[i], S2, Dd * edv[i]);
       const float ddr = dDelta * esx[i];
       const int off = elive[i] ? (t0 + row) * row_bytes + lane * ES : 0x7ffffff0;
       buf_store<IO, 1>(rs_du, off, 0, &duv);

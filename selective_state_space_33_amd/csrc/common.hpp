@@ -210,6 +210,10 @@ __device__ __forceinline__ float step_of(float x, float sp_k, float sp_lo) {
 // (word 0, which the host reads back with ssm_workspace_status) and the piece
 // goes on from NaN, so every kernel ends and the outputs that depend on the
 // lost hand-off show the failure.
+// Discretisation rules of the scan kernels (forward and backward).
+constexpr int kRuleEuler = 0;    // h_t = exp(delta_t A) h_{t-1} + delta_t B_t u_t
+constexpr int kRuleTrap = 1;     // the trapezoidal three-term recurrence (Mamba-3), see scan_kernel
+
 constexpr unsigned kSpinLimit = 1u << 18;
 constexpr unsigned kStatusHandoffTimeout = 1u;
 

@@ -117,9 +117,6 @@ constexpr int kModeChained = 2;  // one workgroup per CU: a whole tile with one 
 constexpr int kModeCkpt = 3;     // whole tiles, no readout: the state entering every block (for the backward pass)
 constexpr int kModeChainedCkpt = 4;  // kModeChained's plan with kModeCkpt's work (no readout, checkpoints)
 
-// Discretisation rules of scan_kernel.
-constexpr int kRuleEuler = 0;    // h_t = exp(delta_t A) h_{t-1} + delta_t B_t u_t
-constexpr int kRuleTrap = 1;     // the trapezoidal three-term recurrence (Mamba-3), see scan_kernel
 
 // Tokens per staged block: 16, or 32 where one workgroup has the CU to
 // itself (the block's barrier is then paid half as often, and the staging
@@ -238,7 +235,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   constexpr bool CKPT = MODE == kModeCkpt || MODE == kModeChainedCkpt;
   static_assert(HAS_FULL || G <= TB_, "stop-flag words in the partial-readout buffer");
   constexpr bool TRAP = RULE == kRuleTrap;
-  static_assert(!TRAP || !CKPT, "the backward's checkpoints are of the two-term rule");
+  static_assert(!TRAP || MODE != kModeChainedCkpt, "the trapezoidal backward runs without the chained plan");
   // fp32 storage, two-term rule, outside the backward's checkpoint launches:
   // B and C come straight from the caller's rows, B_t[n] at float t*N + n,
   // instead of from packed records.  A block's record registers then hold its
@@ -638,9 +635,12 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       static_assert((S + kPD + 1) % kRing == Sm1, "ring");
       IC<P> parc;
       if constexpr (CKPT) {
-        // the state entering block k (the padding blocks at the end have room too)
+        // the state entering block k (the padding blocks at the end have room too); under the
+        // trapezoidal rule the registers hold h minus the previous token's delta (u/2) B (zero at a
+        // pass's start), which the checkpoint adds back
 #pragma unroll
-        for (int j = 0; j < NPL; ++j) ckpt_row[static_cast<int64_t>(k) * 64 * NPAD + j] = h[j];
+        for (int j = 0; j < NPL; ++j)
+          ckpt_row[static_cast<int64_t>(k) * 64 * NPAD + j] = TRAP ? __builtin_fmaf(pv_d * pv_hx, Bprev[j], h[j]) : h[j];
       }
       fetch_dd(parc, IC<0>{}, 0);
       if (k > k_begin) epilogue(IC<1 - P>{}, IC<Sm1>{}, k - 1);

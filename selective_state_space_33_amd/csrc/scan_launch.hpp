@@ -18,7 +18,7 @@ namespace ssm {
 template <class IO, int MODE, int RULE = kRuleEuler>
 hipError_t launch_scan(int npl, int G, int vw, int tb, const ScanParams& p, dim3 grid, hipStream_t s);
 
-// Instantiated (each in its own translation unit) for these sixteen combinations.
+// Instantiated (each in its own translation unit) for these eighteen combinations.
 extern template hipError_t launch_scan<F32, kModeFull>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<F32, kModeAgg>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
 extern template hipError_t launch_scan<F32, kModeChained>(int, int, int, int, const ScanParams&, dim3, hipStream_t);
@@ -44,6 +44,10 @@ extern template hipError_t launch_scan<BF16, kModeAgg, kRuleTrap>(int, int, int,
                                                                  hipStream_t);
 extern template hipError_t launch_scan<BF16, kModeChained, kRuleTrap>(int, int, int, int, const ScanParams&, dim3,
                                                                      hipStream_t);
+extern template hipError_t launch_scan<F32, kModeCkpt, kRuleTrap>(int, int, int, int, const ScanParams&, dim3,
+                                                                 hipStream_t);
+extern template hipError_t launch_scan<BF16, kModeCkpt, kRuleTrap>(int, int, int, int, const ScanParams&, dim3,
+                                                                  hipStream_t);
 
 // Variants (states per lane, wavefronts).  Each exists with its preferred
 // prologue width (channels per thread: 4 up to 4 wavefronts, 2 for 8, 1 for

@@ -59,7 +59,7 @@ struct BwdPlan {
 // no chained plan; each sequence's checkpoints start kPackedCkptSlack blocks
 // further per sequence before it, so a tile column holds Lp / 16 +
 // kPackedCkptSlack * nseq of them.
-BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t nseq) {
+BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t nseq, int rule) {
   BwdPlan pl;
   pl.npl = N <= 16 ? 2 : 4;
   pl.G = 8;
@@ -77,7 +77,8 @@ BwdPlan plan_bwd(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t nseq)
   pl.Kc = 1;
   pl.ck_len = 0;
   const char* env = getenv("SSM_BWD_CHAINED");
-  const bool chained_ok = !(env && atoi(env) == 0) && pl.nseq == 0 && !pl.wide;
+  // (the trapezoidal rule's backward runs one workgroup per tile: no chained plan)
+  const bool chained_ok = !(env && atoi(env) == 0) && pl.nseq == 0 && !pl.wide && rule == kRuleEuler;
   const int64_t kBwdNumCU = device_cu_count();
   if (chained_ok && pl.T > kBwdNumCU && 2 * (pl.T - kBwdNumCU) <= kBwdNumCU) {
     const int64_t r = pl.T - kBwdNumCU;
@@ -143,7 +144,7 @@ bool plan_fits(const BwdPlan& pl, int64_t L, int64_t dim) {
   return !pl.wide || rows_fit(L, dim, 4);
 }
 
-template <class IO>
+template <class IO, int RULE>
 hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const void* C, float* bc, ScanParams sp,
                    BwdParams bp, void* dB, void* dC, float* dA, float* dD, float* dbias, int vw, hipStream_t s) {
   const int64_t npad = static_cast<int64_t>(pl.npl) * pl.g_total;
@@ -163,23 +164,27 @@ hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (pl.n_split > 0)
-    e = launch_scan<IO, kModeChainedCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.n_long)), s);
-  else if (pl.wide)  // the forward's 4-per-lane, 16-wavefront variant covers all 64 states
-    e = launch_scan<IO, kModeCkpt>(pl.npl, pl.g_total, 1, kBwdTB, sp, dim3(static_cast<unsigned>(pl.T)), s);
-  else
-    e = launch_scan<IO, kModeCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.T)), s);
+  if constexpr (RULE == kRuleEuler) {
+    if (pl.n_split > 0)
+      e = launch_scan<IO, kModeChainedCkpt>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.n_long)), s);
+  }
+  if (pl.n_split == 0) {
+    if (pl.wide)  // the forward's 4-per-lane, 16-wavefront variant covers all 64 states
+      e = launch_scan<IO, kModeCkpt, RULE>(pl.npl, pl.g_total, 1, kBwdTB, sp, dim3(static_cast<unsigned>(pl.T)), s);
+    else
+      e = launch_scan<IO, kModeCkpt, RULE>(pl.npl, pl.G, vw, kBwdTB, sp, dim3(static_cast<unsigned>(pl.T)), s);
+  }
   if (e != hipSuccess) return e;
   const dim3 bgrid(static_cast<unsigned>(pl.n_split > 0 ? pl.n_long : pl.T));
   if (pl.wide) {  // one launch per half of the states; the second finishes the per-(token, channel) gradients
     bp.n_base = 0;
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8, 1>), bgrid, dim3(512), 0, s, bp);
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8, 1, RULE>), bgrid, dim3(512), 0, s, bp);
     bp.n_base = static_cast<int>(kBwdOneLaunchState);
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8, 2>), bgrid, dim3(512), 0, s, bp);
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8, 2, RULE>), bgrid, dim3(512), 0, s, bp);
   } else if (pl.npl == 2) {
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, 2, 8>), bgrid, dim3(512), 0, s, bp);
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, 2, 8, 0, RULE>), bgrid, dim3(512), 0, s, bp);
   } else {
-    hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8>), bgrid, dim3(512), 0, s, bp);
+    hipLaunchKernelGGL((scan_bwd_kernel<IO, 4, 8, 0, RULE>), bgrid, dim3(512), 0, s, bp);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -201,26 +206,41 @@ hipError_t run_bwd(const BwdPlan& pl, const BwdLayout& lay, const void* B, const
 
 using namespace ssm;
 
-extern "C" size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int64_t nseq,
-                                               ssm_dtype_t dt) {
+namespace ssm {
+namespace {
+size_t bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int64_t nseq, ssm_dtype_t dt,
+                          int rule) {
   if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > kBwdMaxState || batch > kBwdMaxBatch) return 0;
   if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return 0;
   if (nseq > 0 && batch != 1) return 0;
   const int64_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
   if (!rows_fit(L, dim, es)) return 0;
-  const BwdPlan pl = plan_bwd(batch, L, dim, dstate, nseq);
+  const BwdPlan pl = plan_bwd(batch, L, dim, dstate, nseq, rule);
   if (!plan_fits(pl, L, dim)) return 0;
   return bwd_layout(pl, batch, L, dim).total;
 }
+}  // namespace
+}  // namespace ssm
 
-extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
-                                     const float* D, const void* z, const float* delta_bias, int softplus_flag,
-                                     const void* dy, const float* dfinal_state, const float* initial_state,
-                                     const int64_t* cu_seqlens, int64_t nseq, void* du,
-                                     void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
-                                     float* ddelta_bias, float* dinitial_state, int64_t batch,
-                                     int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt, void* workspace,
-                                     size_t workspace_bytes, hipStream_t stream) {
+extern "C" size_t ssm_scan_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate, int64_t nseq,
+                                               ssm_dtype_t dt) {
+  return bwd_workspace_size(batch, L, dim, dstate, nseq, dt, kRuleEuler);
+}
+
+extern "C" size_t ssm_scan_trap_bwd_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate,
+                                                    int64_t nseq, ssm_dtype_t dt) {
+  return bwd_workspace_size(batch, L, dim, dstate, nseq, dt, kRuleTrap);
+}
+
+namespace ssm {
+namespace {
+ssm_status_t scan_bwd_impl(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                           const float* D, const void* z, const float* delta_bias, int softplus_flag, const void* dy,
+                           const float* dfinal_state, const float* initial_state, const int64_t* cu_seqlens,
+                           int64_t nseq, void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                           float* ddelta_bias, float* dinitial_state, int64_t batch, int64_t L, int64_t dim,
+                           int64_t dstate, ssm_dtype_t dt, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream, int rule) {
   if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return SSM_ERR_INVALID_ARG;
   if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0) return SSM_ERR_INVALID_ARG;
   if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return SSM_ERR_INVALID_ARG;
@@ -234,7 +254,7 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
   if (cu_seqlens && (!is_aligned(cu_seqlens, 8) || batch != 1 || nseq <= 0)) return SSM_ERR_INVALID_ARG;
   if (dstate > kBwdMaxState || batch > kBwdMaxBatch) return SSM_ERR_UNSUPPORTED;
   if (!rows_fit(L, dim, static_cast<int64_t>(es))) return SSM_ERR_UNSUPPORTED;
-  const BwdPlan pl = plan_bwd(batch, L, dim, dstate, cu_seqlens ? nseq : 0);
+  const BwdPlan pl = plan_bwd(batch, L, dim, dstate, cu_seqlens ? nseq : 0, rule);
   if (!plan_fits(pl, L, dim)) return SSM_ERR_UNSUPPORTED;
   if (pl.T > 0x7fffffffLL || batch * (pl.Lp / kPackT) > 0x7fffffffLL || batch * L * dstate / 256 > 0x7fffffffLL)
     return SSM_ERR_UNSUPPORTED;
@@ -359,9 +379,42 @@ extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const flo
 
   float* dD_out = D ? dD : nullptr;
   float* dbias_out = delta_bias ? ddelta_bias : nullptr;
-  const hipError_t e =
-      dt == SSM_DTYPE_F32
-          ? run_bwd<F32>(pl, lay, B, C, bc, sp, bp, dB, dC, dA, dD_out, dbias_out, vw, stream)
-          : run_bwd<BF16>(pl, lay, B, C, bc, sp, bp, dB, dC, dA, dD_out, dbias_out, vw, stream);
+  hipError_t e;
+  if (rule == kRuleTrap)
+    e = dt == SSM_DTYPE_F32
+            ? run_bwd<F32, kRuleTrap>(pl, lay, B, C, bc, sp, bp, dB, dC, dA, dD_out, dbias_out, vw, stream)
+            : run_bwd<BF16, kRuleTrap>(pl, lay, B, C, bc, sp, bp, dB, dC, dA, dD_out, dbias_out, vw, stream);
+  else
+    e = dt == SSM_DTYPE_F32
+            ? run_bwd<F32, kRuleEuler>(pl, lay, B, C, bc, sp, bp, dB, dC, dA, dD_out, dbias_out, vw, stream)
+            : run_bwd<BF16, kRuleEuler>(pl, lay, B, C, bc, sp, bp, dB, dC, dA, dD_out, dbias_out, vw, stream);
   return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+}  // namespace
+}  // namespace ssm
+
+extern "C" ssm_status_t ssm_scan_bwd(const void* u, const void* delta, const float* A, const void* B, const void* C,
+                                     const float* D, const void* z, const float* delta_bias, int softplus_flag,
+                                     const void* dy, const float* dfinal_state, const float* initial_state,
+                                     const int64_t* cu_seqlens, int64_t nseq, void* du,
+                                     void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                                     float* ddelta_bias, float* dinitial_state, int64_t batch,
+                                     int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus_flag, dy, dfinal_state, initial_state,
+                       cu_seqlens, nseq, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, batch, L, dim,
+                       dstate, dt, workspace, workspace_bytes, stream, kRuleEuler);
+}
+
+extern "C" ssm_status_t ssm_scan_trap_bwd(const void* u, const void* delta, const float* A, const void* B,
+                                          const void* C, const float* D, const void* z, const float* delta_bias,
+                                          int softplus_flag, const void* dy, const float* dfinal_state,
+                                          const float* initial_state, const int64_t* cu_seqlens, int64_t nseq,
+                                          void* du, void* ddelta, float* dA, void* dB, void* dC, float* dD, void* dz,
+                                          float* ddelta_bias, float* dinitial_state, int64_t batch, int64_t L,
+                                          int64_t dim, int64_t dstate, ssm_dtype_t dt, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream) {
+  return scan_bwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus_flag, dy, dfinal_state, initial_state,
+                       cu_seqlens, nseq, du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, batch, L, dim,
+                       dstate, dt, workspace, workspace_bytes, stream, kRuleTrap);
 }

@@ -33,7 +33,8 @@ SSM_DTYPE_F32, SSM_DTYPE_BF16 = 0, 1
 EXPORTED = ("ssm_scan_workspace_size", "ssm_scan_fwd", "ssm_scan_fwd_noalloc", "ssm_scan_fwd_ex_workspace_size", "ssm_scan_fwd_ex",
             "ssm_scan_trap_fwd_workspace_size", "ssm_scan_trap_fwd", "ssm_ssd_fwd_workspace_size", "ssm_ssd_fwd",
             "ssm_state_update",
-            "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_workspace_status", "ssm_status_string")
+            "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_scan_trap_bwd_workspace_size", "ssm_scan_trap_bwd",
+            "ssm_workspace_status", "ssm_status_string")
 
 _lib = None
 _vp = ctypes.c_void_p
@@ -78,9 +79,12 @@ def lib() -> ctypes.CDLL:
         L.ssm_ssd_fwd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int]
         L.ssm_scan_bwd_workspace_size.restype = ctypes.c_size_t
         L.ssm_scan_bwd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int]
-        L.ssm_scan_bwd.restype = ctypes.c_int
-        L.ssm_scan_bwd.argtypes = ([_vp] * 8 + [ctypes.c_int] + [_vp] * 4 + [_i64] + [_vp] * 9 + [_i64] * 4 +
-                                   [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
+        for name in ("ssm_scan_bwd", "ssm_scan_trap_bwd"):
+            getattr(L, name).restype = ctypes.c_int
+            getattr(L, name).argtypes = ([_vp] * 8 + [ctypes.c_int] + [_vp] * 4 + [_i64] + [_vp] * 9 + [_i64] * 4 +
+                                         [ctypes.c_int, _vp, ctypes.c_size_t, _vp])
+        L.ssm_scan_trap_bwd_workspace_size.restype = ctypes.c_size_t
+        L.ssm_scan_trap_bwd_workspace_size.argtypes = [_i64] * 5 + [ctypes.c_int]
         L.ssm_workspace_status.restype = ctypes.c_int
         L.ssm_workspace_status.argtypes = [_vp, ctypes.c_size_t, _vp]
         L.ssm_status_string.restype = ctypes.c_char_p
@@ -336,15 +340,17 @@ def ssm_scan_fwd_ex_workspace_size(batch: int, L: int, dim: int, dstate: int, ns
     return int(lib().ssm_scan_fwd_ex_workspace_size(batch, L, dim, dstate, nseq, _dtype_code(dtype)))
 
 
-def ssm_scan_bwd_workspace_size(batch: int, L: int, dim: int, dstate: int, dtype: torch.dtype, nseq: int = 0) -> int:
-    return int(lib().ssm_scan_bwd_workspace_size(batch, L, dim, dstate, nseq, _dtype_code(dtype)))
+def ssm_scan_bwd_workspace_size(batch: int, L: int, dim: int, dstate: int, dtype: torch.dtype, nseq: int = 0,
+                                trapezoid: bool = False) -> int:
+    fn = lib().ssm_scan_trap_bwd_workspace_size if trapezoid else lib().ssm_scan_bwd_workspace_size
+    return int(fn(batch, L, dim, dstate, nseq, _dtype_code(dtype)))
 
 
 def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus: bool = True,
                  dfinal_state=None, initial_state=None, want_dinitial_state: bool = False, cu_seqlens=None,
-                 workspace=None, stream=None, check_status: bool = False):
+                 workspace=None, stream=None, check_status: bool = False, trapezoid: bool = False):
     """Backward of ssm_scan_fwd (or ssm_scan_fwd_ex) on the GPU: gradients of sum(y*dy) +
-    sum(final_state*dfinal_state).
+    sum(final_state*dfinal_state).  trapezoid=True: the backward of ssm_scan_trap_fwd (ssm_scan_trap_bwd).
 
     Same inputs as ssm_scan_fwd plus dy [batch, L, dim] (storage dtype) and dfinal_state
     [rows, dim, dstate] (float32, optional); cu_seqlens: int64 device offsets of packed sequences of batch
@@ -378,17 +384,18 @@ def ssm_scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplu
                  ddelta_bias=None if delta_bias is None else torch.empty_like(delta_bias),
                  dinitial_state=(torch.empty((rows, dim, dstate), dtype=torch.float32, device=dev)
                                  if (initial_state is not None or want_dinitial_state) else None))
-        need = ssm_scan_bwd_workspace_size(batch, L, dim, dstate, dt, nseq)
+        need = ssm_scan_bwd_workspace_size(batch, L, dim, dstate, dt, nseq, trapezoid=trapezoid)
         if workspace is None and need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    rc = lib().ssm_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+    name = "ssm_scan_trap_bwd" if trapezoid else "ssm_scan_bwd"
+    rc = getattr(lib(), name)(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
                             1 if softplus else 0, _ptr(dy), _ptr(dfinal_state), _ptr(initial_state),
                             _ptr(cu_seqlens), nseq, _ptr(g["du"]),
                             _ptr(g["ddelta"]), _ptr(g["dA"]), _ptr(g["dB"]), _ptr(g["dC"]), _ptr(g["dD"]),
                             _ptr(g["dz"]), _ptr(g["ddelta_bias"]), _ptr(g["dinitial_state"]), batch, L, dim, dstate,
                             code, _ptr(workspace), _ws_bytes(workspace), s.cuda_stream)
     if rc != SSM_OK:
-        raise SSMError(rc, "ssm_scan_bwd")
+        raise SSMError(rc, name)
     if check_status:
-        _check_status(workspace, s, "ssm_scan_bwd")
+        _check_status(workspace, s, name)
     return g

@@ -201,6 +201,16 @@ def test_bwd_workspace_size():
                                                                                                    0, F32)
 
 
+def test_trap_bwd_workspace_size():
+    L = ops.lib()
+    e = L.ssm_scan_bwd_workspace_size(2, 1000, 136, 16, 0, BF16)
+    t = L.ssm_scan_trap_bwd_workspace_size(2, 1000, 136, 16, 0, BF16)
+    assert t > 0 and t % 256 == 0 and t <= e   # no chained plan, so no carried adjoints
+    assert L.ssm_scan_trap_bwd_workspace_size(1, 1000, 136, 64, 3, F32) > 0   # wide states, packed sequences
+    assert L.ssm_scan_trap_bwd_workspace_size(2, 1000, 136, 65, 0, F32) == 0
+    assert L.ssm_scan_trap_bwd_workspace_size(2, 1000, 136, 16, 3, F32) == 0   # packed needs batch 1
+
+
 def _bwd(lib_, **kw):
     """Call ssm_scan_bwd with fake (never dereferenced) pointers; only rejection paths are used."""
     a = dict(u=0x1000, delta=0x2000, A=0x3000, B=0x4000, C=0x5000, D=None, z=None, bias=None, sp=1, dy=0x6000,
@@ -232,6 +242,16 @@ def _bwd(lib_, **kw):
 ])
 def test_bwd_rejects_bad_arguments_without_launching(kw, expect):
     assert _bwd(ops.lib(), **kw) == expect
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(u=None), INVALID), (dict(dy=None), INVALID), (dict(N=65), UNSUPPORTED), (dict(), INVALID),
+    (dict(ws=0x100000, wsb=256), INVALID), (dict(cu=0x8000, nseq=2, batch=2), INVALID),
+])
+def test_trap_bwd_rejects_bad_arguments_without_launching(kw, expect, monkeypatch):
+    lib_ = ops.lib()
+    monkeypatch.setattr(lib_, "ssm_scan_bwd", lib_.ssm_scan_trap_bwd)
+    assert _bwd(lib_, **kw) == expect
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
