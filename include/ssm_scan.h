@@ -137,6 +137,37 @@ ssm_status_t ssm_scan_fwd_noalloc(const void* u, const void* delta, const float*
                                   int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
                                   hipStream_t stream);
 
+/* Workspace for ssm_scan_fwd_structured: the header words, for bf16 storage B
+ * and C repacked as fp32 records (batch * L * 128 bytes, rounded up), and
+ * three arrays of n_tiles * K * 64 * ns floats for the chunks' fade-and-add
+ * pairs and carried-in states (n_tiles = batch * ceil(dim / 64), ns = 4, 8
+ * or 16 states per lane, K the chunks per tile: about 10 * CUs / n_tiles).
+ * Returns 0 for arguments the call would reject. */
+size_t ssm_scan_fwd_structured_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate,
+                                              ssm_dtype_t dt);
+
+/* ssm_scan_fwd_ex (without packed sequences) for the structured state matrix
+ *     A[d, n] = (n + 1) * A0[d],
+ * a specialisation that the caller asserts by passing A0 [dim] (fp32) in
+ * place of A: the fade of state n is then q^(n+1) with q = exp(delta_t
+ * A0[d]), so a token costs one exp per channel and the fades follow by
+ * repeated multiplication ("Mamba is attention all you really need, part 2",
+ * "Keeping the pad on the desk": sixteen numbers per channel, one fade per
+ * step; "The relay" for the chunk pairs).  The caller decides whether A has
+ * this form (for instance once per weight, on the host); the library does not
+ * inspect A.  The result equals ssm_scan_fwd_ex with that A up to fp32
+ * rounding (the powers round differently from separate exps).
+ *   dstate <= 16 (else SSM_ERR_UNSUPPORTED).  initial_state (NULL: zero):
+ *   [batch, dim, dstate] fp32.  Everything else (arguments, layouts,
+ *   ownership, errors) as ssm_scan_fwd; the workspace comes from
+ *   ssm_scan_fwd_structured_workspace_size.  The plan has no chained
+ *   hand-offs, so ssm_workspace_status always reports SSM_OK for it. */
+ssm_status_t ssm_scan_fwd_structured(const void* u, const void* delta, const float* A0, const void* B,
+                                     const void* C, const float* D, const void* z, const float* delta_bias,
+                                     int softplus_flag, const float* initial_state, void* y, float* final_state,
+                                     int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt,
+                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Workspace for ssm_scan_fwd_ex: for nseq <= 0 (no packed sequences) the same
  * as ssm_scan_workspace_size; for nseq > 0 packed sequences (batch must be 1)
  * the packed B/C records and the order in which the sequences are launched

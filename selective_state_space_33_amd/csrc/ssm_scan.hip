@@ -18,6 +18,7 @@
 #include "carry_kernel.hpp"
 #include "decode_kernel.hpp"
 #include "host_common.hpp"
+#include "lane_kernels.hpp"
 #include "order_kernel.hpp"
 #include "scan_launch.hpp"
 
@@ -322,8 +323,8 @@ hipError_t run_scan(const Plan& pl, const Layout& lay, const void* B, const void
     e = launch_scan<IO, kModeAgg, RULE>(pl.npl, pl.G, pl.vw, 16, p, grid_agg, s);
     if (e != hipSuccess) return e;
     const int64_t cols = static_cast<int64_t>(pl.n_split) * 64 * npad;
-    hipLaunchKernelGGL(carry_kernel, dim3(static_cast<unsigned>(ceil_div(cols, kCarryCols))), dim3(256), 0, s,
-                       static_cast<const float*>(p.aggP), static_cast<const float*>(p.aggS), p.carry,
+    hipLaunchKernelGGL(carry_kernel<kCarryRuns>, dim3(static_cast<unsigned>(ceil_div(cols, kCarryCols))), dim3(256),
+                       0, s, static_cast<const float*>(p.aggP), static_cast<const float*>(p.aggS), p.carry,
                        static_cast<int64_t>(pl.n_split), pl.Ks, npad, p.h0, static_cast<int64_t>(pl.n_long),
                        static_cast<int64_t>(pl.ntd), p.dim, p.N);
     e = hipGetLastError();
@@ -655,6 +656,201 @@ extern "C" ssm_status_t ssm_scan_fwd_noalloc(const void* u, const void* delta, c
   if (!ws) return SSM_ERR_HIP;
   return scan_fwd_impl(u, delta, A, B, C, D, z, delta_bias, softplus_flag, nullptr, nullptr, 0, y, final_state,
                        batch, L, dim, dstate, dt, ws, kScratchBytes, stream, kRuleEuler);
+}
+
+// ---- the structured-A forward: one channel per lane (lane_kernels.hpp)
+namespace ssm {
+namespace {
+
+constexpr int64_t kLaneQuantum = 2 * kLaneTG;  // chunk lengths: whole trips of the main loop (two groups)
+constexpr int64_t kLaneMinChunk = 64;          // never cut the sequence finer than this
+constexpr int64_t kLaneUnitsPerCU = 10;        // chunk units per CU: about 2.5 wavefronts per SIMD
+constexpr int64_t kLaneMaxDstate = 16;         // a lane holds all states of its channel
+constexpr int kLaneShortChain = 64;            // carries of at most this many pairs: one thread per column
+
+struct LanePlan {
+  int ns;             // states per lane: 4, 8 or 16
+  int ntd, n_tiles;   // 64-channel tiles per batch row, in all
+  int K;              // chunks per tile
+  int64_t chunk_len;
+  int64_t Lp;         // token rows of the packed B/C records per batch row
+  bool packed_bc;     // bf16 storage: B and C packed into fp32 records first
+};
+
+struct LaneLayout {
+  size_t words, bc, pairs, total;
+};
+
+// A tile (64 channels of one batch row) is one wavefront, so every tile is cut
+// into K chunks.  The passes are issue-bound and their units are equal, so a
+// pass takes about (units on the busiest SIMD) x (tokens per chunk); K is
+// chosen to minimise the pair pass (about 0.56 of a full-pass token each, one
+// unit fewer per tile) plus the full pass plus the carry's memory traffic,
+// with a single wavefront on a SIMD counted at 0.7 of the issue rate, chunks
+// of at least kLaneMinChunk tokens and chunk rows within 32-bit byte offsets.
+// SSM_LANE_K (environment) overrides K for tuning sweeps and tests.
+double lane_pass_cost(int64_t units, int64_t simds, int64_t chunk) {
+  if (units <= 0) return 0.0;
+  const int64_t w = ceil_div(units, simds);
+  return static_cast<double>(w * chunk) / (w >= 2 ? 1.0 : 0.7);
+}
+
+bool plan_lane(int64_t batch, int64_t L, int64_t dim, int64_t N, int64_t es, LanePlan* pl) {
+  pl->ns = N <= 4 ? 4 : (N <= 8 ? 8 : 16);
+  pl->ntd = static_cast<int>(ceil_div(dim, 64));
+  const int64_t T = batch * pl->ntd;
+  if (T > 0x7fffffffLL) return false;
+  pl->n_tiles = static_cast<int>(T);
+  // a chunk and the padding of its last trip within 2^31 bytes of token rows (and, read directly, of B rows)
+  const int64_t row = (es == 4 && N * 4 > dim * es) ? N * 4 : dim * es;
+  const int64_t cmax = (0x7fffffffLL / row - 2 * kLaneQuantum) / kLaneQuantum * kLaneQuantum;
+  if (cmax < kLaneQuantum) return false;
+  const int64_t simds = 4 * device_cu_count();
+  int64_t kmax = ceil_div(L, kLaneMinChunk) < kMaxChunks ? ceil_div(L, kLaneMinChunk) : kMaxChunks;
+  const int64_t kmin = ceil_div(L, cmax);
+  if (kmax < kmin) kmax = kmin;
+  // about 0.18 us per full-pass token of one wavefront; the carry moves 3 floats per (chunk, lane, state)
+  constexpr double kUsPerToken = 0.18, kBytesPerUs = 5.0e6, kCarryLaunchUs = 4.0;
+  int64_t best_k = kmin;
+  double best = -1.0;
+  for (int64_t K = kmin; K <= kmax; ++K) {
+    const int64_t chunk = ceil_div(ceil_div(L, K), kLaneQuantum) * kLaneQuantum;
+    if (chunk > cmax || ceil_div(L, chunk) != K) continue;
+    double cost = lane_pass_cost(T * K, simds, chunk) + 0.56 * lane_pass_cost(T * (K - 1), simds, chunk);
+    if (K > 1) cost += (12.0 * T * K * 64 * pl->ns / kBytesPerUs + kCarryLaunchUs) / kUsPerToken;
+    if (best < 0.0 || cost < best) {
+      best = cost;
+      best_k = K;
+    }
+  }
+  int64_t K = best_k;
+  const char* ke = getenv("SSM_LANE_K");
+  if (ke && atoi(ke) > 0) K = atoi(ke) < kmin ? kmin : atoi(ke);
+  if (K > kMaxChunks) K = kMaxChunks;
+  int64_t chunk = ceil_div(ceil_div(L, K), kLaneQuantum) * kLaneQuantum;
+  if (chunk > cmax) chunk = cmax;
+  K = ceil_div(L, chunk);
+  if (K > kMaxChunks || T * K > 0x7fffffffLL) return false;
+  pl->K = static_cast<int>(K);
+  pl->chunk_len = chunk;
+  pl->Lp = ceil_div(L, kTrip) * kTrip;
+  pl->packed_bc = es == 2;
+  return true;
+}
+
+LaneLayout lane_layout(const LanePlan& pl, int64_t batch) {
+  LaneLayout l;
+  l.words = align256(static_cast<size_t>(kHeaderWords) * sizeof(unsigned));
+  l.bc = pl.packed_bc ? align256((static_cast<size_t>(batch) * pl.Lp + kTBMax) * 32 * sizeof(float)) : 0;
+  l.pairs = pl.K > 1 ? align256(static_cast<size_t>(pl.n_tiles) * pl.K * 64 * pl.ns * sizeof(float)) : 0;
+  l.total = l.words + l.bc + 3 * l.pairs;  // chunk fades P, chunk states S, carried-in states
+  return l;
+}
+
+size_t structured_workspace(int64_t batch, int64_t L, int64_t dim, int64_t dstate, ssm_dtype_t dt) {
+  if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > kLaneMaxDstate || batch > kMaxBatch) return 0;
+  if (dt != SSM_DTYPE_F32 && dt != SSM_DTYPE_BF16) return 0;
+  LanePlan pl;
+  if (!plan_lane(batch, L, dim, dstate, dt == SSM_DTYPE_F32 ? 4 : 2, &pl)) return 0;
+  return lane_layout(pl, batch).total;
+}
+
+template <class IO>
+hipError_t run_lane(const LanePlan& pl, const LaneLayout& lay, unsigned* words, const LaneParams& p, hipStream_t s) {
+  if (pl.packed_bc) {
+    // fp32 records of 16 states (zero past dstate): B_t then C_t; also zeroes the header words
+    const dim3 pgrid(static_cast<unsigned>(p.batch * (pl.Lp / kPackT)));
+    hipLaunchKernelGGL((pack_bc_kernel<IO, 16>), pgrid, dim3(256), 0, s, p.Braw, p.Craw, const_cast<float*>(p.bc),
+                       p.batch, p.L, pl.Lp, p.N, 1, words, kHeaderWords, static_cast<float*>(nullptr));
+  } else {
+    hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(256), 0, s, words, kHeaderWords);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (pl.K > 1) {
+    e = launch_lane<IO>(pl.ns, true, false, p, s);
+    if (e != hipSuccess) return e;
+    // short chains: one thread walks a whole column; long ones are cut into runs
+    const int64_t cols = static_cast<int64_t>(pl.n_tiles) * 64 * pl.ns;
+    const bool one = pl.K - 1 <= kLaneShortChain;
+    const dim3 cgrid(static_cast<unsigned>(ceil_div(cols, one ? 256 : kCarryCols)));
+    if (one)
+      hipLaunchKernelGGL(carry_kernel<1>, cgrid, dim3(256), 0, s, static_cast<const float*>(p.aggP),
+                         static_cast<const float*>(p.aggS), p.carry, static_cast<int64_t>(pl.n_tiles), pl.K,
+                         static_cast<int64_t>(pl.ns), p.h0, static_cast<int64_t>(0), static_cast<int64_t>(pl.ntd),
+                         p.dim, p.N);
+    else
+      hipLaunchKernelGGL(carry_kernel<kCarryRuns>, cgrid, dim3(256), 0, s, static_cast<const float*>(p.aggP),
+                         static_cast<const float*>(p.aggS), p.carry, static_cast<int64_t>(pl.n_tiles), pl.K,
+                         static_cast<int64_t>(pl.ns), p.h0, static_cast<int64_t>(0), static_cast<int64_t>(pl.ntd),
+                         p.dim, p.N);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_lane<IO>(pl.ns, true, true, p, s);
+}
+
+}  // namespace
+}  // namespace ssm
+
+extern "C" size_t ssm_scan_fwd_structured_workspace_size(int64_t batch, int64_t L, int64_t dim, int64_t dstate,
+                                                         ssm_dtype_t dt) {
+  return structured_workspace(batch, L, dim, dstate, dt);
+}
+
+extern "C" ssm_status_t ssm_scan_fwd_structured(const void* u, const void* delta, const float* A0, const void* B,
+                                                const void* C, const float* D, const void* z,
+                                                const float* delta_bias, int softplus_flag,
+                                                const float* initial_state, void* y, float* final_state,
+                                                int64_t batch, int64_t L, int64_t dim, int64_t dstate,
+                                                ssm_dtype_t dt, void* workspace, size_t workspace_bytes,
+                                                hipStream_t stream) {
+  const ssm_status_t st =
+      check_scan_args(u, delta, A0, B, C, D, z, delta_bias, y, final_state, batch, L, dim, dstate, dt);
+  if (st != SSM_OK) return st;
+  if (initial_state && !aligned(initial_state, 4)) return SSM_ERR_INVALID_ARG;
+  if (dstate > kLaneMaxDstate) return SSM_ERR_UNSUPPORTED;
+  const int64_t es = dt == SSM_DTYPE_F32 ? 4 : 2;
+  LanePlan pl;
+  if (!plan_lane(batch, L, dim, dstate, es, &pl)) return SSM_ERR_UNSUPPORTED;
+  if (pl.packed_bc && batch * (pl.Lp / kPackT) > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
+  const LaneLayout lay = lane_layout(pl, batch);
+  if (!workspace || workspace_bytes < lay.total || !aligned(workspace, 256)) return SSM_ERR_INVALID_ARG;
+  char* ws = static_cast<char*>(workspace);
+  unsigned* words = reinterpret_cast<unsigned*>(ws);
+  LaneParams p = {};
+  p.u = u;
+  p.delta = delta;
+  p.A = A0;
+  p.D = D;
+  p.z = z;
+  p.bias = delta_bias;
+  p.bc = pl.packed_bc ? reinterpret_cast<const float*>(ws + lay.words) : nullptr;
+  p.bc_rows = batch * pl.Lp + kTBMax;
+  p.Braw = B;
+  p.Craw = C;
+  p.y = y;
+  p.final_state = final_state;
+  p.h0 = initial_state;
+  if (lay.pairs) {
+    char* pr = ws + lay.words + lay.bc;
+    p.aggP = reinterpret_cast<float*>(pr);
+    p.aggS = reinterpret_cast<float*>(pr + lay.pairs);
+    p.carry = reinterpret_cast<float*>(pr + 2 * lay.pairs);
+  }
+  p.batch = batch;
+  p.L = L;
+  p.Lp = pl.Lp;
+  p.dim = dim;
+  p.N = dstate;
+  p.chunk_len = pl.chunk_len;
+  p.ntd = pl.ntd;
+  p.n_tiles = pl.n_tiles;
+  p.K = pl.K;
+  p.softplus = softplus_flag ? 1 : 0;
+  const hipError_t e = dt == SSM_DTYPE_F32 ? run_lane<F32>(pl, lay, words, p, stream)
+                                           : run_lane<BF16>(pl, lay, words, p, stream);
+  return e == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
 extern "C" ssm_status_t ssm_workspace_status(const void* workspace, size_t workspace_bytes, hipStream_t stream) {

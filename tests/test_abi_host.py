@@ -321,3 +321,33 @@ def test_noalloc_rejects_shapes_beyond_its_scratch():
     assert lib.ssm_scan_fwd_noalloc(*a, *shape, BF16, None) == ops.SSM_ERR_SCRATCH_TOO_SMALL
     assert lib.ssm_scan_fwd_noalloc(*a, 0, 10, 64, 16, F32, None) == INVALID
     assert lib.ssm_scan_fwd_noalloc(*a, 1, 10, 64, 65, F32, None) == UNSUPPORTED
+
+
+def test_structured_host_paths():
+    """ssm_scan_fwd_structured: workspace sizes and rejections before any HIP call."""
+    L = ops.lib()
+    ws = L.ssm_scan_fwd_structured_workspace_size(4, 4096, 5120, 16, BF16)
+    assert ws > 0 and ws % 256 == 0
+    # fp32 storage reads B and C directly: no records
+    ws32 = L.ssm_scan_fwd_structured_workspace_size(4, 4096, 5120, 16, F32)
+    assert 0 < ws32 < ws
+    assert L.ssm_scan_fwd_structured_workspace_size(1, 100, 64, 17, F32) == 0   # a lane holds at most 16 states
+    assert L.ssm_scan_fwd_structured_workspace_size(0, 100, 64, 16, F32) == 0
+    p = ctypes.c_void_p(0x100000)
+    args = lambda dstate, ws, nbytes: (p, p, p, p, p, None, None, None, 1, None, p, None, 1, 100, 64, dstate, F32,
+                                       ws, nbytes, None)
+    assert L.ssm_scan_fwd_structured(*args(17, p, 1 << 20)) == UNSUPPORTED
+    assert L.ssm_scan_fwd_structured(*args(16, None, 0)) == INVALID            # no workspace
+    assert L.ssm_scan_fwd_structured(*args(16, ctypes.c_void_p(0x100010), 1 << 20)) == INVALID  # misaligned
+    assert L.ssm_scan_fwd_structured(None, p, p, p, p, None, None, None, 1, None, p, None, 1, 100, 64, 16, F32, p,
+                                     1 << 20, None) == INVALID
+
+
+def test_structured_base_detection_host():
+    import torch
+
+    a0 = torch.tensor([-1.0, -0.3, -7.5])
+    A = a0[:, None] * torch.arange(1, 17, dtype=torch.float32)[None, :]
+    assert torch.equal(ops.structured_A_base(A), a0)
+    A[2, 15] = A[2, 15] * (1 + 1e-6)
+    assert ops.structured_A_base(A) is None
