@@ -17,7 +17,7 @@
 // One workgroup (16 wavefronts, 8 for dstate 32) per (batch row, head) walks the chunks in
 // order; the head's state stays in MFMA accumulators (fp32), so no chunk
 // state goes to HBM and x, z, y, B, C are each read or written once.  Per
-// chunk (v_mfma_f32_16x16x32_bf16, bf16 operands, fp32 accumulation):
+// chunk (v_mfma_f32_16x16x32_bf16 for G, v_mfma_f32_16x16x32_f16 for the rest; fp32 accumulation):
 //   G^T = B C^T              (Q x Q, K = N) -> M[t][s] = G[t][s] exp(cs_t - cs_s) delta_s on s <= t
 //   Y   = exp(cs_t) C H + M x  (Q x P; K = N, then K = Q)  -> + D x, times SiLU(z), y
 //   H   = exp(cs_end) H + W^T x   (N x P, K = Q),  W[s][n] = exp(cs_end - cs_s) delta_s B[s][n]
@@ -28,13 +28,15 @@
 // consecutive K-side indices per lane, and B and x are loaded four token rows
 // at a time so that their transposes are written four tokens per store.
 //
-// Precision.  C, B and x arrive as bf16 and are exact operands.  M, W and the
-// state are fp32 values; rounded to bf16 once, the sums they enter lose about
-// 2^-9 of their largest terms, which against the fp64 oracle puts y near 2e-2
-// of its scale.  Each of the three is therefore carried as a pair hi + lo of
-// bf16 (hi = bf16(v), lo = bf16(v - hi)) and enters its product as two
-// MFMAs, which keeps y at the rounding of its own bf16 store (~4e-3) and the
-// state near 2e-5.
+// Precision.  B, C and x arrive as bf16; G^T = B C^T takes them as bf16
+// operands, exactly.  The other products take fp16 operands (11 significant
+// bits, fp32 accumulation): x and C are converted exactly (every bf16 value of
+// magnitude 2^-14 .. 65504 is an fp16 value), M and the state H^T are rounded
+// to fp16 once (relative 2^-12), which leaves y at the rounding of its own
+// bf16 store (~4e-3); W, which carries every input into the state, is a pair
+// hi + lo of fp16 (22 significant bits) entering its product as two MFMAs, so
+// the state keeps its fp32 accuracy (~2e-5).  x, C, M, W and H must stay
+// below 65504 in magnitude (the fp16 range); larger values give inf/NaN.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -92,6 +94,9 @@ constexpr int kSsdP = 64;         // channels per head
 constexpr int ssd_waves(int N) { return N >= 64 ? 16 : 8; }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ unsigned short bf16_bits_of(float f) {
@@ -101,16 +106,29 @@ __device__ __forceinline__ float bf16_value(unsigned short b) { return __uint_as
 __device__ __forceinline__ float bf16_lo_of(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi_of(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
 
-// hi and lo bf16 of four fp32 values, packed as two 8-byte runs.
-__device__ __forceinline__ void split4(const float* v, u32x2_t& hi, u32x2_t& lo) {
-  unsigned short hb[4], lb[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    hb[j] = bf16_bits_of(v[j]);
-    lb[j] = bf16_bits_of(v[j] - bf16_value(hb[j]));
-  }
-  hi = u32x2_t{hb[0] | (static_cast<uint32_t>(hb[1]) << 16), hb[2] | (static_cast<uint32_t>(hb[3]) << 16)};
-  lo = u32x2_t{lb[0] | (static_cast<uint32_t>(lb[1]) << 16), lb[2] | (static_cast<uint32_t>(lb[3]) << 16)};
+// Four fp32 values rounded to fp16 (nearest even), packed as one 8-byte run; and as a pair hi + lo of fp16
+// runs (hi = fp16(v), lo = fp16(v - hi)), 22 significant bits.
+__device__ __forceinline__ u32x2_t cvt4_f16(const float* v) {
+  const f16x4_t h = __builtin_convertvector((f32x4_t){v[0], v[1], v[2], v[3]}, f16x4_t);
+  return __builtin_bit_cast(u32x2_t, h);
+}
+__device__ __forceinline__ void split4_f16(const float* v, u32x2_t& hi, u32x2_t& lo) {
+  const f32x4_t x = {v[0], v[1], v[2], v[3]};
+  const f16x4_t h = __builtin_convertvector(x, f16x4_t);
+  const f16x4_t l = __builtin_convertvector(x - __builtin_convertvector(h, f32x4_t), f16x4_t);
+  hi = __builtin_bit_cast(u32x2_t, h);
+  lo = __builtin_bit_cast(u32x2_t, l);
+}
+// Eight bf16 values as fp16 (exact for |v| in [2^-14, 65504] with at most 11 significant bits, which every
+// bf16 value in that range has).
+__device__ __forceinline__ f16x8_t bf16x8_to_f16(bf16x8_t v) {
+  return __builtin_convertvector(__builtin_convertvector(v, f32x8_t), f16x8_t);
+}
+__device__ __forceinline__ float f16_lo_of(uint32_t pair) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(pair & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi_of(uint32_t pair) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(pair >> 16)));
 }
 
 template <int N>
@@ -132,14 +150,12 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
 
   __shared__ __attribute__((aligned(16))) unsigned short sC[Q * SN];   // C [t][n]
   __shared__ __attribute__((aligned(16))) unsigned short sB[Q * SN];   // B [s][n]
-  __shared__ __attribute__((aligned(16))) unsigned short sWh[N * SQ];  // W^T [n][s], hi
-  __shared__ __attribute__((aligned(16))) unsigned short sWl[N * SQ];  // lo
-  __shared__ __attribute__((aligned(16))) unsigned short sXT[P * SQ];  // x^T [p][s]
+  __shared__ __attribute__((aligned(16))) unsigned short sWh[N * SQ];  // W^T [n][s], fp16 hi
+  __shared__ __attribute__((aligned(16))) unsigned short sWl[N * SQ];  // fp16 lo
+  __shared__ __attribute__((aligned(16))) unsigned short sXT[P * SQ];  // x^T [p][s], fp16
   __shared__ __attribute__((aligned(16))) unsigned short sZT[P * SQ];  // z^T [p][t]
-  __shared__ __attribute__((aligned(16))) unsigned short sMh[Q * SQ];  // M [t][s], hi
-  __shared__ __attribute__((aligned(16))) unsigned short sMl[Q * SQ];  // lo
-  __shared__ __attribute__((aligned(16))) unsigned short sHh[P * SN];  // H^T [p][n], hi
-  __shared__ __attribute__((aligned(16))) unsigned short sHl[P * SN];  // lo
+  __shared__ __attribute__((aligned(16))) unsigned short sM[Q * SQ];   // M [t][s], fp16
+  __shared__ __attribute__((aligned(16))) unsigned short sH[P * SN];   // H^T [p][n], fp16
   // per chunk parity: A * (cumulative step) within the chunk, and the step delta_t; wavefront 0
   // prepares the next chunk's while the others finish the current one
   __shared__ __attribute__((aligned(16))) float sCS[2][Q];
@@ -238,11 +254,8 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
 #pragma unroll
     for (int i = 0; i < HT; ++i) {
       const float v[4] = {hacc[i][0], hacc[i][1], hacc[i][2], hacc[i][3]};
-      u32x2_t hi, lo;
-      split4(v, hi, lo);
       const int idx = (16 * ph + lr) * SN + 16 * (nb0 + NBS * i) + 4 * lq;
-      *reinterpret_cast<u32x2_t*>(&sHh[idx]) = hi;
-      *reinterpret_cast<u32x2_t*>(&sHl[idx]) = lo;
+      *reinterpret_cast<u32x2_t*>(&sH[idx]) = cvt4_f16(v);
     }
   };
   // state element (channel, state) of this lane's tile i, entry q
@@ -293,11 +306,11 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       }
     }
     if (tid < XI) {
-      // x^T: channel 2xpp takes the low halves of the four rows, 2xpp+1 the high halves
-      const u32x2_t even = {(gx[0] & 0xffffu) | (gx[1] << 16), (gx[2] & 0xffffu) | (gx[3] << 16)};
-      const u32x2_t odd = {(gx[0] >> 16) | (gx[1] & 0xffff0000u), (gx[2] >> 16) | (gx[3] & 0xffff0000u)};
-      *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp) * SQ + xs0]) = even;
-      *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp + 1) * SQ + xs0]) = odd;
+      // x^T as fp16: channel 2xpp takes the low halves of the four rows, 2xpp+1 the high halves
+      const float even[4] = {bf16_lo_of(gx[0]), bf16_lo_of(gx[1]), bf16_lo_of(gx[2]), bf16_lo_of(gx[3])};
+      const float odd[4] = {bf16_hi_of(gx[0]), bf16_hi_of(gx[1]), bf16_hi_of(gx[2]), bf16_hi_of(gx[3])};
+      *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp) * SQ + xs0]) = cvt4_f16(even);
+      *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp + 1) * SQ + xs0]) = cvt4_f16(odd);
       if (p.z) {
         *reinterpret_cast<u32x2_t*>(&sZT[(2 * xpp) * SQ + xs0]) =
             u32x2_t{(gzz[0] & 0xffffu) | (gzz[1] << 16), (gzz[2] & 0xffffu) | (gzz[3] << 16)};
@@ -319,14 +332,13 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
     for (int c = 0; c < YT; ++c) yacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < N / 32; ++kk) {
-      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sC[(16 * ty + lr) * SN + 32 * kk + 8 * lq]);
+      const f16x8_t a =
+          bf16x8_to_f16(*reinterpret_cast<const bf16x8_t*>(&sC[(16 * ty + lr) * SN + 32 * kk + 8 * lq]));
 #pragma unroll
       for (int c = 0; c < YT; ++c) {
         const int pr = (16 * (py0 + c) + lr) * SN + 32 * kk + 8 * lq;
-        const bf16x8_t bh = *reinterpret_cast<const bf16x8_t*>(&sHh[pr]);
-        const bf16x8_t bl = *reinterpret_cast<const bf16x8_t*>(&sHl[pr]);
-        yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bh, yacc[c], 0, 0, 0);
-        yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bl, yacc[c], 0, 0, 0);
+        const f16x8_t bh = *reinterpret_cast<const f16x8_t*>(&sH[pr]);
+        yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, yacc[c], 0, 0, 0);
       }
     }
 
@@ -368,10 +380,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
         for (int j = 0; j < 4; ++j)
           m[j] = (s0 + j <= t) ? g[j] * __builtin_amdgcn_exp2f((cst - css[j]) * kLog2eF) * dls[j] : 0.0f;
       }
-      u32x2_t hi, lo;
-      split4(m, hi, lo);
-      *reinterpret_cast<u32x2_t*>(&sMh[t * SQ + s0]) = hi;
-      *reinterpret_cast<u32x2_t*>(&sMl[t * SQ + s0]) = lo;
+      *reinterpret_cast<u32x2_t*>(&sM[t * SQ + s0]) = cvt4_f16(m);
     }
     // ---- W^T[n][s] = exp(cs_end - cs_s) delta_s B[s][n], from the B rows in registers
     {
@@ -391,10 +400,10 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
             v1[r] = ws * bf16_hi_of(gb[i][r]);
           }
           u32x2_t hi, lo;
-          split4(v0, hi, lo);
+          split4_f16(v0, hi, lo);
           *reinterpret_cast<u32x2_t*>(&sWh[(2 * np) * SQ + s0]) = hi;
           *reinterpret_cast<u32x2_t*>(&sWl[(2 * np) * SQ + s0]) = lo;
-          split4(v1, hi, lo);
+          split4_f16(v1, hi, lo);
           *reinterpret_cast<u32x2_t*>(&sWh[(2 * np + 1) * SQ + s0]) = hi;
           *reinterpret_cast<u32x2_t*>(&sWl[(2 * np + 1) * SQ + s0]) = lo;
         }
@@ -414,13 +423,11 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       for (int kk = 0; kk < 2; ++kk) {
         if (32 * kk > 16 * ty + 15) continue;  // M is zero past the diagonal
         const int mr = (16 * ty + lr) * SQ + 32 * kk + 8 * lq;
-        const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sMh[mr]);
-        const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sMl[mr]);
+        const f16x8_t ah = *reinterpret_cast<const f16x8_t*>(&sM[mr]);
 #pragma unroll
         for (int c = 0; c < YT; ++c) {
-          const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sXT[(16 * (py0 + c) + lr) * SQ + 32 * kk + 8 * lq]);
-          yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, yacc[c], 0, 0, 0);
-          yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb, yacc[c], 0, 0, 0);
+          const f16x8_t bb = *reinterpret_cast<const f16x8_t*>(&sXT[(16 * (py0 + c) + lr) * SQ + 32 * kk + 8 * lq]);
+          yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bb, yacc[c], 0, 0, 0);
         }
       }
       // + D x, times SiLU(z), rounded to bf16; x of four consecutive tokens is one 8-byte read of x^T
@@ -428,7 +435,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       for (int c = 0; c < YT; ++c) {
         const int pch = 16 * (py0 + c) + lr;
         const u32x2_t xq = *reinterpret_cast<const u32x2_t*>(&sXT[pch * SQ + 16 * ty + 4 * lq]);
-        const float xv[4] = {bf16_lo_of(xq[0]), bf16_hi_of(xq[0]), bf16_lo_of(xq[1]), bf16_hi_of(xq[1])};
+        const float xv[4] = {f16_lo_of(xq[0]), f16_hi_of(xq[0]), f16_lo_of(xq[1]), f16_hi_of(xq[1])};
         u32x2_t zq = {0u, 0u};
         if (p.z) zq = *reinterpret_cast<const u32x2_t*>(&sZT[pch * SQ + 16 * ty + 4 * lq]);
         const float zv[4] = {bf16_lo_of(zq[0]), bf16_hi_of(zq[0]), bf16_lo_of(zq[1]), bf16_hi_of(zq[1])};
@@ -452,14 +459,14 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
         for (int j = 0; j < 4; ++j) hacc[i][j] *= fade;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sXT[(16 * ph + lr) * SQ + 32 * kk + 8 * lq]);
+        const f16x8_t bb = *reinterpret_cast<const f16x8_t*>(&sXT[(16 * ph + lr) * SQ + 32 * kk + 8 * lq]);
 #pragma unroll
         for (int i = 0; i < HT; ++i) {
           const int wr = (16 * (nb0 + NBS * i) + lr) * SQ + 32 * kk + 8 * lq;
-          const bf16x8_t ah = *reinterpret_cast<const bf16x8_t*>(&sWh[wr]);
-          const bf16x8_t al = *reinterpret_cast<const bf16x8_t*>(&sWl[wr]);
-          hacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bb, hacc[i], 0, 0, 0);
-          hacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bb, hacc[i], 0, 0, 0);
+          const f16x8_t ah = *reinterpret_cast<const f16x8_t*>(&sWh[wr]);
+          const f16x8_t al = *reinterpret_cast<const f16x8_t*>(&sWl[wr]);
+          hacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bb, hacc[i], 0, 0, 0);
+          hacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bb, hacc[i], 0, 0, 0);
         }
       }
     }
