@@ -260,8 +260,15 @@ ssm_status_t ssm_scan_trap_fwd(const void* u, const void* delta, const float* A,
  *   x, B, C must be 16-byte aligned, delta, z, y 2-byte, the fp32 arrays
  *   4-byte (else INVALID_ARG).  Supported: dt = BF16, headdim = 64 and
  *   dstate = 32, 64 or 128, with (L + 64) * heads * headdim * 2 and
- *   (L + 64) * ngroups * dstate * 2 bytes below 2^31 (else UNSUPPORTED).  Arithmetic: bf16 matrix products with fp32
- *   accumulation, fp32 state.  workspace: workspace_bytes >=
+ *   (L + 64) * ngroups * dstate * 2 bytes below 2^31 (else UNSUPPORTED).  Arithmetic: matrix products with
+ *   fp32 accumulation and an fp32 state; C B^T takes bf16 operands (exact),
+ *   the other products fp16 operands: x and C convert exactly, the decay-
+ *   weighted intra-chunk matrix and the state are rounded to fp16 once where
+ *   they enter the output, and the inputs' path into the state is an fp16
+ *   hi + lo pair (22 significant bits).  So x, C, the state and the
+ *   intermediate products must stay below 65504 in magnitude (the fp16
+ *   range): beyond it the outputs become inf or NaN (values are not
+ *   inspected).  workspace: workspace_bytes >=
  *   ssm_ssd_fwd_workspace_size() bytes of device memory, 256-byte aligned
  *   (may be NULL when that size is 0), overwritten by the call and not to be
  *   shared with a concurrent call.  y must not alias an input. */
