@@ -74,6 +74,12 @@ def oracle_scan(x, softplus=True, with_D=True, with_bias=True, with_z=True, nthr
                       softplus=softplus, nthreads=nthreads)
 
 
+def oracle_threads():
+    """Threads for the oracle on whole workloads: the cores this process may use, at most 16."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, n))
+
+
 def oracle_channels(x, samples, nthreads=8):
     """Oracle on selected (b, d) channels only, full sequence.  Returns y [L, S] and final state [S, N]."""
     bsel = np.array([b for b, _ in samples])

@@ -15,7 +15,7 @@ from oracle import ssd as S
 from selective_state_space_33_amd import inputs as I
 from selective_state_space_33_amd import ops
 
-from .gpu_util import TOL, SsdChained, rel_err, say
+from .gpu_util import TOL, SsdChained, oracle_threads, rel_err, say
 
 pytestmark = pytest.mark.gpu
 
@@ -88,8 +88,8 @@ def test_ssd_many_heads_and_batch_rows():
 
 
 def test_ssd_full_size_sampled_heads():
-    """The 2.7B-shaped layer (batch 4, L 4096, 80 heads of 64, state 128) as bench.py times it; oracle on 6
-    sampled (batch row, head) pairs."""
+    """The 2.7B-shaped layer (batch 4, L 4096, 80 heads of 64, state 128) as bench.py times it; the masked-matrix
+    oracle on 6 sampled (batch row, head) pairs."""
     cfg = I.SSD_WORKLOADS["mamba2_2p7b_bf16"]
     x = I.random_ssd_inputs(np.random.default_rng(0), cfg["batch"], cfg["L"], cfg["heads"], cfg["headdim"],
                             cfg["dstate"])
@@ -98,7 +98,6 @@ def test_ssd_full_size_sampled_heads():
     assert np.all(np.isfinite(yg))
     ey = ef = 0.0
     for b, h in [(0, 0), (0, 79), (1, 17), (2, 40), (3, 63), (3, 79)]:
-        sub = {k: None if v is None else v for k, v in x.items()}
         sub = dict(x=x["x"][b:b + 1, :, h:h + 1], z=x["z"][b:b + 1, :, h:h + 1], delta=x["delta"][b:b + 1, :, h:h + 1],
                    B=x["B"][b:b + 1], C=x["C"][b:b + 1], A=x["A"][h:h + 1], D=x["D"][h:h + 1],
                    delta_bias=x["delta_bias"][h:h + 1])
@@ -107,6 +106,28 @@ def test_ssd_full_size_sampled_heads():
         ey = max(ey, rel_err(yg[b:b + 1, :, h:h + 1], yo))
         ef = max(ef, rel_err(fg[b:b + 1, h:h + 1], fo))
     print(f"[parity] ssd 2.7B sampled heads: y {ey:.2e}  final {ef:.2e}", flush=True)
+    assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (ey, ef)
+
+
+def test_ssd_full_size_all_heads_against_the_recurrence():
+    """The whole 2.7B-shaped layer against the recurrent C oracle: with one group the layer is the two-term scan
+    over heads x headdim channels with A[d][n] = A[head of d] and the head's step on each of its channels (the
+    duality tests/test_oracle_ssd.py pins).  Every output of every (row, head) is compared."""
+    from oracle import ref as R
+
+    cfg = I.SSD_WORKLOADS["mamba2_2p7b_bf16"]
+    bt, L, H, P, N = cfg["batch"], cfg["L"], cfg["heads"], cfg["headdim"], cfg["dstate"]
+    x = I.random_ssd_inputs(np.random.default_rng(0), bt, L, H, P, N)
+    say("ssd full-size 2.7B layer, all heads")
+    yg, fg = _run(x)
+    rep = lambda a: np.repeat(np.asarray(a, np.float32), P, axis=-1)  # per head -> per channel (head major)
+    yo, fo = R.scan_fwd(x["x"].reshape(bt, L, H * P), rep(x["delta"]),
+                        np.repeat(x["A"], P)[:, None] * np.ones((1, N), np.float32), x["B"], x["C"],
+                        D=rep(x["D"]), z=x["z"].reshape(bt, L, H * P), delta_bias=rep(x["delta_bias"]),
+                        nthreads=oracle_threads())
+    ey = rel_err(yg.reshape(bt, L, H * P), yo)
+    ef = rel_err(fg.reshape(bt, H * P, N), fo)
+    print(f"[parity] ssd 2.7B all {bt * H} (row, head) units: y {ey:.2e}  final {ef:.2e}", flush=True)
     assert ey <= TOL["bf16"] and ef <= TOL["bf16"], (ey, ef)
 
 
