@@ -17,7 +17,7 @@
 // One workgroup (16 wavefronts, 8 for dstate 32) per (batch row, head) walks the chunks in
 // order; the head's state stays in MFMA accumulators (fp32), so no chunk
 // state goes to HBM and x, z, y, B, C are each read or written once.  Per
-// chunk (v_mfma_f32_16x16x32_bf16 for G, v_mfma_f32_16x16x32_f16 for the rest; fp32 accumulation):
+// chunk (v_mfma_f32_16x16x32_f16, fp32 accumulation):
 //   G^T = B C^T              (Q x Q, K = N) -> M[t][s] = G[t][s] exp(cs_t - cs_s) delta_s on s <= t
 //   Y   = exp(cs_t) C H + M x  (Q x P; K = N, then K = Q)  -> + D x, times SiLU(z), y
 //   H   = exp(cs_end) H + W^T x   (N x P, K = Q),  W[s][n] = exp(cs_end - cs_s) delta_s B[s][n]
@@ -28,10 +28,10 @@
 // consecutive K-side indices per lane, and B and x are loaded four token rows
 // at a time so that their transposes are written four tokens per store.
 //
-// Precision.  B, C and x arrive as bf16; G^T = B C^T takes them as bf16
-// operands, exactly.  The other products take fp16 operands (11 significant
-// bits, fp32 accumulation): x and C are converted exactly (every bf16 value of
-// magnitude 2^-14 .. 65504 is an fp16 value), M and the state H^T are rounded
+// Precision.  B, C and x arrive as bf16 and are staged as fp16, exactly
+// (every bf16 value of magnitude 2^-14 .. 65504 is an fp16 value), so G^T =
+// B C^T is exact.  The products take fp16 operands (11 significant bits,
+// fp32 accumulation): M and the state H^T are rounded
 // to fp16 once (relative 2^-12), which leaves y at the rounding of its own
 // bf16 store (~4e-3); W, which carries every input into the state, is a pair
 // hi + lo of fp16 (22 significant bits) entering its product as two MFMAs, so
@@ -96,6 +96,7 @@ constexpr int ssd_waves(int N) { return N >= 64 ? 16 : 8; }
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -119,10 +120,15 @@ __device__ __forceinline__ void split4_f16(const float* v, u32x2_t& hi, u32x2_t&
   hi = __builtin_bit_cast(u32x2_t, h);
   lo = __builtin_bit_cast(u32x2_t, l);
 }
-// Eight bf16 values as fp16 (exact for |v| in [2^-14, 65504] with at most 11 significant bits, which every
-// bf16 value in that range has).
-__device__ __forceinline__ f16x8_t bf16x8_to_f16(bf16x8_t v) {
-  return __builtin_convertvector(__builtin_convertvector(v, f32x8_t), f16x8_t);
+// bf16 values as fp16 (exact for |v| in [2^-14, 65504]: every bf16 value there has at most 8 significant bits),
+// two per 32-bit word and eight per 16-byte piece.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  const f16x2_t h = __builtin_convertvector((f32x2_t){__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u)},
+                                            f16x2_t);
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ u32x4_t bf16x8_to_f16(u32x4_t v) {
+  return u32x4_t{bf16x2_to_f16x2(v[0]), bf16x2_to_f16x2(v[1]), bf16x2_to_f16x2(v[2]), bf16x2_to_f16x2(v[3])};
 }
 __device__ __forceinline__ float f16_lo_of(uint32_t pair) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(pair & 0xffffu)));
@@ -148,8 +154,8 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   static_assert(XI <= NTH && HT >= 1 && YT >= 1, "work split");
   constexpr float kLog2eF = 1.4426950408889634f;
 
-  __shared__ __attribute__((aligned(16))) unsigned short sC[Q * SN];   // C [t][n]
-  __shared__ __attribute__((aligned(16))) unsigned short sB[Q * SN];   // B [s][n]
+  __shared__ __attribute__((aligned(16))) unsigned short sC[Q * SN];   // C [t][n], fp16
+  __shared__ __attribute__((aligned(16))) unsigned short sB[Q * SN];   // B [s][n], fp16
   __shared__ __attribute__((aligned(16))) unsigned short sWh[N * SQ];  // W^T [n][s], fp16 hi
   __shared__ __attribute__((aligned(16))) unsigned short sWl[N * SQ];  // fp16 lo
   __shared__ __attribute__((aligned(16))) unsigned short sXT[P * SQ];  // x^T [p][s], fp16
@@ -294,7 +300,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
 #pragma unroll
     for (int i = 0; i < C_PER; ++i) {
       const int e = tid + NTH * i;
-      if (e < C_PIECES) *reinterpret_cast<u32x4_t*>(&sC[(e / (N / 8)) * SN + (e % (N / 8)) * 8]) = gc[i];
+      if (e < C_PIECES) *reinterpret_cast<u32x4_t*>(&sC[(e / (N / 8)) * SN + (e % (N / 8)) * 8]) = bf16x8_to_f16(gc[i]);
     }
 #pragma unroll
     for (int i = 0; i < B_PER; ++i) {
@@ -302,7 +308,8 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       if (e < B_ITEMS) {
         const int np = e % (N / 2), s0 = 4 * (e / (N / 2));
 #pragma unroll
-        for (int r = 0; r < 4; ++r) *reinterpret_cast<uint32_t*>(&sB[(s0 + r) * SN + 2 * np]) = gb[i][r];
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<uint32_t*>(&sB[(s0 + r) * SN + 2 * np]) = bf16x2_to_f16x2(gb[i][r]);
       }
     }
     if (tid < XI) {
@@ -332,8 +339,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
     for (int c = 0; c < YT; ++c) yacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < N / 32; ++kk) {
-      const f16x8_t a =
-          bf16x8_to_f16(*reinterpret_cast<const bf16x8_t*>(&sC[(16 * ty + lr) * SN + 32 * kk + 8 * lq]));
+      const f16x8_t a = *reinterpret_cast<const f16x8_t*>(&sC[(16 * ty + lr) * SN + 32 * kk + 8 * lq]);
 #pragma unroll
       for (int c = 0; c < YT; ++c) {
         const int pr = (16 * (py0 + c) + lr) * SN + 32 * kk + 8 * lq;
@@ -369,9 +375,9 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
         f32x4_t g = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kk = 0; kk < N / 32; ++kk) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(&sB[(16 * gs + lr) * SN + 32 * kk + 8 * lq]);
-          const bf16x8_t bb = *reinterpret_cast<const bf16x8_t*>(&sC[(16 * gt + lr) * SN + 32 * kk + 8 * lq]);
-          g = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, g, 0, 0, 0);
+          const f16x8_t a = *reinterpret_cast<const f16x8_t*>(&sB[(16 * gs + lr) * SN + 32 * kk + 8 * lq]);
+          const f16x8_t bb = *reinterpret_cast<const f16x8_t*>(&sC[(16 * gt + lr) * SN + 32 * kk + 8 * lq]);
+          g = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bb, g, 0, 0, 0);
         }
         const float cst = sCS[par][t];
         const f32x4_t css = *reinterpret_cast<const f32x4_t*>(&sCS[par][s0]);
