@@ -337,7 +337,6 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
     f32x4_t yacc[YT];
 #pragma unroll
     for (int c = 0; c < YT; ++c) yacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
     for (int kk = 0; kk < N / 32; ++kk) {
       const f16x8_t a = *reinterpret_cast<const f16x8_t*>(&sC[(16 * ty + lr) * SN + 32 * kk + 8 * lq]);
 #pragma unroll
@@ -540,10 +539,16 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       }
     }
   };
-  // unit j's starting state, kept here while a segment runs first (phase 0)
-  f32x4_t saved[HT];
+  // unit j's state while a segment runs (phase 1): each thread's own state tiles, kept in LDS rather than in
+  // registers that would stay allocated through the chunk loop
+  __shared__ f32x4_t sSaved[HT][NTH];
   int rest = 0;
-  initial(j, saved);
+  {
+    f32x4_t s0[HT];
+    initial(j, s0);
+#pragma unroll
+    for (int i = 0; i < HT; ++i) sSaved[i][tid] = s0[i];
+  }
   for (int phase = 0; phase < 3; ++phase) {
     if (phase == 0 && !(has_seg && sg > 0)) continue;
     if (phase == 1 && !has_seg) continue;
@@ -554,7 +559,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       initial(p.n_long + st, hacc);
     } else {
 #pragma unroll
-      for (int i = 0; i < HT; ++i) hacc[i] = saved[i];
+      for (int i = 0; i < HT; ++i) hacc[i] = sSaved[i][tid];
     }
     if (phase == 1 && sg > 0) {
       // the state after segment sg-1: wait for its flag, then read it coherently
@@ -580,7 +585,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
     if (phase == 0) {
       rest = r;
 #pragma unroll
-      for (int i = 0; i < HT; ++i) saved[i] = hacc[i];
+      for (int i = 0; i < HT; ++i) sSaved[i][tid] = hacc[i];
     } else if (phase == 1 && sg + 1 < p.Ks) {
       float* next = crow + P * N;
 #pragma unroll
