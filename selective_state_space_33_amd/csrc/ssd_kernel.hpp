@@ -337,6 +337,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
     f32x4_t yacc[YT];
 #pragma unroll
     for (int c = 0; c < YT; ++c) yacc[c] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
     for (int kk = 0; kk < N / 32; ++kk) {
       const f16x8_t a = *reinterpret_cast<const f16x8_t*>(&sC[(16 * ty + lr) * SN + 32 * kk + 8 * lq]);
 #pragma unroll
