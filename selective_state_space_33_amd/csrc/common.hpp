@@ -108,7 +108,11 @@ template <> __device__ __forceinline__ void store_vals<BF16, 1>(void* base, int6
 
 // Buffer (V#) access.  A raw buffer resource covers [base, base + bytes);
 // loads at offsets outside it return zero and stores there are dropped by the
-// hardware, so a ragged tail needs no branch.  Offsets are 32-bit bytes.
+// hardware, so a ragged tail needs no branch.  Offsets are 32-bit bytes.  The
+// range check takes the whole offset, the scalar (soff) part included (as
+// measured on gfx950), so a wave-uniform part of an offset (a block's start)
+// goes in soff: one scalar value for every lane instead of a vector add per
+// lane, with the same zero reads and dropped stores past the range.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kBufWord3 = 0x00020000;  // gfx9 descriptor word 3: 32-bit data format, raw (unswizzled) addressing
 

@@ -73,21 +73,21 @@ struct LaneTok {
   float B, C;
 };
 
-template <class IO> __device__ __forceinline__ uint32_t lane_load(rsrc_t r, unsigned off) {
+template <class IO> __device__ __forceinline__ uint32_t lane_load(rsrc_t r, unsigned off, int soff) {
   if constexpr (__is_same(IO, F32))
-    return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(off), soff, 0);
   else
-    return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), 0, 0);
+    return __builtin_amdgcn_raw_buffer_load_b16(r, static_cast<int>(off), soff, 0);
 }
 template <class IO> __device__ __forceinline__ float lane_value(uint32_t raw) {
   if constexpr (__is_same(IO, F32)) return __uint_as_float(raw);
   else return __uint_as_float(raw << 16);
 }
-template <class IO> __device__ __forceinline__ void lane_store(rsrc_t r, unsigned off, float v) {
+template <class IO> __device__ __forceinline__ void lane_store(rsrc_t r, unsigned off, int soff, float v) {
   if constexpr (__is_same(IO, F32))
-    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(off), soff, 0);
   else
-    __builtin_amdgcn_raw_buffer_store_b16(to_bf16(v), r, static_cast<int>(off), 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(to_bf16(v), r, static_cast<int>(off), soff, 0);
 }
 
 template <class IO, int NS, bool STRUCT, bool FULL, bool GATE>
@@ -113,8 +113,10 @@ __global__ void __launch_bounds__(64 * kLaneWaves) lane_scan_kernel(LaneParams p
   const int nt = static_cast<int>(t1 - t0);
 
   // Token rows of u, delta_raw, z, y through buffer resources covering (b, t0, d0) to the end of the
-  // chunk's last row: tokens past the chunk read zero and are not written.  A channel past dim gets an
-  // offset at or above 2^31, past the range (the host keeps a chunk and its padding below 2^31 bytes).
+  // chunk's last row: tokens past the chunk read zero and are not written.  A group of TG tokens is
+  // addressed by the (scalar) offset of its first row plus a lane's fixed offset of each token in it.  A
+  // channel past dim gets offsets at or above 2^31, past the range (the host keeps a chunk and its
+  // padding below 2^31 bytes).
   const unsigned row_bytes = static_cast<unsigned>(dim * ES);
   const int64_t base = ((b * L + t0) * dim + d0) * ES;
   const int64_t bytes = static_cast<int64_t>(nt) * row_bytes - d0 * ES;
@@ -127,22 +129,33 @@ __global__ void __launch_bounds__(64 * kLaneWaves) lane_scan_kernel(LaneParams p
   // B and C: lane l reads state l % 16 of each token (zero past N)
   rsrc_t rs_B, rs_C;
   unsigned b_lo, c_lo, bc_stride;
+  int64_t bc_bytes;
   if (p.bc) {
     const float* rec = p.bc + (b * p.Lp + t0) * 32;
-    rs_B = make_rsrc(rec, (p.bc_rows - b * p.Lp - t0) * 32 * static_cast<int64_t>(sizeof(float)));
+    bc_bytes = (p.bc_rows - b * p.Lp - t0) * 32 * static_cast<int64_t>(sizeof(float));
+    rs_B = make_rsrc(rec, bc_bytes);
     rs_C = rs_B;
     b_lo = static_cast<unsigned>((lane & 15) * 4);
     c_lo = b_lo + 64u;
     bc_stride = 128u;
   } else {
     const int64_t rb = (b * L + t0) * N * static_cast<int64_t>(sizeof(float));
-    int64_t rbytes = (L - t0) * N * static_cast<int64_t>(sizeof(float));
-    if (rbytes > 0x7fffffffLL) rbytes = 0x7fffffffLL;
-    rs_B = make_rsrc(static_cast<const char*>(p.Braw) + rb, rbytes);
-    rs_C = make_rsrc(static_cast<const char*>(p.Craw) + rb, rbytes);
+    bc_bytes = (L - t0) * N * static_cast<int64_t>(sizeof(float));
+    if (bc_bytes > 0x7fffffffLL) bc_bytes = 0x7fffffffLL;
+    rs_B = make_rsrc(static_cast<const char*>(p.Braw) + rb, bc_bytes);
+    rs_C = make_rsrc(static_cast<const char*>(p.Craw) + rb, bc_bytes);
     b_lo = (lane & 15) < N ? static_cast<unsigned>((lane & 15) * 4) : 0x80000000u;
     c_lo = b_lo;
     bc_stride = static_cast<unsigned>(N * 4);
+  }
+  // Token j of a group sits at row jr = j (forward) or TG-1-j (backward) from the group's first row.
+  constexpr bool BACKWARD = STRUCT && !FULL;
+  unsigned tok_off[TG], rec_off[TG];
+#pragma unroll
+  for (int j = 0; j < TG; ++j) {
+    const unsigned jr = BACKWARD ? TG - 1 - j : j;
+    tok_off[j] = lo + jr * static_cast<unsigned>(row_bytes);
+    rec_off[j] = b_lo + jr * bc_stride;
   }
 
   // per-channel constants
@@ -182,25 +195,33 @@ __global__ void __launch_bounds__(64 * kLaneWaves) lane_scan_kernel(LaneParams p
     }
   }
 
-  // Token i of the walk: token i of the chunk (forward), or token nt-1-i (the structured pair pass walks
-  // backwards); past the chunk, token nt, which reads zero.
-  constexpr bool BACKWARD = STRUCT && !FULL;
-  auto token_of = [&](int i) -> unsigned {
-    const int k = i < nt ? (BACKWARD ? nt - 1 - i : i) : nt;
-    return static_cast<unsigned>(k);
+  // Group g of the walk: tokens g*TG .. g*TG+TG-1 of the chunk (forward), or tokens nt-1-g*TG down to
+  // nt-TG-g*TG (the structured pair pass walks backwards; its chunks are whole groups).  The scalar
+  // offsets of the group's first row in the token rows and in the B/C rows; a group wholly past the
+  // chunk takes each range's size, so all of it reads zero.
+  auto first_row = [&](int g) -> int {
+    if constexpr (BACKWARD) return g * TG < nt ? nt - TG - g * TG : -1;
+    else return g * TG < nt ? g * TG : -1;
+  };
+  auto tok_soff = [&](int g) -> int {
+    const int r0 = first_row(g);
+    return r0 < 0 ? static_cast<int>(bytes) : r0 * static_cast<int>(row_bytes);
+  };
+  auto rec_soff = [&](int g) -> int {
+    const int r0 = first_row(g);
+    return r0 < 0 ? static_cast<int>(bc_bytes) : r0 * static_cast<int>(bc_stride);
   };
   auto issue = [&](LaneTok (&r)[TG], int g) {
+    const int so = tok_soff(g), sr = rec_soff(g);
 #pragma unroll
     for (int j = 0; j < TG; ++j) {
-      const unsigned k = token_of(g * TG + j);
-      const unsigned off = k * row_bytes + lo;
-      r[j].u = lane_load<IO>(rs_u, off);
-      r[j].d = lane_load<IO>(rs_d, off);
-      if constexpr (has_z) r[j].z = lane_load<IO>(rs_z, off);
-      r[j].B = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_B, static_cast<int>(k * bc_stride + b_lo), 0, 0));
+      r[j].u = lane_load<IO>(rs_u, tok_off[j], so);
+      r[j].d = lane_load<IO>(rs_d, tok_off[j], so);
+      if constexpr (has_z) r[j].z = lane_load<IO>(rs_z, tok_off[j], so);
+      r[j].B = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_B, static_cast<int>(rec_off[j]), sr, 0));
       if constexpr (FULL)
         r[j].C = __uint_as_float(
-            __builtin_amdgcn_raw_buffer_load_b32(rs_C, static_cast<int>(k * bc_stride + c_lo), 0, 0));
+            __builtin_amdgcn_raw_buffer_load_b32(rs_C, static_cast<int>(rec_off[j] + (c_lo - b_lo)), sr, 0));
     }
   };
 
@@ -209,19 +230,20 @@ __global__ void __launch_bounds__(64 * kLaneWaves) lane_scan_kernel(LaneParams p
   // the updates of the tokens before them), then its updates in order.  The powers of q (and Q) run as two
   // chains of alternate states and the readout as two partial sums, so no long dependency chain stalls a
   // wavefront that has a SIMD to itself.
-  auto compute = [&](LaneTok (&r)[TG], int g) {
+  // MASK: the group may hold tokens past the chunk, which take the identity step (1, 0).
+  auto compute = [&](LaneTok (&r)[TG], int g, auto maskc) {
+    constexpr bool MASK = decltype(maskc)::value != 0;
     float dl[TG], du[TG], q[TG];
 #pragma unroll
     for (int j = 0; j < TG; ++j) {
-      const bool live = g * TG + j < nt;
       float x = step_of(lane_value<IO>(r[j].d) + biasv, sp_k, sp_lo);
-      dl[j] = live ? x : 0.0f;  // past the chunk: the identity step (1, 0)
+      dl[j] = (!MASK || g * TG + j < nt) ? x : 0.0f;
       du[j] = dl[j] * lane_value<IO>(r[j].u);
       if constexpr (STRUCT && FULL) q[j] = __builtin_amdgcn_exp2f(dl[j] * A2[0]);
     }
+    const int so = FULL ? tok_soff(g) : 0;
 #pragma unroll
     for (int j = 0; j < TG; ++j) {
-      const int i = g * TG + j;
       if constexpr (FULL) {
         float y0 = 0.0f, y1 = 0.0f;
         if constexpr (STRUCT) {
@@ -259,7 +281,7 @@ __global__ void __launch_bounds__(64 * kLaneWaves) lane_scan_kernel(LaneParams p
         }
         float out = __builtin_fmaf(Dv, lane_value<IO>(r[j].u), y0 + y1);
         if constexpr (has_z) out *= silu_f(lane_value<IO>(r[j].z));
-        lane_store<IO>(rs_y, token_of(i) * row_bytes + lo, out);
+        lane_store<IO>(rs_y, tok_off[j], so, out);
       } else if constexpr (STRUCT) {
         // backwards: Q = prod over the tokens after this one of q
         const float Q = __builtin_amdgcn_exp2f(A2[0] * sfx);
@@ -293,15 +315,30 @@ __global__ void __launch_bounds__(64 * kLaneWaves) lane_scan_kernel(LaneParams p
     }
   };
 
-  // groups of TG tokens, two register sets: group g+1 loads while group g computes
+  // groups of TG tokens, two register sets: group g+1 loads while group g computes; pairs of groups
+  // wholly inside the chunk first, then (only in a chunk that ends ragged, the sequence's last) a masked
+  // pair holding its end
   LaneTok r0[TG], r1[TG];
   const int ng = (nt + TG - 1) / TG;
+  const int ngf = nt / (2 * TG) * 2;
   issue(r0, 0);
-  for (int g = 0; g < ng; g += 2) {
+  int g = 0;
+  // The scheduling barriers keep each group's loads where they are written, a whole group ahead of
+  // their use: their offsets need no vector work, and left free the scheduler sinks them next to it.
+  for (; g < ngf; g += 2) {
     issue(r1, g + 1);
-    compute(r0, g);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(r0, g, IC<0>{});
+    __builtin_amdgcn_sched_barrier(0);
     issue(r0, g + 2);
-    compute(r1, g + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(r1, g + 1, IC<0>{});
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (g < ng) {
+    issue(r1, g + 1);
+    compute(r0, g, IC<1>{});
+    compute(r1, g + 1, IC<1>{});
   }
 
   if constexpr (FULL) {

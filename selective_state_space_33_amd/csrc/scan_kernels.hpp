@@ -242,6 +242,14 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
   // B floats (16 per register: 16/NPL tokens of this wavefront's NPL states)
   // followed by its C floats, and need the host to have made N = NPL * G.
   constexpr bool DIRECT = __is_same(IO, F32) && RULE == kRuleEuler && !CKPT;
+  // A block's start goes in the loads' scalar offset (SO = the block's byte
+  // offset, no vector add per lane) with 16-token blocks, two workgroups per
+  // CU.  With 32-token blocks (one workgroup per CU, two wavefronts per SIMD)
+  // the lanes add it themselves: measured on the 2.8B and 130M layers, the
+  // scalar form ran 1.5-2.5% slower there in spite of 3% fewer VALU
+  // instructions, while it gains 3% on the 16-token blocks of the long fp32
+  // sequence.
+  constexpr bool SO = TB == 16;
 
   // Double-buffered by block parity.  (delta, delta*u) per token, channel;
   // (delta, u/2) with the trapezoidal rule.
@@ -400,19 +408,20 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
     auto load_records = [&](auto parc, int blk) {
       constexpr int P = decltype(parc)::value;
       if constexpr (DIRECT) {
-        const unsigned bo = static_cast<unsigned>(blk) * TB * static_cast<unsigned>(N) * 4u + dir_voff;
+        const int bo = blk * TB * static_cast<int>(N) * 4;
         const unsigned rstep = (16 / NPL) * static_cast<unsigned>(N) * 4u;  // bytes of B per register
 #pragma unroll
         for (int v = 0; v < NRV / 2; ++v) {
-          const int off = static_cast<int>(bo + v * rstep);
-          rv[P][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_B, off, 0, 0));
-          rv[P][NRV / 2 + v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_C, off, 0, 0));
+          const int off = static_cast<int>(dir_voff + v * rstep) + (SO ? 0 : bo);
+          rv[P][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_B, off, SO ? bo : 0, 0));
+          rv[P][NRV / 2 + v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_C, off, SO ? bo : 0, 0));
         }
       } else {
         const int bo = blk * (TB * 2 * NPL * 4);
 #pragma unroll
         for (int v = 0; v < NRV; ++v)
-          rv[P][v] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_bc, rec_voff + bo + v * 64, 0, 0));
+          rv[P][v] = __uint_as_float(
+              __builtin_amdgcn_raw_buffer_load_b32(rs_bc, rec_voff + v * 64 + (SO ? 0 : bo), SO ? bo : 0, 0));
       }
     };
     // float index within a block's records of B_t[n0 + j] and C_t[n0 + j], t = token q of the block
@@ -424,17 +433,18 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
       const int bo = blk * blk_bytes;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
-        ru[S][i] = buf_load<IO, VW>(rs_u, voff[i] + bo, 0);
-        rd[S][i] = buf_load<IO, VW>(rs_d, voff[i] + bo, 0);
+        ru[S][i] = buf_load<IO, VW>(rs_u, voff[i] + (SO ? 0 : bo), SO ? bo : 0);
+        rd[S][i] = buf_load<IO, VW>(rs_d, voff[i] + (SO ? 0 : bo), SO ? bo : 0);
       }
       if (FULL && has_z) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) rz[S][i] = buf_load<IO, VW>(rs_z, voff[i] + bo, 0);
+        for (int i = 0; i < RPT; ++i) rz[S][i] = buf_load<IO, VW>(rs_z, voff[i] + (SO ? 0 : bo), SO ? bo : 0);
       }
       if constexpr (TRAP && FULL) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
-          rcb[S][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_cb, (blk * TB + voff_rel[i]) * 4, 0, 0));
+          rcb[S][i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rs_cb, voff_rel[i] * 4 + (SO ? 0 : blk * TB * 4), SO ? blk * TB * 4 : 0, 0));
       }
     };
 
@@ -528,7 +538,7 @@ __global__ void __launch_bounds__(64 * G) scan_kernel(ScanParams p) {
             if (has_z) v *= silu_f(zf[e]);
             out[e] = v;
           }
-          if (pvalid) buf_store<IO, VW>(rs_y, voff[i] + bo, 0, out);
+          if (pvalid) buf_store<IO, VW>(rs_y, voff[i] + (SO ? 0 : bo), SO ? bo : 0, out);
         }
       }
     };
