@@ -166,6 +166,10 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   // prepares the next chunk's while the others finish the current one
   __shared__ __attribute__((aligned(16))) float sCS[2][Q];
   __shared__ __attribute__((aligned(16))) float sDL[2][Q];
+  // and per token, once: exp(cs_t) (the inter-chunk readout's fade) and exp(cs_end - cs_s) delta_s (the
+  // weight of token s in the state update)
+  __shared__ __attribute__((aligned(16))) float sECS[2][Q];
+  __shared__ __attribute__((aligned(16))) float sWS[2][Q];
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -254,7 +258,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
           rs_d, (t0 + lane) * H32 * 2, 0, 0)));
   };
   f32x4_t hacc[HT];
-  // H^T as bf16 pairs for the Y products, from the accumulators: four
+  // H^T in fp16 for the Y products, from the accumulators: four
   // consecutive states of one channel per lane (this wavefront's tiles only)
   auto stage_state = [&]() {
 #pragma unroll
@@ -273,7 +277,8 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   // k_stop chunks are done and the flag is set (thread 0 polls it, the
   // workgroup reads it through LDS); returns the first chunk not done.
   // (wavefront 0) the steps of the chunk at token t0 from the raw values in
-  // graw, and their cumulative sum times A, into parity buffer `par`
+  // graw, their cumulative sum times A, and the fades that depend on one token
+  // only, into parity buffer `par`
   auto steps = [&](int t0, int par) {
     const float xv = graw + biash;
     float dl = p.softplus ? softplus_f(xv) : xv;
@@ -284,8 +289,11 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       const float up = __shfl_up(cs, o, 64);
       cs += lane >= o ? up : 0.0f;
     }
+    const float cse = __shfl(cs, Q - 1, 64);
     sDL[par][lane] = dl;
     sCS[par][lane] = cs;
+    sECS[par][lane] = __builtin_amdgcn_exp2f(cs * kLog2eF);
+    sWS[par][lane] = __builtin_amdgcn_exp2f((cse - cs) * kLog2eF) * dl;
   };
   auto run_chunks = [&](int kb, int ke, const unsigned* stop_flag, int k_stop) -> int {
   if (ke <= kb) return kb;
@@ -390,20 +398,17 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
     }
     // ---- W^T[n][s] = exp(cs_end - cs_s) delta_s B[s][n], from the B rows in registers
     {
-      const float cse = sCS[par][Q - 1];
 #pragma unroll
       for (int i = 0; i < B_PER; ++i) {
         const int e = tid + NTH * i;
         if (e < B_ITEMS) {
           const int np = e % (N / 2), s0 = 4 * (e / (N / 2));
-          const f32x4_t css = *reinterpret_cast<const f32x4_t*>(&sCS[par][s0]);
-          const f32x4_t dls = *reinterpret_cast<const f32x4_t*>(&sDL[par][s0]);
+          const f32x4_t ws = *reinterpret_cast<const f32x4_t*>(&sWS[par][s0]);
           float v0[4], v1[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float ws = __builtin_amdgcn_exp2f((cse - css[r]) * kLog2eF) * dls[r];
-            v0[r] = ws * bf16_lo_of(gb[i][r]);
-            v1[r] = ws * bf16_hi_of(gb[i][r]);
+            v0[r] = ws[r] * bf16_lo_of(gb[i][r]);
+            v1[r] = ws[r] * bf16_hi_of(gb[i][r]);
           }
           u32x2_t hi, lo;
           split4_f16(v0, hi, lo);
@@ -420,11 +425,11 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
 
     // ---- Y = exp(cs_t) C H + M x  (token block ty, channel blocks py0, py0+1), then the epilogue
     {
-      const f32x4_t cst = *reinterpret_cast<const f32x4_t*>(&sCS[par][16 * ty + 4 * lq]);
+      const f32x4_t ecs = *reinterpret_cast<const f32x4_t*>(&sECS[par][16 * ty + 4 * lq]);
 #pragma unroll
       for (int c = 0; c < YT; ++c)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) yacc[c][j] *= __builtin_amdgcn_exp2f(cst[j] * kLog2eF);
+        for (int j = 0; j < 4; ++j) yacc[c][j] *= ecs[j];
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         if (32 * kk > 16 * ty + 15) continue;  // M is zero past the diagonal
@@ -458,7 +463,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
 
     // ---- H = exp(cs_end) H + W^T x  (channel block ph, state blocks nb0 + NBS i)
     {
-      const float fade = __builtin_amdgcn_exp2f(sCS[par][Q - 1] * kLog2eF);
+      const float fade = sECS[par][Q - 1];
 #pragma unroll
       for (int i = 0; i < HT; ++i)
 #pragma unroll
