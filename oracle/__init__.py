@@ -10,6 +10,12 @@ numpy arrays into it.  Parity pins are in ``tests/test_oracle_pins.py``.
 ``bwd.py`` is the backward pass: fp64 automatic differentiation (torch, CPU)
 of its own transcription of the forward, pinned in ``tests/test_oracle_bwd.py``
 against the C oracle's forward and central finite differences of it.
+``ssm_ref.c`` also holds a second backward, ``ssm_ref_scan_bwd`` (``ref.scan_bwd``):
+the hand-derived adjoint recurrence in C, threaded over channels, fast enough
+for whole layers; it is pinned in ``tests/test_oracle_bwd_c.py`` against
+central finite differences of the C forward, the relay example by hand and
+the automatic-differentiation backward, with planted mistakes in
+``tests/test_oracle_mutants.py``.
 ``ssd.py`` is the Mamba-2 SSD layer in its quadratic masked-matrix form (numpy),
 pinned in ``tests/test_oracle_ssd.py`` against the C oracle's recurrence.
 

@@ -35,6 +35,9 @@ def _load():
         lib.ssm_ref_scan_trap_fwd_ex.argtypes = lib.ssm_ref_scan_fwd_ex.argtypes
         lib.ssm_ref_state_update.restype = ctypes.c_int
         lib.ssm_ref_state_update.argtypes = [_dp] * 9 + [ctypes.c_int, _dp] + [ctypes.c_long] * 3
+        lib.ssm_ref_scan_bwd.restype = ctypes.c_int
+        lib.ssm_ref_scan_bwd.argtypes = ([_dp] * 8 + [ctypes.c_int] + [_dp] * 12 + [ctypes.c_long] * 4 +
+                                         [ctypes.c_int])
         lib.ssm_ref_pair_then.restype = None
         lib.ssm_ref_pair_then.argtypes = [ctypes.c_long] + [_dp] * 6
         lib.ssm_ref_softplus.restype = ctypes.c_double
@@ -116,6 +119,37 @@ def _scan_rows(fn, u, delta, A, B, C, D, z, delta_bias, softplus, initial_state,
     if rc != 0:
         raise ValueError("oracle scan rejected its arguments")
     return y, fs
+
+
+def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, dfinal_state=None,
+             initial_state=None, nthreads=1):
+    """Gradients of sum(y*dy) + sum(final_state*dfinal_state) with respect to every input of scan_fwd_ex
+    (batch rows, no packed sequences), by the C oracle's adjoint recurrence (ssm_ref_scan_bwd).
+
+    Returns a dict of float64 arrays: du, ddelta, dA, dB, dC, dinitial_state (zero initial state when none is
+    given), and dD, dz, ddelta_bias for the optional inputs that were given (None otherwise)."""
+    lib = _load()
+    u, delta, A, B, C, D, z, bias, h0, dy, dfs = map(_f64, (u, delta, A, B, C, D, z, delta_bias, initial_state,
+                                                           dy, dfinal_state))
+    batch, L, dim = u.shape
+    N = A.shape[1]
+    assert delta.shape == u.shape and dy.shape == u.shape and A.shape == (dim, N)
+    assert B.shape == (batch, L, N) and C.shape == (batch, L, N)
+    assert z is None or z.shape == u.shape
+    assert h0 is None or h0.shape == (batch, dim, N)
+    assert dfs is None or dfs.shape == (batch, dim, N)
+    out = {"du": np.empty(u.shape), "ddelta": np.empty(u.shape), "dA": np.empty((dim, N)),
+           "dB": np.empty(B.shape), "dC": np.empty(C.shape), "dinitial_state": np.empty((batch, dim, N)),
+           "dD": None if D is None else np.empty(dim), "dz": None if z is None else np.empty(u.shape),
+           "ddelta_bias": None if bias is None else np.empty(dim)}
+    rc = lib.ssm_ref_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(bias),
+                              1 if softplus else 0, _ptr(h0), _ptr(dy), _ptr(dfs), _ptr(out["du"]),
+                              _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
+                              _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
+                              _ptr(out["dinitial_state"]), batch, L, dim, N, int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle backward failed ({rc})")
+    return out
 
 
 def state_update(state, u, delta, A, B, C, D=None, z=None, delta_bias=None, softplus=True):

@@ -27,6 +27,7 @@
 #include <math.h>
 #include <pthread.h>
 #include <stddef.h>
+#include <stdlib.h>
 
 double ssm_ref_softplus(double x) {
   /* log(1 + e^x), written so that e^x never overflows:
@@ -237,4 +238,176 @@ int ssm_ref_state_update(double* state, const double* u, const double* delta,
     }
   }
   return 0;
+}
+
+/*
+ * Backward pass of the two-term scan (batch rows, optional initial state):
+ * the gradients of  sum_t y_t dy_t + sum_n final_state[n] dfinal_state[n]
+ * with respect to every input, by the adjoint of the recurrence, one
+ * (row, channel) at a time.  The pages only say that training recomputes the
+ * states instead of storing them ("Mamba is attention all you really need,
+ * part 2", "Keeping the pad on the desk"); the gradients themselves follow
+ * from the forward definition above.  With lambda_t the gradient reaching
+ * h_t (from y_t, and from h_{t+1} through the fade a_{t+1}):
+ *   lambda_{L-1} = dfinal_state + C_{L-1} dv_{L-1},
+ *   lambda_t     = C_t dv_t + a_{t+1} lambda_{t+1},      dv_t = dy_t SiLU(z_t),
+ * and for h_t = a_t h_{t-1} + Delta_t u_t B_t, a_t = exp(Delta_t A):
+ *   dDelta_t = sum_n lambda_t[n] (A[n] a_t[n] h_{t-1}[n] + u_t B_t[n]),
+ *   dA[n]   += lambda_t[n] Delta_t a_t[n] h_{t-1}[n],
+ *   du_t     = sum_n lambda_t[n] Delta_t B_t[n] + D dv_t,
+ *   dB_t[n] += lambda_t[n] Delta_t u_t,   dC_t[n] += dv_t h_t[n],
+ *   dz_t     = dy_t v_t SiLU'(z_t),       dD += dv_t u_t,
+ *   ddelta_t = dDelta_t sigmoid(x_t) (softplus' = sigmoid; 1 without softplus),
+ *   dbias   += ddelta_t,                  dinitial_state = a_0 lambda_0.
+ * dB, dC, dA, dD and dbias sum over channels or rows: each worker sums its
+ * own share, and the shares are added in worker order (deterministic).
+ */
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+typedef struct {
+  const double *u, *delta, *A, *B, *C, *D, *z, *bias, *h0, *dy, *dfs;
+  int softplus_flag;
+  long batch, L, dim, N;
+  double *du, *ddelta, *dz, *dinit;     /* per (row, channel): written directly */
+  double *dA, *dB, *dC, *dD, *dbias;    /* this worker's partial sums */
+  double* work;                          /* L*N + 2*L doubles: states, steps, pre-gate outputs */
+  long first, last;
+  int ok;
+} bwd_job;
+
+static void bwd_channels(bwd_job* j) {
+  const long L = j->L, N = j->N, dim = j->dim;
+  double* hs = j->work;            /* h_t[n] at hs[t*N + n] */
+  double* dls = hs + L * N;        /* Delta_t */
+  double* vs = dls + L;            /* v_t, before the gate */
+  double lam[4096], hprev[4096];
+  for (long rd = j->first; rd < j->last; ++rd) {
+    const long b = rd / dim, d = rd % dim;
+    const double* Ad = &j->A[d * N];
+    /* forward, keeping every state */
+    for (long n = 0; n < N; ++n) hprev[n] = j->h0 ? j->h0[(b * dim + d) * N + n] : 0.0;
+    for (long t = 0; t < L; ++t) {
+      const long io = (b * L + t) * dim + d, bc = (b * L + t) * N;
+      const double dl = step_delta(j->delta[io], j->bias, d, j->softplus_flag);
+      const double* hp = t ? &hs[(t - 1) * N] : hprev;
+      double v = 0.0;
+      for (long n = 0; n < N; ++n) {
+        const double h = exp(dl * Ad[n]) * hp[n] + dl * j->u[io] * j->B[bc + n];
+        hs[t * N + n] = h;
+        v += j->C[bc + n] * h;
+      }
+      dls[t] = dl;
+      vs[t] = v + (j->D ? j->D[d] * j->u[io] : 0.0);
+    }
+    /* backward */
+    for (long n = 0; n < N; ++n) lam[n] = j->dfs ? j->dfs[(b * dim + d) * N + n] : 0.0;
+    for (long t = L - 1; t >= 0; --t) {
+      const long io = (b * L + t) * dim + d, bc = (b * L + t) * N;
+      const double dl = dls[t], ut = j->u[io];
+      double dv = j->dy[io];
+      if (j->z) {
+        const double zt = j->z[io], s = sigmoid(zt);
+        j->dz[io] = j->dy[io] * vs[t] * s * (1.0 + zt * (1.0 - s));
+        dv = j->dy[io] * zt * s;
+      }
+      double du = j->D ? j->D[d] * dv : 0.0, ddl = 0.0;
+      if (j->D) j->dD[d] += dv * ut;
+      const double* hp = t ? &hs[(t - 1) * N] : hprev;
+      for (long n = 0; n < N; ++n) {
+        lam[n] += j->C[bc + n] * dv;
+        j->dC[bc + n] += dv * hs[t * N + n];
+        const double a = exp(dl * Ad[n]);
+        ddl += lam[n] * (Ad[n] * a * hp[n] + ut * j->B[bc + n]);
+        j->dA[d * N + n] += lam[n] * dl * a * hp[n];
+        du += lam[n] * dl * j->B[bc + n];
+        j->dB[bc + n] += lam[n] * dl * ut;
+        lam[n] *= a;                                   /* on to h_{t-1} */
+      }
+      j->du[io] = du;
+      const double x = j->delta[io] + (j->bias ? j->bias[d] : 0.0);
+      const double dx = j->softplus_flag ? ddl * sigmoid(x) : ddl;
+      j->ddelta[io] = dx;
+      if (j->bias) j->dbias[d] += dx;
+    }
+    if (j->dinit)
+      for (long n = 0; n < N; ++n) j->dinit[(b * dim + d) * N + n] = lam[n];
+  }
+}
+
+static void* bwd_worker(void* arg) {
+  bwd_channels((bwd_job*)arg);
+  return NULL;
+}
+
+int ssm_ref_scan_bwd(const double* u, const double* delta, const double* A,
+                     const double* B, const double* C, const double* D,
+                     const double* z, const double* delta_bias, int softplus_flag,
+                     const double* initial_state, const double* dy, const double* dfinal_state,
+                     double* du, double* ddelta, double* dA, double* dB, double* dC,
+                     double* dD, double* dz, double* ddelta_bias, double* dinitial_state,
+                     long batch, long L, long dim, long dstate, int nthreads) {
+  if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return -1;
+  if ((D && !dD) || (z && !dz) || (delta_bias && !ddelta_bias)) return -1;
+  if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 4096) return -1;
+  const long channels = batch * dim;
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (nthreads > channels) nthreads = (int)channels;
+  const long nA = dim * dstate, nBC = batch * L * dstate;
+  bwd_job jobs[256];
+  pthread_t tids[256];
+  int running[256];
+  int rc = 0;
+  for (int i = 0; i < nthreads; ++i) {
+    bwd_job j = {u, delta, A, B, C, D, z, delta_bias, initial_state, dy, dfinal_state, softplus_flag,
+                 batch, L, dim, dstate, du, ddelta, dz, dinitial_state,
+                 (double*)calloc((size_t)nA, sizeof(double)), (double*)calloc((size_t)nBC, sizeof(double)),
+                 (double*)calloc((size_t)nBC, sizeof(double)), (double*)calloc((size_t)dim, sizeof(double)),
+                 (double*)calloc((size_t)dim, sizeof(double)),
+                 (double*)malloc((size_t)(L * dstate + 2 * L) * sizeof(double)),
+                 channels * i / nthreads, channels * (i + 1) / nthreads, 1};
+    if (!j.dA || !j.dB || !j.dC || !j.dD || !j.dbias || !j.work) rc = -2;
+    jobs[i] = j;
+  }
+  if (rc == 0) {
+    for (int i = 0; i < nthreads; ++i) {
+      running[i] = nthreads > 1 && pthread_create(&tids[i], NULL, bwd_worker, &jobs[i]) == 0;
+      if (!running[i]) bwd_channels(&jobs[i]);
+    }
+    for (int i = 0; i < nthreads; ++i)
+      if (running[i]) pthread_join(tids[i], NULL);
+    /* the workers' partial sums, in worker order */
+    for (long e = 0; e < nA; ++e) {
+      double s = 0.0;
+      for (int i = 0; i < nthreads; ++i) s += jobs[i].dA[e];
+      dA[e] = s;
+    }
+    for (long e = 0; e < nBC; ++e) {
+      double sb = 0.0, sc = 0.0;
+      for (int i = 0; i < nthreads; ++i) {
+        sb += jobs[i].dB[e];
+        sc += jobs[i].dC[e];
+      }
+      dB[e] = sb;
+      dC[e] = sc;
+    }
+    for (long e = 0; e < dim; ++e) {
+      double sd = 0.0, sbias = 0.0;
+      for (int i = 0; i < nthreads; ++i) {
+        sd += jobs[i].dD[e];
+        sbias += jobs[i].dbias[e];
+      }
+      if (dD) dD[e] = sd;
+      if (ddelta_bias) ddelta_bias[e] = sbias;
+    }
+  }
+  for (int i = 0; i < nthreads; ++i) {
+    free(jobs[i].dA);
+    free(jobs[i].dB);
+    free(jobs[i].dC);
+    free(jobs[i].dD);
+    free(jobs[i].dbias);
+    free(jobs[i].work);
+  }
+  return rc;
 }

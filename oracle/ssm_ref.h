@@ -83,6 +83,27 @@ int ssm_ref_scan_trap_fwd_ex(const double* u, const double* delta, const double*
                              double* y, double* final_state,
                              long batch, long L, long dim, long dstate, int nthreads);
 
+/* Backward of ssm_ref_scan_fwd_ex without packed sequences: the gradients of
+ *   sum(y * dy) + sum(final_state * dfinal_state)
+ * with respect to every input, by the adjoint recurrence run backwards over
+ * each (row, channel) after a forward pass that keeps its states.
+ *   dy, du, ddelta, dz: [batch, L, dim];  dB, dC: [batch, L, dstate];
+ *   dA: [dim, dstate];  dD, ddelta_bias: [dim];
+ *   dfinal_state, initial_state, dinitial_state: [batch, dim, dstate].
+ * dfinal_state, initial_state (NULL: zero) and dinitial_state are optional;
+ * dD, dz and ddelta_bias are required exactly when D, z and delta_bias are
+ * given.  Sums over rows or channels (dA, dB, dC, dD, ddelta_bias) are added
+ * per worker and then across workers in worker order, so a result depends
+ * on nthreads only through that order.  Returns 0, -1 on bad arguments, -2
+ * when its work buffers cannot be allocated. */
+int ssm_ref_scan_bwd(const double* u, const double* delta, const double* A,
+                     const double* B, const double* C, const double* D,
+                     const double* z, const double* delta_bias, int softplus_flag,
+                     const double* initial_state, const double* dy, const double* dfinal_state,
+                     double* du, double* ddelta, double* dA, double* dB, double* dC,
+                     double* dD, double* dz, double* ddelta_bias, double* dinitial_state,
+                     long batch, long L, long dim, long dstate, int nthreads);
+
 /* One recurrent (decode) step from the given state, updated in place.
  *   u, delta, z, y: [batch, dim];  B, C: [batch, dstate];
  *   state: [batch, dim, dstate].  Same arithmetic as one step of the scan. */

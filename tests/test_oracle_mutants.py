@@ -13,6 +13,7 @@ import pytest
 import oracle.ref as R
 from oracle import build as OB
 import tests.test_oracle_pins as P
+import tests.test_oracle_bwd_c as PB
 import tests.test_oracle_trap as PT
 
 SRC = os.path.join(os.path.dirname(OB.__file__), "ssm_ref.c")
@@ -54,6 +55,32 @@ TRAP_MUTANTS = {
                           "  double v = acc;\n  if (zt) v = v * ssm_ref_silu(*zt);\n  return v;\n}\n\ntypedef"),
 }
 
+# Mistakes in the backward oracle's adjoint recurrence, caught by the pins of test_oracle_bwd_c.py.
+BWD_MUTANTS = {
+    "bwd_adjoint_not_faded": ("        lam[n] *= a;                                   /* on to h_{t-1} */\n", ""),
+    "bwd_dC_reads_previous_state": ("j->dC[bc + n] += dv * hs[t * N + n];", "j->dC[bc + n] += dv * hp[n];"),
+    "bwd_step_gradient_misses_fade_term": ("ddl += lam[n] * (Ad[n] * a * hp[n] + ut * j->B[bc + n]);",
+                                           "ddl += lam[n] * (ut * j->B[bc + n]);"),
+    "bwd_dA_misses_step": ("j->dA[d * N + n] += lam[n] * dl * a * hp[n];", "j->dA[d * N + n] += lam[n] * a * hp[n];"),
+    "bwd_softplus_derivative_dropped": ("const double dx = j->softplus_flag ? ddl * sigmoid(x) : ddl;",
+                                        "const double dx = ddl;"),
+    "bwd_gate_derivative_is_sigmoid": ("j->dz[io] = j->dy[io] * vs[t] * s * (1.0 + zt * (1.0 - s));",
+                                       "j->dz[io] = j->dy[io] * vs[t] * s;"),
+    "bwd_skip_gradient_dropped": ("double du = j->D ? j->D[d] * dv : 0.0, ddl = 0.0;", "double du = 0.0, ddl = 0.0;"),
+    "bwd_dB_from_output_gradient": ("j->dB[bc + n] += lam[n] * dl * ut;", "j->dB[bc + n] += dv * dl * ut;"),
+    "bwd_only_first_worker_summed": ("for (int i = 0; i < nthreads; ++i) s += jobs[i].dA[e];",
+                                     "s += jobs[0].dA[e];"),
+    "bwd_final_state_gradient_ignored": ("lam[n] = j->dfs ? j->dfs[(b * dim + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
+}
+
+BWD_PINS = [
+    lambda: PB.test_gradients_match_central_differences(True, True, True, True),
+    lambda: PB.test_gradients_match_central_differences(False, False, True, False),
+    PB.test_relay_example_gradients_by_hand,
+    lambda: PB.test_agrees_with_autograd_oracle("all"),
+    PB.test_thread_count_changes_only_the_order_of_sums,
+]
+
 TRAP_PINS = [
     PT.test_impulse_response_by_hand,
     PT.test_constant_inputs_closed_form,
@@ -79,10 +106,11 @@ PINS = [
 ]
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(TRAP_MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(TRAP_MUTANTS) + sorted(BWD_MUTANTS))
 def test_mutant_is_caught(name, tmp_path, monkeypatch):
-    old, new = MUTANTS[name] if name in MUTANTS else TRAP_MUTANTS[name]
-    pins = PINS if name in MUTANTS else TRAP_PINS
+    for table, table_pins in ((MUTANTS, PINS), (TRAP_MUTANTS, TRAP_PINS), (BWD_MUTANTS, BWD_PINS)):
+        if name in table:
+            (old, new), pins = table[name], table_pins
     src = open(SRC).read()
     assert src.count(old) >= 1, f"mutation site for {name} not found"
     mutated = src.replace(old, new, 1)
