@@ -1,7 +1,9 @@
 """GPU parity of the backward pass (ssm_scan_bwd through the C ABI) against the fp64 oracle.
 
-Every gradient is compared element by element with oracle/bwd.py on the same
-(rounded) inputs, with the error measure of gpu_util.rel_err.  Tolerances:
+Every gradient is compared element by element with the fp64 oracle on the same
+(rounded) inputs: oracle/bwd.py (automatic differentiation) at the small shapes,
+the C adjoint recurrence (oracle ref.scan_bwd) on the whole 2.8B-shaped layer;
+the error measure is gpu_util.rel_err.  Tolerances:
 1e-4 for fp32 storage and for the fp32 outputs (dA, dD, d bias); 2e-2 for the
 outputs stored in bf16 (du, d delta, dz, dB, dC), whose rounding alone is up
 to 2^-9.
@@ -11,10 +13,11 @@ import pytest
 import torch
 
 from oracle import bwd as OB
+from oracle import ref as R
 from selective_state_space_33_amd import inputs as I
 from selective_state_space_33_amd import ops
 
-from .gpu_util import TOL, BwdChained, rel_err, say, to_dev, to_dev_f32
+from .gpu_util import TOL, BwdChained, oracle_threads, rel_err, say, to_dev, to_dev_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -165,12 +168,12 @@ def test_bwd_extreme_steps():
     _run_and_compare(x, dy, dfs, "f32", label="extreme steps")
 
 
-def test_bwd_full_size_sampled_channels():
+def test_bwd_full_size_all_outputs():
     """The backward at the shape the benchmark times (4 x 4096 x 5120 x 16 bf16, z, D, bias, softplus on, the
     chained plan: 256 whole tiles and 64 cut into 4 chunks of blocks, the checkpoint pass chained alike), with a
-    gradient on the final state.  du, d delta and dz of 12 sampled channels in every batch row (48 (row, channel)
-    recurrences) and dA, dD, d bias of those channels -- each a sum over all 16384 (row, token) terms -- against
-    the oracle run on those channels (a channel's gradients depend on its own inputs, B, C and dy only)."""
+    gradient on the final state: every gradient of every (row, channel) -- du, d delta, dz; dB and dC, each a
+    sum over all 5120 channels; dA, dD and d bias, each a sum over all 16384 (row, token) terms -- against the
+    C oracle's adjoint recurrence (ref.scan_bwd) on the whole layer."""
     w = I.WORKLOADS["mamba2p8b_bf16"]
     x = I.make_inputs(w, 0)
     rng = np.random.default_rng(4242)
@@ -182,20 +185,18 @@ def test_bwd_full_size_sampled_channels():
                          z=to_dev(x["z"], "bf16"), delta_bias=to_dev_f32(x["delta_bias"]),
                          dfinal_state=to_dev_f32(dfs), check_status=True)
     torch.cuda.synchronize()
-    ds = np.sort(rng.choice(w.dim, size=12, replace=False))
-    ds[0], ds[-1] = 0, w.dim - 1   # tile edges of the first and last tile
-    dsel = torch.from_numpy(ds).to(g["du"].device)
-    got = {k: g[k].index_select(-1, dsel).float().cpu().numpy().astype(np.float64) for k in ("du", "ddelta", "dz")}
-    for k in ("dD", "ddelta_bias"):
-        got[k] = g[k][dsel].cpu().numpy().astype(np.float64)
-    got["dA"] = g["dA"][dsel].cpu().numpy().astype(np.float64)
+    got = {k: g[k].float().cpu().numpy().astype(np.float64) for k in SEQ_OUT + ("dA", "dD", "ddelta_bias")}
     del g
-    o = OB.scan_bwd(x["u"][:, :, ds], x["delta"][:, :, ds], x["A"][ds], x["B"], x["C"], dy[:, :, ds], D=x["D"][ds],
-                    z=x["z"][:, :, ds], delta_bias=x["delta_bias"][ds], dfinal_state=dfs[:, ds])
-    errs = {k: rel_err(got[k], o[k]) for k in got}
-    print("[parity] bwd full size, 48 sampled (row, channel) pairs: " +
+    torch.cuda.empty_cache()
+    o = R.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                   dfinal_state=dfs, nthreads=oracle_threads())
+    errs = {}
+    for k in got:
+        errs[k] = rel_err(got[k], o[k])
+        del o[k]
+    print(f"[parity] bwd full size, all {w.batch * w.dim} (row, channel) pairs: " +
           "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
-    for k in ("du", "ddelta", "dz"):
+    for k in SEQ_OUT:
         assert errs[k] <= TOL["bf16"], (k, errs[k])
     for k in ("dA", "dD", "ddelta_bias"):
         assert errs[k] <= TOL["f32"], (k, errs[k])
