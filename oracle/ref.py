@@ -38,6 +38,8 @@ def _load():
         lib.ssm_ref_scan_bwd.restype = ctypes.c_int
         lib.ssm_ref_scan_bwd.argtypes = ([_dp] * 8 + [ctypes.c_int] + [_dp] * 12 + [ctypes.c_long] * 4 +
                                          [ctypes.c_int])
+        lib.ssm_ref_scan_trap_bwd.restype = ctypes.c_int
+        lib.ssm_ref_scan_trap_bwd.argtypes = lib.ssm_ref_scan_bwd.argtypes
         lib.ssm_ref_pair_then.restype = None
         lib.ssm_ref_pair_then.argtypes = [ctypes.c_long] + [_dp] * 6
         lib.ssm_ref_softplus.restype = ctypes.c_double
@@ -122,9 +124,10 @@ def _scan_rows(fn, u, delta, A, B, C, D, z, delta_bias, softplus, initial_state,
 
 
 def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=True, dfinal_state=None,
-             initial_state=None, nthreads=1):
+             initial_state=None, nthreads=1, rule="euler"):
     """Gradients of sum(y*dy) + sum(final_state*dfinal_state) with respect to every input of scan_fwd_ex
-    (batch rows, no packed sequences), by the C oracle's adjoint recurrence (ssm_ref_scan_bwd).
+    (rule "euler") or scan_trap_fwd_ex (rule "trap"), batch rows, no packed sequences, by the C oracle's adjoint
+    recurrence (ssm_ref_scan_bwd, ssm_ref_scan_trap_bwd).
 
     Returns a dict of float64 arrays: du, ddelta, dA, dB, dC, dinitial_state (zero initial state when none is
     given), and dD, dz, ddelta_bias for the optional inputs that were given (None otherwise)."""
@@ -142,11 +145,11 @@ def scan_bwd(u, delta, A, B, C, dy, D=None, z=None, delta_bias=None, softplus=Tr
            "dB": np.empty(B.shape), "dC": np.empty(C.shape), "dinitial_state": np.empty((batch, dim, N)),
            "dD": None if D is None else np.empty(dim), "dz": None if z is None else np.empty(u.shape),
            "ddelta_bias": None if bias is None else np.empty(dim)}
-    rc = lib.ssm_ref_scan_bwd(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(bias),
-                              1 if softplus else 0, _ptr(h0), _ptr(dy), _ptr(dfs), _ptr(out["du"]),
-                              _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]),
-                              _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]),
-                              _ptr(out["dinitial_state"]), batch, L, dim, N, int(nthreads))
+    fn = {"euler": lib.ssm_ref_scan_bwd, "trap": lib.ssm_ref_scan_trap_bwd}[rule]
+    rc = fn(_ptr(u), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(bias), 1 if softplus else 0,
+            _ptr(h0), _ptr(dy), _ptr(dfs), _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA"]), _ptr(out["dB"]),
+            _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dz"]), _ptr(out["ddelta_bias"]), _ptr(out["dinitial_state"]),
+            batch, L, dim, N, int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle backward failed ({rc})")
     return out

@@ -259,6 +259,14 @@ int ssm_ref_state_update(double* state, const double* u, const double* delta,
  *   dz_t     = dy_t v_t SiLU'(z_t),       dD += dv_t u_t,
  *   ddelta_t = dDelta_t sigmoid(x_t) (softplus' = sigmoid; 1 without softplus),
  *   dbias   += ddelta_t,                  dinitial_state = a_0 lambda_0.
+ * With the trapezoidal rule (ssm_ref_scan_trap_bwd), h_t = a_t h_{t-1} +
+ * beta_t B_{t-1} u_{t-1} + gamma_t B_t u_t with beta_t = Delta_t/2 a_t and
+ * gamma_t = Delta_t/2 (no previous term at a row's first token), so besides
+ * the fade's terms
+ *   dDelta_t += sum_n lambda_t[n] (B_t u_t / 2 + B_{t-1} u_{t-1} (a_t/2 + Delta_t/2 A a_t)),
+ *   dA[n]   += lambda_t[n] B_{t-1}[n] u_{t-1} Delta_t^2/2 a_t[n],
+ * and the input terms reach both tokens: du_t and dB_t through gamma_t,
+ * du_{t-1} and dB_{t-1} through beta_t.
  * dB, dC, dA, dD and dbias sum over channels or rows: each worker sums its
  * own share, and the shares are added in worker order (deterministic).
  */
@@ -267,6 +275,7 @@ static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 typedef struct {
   const double *u, *delta, *A, *B, *C, *D, *z, *bias, *h0, *dy, *dfs;
   int softplus_flag;
+  int trapezoid;                         /* the three-term recurrence of ssm_ref_scan_trap_fwd_ex */
   long batch, L, dim, N;
   double *du, *ddelta, *dz, *dinit;     /* per (row, channel): written directly */
   double *dA, *dB, *dC, *dD, *dbias;    /* this worker's partial sums */
@@ -292,7 +301,14 @@ static void bwd_channels(bwd_job* j) {
       const double* hp = t ? &hs[(t - 1) * N] : hprev;
       double v = 0.0;
       for (long n = 0; n < N; ++n) {
-        const double h = exp(dl * Ad[n]) * hp[n] + dl * j->u[io] * j->B[bc + n];
+        const double a = exp(dl * Ad[n]);
+        double h;
+        if (j->trapezoid) {   /* the previous token's input (none at a row's first token), then this one's */
+          const double prev_in = t ? 0.5 * dl * a * j->B[bc - N + n] * j->u[io - dim] : 0.0;
+          h = a * hp[n] + prev_in + 0.5 * dl * j->B[bc + n] * j->u[io];
+        } else {
+          h = a * hp[n] + dl * j->u[io] * j->B[bc + n];
+        }
         hs[t * N + n] = h;
         v += j->C[bc + n] * h;
       }
@@ -301,6 +317,7 @@ static void bwd_channels(bwd_job* j) {
     }
     /* backward */
     for (long n = 0; n < N; ++n) lam[n] = j->dfs ? j->dfs[(b * dim + d) * N + n] : 0.0;
+    double du_next = 0.0;   /* trapezoidal rule: the part of du_t that step t+1 contributes */
     for (long t = L - 1; t >= 0; --t) {
       const long io = (b * L + t) * dim + d, bc = (b * L + t) * N;
       const double dl = dls[t], ut = j->u[io];
@@ -311,16 +328,33 @@ static void bwd_channels(bwd_job* j) {
         dv = j->dy[io] * zt * s;
       }
       double du = j->D ? j->D[d] * dv : 0.0, ddl = 0.0;
+      du += du_next;
+      du_next = 0.0;
       if (j->D) j->dD[d] += dv * ut;
       const double* hp = t ? &hs[(t - 1) * N] : hprev;
       for (long n = 0; n < N; ++n) {
         lam[n] += j->C[bc + n] * dv;
         j->dC[bc + n] += dv * hs[t * N + n];
         const double a = exp(dl * Ad[n]);
-        ddl += lam[n] * (Ad[n] * a * hp[n] + ut * j->B[bc + n]);
-        j->dA[d * N + n] += lam[n] * dl * a * hp[n];
-        du += lam[n] * dl * j->B[bc + n];
-        j->dB[bc + n] += lam[n] * dl * ut;
+        if (j->trapezoid) {
+          /* h_t = a h_{t-1} + (dl/2) a B_{t-1} u_{t-1} + (dl/2) B_t u_t */
+          ddl += lam[n] * (Ad[n] * a * hp[n] + 0.5 * ut * j->B[bc + n]);
+          j->dA[d * N + n] += lam[n] * dl * a * hp[n];
+          du += lam[n] * 0.5 * dl * j->B[bc + n];
+          j->dB[bc + n] += lam[n] * 0.5 * dl * ut;
+          if (t) {
+            const double bu = j->B[bc - N + n] * j->u[io - dim];     /* B_{t-1} u_{t-1} */
+            ddl += lam[n] * bu * (0.5 * a + 0.5 * dl * Ad[n] * a);   /* d beta / d delta */
+            j->dA[d * N + n] += lam[n] * bu * 0.5 * dl * dl * a;     /* d beta / d A */
+            du_next += lam[n] * 0.5 * dl * a * j->B[bc - N + n];
+            j->dB[bc - N + n] += lam[n] * 0.5 * dl * a * j->u[io - dim];
+          }
+        } else {
+          ddl += lam[n] * (Ad[n] * a * hp[n] + ut * j->B[bc + n]);
+          j->dA[d * N + n] += lam[n] * dl * a * hp[n];
+          du += lam[n] * dl * j->B[bc + n];
+          j->dB[bc + n] += lam[n] * dl * ut;
+        }
         lam[n] *= a;                                   /* on to h_{t-1} */
       }
       j->du[io] = du;
@@ -339,13 +373,13 @@ static void* bwd_worker(void* arg) {
   return NULL;
 }
 
-int ssm_ref_scan_bwd(const double* u, const double* delta, const double* A,
-                     const double* B, const double* C, const double* D,
-                     const double* z, const double* delta_bias, int softplus_flag,
-                     const double* initial_state, const double* dy, const double* dfinal_state,
-                     double* du, double* ddelta, double* dA, double* dB, double* dC,
-                     double* dD, double* dz, double* ddelta_bias, double* dinitial_state,
-                     long batch, long L, long dim, long dstate, int nthreads) {
+static int scan_bwd_rows(const double* u, const double* delta, const double* A,
+                         const double* B, const double* C, const double* D,
+                         const double* z, const double* delta_bias, int softplus_flag,
+                         const double* initial_state, const double* dy, const double* dfinal_state,
+                         double* du, double* ddelta, double* dA, double* dB, double* dC,
+                         double* dD, double* dz, double* ddelta_bias, double* dinitial_state,
+                         long batch, long L, long dim, long dstate, int nthreads, int trapezoid) {
   if (!u || !delta || !A || !B || !C || !dy || !du || !ddelta || !dA || !dB || !dC) return -1;
   if ((D && !dD) || (z && !dz) || (delta_bias && !ddelta_bias)) return -1;
   if (batch <= 0 || L <= 0 || dim <= 0 || dstate <= 0 || dstate > 4096) return -1;
@@ -359,7 +393,7 @@ int ssm_ref_scan_bwd(const double* u, const double* delta, const double* A,
   int running[256];
   int rc = 0;
   for (int i = 0; i < nthreads; ++i) {
-    bwd_job j = {u, delta, A, B, C, D, z, delta_bias, initial_state, dy, dfinal_state, softplus_flag,
+    bwd_job j = {u, delta, A, B, C, D, z, delta_bias, initial_state, dy, dfinal_state, softplus_flag, trapezoid,
                  batch, L, dim, dstate, du, ddelta, dz, dinitial_state,
                  (double*)calloc((size_t)nA, sizeof(double)), (double*)calloc((size_t)nBC, sizeof(double)),
                  (double*)calloc((size_t)nBC, sizeof(double)), (double*)calloc((size_t)dim, sizeof(double)),
@@ -410,4 +444,28 @@ int ssm_ref_scan_bwd(const double* u, const double* delta, const double* A,
     free(jobs[i].work);
   }
   return rc;
+}
+
+int ssm_ref_scan_bwd(const double* u, const double* delta, const double* A,
+                     const double* B, const double* C, const double* D,
+                     const double* z, const double* delta_bias, int softplus_flag,
+                     const double* initial_state, const double* dy, const double* dfinal_state,
+                     double* du, double* ddelta, double* dA, double* dB, double* dC,
+                     double* dD, double* dz, double* ddelta_bias, double* dinitial_state,
+                     long batch, long L, long dim, long dstate, int nthreads) {
+  return scan_bwd_rows(u, delta, A, B, C, D, z, delta_bias, softplus_flag, initial_state, dy, dfinal_state,
+                       du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, batch, L, dim, dstate,
+                       nthreads, 0);
+}
+
+int ssm_ref_scan_trap_bwd(const double* u, const double* delta, const double* A,
+                          const double* B, const double* C, const double* D,
+                          const double* z, const double* delta_bias, int softplus_flag,
+                          const double* initial_state, const double* dy, const double* dfinal_state,
+                          double* du, double* ddelta, double* dA, double* dB, double* dC,
+                          double* dD, double* dz, double* ddelta_bias, double* dinitial_state,
+                          long batch, long L, long dim, long dstate, int nthreads) {
+  return scan_bwd_rows(u, delta, A, B, C, D, z, delta_bias, softplus_flag, initial_state, dy, dfinal_state,
+                       du, ddelta, dA, dB, dC, dD, dz, ddelta_bias, dinitial_state, batch, L, dim, dstate,
+                       nthreads, 1);
 }

@@ -104,6 +104,17 @@ int ssm_ref_scan_bwd(const double* u, const double* delta, const double* A,
                      double* dD, double* dz, double* ddelta_bias, double* dinitial_state,
                      long batch, long L, long dim, long dstate, int nthreads);
 
+/* The same backward for the trapezoidal three-term recurrence of
+ * ssm_ref_scan_trap_fwd_ex (batch rows, no packed sequences); arguments as
+ * ssm_ref_scan_bwd. */
+int ssm_ref_scan_trap_bwd(const double* u, const double* delta, const double* A,
+                          const double* B, const double* C, const double* D,
+                          const double* z, const double* delta_bias, int softplus_flag,
+                          const double* initial_state, const double* dy, const double* dfinal_state,
+                          double* du, double* ddelta, double* dA, double* dB, double* dC,
+                          double* dD, double* dz, double* ddelta_bias, double* dinitial_state,
+                          long batch, long L, long dim, long dstate, int nthreads);
+
 /* One recurrent (decode) step from the given state, updated in place.
  *   u, delta, z, y: [batch, dim];  B, C: [batch, dstate];
  *   state: [batch, dim, dstate].  Same arithmetic as one step of the scan. */

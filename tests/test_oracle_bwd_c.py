@@ -136,3 +136,71 @@ def test_thread_count_changes_only_the_order_of_sums():
     for k in ("dA", "dB", "dC", "dD", "ddelta_bias"):     # sums over channels or rows: the order may differ
         assert _rel(g5[k], g1[k]) < 1e-13, k
     assert all(np.array_equal(_bwd(x, dy, dfs, nthreads=5)[k], g5[k]) for k in g5 if g5[k] is not None)
+
+
+# The trapezoidal rule (ssm_ref_scan_trap_bwd): the backward of ssm_ref_scan_trap_fwd_ex, pinned the same way
+# against that forward.
+
+@pytest.mark.parametrize("softplus,gated,with_h0", [(True, True, True), (False, False, False)])
+def test_trap_gradients_match_central_differences(softplus, gated, with_h0):
+    rng = np.random.default_rng(61 + 2 * softplus + with_h0)
+    batch, L, dim, N = 2, 7, 3, 4
+    x = _inputs(rng, batch, L, dim, N, gated=gated, with_D=gated, with_bias=gated)
+    if not softplus:
+        x["delta"] = np.abs(x["delta"]) + 0.05
+    h0 = rng.standard_normal((batch, dim, N)) if with_h0 else None
+    dy = rng.standard_normal((batch, L, dim))
+    dfs = rng.standard_normal((batch, dim, N))
+    g = R.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                   softplus=softplus, dfinal_state=dfs, initial_state=h0, rule="trap")
+
+    def obj():
+        y, fs = R.scan_trap_fwd_ex(x["u"], x["delta"], x["A"], x["B"], x["C"], D=x["D"], z=x["z"],
+                                   delta_bias=x["delta_bias"], softplus=softplus, initial_state=h0)
+        return float(np.sum(y * dy) + np.sum(fs * dfs))
+
+    arrays = [(x[n], "d" + n) for n in ["u", "delta", "A", "B", "C", "D", "z", "delta_bias"]]
+    if h0 is not None:
+        arrays.append((h0, "dinitial_state"))
+    checked = 0
+    for arr, name in arrays:
+        if arr is None:
+            assert g[name] is None, name
+            continue
+        flat = arr.reshape(-1)
+        for i in rng.choice(flat.size, size=min(6, flat.size), replace=False):
+            e = 1e-6 * max(1.0, abs(flat[i]))
+            o = flat[i]
+            flat[i] = o + e
+            fp = obj()
+            flat[i] = o - e
+            fm = obj()
+            flat[i] = o
+            fd = (fp - fm) / (2 * e)
+            an = g[name].reshape(-1)[i]
+            assert abs(an - fd) <= 2e-7 * max(1.0, abs(fd)), (name, i, an, fd)
+            checked += 1
+    assert checked >= 24
+
+
+@pytest.mark.parametrize("opts", ["all", "no_z", "no_softplus", "h0"])
+def test_trap_agrees_with_autograd_oracle(opts):
+    rng = np.random.default_rng(70 + ["all", "no_z", "no_softplus", "h0"].index(opts))
+    batch, L, dim, N = 2, 29, 5, 6
+    x = _inputs(rng, batch, L, dim, N, gated=opts != "no_z")
+    softplus = opts != "no_softplus"
+    if not softplus:
+        x["delta"] = np.abs(x["delta"]) + 0.05
+    h0 = rng.standard_normal((batch, dim, N)) * 0.5 if opts == "h0" else None
+    dy = rng.standard_normal((batch, L, dim))
+    dfs = rng.standard_normal((batch, dim, N))
+    a = R.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                   softplus=softplus, dfinal_state=dfs, initial_state=h0, nthreads=2, rule="trap")
+    b = OB.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                    softplus=softplus, dfinal_state=dfs, initial_state=h0, rule="trap")
+    for k in ("du", "ddelta", "dA", "dB", "dC", "dD", "dz", "ddelta_bias"):
+        assert (a[k] is None) == (b[k] is None), k
+        if a[k] is not None:
+            assert _rel(a[k], b[k]) < 1e-12, (k, _rel(a[k], b[k]))
+    if h0 is not None:
+        assert _rel(a["dinitial_state"], b["dinitial_state"]) < 1e-12

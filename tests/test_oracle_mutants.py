@@ -71,6 +71,12 @@ BWD_MUTANTS = {
     "bwd_only_first_worker_summed": ("for (int i = 0; i < nthreads; ++i) s += jobs[i].dA[e];",
                                      "s += jobs[0].dA[e];"),
     "bwd_final_state_gradient_ignored": ("lam[n] = j->dfs ? j->dfs[(b * dim + d) * N + n] : 0.0;", "lam[n] = 0.0;"),
+    "bwd_trap_previous_input_gradient_to_current_token": (
+        "            du_next += lam[n] * 0.5 * dl * a * j->B[bc - N + n];",
+        "            du += lam[n] * 0.5 * dl * a * j->B[bc - N + n];"),
+    "bwd_trap_beta_step_derivative_without_fade": (
+        "ddl += lam[n] * bu * (0.5 * a + 0.5 * dl * Ad[n] * a);", "ddl += lam[n] * bu * 0.5;"),
+    "bwd_trap_current_input_full_step": ("du += lam[n] * 0.5 * dl * j->B[bc + n];", "du += lam[n] * dl * j->B[bc + n];"),
 }
 
 BWD_PINS = [
@@ -79,6 +85,8 @@ BWD_PINS = [
     PB.test_relay_example_gradients_by_hand,
     lambda: PB.test_agrees_with_autograd_oracle("all"),
     PB.test_thread_count_changes_only_the_order_of_sums,
+    lambda: PB.test_trap_gradients_match_central_differences(True, True, True),
+    lambda: PB.test_trap_agrees_with_autograd_oracle("all"),
 ]
 
 TRAP_PINS = [
