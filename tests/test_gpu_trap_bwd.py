@@ -1,16 +1,18 @@
-"""GPU parity of the trapezoidal rule's backward (ssm_scan_trap_bwd through the C ABI) against the fp64 oracle
-(oracle/bwd.py with rule="trap", pinned by central differences of the C oracle's trapezoidal forward in
-test_oracle_bwd.py).  Tolerances as for the two-term backward: 1e-4 for fp32 storage and the fp32 outputs, 2e-2
+"""GPU parity of the trapezoidal rule's backward (ssm_scan_trap_bwd through the C ABI) against the fp64 oracles:
+oracle/bwd.py with rule="trap" at the small shapes (pinned by central differences of the C oracle's trapezoidal
+forward in test_oracle_bwd.py), and the C adjoint (ref.scan_bwd, rule="trap", pinned in test_oracle_bwd_c.py) on
+the whole 2.8B-shaped layer.  Tolerances as for the two-term backward: 1e-4 for fp32 storage and the fp32 outputs, 2e-2
 for the gradients stored in bf16."""
 import numpy as np
 import pytest
 import torch
 
 from oracle import bwd as OB
+from oracle import ref as R
 from selective_state_space_33_amd import inputs as I
 from selective_state_space_33_amd import ops
 
-from .gpu_util import TOL, rel_err, say, to_dev, to_dev_f32
+from .gpu_util import TOL, oracle_threads, rel_err, say, to_dev, to_dev_f32
 from .test_gpu_bwd import F32_OUT, SEQ_OUT, _case, _packed_case, _round
 
 pytestmark = pytest.mark.gpu
@@ -104,9 +106,11 @@ def test_trap_bwd_deterministic():
             assert torch.equal(g1[k], g2[k]), k
 
 
-def test_trap_bwd_full_size_sampled_channels():
-    """The 2.8B-shaped layer (4 x 4096 x 5120 x 16 bf16, every optional input, a final-state gradient): du, d delta,
-    dz, dA, dD and d bias of 12 sampled channels per row against the oracle run on those channels."""
+def test_trap_bwd_full_size_all_outputs():
+    """The 2.8B-shaped layer (4 x 4096 x 5120 x 16 bf16, every optional input, a final-state gradient): every
+    gradient of every (row, channel) -- du, d delta, dz; dB and dC summed over all 5120 channels; dA, dD and d bias
+    summed over all 16384 (row, token) terms -- against the C oracle's trapezoidal adjoint (ref.scan_bwd with
+    rule="trap") on the whole layer."""
     w = I.WORKLOADS["mamba2p8b_bf16"]
     x = I.make_inputs(w, 0)
     rng = np.random.default_rng(4545)
@@ -118,19 +122,18 @@ def test_trap_bwd_full_size_sampled_channels():
                          z=to_dev(x["z"], "bf16"), delta_bias=to_dev_f32(x["delta_bias"]),
                          dfinal_state=to_dev_f32(dfs), trapezoid=True, check_status=True)
     torch.cuda.synchronize()
-    ds = np.sort(rng.choice(w.dim, size=12, replace=False))
-    ds[0], ds[-1] = 0, w.dim - 1
-    dsel = torch.from_numpy(ds).to(g["du"].device)
-    got = {k: g[k].index_select(-1, dsel).float().cpu().numpy().astype(np.float64) for k in ("du", "ddelta", "dz")}
-    for k in ("dD", "ddelta_bias", "dA"):
-        got[k] = g[k][dsel].cpu().numpy().astype(np.float64)
+    got = {k: g[k].float().cpu().numpy().astype(np.float64) for k in SEQ_OUT + ("dA", "dD", "ddelta_bias")}
     del g
-    o = OB.scan_bwd(x["u"][:, :, ds], x["delta"][:, :, ds], x["A"][ds], x["B"], x["C"], dy[:, :, ds], D=x["D"][ds],
-                    z=x["z"][:, :, ds], delta_bias=x["delta_bias"][ds], dfinal_state=dfs[:, ds], rule="trap")
-    errs = {k: rel_err(got[k], o[k]) for k in got}
-    print("[parity] trap bwd full size, 48 sampled (row, channel) pairs: " +
+    torch.cuda.empty_cache()
+    o = R.scan_bwd(x["u"], x["delta"], x["A"], x["B"], x["C"], dy, D=x["D"], z=x["z"], delta_bias=x["delta_bias"],
+                   dfinal_state=dfs, nthreads=oracle_threads(), rule="trap")
+    errs = {}
+    for k in got:
+        errs[k] = rel_err(got[k], o[k])
+        del o[k]
+    print(f"[parity] trap bwd full size, all {w.batch * w.dim} (row, channel) pairs: " +
           "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
-    for k in ("du", "ddelta", "dz"):
+    for k in SEQ_OUT:
         assert errs[k] <= TOL["bf16"], (k, errs[k])
     for k in ("dA", "dD", "ddelta_bias"):
         assert errs[k] <= TOL["f32"], (k, errs[k])
