@@ -80,37 +80,6 @@ def oracle_threads():
     return max(1, min(16, n))
 
 
-def oracle_channels(x, samples, nthreads=8):
-    """Oracle on selected (b, d) channels only, full sequence.  Returns y [L, S] and final state [S, N]."""
-    bsel = np.array([b for b, _ in samples])
-    dsel = np.array([d for _, d in samples])
-    S = len(samples)
-    L = x["u"].shape[1]
-    ys = np.empty((L, S))
-    fs = np.empty((S, x["A"].shape[1]))
-    # channels of the same batch row can share one oracle call
-    for b in np.unique(bsel):
-        idx = np.nonzero(bsel == b)[0]
-        ds = dsel[idx]
-        sub = dict(u=x["u"][b:b + 1][:, :, ds], delta=x["delta"][b:b + 1][:, :, ds],
-                   z=None if x["z"] is None else x["z"][b:b + 1][:, :, ds],
-                   B=x["B"][b:b + 1], C=x["C"][b:b + 1], A=x["A"][ds], D=x["D"][ds],
-                   delta_bias=x["delta_bias"][ds])
-        y, f = R.scan_fwd(sub["u"], sub["delta"], sub["A"], sub["B"], sub["C"], D=sub["D"], z=sub["z"],
-                          delta_bias=sub["delta_bias"], softplus=True, nthreads=nthreads)
-        ys[:, idx] = y[0]
-        fs[idx] = f[0]
-    return ys, fs
-
-
-def sample_channels(rng, batch, dim, count):
-    count = min(count, batch * dim)
-    flat = rng.choice(batch * dim, size=count, replace=False)
-    # always include the first and last channel (tile edges)
-    flat[0], flat[-1] = 0, batch * dim - 1
-    return [(int(f // dim), int(f % dim)) for f in flat]
-
-
 class _Env:
     def __init__(self, name, value):
         self.name, self.value = name, value
