@@ -207,9 +207,12 @@ __global__ void __launch_bounds__(64 * kLaneWaves) lane_scan_kernel(LaneParams p
     const int r0 = first_row(g);
     return r0 < 0 ? static_cast<int>(bytes) : r0 * static_cast<int>(row_bytes);
   };
+  // (a group wholly past the chunk is only prefetched, never computed: past 2^31 - 1 bytes of records its
+  // offset may stay in range and read records of later tokens)
+  const int bc_past = static_cast<int>(bc_bytes < 0x7fffffffLL ? bc_bytes : 0x7fffffffLL);
   auto rec_soff = [&](int g) -> int {
     const int r0 = first_row(g);
-    return r0 < 0 ? static_cast<int>(bc_bytes) : r0 * static_cast<int>(bc_stride);
+    return r0 < 0 ? bc_past : r0 * static_cast<int>(bc_stride);
   };
   auto issue = [&](LaneTok (&r)[TG], int g) {
     const int so = tok_soff(g), sr = rec_soff(g);
@@ -336,9 +339,10 @@ __global__ void __launch_bounds__(64 * kLaneWaves) lane_scan_kernel(LaneParams p
     __builtin_amdgcn_sched_barrier(0);
   }
   if (g < ng) {
-    issue(r1, g + 1);
+    const bool two = g + 1 < ng;
+    if (two) issue(r1, g + 1);
     compute(r0, g, IC<1>{});
-    compute(r1, g + 1, IC<1>{});
+    if (two) compute(r1, g + 1, IC<1>{});
   }
 
   if constexpr (FULL) {
