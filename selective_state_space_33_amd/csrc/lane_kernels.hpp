@@ -196,9 +196,11 @@ __global__ void __launch_bounds__(64 * kLaneWaves) lane_scan_kernel(LaneParams p
   }
 
   // Group g of the walk: tokens g*TG .. g*TG+TG-1 of the chunk (forward), or tokens nt-1-g*TG down to
-  // nt-TG-g*TG (the structured pair pass walks backwards; its chunks are whole groups).  The scalar
-  // offsets of the group's first row in the token rows and in the B/C rows; a group wholly past the
-  // chunk takes each range's size, so all of it reads zero.
+  // nt-TG-g*TG (the structured pair pass walks backwards; its chunks, all but the sequence's last, are
+  // whole groups).  The scalar offsets of the group's first row in the token rows and in the B/C rows.  A
+  // group wholly past the chunk is only prefetched, never computed: its token offset is the range's size
+  // (it reads zero), its record offset the records' size or 2^31 - 1, whichever is less (past 2^31 - 1
+  // bytes of records it may read records of later tokens).
   auto first_row = [&](int g) -> int {
     if constexpr (BACKWARD) return g * TG < nt ? nt - TG - g * TG : -1;
     else return g * TG < nt ? g * TG : -1;
@@ -207,8 +209,6 @@ __global__ void __launch_bounds__(64 * kLaneWaves) lane_scan_kernel(LaneParams p
     const int r0 = first_row(g);
     return r0 < 0 ? static_cast<int>(bytes) : r0 * static_cast<int>(row_bytes);
   };
-  // (a group wholly past the chunk is only prefetched, never computed: past 2^31 - 1 bytes of records its
-  // offset may stay in range and read records of later tokens)
   const int bc_past = static_cast<int>(bc_bytes < 0x7fffffffLL ? bc_bytes : 0x7fffffffLL);
   auto rec_soff = [&](int g) -> int {
     const int r0 = first_row(g);
