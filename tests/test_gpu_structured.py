@@ -105,6 +105,15 @@ def test_every_dstate(N):
         compare(x, "f32")
 
 
+@pytest.mark.parametrize("N", [3, 8, 12])
+def test_every_states_per_lane_bf16(N):
+    """4, 8 and 16 states per lane with bf16 storage (B and C packed into records, zero past N), ragged tiles."""
+    x = structured_inputs(np.random.default_rng(80 + N), 2, 530, 150, N, "bf16")
+    say(f"structured bf16 2x530x150x{N}")
+    with LaneK(3):
+        compare(x, "bf16")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_optional_inputs_off(dtype):
     """No z, D or bias, and softplus off (the raw steps are then the steps: made positive and small here)."""
