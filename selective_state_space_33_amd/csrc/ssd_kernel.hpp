@@ -21,12 +21,15 @@
 //   G^T = B C^T              (Q x Q, K = N) -> M[t][s] = G[t][s] exp(cs_t - cs_s) delta_s on s <= t
 //   Y   = exp(cs_t) C H + M x  (Q x P; K = N, then K = Q)  -> + D x, times SiLU(z), y
 //   H   = exp(cs_end) H + W^T x   (N x P, K = Q),  W[s][n] = exp(cs_end - cs_s) delta_s B[s][n]
-// Every operand sits in LDS with its K index contiguous, so a fragment is one
-// 16-byte read: C and B by token row, M by output row, x, W and H transposed
-// (x^T [p][s], W^T [n][s], H^T [p][n]).  The orientations are chosen so that
-// every write is an 8-byte run: the accumulators of G^T and H hold four
-// consecutive K-side indices per lane, and B and x are loaded four token rows
-// at a time so that their transposes are written four tokens per store.
+// C, B (by token row), M (by output row) and H^T [p][n] sit in LDS with their
+// K index contiguous, so a fragment is one 16-byte read; the accumulators of
+// G^T and H hold four consecutive K-side indices per lane, so M and H^T are
+// written as 8-byte runs.  x, z and W, whose K index is the token, are stored
+// by token row as they arrive (x [s][p], z [t][p], W [s][n]: consecutive lanes
+// write consecutive columns of one row, free of bank conflicts) and read with
+// gfx950's transposed LDS read (ds_read_b64_tr_b16), which hands each lane
+// four consecutive tokens of one column.  (Writing them transposed instead put
+// the 64 lanes of a store on rows two apart, eight banks for 128 dwords.)
 //
 // Precision.  B, C and x arrive as bf16 and are staged as fp16, exactly
 // (every bf16 value of magnitude 2^-14 .. 65504 is an fp16 value), so G^T =
@@ -137,12 +140,49 @@ __device__ __forceinline__ float f16_hi_of(uint32_t pair) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<unsigned short>(pair >> 16)));
 }
 
+// Transposed LDS read (ds_read_b64_tr_b16, gfx950).  Within each group of 16
+// lanes, lane i returns, as element j, the 16-bit value that lane 4j + i/4 of
+// its group addresses at position i % 4 of its own 8-byte run.  So if lane
+// (g, i) of group g addresses row r0(g) + i/4 of a row-major array at column
+// c0 + 4 (i % 4), lane (g, i) receives column c0 + i of rows r0(g) .. r0(g)+3:
+// four consecutive K values of one MFMA row or column, from an array stored
+// with K as its row index.  row_of / col_of give that addressing.
+__device__ __forceinline__ u32x2_t lds_read_tr4(const unsigned short* base, int row0, int col0, int stride) {
+  typedef short v4i16 __attribute__((ext_vector_type(4)));
+  const int i = threadIdx.x & 15;
+  const unsigned short* a = base + (row0 + (i >> 2)) * stride + col0 + 4 * (i & 3);
+  const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(a));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+// An MFMA 16x16x32 operand fragment from a row-major [K][.] array (K rows k0 .. k0+31, column col0 + lr): two
+// transposed reads.  Lane group lq takes K rows k0 + 4 lq .. k0 + 4 lq + 3 and k0 + 16 + 4 lq .. k0 + 16 + 4 lq + 3,
+// not 8 lq .. 8 lq + 7: the two groups of 16 lanes that a read serves together then touch 8 consecutive rows,
+// which lie on distinct banks.  The contraction does not depend on the order of K as long as both operands of a
+// product share it: the other operand is a fragment from here too, or M, whose columns are stored in this order
+// (kperm_col).
+__device__ __forceinline__ f16x8_t lds_frag_tr(const unsigned short* base, int k0, int col0, int lq, int stride) {
+  const u32x2_t a = lds_read_tr4(base, k0 + 4 * lq, col0, stride);
+  const u32x2_t b = lds_read_tr4(base, k0 + 16 + 4 * lq, col0, stride);
+  return __builtin_bit_cast(f16x8_t, u32x4_t{a[0], a[1], b[0], b[1]});
+}
+// Where the run of four K indices starting at k (a multiple of 4) is stored in a row whose 16-byte fragment
+// reads must follow lds_frag_tr's K order: run j of a 32-wide block goes to position 2 j (j < 4) or 2 (j - 4) + 1.
+__device__ __forceinline__ int kperm_col(int k) {
+  const int j = (k >> 2) & 7;
+  return (k & ~31) + 4 * (j < 4 ? 2 * j : 2 * (j - 4) + 1);
+}
+
 template <int N>
 __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   constexpr int Q = kSsdQ, P = kSsdP, NW = ssd_waves(N), NTH = 64 * NW;
   static_assert(N == 32 || N == 64 || N == 128, "dstate: 32, 64 or 128");
   constexpr int SN = N + 8;  // padded rows (elements) of the [.][N] arrays: 16-byte aligned, banks staggered
   constexpr int SQ = Q + 8;  // padded rows of the [.][Q] arrays
+  // Rows of the arrays read transposed (x, z by channel, W by state): a row is (8 x odd) dwords, so the 16
+  // rows x 32 bytes that a transposed read of 64 lanes touches cover every bank four times, and the row
+  // writes (one token row, consecutive lanes on consecutive columns) are conflict-free.
+  constexpr int SX = P + 16;
+  constexpr int SW = N + 16;
   constexpr int NT = N / 16;  // 16-wide state tiles
   constexpr int HT = NT * 4 / NW;  // state tiles per wavefront (NT x 4 tiles over NW wavefronts)
   constexpr int YT = 16 / NW;      // Y tiles per wavefront (4 x 4 over NW wavefronts)
@@ -156,10 +196,10 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
 
   __shared__ __attribute__((aligned(16))) unsigned short sC[Q * SN];   // C [t][n], fp16
   __shared__ __attribute__((aligned(16))) unsigned short sB[Q * SN];   // B [s][n], fp16
-  __shared__ __attribute__((aligned(16))) unsigned short sWh[N * SQ];  // W^T [n][s], fp16 hi
-  __shared__ __attribute__((aligned(16))) unsigned short sWl[N * SQ];  // fp16 lo
-  __shared__ __attribute__((aligned(16))) unsigned short sXT[P * SQ];  // x^T [p][s], fp16
-  __shared__ __attribute__((aligned(16))) unsigned short sZT[P * SQ];  // z^T [p][t]
+  __shared__ __attribute__((aligned(16))) unsigned short sWh[Q * SW];  // W [s][n], fp16 hi
+  __shared__ __attribute__((aligned(16))) unsigned short sWl[Q * SW];  // fp16 lo
+  __shared__ __attribute__((aligned(16))) unsigned short sX[Q * SX];   // x [s][p], fp16
+  __shared__ __attribute__((aligned(16))) unsigned short sZ[Q * SX];   // z [t][p], bf16
   __shared__ __attribute__((aligned(16))) unsigned short sM[Q * SQ];   // M [t][s], fp16
   __shared__ __attribute__((aligned(16))) unsigned short sH[P * SN];   // H^T [p][n], fp16
   // per chunk parity: A * (cumulative step) within the chunk, and the step delta_t; wavefront 0
@@ -321,16 +361,12 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       }
     }
     if (tid < XI) {
-      // x^T as fp16: channel 2xpp takes the low halves of the four rows, 2xpp+1 the high halves
-      const float even[4] = {bf16_lo_of(gx[0]), bf16_lo_of(gx[1]), bf16_lo_of(gx[2]), bf16_lo_of(gx[3])};
-      const float odd[4] = {bf16_hi_of(gx[0]), bf16_hi_of(gx[1]), bf16_hi_of(gx[2]), bf16_hi_of(gx[3])};
-      *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp) * SQ + xs0]) = cvt4_f16(even);
-      *reinterpret_cast<u32x2_t*>(&sXT[(2 * xpp + 1) * SQ + xs0]) = cvt4_f16(odd);
+      // x as fp16 and z as loaded, by token row: channels 2xpp, 2xpp+1 of rows xs0 .. xs0+3
+#pragma unroll
+      for (int r = 0; r < 4; ++r) *reinterpret_cast<uint32_t*>(&sX[(xs0 + r) * SX + 2 * xpp]) = bf16x2_to_f16x2(gx[r]);
       if (p.z) {
-        *reinterpret_cast<u32x2_t*>(&sZT[(2 * xpp) * SQ + xs0]) =
-            u32x2_t{(gzz[0] & 0xffffu) | (gzz[1] << 16), (gzz[2] & 0xffffu) | (gzz[3] << 16)};
-        *reinterpret_cast<u32x2_t*>(&sZT[(2 * xpp + 1) * SQ + xs0]) =
-            u32x2_t{(gzz[0] >> 16) | (gzz[1] & 0xffff0000u), (gzz[2] >> 16) | (gzz[3] & 0xffff0000u)};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) *reinterpret_cast<uint32_t*>(&sZ[(xs0 + r) * SX + 2 * xpp]) = gzz[r];
       }
     }
     __syncthreads();
@@ -394,9 +430,9 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
         for (int j = 0; j < 4; ++j)
           m[j] = (s0 + j <= t) ? g[j] * __builtin_amdgcn_exp2f((cst - css[j]) * kLog2eF) * dls[j] : 0.0f;
       }
-      *reinterpret_cast<u32x2_t*>(&sM[t * SQ + s0]) = cvt4_f16(m);
+      *reinterpret_cast<u32x2_t*>(&sM[t * SQ + kperm_col(s0)]) = cvt4_f16(m);  // in lds_frag_tr's K order
     }
-    // ---- W^T[n][s] = exp(cs_end - cs_s) delta_s B[s][n], from the B rows in registers
+    // ---- W[s][n] = exp(cs_end - cs_s) delta_s B[s][n], from the B rows in registers, by token row
     {
 #pragma unroll
       for (int i = 0; i < B_PER; ++i) {
@@ -404,19 +440,19 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
         if (e < B_ITEMS) {
           const int np = e % (N / 2), s0 = 4 * (e / (N / 2));
           const f32x4_t ws = *reinterpret_cast<const f32x4_t*>(&sWS[par][s0]);
-          float v0[4], v1[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            v0[r] = ws[r] * bf16_lo_of(gb[i][r]);
-            v1[r] = ws[r] * bf16_hi_of(gb[i][r]);
+          for (int r2 = 0; r2 < 2; ++r2) {
+            // rows s0 + 2 r2 and s0 + 2 r2 + 1: four values, split as hi + lo
+            const float v[4] = {ws[2 * r2] * bf16_lo_of(gb[i][2 * r2]), ws[2 * r2] * bf16_hi_of(gb[i][2 * r2]),
+                                ws[2 * r2 + 1] * bf16_lo_of(gb[i][2 * r2 + 1]),
+                                ws[2 * r2 + 1] * bf16_hi_of(gb[i][2 * r2 + 1])};
+            u32x2_t hi, lo;
+            split4_f16(v, hi, lo);
+            *reinterpret_cast<uint32_t*>(&sWh[(s0 + 2 * r2) * SW + 2 * np]) = hi[0];
+            *reinterpret_cast<uint32_t*>(&sWl[(s0 + 2 * r2) * SW + 2 * np]) = lo[0];
+            *reinterpret_cast<uint32_t*>(&sWh[(s0 + 2 * r2 + 1) * SW + 2 * np]) = hi[1];
+            *reinterpret_cast<uint32_t*>(&sWl[(s0 + 2 * r2 + 1) * SW + 2 * np]) = lo[1];
           }
-          u32x2_t hi, lo;
-          split4_f16(v0, hi, lo);
-          *reinterpret_cast<u32x2_t*>(&sWh[(2 * np) * SQ + s0]) = hi;
-          *reinterpret_cast<u32x2_t*>(&sWl[(2 * np) * SQ + s0]) = lo;
-          split4_f16(v1, hi, lo);
-          *reinterpret_cast<u32x2_t*>(&sWh[(2 * np + 1) * SQ + s0]) = hi;
-          *reinterpret_cast<u32x2_t*>(&sWl[(2 * np + 1) * SQ + s0]) = lo;
         }
       }
     }
@@ -437,18 +473,18 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
         const f16x8_t ah = *reinterpret_cast<const f16x8_t*>(&sM[mr]);
 #pragma unroll
         for (int c = 0; c < YT; ++c) {
-          const f16x8_t bb = *reinterpret_cast<const f16x8_t*>(&sXT[(16 * (py0 + c) + lr) * SQ + 32 * kk + 8 * lq]);
+          const f16x8_t bb = lds_frag_tr(sX, 32 * kk, 16 * (py0 + c), lq, SX);
           yacc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bb, yacc[c], 0, 0, 0);
         }
       }
-      // + D x, times SiLU(z), rounded to bf16; x of four consecutive tokens is one 8-byte read of x^T
+      // + D x, times SiLU(z), rounded to bf16; x and z of four consecutive tokens are one transposed read each
 #pragma unroll
       for (int c = 0; c < YT; ++c) {
         const int pch = 16 * (py0 + c) + lr;
-        const u32x2_t xq = *reinterpret_cast<const u32x2_t*>(&sXT[pch * SQ + 16 * ty + 4 * lq]);
+        const u32x2_t xq = lds_read_tr4(sX, 16 * ty + 4 * lq, 16 * (py0 + c), SX);
         const float xv[4] = {f16_lo_of(xq[0]), f16_hi_of(xq[0]), f16_lo_of(xq[1]), f16_hi_of(xq[1])};
         u32x2_t zq = {0u, 0u};
-        if (p.z) zq = *reinterpret_cast<const u32x2_t*>(&sZT[pch * SQ + 16 * ty + 4 * lq]);
+        if (p.z) zq = lds_read_tr4(sZ, 16 * ty + 4 * lq, 16 * (py0 + c), SX);
         const float zv[4] = {bf16_lo_of(zq[0]), bf16_hi_of(zq[0]), bf16_lo_of(zq[1]), bf16_hi_of(zq[1])};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -470,19 +506,18 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
         for (int j = 0; j < 4; ++j) hacc[i][j] *= fade;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const f16x8_t bb = *reinterpret_cast<const f16x8_t*>(&sXT[(16 * ph + lr) * SQ + 32 * kk + 8 * lq]);
+        const f16x8_t bb = lds_frag_tr(sX, 32 * kk, 16 * ph, lq, SX);
 #pragma unroll
         for (int i = 0; i < HT; ++i) {
-          const int wr = (16 * (nb0 + NBS * i) + lr) * SQ + 32 * kk + 8 * lq;
-          const f16x8_t ah = *reinterpret_cast<const f16x8_t*>(&sWh[wr]);
-          const f16x8_t al = *reinterpret_cast<const f16x8_t*>(&sWl[wr]);
+          const f16x8_t ah = lds_frag_tr(sWh, 32 * kk, 16 * (nb0 + NBS * i), lq, SW);
+          const f16x8_t al = lds_frag_tr(sWl, 32 * kk, 16 * (nb0 + NBS * i), lq, SW);
           hacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bb, hacc[i], 0, 0, 0);
           hacc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bb, hacc[i], 0, 0, 0);
         }
       }
     }
     if (w == 0 && k + 1 < ke) steps(t0 + Q, par ^ 1);  // the next chunk's raw steps arrived meanwhile
-    __syncthreads();  // every read of H^T, x^T, W^T, C, B and M for this chunk is done
+    __syncthreads();  // every read of H^T, x, W, C, B and M for this chunk is done
     stage_state();      // H^T for the next chunk
     if (stop_flag != nullptr && k + 1 - kb >= k_stop && k + 1 < ke) {
       if (tid == 0) sWord = __hip_atomic_load(stop_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
