@@ -281,9 +281,13 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       }
     }
   };
-  const int xpp = tid % (P / 2), xs0 = 4 * (tid / (P / 2));  // x item: channels 2xpp, 2xpp+1 of tokens xs0..xs0+3
+  // x item of the last XI threads (the wavefronts with the fewest tiles of G): channels 2xpp, 2xpp+1 of tokens
+  // xs0 .. xs0+3
+  const int xt = tid - (NTH - XI);
+  const bool xthr = xt >= 0;
+  const int xpp = (xthr ? xt : 0) % (P / 2), xs0 = 4 * ((xthr ? xt : 0) / (P / 2));
   auto load_x = [&](int t0) {
-    if (tid < XI) {
+    if (xthr) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         gx[r] = __builtin_amdgcn_raw_buffer_load_b32(rs_x, ((t0 + xs0 + r) * rowe + 2 * xpp) * 2, 0, 0);
@@ -360,8 +364,11 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
           *reinterpret_cast<uint32_t*>(&sB[(s0 + r) * SN + 2 * np]) = bf16x2_to_f16x2(gb[i][r]);
       }
     }
-    if (tid < XI) {
-      // x as fp16 and z as loaded, by token row: channels 2xpp, 2xpp+1 of rows xs0 .. xs0+3
+    __syncthreads();
+    // x as fp16 and z as loaded, by token row (channels 2xpp, 2xpp+1 of rows xs0 .. xs0+3).  They are first read
+    // after the next barrier, and the last chunk's reads of them ended before the one above, so staging them
+    // here spares a barrier at the end of the chunk.
+    if (xthr) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) *reinterpret_cast<uint32_t*>(&sX[(xs0 + r) * SX + 2 * xpp]) = bf16x2_to_f16x2(gx[r]);
       if (p.z) {
@@ -369,7 +376,6 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
         for (int r = 0; r < 4; ++r) *reinterpret_cast<uint32_t*>(&sZ[(xs0 + r) * SX + 2 * xpp]) = gzz[r];
       }
     }
-    __syncthreads();
     if (k + 1 < ke) {  // in flight through the chunk's products
       load_c(t0 + Q);
       load_x(t0 + Q);
@@ -517,8 +523,9 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       }
     }
     if (w == 0 && k + 1 < ke) steps(t0 + Q, par ^ 1);  // the next chunk's raw steps arrived meanwhile
-    __syncthreads();  // every read of H^T, x, W, C, B and M for this chunk is done
-    stage_state();      // H^T for the next chunk
+    // No barrier here: the next chunk's C and B (staged next) and H^T are not read in this part of the chunk, and
+    // its M, W, x and z are written only after the next chunk's first barrier.
+    stage_state();      // H^T for the next chunk (read after the next chunk's first barrier)
     if (stop_flag != nullptr && k + 1 - kb >= k_stop && k + 1 < ke) {
       if (tid == 0) sWord = __hip_atomic_load(stop_flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __syncthreads();
@@ -527,6 +534,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       if (stop) return k + 1;
     }
   }
+  __syncthreads();  // every read of this run's operands is done before the caller stages anything
   return ke;
   };
   auto write_final = [&]() {
