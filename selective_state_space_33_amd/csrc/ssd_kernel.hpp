@@ -31,6 +31,12 @@
 // four consecutive tokens of one column.  (Writing them transposed instead put
 // the 64 lanes of a store on rows two apart, eight banks for 128 dwords.)
 //
+// Two barriers per chunk: C and B are staged before the first; x, z, C H, M
+// and W between the two; M x, the epilogue, the state update and the staging
+// of the next state after the second, from where each wavefront goes straight
+// on to the next chunk's C and B (no operand that this last part reads is
+// rewritten before the next chunk's first barrier).
+//
 // Precision.  B, C and x arrive as bf16 and are staged as fp16, exactly
 // (every bf16 value of magnitude 2^-14 .. 65504 is an fp16 value), so G^T =
 // B C^T is exact.  The products take fp16 operands (11 significant bits,
