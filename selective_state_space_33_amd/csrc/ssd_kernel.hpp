@@ -192,12 +192,12 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   constexpr int NT = N / 16;  // 16-wide state tiles
   constexpr int HT = NT * 4 / NW;  // state tiles per wavefront (NT x 4 tiles over NW wavefronts)
   constexpr int YT = 16 / NW;      // Y tiles per wavefront (4 x 4 over NW wavefronts)
-  constexpr int XI = (Q / 4) * (P / 2);  // x items (4 tokens x 2 channels), one per thread up to XI
+  constexpr int XR = Q * (P / 2) / NTH;  // token rows of a thread's x item (two channels of XR consecutive rows)
   constexpr int C_PIECES = Q * N / 8;         // 16-byte pieces of a chunk's C
   constexpr int C_PER = (C_PIECES + NTH - 1) / NTH;
   constexpr int B_ITEMS = (Q / 4) * (N / 2);  // (4 tokens) x (2 states) items of a chunk's B
   constexpr int B_PER = (B_ITEMS + NTH - 1) / NTH;
-  static_assert(XI <= NTH && HT >= 1 && YT >= 1, "work split");
+  static_assert(XR >= 1 && XR * NTH == Q * (P / 2) && HT >= 1 && YT >= 1, "work split");
   constexpr float kLog2eF = 1.4426950408889634f;
 
   __shared__ __attribute__((aligned(16))) unsigned short sC[Q * SN];   // C [t][n], fp16
@@ -263,7 +263,7 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
   // raw step.  x and z are staged transposed, so that the epilogue reads the
   // z of four consecutive tokens as one 8-byte piece.
   u32x4_t gc[C_PER];
-  uint32_t gb[B_PER][4], gx[4], gzz[4];
+  uint32_t gb[B_PER][4], gx[XR], gzz[XR];
   float graw = 0.0f;
   auto load_c = [&](int t0) {
 #pragma unroll
@@ -287,19 +287,16 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
       }
     }
   };
-  // x item of the last XI threads (the wavefronts with the fewest tiles of G): channels 2xpp, 2xpp+1 of tokens
-  // xs0 .. xs0+3
-  const int xt = tid - (NTH - XI);
-  const bool xthr = xt >= 0;
-  const int xpp = (xthr ? xt : 0) % (P / 2), xs0 = 4 * ((xthr ? xt : 0) / (P / 2));
+  // x item of every thread: channels 2xpp, 2xpp+1 of tokens xs0 .. xs0+XR-1
+  const int xpp = tid % (P / 2), xs0 = XR * (tid / (P / 2));
   auto load_x = [&](int t0) {
-    if (xthr) {
+    {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < XR; ++r)
         gx[r] = __builtin_amdgcn_raw_buffer_load_b32(rs_x, ((t0 + xs0 + r) * rowe + 2 * xpp) * 2, 0, 0);
       if (p.z) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < XR; ++r)
           gzz[r] = __builtin_amdgcn_raw_buffer_load_b32(rs_z, ((t0 + xs0 + r) * rowe + 2 * xpp) * 2, 0, 0);
       }
     }
@@ -374,12 +371,12 @@ __global__ void __launch_bounds__(64 * ssd_waves(N)) ssd_kernel(SsdParams p) {
     // x as fp16 and z as loaded, by token row (channels 2xpp, 2xpp+1 of rows xs0 .. xs0+3).  They are first read
     // after the next barrier, and the last chunk's reads of them ended before the one above, so staging them
     // here spares a barrier at the end of the chunk.
-    if (xthr) {
+    {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) *reinterpret_cast<uint32_t*>(&sX[(xs0 + r) * SX + 2 * xpp]) = bf16x2_to_f16x2(gx[r]);
+      for (int r = 0; r < XR; ++r) *reinterpret_cast<uint32_t*>(&sX[(xs0 + r) * SX + 2 * xpp]) = bf16x2_to_f16x2(gx[r]);
       if (p.z) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) *reinterpret_cast<uint32_t*>(&sZ[(xs0 + r) * SX + 2 * xpp]) = gzz[r];
+        for (int r = 0; r < XR; ++r) *reinterpret_cast<uint32_t*>(&sZ[(xs0 + r) * SX + 2 * xpp]) = gzz[r];
       }
     }
     if (k + 1 < ke) {  // in flight through the chunk's products
